@@ -1,0 +1,318 @@
+"""Plain CPU oracle for the SVDQuant W4A4 + low-rank linear layer.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the library imports this module; only
+the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` use it. It shares no code, tables or helpers with the HIP path.
+
+What the method computes (sources are the five web pages on SVDQuant):
+
+* The layer is Y ~= Xhat.L1.L2 + Q(Xhat).Q(R) + b, with Xhat = X.diag(lam)^-1.
+  Smoothing moves activation outliers onto the weights; the smoothed weight
+  diag(lam).W is split by an SVD into a 16-bit low-rank branch L1.L2 and a
+  residual R; both Xhat and R are quantized to 4 bits
+  (chattools.cn overview, section "SVDQuant的技术原理" (technical principles),
+  items on outlier handling and the low-rank branch; SVDQuant paper abstract
+  on ai-digest.ru).
+* Dropping the dominant singular values is optimal in the Frobenius norm
+  (Eckart-Young-Mirsky; chattools.cn overview, same section, EYM item).
+* LoRA adapters join the low-rank branch without re-quantizing R
+  (chattools.cn overview, section "SVDQuant的主要功能" (main features), LoRA
+  item; SVDQuant abstract).
+
+The pages print no formulas, group size or rounding rule. The readings taken
+here, each applied in exactly one function below, are:
+
+* lam_j = sqrt(max_i |X_ij| / max_n |W_jn|) (migration strength 1/2), 1 where
+  either max is 0, rounded to fp32; inv_lam = fp32(1/lam).
+* Sigma is split as Sigma^(1/2) on each side; L1, L2 are rounded to fp16 once
+  from fp64; the residual is formed from the *stored* fp16 factors.
+* Quantizer Q over each group of 64 consecutive input channels: symmetric,
+  scale s = fp16(min(absmax/7, 65504)) (fp32 division, then fp16 RNE),
+  codes q = clamp(rint(v * fp32(1/s)), -7, 7), s == 0 -> all codes 0.
+  X-hat groups run along each token row; R groups run down K for each output
+  column.
+* Codes are 4-bit two's complement, element 2j in the low nibble of byte j.
+* The low-rank branch is fp16 x fp16: Xhat and D are rounded to fp16 where
+  they enter a product.
+
+Data are fp64 except at the rounding points named in each function.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 64
+QMAX = 7
+F16_MAX = 65504.0
+
+
+# --------------------------------------------------------------------------
+# rounding helpers
+
+
+def to_f16(x) -> np.ndarray:
+    """Round to IEEE binary16, nearest-even, in one step from the input type
+    (numpy converts float64 -> float16 directly, without passing through
+    float32)."""
+    return np.asarray(x).astype(np.float16)
+
+
+def to_f32(x) -> np.ndarray:
+    return np.asarray(x).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# smoothing (chattools.cn overview, technical principles, outlier item;
+# SVDQuant abstract: outliers are first moved from activations to weights)
+
+
+def channel_absmax(X) -> np.ndarray:
+    """max_i |X_ij| per input channel j, as float64 (exact)."""
+    return np.max(np.abs(np.asarray(X, dtype=np.float64)), axis=0)
+
+
+def smoothing_factors(x_absmax, W) -> np.ndarray:
+    """lam_j = sqrt(max|X_j| / max|W_j|) in fp64, rounded to fp32; 1 if either is 0."""
+    xa = np.asarray(x_absmax, dtype=np.float64)
+    wa = np.max(np.abs(np.asarray(W, dtype=np.float64)), axis=1)
+    ok = (xa > 0) & (wa > 0)
+    lam = np.ones_like(xa)
+    lam[ok] = np.sqrt(xa[ok] / wa[ok])
+    return to_f32(lam)
+
+
+def inv_smoothing(lam32) -> np.ndarray:
+    """inv_lam = 1/lam as a correctly rounded fp32 division."""
+    lam32 = to_f32(lam32)
+    return (np.float32(1.0) / lam32).astype(np.float32)
+
+
+def smooth_weight(W, lam32) -> np.ndarray:
+    """What = diag(lam).W in fp64 (exact: fp32 x fp32 fits in 53 bits)."""
+    return np.asarray(lam32, dtype=np.float64)[:, None] * np.asarray(W, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# SVD split (chattools.cn overview, technical principles, low-rank-branch and
+# EYM items)
+
+
+def svd_canonical(What):
+    """What = U diag(S) Vt (LAPACK, fp64), with a fixed sign per singular pair:
+    the entry of largest magnitude in each column of U is positive (first such
+    index on ties)."""
+    U, S, Vt = np.linalg.svd(np.asarray(What, dtype=np.float64), full_matrices=False)
+    idx = np.argmax(np.abs(U), axis=0)
+    sgn = np.sign(U[idx, np.arange(U.shape[1])])
+    sgn[sgn == 0] = 1.0
+    return U * sgn[None, :], S, Vt * sgn[:, None]
+
+
+def lowrank_factors_f64(U, S, Vt, r: int):
+    """L1 = U_r Sigma_r^(1/2) (K x r), L2 = Sigma_r^(1/2) Vt_r (r x N), in fp64."""
+    h = np.sqrt(S[:r])
+    return U[:, :r] * h[None, :], h[:, None] * Vt[:r, :]
+
+
+def lowrank_factors(U, S, Vt, r: int):
+    """The 16-bit branch: the fp64 factors rounded once to fp16."""
+    L1, L2 = lowrank_factors_f64(U, S, Vt, r)
+    return to_f16(L1), to_f16(L2)
+
+
+def residual(What, L1, L2) -> np.ndarray:
+    """R = What - L1.L2 from the stored factors, in fp64."""
+    return np.asarray(What, dtype=np.float64) - (
+        np.asarray(L1, dtype=np.float64) @ np.asarray(L2, dtype=np.float64))
+
+
+# --------------------------------------------------------------------------
+# 4-bit group quantizer (chattools.cn overview, main features: weights and
+# activations at 4 bits; technical principles: the residual is quantized to
+# 4 bits)
+
+
+def quantize_groups(v32, group: int = GROUP):
+    """Q along the last axis, in groups of ``group`` consecutive values.
+
+    v32 is rounded to fp32 first. Returns (codes int8 in [-7, 7], scales fp16)
+    with scales shaped (..., K/group)."""
+    v = to_f32(v32)
+    *lead, K = v.shape
+    assert K % group == 0
+    vg = v.reshape(*lead, K // group, group)
+    a = np.max(np.abs(vg), axis=-1)                                   # exact
+    s32 = np.minimum(a / np.float32(QMAX), np.float32(F16_MAX))       # fp32 division
+    s16 = s32.astype(np.float16)                                      # RNE
+    sf = s16.astype(np.float32)
+    zero = sf == 0
+    inv = np.where(zero, np.float32(0.0),
+                   np.float32(1.0) / np.where(zero, np.float32(1.0), sf)).astype(np.float32)
+    prod = (vg * inv[..., None]).astype(np.float32)                   # fp32 multiply
+    q = np.clip(np.rint(prod), -QMAX, QMAX).astype(np.int8)           # half to even
+    return q.reshape(*lead, K), s16
+
+
+def dequantize_groups(q, s16, group: int = GROUP) -> np.ndarray:
+    """s * q in fp64 (exact)."""
+    q = np.asarray(q, dtype=np.float64)
+    *lead, K = q.shape
+    s = np.asarray(s16, dtype=np.float64)
+    return (q.reshape(*lead, K // group, group) * s[..., None]).reshape(*lead, K)
+
+
+def pack_nibbles(q) -> np.ndarray:
+    """int8 codes (..., K) -> uint8 (..., K/2); element 2j in the low nibble."""
+    q = np.asarray(q, dtype=np.int16)
+    lo = q[..., 0::2] & 0xF
+    hi = q[..., 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(b) -> np.ndarray:
+    """uint8 (..., K/2) -> int8 codes (..., K), sign-extending each nibble."""
+    b = np.asarray(b, dtype=np.int16)
+    lo = b & 0xF
+    hi = (b >> 4) & 0xF
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def quantize_weight(R, group: int = GROUP):
+    """Q of R (K x N) down K for each output column: (w_codes N x K/2, w_scales N x K/group)."""
+    q, s = quantize_groups(to_f32(R).T, group)
+    return pack_nibbles(q), s
+
+
+def smooth_activation(X, inv_lam32) -> np.ndarray:
+    """Xhat = fp32(float(x) * inv_lam[k]) per element (fp32 multiply)."""
+    return (to_f32(X) * to_f32(inv_lam32)[None, :]).astype(np.float32)
+
+
+def quantize_activation(X, inv_lam32, group: int = GROUP):
+    """(a_codes M x K/2, a_scales M x K/group, Xhat fp32)."""
+    xh = smooth_activation(X, inv_lam32)
+    q, s = quantize_groups(xh, group)
+    return pack_nibbles(q), s, xh
+
+
+# --------------------------------------------------------------------------
+# online part of the layer
+
+
+def down_projection(xhat32, L1) -> np.ndarray:
+    """D = fp16(Xhat) . L1, accumulated in fp64 (the products of fp16 values are exact)."""
+    return to_f16(xhat32).astype(np.float64) @ np.asarray(L1, dtype=np.float64)
+
+
+def group_partials(a_codes, w_codes, group: int = GROUP) -> np.ndarray:
+    """P[m, n, g] = sum over k in group g of qx[m,k] * qw[n,k], exact integers (int64)."""
+    qx = unpack_nibbles(a_codes).astype(np.int64)
+    qw = unpack_nibbles(w_codes).astype(np.int64)
+    M, K = qx.shape
+    N = qw.shape[0]
+    G = K // group
+    P = np.empty((M, N, G), dtype=np.int64)
+    for g in range(G):
+        sl = slice(g * group, (g + 1) * group)
+        # float64 matmul of small integers: every partial sum is an integer
+        # below 2^53, so the result is exact
+        P[:, :, g] = np.rint(qx[:, sl].astype(np.float64) @ qw[:, sl].astype(np.float64).T)
+    return P
+
+
+def scaled_group_sum(P, a_scales, w_scales) -> np.ndarray:
+    """sum_g s_x[m,g] * s_w[n,g] * P[m,n,g] in fp64."""
+    sx = np.asarray(a_scales, dtype=np.float64)
+    sw = np.asarray(w_scales, dtype=np.float64)
+    return np.einsum("mng,mg,ng->mn", np.asarray(P, dtype=np.float64), sx, sw, optimize=True)
+
+
+def lowrank_up(D, L2) -> np.ndarray:
+    """fp16(D) . L2 in fp64."""
+    return to_f16(D).astype(np.float64) @ np.asarray(L2, dtype=np.float64)
+
+
+def finalize(acc, lr, bias, out_dtype: str) -> np.ndarray:
+    y = np.asarray(acc, dtype=np.float64) + np.asarray(lr, dtype=np.float64)
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    return y.astype(np.float16 if out_dtype == "f16" else np.float32)
+
+
+# --------------------------------------------------------------------------
+# whole steps
+
+
+def prepare(W, lam32, rank: int, group: int = GROUP, svd=None):
+    """Offline prep: dict with inv_smooth, L1 (K x r fp16), L2 (r x N fp16),
+    w_codes, w_scales, sigma, and the fp64 What/R."""
+    What = smooth_weight(W, lam32)
+    U, S, Vt = svd if svd is not None else svd_canonical(What)
+    L1, L2 = lowrank_factors(U, S, Vt, rank)
+    R = residual(What, L1, L2)
+    w_codes, w_scales = quantize_weight(R, group)
+    return dict(inv_smooth=inv_smoothing(lam32), L1=L1, L2=L2, w_codes=w_codes,
+                w_scales=w_scales, sigma=S, What=What, R=R)
+
+
+def quantize_residual_from_factors(W, lam32, L1, L2, group: int = GROUP):
+    """(w_codes, w_scales) for given fp16 factors: the codes a prep with these
+    factors must produce, whatever SVD produced them."""
+    R = residual(smooth_weight(W, lam32), L1, L2)
+    return quantize_weight(R, group)
+
+
+def linear(X, inv_lam32, L1, L2, w_codes, w_scales, bias=None, out_dtype: str = "f16",
+           group: int = GROUP, return_parts: bool = False):
+    """Y = sum_g s_x s_w P + fp16(D).L2 + b, rounded to ``out_dtype``."""
+    a_codes, a_scales, xh = quantize_activation(X, inv_lam32, group)
+    D = down_projection(xh, L1)
+    P = group_partials(a_codes, w_codes, group)
+    acc = scaled_group_sum(P, a_scales, w_scales)
+    lr = lowrank_up(D, L2)
+    Y = finalize(acc, lr, bias, out_dtype)
+    if return_parts:
+        return Y, dict(a_codes=a_codes, a_scales=a_scales, xhat=xh, D=D, P=P, acc=acc, lr=lr)
+    return Y
+
+
+def linear_rows(X_rows, inv_lam32, L1, L2, w_codes, w_scales, bias=None,
+                out_dtype: str = "f16", group: int = GROUP):
+    """``linear`` on a subset of rows (rows are independent)."""
+    return linear(X_rows, inv_lam32, L1, L2, w_codes, w_scales, bias, out_dtype, group)
+
+
+# --------------------------------------------------------------------------
+# LoRA (chattools.cn overview, main features, LoRA item; SVDQuant abstract:
+# off-the-shelf LoRAs without re-quantization)
+
+
+def concat_lora(L1, L2, lam32, A, B, scale: float = 1.0):
+    """L1' = [L1 | fp16(lam (.) A * scale)], L2' = [L2 ; B].
+
+    The branch multiplies the smoothed activation, so row j of A is scaled by
+    lam_j to give Xhat.(lam (.) A) = X.A. The product lam*A is exact in fp64;
+    the scale multiply rounds once in fp64; the result rounds once to fp16."""
+    lam = np.asarray(lam32, dtype=np.float32).astype(np.float64)
+    t = lam[:, None] * np.asarray(A, dtype=np.float64)
+    t = t * np.float64(np.float32(scale))
+    L1n = np.concatenate([np.asarray(L1, dtype=np.float16), to_f16(t)], axis=1)
+    L2n = np.concatenate([np.asarray(L2, dtype=np.float16), np.asarray(B, dtype=np.float16)], axis=0)
+    return L1n, L2n
+
+
+# --------------------------------------------------------------------------
+# glue between the two layers of a DiT MLP (textbook GELU, tanh form; the
+# pages do not describe it)
+
+
+def gelu_tanh(x) -> np.ndarray:
+    """0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) in fp64, rounded to fp16."""
+    x = np.asarray(x, dtype=np.float64)
+    y = 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+    return to_f16(y)

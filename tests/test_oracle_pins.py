@@ -1,0 +1,11 @@
+"""The CPU oracle against its pins (closed forms, invariants, hand-derived
+golden values and plain-Python brute force). Runs on the CPU."""
+import pytest
+
+import oracle
+import pins
+
+
+@pytest.mark.parametrize("check", pins.ALL_CHECKS, ids=lambda f: f.__name__)
+def test_pin(check):
+    check(oracle.svdq_ref)

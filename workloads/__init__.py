@@ -1,0 +1,147 @@
+"""Seeded synthetic inputs for the SVDQuant linear layer.
+
+This module only draws random numbers and shapes. It holds none of the
+method's arithmetic (no smoothing, SVD, quantization or matmul), so both the
+CPU oracle and the HIP path can take their inputs from it without sharing
+any of the computation.
+
+Every tensor comes from ``numpy.random.default_rng([config, layer, tensor])``
+so each one can be regenerated on its own, on any machine.
+
+Distributions (the workloads are DiT- and UNet-shaped linear layers; the
+pages describe SVDQuant on DiT and UNet diffusion models such as FLUX.1,
+PixArt-Sigma and SDXL: the SVDQuant paper abstract as given on ai-digest.ru,
+and the chattools.cn overview, section "SVDQuant的主要功能" (main features),
+item on supported architectures):
+
+* activations X ~ N(0, 1), with ``max(1, rint(frac*K))`` input channels,
+  drawn without replacement, multiplied by an outlier factor (x20 at 1%);
+* weights W ~ N(0, 0.02^2) in fp32, with the same count of input rows
+  (drawn independently of X's channels) multiplied by x10;
+* pre-activations for a down-projection: N(0, 1) with 0.5% channels x15
+  (the consumer applies GELU-tanh to them);
+* LoRA factors A (K x rl) and B (rl x N) ~ N(0, 0.01^2), stored as fp16.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List
+
+import numpy as np
+
+# tensor ids inside one (config, layer) stream
+T_X, T_W, T_BIAS, T_LORA_A, T_LORA_B, T_PREACT = 0, 1, 2, 3, 4, 5
+
+
+@dataclasses.dataclass(frozen=True)
+class Layer:
+    """One linear layer Y = X @ W (+ b): X is M x K, W is K x N."""
+    M: int
+    K: int
+    N: int
+    rank: int
+    x_dtype: str = "f16"          # "f16" or "f32"
+    y_dtype: str = "f16"
+    x_outlier_frac: float = 0.01
+    x_outlier_scale: float = 20.0
+    w_outlier_frac: float = 0.01
+    w_outlier_scale: float = 10.0
+    lora_rank: int = 0            # extra rank concatenated onto the SVD factors
+    preact: bool = False          # X = GELU_tanh(Z) with Z drawn by ``preactivation``
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    index: int
+    name: str
+    layers: List[Layer]
+    note: str
+
+
+def _cfgs() -> List[Config]:
+    c0 = Config(0, "tiny", [Layer(256, 512, 512, 16, "f32", "f32")],
+                "X fp32 256x512, W 512x512, r=16, bias 0 (plus a seeded-bias variant)")
+    c1 = Config(1, "dit_qkv", [Layer(4608, 3072, 9216, 32)],
+                "DiT fused QKV projection: 4096 image + 512 text tokens, K=3072, N=9216, r=32")
+    c2 = Config(2, "dit_mlp", [
+        Layer(4608, 3072, 12288, 32),
+        Layer(4608, 12288, 3072, 32, x_outlier_frac=0.005, x_outlier_scale=15.0, preact=True),
+    ], "DiT MLP: up 3072->12288, GELU-tanh in fp16, down 12288->3072, r=32 on both")
+    # UNet-style mixed shapes; "batch 2" doubles the listed token count.
+    unet = [(16384, 320, 320), (4096, 640, 640), (4096, 640, 5120),
+            (1024, 1280, 1280), (1024, 1280, 10240)]
+    c3 = Config(3, "unet_mixed", [Layer(2 * m, k, n, 32) for (m, k, n) in unet],
+                "UNet-style linears, batch 2, r=32")
+    c4 = Config(4, "dit_lora_stack", [Layer(9216, 3072, 3072, 32, lora_rank=64) for _ in range(19)],
+                "19 sequential DiT linears K=N=3072, M=2x4608, SVD rank 32 + LoRA rank 64 -> r=96")
+    return [c0, c1, c2, c3, c4]
+
+
+CONFIGS: List[Config] = _cfgs()
+
+
+def _rng(cfg: int, layer: int, tensor: int) -> np.random.Generator:
+    return np.random.default_rng([int(cfg), int(layer), int(tensor)])
+
+
+def outlier_count(n: int, frac: float) -> int:
+    return max(1, int(np.rint(frac * n)))
+
+
+def activation(cfg: int, layer: int, M: int, K: int, dtype: str = "f16",
+               frac: float = 0.01, scale: float = 20.0, rows: slice | None = None) -> np.ndarray:
+    """X (M x K): N(0,1) with ``outlier_count(K, frac)`` channels times ``scale``.
+
+    ``rows`` returns a slice of the same matrix (the full matrix is drawn,
+    so a slice equals the corresponding rows of the whole)."""
+    g = _rng(cfg, layer, T_X)
+    x = g.standard_normal((M, K))
+    idx = g.choice(K, outlier_count(K, frac), replace=False)
+    x[:, idx] *= scale
+    if rows is not None:
+        x = x[rows]
+    return x.astype(np.float16 if dtype == "f16" else np.float32)
+
+
+def preactivation(cfg: int, layer: int, M: int, K: int, frac: float = 0.005,
+                  scale: float = 15.0) -> np.ndarray:
+    """Z (M x K) fp16: N(0,1) pre-activations with a few channels times ``scale``."""
+    g = _rng(cfg, layer, T_PREACT)
+    z = g.standard_normal((M, K))
+    idx = g.choice(K, outlier_count(K, frac), replace=False)
+    z[:, idx] *= scale
+    return z.astype(np.float16)
+
+
+def weight(cfg: int, layer: int, K: int, N: int, frac: float = 0.01,
+           scale: float = 10.0) -> np.ndarray:
+    """W (K x N) fp32: N(0, 0.02^2) with ``outlier_count(K, frac)`` input rows times ``scale``."""
+    g = _rng(cfg, layer, T_W)
+    w = g.standard_normal((K, N)) * 0.02
+    idx = g.choice(K, outlier_count(K, frac), replace=False)
+    w[idx, :] *= scale
+    return w.astype(np.float32)
+
+
+def bias(cfg: int, layer: int, N: int, std: float = 0.1) -> np.ndarray:
+    return (_rng(cfg, layer, T_BIAS).standard_normal(N) * std).astype(np.float32)
+
+
+def lora(cfg: int, layer: int, K: int, N: int, rl: int = 64, std: float = 0.01):
+    """(A, B): A is K x rl, B is rl x N, both N(0, std^2) rounded to fp16."""
+    a = (_rng(cfg, layer, T_LORA_A).standard_normal((K, rl)) * std).astype(np.float16)
+    b = (_rng(cfg, layer, T_LORA_B).standard_normal((rl, N)) * std).astype(np.float16)
+    return a, b
+
+
+def layer_inputs(cfg: int, layer_idx: int = 0):
+    """Convenience: (Layer, X or None, W) for one layer of a config.
+
+    For a layer whose input is a GELU output, X is None: the caller draws
+    ``preactivation`` and applies its own GELU."""
+    L = CONFIGS[cfg].layers[layer_idx]
+    W = weight(cfg, layer_idx, L.K, L.N, L.w_outlier_frac, L.w_outlier_scale)
+    if L.preact:
+        return L, None, W
+    X = activation(cfg, layer_idx, L.M, L.K, L.x_dtype, L.x_outlier_frac, L.x_outlier_scale)
+    return L, X, W
