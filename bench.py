@@ -1,0 +1,240 @@
+"""Benchmark of the SVDQuant W4A4 + low-rank linear layer on one MI355X.
+
+One step = the whole hot path on one batch: K1 (smoothing, 4-bit quantization
+and the low-rank down-projection of X) then K2 (the W4A4 GEMM with the fused
+up-projection and bias). The default workload is the DiT fused-QKV projection:
+X fp16 4608 x 3072 (4096 image + 512 text tokens), W 3072 x 9216, rank 32,
+groups of 64, Y fp16. Inputs are seeded synthetic data with outlier channels;
+weights are prepared on the host by the library before timing.
+
+Prints one JSON line. ``value`` is the effective throughput 2*M*N*K / t of the
+whole step (TOPS); ``roofline`` reports the dominant kernel (K2) against the
+dense INT8 matrix-core peak, timed with HIP events on the stream it runs on;
+``cpu_baseline`` times the CPU oracle on a bounded row sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+PROFILE_PMC = os.path.join(ROOT, "profiles", "k2_dit_qkv_pmc.json")
+K2_SOURCES = ["bit_post_quantized_smooth_amd/csrc/k2_w4a4_gemm.hip",
+              "bit_post_quantized_smooth_amd/csrc/device_common.hpp"]
+
+
+def k2_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in K2_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1, help="workload index (1 = DiT QKV)")
+    ap.add_argument("--layer", type=int, default=0)
+    ap.add_argument("--sets", type=int, default=4, help="rotating buffer sets (cold MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-overhead", action="store_true", help="skip the rank-0 comparison run")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain fp32 copy kernel of known size (for PMC scaling)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+class Sets:
+    """`n` independent device copies of one layer's inputs, weights and outputs."""
+
+    def __init__(self, torch, X, prep, bias, n, y_dtype):
+        import bit_post_quantized_smooth_amd as sq
+        self.sq = sq
+        M, K = X.shape
+        self.M, self.K, self.N, self.R = M, K, prep.N, prep.rank
+        G = K // 64
+        d = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16
+                                       else np.ascontiguousarray(a)).to("cuda")
+        self.sets = []
+        for _ in range(n):
+            s = dict(
+                X=d(X), inv=d(prep.inv_smooth),
+                L1t=d(prep.L1t) if self.R else None, L2t=d(prep.L2t) if self.R else None,
+                wc=d(prep.w_codes), ws=d(prep.w_scales), b=None if bias is None else d(bias),
+                ac=torch.empty((M, K // 2), dtype=torch.uint8, device="cuda"),
+                asc=torch.empty((M, G), dtype=torch.int16, device="cuda"),
+                D=torch.empty((M, max(self.R, 1)), dtype=torch.float32, device="cuda"),
+                Y=torch.empty((M, self.N), dtype=torch.float16 if y_dtype == "f16" else torch.float32,
+                              device="cuda"))
+            self.sets.append(s)
+
+    def k1(self, i):
+        s = self.sets[i % len(self.sets)]
+        self.sq.quantize_act_lowrank_down(s["X"], s["inv"], s["L1t"], self.R, s["ac"], s["asc"],
+                                          s["D"] if self.R else None)
+
+    def k2(self, i):
+        s = self.sets[i % len(self.sets)]
+        self.sq.w4a4_gemm_lowrank_up(s["ac"], s["asc"], s["wc"], s["ws"], s["D"] if self.R else None,
+                                     s["L2t"], self.R, s["b"], s["Y"], self.K)
+
+
+def time_steps(torch, sets, steps, warmup):
+    for i in range(warmup):
+        sets.k1(i)
+        sets.k2(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        e0, e1, e2 = ev[i]
+        e0.record()
+        sets.k1(i)
+        e1.record()
+        sets.k2(i)
+        e2.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    k1 = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e-3
+    k2 = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e-3
+    return (t1 - t0) / steps, k1, k2
+
+
+def cpu_baseline(X, W, prep, bias, budget_s):
+    """The oracle's online part (quantize X, down-projection, integer partials,
+    scaled sum, up-projection, bias) on chunks of rows until ~budget_s seconds."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    lam = O.smoothing_factors(O.channel_absmax(X), W)
+    inv = O.inv_smoothing(lam)
+    wc, ws = O.quantize_residual_from_factors(W, lam, prep.L1, prep.L2)
+    M, K = X.shape
+    N = W.shape[1]
+    chunk = 32
+    rows = 0
+    t0 = time.perf_counter()
+    while rows < M and time.perf_counter() - t0 < budget_s:
+        r = slice(rows, min(M, rows + chunk))
+        O.linear(X[r], inv, prep.L1, prep.L2, wc, ws, bias, "f16")
+        rows = r.stop
+    t = time.perf_counter() - t0
+    return dict(value=2.0 * rows * N * K / t / 1e12, unit="TOPS", cores=int(cores), kind="oracle",
+                sample=f"first {rows} of {M} rows of the same layer, online part only "
+                       f"({t:.1f} s, numpy fp64, chunks of {chunk} rows)")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is built and measured on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bit_post_quantized_smooth_amd as sq
+    import workloads as wl
+
+    cfg = wl.CONFIGS[args.config]
+    L = cfg.layers[args.layer]
+    Lx, X, W = wl.layer_inputs(args.config, args.layer)
+    if X is None:
+        import oracle as O   # input synthesis only: GELU of the seeded pre-activations
+        X = O.gelu_tanh(wl.preactivation(args.config, args.layer, L.M, L.K, L.x_outlier_frac,
+                                         L.x_outlier_scale))
+    bias = None
+    lam = sq.smoothing_factors(sq.channel_absmax(X), W)
+    prep = sq.prepare_weights(W, lam, L.rank)
+    if L.lora_rank:
+        A, B = wl.lora(args.config, args.layer, L.K, L.N, L.lora_rank)
+        prep = sq.concat_lora(prep, lam, A, B, 1.0)
+    M, K, N, R = L.M, L.K, L.N, prep.rank
+    sets = Sets(torch, X, prep, bias, args.sets, L.y_dtype)
+    t_step, k1, k2 = time_steps(torch, sets, args.steps, args.warmup)
+    ops = 2.0 * M * N * K
+    value = ops / t_step / 1e12
+    k2_avg = float(np.mean(k2))
+    k1_avg = float(np.mean(k1))
+    xb = 2 if L.x_dtype == "f16" else 4
+    yb = 2 if L.y_dtype == "f16" else 4
+    k1_bytes = M * K * xb + M * K // 2 + 2 * M * (K // 64) + 4 * M * R + 2 * K * R + 4 * K
+    k2_bytes = (M + N) * K // 2 + 2 * (M + N) * (K // 64) + 4 * M * R + 2 * R * N + M * N * yb
+
+    traffic = None
+    if os.path.exists(PROFILE_PMC):
+        try:
+            pm = json.load(open(PROFILE_PMC))
+            if pm.get("k2_source_hash") == k2_source_hash() and pm.get("config") == args.config:
+                traffic = pm.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    overhead = None
+    if not args.no_overhead and R > 0:
+        prep0 = sq.prepare_weights(W, lam, 0)
+        sets0 = Sets(torch, X, prep0, bias, args.sets, L.y_dtype)
+        t0_step, _, k2_0 = time_steps(torch, sets0, args.steps, args.warmup)
+        overhead = dict(step_ms_rank0=t0_step * 1e3, k2_ms_rank0=float(np.mean(k2_0)) * 1e3,
+                        frac=(t_step - t0_step) / float(np.mean(k2_0)))
+        del sets0
+
+    if args.copy_probe:
+        n = 64 << 20                      # 64 Mi fp32 = 256 MiB read + 256 MiB written
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+
+    out = {
+        "metric": "effective TOPS of SVDQuant W4A4+rank-32 linear, % of INT8 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} layer {args.layer}: X {L.x_dtype} {M}x{K}, "
+                               f"W {K}x{N}, rank {R}, INT4 per-64 groups, Y {L.y_dtype}",
+                   "M": M, "K": K, "N": N, "rank": R, "group": 64, "buffer_sets": args.sets},
+        "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": "k2_w4a4_kernel",
+                     "achieved": round(ops / k2_avg / 1e12, 2), "peak": INT8_PEAK_TOPS,
+                     "unit": "TOPS", "frac": round(ops / k2_avg / 1e12 / INT8_PEAK_TOPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": k2_bytes,
+                     "avg_ms": round(k2_avg * 1e3, 4)},
+        "k1": {"kernel": "k1_quant_down_kernel", "avg_ms": round(k1_avg * 1e3, 4),
+               "algorithmic_bytes": k1_bytes, "achieved_gbs": round(k1_bytes / k1_avg / 1e9, 1),
+               "peak_gbs": HBM_PEAK_GBS, "frac": round(k1_bytes / k1_avg / 1e9 / HBM_PEAK_GBS, 4)},
+        "lowrank_overhead": None if overhead is None else {
+            k: round(v, 4) for k, v in overhead.items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(X, W, prep, bias, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,14 @@
+"""SVDQuant W4A4 + low-rank linear layer for AMD Instinct MI355X (gfx950).
+
+The compute lives in libsvdq.so (hand-written HIP kernels behind the C ABI in
+include/svdq.h); this package is its thin Python binding. Importing it
+without a built library raises ImportError.
+"""
+from . import _lib  # noqa: F401  (fails loudly when libsvdq.so is missing)
+from .api import (Linear, Prepared, channel_absmax, concat_lora, debug_group_partials,  # noqa: F401
+                  gelu_tanh_f16, linear, linear_workspace_bytes, prepare_weights,
+                  quantize_act_lowrank_down, smoothing_factors, w4a4_gemm_lowrank_up)
+
+__all__ = ["Linear", "Prepared", "channel_absmax", "concat_lora", "debug_group_partials",
+           "gelu_tanh_f16", "linear", "linear_workspace_bytes", "prepare_weights",
+           "quantize_act_lowrank_down", "smoothing_factors", "w4a4_gemm_lowrank_up"]

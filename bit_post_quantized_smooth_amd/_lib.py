@@ -1,0 +1,88 @@
+"""ctypes binding of libsvdq.so (the C ABI in include/svdq.h).
+
+Argument marshalling only: every computation happens in the library. If the
+library has not been built this module raises ImportError; there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsvdq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m bit_post_quantized_smooth_amd.build` "
+        "(hipcc for gfx950). There is no CPU fallback.")
+
+# PyTorch-ROCm ships its own HIP runtime with the same soname as the system
+# one. Whichever is loaded first serves the whole process, so torch (when
+# present) is imported first: its allocations, its streams and our launches
+# must all go through the runtime torch was built against.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    torch = None
+
+lib = C.CDLL(LIB_PATH)
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_RANK, ERR_WORKSPACE, ERR_HIP, \
+    ERR_NO_DEVICE, ERR_INTERNAL, ERR_GROUP = range(11)
+F16, F32 = 1, 2
+GROUP = 64
+MAX_RANK = 256
+
+_p = C.c_void_p
+_i64 = C.c_int64
+_i32 = C.c_int32
+_int = C.c_int
+
+_SIGS = {
+    "svdq_abi_version": (_int, []),
+    "svdq_status_str": (C.c_char_p, [_int]),
+    "svdq_last_error": (C.c_char_p, []),
+    "svdq_channel_absmax": (_int, [_p, _int, _i64, _i64, _i64, _p]),
+    "svdq_smoothing_factors": (_int, [_p, _p, _i64, _i64, _p]),
+    "svdq_prepare_weights": (_int, [_p, _p, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p]),
+    "svdq_concat_lora": (_int, [_p, _p, _i64, _i64, _i32, _p, _p, _p, _i32, C.c_float, _p, _p]),
+    "svdq_quantize_act_lowrank_down": (_int, [_p, _int, _i64, _i64, _i64, _p, _p, _i32, _i32,
+                                              _p, _p, _p, _p]),
+    "svdq_w4a4_gemm_lowrank_up": (_int, [_p, _p, _p, _p, _p, _p, _i32, _p, _p, _int, _i64, _i64,
+                                         _i64, _i64, _i32, _p]),
+    "svdq_linear_workspace_bytes": (C.c_size_t, [_i64, _i64, _i32, _i32]),
+    "svdq_linear": (_int, [_p, _int, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _int, _i64, _i64,
+                           _i64, _i64, _i32, _p, C.c_size_t, _p]),
+    "svdq_debug_group_partials": (_int, [_p, _p, _i64, _i64, _i64, _i32, _i64, _i64, _p, _p]),
+    "svdq_gelu_tanh_f16": (_int, [_p, _p, _i64, _p]),
+}
+
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class SvdqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.svdq_last_error().decode() or lib.svdq_status_str(status).decode()
+        super().__init__(f"{where}: status {status} ({lib.svdq_status_str(status).decode()}): {msg}")
+
+
+def check(status: int, where: str) -> None:
+    if status != OK:
+        raise SvdqError(status, where)
+
+
+def status_str(status: int) -> str:
+    return lib.svdq_status_str(status).decode()
+
+
+def last_error() -> str:
+    return lib.svdq_last_error().decode()
+
+
+def abi_version() -> int:
+    return lib.svdq_abi_version()

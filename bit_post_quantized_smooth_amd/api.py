@@ -1,0 +1,211 @@
+"""Python front end of libsvdq: the same entry points as include/svdq.h.
+
+Host prep functions take and return numpy arrays. Device functions take
+torch tensors on a ROCm device and enqueue work on torch's current stream
+(or the stream passed in); PyTorch only provides the memory and the stream.
+All checks and all arithmetic are done by the library.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+from . import _lib
+from ._lib import F16, F32, GROUP, check, lib
+
+# --------------------------------------------------------------------------
+# host prep (numpy)
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def channel_absmax(X: np.ndarray) -> np.ndarray:
+    X = np.ascontiguousarray(X)
+    dt = F16 if X.dtype == np.float16 else F32
+    if dt == F32:
+        X = _c(X, np.float32)
+    M, K = X.shape
+    out = np.empty(K, dtype=np.float32)
+    check(lib.svdq_channel_absmax(_np_ptr(X), dt, M, K, K, _np_ptr(out)), "svdq_channel_absmax")
+    return out
+
+
+def smoothing_factors(x_absmax: np.ndarray, W: np.ndarray) -> np.ndarray:
+    xa = _c(x_absmax, np.float32)
+    W = _c(W, np.float32)
+    K, N = W.shape
+    lam = np.empty(K, dtype=np.float32)
+    check(lib.svdq_smoothing_factors(_np_ptr(xa), _np_ptr(W), K, N, _np_ptr(lam)),
+          "svdq_smoothing_factors")
+    return lam
+
+
+@dataclasses.dataclass
+class Prepared:
+    """Offline products for one layer, host side. L1t is R x K, L2t is N x R (fp16 bits)."""
+    K: int
+    N: int
+    rank: int
+    inv_smooth: np.ndarray
+    L1t: np.ndarray
+    L2t: np.ndarray
+    w_codes: np.ndarray
+    w_scales: np.ndarray
+    sigma: Optional[np.ndarray] = None
+
+    @property
+    def L1(self) -> np.ndarray:
+        """K x R fp16 view of the factor (a copy)."""
+        return np.ascontiguousarray(self.L1t.view(np.float16).T)
+
+    @property
+    def L2(self) -> np.ndarray:
+        """R x N fp16 (a copy)."""
+        return np.ascontiguousarray(self.L2t.view(np.float16).T)
+
+
+def prepare_weights(W: np.ndarray, lam: np.ndarray, rank: int, want_sigma: bool = False) -> Prepared:
+    W = _c(W, np.float32)
+    lam = _c(lam, np.float32)
+    K, N = W.shape
+    inv = np.empty(K, dtype=np.float32)
+    L1t = np.empty((rank, K), dtype=np.uint16)
+    L2t = np.empty((N, rank), dtype=np.uint16)
+    wc = np.empty((N, K // 2), dtype=np.uint8)
+    ws = np.empty((N, K // GROUP), dtype=np.uint16)
+    sig = np.empty(min(K, N), dtype=np.float64) if want_sigma else None
+    check(lib.svdq_prepare_weights(_np_ptr(W), _np_ptr(lam), K, N, rank, GROUP, _np_ptr(inv),
+                                   _np_ptr(L1t) if rank else None, _np_ptr(L2t) if rank else None,
+                                   _np_ptr(wc), _np_ptr(ws), _np_ptr(sig)),
+          "svdq_prepare_weights")
+    return Prepared(K, N, rank, inv, L1t, L2t, wc, ws, sig)
+
+
+def concat_lora(prep: Prepared, lam: np.ndarray, A: np.ndarray, B: np.ndarray,
+                scale: float = 1.0) -> Prepared:
+    A = _c(A, np.float16).view(np.uint16)
+    B = _c(B, np.float16).view(np.uint16)
+    lam = _c(lam, np.float32)
+    K, N, r = prep.K, prep.N, prep.rank
+    rl = A.shape[1]
+    L1o = np.empty((r + rl, K), dtype=np.uint16)
+    L2o = np.empty((N, r + rl), dtype=np.uint16)
+    check(lib.svdq_concat_lora(_np_ptr(prep.L1t) if r else None, _np_ptr(prep.L2t) if r else None,
+                               K, N, r, _np_ptr(lam), _np_ptr(A), _np_ptr(B), rl, float(scale),
+                               _np_ptr(L1o), _np_ptr(L2o)), "svdq_concat_lora")
+    return dataclasses.replace(prep, rank=r + rl, L1t=L1o, L2t=L2o)
+
+
+# --------------------------------------------------------------------------
+# device entry points (torch tensors)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _tp(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def quantize_act_lowrank_down(X, inv_smooth, L1t, R: int, a_codes, a_scales, D, stream=None):
+    M, K = X.shape
+    check(lib.svdq_quantize_act_lowrank_down(_tp(X), _dt(X), M, K, X.stride(0), _tp(inv_smooth),
+                                             _tp(L1t) if R else None, R, GROUP, _tp(a_codes),
+                                             _tp(a_scales), _tp(D) if R else None, _stream(stream)),
+          "svdq_quantize_act_lowrank_down")
+
+
+def w4a4_gemm_lowrank_up(a_codes, a_scales, w_codes, w_scales, D, L2t, R: int, bias, Y, K: int,
+                         stream=None):
+    M, N = Y.shape
+    check(lib.svdq_w4a4_gemm_lowrank_up(_tp(a_codes), _tp(a_scales), _tp(w_codes), _tp(w_scales),
+                                        _tp(D) if R else None, _tp(L2t) if R else None, R, _tp(bias),
+                                        _tp(Y), _dt(Y), M, N, K, Y.stride(0), GROUP,
+                                        _stream(stream)), "svdq_w4a4_gemm_lowrank_up")
+
+
+def linear_workspace_bytes(M: int, K: int, R: int) -> int:
+    return int(lib.svdq_linear_workspace_bytes(M, K, R, GROUP))
+
+
+def linear(X, inv_smooth, L1t, L2t, R: int, w_codes, w_scales, bias, Y, ws, stream=None):
+    M, K = X.shape
+    N = Y.shape[1]
+    check(lib.svdq_linear(_tp(X), _dt(X), X.stride(0), _tp(inv_smooth), _tp(L1t) if R else None,
+                          _tp(L2t) if R else None, R, _tp(w_codes), _tp(w_scales), _tp(bias), _tp(Y),
+                          _dt(Y), Y.stride(0), M, K, N, GROUP, _tp(ws), ws.numel() * ws.element_size(),
+                          _stream(stream)), "svdq_linear")
+
+
+def debug_group_partials(a_codes, w_codes, M: int, N: int, K: int, row0: int, rows: int, P,
+                         stream=None):
+    check(lib.svdq_debug_group_partials(_tp(a_codes), _tp(w_codes), M, N, K, GROUP, row0, rows,
+                                        _tp(P), _stream(stream)), "svdq_debug_group_partials")
+
+
+def gelu_tanh_f16(x, y, stream=None):
+    check(lib.svdq_gelu_tanh_f16(_tp(x), _tp(y), x.numel(), _stream(stream)), "svdq_gelu_tanh_f16")
+
+
+class Linear:
+    """One prepared SVDQuant layer resident on a device.
+
+    ``Linear(prep, bias)(X)`` runs K1 then K2 on the current stream and
+    returns Y (M x N, ``out_dtype``). The workspace is kept between calls and
+    grown when a larger M arrives."""
+
+    def __init__(self, prep: Prepared, bias: Optional[np.ndarray] = None, device="cuda",
+                 out_dtype=None):
+        torch = _torch()
+        self.K, self.N, self.R = prep.K, prep.N, prep.rank
+        dev = torch.device(device)
+        self.inv_smooth = torch.from_numpy(prep.inv_smooth).to(dev)
+        self.L1t = torch.from_numpy(prep.L1t.view(np.int16)).to(dev)
+        self.L2t = torch.from_numpy(prep.L2t.view(np.int16)).to(dev)
+        self.w_codes = torch.from_numpy(prep.w_codes).to(dev)
+        self.w_scales = torch.from_numpy(prep.w_scales.view(np.int16)).to(dev)
+        self.bias = None if bias is None else torch.from_numpy(_c(bias, np.float32)).to(dev)
+        self.out_dtype = out_dtype
+        self.device = dev
+        self.ws = None
+
+    def workspace(self, M: int):
+        torch = _torch()
+        need = linear_workspace_bytes(M, self.K, self.R)
+        if self.ws is None or self.ws.numel() < need:
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self.ws
+
+    def __call__(self, X, Y=None, stream=None):
+        torch = _torch()
+        M = X.shape[0]
+        if Y is None:
+            Y = torch.empty((M, self.N), dtype=self.out_dtype or X.dtype, device=self.device)
+        linear(X, self.inv_smooth, self.L1t, self.L2t, self.R, self.w_codes, self.w_scales,
+               self.bias, Y, self.workspace(M), stream)
+        return Y

@@ -1,0 +1,249 @@
+// C ABI of the device entry points: argument checks, workspace carving and
+// kernel launches. Every check runs on the host before anything is enqueued;
+// on an error nothing is launched or written.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/svdq.h"
+#include "device_launch.hpp"
+#include "host_internal.hpp"
+
+using namespace svdq;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int device_ready() {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    set_error("no usable GPU: %s", hipGetErrorString(e));
+    return SVDQ_ERR_NO_DEVICE;
+  }
+  return SVDQ_OK;
+}
+
+int check_hip(hipError_t e, const char* what) {
+  if (e != hipSuccess) {
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return SVDQ_ERR_HIP;
+  }
+  return SVDQ_OK;
+}
+
+int esize(int dtype) { return dtype == SVDQ_F16 ? 2 : 4; }
+
+bool known_dtype(int d) { return d == SVDQ_F16 || d == SVDQ_F32; }
+
+int check_common(int64_t M, int64_t K, int32_t R, int32_t group, const char* fn) {
+  if (group != SVDQ_GROUP || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) {
+    set_error("%s: group=%d K=%lld (need group 64 and K a positive multiple of 64)", fn, group,
+              (long long)K);
+    return SVDQ_ERR_GROUP;
+  }
+  if (M < 1 || M > (int64_t(1) << 31) * 16 - 16) {
+    set_error("%s: M=%lld out of range", fn, (long long)M);
+    return SVDQ_ERR_SHAPE;
+  }
+  if (R < 0 || R > SVDQ_MAX_RANK || R % 16 != 0) {
+    set_error("%s: R=%d (need 0 <= R <= %d, R %% 16 == 0)", fn, R, SVDQ_MAX_RANK);
+    return SVDQ_ERR_RANK;
+  }
+  return SVDQ_OK;
+}
+
+int validate_k1(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                const float* inv_smooth, const uint16_t* L1t, int32_t R, int32_t group,
+                const uint8_t* a_codes, const uint16_t* a_scales, const float* D) {
+  const char* fn = "svdq_quantize_act_lowrank_down";
+  if (!X || !inv_smooth || !a_codes || !a_scales || (R > 0 && (!L1t || !D))) {
+    set_error("%s: null pointer", fn);
+    return SVDQ_ERR_NULL;
+  }
+  if (!known_dtype(x_dtype)) {
+    set_error("%s: x_dtype %d", fn, x_dtype);
+    return SVDQ_ERR_DTYPE;
+  }
+  if (int s = check_common(M, K, R, group, fn)) return s;
+  if (ldx < K) {
+    set_error("%s: ldx=%lld < K=%lld", fn, (long long)ldx, (long long)K);
+    return SVDQ_ERR_SHAPE;
+  }
+  if (!aligned16(X) || !aligned16(inv_smooth) || !aligned16(a_codes) || !aligned16(a_scales) ||
+      (R > 0 && (!aligned16(L1t) || !aligned16(D))) || (ldx * esize(x_dtype)) % 16 != 0) {
+    set_error("%s: device pointers and the X row stride must be 16-byte aligned", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  return SVDQ_OK;
+}
+
+int validate_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* w_codes,
+                const uint16_t* w_scales, const float* D, const uint16_t* L2t, int32_t R,
+                const float* bias, const void* Y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                int64_t ldy, int32_t group, const char* fn) {
+  if (!a_codes || !a_scales || !w_codes || !w_scales || !Y || (R > 0 && (!D || !L2t))) {
+    set_error("%s: null pointer", fn);
+    return SVDQ_ERR_NULL;
+  }
+  if (!known_dtype(y_dtype)) {
+    set_error("%s: y_dtype %d", fn, y_dtype);
+    return SVDQ_ERR_DTYPE;
+  }
+  if (int s = check_common(M, K, R, group, fn)) return s;
+  if (N < 1 || ldy < N || ((M + 127) / 128) * ((N + 127) / 128) > 0x7FFFFFFF) {
+    set_error("%s: N=%lld ldy=%lld", fn, (long long)N, (long long)ldy);
+    return SVDQ_ERR_SHAPE;
+  }
+  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      (R > 0 && (!aligned16(D) || !aligned16(L2t)))) {
+    set_error("%s: codes, scales, D and L2t must be 16-byte aligned", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  if ((reinterpret_cast<uintptr_t>(Y) % esize(y_dtype)) != 0 ||
+      (bias && (reinterpret_cast<uintptr_t>(bias) & 3u) != 0)) {
+    set_error("%s: Y and bias must be aligned to their element size", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  return SVDQ_OK;
+}
+
+struct WsLayout {
+  size_t codes, scales, d, total;
+};
+
+WsLayout ws_layout(int64_t M, int64_t K, int32_t R) {
+  WsLayout w;
+  w.codes = 0;
+  w.scales = round_up(static_cast<size_t>(M) * (K / 2), 256);
+  w.d = w.scales + round_up(static_cast<size_t>(M) * (K / SVDQ_GROUP) * 2, 256);
+  w.total = w.d + round_up(static_cast<size_t>(M) * R * 4, 256);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int svdq_quantize_act_lowrank_down(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                   const float* inv_smooth, const uint16_t* L1t, int32_t R,
+                                   int32_t group, uint8_t* a_codes, uint16_t* a_scales, float* D,
+                                   hipStream_t stream) {
+  clear_error();
+  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1t, R, group, a_codes, a_scales, D))
+    return s;
+  if (int s = device_ready()) return s;
+  return check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1t, R, a_codes,
+                             a_scales, D, stream),
+                   "svdq_quantize_act_lowrank_down launch");
+}
+
+int svdq_w4a4_gemm_lowrank_up(const uint8_t* a_codes, const uint16_t* a_scales,
+                              const uint8_t* w_codes, const uint16_t* w_scales, const float* D,
+                              const uint16_t* L2t, int32_t R, const float* bias, void* Y,
+                              int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
+                              int32_t group, hipStream_t stream) {
+  clear_error();
+  if (int s = validate_k2(a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y, y_dtype, M, N,
+                          K, ldy, group, "svdq_w4a4_gemm_lowrank_up"))
+    return s;
+  if (int s = device_ready()) return s;
+  return check_hip(launch_k2(a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y,
+                             y_dtype == SVDQ_F16, M, N, K, ldy, stream),
+                   "svdq_w4a4_gemm_lowrank_up launch");
+}
+
+size_t svdq_linear_workspace_bytes(int64_t M, int64_t K, int32_t R, int32_t group) {
+  if (M < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0 || group != SVDQ_GROUP || R < 0) return 0;
+  return ws_layout(M, K, R).total;
+}
+
+int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
+                const uint16_t* L1t, const uint16_t* L2t, int32_t R, const uint8_t* w_codes,
+                const uint16_t* w_scales, const float* bias, void* Y, int y_dtype, int64_t ldy,
+                int64_t M, int64_t K, int64_t N, int32_t group, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  clear_error();
+  const char* fn = "svdq_linear";
+  if (!ws) {
+    set_error("%s: null workspace", fn);
+    return SVDQ_ERR_NULL;
+  }
+  if (int s = check_common(M, K, R, group, fn)) return s;
+  const WsLayout L = ws_layout(M, K, R);
+  if (ws_bytes < L.total) {
+    set_error("%s: workspace %zu bytes < %zu needed", fn, ws_bytes, L.total);
+    return SVDQ_ERR_WORKSPACE;
+  }
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) {
+    set_error("%s: workspace must be 256-byte aligned", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* a_codes = base + L.codes;
+  uint16_t* a_scales = reinterpret_cast<uint16_t*>(base + L.scales);
+  float* D = R > 0 ? reinterpret_cast<float*>(base + L.d) : nullptr;
+  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1t, R, group, a_codes, a_scales, D))
+    return s;
+  if (int s = validate_k2(a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y, y_dtype, M, N,
+                          K, ldy, group, fn))
+    return s;
+  if (int s = device_ready()) return s;
+  if (int s = check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1t, R, a_codes,
+                                  a_scales, D, stream),
+                        "svdq_linear K1 launch"))
+    return s;
+  return check_hip(launch_k2(a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y,
+                             y_dtype == SVDQ_F16, M, N, K, ldy, stream),
+                   "svdq_linear K2 launch");
+}
+
+int svdq_debug_group_partials(const uint8_t* a_codes, const uint8_t* w_codes, int64_t M, int64_t N,
+                              int64_t K, int32_t group, int64_t row0, int64_t rows, int32_t* P,
+                              hipStream_t stream) {
+  clear_error();
+  const char* fn = "svdq_debug_group_partials";
+  if (!a_codes || !w_codes || !P) {
+    set_error("%s: null pointer", fn);
+    return SVDQ_ERR_NULL;
+  }
+  if (int s = check_common(M, K, 0, group, fn)) return s;
+  if (N < 1 || row0 < 0 || rows < 1 || row0 + rows > M || (rows + 15) / 16 > 0x7FFFFFFF ||
+      (N + 15) / 16 > 65535) {
+    set_error("%s: N=%lld row0=%lld rows=%lld M=%lld", fn, (long long)N, (long long)row0,
+              (long long)rows, (long long)M);
+    return SVDQ_ERR_SHAPE;
+  }
+  if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned16(P)) {
+    set_error("%s: device pointers must be 16-byte aligned", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  if (int s = device_ready()) return s;
+  return check_hip(launch_debug_partials(a_codes, w_codes, M, N, K, row0, rows, P, stream),
+                   "svdq_debug_group_partials launch");
+}
+
+int svdq_gelu_tanh_f16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream) {
+  clear_error();
+  if (!x || !y) {
+    set_error("svdq_gelu_tanh_f16: null pointer");
+    return SVDQ_ERR_NULL;
+  }
+  if (n < 0) {
+    set_error("svdq_gelu_tanh_f16: n=%lld", (long long)n);
+    return SVDQ_ERR_SHAPE;
+  }
+  if (!aligned16(x) || !aligned16(y)) {
+    set_error("svdq_gelu_tanh_f16: pointers must be 16-byte aligned");
+    return SVDQ_ERR_ALIGN;
+  }
+  if (n == 0) return SVDQ_OK;
+  if (int s = device_ready()) return s;
+  return check_hip(launch_gelu_f16(x, y, n, stream), "svdq_gelu_tanh_f16 launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,25 @@
+// Host-side launchers of the gfx950 kernels (called by the C ABI layer after
+// it has validated every argument).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace svdq {
+
+hipError_t launch_k1(const void* X, bool x_f16, int64_t M, int64_t K, int64_t ldx,
+                     const float* inv_smooth, const uint16_t* L1t, int R, uint8_t* a_codes,
+                     uint16_t* a_scales, float* D, hipStream_t stream);
+
+hipError_t launch_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* w_codes,
+                     const uint16_t* w_scales, const float* D, const uint16_t* L2t, int R,
+                     const float* bias, void* Y, bool y_f16, int64_t M, int64_t N, int64_t K,
+                     int64_t ldy, hipStream_t stream);
+
+hipError_t launch_debug_partials(const uint8_t* a_codes, const uint8_t* w_codes, int64_t M,
+                                 int64_t N, int64_t K, int64_t row0, int64_t rows, int32_t* P,
+                                 hipStream_t stream);
+
+hipError_t launch_gelu_f16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream);
+
+}  // namespace svdq

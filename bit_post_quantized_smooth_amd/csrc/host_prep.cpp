@@ -1,0 +1,366 @@
+// Host-side offline preparation of an SVDQuant linear layer.
+//
+// chattools.cn overview, section "SVDQuant的技术原理" (technical principles):
+// outliers are moved from the activations onto the weights by smoothing, the
+// smoothed weight is split by SVD into a 16-bit low-rank branch and a residual,
+// and the residual is quantized to 4 bits; the Eckart-Young-Mirsky item there
+// is why the dominant singular values go to the branch. Section
+// "SVDQuant的主要功能" (main features) adds LoRA integration without
+// re-quantization. The SVDQuant abstract (ai-digest.ru) states the same steps.
+//
+// Built without floating-point contraction: the quantizer's fp32 divide and
+// multiply must round exactly as the reading in svdq.h states.
+#include <omp.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <exception>
+#include <new>
+#include <vector>
+
+#include "../../include/svdq.h"
+#include "host_f16.hpp"
+#include "host_internal.hpp"
+
+namespace svdq {
+
+namespace {
+thread_local char g_last_error[512] = "";
+}
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+const char* last_error() { return g_last_error; }
+
+// The 4-bit group quantizer on fp32 values (the reading in svdq.h):
+// a = max|v|; s = fp16(min(a/7, 65504)); inv = s ? 1/s : 0;
+// q = clamp(rint(v*inv), -7, 7). Writes `n/2` packed bytes and one scale.
+static void quantize_group_f32(const float* v, int n, uint8_t* codes, uint16_t* scale) {
+  float a = 0.0f;
+  for (int i = 0; i < n; ++i) a = std::max(a, std::fabs(v[i]));
+  volatile float s32 = a / 7.0f;                 // correctly rounded fp32 division
+  float sc = std::min(static_cast<float>(s32), 65504.0f);
+  const uint16_t s16 = f32_to_f16(sc);
+  const float sf = f16_to_f32(s16);
+  const float inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
+  for (int i = 0; i < n; i += 2) {
+    int q[2];
+    for (int t = 0; t < 2; ++t) {
+      volatile float prod = v[i + t] * inv;        // fp32 multiply, no contraction
+      float r = std::nearbyint(static_cast<float>(prod));   // ties to even
+      r = std::min(7.0f, std::max(-7.0f, r));
+      q[t] = static_cast<int>(r);
+    }
+    codes[i / 2] = static_cast<uint8_t>((q[0] & 0xF) | ((q[1] & 0xF) << 4));
+  }
+  *scale = s16;
+}
+
+}  // namespace svdq
+
+using namespace svdq;
+
+#define SVDQ_TRY try {
+#define SVDQ_CATCH                                               \
+  }                                                              \
+  catch (const std::bad_alloc&) {                                \
+    set_error("host allocation failed");                         \
+    return SVDQ_ERR_INTERNAL;                                    \
+  }                                                              \
+  catch (const std::exception& ex) {                             \
+    set_error("internal error: %s", ex.what());                  \
+    return SVDQ_ERR_INTERNAL;                                    \
+  }                                                              \
+  catch (...) {                                                  \
+    set_error("internal error");                                 \
+    return SVDQ_ERR_INTERNAL;                                    \
+  }
+
+extern "C" {
+
+int svdq_channel_absmax(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                        float* out) {
+  clear_error();
+  if (!X || !out) {
+    set_error("svdq_channel_absmax: null pointer");
+    return SVDQ_ERR_NULL;
+  }
+  if (x_dtype != SVDQ_F16 && x_dtype != SVDQ_F32) {
+    set_error("svdq_channel_absmax: x_dtype %d", x_dtype);
+    return SVDQ_ERR_DTYPE;
+  }
+  if (M < 1 || K < 1 || ldx < K) {
+    set_error("svdq_channel_absmax: bad shape M=%lld K=%lld ldx=%lld", (long long)M,
+              (long long)K, (long long)ldx);
+    return SVDQ_ERR_SHAPE;
+  }
+  SVDQ_TRY
+  const int nt = omp_get_max_threads();
+  std::vector<float> part(static_cast<size_t>(nt) * K, 0.0f);
+#pragma omp parallel
+  {
+    float* mine = &part[static_cast<size_t>(omp_get_thread_num()) * K];
+#pragma omp for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+      if (x_dtype == SVDQ_F32) {
+        const float* row = static_cast<const float*>(X) + m * ldx;
+        for (int64_t k = 0; k < K; ++k) mine[k] = std::max(mine[k], std::fabs(row[k]));
+      } else {
+        const uint16_t* row = static_cast<const uint16_t*>(X) + m * ldx;
+        for (int64_t k = 0; k < K; ++k) mine[k] = std::max(mine[k], std::fabs(f16_to_f32(row[k])));
+      }
+    }
+  }
+  for (int64_t k = 0; k < K; ++k) {
+    float a = 0.0f;
+    for (int t = 0; t < nt; ++t) a = std::max(a, part[static_cast<size_t>(t) * K + k]);
+    out[k] = a;
+  }
+  return SVDQ_OK;
+  SVDQ_CATCH
+}
+
+int svdq_smoothing_factors(const float* x_absmax, const float* W, int64_t K, int64_t N,
+                           float* lambda) {
+  clear_error();
+  if (!x_absmax || !W || !lambda) {
+    set_error("svdq_smoothing_factors: null pointer");
+    return SVDQ_ERR_NULL;
+  }
+  if (K < 1 || N < 1) {
+    set_error("svdq_smoothing_factors: bad shape K=%lld N=%lld", (long long)K, (long long)N);
+    return SVDQ_ERR_SHAPE;
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < K; ++j) {
+    double wa = 0.0;
+    const float* row = W + j * N;
+    for (int64_t n = 0; n < N; ++n) wa = std::max(wa, std::fabs(static_cast<double>(row[n])));
+    const double xa = std::fabs(static_cast<double>(x_absmax[j]));
+    double lam = 1.0;
+    if (xa > 0.0 && wa > 0.0) lam = std::sqrt(xa / wa);
+    lambda[j] = static_cast<float>(lam);
+  }
+  return SVDQ_OK;
+}
+
+int svdq_prepare_weights(const float* W, const float* lambda, int64_t K, int64_t N, int32_t rank,
+                         int32_t group, float* inv_smooth, uint16_t* L1t, uint16_t* L2t,
+                         uint8_t* w_codes, uint16_t* w_scales, double* sigma) {
+  clear_error();
+  if (!W || !lambda || !inv_smooth || !w_codes || !w_scales || (rank > 0 && (!L1t || !L2t))) {
+    set_error("svdq_prepare_weights: null pointer");
+    return SVDQ_ERR_NULL;
+  }
+  if (group != SVDQ_GROUP || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) {
+    set_error("svdq_prepare_weights: group=%d K=%lld (need group 64 and K %% 64 == 0)", group,
+              (long long)K);
+    return SVDQ_ERR_GROUP;
+  }
+  if (N < 1) {
+    set_error("svdq_prepare_weights: N=%lld", (long long)N);
+    return SVDQ_ERR_SHAPE;
+  }
+  const int64_t nmin = std::min(K, N);
+  if (rank < 0 || rank > nmin) {
+    set_error("svdq_prepare_weights: rank %d outside [0, min(K,N)=%lld]", rank, (long long)nmin);
+    return SVDQ_ERR_RANK;
+  }
+  SVDQ_TRY
+  // inv_smooth = 1/lambda in fp32; What = diag(lambda) W in fp64 (exact)
+  for (int64_t k = 0; k < K; ++k) {
+    volatile float inv = 1.0f / lambda[k];
+    inv_smooth[k] = inv;
+  }
+  std::vector<double> What(static_cast<size_t>(K) * N);
+#pragma omp parallel for schedule(static)
+  for (int64_t k = 0; k < K; ++k) {
+    const double l = static_cast<double>(lambda[k]);
+    for (int64_t n = 0; n < N; ++n) What[k * N + n] = l * static_cast<double>(W[k * N + n]);
+  }
+
+  const bool need_svd = rank > 0 || sigma != nullptr;
+  std::vector<double> L1(static_cast<size_t>(K) * rank, 0.0);   // fp16 values, K x r
+  std::vector<double> L2(static_cast<size_t>(rank) * N, 0.0);   // fp16 values, r x N
+  if (need_svd) {
+    // Gram matrix of the shorter side, laid out so its rows are contiguous
+    const bool rows_short = K <= N;     // B = What (K x N)  or  B = What^T (N x K)
+    const int64_t n = nmin, m = rows_short ? N : K;
+    std::vector<double> B;
+    const double* Bp = What.data();
+    if (!rows_short) {
+      B.resize(static_cast<size_t>(N) * K);
+#pragma omp parallel for schedule(static)
+      for (int64_t i = 0; i < N; ++i)
+        for (int64_t k = 0; k < K; ++k) B[i * K + k] = What[k * N + i];
+      Bp = B.data();
+    }
+    std::vector<double> G(static_cast<size_t>(n) * n);
+    gram_rows(Bp, n, m, G.data());
+    std::vector<double> ev, Z, all;
+    const int r = rank;
+    if (!sym_top_eigen(G, n, r, ev, Z, sigma ? &all : nullptr)) {
+      set_error("svdq_prepare_weights: eigen-solver did not converge");
+      return SVDQ_ERR_INTERNAL;
+    }
+    if (sigma)
+      for (int64_t i = 0; i < n; ++i) sigma[i] = std::sqrt(std::max(0.0, all[i]));
+    // Z (n x r): eigenvectors of B B^T = left singular vectors of B.
+    // The other side is B^T z / s.  For rows_short, B = What: u = z, v = What^T u / s.
+    // Otherwise B = What^T: v = z, u = What v / s.
+    std::vector<double> s(r), u(static_cast<size_t>(K) * r), v(static_cast<size_t>(N) * r);
+    for (int j = 0; j < r; ++j) s[j] = std::sqrt(std::max(0.0, ev[j]));
+    std::vector<double>& zside = rows_short ? u : v;    // length n per column
+    std::vector<double>& oside = rows_short ? v : u;    // length m per column
+    for (int64_t i = 0; i < n; ++i)
+      for (int j = 0; j < r; ++j) zside[i * r + j] = Z[i * r + j];
+    // oside[:, j] = B^T z_j / s_j, B rows contiguous: accumulate row by row
+    std::fill(oside.begin(), oside.end(), 0.0);
+#pragma omp parallel
+    {
+      std::vector<double> acc(static_cast<size_t>(r));
+#pragma omp for schedule(static)
+      for (int64_t c = 0; c < m; ++c) {
+        std::fill(acc.begin(), acc.end(), 0.0);
+        for (int64_t i = 0; i < n; ++i) {
+          const double b = Bp[i * m + c];
+          const double* zr = Z.data() + i * r;
+          for (int j = 0; j < r; ++j) acc[j] += b * zr[j];
+        }
+        for (int j = 0; j < r; ++j) oside[c * r + j] = s[j] > 1e-300 ? acc[j] / s[j] : 0.0;
+      }
+    }
+    // canonical sign: the entry of largest magnitude of each u_j is positive
+    for (int j = 0; j < r; ++j) {
+      int64_t best = 0;
+      double bmag = -1.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const double a = std::fabs(u[k * r + j]);
+        if (a > bmag) {
+          bmag = a;
+          best = k;
+        }
+      }
+      if (u[best * r + j] < 0.0) {
+        for (int64_t k = 0; k < K; ++k) u[k * r + j] = -u[k * r + j];
+        for (int64_t c = 0; c < N; ++c) v[c * r + j] = -v[c * r + j];
+      }
+    }
+    // L1 = fp16(U_r S^(1/2)), L2 = fp16(S^(1/2) V_r^T), each rounded once from fp64
+    for (int j = 0; j < r; ++j) {
+      const double h = std::sqrt(s[j]);
+      for (int64_t k = 0; k < K; ++k) {
+        const uint16_t q = f64_to_f16(u[k * r + j] * h);
+        L1t[static_cast<int64_t>(j) * K + k] = q;
+        L1[k * r + j] = f16_to_f64(q);
+      }
+      for (int64_t c = 0; c < N; ++c) {
+        const uint16_t q = f64_to_f16(h * v[c * r + j]);
+        L2t[c * r + j] = q;
+        L2[static_cast<int64_t>(j) * N + c] = f16_to_f64(q);
+      }
+    }
+  }
+
+  // R = What - L1 L2 (from the stored fp16 factors; each product of two fp16
+  // values is exact in fp64), rounded to fp32, then quantized down K for
+  // each output column n.
+  const int64_t G = K / SVDQ_GROUP;
+  const int64_t NB = 16;   // columns per task
+#pragma omp parallel
+  {
+    std::vector<float> col(static_cast<size_t>(NB) * K);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t n0 = 0; n0 < N; n0 += NB) {
+      const int64_t nb = std::min(NB, N - n0);
+      for (int64_t k = 0; k < K; ++k) {
+        const double* wrow = &What[k * N + n0];
+        const double* l1 = L1.data() + k * rank;
+        for (int64_t c = 0; c < nb; ++c) {
+          double acc = 0.0;
+          for (int j = 0; j < rank; ++j) acc += l1[j] * L2[static_cast<int64_t>(j) * N + n0 + c];
+          col[c * K + k] = static_cast<float>(wrow[c] - acc);
+        }
+      }
+      for (int64_t c = 0; c < nb; ++c)
+        for (int64_t g = 0; g < G; ++g)
+          quantize_group_f32(&col[c * K + g * SVDQ_GROUP], SVDQ_GROUP,
+                             &w_codes[(n0 + c) * (K / 2) + g * (SVDQ_GROUP / 2)],
+                             &w_scales[(n0 + c) * G + g]);
+    }
+  }
+  return SVDQ_OK;
+  SVDQ_CATCH
+}
+
+int svdq_concat_lora(const uint16_t* L1t, const uint16_t* L2t, int64_t K, int64_t N, int32_t rank,
+                     const float* lambda, const uint16_t* A, const uint16_t* B, int32_t rl,
+                     float scale, uint16_t* L1t_out, uint16_t* L2t_out) {
+  clear_error();
+  if (!lambda || !A || !B || !L1t_out || !L2t_out || (rank > 0 && (!L1t || !L2t))) {
+    set_error("svdq_concat_lora: null pointer");
+    return SVDQ_ERR_NULL;
+  }
+  if (K < 1 || N < 1) {
+    set_error("svdq_concat_lora: bad shape");
+    return SVDQ_ERR_SHAPE;
+  }
+  if (rank < 0 || rl < 1) {
+    set_error("svdq_concat_lora: rank=%d rl=%d", rank, rl);
+    return SVDQ_ERR_RANK;
+  }
+  const int64_t ro = static_cast<int64_t>(rank) + rl;
+  // L1' rows 0..rank-1 are L1; rows rank.. are fp16(lambda (.) A * scale), transposed
+  if (rank > 0) std::memcpy(L1t_out, L1t, sizeof(uint16_t) * static_cast<size_t>(rank) * K);
+  const double sc = static_cast<double>(scale);
+#pragma omp parallel for schedule(static)
+  for (int64_t k = 0; k < K; ++k) {
+    const double l = static_cast<double>(lambda[k]);
+    for (int32_t j = 0; j < rl; ++j) {
+      double t = l * f16_to_f64(A[k * rl + j]);   // exact
+      t = t * sc;                                   // one fp64 rounding
+      L1t_out[(rank + j) * K + k] = f64_to_f16(t);
+    }
+  }
+  // L2' = [L2 ; B], stored transposed: row n = [L2t[n, :], B[:, n]]
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    for (int32_t j = 0; j < rank; ++j) L2t_out[n * ro + j] = L2t[n * rank + j];
+    for (int32_t j = 0; j < rl; ++j) L2t_out[n * ro + rank + j] = B[static_cast<int64_t>(j) * N + n];
+  }
+  return SVDQ_OK;
+}
+
+int svdq_abi_version(void) { return SVDQ_ABI_VERSION; }
+
+const char* svdq_status_str(int status) {
+  switch (status) {
+    case SVDQ_OK: return "ok";
+    case SVDQ_ERR_NULL: return "null pointer";
+    case SVDQ_ERR_SHAPE: return "bad shape or stride";
+    case SVDQ_ERR_ALIGN: return "misaligned pointer or stride";
+    case SVDQ_ERR_DTYPE: return "unknown dtype";
+    case SVDQ_ERR_RANK: return "bad rank";
+    case SVDQ_ERR_WORKSPACE: return "workspace too small";
+    case SVDQ_ERR_HIP: return "HIP error";
+    case SVDQ_ERR_NO_DEVICE: return "no usable GPU";
+    case SVDQ_ERR_INTERNAL: return "internal error";
+    case SVDQ_ERR_GROUP: return "unsupported group size";
+    default: return "unknown status";
+  }
+}
+
+const char* svdq_last_error(void) { return svdq::last_error(); }
+
+}  // extern "C"

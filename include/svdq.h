@@ -1,0 +1,214 @@
+/*
+ * svdq.h -- C ABI of libsvdq, the SVDQuant W4A4 + low-rank linear layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (SVDQuant paper abstract as given on ai-digest.ru; chattools.cn
+ * overview, section "SVDQuant的技术原理" (technical principles)):
+ *
+ *     Y = Xhat . L1 . L2  +  Q(Xhat) . Q(R)  +  b,      Xhat = X . diag(lam)^-1
+ *
+ * Smoothing moves activation outliers onto the weights; an SVD of the smoothed
+ * weight diag(lam).W gives a 16-bit low-rank branch L1.L2 (rank R) and a
+ * residual; the residual and Xhat are quantized to 4 bits with one fp16 scale
+ * per group of 64 input channels. The inference-engine part of the pages
+ * (the Nunchaku engine: the abstract, and the disruptive-concepts.com post,
+ * section "Nunchaku: Fusing Precision and Speed") fuses the low-rank kernels
+ * into the low-bit ones so the activation is not moved twice; here that is
+ * two kernels:
+ *
+ *   K1  svdq_quantize_act_lowrank_down: one pass over X -> 4-bit codes,
+ *       scales and the down-projection D = fp16(Xhat) . L1;
+ *   K2  svdq_w4a4_gemm_lowrank_up: the W4A4 GEMM on the int8 matrix cores,
+ *       integer partial sums per 64-channel group, fp32 rescale, and in the
+ *       same kernel the up-projection fp16(D) . L2 and the bias.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions (all functions)
+ *   - Integer sizes are int64_t (shapes, strides) or int32_t (rank, group).
+ *   - fp16 values travel as uint16_t bit patterns (IEEE binary16).
+ *   - Return value: SVDQ_OK (0) or one SVDQ_ERR_* status. On an error nothing
+ *     is launched and no output is written. No C++ exception crosses the ABI.
+ *     svdq_last_error() (thread-local) then holds a one-line reason.
+ *   - The caller owns every buffer. Device buffers must stay alive until the
+ *     stream has completed the work that uses them.
+ *   - NaN or Inf inputs give unspecified (but memory-safe) outputs.
+ *
+ * Canonical layouts (the bit-exact contract)
+ *   - 4-bit codes are two's complement in [-7, 7]; element 2j is the low
+ *     nibble of byte j, element 2j+1 the high nibble.
+ *   - a_codes: M x K/2 bytes, row-major (row m holds token m along K).
+ *     w_codes: N x K/2 bytes, row-major (row n holds output column n along K).
+ *   - a_scales: M x K/group fp16, w_scales: N x K/group fp16, row-major.
+ *   - L1t: R x K fp16 row-major  (the transpose of the K x R factor L1).
+ *     L2t: N x R fp16 row-major  (the transpose of the R x N factor L2).
+ *     Both are stored contiguous along the dimension they are summed over,
+ *     which is what a matrix-core operand lane loads.
+ *   - D: M x R fp32 row-major.  X: M x K row-major with row stride ldx
+ *     (elements).  Y: M x N row-major with row stride ldy (elements).
+ *
+ * Quantizer (the pages give only "4 bits"; this is the reading implemented,
+ * for both Xhat rows and residual columns, over each group v of 64 values):
+ *     a = max|v|;  s = fp16_rne(min(fp32(a / 7), 65504));
+ *     inv = (s == 0) ? 0 : fp32(1 / s);  q = clamp(rint(fp32(v * inv)), -7, 7)
+ * with correctly rounded fp32 division and multiplication and rounding half to
+ * even. Xhat = fp32(x * inv_smooth[k]).
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SVDQ_ABI_VERSION 1
+
+/* status codes */
+enum {
+  SVDQ_OK = 0,
+  SVDQ_ERR_NULL = 1,       /* a required pointer is NULL */
+  SVDQ_ERR_SHAPE = 2,      /* a size or stride is out of range */
+  SVDQ_ERR_ALIGN = 3,      /* a device pointer or row stride is not 16-byte aligned */
+  SVDQ_ERR_DTYPE = 4,      /* unknown dtype code */
+  SVDQ_ERR_RANK = 5,       /* rank out of range or not a multiple of 16 */
+  SVDQ_ERR_WORKSPACE = 6,  /* workspace too small */
+  SVDQ_ERR_HIP = 7,        /* a HIP call failed; svdq_last_error() has its message */
+  SVDQ_ERR_NO_DEVICE = 8,  /* no usable GPU */
+  SVDQ_ERR_INTERNAL = 9,   /* host numerical routine failed (e.g. no convergence) */
+  SVDQ_ERR_GROUP = 10      /* group size other than 64, or K not a multiple of it */
+};
+
+/* dtype codes for X and Y */
+enum { SVDQ_F16 = 1, SVDQ_F32 = 2 };
+
+/* The only group size implemented. */
+#define SVDQ_GROUP 64
+/* Largest rank the device kernels accept. */
+#define SVDQ_MAX_RANK 256
+
+/* ---------------------------------------------------------------------------
+ * Utilities
+ */
+int svdq_abi_version(void);
+const char* svdq_status_str(int status);
+/* Reason for the last non-OK status returned on this thread ("" if none). */
+const char* svdq_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Host functions: pointers are host memory; synchronous; thread-safe; no
+ * global state. They never touch a GPU.
+ */
+
+/* out[k] = max over the M rows of |X[m][k]|.  X: M x K, row stride ldx >= K.
+ * Calibration statistic for the smoothing factors. */
+int svdq_channel_absmax(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                        float* out);
+
+/* Smoothing factors (chattools.cn overview, technical principles, outlier
+ * item: activation outliers are moved onto the weights).
+ *   lambda[j] = fp32( sqrt( x_absmax[j] / max_n |W[j][n]| ) ), computed in fp64,
+ *   and 1 where either maximum is 0 (migration strength 1/2).
+ * W: K x N row-major fp32 (Y = X . W). */
+int svdq_smoothing_factors(const float* x_absmax, const float* W, int64_t K, int64_t N,
+                           float* lambda);
+
+/* Offline weight preparation (chattools.cn overview, technical principles:
+ * smoothing, SVD into a 16-bit low-rank branch and a residual, 4-bit residual;
+ * the Eckart-Young-Mirsky item for the choice of the top singular values).
+ *   inv_smooth[k] = fp32(1 / lambda[k])
+ *   What = diag(lambda) . W (fp64), What = U S V^T (top `rank` triplets, fp64;
+ *     the entry of largest magnitude of each u_i is made positive)
+ *   L1 = fp16(U_r S_r^(1/2)) written as L1t (rank x K);
+ *   L2 = fp16(S_r^(1/2) V_r^T) written as L2t (N x rank);
+ *   R  = What - L1 . L2 from the stored fp16 factors (fp64), then fp32;
+ *   w_codes / w_scales = the quantizer applied down K for each column n.
+ *   sigma (optional, may be NULL): all min(K, N) singular values of What,
+ *   descending.
+ * Constraints: K % 64 == 0, group == 64, 0 <= rank <= min(K, N), N >= 1.
+ * rank need not be a multiple of 16 here, but the device kernels require it.
+ * Uses OpenMP threads. Returns SVDQ_ERR_INTERNAL if the eigen-solver fails. */
+int svdq_prepare_weights(const float* W, const float* lambda, int64_t K, int64_t N,
+                         int32_t rank, int32_t group, float* inv_smooth, uint16_t* L1t,
+                         uint16_t* L2t, uint8_t* w_codes, uint16_t* w_scales, double* sigma);
+
+/* LoRA concatenation without re-quantization (chattools.cn overview, main
+ * features, LoRA item; SVDQuant abstract). The branch multiplies Xhat, so row
+ * j of A is scaled by lambda[j]:  Xhat . (lambda (.) A) = X . A.
+ *   L1' = [L1 | fp16(lambda (.) A * scale)]   written as L1t_out ((rank+rl) x K)
+ *   L2' = [L2 ; B]                             written as L2t_out (N x (rank+rl))
+ * The product lambda*A is exact in fp64, the scale multiply rounds once in
+ * fp64, the result rounds once to fp16. A: K x rl fp16, B: rl x N fp16 (both
+ * row-major, the usual LoRA down/up shapes). w_codes and w_scales are reused
+ * unchanged. Inputs and outputs must not overlap. */
+int svdq_concat_lora(const uint16_t* L1t, const uint16_t* L2t, int64_t K, int64_t N,
+                     int32_t rank, const float* lambda, const uint16_t* A, const uint16_t* B,
+                     int32_t rl, float scale, uint16_t* L1t_out, uint16_t* L2t_out);
+
+/* ---------------------------------------------------------------------------
+ * Device functions: pointers are device memory; the work is enqueued on
+ * `stream` (0 = the null stream) and the call returns without waiting. They
+ * never allocate device memory and never synchronize.
+ * Common constraints: M >= 1, N >= 1, K >= 64 with K % 64 == 0, group == 64,
+ * 0 <= R <= SVDQ_MAX_RANK with R % 16 == 0; ldx >= K, ldy >= N.
+ * Alignment: X, inv_smooth, L1t, L2t, D, codes and scales 16 bytes, and
+ * ldx * sizeof(X element) a multiple of 16 bytes (X rows are read in 16-byte
+ * vectors); Y and bias only to their element size, any ldy.
+ */
+
+/* K1: one pass over X (SVDQuant abstract: fuse the low-rank branch with the
+ * low-bit kernels so the activation is not moved again).
+ *   Xhat = fp32(x * inv_smooth[k]);
+ *   a_codes, a_scales = the quantizer over each row's groups of 64;
+ *   D = fp16(Xhat) . L1   (fp16 products, fp32 accumulation), D: M x R.
+ * With R == 0, L1t and D may be NULL. */
+int svdq_quantize_act_lowrank_down(const void* X, int x_dtype, int64_t M, int64_t K,
+                                   int64_t ldx, const float* inv_smooth, const uint16_t* L1t,
+                                   int32_t R, int32_t group, uint8_t* a_codes,
+                                   uint16_t* a_scales, float* D, hipStream_t stream);
+
+/* K2: W4A4 GEMM with the low-rank up-projection and bias fused in.
+ *   P[m,n,g] = sum over k in group g of qx[m,k] * qw[n,k]   (exact int32)
+ *   Y[m,n]   = sum_g s_x[m,g] * s_w[n,g] * P[m,n,g]   (fp32)
+ *              + sum_r fp16(D[m,r]) * L2[r,n]          (fp16 products, fp32 sum)
+ *              + bias[n]                               (bias may be NULL)
+ * rounded once to y_dtype. With R == 0, D and L2t may be NULL. */
+int svdq_w4a4_gemm_lowrank_up(const uint8_t* a_codes, const uint16_t* a_scales,
+                              const uint8_t* w_codes, const uint16_t* w_scales, const float* D,
+                              const uint16_t* L2t, int32_t R, const float* bias, void* Y,
+                              int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
+                              int32_t group, hipStream_t stream);
+
+/* Bytes of workspace svdq_linear needs: a_codes, a_scales and D, each
+ * 256-byte aligned inside the workspace. */
+size_t svdq_linear_workspace_bytes(int64_t M, int64_t K, int32_t R, int32_t group);
+
+/* The whole layer: K1 then K2 on `stream`, intermediates in `ws`
+ * (>= svdq_linear_workspace_bytes(M, K, R, group) bytes, 256-byte aligned).
+ * L1t: R x K, L2t: N x R. */
+int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
+                const uint16_t* L1t, const uint16_t* L2t, int32_t R, const uint8_t* w_codes,
+                const uint16_t* w_scales, const float* bias, void* Y, int y_dtype, int64_t ldy,
+                int64_t M, int64_t K, int64_t N, int32_t group, void* ws, size_t ws_bytes,
+                hipStream_t stream);
+
+/* Test hook: the exact integer partials P[m, n, g] for rows row0 .. row0+rows-1,
+ * computed with the same operand unpacking and int8 matrix-core instruction
+ * as K2. P: rows x N x (K/group) int32, row-major. 0 <= row0, row0+rows <= M. */
+int svdq_debug_group_partials(const uint8_t* a_codes, const uint8_t* w_codes, int64_t M,
+                              int64_t N, int64_t K, int32_t group, int64_t row0, int64_t rows,
+                              int32_t* P, hipStream_t stream);
+
+/* GELU, tanh form, between the two linears of a DiT MLP (not on the pages; the
+ * textbook formula 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))), computed
+ * in fp32 from fp16 and rounded to fp16. x and y may be the same buffer. */
+int svdq_gelu_tanh_f16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

@@ -1,0 +1,122 @@
+"""Shared helpers of the GPU parity tests: seeded layers, device buffers and
+the oracle side of each comparison. The oracle's inputs are the seeded
+inputs and the host-side factors; nothing here feeds a GPU result to it."""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+
+import oracle as O
+import workloads as wl
+
+TOL_Y = 2e-3          # max |Y_gpu - Y_oracle| / max |Y_oracle|
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def dev(a: np.ndarray):
+    torch = torch_mod()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda")
+
+
+def host_u16(t) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def layer(cfg: int, li: int, with_bias: bool = False, use_lora: bool = True):
+    """(Layer, X, W, lam, prep, bias) with the library's host prep."""
+    L, X, W, lam, p = _layer(cfg, li, use_lora)
+    bias = wl.bias(cfg, li, L.N) if with_bias else None
+    return L, X, W, lam, p, bias
+
+
+@functools.lru_cache(maxsize=6)
+def _layer(cfg: int, li: int, use_lora: bool):
+    import bit_post_quantized_smooth_amd as sq
+    L, X, W = wl.layer_inputs(cfg, li)
+    if X is None:          # input of a down-projection: GELU of seeded pre-activations
+        X = O.gelu_tanh(wl.preactivation(cfg, li, L.M, L.K, L.x_outlier_frac, L.x_outlier_scale))
+    lam = sq.smoothing_factors(sq.channel_absmax(X), W)
+    p = sq.prepare_weights(W, lam, L.rank)
+    if L.lora_rank and use_lora:
+        A, B = wl.lora(cfg, li, L.K, L.N, L.lora_rank)
+        p = sq.concat_lora(p, lam, A, B, 1.0)
+    return L, X, W, lam, p
+
+
+class DeviceLayer:
+    def __init__(self, X, p, bias, y_dtype="f16"):
+        torch = torch_mod()
+        self.M, self.K = X.shape
+        self.N, self.R = p.N, p.rank
+        self.X = dev(X)
+        self.inv = dev(p.inv_smooth)
+        self.L1t = dev(p.L1t) if self.R else None
+        self.L2t = dev(p.L2t) if self.R else None
+        self.wc = dev(p.w_codes)
+        self.ws = dev(p.w_scales)
+        self.bias = dev(bias) if bias is not None else None
+        G = self.K // 64
+        self.a_codes = torch.empty((self.M, self.K // 2), dtype=torch.uint8, device="cuda")
+        self.a_scales = torch.empty((self.M, G), dtype=torch.int16, device="cuda")
+        self.D = torch.empty((self.M, max(self.R, 1)), dtype=torch.float32, device="cuda")
+        self.Y = torch.empty((self.M, self.N),
+                             dtype=torch.float16 if y_dtype == "f16" else torch.float32, device="cuda")
+
+    def k1(self):
+        import bit_post_quantized_smooth_amd as sq
+        sq.quantize_act_lowrank_down(self.X, self.inv, self.L1t, self.R, self.a_codes,
+                                     self.a_scales, self.D if self.R else None)
+
+    def k2(self):
+        import bit_post_quantized_smooth_amd as sq
+        sq.w4a4_gemm_lowrank_up(self.a_codes, self.a_scales, self.wc, self.ws,
+                                self.D if self.R else None, self.L2t, self.R, self.bias, self.Y,
+                                self.K)
+
+
+def sample_rows(M: int, seed: int = 0, n_random: int = 48):
+    """First tile, tile boundaries, the last rows (the tail) and random rows."""
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(M, 16)))
+    for b in (127, 128, 129, 255, 256):
+        if b < M:
+            rows.add(b)
+    rows.update(range(max(0, M - 17), M))
+    rows.update(int(r) for r in rng.choice(M, min(M, n_random), replace=False))
+    return np.array(sorted(rows))
+
+
+def oracle_prep(X, W, p, base_rank=None):
+    """The oracle's own smoothing, 1/lambda and residual codes, for the library's
+    fp16 factors (the factors are an input shared by both sides, like X).
+
+    With a LoRA concatenated onto the SVD factors, the residual belongs to the
+    first ``base_rank`` columns only (the codes are not re-quantized)."""
+    lam = O.smoothing_factors(O.channel_absmax(X), W)
+    inv = O.inv_smoothing(lam)
+    r = p.rank if base_rank is None else base_rank
+    wc, ws = O.quantize_residual_from_factors(W, lam, p.L1[:, :r], p.L2[:r])
+    return lam, inv, wc, ws
+
+
+def oracle_rows(X, inv, p, wc, ws, bias, rows, out_dtype, chunk=16):
+    """Oracle Y for the given rows, in chunks of rows (rows are independent)."""
+    Ys = []
+    for i in range(0, len(rows), chunk):
+        r = rows[i:i + chunk]
+        Ys.append(O.linear(X[r], inv, p.L1, p.L2, wc, ws, bias, out_dtype))
+    return np.concatenate(Ys, axis=0)
+
+
+def rel_err(y, ref):
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(y - ref)) / max(np.max(np.abs(ref)), 1e-30))

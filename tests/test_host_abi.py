@@ -1,0 +1,226 @@
+"""The C ABI on the CPU: exported symbols, argument checks and the host prep
+(smoothing, SVD split, residual codes, LoRA concat) against the oracle.
+
+No test here launches GPU work: the device entry points are only called with
+arguments that fail validation (which runs before any HIP call), or, on a
+machine without a GPU, with arguments that pass it (they must report
+SVDQ_ERR_NO_DEVICE)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as wl
+
+sq = pytest.importorskip("bit_post_quantized_smooth_amd")
+from bit_post_quantized_smooth_amd import _lib  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svdq.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(svdq_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert len(names) >= 13, names
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(svdq_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        getattr(_lib.lib, n)
+
+
+def test_version_and_status_strings():
+    assert _lib.abi_version() == 1
+    for s in range(11):
+        assert _lib.status_str(s) and _lib.status_str(s) != "unknown status"
+    assert _lib.status_str(99) == "unknown status"
+
+
+def test_channel_absmax_and_smoothing_bit_exact():
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((37, 192)).astype(np.float32)
+    X[:, 5] = 0.0
+    W = (rng.standard_normal((192, 40)) * 0.02).astype(np.float32)
+    W[7] = 0.0
+    for Xd in (X, X.astype(np.float16)):
+        xa = sq.channel_absmax(Xd)
+        assert np.array_equal(xa, O.channel_absmax(Xd).astype(np.float32))
+        lam = sq.smoothing_factors(xa, W)
+        assert np.array_equal(lam, O.smoothing_factors(O.channel_absmax(Xd), W))
+    assert lam[5] == 1.0 and lam[7] == 1.0
+
+
+@pytest.mark.parametrize("K,N,r", [(64, 16, 0), (128, 96, 16), (256, 64, 32), (192, 300, 48),
+                                   (512, 512, 16)])
+def test_prepare_codes_bit_exact(K, N, r):
+    rng = np.random.default_rng(K * 7 + N + r)
+    X = rng.standard_normal((64, K)).astype(np.float32)
+    X[:, rng.choice(K, 3, replace=False)] *= 20
+    W = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    W[rng.choice(K, 2, replace=False)] *= 10
+    lam = O.smoothing_factors(O.channel_absmax(X), W)
+    p = sq.prepare_weights(W, lam, r, want_sigma=True)
+    assert np.array_equal(p.inv_smooth, O.inv_smoothing(lam))
+    # the residual codes that the oracle derives from the library's own factors
+    wc, ws = O.quantize_residual_from_factors(W, lam, p.L1, p.L2)
+    assert np.array_equal(p.w_codes, wc)
+    assert np.array_equal(p.w_scales, ws.view(np.uint16))
+    # singular values against LAPACK
+    S = np.linalg.svd(O.smooth_weight(W, lam), compute_uv=False)
+    assert np.allclose(p.sigma, S, rtol=0, atol=1e-10 * S[0])
+    if r:
+        # Eckart-Young-Mirsky: the library's fp16 pair cannot beat the optimum and
+        # stays within the fp16 rounding of the factors
+        What = O.smooth_weight(W, lam)
+        L1 = p.L1.astype(np.float64)
+        L2 = p.L2.astype(np.float64)
+        e = np.linalg.norm(What - L1 @ L2)
+        tail = np.sqrt(np.sum(S[r:] ** 2))
+        rnd = 2.0 ** -11 * (np.linalg.norm(L1) * np.linalg.norm(L2, 2) +
+                            np.linalg.norm(L1, 2) * np.linalg.norm(L2)) * 1.01
+        assert tail * (1 - 1e-12) <= e <= tail + rnd
+        # the balanced split: L1^T L1 ~ diag(sigma_r)
+        G1 = L1.T @ L1
+        assert np.allclose(np.diag(G1), S[:r], rtol=4e-3)
+        # canonical sign: the largest-magnitude entry of each column of L1 is positive
+        idx = np.argmax(np.abs(L1), axis=0)
+        assert np.all(L1[idx, np.arange(r)] > 0)
+
+
+def test_prepare_full_rank_reconstructs():
+    rng = np.random.default_rng(5)
+    K, N = 64, 48
+    W = (rng.standard_normal((K, N)) * 0.05).astype(np.float32)
+    lam = np.ones(K, dtype=np.float32)
+    p = sq.prepare_weights(W, lam, min(K, N))
+    L1 = p.L1.astype(np.float64)
+    L2 = p.L2.astype(np.float64)
+    E = O.smooth_weight(W, lam) - L1 @ L2
+    rnd = 2.0 ** -11 * (np.linalg.norm(L1) * np.linalg.norm(L2, 2) +
+                        np.linalg.norm(L1, 2) * np.linalg.norm(L2)) * 1.01
+    assert np.linalg.norm(E) <= rnd
+
+
+@pytest.mark.slow
+def test_prepare_dit_qkv_full_size_bit_exact():
+    """The 3072 x 9216 DiT QKV weight: residual codes bit-exact at full size."""
+    L, X, W = wl.layer_inputs(1, 0)
+    lam = sq.smoothing_factors(sq.channel_absmax(X), W)
+    p = sq.prepare_weights(W, lam, L.rank)
+    wc, ws = O.quantize_residual_from_factors(W, lam, p.L1, p.L2)
+    assert np.array_equal(p.w_codes, wc)
+    assert np.array_equal(p.w_scales, ws.view(np.uint16))
+
+
+def test_concat_lora_bit_exact():
+    rng = np.random.default_rng(9)
+    K, N, r, rl = 128, 80, 16, 8
+    X = rng.standard_normal((16, K)).astype(np.float32)
+    W = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    lam = O.smoothing_factors(O.channel_absmax(X), W)
+    p = sq.prepare_weights(W, lam, r)
+    A = (rng.standard_normal((K, rl)) * 0.01).astype(np.float16)
+    B = (rng.standard_normal((rl, N)) * 0.01).astype(np.float16)
+    for scale in (1.0, 0.37):
+        q = sq.concat_lora(p, lam, A, B, scale)
+        L1o, L2o = O.concat_lora(p.L1, p.L2, lam, A, B, scale)
+        assert np.array_equal(q.L1.view(np.uint16), L1o.view(np.uint16))
+        assert np.array_equal(q.L2.view(np.uint16), L2o.view(np.uint16))
+        assert np.array_equal(q.w_codes, p.w_codes) and q.rank == r + rl
+
+
+def test_host_errors():
+    L = _lib.lib
+    W = np.zeros((128, 8), dtype=np.float32)
+    lam = np.ones(128, dtype=np.float32)
+    buf = np.zeros(1 << 16, dtype=np.uint8)
+    bp = buf.ctypes.data
+    assert L.svdq_prepare_weights(None, lam.ctypes.data, 128, 8, 4, 64, bp, bp, bp, bp, bp, None) == _lib.ERR_NULL
+    assert L.svdq_prepare_weights(W.ctypes.data, lam.ctypes.data, 128, 8, 4, 32, bp, bp, bp, bp, bp, None) == _lib.ERR_GROUP
+    assert L.svdq_prepare_weights(W.ctypes.data, lam.ctypes.data, 100, 8, 4, 64, bp, bp, bp, bp, bp, None) == _lib.ERR_GROUP
+    assert L.svdq_prepare_weights(W.ctypes.data, lam.ctypes.data, 128, 8, 9, 64, bp, bp, bp, bp, bp, None) == _lib.ERR_RANK
+    assert "rank" in _lib.last_error()
+    assert L.svdq_channel_absmax(bp, 3, 4, 4, 4, bp) == _lib.ERR_DTYPE
+    assert L.svdq_channel_absmax(bp, 2, 4, 8, 4, bp) == _lib.ERR_SHAPE
+    assert L.svdq_concat_lora(None, None, 64, 8, 0, lam.ctypes.data, bp, bp, 0, 1.0, bp, bp) == _lib.ERR_RANK
+    assert L.svdq_smoothing_factors(None, bp, 4, 4, bp) == _lib.ERR_NULL
+
+
+# Fake device addresses: never dereferenced because validation rejects the call
+# (or, on a machine without a GPU, the device check does).
+A16 = 0x10000
+MIS = 0x10008
+
+
+def test_device_entry_points_reject_bad_arguments():
+    L = _lib.lib
+    # K1
+    assert L.svdq_quantize_act_lowrank_down(None, 1, 16, 64, 64, A16, A16, 16, 64, A16, A16, A16, None) == _lib.ERR_NULL
+    assert L.svdq_quantize_act_lowrank_down(A16, 7, 16, 64, 64, A16, A16, 16, 64, A16, A16, A16, None) == _lib.ERR_DTYPE
+    assert L.svdq_quantize_act_lowrank_down(A16, 1, 16, 96, 96, A16, A16, 16, 64, A16, A16, A16, None) == _lib.ERR_GROUP
+    assert L.svdq_quantize_act_lowrank_down(A16, 1, 16, 64, 64, A16, A16, 24, 64, A16, A16, A16, None) == _lib.ERR_RANK
+    assert L.svdq_quantize_act_lowrank_down(A16, 1, 16, 64, 64, A16, A16, 512, 64, A16, A16, A16, None) == _lib.ERR_RANK
+    assert L.svdq_quantize_act_lowrank_down(A16, 1, 0, 64, 64, A16, A16, 16, 64, A16, A16, A16, None) == _lib.ERR_SHAPE
+    assert L.svdq_quantize_act_lowrank_down(A16, 1, 16, 64, 32, A16, A16, 16, 64, A16, A16, A16, None) == _lib.ERR_SHAPE
+    assert L.svdq_quantize_act_lowrank_down(MIS, 1, 16, 64, 64, A16, A16, 16, 64, A16, A16, A16, None) == _lib.ERR_ALIGN
+    assert L.svdq_quantize_act_lowrank_down(A16, 1, 16, 64, 68, A16, A16, 16, 64, A16, A16, A16, None) == _lib.ERR_ALIGN
+    assert L.svdq_quantize_act_lowrank_down(A16, 1, 16, 64, 64, A16, None, 16, 64, A16, A16, A16, None) == _lib.ERR_NULL
+    # K2
+    args = [A16, A16, A16, A16, A16, A16, 16, None, A16, 1, 16, 16, 64, 16, 64, None]
+    bad = list(args); bad[8] = None
+    assert L.svdq_w4a4_gemm_lowrank_up(*bad) == _lib.ERR_NULL
+    bad = list(args); bad[9] = 5
+    assert L.svdq_w4a4_gemm_lowrank_up(*bad) == _lib.ERR_DTYPE
+    bad = list(args); bad[13] = 8
+    assert L.svdq_w4a4_gemm_lowrank_up(*bad) == _lib.ERR_SHAPE
+    bad = list(args); bad[8] = 0x10001          # fp16 Y on an odd address
+    assert L.svdq_w4a4_gemm_lowrank_up(*bad) == _lib.ERR_ALIGN
+    bad = list(args); bad[7] = 0x10002          # bias not 4-byte aligned
+    assert L.svdq_w4a4_gemm_lowrank_up(*bad) == _lib.ERR_ALIGN
+    bad = list(args); bad[0] = MIS              # codes
+    assert L.svdq_w4a4_gemm_lowrank_up(*bad) == _lib.ERR_ALIGN
+    bad = list(args); bad[14] = 128
+    assert L.svdq_w4a4_gemm_lowrank_up(*bad) == _lib.ERR_GROUP
+    # whole layer: workspace
+    need = L.svdq_linear_workspace_bytes(16, 64, 16, 64)
+    assert need >= 16 * 32 + 16 * 2 + 16 * 16 * 4 and need % 256 == 0
+    assert L.svdq_linear_workspace_bytes(16, 60, 16, 64) == 0
+    la = [A16, 1, 64, A16, A16, A16, 16, A16, A16, None, A16, 1, 16, 16, 64, 16, 64, A16, need - 1, None]
+    assert L.svdq_linear(*la) == _lib.ERR_WORKSPACE
+    la[18] = need
+    la[17] = 0x10080
+    assert L.svdq_linear(*la) == _lib.ERR_ALIGN
+    # partials hook: slice outside the rows
+    assert L.svdq_debug_group_partials(A16, A16, 16, 16, 64, 64, 10, 7, A16, None) == _lib.ERR_SHAPE
+    assert L.svdq_gelu_tanh_f16(A16, MIS, 8, None) == _lib.ERR_ALIGN
+    assert L.svdq_gelu_tanh_f16(A16, A16, 0, None) == _lib.OK          # empty: nothing to do
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_has_gpu(), reason="only meaningful where no GPU is present")
+def test_device_entry_points_report_no_device():
+    L = _lib.lib
+    assert L.svdq_quantize_act_lowrank_down(A16, 1, 16, 64, 64, A16, A16, 16, 64, A16, A16, A16, None) == _lib.ERR_NO_DEVICE
+    assert _lib.last_error()
+    args = [A16, A16, A16, A16, A16, A16, 16, None, A16, 1, 16, 16, 64, 16, 64, None]
+    assert L.svdq_w4a4_gemm_lowrank_up(*args) == _lib.ERR_NO_DEVICE
+    assert L.svdq_gelu_tanh_f16(A16, A16, 8, None) == _lib.ERR_NO_DEVICE
