@@ -196,7 +196,7 @@ def main():
         del sets0
 
     if args.copy_probe:
-        n = 64 << 20                      # 64 Mi fp32 = 256 MiB read + 256 MiB written
+        n = 256 << 20                     # 256 Mi fp32 = 1 GiB read + 1 GiB written (> MALL)
         a = torch.ones(n, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
         for _ in range(5):

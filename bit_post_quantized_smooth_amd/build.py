@@ -32,6 +32,9 @@ HIPCC_FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     # no packed fp32 (v_pk_fma_f32 and friends) anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results straight into VGPRs: the rescale reads every element
+    # with VALU ops, and an AGPR destination would add a v_accvgpr_read each
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 GXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fopenmp", "-D__HIP_PLATFORM_AMD__",

@@ -4,27 +4,35 @@
 // Both operands are 4-bit (SVDQuant abstract: weights and activations at
 // 4 bits; chattools.cn overview, section "SVDQuant的主要功能", quantization
 // item). gfx950 has no 4-bit integer matrix instruction, so the nibbles are
-// widened in registers to int8 lanes holding 16*q (two bit operations per 4
-// codes, see device_common.hpp) and fed to v_mfma_i32_16x16x64_i8: one
-// instruction covers exactly one 64-channel group of a 16x16 output block, so
-// its int32 result is the exact group partial (times 256).
+// widened to int8 lanes holding 16*q (two bit operations per 4 codes, see
+// device_common.hpp) and fed to v_mfma_i32_16x16x64_i8: one instruction covers
+// exactly one 64-channel group of a 16 x 16 output block, so its int32 result
+// is the exact group partial (times 256).
 //
 // Per-group rescale: the int32 accumulator is seeded with the bit pattern of
-// 1.5*2^23, so the partial reads back as the float 12582912 + 256 P. Then
-//     t   = fma(f, s_w / 256, -49152 * s_w)  = P * s_w  rounded once (fp32)
+// 1.5*2^23, so the partial reads back as the float f = 12582912 + 256 P. Then
+//     t   = fma(f, s_w, -12582912 s_w)  = 256 P s_w  rounded once (fp32)
 //     acc = fma(t, s_x, acc)
-// i.e. two fp32 ops per output and group. The low-rank branch (the Nunchaku
-// engine fuses it into the low-bit kernel: SVDQuant abstract; the
-// disruptive-concepts.com post, section "Nunchaku: Fusing Precision and
-// Speed") runs after the K loop as fp16 MFMAs on the same fp32 accumulators:
-// acc += fp16(D) . L2, then the bias, then one rounding to the output type.
+// i.e. two fp32 ops per output and group, both reading the fp16 scales
+// directly (v_fma_mix_f32); the factor 256 is removed once after the K loop.
+// These two ops per output and group, not the matrix instruction, bound the
+// kernel: one v_mfma_i32_16x16x64_i8 does the integer work of 64 outputs x 1
+// group in about the time of 4 wave-wide fp32 ops.
+//
+// The low-rank branch (the Nunchaku engine fuses it into the low-bit kernel:
+// SVDQuant abstract; the disruptive-concepts.com post, section "Nunchaku:
+// Fusing Precision and Speed") runs after the K loop as fp16 MFMAs on the same
+// fp32 accumulators: acc += fp16(D) . L2, then the bias, then one rounding to
+// the output type.
 //
 // Tiling: a 256-thread workgroup computes a 128 x 128 tile of Y; each of its
 // 4 waves owns a 64 x 64 sub-tile (4 x 4 blocks of 16 x 16). The K loop moves
-// 4 groups (128 bytes of codes per row) per stage through double-buffered LDS;
-// each row's 32-byte group slice is stored as four 8-byte chunks XOR-swizzled
-// by (row / 4) % 4, so the 16 lanes that read one chunk position from 16
-// consecutive rows hit 16 different bank pairs.
+// 2 groups per stage through double-buffered LDS. The loader widens the codes
+// once, as it stores them, and stores them in operand order: the 16 bytes a
+// lane feeds to the matrix instruction for (row block, group) sit at
+// [group][row block][lane], so each operand is one contiguous, conflict-free
+// 16-byte LDS read per lane. The next group's operands are read while the
+// current group computes.
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -36,84 +44,102 @@ namespace {
 
 constexpr int BM = 128;
 constexpr int BN = 128;
-constexpr int KG = 4;               // groups per LDS stage
 constexpr int NT = 256;             // threads per workgroup
-static_assert(BM == BN && BM == 128 && NT == 2 * BM, "loader assumes 128 x 128 tiles");
+static_assert(BM == BN && BM == 128 && NT == 2 * BM,
+              "the loader maps thread t to row t/2, 16-byte half t%2 of one group");
 
-struct StageRegs {
-  uint4 a[4];                       // 64 bytes of A codes (2 groups of one row)
-  uint4 b[4];                       // 64 bytes of B codes
-  uint16_t sc[4];                   // scales of 4 groups: A row t (t < 128) or B row t-128
+struct Smem {
+  v4i a[2][BM / 16][64];            // widened A operands of one group [buf][row block][lane]
+  v4i b[2][BN / 16][64];            // widened B operands
+  uint16_t sx[2][BM];               // activation scales [buf][row]
+  uint16_t sw[2][2][16][4];         // weight scales [buf][col/64][col%16][(col%64)/16]
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+// One group's slice of the tile, staged in registers between its global load
+// and its (widened) store to LDS. Thread t loads 16 bytes of A row m0 + t/2 and
+// of B row n0 + t/2 (half t%2 of the group's 32 bytes) and one scale (A row t
+// for t < 128, else B column t-128). Rows and columns past M or N are clamped
+// to the last one: their results are computed but never stored, so every load
+// is unconditional and in bounds.
+struct Stage {
+  uint4 a, b;                       // 16 bytes of codes of A row t/2 and of B row t/2
+  uint16_t sc;                      // scale: A row t (t < 128) or B column t-128
+};
 
-__device__ __forceinline__ void load_stage(StageRegs& r, const uint8_t* __restrict__ a_codes,
-                                           const uint16_t* __restrict__ a_scales,
-                                           const uint8_t* __restrict__ w_codes,
-                                           const uint16_t* __restrict__ w_scales, int64_t M,
-                                           int64_t N, int64_t K, int64_t G, int64_t m0, int64_t n0,
-                                           int64_t g0) {
+__device__ __forceinline__ void load_group(Stage& r, const uint8_t* __restrict__ a_row,
+                                           const uint8_t* __restrict__ b_row,
+                                           const uint16_t* __restrict__ sc_row, int64_t g) {
+  r.a = *reinterpret_cast<const uint4*>(a_row + g * kGroupBytes);
+  r.b = *reinterpret_cast<const uint4*>(b_row + g * kGroupBytes);
+  r.sc = sc_row[g];
+}
+
+// Widen and store: the 16 bytes of row t/2 hold chunks q = 2h, 2h+1 (codes
+// 16q .. 16q+15), which go to lane q*16 + row%16 of row block row/16.
+__device__ __forceinline__ void store_group(const Stage& r, Smem& sm, int buf) {
   const int t = threadIdx.x;
-  const int row = t >> 1, half = t & 1;
-  const int64_t kb = K / 2;
-  const int64_t ga = g0 + 2 * half;                 // first group of this thread's 64 bytes
-  // A codes
-  {
-    const int64_t m = m0 + row;
-    const uint8_t* p = a_codes + m * kb + ga * kGroupBytes;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t g = ga + (j >> 1);
-      r.a[j] = (m < M && g < G) ? *reinterpret_cast<const uint4*>(p + 16 * j) : make_uint4(0, 0, 0, 0);
-    }
-  }
-  {
-    const int64_t n = n0 + row;
-    const uint8_t* p = w_codes + n * kb + ga * kGroupBytes;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t g = ga + (j >> 1);
-      r.b[j] = (n < N && g < G) ? *reinterpret_cast<const uint4*>(p + 16 * j) : make_uint4(0, 0, 0, 0);
-    }
-  }
-  {
-    const bool is_a = t < BM;
-    const int64_t idx = (is_a ? m0 : n0) + (t & (BM - 1));
-    const bool ok = idx < (is_a ? M : N);
-    const uint16_t* src = (is_a ? a_scales : w_scales) + idx * G;
-#pragma unroll
-    for (int j = 0; j < KG; ++j) r.sc[j] = (ok && g0 + j < G) ? src[g0 + j] : 0;
+  const int row = t >> 1, h = t & 1;
+  const int rb = row >> 4, rr = row & 15;
+  sm.a[buf][rb][(2 * h) * 16 + rr] = widen_codes(make_uint2(r.a.x, r.a.y));
+  sm.a[buf][rb][(2 * h + 1) * 16 + rr] = widen_codes(make_uint2(r.a.z, r.a.w));
+  sm.b[buf][rb][(2 * h) * 16 + rr] = widen_codes(make_uint2(r.b.x, r.b.y));
+  sm.b[buf][rb][(2 * h + 1) * 16 + rr] = widen_codes(make_uint2(r.b.z, r.b.w));
+  if (t < BM) {
+    sm.sx[buf][t] = r.sc;
+  } else {
+    const int c = t - BM;
+    sm.sw[buf][c >> 6][c & 15][(c >> 4) & 3] = r.sc;
   }
 }
 
-struct Smem {
-  uint8_t a[2][KG][BM][kGroupBytes];
-  uint8_t b[2][KG][BN][kGroupBytes];
-  uint16_t sc[2][KG][2][BM];        // [.][.][0][row] = A scales, [.][.][1][col] = B scales
+// Operands and scales of one group for one wave.
+struct Frags {
+  v4i A[4], B[4];
+};
+struct Scales {
+  uint2 sxp[4];                     // fp16 activation scales of the lane's 4 rows, per row block
+  float sw[4];                      // weight scale of the lane's column, per column block
+  float be[4];                      // -12582912 * sw
 };
 
-__device__ __forceinline__ void store_stage(const StageRegs& r, Smem& sm, int buf) {
-  const int t = threadIdx.x;
-  const int row = t >> 1, half = t & 1;
+__device__ __forceinline__ void read_group(Frags& f, Scales& sc, const Smem& sm, int buf, int wm,
+                                           int wn, int lane) {
+  const int q = lane >> 4, rl = lane & 15;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int gg = 2 * half + (j >> 1);
-    const int c0 = 2 * (j & 1);                     // chunk index of the first 8 bytes
-    uint2 lo = make_uint2(r.a[j].x, r.a[j].y), hi = make_uint2(r.a[j].z, r.a[j].w);
-    *reinterpret_cast<uint2*>(&sm.a[buf][gg][row][8 * swz(row, c0)]) = lo;
-    *reinterpret_cast<uint2*>(&sm.a[buf][gg][row][8 * swz(row, c0 + 1)]) = hi;
-    lo = make_uint2(r.b[j].x, r.b[j].y);
-    hi = make_uint2(r.b[j].z, r.b[j].w);
-    *reinterpret_cast<uint2*>(&sm.b[buf][gg][row][8 * swz(row, c0)]) = lo;
-    *reinterpret_cast<uint2*>(&sm.b[buf][gg][row][8 * swz(row, c0 + 1)]) = hi;
+  for (int i = 0; i < 4; ++i) f.A[i] = sm.a[buf][wm * 4 + i][lane];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.B[j] = sm.b[buf][wn * 4 + j][lane];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    sc.sxp[i] = *reinterpret_cast<const uint2*>(&sm.sx[buf][wm * 64 + i * 16 + 4 * q]);
+  const uint2 swp = *reinterpret_cast<const uint2*>(&sm.sw[buf][wn][rl][0]);
+  sc.sw[0] = h2f(static_cast<uint16_t>(swp.x & 0xFFFFu));
+  sc.sw[1] = h2f(static_cast<uint16_t>(swp.x >> 16));
+  sc.sw[2] = h2f(static_cast<uint16_t>(swp.y & 0xFFFFu));
+  sc.sw[3] = h2f(static_cast<uint16_t>(swp.y >> 16));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sc.be[j] = sc.sw[j] * -kMagicF;     // exact: 3 * 2^22 * s_w
+}
+
+__device__ __forceinline__ float sx_of(const Scales& sc, int i, int e) {
+  const uint32_t w = (e < 2) ? sc.sxp[i].x : sc.sxp[i].y;
+  return h2f(static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xFFFFu)));
+}
+
+// Rescale of one 16 x 16 block of group g (two fp32 ops per output):
+//   t = (12582912 + 256 P) s_w - 12582912 s_w = 256 P s_w (rounded once); acc += t s_x
+__device__ __forceinline__ void rescale_block(v4f& acc, const v4i& p, const Scales& sc, int i,
+                                              int j) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int pe = p[e];                     // scalar copy: see as_float()
+    const float t = __builtin_fmaf(as_float(pe), sc.sw[j], sc.be[j]);
+    acc[e] = __builtin_fmaf(t, sx_of(sc, i, e), acc[e]);
   }
-#pragma unroll
-  for (int j = 0; j < KG; ++j) sm.sc[buf][j][t >> 7][t & (BM - 1)] = r.sc[j];
 }
 
 template <bool Y_F16>
-__global__ __launch_bounds__(NT) void k2_w4a4_kernel(
+__global__ __launch_bounds__(NT, 2) void k2_w4a4_kernel(
     const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
     const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales,
     const float* __restrict__ D, const uint16_t* __restrict__ L2t, int R,
@@ -127,71 +153,84 @@ __global__ __launch_bounds__(NT) void k2_w4a4_kernel(
   const int64_t m0 = static_cast<int64_t>(tile / tiles_n) * BM;
   const int64_t n0 = static_cast<int64_t>(tile % tiles_n) * BN;
   const int64_t G = K / kGroup;
-  const int64_t S = (G + KG - 1) / KG;
+  const v4i seed = v4i{kMagicSeed, kMagicSeed, kMagicSeed, kMagicSeed};
 
   v4f acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  const v4i seed = v4i{kMagicSeed, kMagicSeed, kMagicSeed, kMagicSeed};
 
-  StageRegs st;
-  load_stage(st, a_codes, a_scales, w_codes, w_scales, M, N, K, G, m0, n0, 0);
-  store_stage(st, sm, 0);
+  // Software pipeline over the 64-channel groups. Iteration g rescales the
+  // integer partials P of group g block by block and, right after each block,
+  // issues the matrix instruction of group g+1 into the same registers, so the
+  // matrix core and the vector ALU work side by side within the wave. LDS
+  // holds two groups; a thread's registers hold the next group's codes between
+  // their global load and their widened store.
+  const int64_t kb = K / 2;
+  const int t = threadIdx.x;
+  const int64_t ma = (m0 + (t >> 1) < M ? m0 + (t >> 1) : M - 1);
+  const int64_t nb = (n0 + (t >> 1) < N ? n0 + (t >> 1) : N - 1);
+  const uint8_t* a_row = a_codes + ma * kb + 16 * (t & 1);
+  const uint8_t* b_row = w_codes + nb * kb + 16 * (t & 1);
+  const int64_t sidx = t < BM ? (m0 + t < M ? m0 + t : M - 1)
+                              : (n0 + (t - BM) < N ? n0 + (t - BM) : N - 1);
+  const uint16_t* sc_row = (t < BM ? a_scales : w_scales) + sidx * G;
+
+  Stage st;
+  load_group(st, a_row, b_row, sc_row, 0);
+  store_group(st, sm, 0);
+  if (G > 1) {
+    load_group(st, a_row, b_row, sc_row, 1);
+    store_group(st, sm, 1);
+  }
+  if (G > 2) load_group(st, a_row, b_row, sc_row, 2);
   __syncthreads();
 
-  for (int64_t s = 0; s < S; ++s) {
-    const int buf = static_cast<int>(s & 1);
-    if (s + 1 < S)
-      load_stage(st, a_codes, a_scales, w_codes, w_scales, M, N, K, G, m0, n0, (s + 1) * KG);
-#pragma unroll 1
-    for (int gg = 0; gg < KG; ++gg) {
-      v4i A[4], B[4];
+  v4i P[4][4];
+  Frags f;
+  Scales cur, nxt;
+  read_group(f, cur, sm, 0, wm, wn, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + i * 16 + rl;
-        A[i] = widen_codes(*reinterpret_cast<const uint2*>(&sm.a[buf][gg][r][8 * swz(r, q)]));
-      }
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = wn * 64 + j * 16 + rl;
-        B[j] = widen_codes(*reinterpret_cast<const uint2*>(&sm.b[buf][gg][c][8 * swz(c, q)]));
-      }
-      float sx[4][4];
+    for (int j = 0; j < 4; ++j) P[i][j] = mfma_i8_16x16x64(f.A[i], f.B[j], seed);
+
+  for (int64_t g = 0; g + 1 < G; ++g) {
+    const int buf = static_cast<int>(g & 1);
+    __syncthreads();                 // all waves are done reading group g's buffer; group g+1 is stored
+    if (g + 2 < G) {
+      store_group(st, sm, buf);      // group g+2 replaces group g
+      if (g + 3 < G) load_group(st, a_row, b_row, sc_row, g + 3);
+    }
+    read_group(f, nxt, sm, buf ^ 1, wm, wn, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint2 p = *reinterpret_cast<const uint2*>(&sm.sc[buf][gg][0][wm * 64 + i * 16 + 4 * q]);
-        sx[i][0] = h2f(static_cast<uint16_t>(p.x & 0xFFFFu));
-        sx[i][1] = h2f(static_cast<uint16_t>(p.x >> 16));
-        sx[i][2] = h2f(static_cast<uint16_t>(p.y & 0xFFFFu));
-        sx[i][3] = h2f(static_cast<uint16_t>(p.y >> 16));
-      }
-      float al[4], be[4];
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float sw = h2f(sm.sc[buf][gg][1][wn * 64 + j * 16 + rl]);
-        al[j] = sw * 0.00390625f;                 // s_w / 256, exact
-        be[j] = sw * -49152.0f;                   // -(1.5 * 2^23 / 256) s_w, exact
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v4i p = mfma_i8_16x16x64(A[i], B[j], seed);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int pe = p[e];                 // scalar copy: see as_float()
-            const float f = as_float(pe);
-            const float t = __builtin_fmaf(f, al[j], be[j]);
-            acc[i][j][e] = __builtin_fmaf(t, sx[i][e], acc[i][j][e]);
-          }
-        }
+        rescale_block(acc[i][j], P[i][j], cur, i, j);
+        P[i][j] = mfma_i8_16x16x64(f.A[i], f.B[j], seed);
       }
     }
-    if (s + 1 < S) store_stage(st, sm, buf ^ 1);
-    __syncthreads();
+    // keep the schedule interleaved: 8 vector ops (one block's rescale), then
+    // one matrix instruction, 16 times
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    cur = nxt;
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rescale_block(acc[i][j], P[i][j], cur, i, j);
+
+  // the group sums carry the factor 256 of the widened operands: remove it (exact)
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] *= 0.00390625f;
 
   // low-rank up-projection on the same accumulators: acc += fp16(D) . L2
   for (int rc = 0; rc < R; rc += 32) {
@@ -270,7 +309,8 @@ __global__ __launch_bounds__(64) void debug_partials_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int64_t mr = rb + 4 * q + e;                          // output row inside the slice
-      if (mr < rows && nb < N) P[(mr * N + nb) * G + g] = r[e] >> 8;   // 256 P -> P, exact
+      const int pe = r[e];
+      if (mr < rows && nb < N) P[(mr * N + nb) * G + g] = pe >> 8;   // 256 P -> P, exact
     }
   }
 }
