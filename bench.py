@@ -44,8 +44,8 @@ def k2_source_hash() -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=1, help="workload index (1 = DiT QKV)")
     ap.add_argument("--layer", type=int, default=0)
     ap.add_argument("--sets", type=int, default=4, help="rotating buffer sets (cold MALL)")

@@ -51,8 +51,8 @@ static_assert(BM == BN && BM == 128 && NT == 2 * BM,
 struct Smem {
   v4i a[2][BM / 16][64];            // widened A operands of one group [buf][row block][lane]
   v4i b[2][BN / 16][64];            // widened B operands
-  uint16_t sx[2][BM];               // activation scales [buf][row]
-  uint16_t sw[2][2][16][4];         // weight scales [buf][col/64][col%16][(col%64)/16]
+  uint16_t sx[2][2][16][4];         // activation scales [buf][row/64][row%16][(row%64)/16]
+  uint16_t sw[2][BN];               // weight scales [buf][col]
 };
 
 // One group's slice of the tile, staged in registers between its global load
@@ -74,22 +74,28 @@ __device__ __forceinline__ void load_group(Stage& r, const uint8_t* __restrict__
   r.sc = sc_row[g];
 }
 
+// LDS slot of operand entry e = q*16 + row: entries of chunks q = 2, 3 are
+// swapped in blocks of 4 (XOR 12). The two threads of a row store chunks q and
+// q+2 side by side; without the swap those two 16-byte stores fall on the same
+// banks. Reads stay one permutation of 8 (or 16) consecutive slots per lane
+// group, so they remain conflict-free.
+__device__ __forceinline__ int swz(int e) { return e ^ ((e >> 5) * 12); }
+
 // Widen and store: the 16 bytes of row t/2 hold chunks q = 2h, 2h+1 (codes
 // 16q .. 16q+15), which go to lane q*16 + row%16 of row block row/16.
 __device__ __forceinline__ void store_group(const Stage& r, Smem& sm, int buf) {
   const int t = threadIdx.x;
   const int row = t >> 1, h = t & 1;
   const int rb = row >> 4, rr = row & 15;
-  sm.a[buf][rb][(2 * h) * 16 + rr] = widen_codes(make_uint2(r.a.x, r.a.y));
-  sm.a[buf][rb][(2 * h + 1) * 16 + rr] = widen_codes(make_uint2(r.a.z, r.a.w));
-  sm.b[buf][rb][(2 * h) * 16 + rr] = widen_codes(make_uint2(r.b.x, r.b.y));
-  sm.b[buf][rb][(2 * h + 1) * 16 + rr] = widen_codes(make_uint2(r.b.z, r.b.w));
-  if (t < BM) {
-    sm.sx[buf][t] = r.sc;
-  } else {
-    const int c = t - BM;
-    sm.sw[buf][c >> 6][c & 15][(c >> 4) & 3] = r.sc;
-  }
+  const int e0 = swz((2 * h) * 16 + rr), e1 = swz((2 * h + 1) * 16 + rr);
+  sm.a[buf][rb][e0] = widen_codes(make_uint2(r.a.x, r.a.y));
+  sm.a[buf][rb][e1] = widen_codes(make_uint2(r.a.z, r.a.w));
+  sm.b[buf][rb][e0] = widen_codes(make_uint2(r.b.x, r.b.y));
+  sm.b[buf][rb][e1] = widen_codes(make_uint2(r.b.z, r.b.w));
+  if (t < BM)
+    sm.sx[buf][t >> 6][t & 15][(t >> 4) & 3] = r.sc;
+  else
+    sm.sw[buf][t - BM] = r.sc;
 }
 
 // Operands and scales of one group for one wave.
@@ -97,32 +103,33 @@ struct Frags {
   v4i A[4], B[4];
 };
 struct Scales {
-  uint2 sxp[4];                     // fp16 activation scales of the lane's 4 rows, per row block
-  float sw[4];                      // weight scale of the lane's column, per column block
-  float be[4];                      // -12582912 * sw
+  float sx[4];                      // activation scale of the lane's row, per row block
+  float be[4];                      // -12582912 * sx
+  uint2 swp[4];                     // fp16 weight scales of the lane's 4 columns, per column block
 };
 
 __device__ __forceinline__ void read_group(Frags& f, Scales& sc, const Smem& sm, int buf, int wm,
                                            int wn, int lane) {
   const int q = lane >> 4, rl = lane & 15;
+  const int sl = swz(lane);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.A[i] = sm.a[buf][wm * 4 + i][lane];
+  for (int i = 0; i < 4; ++i) f.A[i] = sm.a[buf][wm * 4 + i][sl];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.B[j] = sm.b[buf][wn * 4 + j][lane];
+  for (int j = 0; j < 4; ++j) f.B[j] = sm.b[buf][wn * 4 + j][sl];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    sc.sxp[i] = *reinterpret_cast<const uint2*>(&sm.sx[buf][wm * 64 + i * 16 + 4 * q]);
-  const uint2 swp = *reinterpret_cast<const uint2*>(&sm.sw[buf][wn][rl][0]);
-  sc.sw[0] = h2f(static_cast<uint16_t>(swp.x & 0xFFFFu));
-  sc.sw[1] = h2f(static_cast<uint16_t>(swp.x >> 16));
-  sc.sw[2] = h2f(static_cast<uint16_t>(swp.y & 0xFFFFu));
-  sc.sw[3] = h2f(static_cast<uint16_t>(swp.y >> 16));
+  for (int j = 0; j < 4; ++j)
+    sc.swp[j] = *reinterpret_cast<const uint2*>(&sm.sw[buf][wn * 64 + j * 16 + 4 * q]);
+  const uint2 sxp = *reinterpret_cast<const uint2*>(&sm.sx[buf][wm][rl][0]);
+  sc.sx[0] = h2f(static_cast<uint16_t>(sxp.x & 0xFFFFu));
+  sc.sx[1] = h2f(static_cast<uint16_t>(sxp.x >> 16));
+  sc.sx[2] = h2f(static_cast<uint16_t>(sxp.y & 0xFFFFu));
+  sc.sx[3] = h2f(static_cast<uint16_t>(sxp.y >> 16));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) sc.be[j] = sc.sw[j] * -kMagicF;     // exact: 3 * 2^22 * s_w
+  for (int i = 0; i < 4; ++i) sc.be[i] = sc.sx[i] * -kMagicF;     // exact: 3 * 2^22 * s_x
 }
 
-__device__ __forceinline__ float sx_of(const Scales& sc, int i, int e) {
-  const uint32_t w = (e < 2) ? sc.sxp[i].x : sc.sxp[i].y;
+__device__ __forceinline__ float sw_of(const Scales& sc, int j, int e) {
+  const uint32_t w = (e < 2) ? sc.swp[j].x : sc.swp[j].y;
   return h2f(static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xFFFFu)));
 }
 
@@ -133,9 +140,31 @@ __device__ __forceinline__ void rescale_block(v4f& acc, const v4i& p, const Scal
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int pe = p[e];                     // scalar copy: see as_float()
-    const float t = __builtin_fmaf(as_float(pe), sc.sw[j], sc.be[j]);
-    acc[e] = __builtin_fmaf(t, sx_of(sc, i, e), acc[e]);
+    const float t = __builtin_fmaf(as_float(pe), sc.sx[i], sc.be[i]);
+    acc[e] = __builtin_fmaf(t, sw_of(sc, j, e), acc[e]);
   }
+}
+
+// Tile order. Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs
+// on XCD b % 8), and each XCD has its own L2. Renumber so that every XCD works
+// through one contiguous run of tiles, and walk the tiles in bands of
+// kBandM tile rows, column by column: the tiles an XCD holds at one time then
+// share a few A row panels and B column panels, which stay in its L2.
+constexpr int kXcds = 8;
+constexpr int kBandM = 8;
+
+__device__ __forceinline__ void tile_of_block(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  const int per = T / kXcds, rem = T % kXcds;
+  const int x = b % kXcds, local = b / kXcds;
+  const int t = x * per + (x < rem ? x : rem) + local;      // a bijection of [0, T)
+  const int band_tiles = kBandM * tiles_n;
+  const int band = t / band_tiles;
+  const int first_m = band * kBandM;
+  const int rows = tiles_m - first_m < kBandM ? tiles_m - first_m : kBandM;
+  const int r = t - band * band_tiles;
+  tm = first_m + r % rows;
+  tn = r / rows;
 }
 
 template <bool Y_F16>
@@ -144,14 +173,15 @@ __global__ __launch_bounds__(NT, 2) void k2_w4a4_kernel(
     const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales,
     const float* __restrict__ D, const uint16_t* __restrict__ L2t, int R,
     const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N, int64_t K,
-    int64_t ldy, int tiles_n) {
+    int64_t ldy, int tiles_m, int tiles_n) {
   __shared__ Smem sm;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rl = lane & 15, q = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
-  const int tile = blockIdx.x;
-  const int64_t m0 = static_cast<int64_t>(tile / tiles_n) * BM;
-  const int64_t n0 = static_cast<int64_t>(tile % tiles_n) * BN;
+  int tm, tn;
+  tile_of_block(static_cast<int>(blockIdx.x), tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = static_cast<int64_t>(tm) * BM;
+  const int64_t n0 = static_cast<int64_t>(tn) * BN;
   const int64_t G = K / kGroup;
   const v4i seed = v4i{kMagicSeed, kMagicSeed, kMagicSeed, kMagicSeed};
 
@@ -194,7 +224,7 @@ __global__ __launch_bounds__(NT, 2) void k2_w4a4_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) P[i][j] = mfma_i8_16x16x64(f.A[i], f.B[j], seed);
+    for (int j = 0; j < 4; ++j) P[i][j] = mfma_i8_16x16x64(f.B[j], f.A[i], seed);
 
   for (int64_t g = 0; g + 1 < G; ++g) {
     const int buf = static_cast<int>(g & 1);
@@ -209,7 +239,7 @@ __global__ __launch_bounds__(NT, 2) void k2_w4a4_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         rescale_block(acc[i][j], P[i][j], cur, i, j);
-        P[i][j] = mfma_i8_16x16x64(f.A[i], f.B[j], seed);
+        P[i][j] = mfma_i8_16x16x64(f.B[j], f.A[i], seed);
       }
     }
     // keep the schedule interleaved: 8 vector ops (one block's rescale), then
@@ -262,26 +292,51 @@ __global__ __launch_bounds__(NT, 2) void k2_w4a4_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16_16x16x32(Al[i], Bl[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16_16x16x32(Bl[j], Al[i], acc[i][j]);
   }
 
-  // bias and store; lane holds rows 4q+e of column rl in each 16 x 16 block
+  // bias and store; lane holds columns 4q .. 4q+3 of row rl in each 16 x 16
+  // block, written as one 8-byte (fp16) or 16-byte (fp32) store when Y's
+  // address and row stride allow it
+  constexpr int ES = Y_F16 ? 2 : 4;
+  const bool vec = ((reinterpret_cast<uintptr_t>(Y) | static_cast<uintptr_t>(ldy * ES)) %
+                    (4 * ES)) == 0;
+  float bv[4][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = n0 + wn * 64 + j * 16 + rl;
-    if (n >= N) continue;
-    const float b = bias ? bias[n] : 0.f;
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int e = 0; e < 4; ++e) {
+      const int64_t n = n0 + wn * 64 + j * 16 + 4 * q + e;
+      bv[j][e] = (bias != nullptr && n < N) ? bias[n] : 0.f;
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t m = m0 + wm * 64 + i * 16 + 4 * q + e;
-        if (m < M) {
-          const float v = acc[i][j][e] + b;
-          if constexpr (Y_F16)
-            static_cast<_Float16*>(Y)[m * ldy + n] = static_cast<_Float16>(v);
-          else
-            static_cast<float*>(Y)[m * ldy + n] = v;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + wm * 64 + i * 16 + rl;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + wn * 64 + j * 16 + 4 * q;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e] + bv[j][e];
+      if (vec && n + 3 < N) {
+        if constexpr (Y_F16) {
+          const uint32_t lo = static_cast<uint32_t>(f2h(v[0])) | (static_cast<uint32_t>(f2h(v[1])) << 16);
+          const uint32_t hi = static_cast<uint32_t>(f2h(v[2])) | (static_cast<uint32_t>(f2h(v[3])) << 16);
+          *reinterpret_cast<uint2*>(static_cast<_Float16*>(Y) + m * ldy + n) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(Y) + m * ldy + n) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (n + e < N) {
+            if constexpr (Y_F16)
+              static_cast<_Float16*>(Y)[m * ldy + n + e] = static_cast<_Float16>(v[e]);
+            else
+              static_cast<float*>(Y)[m * ldy + n + e] = v[e];
+          }
         }
       }
     }
@@ -326,10 +381,10 @@ hipError_t launch_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uin
   const dim3 grid(static_cast<unsigned>(tiles_m) * tiles_n), block(NT);
   if (y_f16)
     hipLaunchKernelGGL(k2_w4a4_kernel<true>, grid, block, 0, stream, a_codes, a_scales, w_codes,
-                       w_scales, D, L2t, R, bias, Y, M, N, K, ldy, tiles_n);
+                       w_scales, D, L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n);
   else
     hipLaunchKernelGGL(k2_w4a4_kernel<false>, grid, block, 0, stream, a_codes, a_scales, w_codes,
-                       w_scales, D, L2t, R, bias, Y, M, N, K, ldy, tiles_n);
+                       w_scales, D, L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
