@@ -72,7 +72,7 @@ class Sets:
         for _ in range(n):
             s = dict(
                 X=d(X), inv=d(prep.inv_smooth),
-                L1t=d(prep.L1t) if self.R else None, L2t=d(prep.L2t) if self.R else None,
+                L1p=d(prep.L1p) if self.R else None, L2t=d(prep.L2t) if self.R else None,
                 wc=d(prep.w_codes), ws=d(prep.w_scales), b=None if bias is None else d(bias),
                 ac=torch.empty((M, K // 2), dtype=torch.uint8, device="cuda"),
                 asc=torch.empty((M, G), dtype=torch.int16, device="cuda"),
@@ -83,7 +83,7 @@ class Sets:
 
     def k1(self, i):
         s = self.sets[i % len(self.sets)]
-        self.sq.quantize_act_lowrank_down(s["X"], s["inv"], s["L1t"], self.R, s["ac"], s["asc"],
+        self.sq.quantize_act_lowrank_down(s["X"], s["inv"], s["L1p"], self.R, s["ac"], s["asc"],
                                           s["D"] if self.R else None)
 
     def k2(self, i):

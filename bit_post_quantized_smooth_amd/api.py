@@ -71,6 +71,20 @@ class Prepared:
         """R x N fp16 (a copy)."""
         return np.ascontiguousarray(self.L2t.view(np.float16).T)
 
+    @property
+    def L1p(self) -> Optional[np.ndarray]:
+        """L1 packed in the order the device pre-kernel reads it (None at rank 0)."""
+        return pack_lowrank_down(self.L1t) if self.rank else None
+
+
+def pack_lowrank_down(L1t: np.ndarray) -> np.ndarray:
+    """svdq_pack_lowrank_down: R x K fp16 bits -> R*K fp16 bits in operand order."""
+    L1t = _c(L1t, np.uint16)
+    R, K = L1t.shape
+    out = np.empty(R * K, dtype=np.uint16)
+    check(lib.svdq_pack_lowrank_down(_np_ptr(L1t), K, R, _np_ptr(out)), "svdq_pack_lowrank_down")
+    return out
+
 
 def prepare_weights(W: np.ndarray, lam: np.ndarray, rank: int, want_sigma: bool = False) -> Prepared:
     W = _c(W, np.float32)
@@ -132,10 +146,10 @@ def _dt(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def quantize_act_lowrank_down(X, inv_smooth, L1t, R: int, a_codes, a_scales, D, stream=None):
+def quantize_act_lowrank_down(X, inv_smooth, L1p, R: int, a_codes, a_scales, D, stream=None):
     M, K = X.shape
     check(lib.svdq_quantize_act_lowrank_down(_tp(X), _dt(X), M, K, X.stride(0), _tp(inv_smooth),
-                                             _tp(L1t) if R else None, R, GROUP, _tp(a_codes),
+                                             _tp(L1p) if R else None, R, GROUP, _tp(a_codes),
                                              _tp(a_scales), _tp(D) if R else None, _stream(stream)),
           "svdq_quantize_act_lowrank_down")
 
@@ -153,10 +167,10 @@ def linear_workspace_bytes(M: int, K: int, R: int) -> int:
     return int(lib.svdq_linear_workspace_bytes(M, K, R, GROUP))
 
 
-def linear(X, inv_smooth, L1t, L2t, R: int, w_codes, w_scales, bias, Y, ws, stream=None):
+def linear(X, inv_smooth, L1p, L2t, R: int, w_codes, w_scales, bias, Y, ws, stream=None):
     M, K = X.shape
     N = Y.shape[1]
-    check(lib.svdq_linear(_tp(X), _dt(X), X.stride(0), _tp(inv_smooth), _tp(L1t) if R else None,
+    check(lib.svdq_linear(_tp(X), _dt(X), X.stride(0), _tp(inv_smooth), _tp(L1p) if R else None,
                           _tp(L2t) if R else None, R, _tp(w_codes), _tp(w_scales), _tp(bias), _tp(Y),
                           _dt(Y), Y.stride(0), M, K, N, GROUP, _tp(ws), ws.numel() * ws.element_size(),
                           _stream(stream)), "svdq_linear")
@@ -185,8 +199,8 @@ class Linear:
         self.K, self.N, self.R = prep.K, prep.N, prep.rank
         dev = torch.device(device)
         self.inv_smooth = torch.from_numpy(prep.inv_smooth).to(dev)
-        self.L1t = torch.from_numpy(prep.L1t.view(np.int16)).to(dev)
-        self.L2t = torch.from_numpy(prep.L2t.view(np.int16)).to(dev)
+        self.L1p = torch.from_numpy(prep.L1p.view(np.int16)).to(dev) if self.R else None
+        self.L2t = torch.from_numpy(prep.L2t.view(np.int16)).to(dev) if self.R else None
         self.w_codes = torch.from_numpy(prep.w_codes).to(dev)
         self.w_scales = torch.from_numpy(prep.w_scales.view(np.int16)).to(dev)
         self.bias = None if bias is None else torch.from_numpy(_c(bias, np.float32)).to(dev)
@@ -206,6 +220,6 @@ class Linear:
         M = X.shape[0]
         if Y is None:
             Y = torch.empty((M, self.N), dtype=self.out_dtype or X.dtype, device=self.device)
-        linear(X, self.inv_smooth, self.L1t, self.L2t, self.R, self.w_codes, self.w_scales,
+        linear(X, self.inv_smooth, self.L1p, self.L2t, self.R, self.w_codes, self.w_scales,
                self.bias, Y, self.workspace(M), stream)
         return Y

@@ -58,10 +58,10 @@ int check_common(int64_t M, int64_t K, int32_t R, int32_t group, const char* fn)
 }
 
 int validate_k1(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
-                const float* inv_smooth, const uint16_t* L1t, int32_t R, int32_t group,
+                const float* inv_smooth, const uint16_t* L1p, int32_t R, int32_t group,
                 const uint8_t* a_codes, const uint16_t* a_scales, const float* D) {
   const char* fn = "svdq_quantize_act_lowrank_down";
-  if (!X || !inv_smooth || !a_codes || !a_scales || (R > 0 && (!L1t || !D))) {
+  if (!X || !inv_smooth || !a_codes || !a_scales || (R > 0 && (!L1p || !D))) {
     set_error("%s: null pointer", fn);
     return SVDQ_ERR_NULL;
   }
@@ -75,7 +75,7 @@ int validate_k1(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
     return SVDQ_ERR_SHAPE;
   }
   if (!aligned16(X) || !aligned16(inv_smooth) || !aligned16(a_codes) || !aligned16(a_scales) ||
-      (R > 0 && (!aligned16(L1t) || !aligned16(D))) || (ldx * esize(x_dtype)) % 16 != 0) {
+      (R > 0 && (!aligned16(L1p) || !aligned16(D))) || (ldx * esize(x_dtype)) % 16 != 0) {
     set_error("%s: device pointers and the X row stride must be 16-byte aligned", fn);
     return SVDQ_ERR_ALIGN;
   }
@@ -130,14 +130,14 @@ WsLayout ws_layout(int64_t M, int64_t K, int32_t R) {
 extern "C" {
 
 int svdq_quantize_act_lowrank_down(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
-                                   const float* inv_smooth, const uint16_t* L1t, int32_t R,
+                                   const float* inv_smooth, const uint16_t* L1p, int32_t R,
                                    int32_t group, uint8_t* a_codes, uint16_t* a_scales, float* D,
                                    hipStream_t stream) {
   clear_error();
-  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1t, R, group, a_codes, a_scales, D))
+  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, group, a_codes, a_scales, D))
     return s;
   if (int s = device_ready()) return s;
-  return check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1t, R, a_codes,
+  return check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1p, R, a_codes,
                              a_scales, D, stream),
                    "svdq_quantize_act_lowrank_down launch");
 }
@@ -163,7 +163,7 @@ size_t svdq_linear_workspace_bytes(int64_t M, int64_t K, int32_t R, int32_t grou
 }
 
 int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
-                const uint16_t* L1t, const uint16_t* L2t, int32_t R, const uint8_t* w_codes,
+                const uint16_t* L1p, const uint16_t* L2t, int32_t R, const uint8_t* w_codes,
                 const uint16_t* w_scales, const float* bias, void* Y, int y_dtype, int64_t ldy,
                 int64_t M, int64_t K, int64_t N, int32_t group, void* ws, size_t ws_bytes,
                 hipStream_t stream) {
@@ -187,13 +187,13 @@ int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth
   uint8_t* a_codes = base + L.codes;
   uint16_t* a_scales = reinterpret_cast<uint16_t*>(base + L.scales);
   float* D = R > 0 ? reinterpret_cast<float*>(base + L.d) : nullptr;
-  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1t, R, group, a_codes, a_scales, D))
+  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, group, a_codes, a_scales, D))
     return s;
   if (int s = validate_k2(a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y, y_dtype, M, N,
                           K, ldy, group, fn))
     return s;
   if (int s = device_ready()) return s;
-  if (int s = check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1t, R, a_codes,
+  if (int s = check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1p, R, a_codes,
                                   a_scales, D, stream),
                         "svdq_linear K1 launch"))
     return s;

@@ -8,7 +8,7 @@
 namespace svdq {
 
 hipError_t launch_k1(const void* X, bool x_f16, int64_t M, int64_t K, int64_t ldx,
-                     const float* inv_smooth, const uint16_t* L1t, int R, uint8_t* a_codes,
+                     const float* inv_smooth, const uint16_t* L1p, int R, uint8_t* a_codes,
                      uint16_t* a_scales, float* D, hipStream_t stream);
 
 hipError_t launch_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* w_codes,

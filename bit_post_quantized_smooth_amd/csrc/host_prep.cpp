@@ -342,6 +342,36 @@ int svdq_concat_lora(const uint16_t* L1t, const uint16_t* L2t, int64_t K, int64_
   return SVDQ_OK;
 }
 
+int svdq_pack_lowrank_down(const uint16_t* L1t, int64_t K, int32_t R, uint16_t* L1p) {
+  clear_error();
+  if (!L1t || !L1p) {
+    set_error("svdq_pack_lowrank_down: null pointer");
+    return SVDQ_ERR_NULL;
+  }
+  if (K < SVDQ_GROUP || K % SVDQ_GROUP != 0) {
+    set_error("svdq_pack_lowrank_down: K=%lld is not a positive multiple of %d", (long long)K,
+              SVDQ_GROUP);
+    return SVDQ_ERR_GROUP;
+  }
+  if (R < 16 || R % 16 != 0 || R > SVDQ_MAX_RANK) {
+    set_error("svdq_pack_lowrank_down: R=%d", R);
+    return SVDQ_ERR_RANK;
+  }
+  // operand (g, c, h), lane = q*16 + rl, element j  <-  L1t[c*16 + rl][g*64 + q*16 + h*8 + j]
+  const int64_t G = K / SVDQ_GROUP, ncb = R / 16;
+#pragma omp parallel for schedule(static)
+  for (int64_t g = 0; g < G; ++g)
+    for (int64_t c = 0; c < ncb; ++c)
+      for (int h = 0; h < 2; ++h)
+        for (int lane = 0; lane < 64; ++lane) {
+          const int rl = lane & 15, q = lane >> 4;
+          const uint16_t* src = L1t + (c * 16 + rl) * K + g * SVDQ_GROUP + q * 16 + h * 8;
+          uint16_t* dst = L1p + (((g * ncb + c) * 2 + h) * 64 + lane) * 8;
+          for (int j = 0; j < 8; ++j) dst[j] = src[j];
+        }
+  return SVDQ_OK;
+}
+
 int svdq_abi_version(void) { return SVDQ_ABI_VERSION; }
 
 const char* svdq_status_str(int status) {

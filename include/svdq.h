@@ -39,10 +39,11 @@
  *   - a_codes: M x K/2 bytes, row-major (row m holds token m along K).
  *     w_codes: N x K/2 bytes, row-major (row n holds output column n along K).
  *   - a_scales: M x K/group fp16, w_scales: N x K/group fp16, row-major.
- *   - L1t: R x K fp16 row-major  (the transpose of the K x R factor L1).
- *     L2t: N x R fp16 row-major  (the transpose of the R x N factor L2).
- *     Both are stored contiguous along the dimension they are summed over,
- *     which is what a matrix-core operand lane loads.
+ *   - L1t: R x K fp16 row-major  (the transpose of the K x R factor L1), as
+ *     the host functions produce it; the device side takes it packed in
+ *     operand order (L1p, svdq_pack_lowrank_down).
+ *     L2t: N x R fp16 row-major  (the transpose of the R x N factor L2),
+ *     contiguous along the rank, which is what a matrix-core operand lane loads.
  *   - D: M x R fp32 row-major.  X: M x K row-major with row stride ldx
  *     (elements).  Y: M x N row-major with row stride ldy (elements).
  *
@@ -65,7 +66,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 1
+#define SVDQ_ABI_VERSION 2
 
 /* status codes */
 enum {
@@ -148,13 +149,26 @@ int svdq_concat_lora(const uint16_t* L1t, const uint16_t* L2t, int64_t K, int64_
                      int32_t rank, const float* lambda, const uint16_t* A, const uint16_t* B,
                      int32_t rl, float scale, uint16_t* L1t_out, uint16_t* L2t_out);
 
+/* The low-rank down-projection factor in the order K1 consumes it (a layout,
+ * no arithmetic). K1 feeds fp16(Xhat) to the matrix instruction
+ * v_mfma_f32_16x16x32_f16 as two operands per 64-channel group, lane
+ * l = 16*q + rl holding row rl and channels 16*q + 8*h .. +7 for h = 0, 1.
+ * The matching L1 operands are stored so that each is one contiguous 1 KB
+ * run (64 lanes x 8 fp16):
+ *   L1p[(((g * R/16 + c) * 2 + h) * 64 + 16*q + rl) * 8 + j]
+ *     = L1t[(16*c + rl) * K + 64*g + 16*q + 8*h + j]
+ * for group g < K/64, column block c < R/16, h < 2, q < 4, rl < 16, j < 8.
+ * L1t: R x K fp16 (as written by svdq_prepare_weights / svdq_concat_lora);
+ * L1p: R*K fp16. K % 64 == 0, 16 <= R <= SVDQ_MAX_RANK, R % 16 == 0. */
+int svdq_pack_lowrank_down(const uint16_t* L1t, int64_t K, int32_t R, uint16_t* L1p);
+
 /* ---------------------------------------------------------------------------
  * Device functions: pointers are device memory; the work is enqueued on
  * `stream` (0 = the null stream) and the call returns without waiting. They
  * never allocate device memory and never synchronize.
  * Common constraints: M >= 1, N >= 1, K >= 64 with K % 64 == 0, group == 64,
  * 0 <= R <= SVDQ_MAX_RANK with R % 16 == 0; ldx >= K, ldy >= N.
- * Alignment: X, inv_smooth, L1t, L2t, D, codes and scales 16 bytes, and
+ * Alignment: X, inv_smooth, L1p, L2t, D, codes and scales 16 bytes, and
  * ldx * sizeof(X element) a multiple of 16 bytes (X rows are read in 16-byte
  * vectors); Y and bias only to their element size, any ldy.
  */
@@ -164,9 +178,9 @@ int svdq_concat_lora(const uint16_t* L1t, const uint16_t* L2t, int64_t K, int64_
  *   Xhat = fp32(x * inv_smooth[k]);
  *   a_codes, a_scales = the quantizer over each row's groups of 64;
  *   D = fp16(Xhat) . L1   (fp16 products, fp32 accumulation), D: M x R.
- * With R == 0, L1t and D may be NULL. */
+ * L1p: L1 packed by svdq_pack_lowrank_down. With R == 0, L1p and D may be NULL. */
 int svdq_quantize_act_lowrank_down(const void* X, int x_dtype, int64_t M, int64_t K,
-                                   int64_t ldx, const float* inv_smooth, const uint16_t* L1t,
+                                   int64_t ldx, const float* inv_smooth, const uint16_t* L1p,
                                    int32_t R, int32_t group, uint8_t* a_codes,
                                    uint16_t* a_scales, float* D, hipStream_t stream);
 
@@ -188,9 +202,9 @@ size_t svdq_linear_workspace_bytes(int64_t M, int64_t K, int32_t R, int32_t grou
 
 /* The whole layer: K1 then K2 on `stream`, intermediates in `ws`
  * (>= svdq_linear_workspace_bytes(M, K, R, group) bytes, 256-byte aligned).
- * L1t: R x K, L2t: N x R. */
+ * L1p: packed by svdq_pack_lowrank_down, L2t: N x R. */
 int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
-                const uint16_t* L1t, const uint16_t* L2t, int32_t R, const uint8_t* w_codes,
+                const uint16_t* L1p, const uint16_t* L2t, int32_t R, const uint8_t* w_codes,
                 const uint16_t* w_scales, const float* bias, void* Y, int y_dtype, int64_t ldy,
                 int64_t M, int64_t K, int64_t N, int32_t group, void* ws, size_t ws_bytes,
                 hipStream_t stream);

@@ -58,7 +58,7 @@ class DeviceLayer:
         self.N, self.R = p.N, p.rank
         self.X = dev(X)
         self.inv = dev(p.inv_smooth)
-        self.L1t = dev(p.L1t) if self.R else None
+        self.L1p = dev(p.L1p) if self.R else None
         self.L2t = dev(p.L2t) if self.R else None
         self.wc = dev(p.w_codes)
         self.ws = dev(p.w_scales)
@@ -72,7 +72,7 @@ class DeviceLayer:
 
     def k1(self):
         import bit_post_quantized_smooth_amd as sq
-        sq.quantize_act_lowrank_down(self.X, self.inv, self.L1t, self.R, self.a_codes,
+        sq.quantize_act_lowrank_down(self.X, self.inv, self.L1p, self.R, self.a_codes,
                                      self.a_scales, self.D if self.R else None)
 
     def k2(self):

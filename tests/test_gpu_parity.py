@@ -93,7 +93,7 @@ def test_linear_matches_oracle(spec):
     Y2 = torch.empty_like(d.Y)
     ws_buf = torch.empty(sq.linear_workspace_bytes(L.M, L.K, p.rank), dtype=torch.uint8,
                          device="cuda")
-    sq.linear(d.X, d.inv, d.L1t, d.L2t, p.rank, d.wc, d.ws, d.bias, Y2, ws_buf)
+    sq.linear(d.X, d.inv, d.L1p, d.L2t, p.rank, d.wc, d.ws, d.bias, Y2, ws_buf)
     torch.cuda.synchronize()
     Yg = d.Y.cpu().numpy()
     assert np.array_equal(Yg.view(np.uint8), Y2.cpu().numpy().view(np.uint8))
@@ -114,6 +114,9 @@ EDGE = [
     (64, 1024, 512, 256, "f16", "f16", True),
     (300, 640, 136, 80, "f16", "f16", False),
     (33, 64, 600, 16, "f32", "f16", True),
+    # ranks whose column-block count (7, 9) has no kernel of its own
+    (50, 256, 200, 112, "f16", "f16", True),
+    (40, 384, 150, 144, "f32", "f16", False),
 ]
 
 
@@ -169,7 +172,7 @@ def test_strided_buffers_and_canaries():
     Ybig = torch.full((M + 2, N + 28), -7.0, dtype=torch.float16, device="cuda")
     Y = Ybig[1:M + 1, :N]                     # row stride N + 28 (16-byte multiple)
     wsb = torch.empty(sq.linear_workspace_bytes(M, K, R), dtype=torch.uint8, device="cuda")
-    sq.linear(Xd, dev(p.inv_smooth), dev(p.L1t), dev(p.L2t), R, dev(p.w_codes), dev(p.w_scales),
+    sq.linear(Xd, dev(p.inv_smooth), dev(p.L1p), dev(p.L2t), R, dev(p.w_codes), dev(p.w_scales),
               dev(b), Y, wsb)
     torch.cuda.synchronize()
     Yb = Ybig.cpu().numpy()

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert _lib.abi_version() == 1
+    assert _lib.abi_version() == 2
     for s in range(11):
         assert _lib.status_str(s) and _lib.status_str(s) != "unknown status"
     assert _lib.status_str(99) == "unknown status"
@@ -141,6 +141,24 @@ def test_concat_lora_bit_exact():
         assert np.array_equal(q.w_codes, p.w_codes) and q.rank == r + rl
 
 
+@pytest.mark.parametrize("K,R", [(64, 16), (192, 48), (1024, 112)])
+def test_pack_lowrank_down_is_the_documented_permutation(K, R):
+    """svdq_pack_lowrank_down against the index formula of the header, written
+    here as a reshape: L1t[c*16 + rl, g*64 + q*16 + h*8 + j] goes to operand
+    (g, c, h), lane q*16 + rl, element j."""
+    rng = np.random.default_rng(K + R)
+    L1t = rng.integers(0, 1 << 16, size=(R, K), dtype=np.uint16)
+    got = sq.pack_lowrank_down(L1t)
+    ref = (L1t.reshape(R // 16, 16, K // 64, 4, 2, 8)     # c, rl, g, q, h, j
+              .transpose(2, 0, 4, 3, 1, 5)                 # g, c, h, q, rl, j
+              .reshape(-1))
+    assert got.shape == (R * K,) and np.array_equal(got, ref)
+    # spot check one element by the formula itself
+    g, c, h, q, rl, j = K // 64 - 1, R // 16 - 1, 1, 2, 5, 3
+    idx = (((g * (R // 16) + c) * 2 + h) * 64 + q * 16 + rl) * 8 + j
+    assert got[idx] == L1t[c * 16 + rl, g * 64 + q * 16 + h * 8 + j]
+
+
 def test_host_errors():
     L = _lib.lib
     W = np.zeros((128, 8), dtype=np.float32)
@@ -156,6 +174,10 @@ def test_host_errors():
     assert L.svdq_channel_absmax(bp, 2, 4, 8, 4, bp) == _lib.ERR_SHAPE
     assert L.svdq_concat_lora(None, None, 64, 8, 0, lam.ctypes.data, bp, bp, 0, 1.0, bp, bp) == _lib.ERR_RANK
     assert L.svdq_smoothing_factors(None, bp, 4, 4, bp) == _lib.ERR_NULL
+    assert L.svdq_pack_lowrank_down(None, 64, 16, bp) == _lib.ERR_NULL
+    assert L.svdq_pack_lowrank_down(bp, 96, 16, bp) == _lib.ERR_GROUP
+    assert L.svdq_pack_lowrank_down(bp, 64, 24, bp) == _lib.ERR_RANK
+    assert L.svdq_pack_lowrank_down(bp, 64, 0, bp) == _lib.ERR_RANK
 
 
 # Fake device addresses: never dereferenced because validation rejects the call
