@@ -11,13 +11,14 @@
 //
 // Per-group rescale: the int32 accumulator is seeded with the bit pattern of
 // 1.5*2^23, so the partial reads back as the float f = 12582912 + 256 P. Then
-//     t   = fma(f, s_w, -12582912 s_w)  = 256 P s_w  rounded once (fp32)
-//     acc = fma(t, s_x, acc)
-// i.e. two fp32 ops per output and group, both reading the fp16 scales
-// directly (v_fma_mix_f32); the factor 256 is removed once after the K loop.
-// These two ops per output and group, not the matrix instruction, bound the
-// kernel: one v_mfma_i32_16x16x64_i8 does the integer work of 64 outputs x 1
-// group in about the time of 4 wave-wide fp32 ops.
+//     t   = fma(f, s_x, -12582912 s_x)  = 256 P s_x   (exact: |P| <= 64*49, so
+//                                                       256 P s_x fits in 24 bits)
+//     acc = fma(t, s_w, acc)                            (the one rounding)
+// i.e. two fp32 ops per output and group, the second reading the fp16 weight
+// scale directly (v_fma_mix_f32); the factor 256 is removed once after the K
+// loop. These two ops per output and group, not the matrix instruction, bound
+// the kernel: one v_mfma_i32_16x16x64_i8 does the integer work of 256 outputs
+// x 1 group in about the time of 4 wave-wide fp32 ops.
 //
 // The low-rank branch (the Nunchaku engine fuses it into the low-bit kernel:
 // SVDQuant abstract; the disruptive-concepts.com post, section "Nunchaku:
@@ -25,14 +26,22 @@
 // fp32 accumulators: acc += fp16(D) . L2, then the bias, then one rounding to
 // the output type.
 //
-// Tiling: a 256-thread workgroup computes a 128 x 128 tile of Y; each of its
-// 4 waves owns a 64 x 64 sub-tile (4 x 4 blocks of 16 x 16). The K loop moves
-// 2 groups per stage through double-buffered LDS. The loader widens the codes
-// once, as it stores them, and stores them in operand order: the 16 bytes a
-// lane feeds to the matrix instruction for (row block, group) sit at
-// [group][row block][lane], so each operand is one contiguous, conflict-free
-// 16-byte LDS read per lane. The next group's operands are read while the
-// current group computes.
+// Tiling: a 256-thread workgroup computes a square tile of Y; each of its 4
+// waves owns a WT x WT quarter of it (WT/16 x WT/16 blocks of 16 x 16). The
+// matrix instruction takes the weight fragment as its first operand, so a lane
+// ends up holding 4 consecutive columns of one row of each block, which leave
+// in one 8-byte store. The K loop stages one group at a time through
+// double-buffered LDS; the loader widens the codes once, as it stores them, in
+// operand order: the 16 bytes a lane feeds to the matrix instruction for
+// (row block, group) sit at [buffer][row block][lane], so each operand is one
+// contiguous 16-byte LDS read per lane. The next group's operands are read
+// while the current group computes.
+//
+// Most tiles are 128 x 128 (WT = 64). When the last round of tiles would
+// leave most of the chip idle (fewer leftover tiles than half the resident
+// workgroup slots), the leftover tiles are cut into 64 x 64 tiles (WT = 32) in
+// the same launch, so the tail takes about a quarter of a round. Every output
+// element goes through the same arithmetic in either size.
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -42,37 +51,21 @@ namespace svdq {
 
 namespace {
 
-constexpr int BM = 128;
-constexpr int BN = 128;
 constexpr int NT = 256;             // threads per workgroup
-static_assert(BM == BN && BM == 128 && NT == 2 * BM,
-              "the loader maps thread t to row t/2, 16-byte half t%2 of one group");
 
+template <int WT>
+struct TileCfg {
+  static constexpr int BT = 2 * WT;         // tile edge
+  static constexpr int NB = WT / 16;        // 16 x 16 blocks per wave edge
+};
+
+template <int WT>
 struct Smem {
-  v4i a[2][BM / 16][64];            // widened A operands of one group [buf][row block][lane]
-  v4i b[2][BN / 16][64];            // widened B operands
-  uint16_t sx[2][2][16][4];         // activation scales [buf][row/64][row%16][(row%64)/16]
-  uint16_t sw[2][BN];               // weight scales [buf][col]
+  v4i a[2][2 * WT / 16][64];        // widened A operands of one group [buf][row block][lane]
+  v4i b[2][2 * WT / 16][64];        // widened B operands
+  uint16_t sx[2][2][16][WT / 16];   // activation scales [buf][row/WT][row%16][(row%WT)/16]
+  uint16_t sw[2][2 * WT];           // weight scales [buf][col]
 };
-
-// One group's slice of the tile, staged in registers between its global load
-// and its (widened) store to LDS. Thread t loads 16 bytes of A row m0 + t/2 and
-// of B row n0 + t/2 (half t%2 of the group's 32 bytes) and one scale (A row t
-// for t < 128, else B column t-128). Rows and columns past M or N are clamped
-// to the last one: their results are computed but never stored, so every load
-// is unconditional and in bounds.
-struct Stage {
-  uint4 a, b;                       // 16 bytes of codes of A row t/2 and of B row t/2
-  uint16_t sc;                      // scale: A row t (t < 128) or B column t-128
-};
-
-__device__ __forceinline__ void load_group(Stage& r, const uint8_t* __restrict__ a_row,
-                                           const uint8_t* __restrict__ b_row,
-                                           const uint16_t* __restrict__ sc_row, int64_t g) {
-  r.a = *reinterpret_cast<const uint4*>(a_row + g * kGroupBytes);
-  r.b = *reinterpret_cast<const uint4*>(b_row + g * kGroupBytes);
-  r.sc = sc_row[g];
-}
 
 // LDS slot of operand entry e = q*16 + row: entries of chunks q = 2, 3 are
 // swapped in blocks of 4 (XOR 12). The two threads of a row store chunks q and
@@ -81,62 +74,125 @@ __device__ __forceinline__ void load_group(Stage& r, const uint8_t* __restrict__
 // group, so they remain conflict-free.
 __device__ __forceinline__ int swz(int e) { return e ^ ((e >> 5) * 12); }
 
-// Widen and store: the 16 bytes of row t/2 hold chunks q = 2h, 2h+1 (codes
-// 16q .. 16q+15), which go to lane q*16 + row%16 of row block row/16.
-__device__ __forceinline__ void store_group(const Stage& r, Smem& sm, int buf) {
-  const int t = threadIdx.x;
-  const int row = t >> 1, h = t & 1;
-  const int rb = row >> 4, rr = row & 15;
-  const int e0 = swz((2 * h) * 16 + rr), e1 = swz((2 * h + 1) * 16 + rr);
-  sm.a[buf][rb][e0] = widen_codes(make_uint2(r.a.x, r.a.y));
-  sm.a[buf][rb][e1] = widen_codes(make_uint2(r.a.z, r.a.w));
-  sm.b[buf][rb][e0] = widen_codes(make_uint2(r.b.x, r.b.y));
-  sm.b[buf][rb][e1] = widen_codes(make_uint2(r.b.z, r.b.w));
-  if (t < BM)
-    sm.sx[buf][t >> 6][t & 15][(t >> 4) & 3] = r.sc;
-  else
-    sm.sw[buf][t - BM] = r.sc;
-}
+// One group's slice of the tile, staged in registers between its global load
+// and its widened store to LDS. A group of a tile is 2*BT rows (BT of A, BT of
+// B) of 32 bytes, loaded as 16-byte halves: for BT = 128 thread t loads half
+// t%2 of A row t/2 and of B row t/2; for BT = 64 threads 0..127 load A rows,
+// threads 128..255 B rows. Threads 0..BT-1 also load an A row scale and
+// threads BT..2BT-1 a B column scale (for BT = 64 the others load a scale they
+// do not store). Rows and columns past M or N are clamped to the last one:
+// their results are computed but never stored, so every load is
+// unconditional and in bounds.
+template <int WT>
+struct Loader {
+  static constexpr int BT = TileCfg<WT>::BT;
+  static constexpr int NC = BT == 128 ? 2 : 1;      // 16-byte chunks per thread
+  const uint8_t* row[NC];
+  const uint16_t* sc_row;
+  uint4 c[NC];
+  uint16_t sc;
+
+  __device__ __forceinline__ void init(const uint8_t* a_codes, const uint16_t* a_scales,
+                                       const uint8_t* w_codes, const uint16_t* w_scales,
+                                       int64_t m0, int64_t n0, int64_t M, int64_t N, int64_t K) {
+    const int t = threadIdx.x;
+    const int64_t kb = K / 2, G = K / kGroup;
+    auto clamp_m = [&](int64_t r) { return m0 + r < M ? m0 + r : M - 1; };
+    auto clamp_n = [&](int64_t r) { return n0 + r < N ? n0 + r : N - 1; };
+    if constexpr (BT == 128) {
+      row[0] = a_codes + clamp_m(t >> 1) * kb + 16 * (t & 1);
+      row[1] = w_codes + clamp_n(t >> 1) * kb + 16 * (t & 1);
+    } else {
+      const int r = (t & 127) >> 1;
+      row[0] = (t < 128 ? a_codes + clamp_m(r) * kb : w_codes + clamp_n(r) * kb) + 16 * (t & 1);
+    }
+    const int s = t < 2 * BT ? t : 0;
+    sc_row = s < BT ? a_scales + clamp_m(s) * G : w_scales + clamp_n(s - BT) * G;
+  }
+
+  __device__ __forceinline__ void load(int64_t g) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) c[i] = *reinterpret_cast<const uint4*>(row[i] + g * kGroupBytes);
+    sc = sc_row[g];
+  }
+
+  // Widen and store: the 16 bytes of row r hold chunks q = 2h, 2h+1 (codes
+  // 16q .. 16q+15), which go to lane q*16 + r%16 of row block r/16.
+  __device__ __forceinline__ void store(Smem<WT>& sm, int buf) const {
+    const int t = threadIdx.x;
+    const int h = t & 1;
+    const int r = (BT == 128 ? t : (t & 127)) >> 1;
+    const int rb = r >> 4, rr = r & 15;
+    const int e0 = swz((2 * h) * 16 + rr), e1 = swz((2 * h + 1) * 16 + rr);
+    if constexpr (BT == 128) {
+      sm.a[buf][rb][e0] = widen_codes(make_uint2(c[0].x, c[0].y));
+      sm.a[buf][rb][e1] = widen_codes(make_uint2(c[0].z, c[0].w));
+      sm.b[buf][rb][e0] = widen_codes(make_uint2(c[1].x, c[1].y));
+      sm.b[buf][rb][e1] = widen_codes(make_uint2(c[1].z, c[1].w));
+    } else {
+      v4i(*dst)[64] = t < 128 ? sm.a[buf] : sm.b[buf];
+      dst[rb][e0] = widen_codes(make_uint2(c[0].x, c[0].y));
+      dst[rb][e1] = widen_codes(make_uint2(c[0].z, c[0].w));
+    }
+    if (t < BT)
+      sm.sx[buf][t / WT][t & 15][(t % WT) >> 4] = sc;
+    else if (t < 2 * BT)
+      sm.sw[buf][t - BT] = sc;
+  }
+};
 
 // Operands and scales of one group for one wave.
+template <int NB>
 struct Frags {
-  v4i A[4], B[4];
+  v4i A[NB], B[NB];
 };
+template <int NB>
 struct Scales {
-  float sx[4];                      // activation scale of the lane's row, per row block
-  float be[4];                      // -12582912 * sx
-  uint2 swp[4];                     // fp16 weight scales of the lane's 4 columns, per column block
+  float sx[NB];                     // activation scale of the lane's row, per row block
+  float be[NB];                     // -12582912 * sx
+  uint2 swp[NB];                    // fp16 weight scales of the lane's 4 columns, per column block
 };
 
-__device__ __forceinline__ void read_group(Frags& f, Scales& sc, const Smem& sm, int buf, int wm,
-                                           int wn, int lane) {
+template <int WT>
+__device__ __forceinline__ void read_group(Frags<WT / 16>& f, Scales<WT / 16>& sc,
+                                           const Smem<WT>& sm, int buf, int wm, int wn,
+                                           int lane) {
+  constexpr int NB = WT / 16;
   const int q = lane >> 4, rl = lane & 15;
   const int sl = swz(lane);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.A[i] = sm.a[buf][wm * 4 + i][sl];
+  for (int i = 0; i < NB; ++i) f.A[i] = sm.a[buf][wm * NB + i][sl];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.B[j] = sm.b[buf][wn * 4 + j][sl];
+  for (int j = 0; j < NB; ++j) f.B[j] = sm.b[buf][wn * NB + j][sl];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    sc.swp[j] = *reinterpret_cast<const uint2*>(&sm.sw[buf][wn * 64 + j * 16 + 4 * q]);
-  const uint2 sxp = *reinterpret_cast<const uint2*>(&sm.sx[buf][wm][rl][0]);
-  sc.sx[0] = h2f(static_cast<uint16_t>(sxp.x & 0xFFFFu));
-  sc.sx[1] = h2f(static_cast<uint16_t>(sxp.x >> 16));
-  sc.sx[2] = h2f(static_cast<uint16_t>(sxp.y & 0xFFFFu));
-  sc.sx[3] = h2f(static_cast<uint16_t>(sxp.y >> 16));
+  for (int j = 0; j < NB; ++j)
+    sc.swp[j] = *reinterpret_cast<const uint2*>(&sm.sw[buf][wn * WT + j * 16 + 4 * q]);
+  if constexpr (NB == 4) {
+    const uint2 sxp = *reinterpret_cast<const uint2*>(&sm.sx[buf][wm][rl][0]);
+    sc.sx[0] = h2f(static_cast<uint16_t>(sxp.x & 0xFFFFu));
+    sc.sx[1] = h2f(static_cast<uint16_t>(sxp.x >> 16));
+    sc.sx[2] = h2f(static_cast<uint16_t>(sxp.y & 0xFFFFu));
+    sc.sx[3] = h2f(static_cast<uint16_t>(sxp.y >> 16));
+  } else {
+    const uint32_t sxp = *reinterpret_cast<const uint32_t*>(&sm.sx[buf][wm][rl][0]);
+    sc.sx[0] = h2f(static_cast<uint16_t>(sxp & 0xFFFFu));
+    sc.sx[1] = h2f(static_cast<uint16_t>(sxp >> 16));
+  }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) sc.be[i] = sc.sx[i] * -kMagicF;     // exact: 3 * 2^22 * s_x
+  for (int i = 0; i < NB; ++i) sc.be[i] = sc.sx[i] * -kMagicF;     // exact: 3 * 2^22 * s_x
 }
 
-__device__ __forceinline__ float sw_of(const Scales& sc, int j, int e) {
+template <int NB>
+__device__ __forceinline__ float sw_of(const Scales<NB>& sc, int j, int e) {
   const uint32_t w = (e < 2) ? sc.swp[j].x : sc.swp[j].y;
   return h2f(static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xFFFFu)));
 }
 
 // Rescale of one 16 x 16 block of group g (two fp32 ops per output):
-//   t = (12582912 + 256 P) s_w - 12582912 s_w = 256 P s_w (rounded once); acc += t s_x
-__device__ __forceinline__ void rescale_block(v4f& acc, const v4i& p, const Scales& sc, int i,
-                                              int j) {
+//   t = (12582912 + 256 P) s_x - 12582912 s_x = 256 P s_x (exact); acc += t s_w
+template <int NB>
+__device__ __forceinline__ void rescale_block(v4f& acc, const v4i& p, const Scales<NB>& sc,
+                                              int i, int j) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int pe = p[e];                     // scalar copy: see as_float()
@@ -153,11 +209,13 @@ __device__ __forceinline__ void rescale_block(v4f& acc, const v4i& p, const Scal
 constexpr int kXcds = 8;
 constexpr int kBandM = 8;
 
-__device__ __forceinline__ void tile_of_block(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int T = tiles_m * tiles_n;
+__device__ __forceinline__ int xcd_contiguous(int b, int T) {
   const int per = T / kXcds, rem = T % kXcds;
   const int x = b % kXcds, local = b / kXcds;
-  const int t = x * per + (x < rem ? x : rem) + local;      // a bijection of [0, T)
+  return x * per + (x < rem ? x : rem) + local;             // a bijection of [0, T)
+}
+
+__device__ __forceinline__ void banded_tile(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int band_tiles = kBandM * tiles_n;
   const int band = t / band_tiles;
   const int first_m = band * kBandM;
@@ -167,29 +225,26 @@ __device__ __forceinline__ void tile_of_block(int b, int tiles_m, int tiles_n, i
   tn = r / rows;
 }
 
-template <bool Y_F16>
-__global__ __launch_bounds__(NT, 2) void k2_w4a4_kernel(
-    const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
+// One tile of Y: rows m0 .. m0 + 2*WT - 1, columns n0 .. n0 + 2*WT - 1.
+template <int WT, bool Y_F16>
+__device__ __forceinline__ void gemm_tile(
+    Smem<WT>& sm, const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
     const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales,
     const float* __restrict__ D, const uint16_t* __restrict__ L2t, int R,
     const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N, int64_t K,
-    int64_t ldy, int tiles_m, int tiles_n) {
-  __shared__ Smem sm;
+    int64_t ldy, int64_t m0, int64_t n0) {
+  constexpr int NB = WT / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rl = lane & 15, q = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
-  int tm, tn;
-  tile_of_block(static_cast<int>(blockIdx.x), tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = static_cast<int64_t>(tm) * BM;
-  const int64_t n0 = static_cast<int64_t>(tn) * BN;
   const int64_t G = K / kGroup;
   const v4i seed = v4i{kMagicSeed, kMagicSeed, kMagicSeed, kMagicSeed};
 
-  v4f acc[4][4];
+  v4f acc[NB][NB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // Software pipeline over the 64-channel groups. Iteration g rescales the
   // integer partials P of group g block by block and, right after each block,
@@ -197,79 +252,70 @@ __global__ __launch_bounds__(NT, 2) void k2_w4a4_kernel(
   // matrix core and the vector ALU work side by side within the wave. LDS
   // holds two groups; a thread's registers hold the next group's codes between
   // their global load and their widened store.
-  const int64_t kb = K / 2;
-  const int t = threadIdx.x;
-  const int64_t ma = (m0 + (t >> 1) < M ? m0 + (t >> 1) : M - 1);
-  const int64_t nb = (n0 + (t >> 1) < N ? n0 + (t >> 1) : N - 1);
-  const uint8_t* a_row = a_codes + ma * kb + 16 * (t & 1);
-  const uint8_t* b_row = w_codes + nb * kb + 16 * (t & 1);
-  const int64_t sidx = t < BM ? (m0 + t < M ? m0 + t : M - 1)
-                              : (n0 + (t - BM) < N ? n0 + (t - BM) : N - 1);
-  const uint16_t* sc_row = (t < BM ? a_scales : w_scales) + sidx * G;
-
-  Stage st;
-  load_group(st, a_row, b_row, sc_row, 0);
-  store_group(st, sm, 0);
+  Loader<WT> ld;
+  ld.init(a_codes, a_scales, w_codes, w_scales, m0, n0, M, N, K);
+  ld.load(0);
+  ld.store(sm, 0);
   if (G > 1) {
-    load_group(st, a_row, b_row, sc_row, 1);
-    store_group(st, sm, 1);
+    ld.load(1);
+    ld.store(sm, 1);
   }
-  if (G > 2) load_group(st, a_row, b_row, sc_row, 2);
+  if (G > 2) ld.load(2);
   __syncthreads();
 
-  v4i P[4][4];
-  Frags f;
-  Scales cur, nxt;
-  read_group(f, cur, sm, 0, wm, wn, lane);
+  v4i P[NB][NB];
+  Frags<NB> f;
+  Scales<NB> cur, nxt;
+  read_group<WT>(f, cur, sm, 0, wm, wn, lane);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) P[i][j] = mfma_i8_16x16x64(f.B[j], f.A[i], seed);
+    for (int j = 0; j < NB; ++j) P[i][j] = mfma_i8_16x16x64(f.B[j], f.A[i], seed);
 
   for (int64_t g = 0; g + 1 < G; ++g) {
     const int buf = static_cast<int>(g & 1);
     __syncthreads();                 // all waves are done reading group g's buffer; group g+1 is stored
     if (g + 2 < G) {
-      store_group(st, sm, buf);      // group g+2 replaces group g
-      if (g + 3 < G) load_group(st, a_row, b_row, sc_row, g + 3);
+      ld.store(sm, buf);             // group g+2 replaces group g
+      if (g + 3 < G) ld.load(g + 3);
     }
-    read_group(f, nxt, sm, buf ^ 1, wm, wn, lane);
+    read_group<WT>(f, nxt, sm, buf ^ 1, wm, wn, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NB; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NB; ++j) {
         rescale_block(acc[i][j], P[i][j], cur, i, j);
         P[i][j] = mfma_i8_16x16x64(f.B[j], f.A[i], seed);
       }
     }
     // keep the schedule interleaved: 8 vector ops (one block's rescale), then
-    // one matrix instruction, 16 times
+    // one matrix instruction, for every block
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
+    for (int b = 0; b < NB * NB; ++b) {
       __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
     cur = nxt;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) rescale_block(acc[i][j], P[i][j], cur, i, j);
+    for (int j = 0; j < NB; ++j) rescale_block(acc[i][j], P[i][j], cur, i, j);
 
   // the group sums carry the factor 256 of the widened operands: remove it (exact)
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] *= 0.00390625f;
+    for (int j = 0; j < NB; ++j) acc[i][j] *= 0.00390625f;
 
   // low-rank up-projection on the same accumulators: acc += fp16(D) . L2
   for (int rc = 0; rc < R; rc += 32) {
     const int kk = rc + 8 * q;                       // this lane's 8 rank indices
     const bool kval = kk < R;                        // R % 16 == 0: whole 8-runs are valid or not
-    v8h Al[4], Bl[4];
+    v8h Al[NB], Bl[NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = m0 + wm * 64 + i * 16 + rl;
+    for (int i = 0; i < NB; ++i) {
+      const int64_t m = m0 + wm * WT + i * 16 + rl;
       if (kval && m < M) {
         const float4* dp = reinterpret_cast<const float4*>(D + m * R + kk);
         const float4 u = dp[0], v = dp[1];
@@ -282,17 +328,17 @@ __global__ __launch_bounds__(NT, 2) void k2_w4a4_kernel(
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn * 64 + j * 16 + rl;
+    for (int j = 0; j < NB; ++j) {
+      const int64_t n = n0 + wn * WT + j * 16 + rl;
       if (kval && n < N)
         Bl[j] = *reinterpret_cast<const v8h*>(L2t + n * R + kk);
       else
         Bl[j] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16_16x16x32(Bl[j], Al[i], acc[i][j]);
+      for (int j = 0; j < NB; ++j) acc[i][j] = mfma_f16_16x16x32(Bl[j], Al[i], acc[i][j]);
   }
 
   // bias and store; lane holds columns 4q .. 4q+3 of row rl in each 16 x 16
@@ -301,21 +347,21 @@ __global__ __launch_bounds__(NT, 2) void k2_w4a4_kernel(
   constexpr int ES = Y_F16 ? 2 : 4;
   const bool vec = ((reinterpret_cast<uintptr_t>(Y) | static_cast<uintptr_t>(ldy * ES)) %
                     (4 * ES)) == 0;
-  float bv[4][4];
+  float bv[NB][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int64_t n = n0 + wn * 64 + j * 16 + 4 * q + e;
+      const int64_t n = n0 + wn * WT + j * 16 + 4 * q + e;
       bv[j][e] = (bias != nullptr && n < N) ? bias[n] : 0.f;
     }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + wm * 64 + i * 16 + rl;
+  for (int i = 0; i < NB; ++i) {
+    const int64_t m = m0 + wm * WT + i * 16 + rl;
     if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn * 64 + j * 16 + 4 * q;
+    for (int j = 0; j < NB; ++j) {
+      const int64_t n = n0 + wn * WT + j * 16 + 4 * q;
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e] + bv[j][e];
@@ -340,6 +386,36 @@ __global__ __launch_bounds__(NT, 2) void k2_w4a4_kernel(
         }
       }
     }
+  }
+}
+
+// Workgroups 0 .. n_full-1 take the first n_full 128 x 128 tiles of the banded
+// order; the remaining workgroups take the leftover tiles in quarters.
+template <bool Y_F16>
+__global__ __launch_bounds__(NT, 2) void k2_w4a4_kernel(
+    const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales,
+    const float* __restrict__ D, const uint16_t* __restrict__ L2t, int R,
+    const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N, int64_t K,
+    int64_t ldy, int tiles_m, int tiles_n, int n_full) {
+  __shared__ union {
+    Smem<64> full;
+    Smem<32> quarter;
+  } sm;
+  const int b = static_cast<int>(blockIdx.x);
+  int tm, tn;
+  if (b < n_full) {
+    banded_tile(xcd_contiguous(b, n_full), tiles_m, tiles_n, tm, tn);
+    gemm_tile<64, Y_F16>(sm.full, a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y, M,
+                         N, K, ldy, static_cast<int64_t>(tm) * 128,
+                         static_cast<int64_t>(tn) * 128);
+  } else {
+    const int qb = b - n_full;
+    const int quarter = qb & 3;
+    banded_tile(n_full + (qb >> 2), tiles_m, tiles_n, tm, tn);
+    gemm_tile<32, Y_F16>(sm.quarter, a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y,
+                         M, N, K, ldy, static_cast<int64_t>(tm) * 128 + 64 * (quarter >> 1),
+                         static_cast<int64_t>(tn) * 128 + 64 * (quarter & 1));
   }
 }
 
@@ -370,21 +446,43 @@ __global__ __launch_bounds__(64) void debug_partials_kernel(
   }
 }
 
+// Resident workgroup slots of the device (2 per compute unit), cached per device.
+int resident_slots() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev] = 2 * cus;
+  }
+  return cache[dev];
+}
+
 }  // namespace
 
 hipError_t launch_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* w_codes,
                      const uint16_t* w_scales, const float* D, const uint16_t* L2t, int R,
                      const float* bias, void* Y, bool y_f16, int64_t M, int64_t N, int64_t K,
                      int64_t ldy, hipStream_t stream) {
-  const int tiles_m = static_cast<int>((M + BM - 1) / BM);
-  const int tiles_n = static_cast<int>((N + BN - 1) / BN);
-  const dim3 grid(static_cast<unsigned>(tiles_m) * tiles_n), block(NT);
+  const int tiles_m = static_cast<int>((M + 127) / 128);
+  const int tiles_n = static_cast<int>((N + 127) / 128);
+  const int T = tiles_m * tiles_n;
+  // leftover tiles of the last round; quartered when they would fill less
+  // than half of the resident slots
+  const int S = resident_slots();
+  const int left = T < S ? T : T % S;
+  const int n_quarter_tiles = (left > 0 && 2 * left <= S) ? left : 0;
+  const int n_full = T - n_quarter_tiles;
+  const dim3 grid(static_cast<unsigned>(n_full + 4 * n_quarter_tiles)), block(NT);
   if (y_f16)
     hipLaunchKernelGGL(k2_w4a4_kernel<true>, grid, block, 0, stream, a_codes, a_scales, w_codes,
-                       w_scales, D, L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n);
+                       w_scales, D, L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n, n_full);
   else
     hipLaunchKernelGGL(k2_w4a4_kernel<false>, grid, block, 0, stream, a_codes, a_scales, w_codes,
-                       w_scales, D, L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n);
+                       w_scales, D, L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n, n_full);
   return hipGetLastError();
 }
 
