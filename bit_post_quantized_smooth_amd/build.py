@@ -30,6 +30,11 @@ HOST_SOURCES = {
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # no implicit contraction anywhere: the method fixes its rounding points
+    # (e.g. Xhat = fp32(x * inv), then fp16(Xhat)), and contraction would fuse
+    # that product and its fp16 conversion into one v_fma_mixlo_f16 (a single
+    # rounding). Every FMA the kernels want is written as __builtin_fmaf.
+    "-ffp-contract=off",
     # no packed fp32 (v_pk_fma_f32 and friends) anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # matrix-core results straight into VGPRs: the rescale reads every element

@@ -57,6 +57,10 @@ int check_common(int64_t M, int64_t K, int32_t R, int32_t group, const char* fn)
   return SVDQ_OK;
 }
 
+// Longest X row (elements) the pre-kernel accepts: 16 rows of fp32 stay below
+// 2^31 bytes, so per-lane offsets fit in 32 bits.
+constexpr int64_t kMaxRowElems = int64_t{1} << 25;
+
 int validate_k1(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                 const float* inv_smooth, const uint16_t* L1p, int32_t R, int32_t group,
                 const uint8_t* a_codes, const uint16_t* a_scales, const float* D) {
@@ -72,6 +76,11 @@ int validate_k1(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
   if (int s = check_common(M, K, R, group, fn)) return s;
   if (ldx < K) {
     set_error("%s: ldx=%lld < K=%lld", fn, (long long)ldx, (long long)K);
+    return SVDQ_ERR_SHAPE;
+  }
+  // the kernel addresses 16 rows of X with 32-bit offsets
+  if (ldx > kMaxRowElems) {
+    set_error("%s: ldx=%lld exceeds %lld", fn, (long long)ldx, (long long)kMaxRowElems);
     return SVDQ_ERR_SHAPE;
   }
   if (!aligned16(X) || !aligned16(inv_smooth) || !aligned16(a_codes) || !aligned16(a_scales) ||

@@ -124,6 +124,7 @@ struct GroupIn {
 };
 
 constexpr int kXsStride = kGroup + 8;           // fp16 elements per row of the LDS tile
+constexpr float kInv7 = 0.142857149f;           // fp32(1/7) = 0x3E124925
 
 template <typename XT, int NCB, int NB>
 __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
@@ -136,34 +137,43 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
   __shared__ float dpart[WAVES][16][NCBA * 16];
   __shared__ __attribute__((aligned(16))) uint16_t xs[WAVES][16][kXsStride];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // the wave index is the same in all lanes: keep it (and everything derived
+  // from it: group numbers, group offsets) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int qr = lane >> 2, c4 = lane & 3;         // quantizer map
   const int rl = lane & 15, q = lane >> 4;          // matrix map
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * 16;
-  const int64_t row = row0 + qr;
-  const bool rvalid = row < M;
-  const int64_t lrow = rvalid ? row : M - 1;        // clamped row for loads
-  const int64_t G = K / kGroup;
+  const int nrows = M - row0 < 16 ? static_cast<int>(M - row0) : 16;
+  const bool rvalid = qr < nrows;
+  const uint32_t lq = rvalid ? qr : nrows - 1;      // clamped row of the tile for loads
+  const int G = static_cast<int>(K / kGroup);
   const int ncb = R / 16;                            // real column blocks (<= NCB)
   // this wave's groups are wave, wave+WAVES, ...: n_mine of them
-  const int64_t n_mine = (G > wave) ? (G - wave + WAVES - 1) / WAVES : 0;
+  const int n_mine = (G > wave) ? (G - wave + WAVES - 1) / WAVES : 0;
 
-  const XT* xrow = X + lrow * ldx + c4 * 16;
-  const float* invq = inv_smooth + c4 * 16;
-  const v8h* l1v = reinterpret_cast<const v8h*>(L1p) + lane;
+  // Addresses: a base shared by the workgroup plus a 32-bit per-lane offset
+  // (the host bounds 16 rows of X and of the codes below 2^31 bytes)
+  const XT* xblk = X + row0 * ldx;
+  const uint32_t xoff = lq * static_cast<uint32_t>(ldx) + c4 * 16;
+  const uint32_t ioff = c4 * 16;
+  const v8h* l1b = reinterpret_cast<const v8h*>(L1p);
+  uint8_t* cblk = a_codes + row0 * (K / 2);
+  const uint32_t coff = qr * static_cast<uint32_t>(K / 2) + c4 * 8;
+  uint16_t* sblk = a_scales + row0 * G;
+  const uint32_t soff = qr * static_cast<uint32_t>(G);
 
   // packed operand (g, c, h) of this lane
-  auto l1_operand = [&](int64_t g, int c, int h) -> const v8h* {
+  auto l1_operand = [&](int g, int c, int h) -> const v8h* {
     const int cc = c < ncb ? c : ncb - 1;
-    return l1v + ((g * ncb + cc) * 2 + h) * 64;
+    return l1b + static_cast<int64_t>((g * ncb + cc) * 2 + h) * 64 + lane;
   };
 
-  auto load_group = [&](GroupIn<XT, NCB>& in, int64_t i) {
-    int64_t g = wave + WAVES * i;
+  auto load_group = [&](GroupIn<XT, NCB>& in, int i) {
+    int g = wave + WAVES * i;
     g = g < G ? g : G - 1;
-    const int64_t k0 = g * kGroup;
-    load_raw<XT>(in.x, xrow + k0);
-    const float4* ip = reinterpret_cast<const float4*>(invq + k0);
+    const int k0 = g * kGroup;
+    load_raw<XT>(in.x, xblk + k0 + xoff);
+    const float4* ip = reinterpret_cast<const float4*>(inv_smooth + k0 + ioff);
 #pragma unroll
     for (int j = 0; j < 4; ++j) in.inv[j] = ip[j];
     if constexpr (ring_l1_blocks<NCB>() > 0) {
@@ -183,12 +193,14 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
 #pragma unroll
   for (int b = 0; b < NB; ++b) load_group(ring[b], b);
 
-  for (int64_t i0 = 0; i0 < n_mine; i0 += NB) {
+  for (int i0 = 0; i0 < n_mine; i0 += NB) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int64_t i = i0 + b;
+      const int i = i0 + b;
+      const int g = wave + WAVES * i;
+      uint32_t packed[2] = {0u, 0u};
+      uint16_t s16 = 0;
       if (i < n_mine) {
-        const int64_t g = wave + WAVES * i;
         float xh[16];
         smooth16(ring[b].x, ring[b].inv, xh);
         // group absmax over this lane's 16 values, then across the 4 lanes of the row
@@ -196,32 +208,38 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
 #pragma unroll
         for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(xh[j]));
         a = quad_max(a);
-        const float s32 = fminf(a / 7.0f, 65504.0f);      // correctly rounded division
-        const uint16_t s16 = f2h(s32);
+        // fp32(a / 7), correctly rounded, as one multiply by fp32(1/7) and one
+        // FMA correction (division by a constant known in advance: Brisebarre,
+        // Muller, Raina, IEEE Trans. Computers 2004); for the divisor 7 this is
+        // exact for every non-negative finite fp32 a, which was checked
+        // exhaustively against the IEEE division on the host.
+        const float q7 = a * kInv7;
+        const float s32 = fminf(__builtin_fmaf(__builtin_fmaf(-q7, 7.0f, a), kInv7, q7), 65504.0f);
+        s16 = f2h(s32);
         const float sf = h2f(s16);
         const float inv = (sf == 0.f) ? 0.f : 1.0f / sf;
         // code = clamp(rint(xh * inv), -7, 7): clamping first gives the same
         // result, and adding 1.5 * 2^23 rounds half-to-even to an integer whose
         // low 4 bits are its two's-complement nibble.
-        uint32_t packed[2] = {0u, 0u};
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const float c = __builtin_amdgcn_fmed3f(xh[j] * inv, -7.f, 7.f);
           const uint32_t bits = __builtin_bit_cast(uint32_t, c + kMagicF);
           packed[j >> 3] |= (bits & 0xFu) << (4 * (j & 7));
         }
-        if (rvalid) {
-          *reinterpret_cast<uint2*>(a_codes + row * (K / 2) + g * kGroupBytes + c4 * 8) =
-              make_uint2(packed[0], packed[1]);
-          if (c4 == 0) a_scales[row * G + g] = s16;
-        }
         if constexpr (NCB > 0) {
           // fp16 values to the matrix map through this wave's LDS tile
+          // Xhat is rounded to fp32 first and then to fp16. The empty asm hands
+          // the conversion an opaque fp32 value: otherwise the backend folds
+          // the product and the conversion into one v_fma_mixlo_f16, which
+          // rounds only once and differs in rare double-rounding cases.
           uint32_t h[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            h[j] = static_cast<uint32_t>(f2h(xh[2 * j])) |
-                   (static_cast<uint32_t>(f2h(xh[2 * j + 1])) << 16);
+          for (int j = 0; j < 8; ++j) {
+            float lo = xh[2 * j], hi = xh[2 * j + 1];
+            __asm__ volatile("" : "+v"(lo), "+v"(hi));
+            h[j] = static_cast<uint32_t>(f2h(lo)) | (static_cast<uint32_t>(f2h(hi)) << 16);
+          }
           uint4* wp = reinterpret_cast<uint4*>(&xs[wave][qr][c4 * 16]);
           wp[0] = make_uint4(h[0], h[1], h[2], h[3]);
           wp[1] = make_uint4(h[4], h[5], h[6], h[7]);
@@ -245,6 +263,13 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
           }
         }
       }
+      if (i < n_mine && rvalid) {
+        *reinterpret_cast<uint2*>(cblk + g * kGroupBytes + coff) = make_uint2(packed[0], packed[1]);
+        if (c4 == 0) sblk[g + soff] = s16;
+      }
+      // Refill this slot only after the stores: issued right behind the matrix
+      // instructions that read the slot's L1 operands, the loads corrupted
+      // some of those operands on gfx950 (D off by ~2e-5 relative).
       load_group(ring[b], i + NB);
     }
   }
@@ -272,7 +297,7 @@ hipError_t launch_k1_t(const void* X, int64_t M, int64_t K, int64_t ldx,
                        uint8_t* a_codes, uint16_t* a_scales, float* D, hipStream_t stream) {
   // groups in flight per wave, sized so the ring fits the register budget of
   // two resident workgroups
-  constexpr int NB = (sizeof(XT) == 2 && NCB <= 2) ? 2 : 1;
+  constexpr int NB = 1;
   const dim3 block(64 * k1_waves<NCB>()), grid(static_cast<unsigned>((M + 15) / 16));
   hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB>), grid, block, 0, stream,
                      static_cast<const XT*>(X), M, K, ldx, inv_smooth, L1p, R, a_codes, a_scales,

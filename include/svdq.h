@@ -167,7 +167,7 @@ int svdq_pack_lowrank_down(const uint16_t* L1t, int64_t K, int32_t R, uint16_t* 
  * `stream` (0 = the null stream) and the call returns without waiting. They
  * never allocate device memory and never synchronize.
  * Common constraints: M >= 1, N >= 1, K >= 64 with K % 64 == 0, group == 64,
- * 0 <= R <= SVDQ_MAX_RANK with R % 16 == 0; ldx >= K, ldy >= N.
+ * 0 <= R <= SVDQ_MAX_RANK with R % 16 == 0; K <= ldx <= 2^25, ldy >= N.
  * Alignment: X, inv_smooth, L1p, L2t, D, codes and scales 16 bytes, and
  * ldx * sizeof(X element) a multiple of 16 bytes (X rows are read in 16-byte
  * vectors); Y and bias only to their element size, any ldy.

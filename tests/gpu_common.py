@@ -116,6 +116,64 @@ def oracle_rows(X, inv, p, wc, ws, bias, rows, out_dtype, chunk=16):
     return np.concatenate(Ys, axis=0)
 
 
+def d_stat_bound(xh, L1, K):
+    """Per-element bound on |D_gpu - D| that the pre-kernel must meet: rounding
+    that random-walks over the K/64 accumulating matrix instructions,
+    2^-20 sqrt(K/64) of the envelope |fp16(Xhat)| . |L1| (about 16x the typical
+    error; the worst case K 2^-23 of the envelope is far looser)."""
+    env = np.abs(O.to_f16(xh).astype(np.float64)) @ np.abs(np.asarray(L1, np.float64))
+    return 2.0 ** -20 * np.sqrt(K / 64) * env
+
+
+def oracle_rows_exact(X, inv, p, wc, ws, bias, rows, chunk=16):
+    """For the given rows: the oracle's Y before its final rounding (fp64), the
+    magnitude envelope sum_g |s_x s_w P| + |fp16(D)| . |L2| + |b|, and the
+    largest legitimate change of the low-rank term: where D lies within the
+    pre-kernel's error bound of an fp16 rounding boundary, the device may round
+    it to the neighbouring fp16 value, which moves Y by that step times |L2|."""
+    Ys, envs, jumps = [], [], []
+    K = X.shape[1]
+    L2a = np.abs(np.asarray(p.L2, dtype=np.float64))
+    swa = np.abs(np.asarray(ws, dtype=np.float16).astype(np.float64))
+    for i in range(0, len(rows), chunk):
+        r = rows[i:i + chunk]
+        _, parts = O.linear(X[r], inv, p.L1, p.L2, wc, ws, bias, "f32", return_parts=True)
+        y = parts["acc"] + parts["lr"]
+        sxa = np.abs(np.asarray(parts["a_scales"], dtype=np.float16).astype(np.float64))
+        env = np.einsum("mng,mg,ng->mn", np.abs(parts["P"]).astype(np.float64), sxa, swa,
+                        optimize=True)
+        env += np.abs(O.to_f16(parts["D"]).astype(np.float64)) @ L2a
+        if bias is not None:
+            y = y + np.asarray(bias, dtype=np.float64)[None, :]
+            env += np.abs(np.asarray(bias, dtype=np.float64))[None, :]
+        D = parts["D"]
+        delta = d_stat_bound(parts["xhat"], p.L1, K)
+        step = np.abs(O.to_f16(D + delta).astype(np.float64) - O.to_f16(D - delta).astype(np.float64))
+        Ys.append(y)
+        envs.append(env)
+        jumps.append(step @ L2a)
+    return (np.concatenate(Ys, axis=0), np.concatenate(envs, axis=0),
+            np.concatenate(jumps, axis=0))
+
+
+def assert_y_strict(Yg, Y_exact, env, jump, out_dtype, G, R):
+    """Element-wise bound for a correct kernel: one ulp of the output type (the
+    final rounding, crossing at most one rounding boundary) plus one fp32
+    rounding per group, per 16 ranks of the low-rank sum and a few more, each
+    at most 2^-24 of the envelope, plus the low-rank step where fp16(D) may
+    legitimately round the other way. A corrupted operand or a wrongly rounded
+    intermediate lands far outside this while staying inside 2e-3 of max|Y|."""
+    Yg = np.asarray(Yg, dtype=np.float64)
+    a = np.abs(Y_exact)
+    if out_dtype == "f16":
+        ulp = np.maximum(np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -14))) - 10), 2.0 ** -24)
+    else:
+        ulp = np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -126))) - 23)
+    tol = ulp + (G + R / 16 + 4) * 2.0 ** -24 * env + jump
+    ratio = np.abs(Yg - Y_exact) / tol
+    assert float(ratio.max()) <= 1.0, (int(np.count_nonzero(ratio > 1)), float(ratio.max()))
+
+
 def rel_err(y, ref):
     y = np.asarray(y, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)

@@ -9,7 +9,8 @@ import pytest
 
 import oracle as O
 import workloads as wl
-from gpu_common import (TOL_Y, DeviceLayer, dev, host_u16, layer, oracle_prep, oracle_rows,
+from gpu_common import (TOL_Y, DeviceLayer, assert_y_strict, d_stat_bound, dev, host_u16, layer,
+                        oracle_prep, oracle_rows, oracle_rows_exact,
                         rel_err, sample_rows, torch_mod)
 
 pytestmark = pytest.mark.gpu
@@ -58,6 +59,12 @@ def test_k1_codes_scales_bit_exact(spec):
         tol = _d_tolerance(xh, p.L1, L.K) + 1e-30
         assert np.all(np.abs(Dg - Do) <= tol + 2.0 ** -24 * np.abs(Do))
         assert rel_err(Dg, Do) <= 1e-3
+        # The bound above is the worst case (every fp32 addition rounding the
+        # same way). Rounding that random-walks over the K/64 accumulating
+        # matrix instructions stays near sqrt(K/64) * 2^-24 of the envelope;
+        # 16x that still catches a corrupted operand (seen once at 2e-5).
+        worst = float(np.max(np.abs(Dg - Do) / (d_stat_bound(xh, p.L1, L.K) + 1e-30)))
+        assert worst <= 1.0, worst
 
 
 @pytest.mark.parametrize("spec", SPECS, ids=_ids)
@@ -102,6 +109,8 @@ def test_linear_matches_oracle(spec):
     Yo = oracle_rows(X, inv_o, p, wc, ws, bias, rows, L.y_dtype)
     err = rel_err(Yg[rows], Yo)
     assert err <= TOL_Y, err
+    Ye, env, jump = oracle_rows_exact(X, inv_o, p, wc, ws, bias, rows)
+    assert_y_strict(Yg[rows], Ye, env, jump, L.y_dtype, L.K // 64, p.rank)
 
 
 # small and ragged shapes, compared on every element
@@ -151,6 +160,8 @@ def test_edge_shapes_every_element(case):
     Yo = O.linear(X, inv_o, p.L1, p.L2, wc, ws, bias, ydt)
     err = rel_err(d.Y.cpu().numpy(), Yo)
     assert err <= TOL_Y, err
+    Ye, env, jump = oracle_rows_exact(X, inv_o, p, wc, ws, bias, np.arange(M))
+    assert_y_strict(d.Y.cpu().numpy(), Ye, env, jump, ydt, K // 64, R)
     P = torch.empty((M, N, K // 64), dtype=torch.int32, device="cuda")
     sq.debug_group_partials(d.a_codes, d.wc, M, N, K, 0, M, P)
     torch.cuda.synchronize()

@@ -196,6 +196,8 @@ def test_device_entry_points_reject_bad_arguments():
     assert L.svdq_quantize_act_lowrank_down(A16, 1, 16, 64, 64, A16, A16, 512, 64, A16, A16, A16, None) == _lib.ERR_RANK
     assert L.svdq_quantize_act_lowrank_down(A16, 1, 0, 64, 64, A16, A16, 16, 64, A16, A16, A16, None) == _lib.ERR_SHAPE
     assert L.svdq_quantize_act_lowrank_down(A16, 1, 16, 64, 32, A16, A16, 16, 64, A16, A16, A16, None) == _lib.ERR_SHAPE
+    # rows longer than 2^25 elements would overflow the kernel's 32-bit offsets
+    assert L.svdq_quantize_act_lowrank_down(A16, 1, 16, 64, (1 << 25) + 64, A16, A16, 16, 64, A16, A16, A16, None) == _lib.ERR_SHAPE
     assert L.svdq_quantize_act_lowrank_down(MIS, 1, 16, 64, 64, A16, A16, 16, 64, A16, A16, A16, None) == _lib.ERR_ALIGN
     assert L.svdq_quantize_act_lowrank_down(A16, 1, 16, 64, 68, A16, A16, 16, 64, A16, A16, A16, None) == _lib.ERR_ALIGN
     assert L.svdq_quantize_act_lowrank_down(A16, 1, 16, 64, 64, A16, None, 16, 64, A16, A16, A16, None) == _lib.ERR_NULL
