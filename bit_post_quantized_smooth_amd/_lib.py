@@ -29,7 +29,8 @@ except ImportError:
 lib = C.CDLL(LIB_PATH)
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_RANK, ERR_WORKSPACE, ERR_HIP, \
-    ERR_NO_DEVICE, ERR_INTERNAL, ERR_GROUP = range(11)
+    ERR_NO_DEVICE, ERR_INTERNAL, ERR_GROUP, ERR_ACT = range(12)
+ACT_NONE, ACT_GELU_TANH = 0, 1
 F16, F32 = 1, 2
 GROUP = 64
 MAX_RANK = 256
@@ -51,10 +52,10 @@ _SIGS = {
     "svdq_quantize_act_lowrank_down": (_int, [_p, _int, _i64, _i64, _i64, _p, _p, _i32, _i32,
                                               _p, _p, _p, _p]),
     "svdq_w4a4_gemm_lowrank_up": (_int, [_p, _p, _p, _p, _p, _p, _i32, _p, _p, _int, _i64, _i64,
-                                         _i64, _i64, _i32, _p]),
+                                         _i64, _i64, _i32, _i32, _p]),
     "svdq_linear_workspace_bytes": (C.c_size_t, [_i64, _i64, _i32, _i32]),
     "svdq_linear": (_int, [_p, _int, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _int, _i64, _i64,
-                           _i64, _i64, _i32, _p, C.c_size_t, _p]),
+                           _i64, _i64, _i32, _p, C.c_size_t, _i32, _p]),
     "svdq_debug_group_partials": (_int, [_p, _p, _i64, _i64, _i64, _i32, _i64, _i64, _p, _p]),
     "svdq_gelu_tanh_f16": (_int, [_p, _p, _i64, _p]),
 }

@@ -154,26 +154,36 @@ def quantize_act_lowrank_down(X, inv_smooth, L1p, R: int, a_codes, a_scales, D, 
           "svdq_quantize_act_lowrank_down")
 
 
+def _act(activation) -> int:
+    if activation is None or activation == "none":
+        return _lib.ACT_NONE
+    if activation == "gelu_tanh":
+        return _lib.ACT_GELU_TANH
+    raise ValueError(f"unknown activation {activation!r}")
+
+
 def w4a4_gemm_lowrank_up(a_codes, a_scales, w_codes, w_scales, D, L2t, R: int, bias, Y, K: int,
-                         stream=None):
+                         stream=None, activation=None):
     M, N = Y.shape
     check(lib.svdq_w4a4_gemm_lowrank_up(_tp(a_codes), _tp(a_scales), _tp(w_codes), _tp(w_scales),
                                         _tp(D) if R else None, _tp(L2t) if R else None, R, _tp(bias),
                                         _tp(Y), _dt(Y), M, N, K, Y.stride(0), GROUP,
-                                        _stream(stream)), "svdq_w4a4_gemm_lowrank_up")
+                                        _act(activation), _stream(stream)),
+          "svdq_w4a4_gemm_lowrank_up")
 
 
 def linear_workspace_bytes(M: int, K: int, R: int) -> int:
     return int(lib.svdq_linear_workspace_bytes(M, K, R, GROUP))
 
 
-def linear(X, inv_smooth, L1p, L2t, R: int, w_codes, w_scales, bias, Y, ws, stream=None):
+def linear(X, inv_smooth, L1p, L2t, R: int, w_codes, w_scales, bias, Y, ws, stream=None,
+           activation=None):
     M, K = X.shape
     N = Y.shape[1]
     check(lib.svdq_linear(_tp(X), _dt(X), X.stride(0), _tp(inv_smooth), _tp(L1p) if R else None,
                           _tp(L2t) if R else None, R, _tp(w_codes), _tp(w_scales), _tp(bias), _tp(Y),
                           _dt(Y), Y.stride(0), M, K, N, GROUP, _tp(ws), ws.numel() * ws.element_size(),
-                          _stream(stream)), "svdq_linear")
+                          _act(activation), _stream(stream)), "svdq_linear")
 
 
 def debug_group_partials(a_codes, w_codes, M: int, N: int, K: int, row0: int, rows: int, P,
@@ -190,11 +200,12 @@ class Linear:
     """One prepared SVDQuant layer resident on a device.
 
     ``Linear(prep, bias)(X)`` runs K1 then K2 on the current stream and
-    returns Y (M x N, ``out_dtype``). The workspace is kept between calls and
-    grown when a larger M arrives."""
+    returns Y (M x N, ``out_dtype``), optionally through the fused activation
+    (``"gelu_tanh"``). The workspace is kept between calls and grown when a
+    larger M arrives."""
 
     def __init__(self, prep: Prepared, bias: Optional[np.ndarray] = None, device="cuda",
-                 out_dtype=None):
+                 out_dtype=None, activation=None):
         torch = _torch()
         self.K, self.N, self.R = prep.K, prep.N, prep.rank
         dev = torch.device(device)
@@ -205,6 +216,7 @@ class Linear:
         self.w_scales = torch.from_numpy(prep.w_scales.view(np.int16)).to(dev)
         self.bias = None if bias is None else torch.from_numpy(_c(bias, np.float32)).to(dev)
         self.out_dtype = out_dtype
+        self.activation = activation
         self.device = dev
         self.ws = None
 
@@ -221,5 +233,5 @@ class Linear:
         if Y is None:
             Y = torch.empty((M, self.N), dtype=self.out_dtype or X.dtype, device=self.device)
         linear(X, self.inv_smooth, self.L1p, self.L2t, self.R, self.w_codes, self.w_scales,
-               self.bias, Y, self.workspace(M), stream)
+               self.bias, Y, self.workspace(M), stream, self.activation)
         return Y

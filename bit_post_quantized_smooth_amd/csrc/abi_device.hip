@@ -91,6 +91,14 @@ int validate_k1(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
   return SVDQ_OK;
 }
 
+int check_activation(int32_t activation, const char* fn) {
+  if (activation != SVDQ_ACT_NONE && activation != SVDQ_ACT_GELU_TANH) {
+    set_error("%s: activation %d", fn, activation);
+    return SVDQ_ERR_ACT;
+  }
+  return SVDQ_OK;
+}
+
 int validate_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* w_codes,
                 const uint16_t* w_scales, const float* D, const uint16_t* L2t, int32_t R,
                 const float* bias, const void* Y, int y_dtype, int64_t M, int64_t N, int64_t K,
@@ -155,14 +163,16 @@ int svdq_w4a4_gemm_lowrank_up(const uint8_t* a_codes, const uint16_t* a_scales,
                               const uint8_t* w_codes, const uint16_t* w_scales, const float* D,
                               const uint16_t* L2t, int32_t R, const float* bias, void* Y,
                               int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
-                              int32_t group, hipStream_t stream) {
+                              int32_t group, int32_t activation, hipStream_t stream) {
   clear_error();
+  const char* fn = "svdq_w4a4_gemm_lowrank_up";
   if (int s = validate_k2(a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y, y_dtype, M, N,
-                          K, ldy, group, "svdq_w4a4_gemm_lowrank_up"))
+                          K, ldy, group, fn))
     return s;
+  if (int s = check_activation(activation, fn)) return s;
   if (int s = device_ready()) return s;
   return check_hip(launch_k2(a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y,
-                             y_dtype == SVDQ_F16, M, N, K, ldy, stream),
+                             y_dtype == SVDQ_F16, M, N, K, ldy, activation == SVDQ_ACT_GELU_TANH, stream),
                    "svdq_w4a4_gemm_lowrank_up launch");
 }
 
@@ -175,9 +185,10 @@ int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth
                 const uint16_t* L1p, const uint16_t* L2t, int32_t R, const uint8_t* w_codes,
                 const uint16_t* w_scales, const float* bias, void* Y, int y_dtype, int64_t ldy,
                 int64_t M, int64_t K, int64_t N, int32_t group, void* ws, size_t ws_bytes,
-                hipStream_t stream) {
+                int32_t activation, hipStream_t stream) {
   clear_error();
   const char* fn = "svdq_linear";
+  if (int s = check_activation(activation, fn)) return s;
   if (!ws) {
     set_error("%s: null workspace", fn);
     return SVDQ_ERR_NULL;
@@ -207,7 +218,7 @@ int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth
                         "svdq_linear K1 launch"))
     return s;
   return check_hip(launch_k2(a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y,
-                             y_dtype == SVDQ_F16, M, N, K, ldy, stream),
+                             y_dtype == SVDQ_F16, M, N, K, ldy, activation == SVDQ_ACT_GELU_TANH, stream),
                    "svdq_linear K2 launch");
 }
 

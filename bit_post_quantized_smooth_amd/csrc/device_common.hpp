@@ -66,4 +66,14 @@ __device__ __forceinline__ uint16_t f2h(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));   // v_cvt_f16_f32, RNE
 }
 
+// GELU, tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) in fp32.
+// 0.5 x (1 + tanh(u)) written as x / (1 + exp(-2u)) (the same function:
+// 0.5 (1 + tanh(u)) is the logistic function of 2u). The second form keeps full
+// relative accuracy for large negative x, where 1 + tanh(u) cancels in fp32.
+__device__ __forceinline__ float gelu_tanh_f32(float x) {
+  const float c2 = 1.5957691216057308f;    // 2 sqrt(2/pi)
+  const float u2 = c2 * (x + 0.044715f * x * x * x);
+  return x / (1.0f + expf(-u2));
+}
+
 }  // namespace svdq

@@ -14,7 +14,7 @@ hipError_t launch_k1(const void* X, bool x_f16, int64_t M, int64_t K, int64_t ld
 hipError_t launch_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* w_codes,
                      const uint16_t* w_scales, const float* D, const uint16_t* L2t, int R,
                      const float* bias, void* Y, bool y_f16, int64_t M, int64_t N, int64_t K,
-                     int64_t ldy, hipStream_t stream);
+                     int64_t ldy, bool gelu, hipStream_t stream);
 
 hipError_t launch_debug_partials(const uint8_t* a_codes, const uint8_t* w_codes, int64_t M,
                                  int64_t N, int64_t K, int64_t row0, int64_t rows, int32_t* P,

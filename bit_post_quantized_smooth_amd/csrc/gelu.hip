@@ -12,15 +12,6 @@ namespace svdq {
 
 namespace {
 
-// 0.5 x (1 + tanh(u)) written as x / (1 + exp(-2u)) (the same function:
-// 0.5 (1 + tanh(u)) is the logistic function of 2u). The second form keeps full
-// relative accuracy for large negative x, where 1 + tanh(u) cancels in fp32.
-__device__ __forceinline__ float gelu_tanh_f32(float x) {
-  const float c2 = 1.5957691216057308f;    // 2 sqrt(2/pi)
-  const float u2 = c2 * (x + 0.044715f * x * x * x);
-  return x / (1.0f + expf(-u2));
-}
-
 __global__ __launch_bounds__(256) void gelu_f16_kernel(const uint16_t* __restrict__ x,
                                                        uint16_t* __restrict__ y, int64_t n) {
   const int64_t nvec = n / 8;

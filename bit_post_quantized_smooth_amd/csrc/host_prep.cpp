@@ -387,6 +387,7 @@ const char* svdq_status_str(int status) {
     case SVDQ_ERR_NO_DEVICE: return "no usable GPU";
     case SVDQ_ERR_INTERNAL: return "internal error";
     case SVDQ_ERR_GROUP: return "unsupported group size";
+    case SVDQ_ERR_ACT: return "unknown activation";
     default: return "unknown status";
   }
 }

@@ -23,8 +23,9 @@
 // The low-rank branch (the Nunchaku engine fuses it into the low-bit kernel:
 // SVDQuant abstract; the disruptive-concepts.com post, section "Nunchaku:
 // Fusing Precision and Speed") runs after the K loop as fp16 MFMAs on the same
-// fp32 accumulators: acc += fp16(D) . L2, then the bias, then one rounding to
-// the output type.
+// fp32 accumulators: acc += fp16(D) . L2, then the bias, optionally the GELU
+// of a DiT MLP's first layer (fused so the intermediate is written once), then
+// one rounding to the output type.
 //
 // Tiling: a 256-thread workgroup computes a square tile of Y; each of its 4
 // waves owns a WT x WT quarter of it (WT/16 x WT/16 blocks of 16 x 16). The
@@ -226,7 +227,7 @@ __device__ __forceinline__ void banded_tile(int t, int tiles_m, int tiles_n, int
 }
 
 // One tile of Y: rows m0 .. m0 + 2*WT - 1, columns n0 .. n0 + 2*WT - 1.
-template <int WT, bool Y_F16>
+template <int WT, bool Y_F16, bool GELU>
 __device__ __forceinline__ void gemm_tile(
     Smem<WT>& sm, const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
     const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales,
@@ -364,7 +365,10 @@ __device__ __forceinline__ void gemm_tile(
       const int64_t n = n0 + wn * WT + j * 16 + 4 * q;
       float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e] + bv[j][e];
+      for (int e = 0; e < 4; ++e) {
+        v[e] = acc[i][j][e] + bv[j][e];
+        if constexpr (GELU) v[e] = gelu_tanh_f32(v[e]);
+      }
       if (vec && n + 3 < N) {
         if constexpr (Y_F16) {
           const uint32_t lo = static_cast<uint32_t>(f2h(v[0])) | (static_cast<uint32_t>(f2h(v[1])) << 16);
@@ -391,7 +395,7 @@ __device__ __forceinline__ void gemm_tile(
 
 // Workgroups 0 .. n_full-1 take the first n_full 128 x 128 tiles of the banded
 // order; the remaining workgroups take the leftover tiles in quarters.
-template <bool Y_F16>
+template <bool Y_F16, bool GELU>
 __global__ __launch_bounds__(NT, 2) void k2_w4a4_kernel(
     const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
     const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales,
@@ -406,14 +410,14 @@ __global__ __launch_bounds__(NT, 2) void k2_w4a4_kernel(
   int tm, tn;
   if (b < n_full) {
     banded_tile(xcd_contiguous(b, n_full), tiles_m, tiles_n, tm, tn);
-    gemm_tile<64, Y_F16>(sm.full, a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y, M,
+    gemm_tile<64, Y_F16, GELU>(sm.full, a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y, M,
                          N, K, ldy, static_cast<int64_t>(tm) * 128,
                          static_cast<int64_t>(tn) * 128);
   } else {
     const int qb = b - n_full;
     const int quarter = qb & 3;
     banded_tile(n_full + (qb >> 2), tiles_m, tiles_n, tm, tn);
-    gemm_tile<32, Y_F16>(sm.quarter, a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y,
+    gemm_tile<32, Y_F16, GELU>(sm.quarter, a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y,
                          M, N, K, ldy, static_cast<int64_t>(tm) * 128 + 64 * (quarter >> 1),
                          static_cast<int64_t>(tn) * 128 + 64 * (quarter & 1));
   }
@@ -466,7 +470,7 @@ int resident_slots() {
 hipError_t launch_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* w_codes,
                      const uint16_t* w_scales, const float* D, const uint16_t* L2t, int R,
                      const float* bias, void* Y, bool y_f16, int64_t M, int64_t N, int64_t K,
-                     int64_t ldy, hipStream_t stream) {
+                     int64_t ldy, bool gelu, hipStream_t stream) {
   const int tiles_m = static_cast<int>((M + 127) / 128);
   const int tiles_n = static_cast<int>((N + 127) / 128);
   const int T = tiles_m * tiles_n;
@@ -477,12 +481,14 @@ hipError_t launch_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uin
   const int n_quarter_tiles = (left > 0 && 2 * left <= S) ? left : 0;
   const int n_full = T - n_quarter_tiles;
   const dim3 grid(static_cast<unsigned>(n_full + 4 * n_quarter_tiles)), block(NT);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, a_codes, a_scales, w_codes, w_scales, D,
+                       L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n, n_full);
+  };
   if (y_f16)
-    hipLaunchKernelGGL(k2_w4a4_kernel<true>, grid, block, 0, stream, a_codes, a_scales, w_codes,
-                       w_scales, D, L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n, n_full);
+    gelu ? go(k2_w4a4_kernel<true, true>) : go(k2_w4a4_kernel<true, false>);
   else
-    hipLaunchKernelGGL(k2_w4a4_kernel<false>, grid, block, 0, stream, a_codes, a_scales, w_codes,
-                       w_scales, D, L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n, n_full);
+    gelu ? go(k2_w4a4_kernel<false, true>) : go(k2_w4a4_kernel<false, false>);
   return hipGetLastError();
 }
 

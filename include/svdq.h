@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 2
+#define SVDQ_ABI_VERSION 3
 
 /* status codes */
 enum {
@@ -80,11 +80,18 @@ enum {
   SVDQ_ERR_HIP = 7,        /* a HIP call failed; svdq_last_error() has its message */
   SVDQ_ERR_NO_DEVICE = 8,  /* no usable GPU */
   SVDQ_ERR_INTERNAL = 9,   /* host numerical routine failed (e.g. no convergence) */
-  SVDQ_ERR_GROUP = 10      /* group size other than 64, or K not a multiple of it */
+  SVDQ_ERR_GROUP = 10,     /* group size other than 64, or K not a multiple of it */
+  SVDQ_ERR_ACT = 11        /* unknown activation code */
 };
 
 /* dtype codes for X and Y */
 enum { SVDQ_F16 = 1, SVDQ_F32 = 2 };
+
+/* Activation applied by K2's epilogue to the fp32 result before its one
+ * rounding to the output type. GELU is the tanh form between the two linears
+ * of a DiT MLP (not on the pages: the textbook formula, as in
+ * svdq_gelu_tanh_f16), fused here so the intermediate is written once. */
+enum { SVDQ_ACT_NONE = 0, SVDQ_ACT_GELU_TANH = 1 };
 
 /* The only group size implemented. */
 #define SVDQ_GROUP 64
@@ -189,12 +196,13 @@ int svdq_quantize_act_lowrank_down(const void* X, int x_dtype, int64_t M, int64_
  *   Y[m,n]   = sum_g s_x[m,g] * s_w[n,g] * P[m,n,g]   (fp32)
  *              + sum_r fp16(D[m,r]) * L2[r,n]          (fp16 products, fp32 sum)
  *              + bias[n]                               (bias may be NULL)
- * rounded once to y_dtype. With R == 0, D and L2t may be NULL. */
+ * then the activation (SVDQ_ACT_*) in fp32, rounded once to y_dtype.
+ * With R == 0, D and L2t may be NULL. */
 int svdq_w4a4_gemm_lowrank_up(const uint8_t* a_codes, const uint16_t* a_scales,
                               const uint8_t* w_codes, const uint16_t* w_scales, const float* D,
                               const uint16_t* L2t, int32_t R, const float* bias, void* Y,
                               int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
-                              int32_t group, hipStream_t stream);
+                              int32_t group, int32_t activation, hipStream_t stream);
 
 /* Bytes of workspace svdq_linear needs: a_codes, a_scales and D, each
  * 256-byte aligned inside the workspace. */
@@ -202,12 +210,12 @@ size_t svdq_linear_workspace_bytes(int64_t M, int64_t K, int32_t R, int32_t grou
 
 /* The whole layer: K1 then K2 on `stream`, intermediates in `ws`
  * (>= svdq_linear_workspace_bytes(M, K, R, group) bytes, 256-byte aligned).
- * L1p: packed by svdq_pack_lowrank_down, L2t: N x R. */
+ * L1p: packed by svdq_pack_lowrank_down, L2t: N x R. activation: SVDQ_ACT_*. */
 int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
                 const uint16_t* L1p, const uint16_t* L2t, int32_t R, const uint8_t* w_codes,
                 const uint16_t* w_scales, const float* bias, void* Y, int y_dtype, int64_t ldy,
                 int64_t M, int64_t K, int64_t N, int32_t group, void* ws, size_t ws_bytes,
-                hipStream_t stream);
+                int32_t activation, hipStream_t stream);
 
 /* Test hook: the exact integer partials P[m, n, g] for rows row0 .. row0+rows-1,
  * computed with the same operand unpacking and int8 matrix-core instruction

@@ -268,14 +268,24 @@ def quantize_residual_from_factors(W, lam32, L1, L2, group: int = GROUP):
 
 
 def linear(X, inv_lam32, L1, L2, w_codes, w_scales, bias=None, out_dtype: str = "f16",
-           group: int = GROUP, return_parts: bool = False):
-    """Y = sum_g s_x s_w P + fp16(D).L2 + b, rounded to ``out_dtype``."""
+           group: int = GROUP, return_parts: bool = False, activation=None):
+    """Y = act(sum_g s_x s_w P + fp16(D).L2 + b), rounded once to ``out_dtype``.
+    ``activation``: None or "gelu_tanh" (the GELU of a DiT MLP's first layer,
+    applied to the unrounded sum)."""
     a_codes, a_scales, xh = quantize_activation(X, inv_lam32, group)
     D = down_projection(xh, L1)
     P = group_partials(a_codes, w_codes, group)
     acc = scaled_group_sum(P, a_scales, w_scales)
     lr = lowrank_up(D, L2)
-    Y = finalize(acc, lr, bias, out_dtype)
+    if activation is None:
+        Y = finalize(acc, lr, bias, out_dtype)
+    elif activation == "gelu_tanh":
+        y = np.asarray(acc, dtype=np.float64) + np.asarray(lr, dtype=np.float64)
+        if bias is not None:
+            y = y + np.asarray(bias, dtype=np.float64)[None, :]
+        Y = gelu_tanh_f64(y).astype(np.float16 if out_dtype == "f16" else np.float32)
+    else:
+        raise ValueError(f"unknown activation {activation!r}")
     if return_parts:
         return Y, dict(a_codes=a_codes, a_scales=a_scales, xhat=xh, D=D, P=P, acc=acc, lr=lr)
     return Y
@@ -311,8 +321,12 @@ def concat_lora(L1, L2, lam32, A, B, scale: float = 1.0):
 # pages do not describe it)
 
 
-def gelu_tanh(x) -> np.ndarray:
-    """0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) in fp64, rounded to fp16."""
+def gelu_tanh_f64(x) -> np.ndarray:
+    """0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) in fp64, not rounded."""
     x = np.asarray(x, dtype=np.float64)
-    y = 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
-    return to_f16(y)
+    return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+
+
+def gelu_tanh(x) -> np.ndarray:
+    """The GELU above, rounded to fp16."""
+    return to_f16(gelu_tanh_f64(x))

@@ -467,10 +467,34 @@ def check_gelu(O):
     assert g[0] == 0.0 and g[5] == 20.0 and g[6] == 0.0
 
 
+def check_linear_gelu(O):
+    """The fused activation: GELU of the unrounded layer output, rounded once.
+    Checked against an independent composition: the fp32 layer output, then a
+    pure-Python tanh GELU, rounded to fp16 (double rounding, so at most one
+    fp16 step apart, and equal almost everywhere)."""
+    import workloads as wl
+    L, X, W = wl.layer_inputs(0, 0)
+    b = wl.bias(0, 0, L.N)
+    lam = O.smoothing_factors(O.channel_absmax(X), W)
+    p = O.prepare(W, lam, L.rank)
+    args = (X[:24], p["inv_smooth"], p["L1"], p["L2"], p["w_codes"], p["w_scales"], b)
+    Yg = O.linear(*args, "f16", activation="gelu_tanh").astype(np.float64)
+    Y32 = O.linear(*args, "f32").astype(np.float64)
+    c = math.sqrt(2.0 / math.pi)
+    ref = np.array([[py_f16(0.5 * v * (1.0 + math.tanh(c * (v + 0.044715 * v ** 3)))) for v in row]
+                    for row in Y32])
+    diff = np.abs(Yg - ref)
+    step = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -14))) - 10)
+    assert np.all(diff <= step), float(np.max(diff / step))
+    assert np.mean(diff == 0) > 0.99
+    # and it is not the plain layer: GELU changes the negative outputs
+    assert np.any(np.abs(Yg - O.linear(*args, "f16").astype(np.float64)) > 0.1)
+
+
 ALL_CHECKS = [
     check_fp16_single_rounding, check_golden_quantizer, check_golden_smoothing,
     check_golden_tiny_linear, check_quantizer_bruteforce, check_roundtrip_bound,
     check_invariants, check_pack_roundtrip, check_eym, check_sigma_split, check_full_rank,
     check_reconstruction, check_partials_bruteforce, check_dense_identity, check_lora,
-    check_method_sanity, check_gelu,
+    check_method_sanity, check_gelu, check_linear_gelu,
 ]

@@ -291,6 +291,59 @@ def test_dit_mlp_chain():
     assert rel_err(Yd.cpu().numpy()[rows], Yo) <= TOL_CHAIN
 
 
+def test_fused_gelu_epilogue():
+    """K2 with the GELU of a DiT MLP's first layer fused into its epilogue, on the
+    MLP up-projection (sampled rows): GELU(Y) against the oracle's GELU of the
+    unrounded Y. Besides the 2e-3 bound: one fp16 step of the result, plus the
+    layer's own bound (see assert_y_strict) times GELU's largest slope (< 1.13),
+    plus the fp32 evaluation of GELU itself (a few roundings inside exp's
+    argument, each amplified at most |v|/4)."""
+    torch = torch_mod()
+    L, X, W, lam, p, bias = layer(2, 0, with_bias=True)
+    _, inv_o, wc, ws = oracle_prep(X, W, p, L.rank)
+    d = DeviceLayer(X, p, bias, L.y_dtype)
+    d.k1()
+    import bit_post_quantized_smooth_amd as sq
+    sq.w4a4_gemm_lowrank_up(d.a_codes, d.a_scales, d.wc, d.ws, d.D, d.L2t, d.R, d.bias, d.Y, d.K,
+                            activation="gelu_tanh")
+    torch.cuda.synchronize()
+    Yg = d.Y.cpu().numpy().astype(np.float64)
+    rows = sample_rows(L.M, seed=7)[:40]
+    Go = np.concatenate([O.linear(X[rows[i:i + 8]], inv_o, p.L1, p.L2, wc, ws, bias, "f16",
+                                  activation="gelu_tanh") for i in range(0, len(rows), 8)])
+    assert rel_err(Yg[rows], Go) <= TOL_Y
+    Ye, env, jump = oracle_rows_exact(X, inv_o, p, wc, ws, bias, rows)
+    G = L.K // 64
+    tol_y = (G + p.rank / 16 + 4) * 2.0 ** -24 * env + jump
+    Ge = O.gelu_tanh_f64(Ye)
+    step = np.maximum(np.exp2(np.floor(np.log2(np.maximum(np.abs(Ge), 2.0 ** -14))) - 10), 2.0 ** -24)
+    tol = step + 1.13 * tol_y + 2.0 ** -18 * (1.0 + np.abs(Ye) ** 3)
+    ratio = np.abs(Yg[rows] - Ge) / tol
+    assert float(ratio.max()) <= 1.0, (int(np.count_nonzero(ratio > 1)), float(ratio.max()))
+    assert np.min(Yg[rows]) >= -0.2      # GELU's minimum is about -0.17
+
+
+def test_dit_mlp_chain_fused_gelu():
+    """The MLP chain with the GELU fused into the up-projection's epilogue: the
+    intermediate is written once, in fp16, already activated. Same tolerance as
+    the unfused chain."""
+    import bit_post_quantized_smooth_amd as sq
+    torch = torch_mod()
+    Lu, X, Wu, _, pu, _ = layer(2, 0)
+    Ld, Xd_cal, Wd, _, pd, _ = layer(2, 1)
+    rows = np.arange(0, Lu.M, 97)[:48]
+    _, inv_u, wcu, wsu = oracle_prep(X, Wu, pu, Lu.rank)
+    _, inv_d, wcd, wsd = oracle_prep(Xd_cal, Wd, pd, Ld.rank)
+    Hu = np.concatenate([O.linear(X[rows[i:i + 16]], inv_u, pu.L1, pu.L2, wcu, wsu, None, "f16",
+                                  activation="gelu_tanh") for i in range(0, len(rows), 16)])
+    Yo = oracle_rows(Hu, inv_d, pd, wcd, wsd, None, np.arange(len(rows)), "f16")
+    up = sq.Linear(pu, activation="gelu_tanh")
+    down = sq.Linear(pd)
+    Yd = down(up(dev(X)))
+    torch.cuda.synchronize()
+    assert rel_err(Yd.cpu().numpy()[rows], Yo) <= TOL_CHAIN
+
+
 def test_repeatable_and_any_stream():
     """Same inputs -> same bits, also on a side stream."""
     torch = torch_mod()

@@ -42,8 +42,8 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert _lib.abi_version() == 2
-    for s in range(11):
+    assert _lib.abi_version() == 3
+    for s in range(12):
         assert _lib.status_str(s) and _lib.status_str(s) != "unknown status"
     assert _lib.status_str(99) == "unknown status"
 
@@ -202,7 +202,7 @@ def test_device_entry_points_reject_bad_arguments():
     assert L.svdq_quantize_act_lowrank_down(A16, 1, 16, 64, 68, A16, A16, 16, 64, A16, A16, A16, None) == _lib.ERR_ALIGN
     assert L.svdq_quantize_act_lowrank_down(A16, 1, 16, 64, 64, A16, None, 16, 64, A16, A16, A16, None) == _lib.ERR_NULL
     # K2
-    args = [A16, A16, A16, A16, A16, A16, 16, None, A16, 1, 16, 16, 64, 16, 64, None]
+    args = [A16, A16, A16, A16, A16, A16, 16, None, A16, 1, 16, 16, 64, 16, 64, 0, None]
     bad = list(args); bad[8] = None
     assert L.svdq_w4a4_gemm_lowrank_up(*bad) == _lib.ERR_NULL
     bad = list(args); bad[9] = 5
@@ -217,13 +217,19 @@ def test_device_entry_points_reject_bad_arguments():
     assert L.svdq_w4a4_gemm_lowrank_up(*bad) == _lib.ERR_ALIGN
     bad = list(args); bad[14] = 128
     assert L.svdq_w4a4_gemm_lowrank_up(*bad) == _lib.ERR_GROUP
+    bad = list(args); bad[15] = 7                # activation code
+    assert L.svdq_w4a4_gemm_lowrank_up(*bad) == _lib.ERR_ACT
     # whole layer: workspace
     need = L.svdq_linear_workspace_bytes(16, 64, 16, 64)
     assert need >= 16 * 32 + 16 * 2 + 16 * 16 * 4 and need % 256 == 0
     assert L.svdq_linear_workspace_bytes(16, 60, 16, 64) == 0
-    la = [A16, 1, 64, A16, A16, A16, 16, A16, A16, None, A16, 1, 16, 16, 64, 16, 64, A16, need - 1, None]
+    la = [A16, 1, 64, A16, A16, A16, 16, A16, A16, None, A16, 1, 16, 16, 64, 16, 64, A16, need - 1, 0,
+          None]
     assert L.svdq_linear(*la) == _lib.ERR_WORKSPACE
     la[18] = need
+    la[19] = 2
+    assert L.svdq_linear(*la) == _lib.ERR_ACT
+    la[19] = 1
     la[17] = 0x10080
     assert L.svdq_linear(*la) == _lib.ERR_ALIGN
     # partials hook: slice outside the rows
@@ -245,6 +251,6 @@ def test_device_entry_points_report_no_device():
     L = _lib.lib
     assert L.svdq_quantize_act_lowrank_down(A16, 1, 16, 64, 64, A16, A16, 16, 64, A16, A16, A16, None) == _lib.ERR_NO_DEVICE
     assert _lib.last_error()
-    args = [A16, A16, A16, A16, A16, A16, 16, None, A16, 1, 16, 16, 64, 16, 64, None]
+    args = [A16, A16, A16, A16, A16, A16, 16, None, A16, 1, 16, 16, 64, 16, 64, 0, None]
     assert L.svdq_w4a4_gemm_lowrank_up(*args) == _lib.ERR_NO_DEVICE
     assert L.svdq_gelu_tanh_f16(A16, A16, 8, None) == _lib.ERR_NO_DEVICE

@@ -121,11 +121,26 @@ def mut_clamp_8(mp):
     mp.setattr(R.np, "clip", lambda a, lo, hi: orig_clip(a, -8, 8))
 
 
+def mut_gelu_before_bias(mp):
+    """The fused activation applied to the sum without the bias, bias added after."""
+    orig = _orig("linear")
+
+    def lin(X, inv, L1, L2, wc, ws, bias=None, out_dtype="f16", group=64, return_parts=False,
+            activation=None):
+        if activation != "gelu_tanh" or bias is None:
+            return orig(X, inv, L1, L2, wc, ws, bias, out_dtype, group, return_parts, activation)
+        y = orig(X, inv, L1, L2, wc, ws, None, "f32", group, False, None).astype(np.float64)
+        y = R.gelu_tanh_f64(y) + np.asarray(bias, dtype=np.float64)[None, :]
+        return y.astype(np.float16 if out_dtype == "f16" else np.float32)
+    mp.setattr(R, "linear", lin)
+
+
 MUTATIONS = [mut_scale_div8, mut_ties_away, mut_nibble_order, mut_smoothing_inverted,
              mut_sigma_unsplit, mut_smallest_singulars, mut_residual_sign,
              mut_partials_group_shift, mut_drop_weight_scale, mut_drop_bias,
              mut_down_no_f16, mut_up_no_f16, mut_lora_no_lambda, mut_f16_via_f32,
-             mut_smooth_multiplies_lambda, mut_transposed_weight_groups, mut_clamp_8]
+             mut_smooth_multiplies_lambda, mut_transposed_weight_groups, mut_clamp_8,
+             mut_gelu_before_bias]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
