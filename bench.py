@@ -54,6 +54,11 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain fp32 copy kernel of known size (for PMC scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--mlp", action="store_true",
+                    help="time the DiT MLP pair instead: up-projection with the GELU fused into "
+                         "its epilogue, then the down-projection")
+    ap.add_argument("--unfused-gelu", action="store_true",
+                    help="with --mlp: plain up-projection, then the separate GELU kernel")
     return ap.parse_args()
 
 
@@ -155,6 +160,50 @@ def cpu_baseline(X, W, prep, bias, budget_s):
                        f"({t:.1f} s, numpy fp64, chunks of {chunk} rows)")
 
 
+def mlp_main(args, torch, sq, wl):
+    """Step = the DiT MLP pair on one batch: K1 + K2 (+GELU) of the up-projection
+    4608 x 3072 -> 12288, then K1 + K2 of the down-projection 12288 -> 3072."""
+    (Lu, Xu, Wu), (Ld, _, Wd) = wl.layer_inputs(2, 0), wl.layer_inputs(2, 1)
+    import oracle as O   # input synthesis only: GELU of the seeded pre-activations
+    Xd_cal = O.gelu_tanh(wl.preactivation(2, 1, Ld.M, Ld.K, Ld.x_outlier_frac, Ld.x_outlier_scale))
+    lam_u = sq.smoothing_factors(sq.channel_absmax(Xu), Wu)
+    lam_d = sq.smoothing_factors(sq.channel_absmax(Xd_cal), Wd)
+    up = sq.Linear(sq.prepare_weights(Wu, lam_u, Lu.rank),
+                   activation=None if args.unfused_gelu else "gelu_tanh")
+    down = sq.Linear(sq.prepare_weights(Wd, lam_d, Ld.rank))
+    n = args.sets
+    X = [torch.from_numpy(Xu).to("cuda") for _ in range(n)]
+    H = [torch.empty((Lu.M, Lu.N), dtype=torch.float16, device="cuda") for _ in range(n)]
+    Y = [torch.empty((Ld.M, Ld.N), dtype=torch.float16, device="cuda") for _ in range(n)]
+
+    def step(i):
+        j = i % n
+        up(X[j], H[j])
+        if args.unfused_gelu:
+            sq.gelu_tanh_f16(H[j], H[j])
+        down(H[j], Y[j])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / args.steps
+    ops = 2.0 * Lu.M * Lu.N * Lu.K + 2.0 * Ld.M * Ld.N * Ld.K
+    value = ops / t / 1e12
+    print(json.dumps({
+        "metric": "effective TOPS of the DiT MLP pair (SVDQuant W4A4+rank-32 up, GELU, down)",
+        "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "dit_mlp: X f16 4608x3072 -> 12288 (GELU-tanh) -> 3072, rank 32",
+                   "gelu": "separate kernel" if args.unfused_gelu else "fused into the up epilogue",
+                   "buffer_sets": n},
+        "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -166,6 +215,9 @@ def main():
     import bit_post_quantized_smooth_amd as sq
     import workloads as wl
 
+    if args.mlp:
+        mlp_main(args, torch, sq, wl)
+        return
     cfg = wl.CONFIGS[args.config]
     L = cfg.layers[args.layer]
     Lx, X, W = wl.layer_inputs(args.config, args.layer)
