@@ -330,3 +330,142 @@ def gelu_tanh_f64(x) -> np.ndarray:
 def gelu_tanh(x) -> np.ndarray:
     """The GELU above, rounded to fp16."""
     return to_f16(gelu_tanh_f64(x))
+
+
+# --------------------------------------------------------------------------
+# MXFP4 variant of the 4-bit part.
+#
+# The pages name a 4-bit floating-point variant of the method for the newest
+# hardware of one vendor (taicenter.com news page on SVDQuant, section on
+# hardware co-design for Blackwell GPUs, NVFP4 item); they give no format
+# details. Its counterpart on CDNA4 is the OCP Microscaling format MXFP4 (OCP
+# "Microscaling Formats (MX) Specification" v1.0, sections on the scale and
+# element data types and on conversion): blocks of 32 values share one
+# power-of-two scale (E8M0) and each value is an FP4 E2M1 number.
+# Smoothing, the SVD split and the fp16 low-rank branch are unchanged; X-hat
+# and R are quantized with this block quantizer instead of Q above. Readings:
+#
+# * shared exponent e = floor(log2(max|v|)) - 2 (2 is the largest exponent of
+#   E2M1, whose largest value is 6 = 1.5 * 2^2), clamped to [-127, 127];
+#   stored as the E8M0 byte e + 127; an all-zero block gets e = -127.
+# * each value is v / 2^e rounded to the nearest E2M1 value (0, 0.5, 1, 1.5,
+#   2, 3, 4, 6) with ties to the even encoding and magnitudes above 6
+#   saturated to 6; the sign is kept (negative values that round to 0 give
+#   the code of -0).
+# * the code is the E2M1 bit pattern s e1 e0 m; codes pack two per byte like
+#   the INT4 codes (element 2j in the low nibble). Blocks run along K: along
+#   each token row for X-hat, down K for each output column of R.
+
+MX_BLOCK = 32
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """Value of each 4-bit E2M1 code (bit 3 is the sign)."""
+    c = np.asarray(codes, dtype=np.int64)
+    mag = E2M1_VALUES[c & 7]
+    return np.where(c & 8, -mag, mag)
+
+
+def e2m1_round(x) -> np.ndarray:
+    """Nearest E2M1 code of each x (fp64): ties to the even encoding (even
+    mantissa bit), magnitudes above 6 saturate to 6, sign kept."""
+    x = np.asarray(x, dtype=np.float64)
+    m = np.abs(x)
+    d = np.abs(m[..., None] - E2M1_VALUES)                 # distance to each magnitude
+    cand = d == np.min(d, axis=-1, keepdims=True)          # one or two nearest
+    # two nearest only at a midpoint: take the even encoding (even index)
+    pick_even = cand & (np.arange(8) % 2 == 0)
+    idx = np.where(pick_even.any(-1), np.argmax(pick_even, -1), np.argmax(cand, -1))
+    idx = np.where(m > 6.0, 7, idx)
+    sign = np.signbit(x).astype(np.int64) * 8
+    return (idx + sign).astype(np.uint8)
+
+
+def mx_quantize_blocks(v32, block: int = MX_BLOCK):
+    """MXFP4 quantization of the last axis in blocks of ``block`` values.
+    Returns (codes (..., n) uint8 in 0..15, e8m0 (..., n/block) uint8)."""
+    v = np.asarray(v32, dtype=np.float32)
+    sh = v.shape
+    vb = v.reshape(sh[:-1] + (sh[-1] // block, block)).astype(np.float64)
+    amax = np.max(np.abs(vb), axis=-1)
+    mant, ex = np.frexp(amax)                 # amax = mant * 2^ex, mant in [0.5, 1)
+    e = np.where(amax > 0, ex - 1 - 2, -127)
+    e = np.clip(e, -127, 127)
+    scale = np.ldexp(1.0, e)                  # 2^e (exact in fp64)
+    codes = e2m1_round(vb / scale[..., None])
+    return codes.reshape(sh), (e + 127).astype(np.uint8)
+
+
+def mx_dequantize_blocks(codes, e8m0, block: int = MX_BLOCK) -> np.ndarray:
+    c = np.asarray(codes)
+    sh = c.shape
+    vals = e2m1_decode(c).reshape(sh[:-1] + (sh[-1] // block, block))
+    s = np.ldexp(1.0, np.asarray(e8m0, dtype=np.int64) - 127)
+    return (vals * s[..., None]).reshape(sh)
+
+
+def pack_codes4(codes) -> np.ndarray:
+    """Two 4-bit codes per byte, element 2j in the low nibble."""
+    c = np.asarray(codes, dtype=np.uint8) & 15
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_codes4(b) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (b.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = b & 15
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def mx_quantize_activation(X, inv_lam32):
+    """Xhat rows in MXFP4: packed codes (M x K/2), E8M0 exponents (M x K/32), Xhat."""
+    xh = smooth_activation(X, inv_lam32)
+    codes, e8 = mx_quantize_blocks(xh)
+    return pack_codes4(codes), e8, xh
+
+
+def mx_quantize_residual_from_factors(W, lam32, L1, L2):
+    """R (from the stored fp16 factors, rounded to fp32) in MXFP4 down K for each
+    output column: packed codes (N x K/2), E8M0 exponents (N x K/32)."""
+    R32 = to_f32(residual(smooth_weight(W, lam32), L1, L2))
+    codes, e8 = mx_quantize_blocks(R32.T)
+    return pack_codes4(codes), e8
+
+
+def mx_prepare(W, lam32, rank: int, svd=None):
+    """Offline prep of the MXFP4 variant: the same smoothing and SVD split as
+    ``prepare``, then R in MXFP4 (w_codes N x K/2, w_e8m0 N x K/32)."""
+    What = smooth_weight(W, lam32)
+    U, S, Vt = svd if svd is not None else svd_canonical(What)
+    L1, L2 = lowrank_factors(U, S, Vt, rank)
+    w_codes, w_e8m0 = mx_quantize_residual_from_factors(W, lam32, L1, L2)
+    return dict(inv_smooth=inv_smoothing(lam32), L1=L1, L2=L2, w_codes=w_codes,
+                w_e8m0=w_e8m0, sigma=S)
+
+
+def mx_linear(X, inv_lam32, L1, L2, w_codes, w_e8m0, bias=None, out_dtype: str = "f16",
+              activation=None, return_parts: bool = False):
+    """Y = act(deq(Q_mx(Xhat)).deq(Q_mx(R))^T + fp16(D).L2 + b), exact in fp64
+    and rounded once. Products of E2M1 values and powers of two are exact, and
+    so is their fp64 sum over K while the block exponents of a row and a column
+    span fewer than about 40 binades (true of every input used here)."""
+    a_codes, a_e8, xh = mx_quantize_activation(X, inv_lam32)
+    A = mx_dequantize_blocks(unpack_codes4(a_codes), a_e8)
+    B = mx_dequantize_blocks(unpack_codes4(w_codes), w_e8m0)
+    acc = A @ B.T
+    D = down_projection(xh, L1)
+    lr = lowrank_up(D, L2)
+    if activation is None:
+        Y = finalize(acc, lr, bias, out_dtype)
+    elif activation == "gelu_tanh":
+        y = acc + np.asarray(lr, dtype=np.float64)
+        if bias is not None:
+            y = y + np.asarray(bias, dtype=np.float64)[None, :]
+        Y = gelu_tanh_f64(y).astype(np.float16 if out_dtype == "f16" else np.float32)
+    else:
+        raise ValueError(f"unknown activation {activation!r}")
+    if return_parts:
+        return Y, dict(a_codes=a_codes, a_e8m0=a_e8, xhat=xh, D=D, acc=acc, lr=lr)
+    return Y

@@ -498,3 +498,261 @@ ALL_CHECKS = [
     check_reconstruction, check_partials_bruteforce, check_dense_identity, check_lora,
     check_method_sanity, check_gelu, check_linear_gelu,
 ]
+
+
+# --------------------------------------------------------------------------
+# MXFP4 variant (OCP Microscaling v1.0 reading of the pages' 4-bit float
+# variant; taicenter.com news page on SVDQuant, hardware co-design section)
+
+PY_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def py_e2m1_code(t: float) -> int:
+    """E2M1 code of the Python float t: nearest magnitude by threshold
+    comparisons (midpoints go to the even encoding), saturating, sign bit kept."""
+    m = abs(t)
+    # (midpoint, goes up on a tie): ties go to the even code of the two
+    code = 0
+    for mid, up_on_tie in ((0.25, False), (0.75, True), (1.25, False), (1.75, True),
+                           (2.5, False), (3.5, True), (5.0, False)):
+        if m > mid or (up_on_tie and m == mid):
+            code += 1
+    return code | (8 if math.copysign(1.0, t) < 0 else 0)
+
+
+def py_mx_block(vals):
+    """One 32-block through the MXFP4 reading in plain Python: (codes, e8m0)."""
+    v = [py_f32(x) for x in vals]
+    a = max(abs(x) for x in v)
+    if a == 0.0:
+        e = -127
+    else:
+        e = math.frexp(a)[1] - 1 - 2          # floor(log2 a) - 2
+        e = max(-127, min(127, e))
+    return [py_e2m1_code(x / 2.0 ** e) for x in v], e + 127
+
+
+def load_mx_cases():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "mx_cases.txt")) as f:
+        for raw in f:
+            line = raw.split("#", 1)[0].strip()
+            if not line:
+                continue
+            tok = line.split()
+            if tok[0] == "case":
+                cur = dict(name=tok[1], v=[0.0] * 32, codes=[0] * 32, bytes=[0] * 16)
+            elif tok[0] == "v":
+                cur["v"][int(tok[1])] = bits_f32(int(tok[2], 16))
+            elif tok[0] == "e8m0":
+                cur["e8m0"] = int(tok[1])
+            elif tok[0] in ("codes", "bytes"):
+                for t in tok[1:]:
+                    i, c = t.split(":")
+                    cur[tok[0]][int(i)] = int(c, 0)
+            elif tok[0] == "end":
+                cases.append(cur)
+                cur = None
+    return cases
+
+
+def check_golden_mx(O):
+    cases = load_mx_cases()
+    assert len(cases) >= 7
+    V = np.array([c["v"] for c in cases], dtype=np.float32)
+    codes, e8 = O.mx_quantize_blocks(V)
+    packed = O.pack_codes4(codes)
+    for i, c in enumerate(cases):
+        assert int(e8[i, 0]) == c["e8m0"], (c["name"], int(e8[i, 0]))
+        assert list(codes[i]) == c["codes"], (c["name"], list(codes[i]))
+        assert list(packed[i]) == c["bytes"], (c["name"], [hex(b) for b in packed[i]])
+        # decoding: every nonzero code is +-magnitude * 2^(byte-127)
+        dec = O.mx_dequantize_blocks(codes[i:i + 1], e8[i:i + 1])[0]
+        for k in range(32):
+            cc = c["codes"][k]
+            want = (-1 if cc & 8 else 1) * PY_E2M1[cc & 7] * 2.0 ** (c["e8m0"] - 127)
+            assert dec[k] == want, (c["name"], k, dec[k], want)
+
+
+def check_golden_mx_linear(O):
+    d = {}
+    with open(os.path.join(GOLDEN, "mx_linear_tiny.txt")) as f:
+        for raw in f:
+            line = raw.split("#", 1)[0].strip()
+            if line:
+                tok = line.split()
+                d.setdefault(tok[0], []).append(tok[1:])
+    X = np.zeros((1, 64), dtype=np.float32)
+    for i, v in d["x"]:
+        X[0, int(i)] = float(v)
+    W = np.zeros((64, 1), dtype=np.float32)
+    for i, h in d["w"]:
+        W[int(i), 0] = bits_f32(int(h, 16))
+    lam = np.ones(64, dtype=np.float32)
+    p = O.mx_prepare(W, lam, rank=0)
+    assert [int(t) for t in p["w_e8m0"][0]] == [int(t) for t in d["w_e8m0"][0]]
+    wc = O.unpack_codes4(p["w_codes"])[0]
+    want = [0] * 64
+    for t in d["w_codes"][0]:
+        i, c = t.split(":")
+        want[int(i)] = int(c)
+    assert list(wc) == want
+    Y, parts = O.mx_linear(X, p["inv_smooth"], p["L1"], p["L2"], p["w_codes"], p["w_e8m0"],
+                           None, "f32", return_parts=True)
+    assert [int(t) for t in parts["a_e8m0"][0]] == [int(t) for t in d["x_e8m0"][0]]
+    xc = O.unpack_codes4(parts["a_codes"])[0]
+    want = [0] * 64
+    for t in d["x_codes"][0]:
+        i, c = t.split(":")
+        want[int(i)] = int(c)
+    assert list(xc) == want
+    assert float(Y[0, 0]) == float(d["y"][0][0]), float(Y[0, 0])
+
+
+def _random_mx_blocks(rng, n):
+    """Blocks of normal, tiny, huge, midpoint-heavy and signed-zero values."""
+    out = []
+    for i in range(n):
+        kind = i % 6
+        if kind == 0:
+            v = rng.standard_normal(32)
+        elif kind == 1:
+            v = rng.standard_normal(32) * 1e-30
+        elif kind == 2:
+            v = rng.standard_normal(32) * 1e30
+        elif kind == 3:   # exact midpoints and grid points at one scale
+            v = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 0.5, 3.0], 32)
+            v *= rng.choice([-1.0, 1.0], 32) * 2.0 ** int(rng.integers(-20, 20))
+        elif kind == 4:
+            v = rng.standard_normal(32) * 10.0 ** rng.uniform(-6, 6)
+            v[rng.integers(0, 32, 4)] = -0.0
+        else:
+            v = rng.standard_normal(32) * 1e-40       # subnormal fp32
+        out.append(v)
+    return np.array(out, dtype=np.float32)
+
+
+def check_mx_bruteforce(O, n=360, seed=43):
+    V = _random_mx_blocks(np.random.default_rng(seed), n)
+    codes, e8 = O.mx_quantize_blocks(V)
+    for i in range(n):
+        cc, ee = py_mx_block([float(x) for x in V[i]])
+        assert list(codes[i]) == cc, (i, list(codes[i]), cc)
+        assert int(e8[i, 0]) == ee, (i, int(e8[i, 0]), ee)
+
+
+def check_mx_roundtrip_bound(O, seed=47):
+    """|v - deq| <= max(2^e / 4, |v| / 4): half an E2M1 step below 2, a quarter
+    of |v| from 2 up, and under |v|/4 in the saturated band (6, 8) * 2^e."""
+    rng = np.random.default_rng(seed)
+    V = (rng.standard_normal((500, 32)) * 10.0 ** rng.uniform(-8, 8, (500, 1))).astype(np.float32)
+    codes, e8 = O.mx_quantize_blocks(V)
+    deq = O.mx_dequantize_blocks(codes, e8)
+    s = np.ldexp(1.0, e8.astype(np.int64) - 127)
+    v = V.astype(np.float64)
+    err = np.abs(v - deq)
+    bound = np.maximum(np.repeat(s, 32, axis=1) / 4, np.abs(v) / 4)
+    assert np.all(err <= bound)
+    # the block maximum lands in [4, 8) * 2^e, so its code is 6 or 7
+    amax_code = (codes & 7).max(axis=1)
+    assert np.all(amax_code >= 6)
+
+
+def check_mx_invariants(O, seed=53):
+    rng = np.random.default_rng(seed)
+    V = (rng.standard_normal((40, 64)) * 0.3).astype(np.float32)
+    c, e = O.mx_quantize_blocks(V)
+    assert c.shape == (40, 64) and e.shape == (40, 2)
+    cn, en = O.mx_quantize_blocks(-V)
+    assert np.array_equal(cn, c ^ 8) and np.array_equal(en, e)      # sign is bit 3
+    for k in (-9, 3, 40):                     # power-of-two scaling shifts only e
+        ck, ek = O.mx_quantize_blocks(V * np.float32(2.0 ** k))
+        assert np.array_equal(ck, c)
+        assert np.array_equal(ek.astype(np.int64), e.astype(np.int64) + k)
+    # blocks are independent, and run along the last axis
+    c2, _ = O.mx_quantize_blocks(V.reshape(-1, 32))
+    assert np.array_equal(c2.reshape(40, 64), c)
+    Vb = V.copy()
+    Vb[:, 32:] *= 1000
+    cb, eb = O.mx_quantize_blocks(Vb)
+    assert np.array_equal(cb[:, :32], c[:, :32]) and np.array_equal(eb[:, 0], e[:, 0])
+    # pack: element 2j in the low nibble
+    assert list(O.pack_codes4(np.array([[1, 2, 15, 8]], np.uint8))[0]) == [0x21, 0x8F]
+    b = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    assert np.array_equal(O.pack_codes4(O.unpack_codes4(b)), b)
+
+
+def check_mx_linear_bruteforce(O, seed=59):
+    """Python loops over the plain-Python block quantizer give the oracle's
+    codes, exponents and Y; R's blocks run down K for each output column."""
+    rng = np.random.default_rng(seed)
+    for (M, K, N, r) in [(4, 64, 6, 3), (3, 128, 5, 0)]:
+        X = (rng.standard_normal((M, K)) * 2).astype(np.float32)
+        X[:, 5] *= 30
+        W = (rng.standard_normal((K, N)) * 0.05).astype(np.float32)
+        lam = O.smoothing_factors(np.abs(X).max(0), W)
+        p = O.mx_prepare(W, lam, r)
+        bias = (rng.standard_normal(N) * 0.1).astype(np.float32)
+        Y, parts = O.mx_linear(X, p["inv_smooth"], p["L1"], p["L2"], p["w_codes"], p["w_e8m0"],
+                               bias, "f32", return_parts=True)
+        inv = [float(t) for t in p["inv_smooth"]]
+        lamf = [float(t) for t in lam]
+        L1 = p["L1"].astype(np.float64).tolist()
+        L2 = p["L2"].astype(np.float64).tolist()
+        nb = K // 32
+
+        def deq(codes, e8):
+            return [(-1 if c & 8 else 1) * PY_E2M1[c & 7] * 2.0 ** (e8[k // 32] - 127)
+                    for k, c in enumerate(codes)]
+
+        wdeq = []
+        for n in range(N):
+            Rcol = [py_f32(lamf[k] * float(W[k, n]) - sum(L1[k][j] * L2[j][n] for j in range(r)))
+                    for k in range(K)]
+            cs, es = [], []
+            for b in range(nb):
+                cc, ee = py_mx_block(Rcol[32 * b:32 * b + 32])
+                cs += cc
+                es.append(ee)
+            assert list(O.unpack_codes4(p["w_codes"][n])) == cs, n
+            assert [int(t) for t in p["w_e8m0"][n]] == es, n
+            wdeq.append(deq(cs, es))
+        for m in range(M):
+            xh = [py_f32(float(X[m, k]) * inv[k]) for k in range(K)]
+            cs, es = [], []
+            for b in range(nb):
+                cc, ee = py_mx_block(xh[32 * b:32 * b + 32])
+                cs += cc
+                es.append(ee)
+            assert list(O.unpack_codes4(parts["a_codes"][m])) == cs, m
+            assert [int(t) for t in parts["a_e8m0"][m]] == es, m
+            xd = deq(cs, es)
+            D16 = [py_f16(sum(py_f16(xh[k]) * L1[k][j] for k in range(K))) for j in range(r)]
+            for n in range(N):
+                y = (sum(xd[k] * wdeq[n][k] for k in range(K))
+                     + sum(D16[j] * L2[j][n] for j in range(r)) + float(bias[n]))
+                assert abs(y - float(Y[m, n])) <= 1e-6 * max(1.0, abs(y)), (m, n, y, float(Y[m, n]))
+
+
+def check_mx_method_sanity(O):
+    """MXFP4 on the tiny workload: the low-rank branch lowers the error against
+    the exact X.W, and the error is of the same order as the INT4 path's."""
+    import workloads as wl
+    L, X, W = wl.layer_inputs(0, 0)
+    lam = O.smoothing_factors(np.abs(X.astype(np.float64)).max(0), W)
+    ref = X.astype(np.float64) @ W.astype(np.float64)
+    errs = {}
+    for r in (0, L.rank):
+        p = O.mx_prepare(W, lam, r)
+        Y = O.mx_linear(X, p["inv_smooth"], p["L1"], p["L2"], p["w_codes"], p["w_e8m0"], None, "f32")
+        errs[r] = float(np.linalg.norm(Y.astype(np.float64) - ref) / np.linalg.norm(ref))
+    p = O.prepare(W, lam, L.rank)
+    Yi = O.linear(X, p["inv_smooth"], p["L1"], p["L2"], p["w_codes"], p["w_scales"], None, "f32")
+    e_int4 = float(np.linalg.norm(Yi.astype(np.float64) - ref) / np.linalg.norm(ref))
+    assert errs[L.rank] < 0.9 * errs[0], errs
+    assert 0.25 * e_int4 < errs[L.rank] < 4 * e_int4, (errs, e_int4)
+
+
+ALL_CHECKS += [check_golden_mx, check_golden_mx_linear, check_mx_bruteforce,
+               check_mx_roundtrip_bound, check_mx_invariants, check_mx_linear_bruteforce,
+               check_mx_method_sanity]

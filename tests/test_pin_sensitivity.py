@@ -135,12 +135,96 @@ def mut_gelu_before_bias(mp):
     mp.setattr(R, "linear", lin)
 
 
+def _mx_blocks_with(e_of_amax=None, round_fn=None, bias=127):
+    """An MXFP4 block quantizer with one step replaced (the rest as the oracle's)."""
+    def q(v32, block=32):
+        v = np.asarray(v32, dtype=np.float32)
+        sh = v.shape
+        vb = v.reshape(sh[:-1] + (sh[-1] // block, block)).astype(np.float64)
+        amax = np.max(np.abs(vb), axis=-1)
+        if e_of_amax is None:
+            e = np.where(amax > 0, np.frexp(amax)[1] - 3, -127)
+        else:
+            e = e_of_amax(amax)
+        e = np.clip(e, -127, 127)
+        codes = (round_fn or R.e2m1_round)(vb / np.ldexp(1.0, e)[..., None])
+        return codes.reshape(sh), (e + bias).astype(np.uint8)
+    return q
+
+
+def mut_mx_ties_up(mp):
+    """E2M1 midpoints rounded up (away from zero) instead of to the even code."""
+    def rnd(x):
+        m = np.abs(x)
+        c = sum((m >= t).astype(np.int64) for t in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0))
+        return (c + 8 * np.signbit(x)).astype(np.uint8)
+    mp.setattr(R, "mx_quantize_blocks", _mx_blocks_with(round_fn=rnd))
+
+
+def mut_mx_exponent_ceil(mp):
+    """Shared exponent from ceil(log2 amax) instead of floor."""
+    mp.setattr(R, "mx_quantize_blocks", _mx_blocks_with(
+        e_of_amax=lambda a: np.where(a > 0, np.ceil(np.log2(np.where(a > 0, a, 1))) - 2, -127)
+        .astype(np.int64)))
+
+
+def mut_mx_exponent_nearest(mp):
+    """Shared exponent rounded from log2(amax / 6) (amax mapped near 6, not floored)."""
+    mp.setattr(R, "mx_quantize_blocks", _mx_blocks_with(
+        e_of_amax=lambda a: np.where(a > 0, np.rint(np.log2(np.where(a > 0, a, 6) / 6)), -127)
+        .astype(np.int64)))
+
+
+def mut_mx_negative_zero_dropped(mp):
+    """Negative values that round to zero get code 0 instead of the -0 code."""
+    orig = _orig("e2m1_round")
+    mp.setattr(R, "e2m1_round", lambda x: np.where(orig(x) == 8, 0, orig(x)).astype(np.uint8))
+
+
+def mut_mx_bias_128(mp):
+    """E8M0 stored with bias 128 (and read back the same way, so Y is unchanged)."""
+    mp.setattr(R, "mx_quantize_blocks", _mx_blocks_with(bias=128))
+    orig = _orig("mx_dequantize_blocks")
+    mp.setattr(R, "mx_dequantize_blocks",
+               lambda c, e8, block=32: orig(c, np.asarray(e8, np.int64) - 1, block))
+
+
+def mut_mx_nibble_order(mp):
+    def pack(c):
+        c = np.asarray(c, dtype=np.uint8) & 15
+        return (c[..., 1::2] | (c[..., 0::2] << 4)).astype(np.uint8)
+    mp.setattr(R, "pack_codes4", pack)
+
+
+def mut_mx_weight_blocks_along_n(mp):
+    """R's 32-blocks taken along the output dimension instead of down K."""
+    def f(W, lam32, L1, L2):
+        R32 = R.to_f32(R.residual(R.smooth_weight(W, lam32), L1, L2))
+        Np = -(-R32.shape[1] // 32) * 32
+        pad = np.zeros((R32.shape[0], Np), dtype=np.float32)
+        pad[:, :R32.shape[1]] = R32
+        codes, _ = R.mx_quantize_blocks(pad)
+        codes = codes[:, :R32.shape[1]].T
+        _, e8 = R.mx_quantize_blocks(R32.T)
+        return R.pack_codes4(codes), e8
+    mp.setattr(R, "mx_quantize_residual_from_factors", f)
+
+
+def mut_mx_unsmoothed_activation(mp):
+    """The activation quantized before smoothing (X instead of Xhat)."""
+    orig = _orig("mx_quantize_activation")
+    mp.setattr(R, "mx_quantize_activation",
+               lambda X, inv: orig(X, np.ones_like(np.asarray(inv, np.float32))))
+
+
 MUTATIONS = [mut_scale_div8, mut_ties_away, mut_nibble_order, mut_smoothing_inverted,
              mut_sigma_unsplit, mut_smallest_singulars, mut_residual_sign,
              mut_partials_group_shift, mut_drop_weight_scale, mut_drop_bias,
              mut_down_no_f16, mut_up_no_f16, mut_lora_no_lambda, mut_f16_via_f32,
              mut_smooth_multiplies_lambda, mut_transposed_weight_groups, mut_clamp_8,
-             mut_gelu_before_bias]
+             mut_gelu_before_bias, mut_mx_ties_up, mut_mx_exponent_ceil,
+             mut_mx_exponent_nearest, mut_mx_negative_zero_dropped, mut_mx_bias_128,
+             mut_mx_nibble_order, mut_mx_weight_blocks_along_n, mut_mx_unsmoothed_activation]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
