@@ -33,6 +33,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_RANK, ERR_WORKSPACE, ERR_HIP,
 ACT_NONE, ACT_GELU_TANH = 0, 1
 F16, F32 = 1, 2
 GROUP = 64
+MX_BLOCK = 32
 MAX_RANK = 256
 
 _p = C.c_void_p
@@ -56,6 +57,14 @@ _SIGS = {
     "svdq_linear_workspace_bytes": (C.c_size_t, [_i64, _i64, _i32, _i32]),
     "svdq_linear": (_int, [_p, _int, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _int, _i64, _i64,
                            _i64, _i64, _i32, _p, C.c_size_t, _i32, _p]),
+    "svdq_prepare_weights_mx": (_int, [_p, _p, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p]),
+    "svdq_quantize_act_lowrank_down_mx": (_int, [_p, _int, _i64, _i64, _i64, _p, _p, _i32, _p, _p,
+                                                 _p, _p]),
+    "svdq_mx_gemm_lowrank_up": (_int, [_p, _p, _p, _p, _p, _p, _i32, _p, _p, _int, _i64, _i64,
+                                       _i64, _i64, _i32, _p]),
+    "svdq_linear_mx_workspace_bytes": (C.c_size_t, [_i64, _i64, _i32]),
+    "svdq_linear_mx": (_int, [_p, _int, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _int, _i64, _i64,
+                              _i64, _i64, _p, C.c_size_t, _i32, _p]),
     "svdq_debug_group_partials": (_int, [_p, _p, _i64, _i64, _i64, _i32, _i64, _i64, _p, _p]),
     "svdq_gelu_tanh_f16": (_int, [_p, _p, _i64, _p]),
 }

@@ -13,7 +13,7 @@ from typing import Optional
 import numpy as np
 
 from . import _lib
-from ._lib import F16, F32, GROUP, check, lib
+from ._lib import F16, F32, GROUP, MX_BLOCK, check, lib
 
 # --------------------------------------------------------------------------
 # host prep (numpy)
@@ -50,7 +50,9 @@ def smoothing_factors(x_absmax: np.ndarray, W: np.ndarray) -> np.ndarray:
 
 @dataclasses.dataclass
 class Prepared:
-    """Offline products for one layer, host side. L1t is R x K, L2t is N x R (fp16 bits)."""
+    """Offline products for one layer, host side. L1t is R x K, L2t is N x R (fp16 bits).
+    ``fmt`` "int4": w_scales are the fp16 group scales (N x K/64, as uint16 bits);
+    ``fmt`` "mxfp4": w_scales are the E8M0 block exponents (N x K/32, uint8)."""
     K: int
     N: int
     rank: int
@@ -60,6 +62,7 @@ class Prepared:
     w_codes: np.ndarray
     w_scales: np.ndarray
     sigma: Optional[np.ndarray] = None
+    fmt: str = "int4"
 
     @property
     def L1(self) -> np.ndarray:
@@ -101,6 +104,26 @@ def prepare_weights(W: np.ndarray, lam: np.ndarray, rank: int, want_sigma: bool 
                                    _np_ptr(wc), _np_ptr(ws), _np_ptr(sig)),
           "svdq_prepare_weights")
     return Prepared(K, N, rank, inv, L1t, L2t, wc, ws, sig)
+
+
+def prepare_weights_mx(W: np.ndarray, lam: np.ndarray, rank: int,
+                       want_sigma: bool = False) -> Prepared:
+    """svdq_prepare_weights_mx: the same split, residual in MXFP4 (fmt "mxfp4")."""
+    W = _c(W, np.float32)
+    lam = _c(lam, np.float32)
+    K, N = W.shape
+    inv = np.empty(K, dtype=np.float32)
+    L1t = np.empty((rank, K), dtype=np.uint16)
+    L2t = np.empty((N, rank), dtype=np.uint16)
+    wc = np.empty((N, K // 2), dtype=np.uint8)
+    we = np.empty((N, K // MX_BLOCK), dtype=np.uint8)
+    sig = np.empty(min(K, N), dtype=np.float64) if want_sigma else None
+    check(lib.svdq_prepare_weights_mx(_np_ptr(W), _np_ptr(lam), K, N, rank, _np_ptr(inv),
+                                      _np_ptr(L1t) if rank else None,
+                                      _np_ptr(L2t) if rank else None, _np_ptr(wc), _np_ptr(we),
+                                      _np_ptr(sig)),
+          "svdq_prepare_weights_mx")
+    return Prepared(K, N, rank, inv, L1t, L2t, wc, we, sig, fmt="mxfp4")
 
 
 def concat_lora(prep: Prepared, lam: np.ndarray, A: np.ndarray, B: np.ndarray,
@@ -186,6 +209,40 @@ def linear(X, inv_smooth, L1p, L2t, R: int, w_codes, w_scales, bias, Y, ws, stre
                           _act(activation), _stream(stream)), "svdq_linear")
 
 
+def quantize_act_lowrank_down_mx(X, inv_smooth, L1p, R: int, a_codes, a_e8m0, D, stream=None):
+    M, K = X.shape
+    check(lib.svdq_quantize_act_lowrank_down_mx(_tp(X), _dt(X), M, K, X.stride(0), _tp(inv_smooth),
+                                                _tp(L1p) if R else None, R, _tp(a_codes),
+                                                _tp(a_e8m0), _tp(D) if R else None,
+                                                _stream(stream)),
+          "svdq_quantize_act_lowrank_down_mx")
+
+
+def mx_gemm_lowrank_up(a_codes, a_e8m0, w_codes, w_e8m0, D, L2t, R: int, bias, Y, K: int,
+                       stream=None, activation=None):
+    M, N = Y.shape
+    check(lib.svdq_mx_gemm_lowrank_up(_tp(a_codes), _tp(a_e8m0), _tp(w_codes), _tp(w_e8m0),
+                                      _tp(D) if R else None, _tp(L2t) if R else None, R, _tp(bias),
+                                      _tp(Y), _dt(Y), M, N, K, Y.stride(0), _act(activation),
+                                      _stream(stream)),
+          "svdq_mx_gemm_lowrank_up")
+
+
+def linear_mx_workspace_bytes(M: int, K: int, R: int) -> int:
+    return int(lib.svdq_linear_mx_workspace_bytes(M, K, R))
+
+
+def linear_mx(X, inv_smooth, L1p, L2t, R: int, w_codes, w_e8m0, bias, Y, ws, stream=None,
+              activation=None):
+    M, K = X.shape
+    N = Y.shape[1]
+    check(lib.svdq_linear_mx(_tp(X), _dt(X), X.stride(0), _tp(inv_smooth),
+                             _tp(L1p) if R else None, _tp(L2t) if R else None, R, _tp(w_codes),
+                             _tp(w_e8m0), _tp(bias), _tp(Y), _dt(Y), Y.stride(0), M, K, N, _tp(ws),
+                             ws.numel() * ws.element_size(), _act(activation), _stream(stream)),
+          "svdq_linear_mx")
+
+
 def debug_group_partials(a_codes, w_codes, M: int, N: int, K: int, row0: int, rows: int, P,
                          stream=None):
     check(lib.svdq_debug_group_partials(_tp(a_codes), _tp(w_codes), M, N, K, GROUP, row0, rows,
@@ -199,7 +256,8 @@ def gelu_tanh_f16(x, y, stream=None):
 class Linear:
     """One prepared SVDQuant layer resident on a device.
 
-    ``Linear(prep, bias)(X)`` runs K1 then K2 on the current stream and
+    ``Linear(prep, bias)(X)`` runs K1 then K2 (their MXFP4 versions for a
+    prep of fmt "mxfp4") on the current stream and
     returns Y (M x N, ``out_dtype``), optionally through the fused activation
     (``"gelu_tanh"``). The workspace is kept between calls and grown when a
     larger M arrives."""
@@ -212,8 +270,12 @@ class Linear:
         self.inv_smooth = torch.from_numpy(prep.inv_smooth).to(dev)
         self.L1p = torch.from_numpy(prep.L1p.view(np.int16)).to(dev) if self.R else None
         self.L2t = torch.from_numpy(prep.L2t.view(np.int16)).to(dev) if self.R else None
+        self.fmt = prep.fmt
         self.w_codes = torch.from_numpy(prep.w_codes).to(dev)
-        self.w_scales = torch.from_numpy(prep.w_scales.view(np.int16)).to(dev)
+        if self.fmt == "mxfp4":
+            self.w_scales = torch.from_numpy(prep.w_scales).to(dev)
+        else:
+            self.w_scales = torch.from_numpy(prep.w_scales.view(np.int16)).to(dev)
         self.bias = None if bias is None else torch.from_numpy(_c(bias, np.float32)).to(dev)
         self.out_dtype = out_dtype
         self.activation = activation
@@ -222,7 +284,8 @@ class Linear:
 
     def workspace(self, M: int):
         torch = _torch()
-        need = linear_workspace_bytes(M, self.K, self.R)
+        need = (linear_mx_workspace_bytes(M, self.K, self.R) if self.fmt == "mxfp4"
+                else linear_workspace_bytes(M, self.K, self.R))
         if self.ws is None or self.ws.numel() < need:
             self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self.ws
@@ -232,6 +295,7 @@ class Linear:
         M = X.shape[0]
         if Y is None:
             Y = torch.empty((M, self.N), dtype=self.out_dtype or X.dtype, device=self.device)
-        linear(X, self.inv_smooth, self.L1p, self.L2t, self.R, self.w_codes, self.w_scales,
-               self.bias, Y, self.workspace(M), stream, self.activation)
+        run = linear_mx if self.fmt == "mxfp4" else linear
+        run(X, self.inv_smooth, self.L1p, self.L2t, self.R, self.w_codes, self.w_scales,
+            self.bias, Y, self.workspace(M), stream, self.activation)
         return Y

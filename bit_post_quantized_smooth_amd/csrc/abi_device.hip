@@ -61,10 +61,10 @@ int check_common(int64_t M, int64_t K, int32_t R, int32_t group, const char* fn)
 // 2^31 bytes, so per-lane offsets fit in 32 bits.
 constexpr int64_t kMaxRowElems = int64_t{1} << 25;
 
+// a_meta: the fp16 scales, or the E8M0 exponents of the MXFP4 entry points
 int validate_k1(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                 const float* inv_smooth, const uint16_t* L1p, int32_t R, int32_t group,
-                const uint8_t* a_codes, const uint16_t* a_scales, const float* D) {
-  const char* fn = "svdq_quantize_act_lowrank_down";
+                const uint8_t* a_codes, const void* a_scales, const float* D, const char* fn) {
   if (!X || !inv_smooth || !a_codes || !a_scales || (R > 0 && (!L1p || !D))) {
     set_error("%s: null pointer", fn);
     return SVDQ_ERR_NULL;
@@ -99,8 +99,8 @@ int check_activation(int32_t activation, const char* fn) {
   return SVDQ_OK;
 }
 
-int validate_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* w_codes,
-                const uint16_t* w_scales, const float* D, const uint16_t* L2t, int32_t R,
+int validate_k2(const uint8_t* a_codes, const void* a_scales, const uint8_t* w_codes,
+                const void* w_scales, const float* D, const uint16_t* L2t, int32_t R,
                 const float* bias, const void* Y, int y_dtype, int64_t M, int64_t N, int64_t K,
                 int64_t ldy, int32_t group, const char* fn) {
   if (!a_codes || !a_scales || !w_codes || !w_scales || !Y || (R > 0 && (!D || !L2t))) {
@@ -118,7 +118,7 @@ int validate_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t*
   }
   if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
       (R > 0 && (!aligned16(D) || !aligned16(L2t)))) {
-    set_error("%s: codes, scales, D and L2t must be 16-byte aligned", fn);
+    set_error("%s: codes, scales or exponents, D and L2t must be 16-byte aligned", fn);
     return SVDQ_ERR_ALIGN;
   }
   if ((reinterpret_cast<uintptr_t>(Y) % esize(y_dtype)) != 0 ||
@@ -133,11 +133,14 @@ struct WsLayout {
   size_t codes, scales, d, total;
 };
 
-WsLayout ws_layout(int64_t M, int64_t K, int32_t R) {
+// INT4: fp16 scales, 2 bytes per 64 channels; MXFP4: 1 byte per 32 channels
+WsLayout ws_layout(int64_t M, int64_t K, int32_t R, bool mx) {
   WsLayout w;
   w.codes = 0;
   w.scales = round_up(static_cast<size_t>(M) * (K / 2), 256);
-  w.d = w.scales + round_up(static_cast<size_t>(M) * (K / SVDQ_GROUP) * 2, 256);
+  const size_t meta = mx ? static_cast<size_t>(M) * (K / SVDQ_MX_BLOCK)
+                         : static_cast<size_t>(M) * (K / SVDQ_GROUP) * 2;
+  w.d = w.scales + round_up(meta, 256);
   w.total = w.d + round_up(static_cast<size_t>(M) * R * 4, 256);
   return w;
 }
@@ -151,11 +154,12 @@ int svdq_quantize_act_lowrank_down(const void* X, int x_dtype, int64_t M, int64_
                                    int32_t group, uint8_t* a_codes, uint16_t* a_scales, float* D,
                                    hipStream_t stream) {
   clear_error();
-  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, group, a_codes, a_scales, D))
+  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, group, a_codes, a_scales, D,
+                          "svdq_quantize_act_lowrank_down"))
     return s;
   if (int s = device_ready()) return s;
   return check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1p, R, a_codes,
-                             a_scales, D, stream),
+                             a_scales, false, D, stream),
                    "svdq_quantize_act_lowrank_down launch");
 }
 
@@ -178,7 +182,7 @@ int svdq_w4a4_gemm_lowrank_up(const uint8_t* a_codes, const uint16_t* a_scales,
 
 size_t svdq_linear_workspace_bytes(int64_t M, int64_t K, int32_t R, int32_t group) {
   if (M < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0 || group != SVDQ_GROUP || R < 0) return 0;
-  return ws_layout(M, K, R).total;
+  return ws_layout(M, K, R, false).total;
 }
 
 int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
@@ -194,7 +198,7 @@ int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth
     return SVDQ_ERR_NULL;
   }
   if (int s = check_common(M, K, R, group, fn)) return s;
-  const WsLayout L = ws_layout(M, K, R);
+  const WsLayout L = ws_layout(M, K, R, false);
   if (ws_bytes < L.total) {
     set_error("%s: workspace %zu bytes < %zu needed", fn, ws_bytes, L.total);
     return SVDQ_ERR_WORKSPACE;
@@ -207,19 +211,101 @@ int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth
   uint8_t* a_codes = base + L.codes;
   uint16_t* a_scales = reinterpret_cast<uint16_t*>(base + L.scales);
   float* D = R > 0 ? reinterpret_cast<float*>(base + L.d) : nullptr;
-  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, group, a_codes, a_scales, D))
+  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, group, a_codes, a_scales, D,
+                          fn))
     return s;
   if (int s = validate_k2(a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y, y_dtype, M, N,
                           K, ldy, group, fn))
     return s;
   if (int s = device_ready()) return s;
   if (int s = check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1p, R, a_codes,
-                                  a_scales, D, stream),
+                                  a_scales, false, D, stream),
                         "svdq_linear K1 launch"))
     return s;
   return check_hip(launch_k2(a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y,
                              y_dtype == SVDQ_F16, M, N, K, ldy, activation == SVDQ_ACT_GELU_TANH, stream),
                    "svdq_linear K2 launch");
+}
+
+int svdq_quantize_act_lowrank_down_mx(const void* X, int x_dtype, int64_t M, int64_t K,
+                                      int64_t ldx, const float* inv_smooth, const uint16_t* L1p,
+                                      int32_t R, uint8_t* a_codes, uint8_t* a_e8m0, float* D,
+                                      hipStream_t stream) {
+  clear_error();
+  const char* fn = "svdq_quantize_act_lowrank_down_mx";
+  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, SVDQ_GROUP, a_codes, a_e8m0,
+                          D, fn))
+    return s;
+  if (int s = device_ready()) return s;
+  return check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1p, R, a_codes,
+                             a_e8m0, true, D, stream),
+                   "svdq_quantize_act_lowrank_down_mx launch");
+}
+
+int svdq_mx_gemm_lowrank_up(const uint8_t* a_codes, const uint8_t* a_e8m0,
+                            const uint8_t* w_codes, const uint8_t* w_e8m0, const float* D,
+                            const uint16_t* L2t, int32_t R, const float* bias, void* Y,
+                            int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
+                            int32_t activation, hipStream_t stream) {
+  clear_error();
+  const char* fn = "svdq_mx_gemm_lowrank_up";
+  if (int s = validate_k2(a_codes, a_e8m0, w_codes, w_e8m0, D, L2t, R, bias, Y, y_dtype, M, N, K,
+                          ldy, SVDQ_GROUP, fn))
+    return s;
+  if (int s = check_activation(activation, fn)) return s;
+  if (int s = device_ready()) return s;
+  return check_hip(launch_k2_mx(a_codes, a_e8m0, w_codes, w_e8m0, D, L2t, R, bias, Y,
+                                y_dtype == SVDQ_F16, M, N, K, ldy,
+                                activation == SVDQ_ACT_GELU_TANH, stream),
+                   "svdq_mx_gemm_lowrank_up launch");
+}
+
+size_t svdq_linear_mx_workspace_bytes(int64_t M, int64_t K, int32_t R) {
+  if (M < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0 || R < 0) return 0;
+  return ws_layout(M, K, R, true).total;
+}
+
+int svdq_linear_mx(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
+                   const uint16_t* L1p, const uint16_t* L2t, int32_t R, const uint8_t* w_codes,
+                   const uint8_t* w_e8m0, const float* bias, void* Y, int y_dtype, int64_t ldy,
+                   int64_t M, int64_t K, int64_t N, void* ws, size_t ws_bytes,
+                   int32_t activation, hipStream_t stream) {
+  clear_error();
+  const char* fn = "svdq_linear_mx";
+  if (int s = check_activation(activation, fn)) return s;
+  if (!ws) {
+    set_error("%s: null workspace", fn);
+    return SVDQ_ERR_NULL;
+  }
+  if (int s = check_common(M, K, R, SVDQ_GROUP, fn)) return s;
+  const WsLayout L = ws_layout(M, K, R, true);
+  if (ws_bytes < L.total) {
+    set_error("%s: workspace %zu bytes < %zu needed", fn, ws_bytes, L.total);
+    return SVDQ_ERR_WORKSPACE;
+  }
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) {
+    set_error("%s: workspace must be 256-byte aligned", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* a_codes = base + L.codes;
+  uint8_t* a_e8m0 = base + L.scales;
+  float* D = R > 0 ? reinterpret_cast<float*>(base + L.d) : nullptr;
+  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, SVDQ_GROUP, a_codes, a_e8m0,
+                          D, fn))
+    return s;
+  if (int s = validate_k2(a_codes, a_e8m0, w_codes, w_e8m0, D, L2t, R, bias, Y, y_dtype, M, N, K,
+                          ldy, SVDQ_GROUP, fn))
+    return s;
+  if (int s = device_ready()) return s;
+  if (int s = check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1p, R, a_codes,
+                                  a_e8m0, true, D, stream),
+                        "svdq_linear_mx K1 launch"))
+    return s;
+  return check_hip(launch_k2_mx(a_codes, a_e8m0, w_codes, w_e8m0, D, L2t, R, bias, Y,
+                                y_dtype == SVDQ_F16, M, N, K, ldy,
+                                activation == SVDQ_ACT_GELU_TANH, stream),
+                   "svdq_linear_mx K2 launch");
 }
 
 int svdq_debug_group_partials(const uint8_t* a_codes, const uint8_t* w_codes, int64_t M, int64_t N,

@@ -7,14 +7,20 @@
 
 namespace svdq {
 
+// a_meta: fp16 group scales (mx = false) or E8M0 block exponents (mx = true)
 hipError_t launch_k1(const void* X, bool x_f16, int64_t M, int64_t K, int64_t ldx,
                      const float* inv_smooth, const uint16_t* L1p, int R, uint8_t* a_codes,
-                     uint16_t* a_scales, float* D, hipStream_t stream);
+                     void* a_meta, bool mx, float* D, hipStream_t stream);
 
 hipError_t launch_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* w_codes,
                      const uint16_t* w_scales, const float* D, const uint16_t* L2t, int R,
                      const float* bias, void* Y, bool y_f16, int64_t M, int64_t N, int64_t K,
                      int64_t ldy, bool gelu, hipStream_t stream);
+
+hipError_t launch_k2_mx(const uint8_t* a_codes, const uint8_t* a_e8m0, const uint8_t* w_codes,
+                        const uint8_t* w_e8m0, const float* D, const uint16_t* L2t, int R,
+                        const float* bias, void* Y, bool y_f16, int64_t M, int64_t N, int64_t K,
+                        int64_t ldy, bool gelu, hipStream_t stream);
 
 hipError_t launch_debug_partials(const uint8_t* a_codes, const uint8_t* w_codes, int64_t M,
                                  int64_t N, int64_t K, int64_t row0, int64_t rows, int32_t* P,

@@ -67,6 +67,34 @@ static void quantize_group_f32(const float* v, int n, uint8_t* codes, uint16_t* 
   *scale = s16;
 }
 
+// The MXFP4 block quantizer on fp32 values (the reading in svdq.h): e is the
+// exponent of the block's largest magnitude minus 2, at least -127 (the E8M0
+// byte is the biased exponent field of max|v| minus 2, floored at 0); each
+// value is v * 2^-e (exact in fp64) rounded to the nearest E2M1 value, ties to
+// the even encoding, saturating at 6, sign bit kept. Writes 16 packed bytes
+// and one E8M0 byte for 32 values.
+static void quantize_block_mx(const float* v, uint8_t* codes, uint8_t* e8m0) {
+  float a = 0.0f;
+  for (int i = 0; i < SVDQ_MX_BLOCK; ++i) a = std::max(a, std::fabs(v[i]));
+  uint32_t abits;
+  std::memcpy(&abits, &a, sizeof(abits));
+  const int e8 = std::max(static_cast<int>(abits >> 23) - 2, 0);
+  // nearest E2M1 magnitude of m >= 0: counts the midpoints below m, a midpoint
+  // itself going to the even code (E2M1 magnitudes 0 .5 1 1.5 2 3 4 6)
+  auto code_of = [](double t) -> uint8_t {
+    const double m = std::fabs(t);
+    const int c = (m > 0.25) + (m >= 0.75) + (m > 1.25) + (m >= 1.75) + (m > 2.5) +
+                  (m >= 3.5) + (m > 5.0);
+    return static_cast<uint8_t>(c | (std::signbit(t) ? 8 : 0));
+  };
+  for (int i = 0; i < SVDQ_MX_BLOCK; i += 2) {
+    const uint8_t c0 = code_of(std::ldexp(static_cast<double>(v[i]), 127 - e8));
+    const uint8_t c1 = code_of(std::ldexp(static_cast<double>(v[i + 1]), 127 - e8));
+    codes[i / 2] = static_cast<uint8_t>(c0 | (c1 << 4));
+  }
+  *e8m0 = static_cast<uint8_t>(e8);
+}
+
 }  // namespace svdq
 
 using namespace svdq;
@@ -86,6 +114,159 @@ using namespace svdq;
     set_error("internal error");                                 \
     return SVDQ_ERR_INTERNAL;                                    \
   }
+
+namespace {
+
+// The offline steps both 4-bit formats share: inv_smooth, the smoothing of W,
+// the SVD split into the fp16 factors, and the fp32 residual R, handed column
+// by column (K values down K for output column n) to quantize_column(col, n).
+// Shapes and pointers are checked by the caller.
+template <class QuantizeColumn>
+int prepare_common(const char* fn, const float* W, const float* lambda, int64_t K, int64_t N,
+                   int32_t rank, float* inv_smooth, uint16_t* L1t, uint16_t* L2t,
+                   double* sigma, QuantizeColumn&& quantize_column) {
+  const int64_t nmin = std::min(K, N);
+  SVDQ_TRY
+  // inv_smooth = 1/lambda in fp32; What = diag(lambda) W in fp64 (exact)
+  for (int64_t k = 0; k < K; ++k) {
+    volatile float inv = 1.0f / lambda[k];
+    inv_smooth[k] = inv;
+  }
+  std::vector<double> What(static_cast<size_t>(K) * N);
+#pragma omp parallel for schedule(static)
+  for (int64_t k = 0; k < K; ++k) {
+    const double l = static_cast<double>(lambda[k]);
+    for (int64_t n = 0; n < N; ++n) What[k * N + n] = l * static_cast<double>(W[k * N + n]);
+  }
+
+  const bool need_svd = rank > 0 || sigma != nullptr;
+  std::vector<double> L1(static_cast<size_t>(K) * rank, 0.0);   // fp16 values, K x r
+  std::vector<double> L2(static_cast<size_t>(rank) * N, 0.0);   // fp16 values, r x N
+  if (need_svd) {
+    // Gram matrix of the shorter side, laid out so its rows are contiguous
+    const bool rows_short = K <= N;     // B = What (K x N)  or  B = What^T (N x K)
+    const int64_t n = nmin, m = rows_short ? N : K;
+    std::vector<double> B;
+    const double* Bp = What.data();
+    if (!rows_short) {
+      B.resize(static_cast<size_t>(N) * K);
+#pragma omp parallel for schedule(static)
+      for (int64_t i = 0; i < N; ++i)
+        for (int64_t k = 0; k < K; ++k) B[i * K + k] = What[k * N + i];
+      Bp = B.data();
+    }
+    std::vector<double> G(static_cast<size_t>(n) * n);
+    gram_rows(Bp, n, m, G.data());
+    std::vector<double> ev, Z, all;
+    const int r = rank;
+    if (!sym_top_eigen(G, n, r, ev, Z, sigma ? &all : nullptr)) {
+      set_error("%s: eigen-solver did not converge", fn);
+      return SVDQ_ERR_INTERNAL;
+    }
+    if (sigma)
+      for (int64_t i = 0; i < n; ++i) sigma[i] = std::sqrt(std::max(0.0, all[i]));
+    // Z (n x r): eigenvectors of B B^T = left singular vectors of B.
+    // The other side is B^T z / s.  For rows_short, B = What: u = z, v = What^T u / s.
+    // Otherwise B = What^T: v = z, u = What v / s.
+    std::vector<double> s(r), u(static_cast<size_t>(K) * r), v(static_cast<size_t>(N) * r);
+    for (int j = 0; j < r; ++j) s[j] = std::sqrt(std::max(0.0, ev[j]));
+    std::vector<double>& zside = rows_short ? u : v;    // length n per column
+    std::vector<double>& oside = rows_short ? v : u;    // length m per column
+    for (int64_t i = 0; i < n; ++i)
+      for (int j = 0; j < r; ++j) zside[i * r + j] = Z[i * r + j];
+    // oside[:, j] = B^T z_j / s_j, B rows contiguous: accumulate row by row
+    std::fill(oside.begin(), oside.end(), 0.0);
+#pragma omp parallel
+    {
+      std::vector<double> acc(static_cast<size_t>(r));
+#pragma omp for schedule(static)
+      for (int64_t c = 0; c < m; ++c) {
+        std::fill(acc.begin(), acc.end(), 0.0);
+        for (int64_t i = 0; i < n; ++i) {
+          const double b = Bp[i * m + c];
+          const double* zr = Z.data() + i * r;
+          for (int j = 0; j < r; ++j) acc[j] += b * zr[j];
+        }
+        for (int j = 0; j < r; ++j) oside[c * r + j] = s[j] > 1e-300 ? acc[j] / s[j] : 0.0;
+      }
+    }
+    // canonical sign: the entry of largest magnitude of each u_j is positive
+    for (int j = 0; j < r; ++j) {
+      int64_t best = 0;
+      double bmag = -1.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const double a = std::fabs(u[k * r + j]);
+        if (a > bmag) {
+          bmag = a;
+          best = k;
+        }
+      }
+      if (u[best * r + j] < 0.0) {
+        for (int64_t k = 0; k < K; ++k) u[k * r + j] = -u[k * r + j];
+        for (int64_t c = 0; c < N; ++c) v[c * r + j] = -v[c * r + j];
+      }
+    }
+    // L1 = fp16(U_r S^(1/2)), L2 = fp16(S^(1/2) V_r^T), each rounded once from fp64
+    for (int j = 0; j < r; ++j) {
+      const double h = std::sqrt(s[j]);
+      for (int64_t k = 0; k < K; ++k) {
+        const uint16_t q = f64_to_f16(u[k * r + j] * h);
+        L1t[static_cast<int64_t>(j) * K + k] = q;
+        L1[k * r + j] = f16_to_f64(q);
+      }
+      for (int64_t c = 0; c < N; ++c) {
+        const uint16_t q = f64_to_f16(h * v[c * r + j]);
+        L2t[c * r + j] = q;
+        L2[static_cast<int64_t>(j) * N + c] = f16_to_f64(q);
+      }
+    }
+  }
+
+  // R = What - L1 L2 (from the stored fp16 factors; each product of two fp16
+  // values is exact in fp64), rounded to fp32, then quantized down K for
+  // each output column n.
+  const int64_t NB = 16;   // columns per task
+#pragma omp parallel
+  {
+    std::vector<float> col(static_cast<size_t>(NB) * K);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t n0 = 0; n0 < N; n0 += NB) {
+      const int64_t nb = std::min(NB, N - n0);
+      for (int64_t k = 0; k < K; ++k) {
+        const double* wrow = &What[k * N + n0];
+        const double* l1 = L1.data() + k * rank;
+        for (int64_t c = 0; c < nb; ++c) {
+          double acc = 0.0;
+          for (int j = 0; j < rank; ++j) acc += l1[j] * L2[static_cast<int64_t>(j) * N + n0 + c];
+          col[c * K + k] = static_cast<float>(wrow[c] - acc);
+        }
+      }
+      for (int64_t c = 0; c < nb; ++c) quantize_column(&col[c * K], n0 + c);
+    }
+  }
+  return SVDQ_OK;
+  SVDQ_CATCH
+}
+
+// Checks shared by both prep functions.
+int check_prep_args(const char* fn, int64_t K, int64_t N, int32_t rank) {
+  if (K < SVDQ_GROUP || K % SVDQ_GROUP != 0) {
+    set_error("%s: K=%lld (need K %% 64 == 0)", fn, (long long)K);
+    return SVDQ_ERR_GROUP;
+  }
+  if (N < 1) {
+    set_error("%s: N=%lld", fn, (long long)N);
+    return SVDQ_ERR_SHAPE;
+  }
+  const int64_t nmin = std::min(K, N);
+  if (rank < 0 || rank > nmin) {
+    set_error("%s: rank %d outside [0, min(K,N)=%lld]", fn, rank, (long long)nmin);
+    return SVDQ_ERR_RANK;
+  }
+  return SVDQ_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -163,145 +344,40 @@ int svdq_prepare_weights(const float* W, const float* lambda, int64_t K, int64_t
     set_error("svdq_prepare_weights: null pointer");
     return SVDQ_ERR_NULL;
   }
-  if (group != SVDQ_GROUP || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) {
-    set_error("svdq_prepare_weights: group=%d K=%lld (need group 64 and K %% 64 == 0)", group,
-              (long long)K);
+  if (group != SVDQ_GROUP) {
+    set_error("svdq_prepare_weights: group=%d (need 64)", group);
     return SVDQ_ERR_GROUP;
   }
-  if (N < 1) {
-    set_error("svdq_prepare_weights: N=%lld", (long long)N);
-    return SVDQ_ERR_SHAPE;
-  }
-  const int64_t nmin = std::min(K, N);
-  if (rank < 0 || rank > nmin) {
-    set_error("svdq_prepare_weights: rank %d outside [0, min(K,N)=%lld]", rank, (long long)nmin);
-    return SVDQ_ERR_RANK;
-  }
-  SVDQ_TRY
-  // inv_smooth = 1/lambda in fp32; What = diag(lambda) W in fp64 (exact)
-  for (int64_t k = 0; k < K; ++k) {
-    volatile float inv = 1.0f / lambda[k];
-    inv_smooth[k] = inv;
-  }
-  std::vector<double> What(static_cast<size_t>(K) * N);
-#pragma omp parallel for schedule(static)
-  for (int64_t k = 0; k < K; ++k) {
-    const double l = static_cast<double>(lambda[k]);
-    for (int64_t n = 0; n < N; ++n) What[k * N + n] = l * static_cast<double>(W[k * N + n]);
-  }
-
-  const bool need_svd = rank > 0 || sigma != nullptr;
-  std::vector<double> L1(static_cast<size_t>(K) * rank, 0.0);   // fp16 values, K x r
-  std::vector<double> L2(static_cast<size_t>(rank) * N, 0.0);   // fp16 values, r x N
-  if (need_svd) {
-    // Gram matrix of the shorter side, laid out so its rows are contiguous
-    const bool rows_short = K <= N;     // B = What (K x N)  or  B = What^T (N x K)
-    const int64_t n = nmin, m = rows_short ? N : K;
-    std::vector<double> B;
-    const double* Bp = What.data();
-    if (!rows_short) {
-      B.resize(static_cast<size_t>(N) * K);
-#pragma omp parallel for schedule(static)
-      for (int64_t i = 0; i < N; ++i)
-        for (int64_t k = 0; k < K; ++k) B[i * K + k] = What[k * N + i];
-      Bp = B.data();
-    }
-    std::vector<double> G(static_cast<size_t>(n) * n);
-    gram_rows(Bp, n, m, G.data());
-    std::vector<double> ev, Z, all;
-    const int r = rank;
-    if (!sym_top_eigen(G, n, r, ev, Z, sigma ? &all : nullptr)) {
-      set_error("svdq_prepare_weights: eigen-solver did not converge");
-      return SVDQ_ERR_INTERNAL;
-    }
-    if (sigma)
-      for (int64_t i = 0; i < n; ++i) sigma[i] = std::sqrt(std::max(0.0, all[i]));
-    // Z (n x r): eigenvectors of B B^T = left singular vectors of B.
-    // The other side is B^T z / s.  For rows_short, B = What: u = z, v = What^T u / s.
-    // Otherwise B = What^T: v = z, u = What v / s.
-    std::vector<double> s(r), u(static_cast<size_t>(K) * r), v(static_cast<size_t>(N) * r);
-    for (int j = 0; j < r; ++j) s[j] = std::sqrt(std::max(0.0, ev[j]));
-    std::vector<double>& zside = rows_short ? u : v;    // length n per column
-    std::vector<double>& oside = rows_short ? v : u;    // length m per column
-    for (int64_t i = 0; i < n; ++i)
-      for (int j = 0; j < r; ++j) zside[i * r + j] = Z[i * r + j];
-    // oside[:, j] = B^T z_j / s_j, B rows contiguous: accumulate row by row
-    std::fill(oside.begin(), oside.end(), 0.0);
-#pragma omp parallel
-    {
-      std::vector<double> acc(static_cast<size_t>(r));
-#pragma omp for schedule(static)
-      for (int64_t c = 0; c < m; ++c) {
-        std::fill(acc.begin(), acc.end(), 0.0);
-        for (int64_t i = 0; i < n; ++i) {
-          const double b = Bp[i * m + c];
-          const double* zr = Z.data() + i * r;
-          for (int j = 0; j < r; ++j) acc[j] += b * zr[j];
-        }
-        for (int j = 0; j < r; ++j) oside[c * r + j] = s[j] > 1e-300 ? acc[j] / s[j] : 0.0;
-      }
-    }
-    // canonical sign: the entry of largest magnitude of each u_j is positive
-    for (int j = 0; j < r; ++j) {
-      int64_t best = 0;
-      double bmag = -1.0;
-      for (int64_t k = 0; k < K; ++k) {
-        const double a = std::fabs(u[k * r + j]);
-        if (a > bmag) {
-          bmag = a;
-          best = k;
-        }
-      }
-      if (u[best * r + j] < 0.0) {
-        for (int64_t k = 0; k < K; ++k) u[k * r + j] = -u[k * r + j];
-        for (int64_t c = 0; c < N; ++c) v[c * r + j] = -v[c * r + j];
-      }
-    }
-    // L1 = fp16(U_r S^(1/2)), L2 = fp16(S^(1/2) V_r^T), each rounded once from fp64
-    for (int j = 0; j < r; ++j) {
-      const double h = std::sqrt(s[j]);
-      for (int64_t k = 0; k < K; ++k) {
-        const uint16_t q = f64_to_f16(u[k * r + j] * h);
-        L1t[static_cast<int64_t>(j) * K + k] = q;
-        L1[k * r + j] = f16_to_f64(q);
-      }
-      for (int64_t c = 0; c < N; ++c) {
-        const uint16_t q = f64_to_f16(h * v[c * r + j]);
-        L2t[c * r + j] = q;
-        L2[static_cast<int64_t>(j) * N + c] = f16_to_f64(q);
-      }
-    }
-  }
-
-  // R = What - L1 L2 (from the stored fp16 factors; each product of two fp16
-  // values is exact in fp64), rounded to fp32, then quantized down K for
-  // each output column n.
+  const int st = check_prep_args("svdq_prepare_weights", K, N, rank);
+  if (st != SVDQ_OK) return st;
   const int64_t G = K / SVDQ_GROUP;
-  const int64_t NB = 16;   // columns per task
-#pragma omp parallel
-  {
-    std::vector<float> col(static_cast<size_t>(NB) * K);
-#pragma omp for schedule(dynamic, 1)
-    for (int64_t n0 = 0; n0 < N; n0 += NB) {
-      const int64_t nb = std::min(NB, N - n0);
-      for (int64_t k = 0; k < K; ++k) {
-        const double* wrow = &What[k * N + n0];
-        const double* l1 = L1.data() + k * rank;
-        for (int64_t c = 0; c < nb; ++c) {
-          double acc = 0.0;
-          for (int j = 0; j < rank; ++j) acc += l1[j] * L2[static_cast<int64_t>(j) * N + n0 + c];
-          col[c * K + k] = static_cast<float>(wrow[c] - acc);
-        }
-      }
-      for (int64_t c = 0; c < nb; ++c)
-        for (int64_t g = 0; g < G; ++g)
-          quantize_group_f32(&col[c * K + g * SVDQ_GROUP], SVDQ_GROUP,
-                             &w_codes[(n0 + c) * (K / 2) + g * (SVDQ_GROUP / 2)],
-                             &w_scales[(n0 + c) * G + g]);
-    }
+  return prepare_common("svdq_prepare_weights", W, lambda, K, N, rank, inv_smooth, L1t, L2t,
+                        sigma, [&](const float* col, int64_t n) {
+                          for (int64_t g = 0; g < G; ++g)
+                            quantize_group_f32(col + g * SVDQ_GROUP, SVDQ_GROUP,
+                                               &w_codes[n * (K / 2) + g * (SVDQ_GROUP / 2)],
+                                               &w_scales[n * G + g]);
+                        });
+}
+
+int svdq_prepare_weights_mx(const float* W, const float* lambda, int64_t K, int64_t N,
+                            int32_t rank, float* inv_smooth, uint16_t* L1t, uint16_t* L2t,
+                            uint8_t* w_codes, uint8_t* w_e8m0, double* sigma) {
+  clear_error();
+  if (!W || !lambda || !inv_smooth || !w_codes || !w_e8m0 || (rank > 0 && (!L1t || !L2t))) {
+    set_error("svdq_prepare_weights_mx: null pointer");
+    return SVDQ_ERR_NULL;
   }
-  return SVDQ_OK;
-  SVDQ_CATCH
+  const int st = check_prep_args("svdq_prepare_weights_mx", K, N, rank);
+  if (st != SVDQ_OK) return st;
+  const int64_t NBK = K / SVDQ_MX_BLOCK;
+  return prepare_common("svdq_prepare_weights_mx", W, lambda, K, N, rank, inv_smooth, L1t, L2t,
+                        sigma, [&](const float* col, int64_t n) {
+                          for (int64_t b = 0; b < NBK; ++b)
+                            quantize_block_mx(col + b * SVDQ_MX_BLOCK,
+                                              &w_codes[n * (K / 2) + b * (SVDQ_MX_BLOCK / 2)],
+                                              &w_e8m0[n * NBK + b]);
+                        });
 }
 
 int svdq_concat_lora(const uint16_t* L1t, const uint16_t* L2t, int64_t K, int64_t N, int32_t rank,

@@ -9,6 +9,12 @@
 //   per row and group of 64: absmax -> fp16 scale -> 4-bit codes (quantizer)
 //   D += fp16(Xhat) . L1                          (down-projection, fp16 MFMA)
 //
+// The MXFP4 instance (MX = true) replaces the quantizer step: per row and
+// block of 32 channels, the E8M0 exponent of the block's absmax and E2M1
+// codes (OCP Microscaling v1.0, the CDNA4 counterpart of the 4-bit float
+// version on the taicenter.com news page, hardware co-design section); the
+// rest of the kernel is the same.
+//
 // Work split: a workgroup owns 16 rows; its waves (8, or 4 at high rank) take
 // the 64-channel groups round-robin.
 //
@@ -104,6 +110,75 @@ __device__ __forceinline__ float quad_max(float a) {
   return a;
 }
 
+// max with the other lane of the pair (lanes 2r, 2r+1): the two lanes that
+// hold one 32-channel block
+__device__ __forceinline__ float pair_max(float a) {
+  return fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a),
+                                                                     0xB1, 0xF, 0xF, false)));
+}
+
+constexpr float kInv7 = 0.142857149f;           // fp32(1/7) = 0x3E124925
+
+// INT4 quantizer of one row's group of 64 (4 lanes, 16 values each): packed
+// codes of this lane's 16 values and the group's fp16 scale.
+__device__ __forceinline__ void quantize_int4(const float* xh, uint32_t packed[2], uint16_t& s16) {
+  // group absmax over this lane's 16 values, then across the 4 lanes of the row
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(xh[j]));
+  a = quad_max(a);
+  // fp32(a / 7), correctly rounded, as one multiply by fp32(1/7) and one
+  // FMA correction (division by a constant known in advance: Brisebarre,
+  // Muller, Raina, IEEE Trans. Computers 2004); for the divisor 7 this is
+  // exact for every non-negative finite fp32 a, which was checked
+  // exhaustively against the IEEE division on the host.
+  const float q7 = a * kInv7;
+  const float s32 = fminf(__builtin_fmaf(__builtin_fmaf(-q7, 7.0f, a), kInv7, q7), 65504.0f);
+  s16 = f2h(s32);
+  const float sf = h2f(s16);
+  const float inv = (sf == 0.f) ? 0.f : 1.0f / sf;
+  // code = clamp(rint(xh * inv), -7, 7): clamping first gives the same
+  // result, and adding 1.5 * 2^23 rounds half-to-even to an integer whose
+  // low 4 bits are its two's-complement nibble.
+  packed[0] = packed[1] = 0u;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float c = __builtin_amdgcn_fmed3f(xh[j] * inv, -7.f, 7.f);
+    const uint32_t bits = __builtin_bit_cast(uint32_t, c + kMagicF);
+    packed[j >> 3] |= (bits & 0xFu) << (4 * (j & 7));
+  }
+}
+
+// MXFP4 quantizer of one row's two 32-channel blocks (lanes 0, 1 of the quad
+// hold the first, lanes 2, 3 the second): packed E2M1 codes of this lane's 16
+// values, and in lane 0 of the quad both E8M0 bytes (first block low).
+// The shared exponent is e = floor(log2 amax) - 2, at least -127, i.e. the
+// E8M0 byte is amax's biased exponent field minus 2, floored at 0. Values are
+// first multiplied by 2^-e (exact: a power of two, and every product that is
+// not a normal fp32 is below 0.25 and gives a zero code of the same sign),
+// then converted with scale 1 by v_cvt_scalef32_pk_fp4_f32, which rounds to
+// the nearest E2M1 value, ties to even, and saturates at 6.
+__device__ __forceinline__ void quantize_mx(const float* xh, uint32_t packed[2], uint32_t& e8pair) {
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(xh[j]));
+  a = pair_max(a);
+  const int ex = static_cast<int>(__builtin_bit_cast(uint32_t, a) >> 23);
+  const int e8 = ex > 2 ? ex - 2 : 0;
+  const float mult = __builtin_bit_cast(float, static_cast<uint32_t>(254 - e8) << 23);
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    uint32_t w = 0u;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xh[8 * d + 0] * mult, xh[8 * d + 1] * mult, 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xh[8 * d + 2] * mult, xh[8 * d + 3] * mult, 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xh[8 * d + 4] * mult, xh[8 * d + 5] * mult, 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xh[8 * d + 6] * mult, xh[8 * d + 7] * mult, 1.0f, 3);
+    packed[d] = w;
+  }
+  const int e8_next = __builtin_amdgcn_mov_dpp(e8, 0x4E, 0xF, 0xF, false);   // lane + 2 of the quad
+  e8pair = static_cast<uint32_t>(e8) | (static_cast<uint32_t>(e8_next) << 8);
+}
+
 // L1 operands travel in the ring up to rank 128; above that they would not fit
 // in registers next to the accumulators and are loaded just before use.
 template <int NCB>
@@ -124,13 +199,13 @@ struct GroupIn {
 };
 
 constexpr int kXsStride = kGroup + 8;           // fp16 elements per row of the LDS tile
-constexpr float kInv7 = 0.142857149f;           // fp32(1/7) = 0x3E124925
 
-template <typename XT, int NCB, int NB>
+// a_meta: the fp16 group scales (M x K/64) or, for MX, the E8M0 bytes (M x K/32)
+template <typename XT, int NCB, int NB, bool MX>
 __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
     const XT* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
     const float* __restrict__ inv_smooth, const uint16_t* __restrict__ L1p, int R,
-    uint8_t* __restrict__ a_codes, uint16_t* __restrict__ a_scales, float* __restrict__ D) {
+    uint8_t* __restrict__ a_codes, void* __restrict__ a_meta, float* __restrict__ D) {
 #pragma clang fp contract(off)
   constexpr int WAVES = k1_waves<NCB>();
   constexpr int NCBA = NCB > 0 ? NCB : 1;
@@ -159,7 +234,8 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
   const v8h* l1b = reinterpret_cast<const v8h*>(L1p);
   uint8_t* cblk = a_codes + row0 * (K / 2);
   const uint32_t coff = qr * static_cast<uint32_t>(K / 2) + c4 * 8;
-  uint16_t* sblk = a_scales + row0 * G;
+  // per row: G fp16 scales, or 2G E8M0 bytes (two per group, stored as one uint16)
+  uint16_t* sblk = static_cast<uint16_t*>(a_meta) + row0 * G;
   const uint32_t soff = qr * static_cast<uint32_t>(G);
 
   // packed operand (g, c, h) of this lane
@@ -199,33 +275,16 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
       const int i = i0 + b;
       const int g = wave + WAVES * i;
       uint32_t packed[2] = {0u, 0u};
-      uint16_t s16 = 0;
+      uint32_t meta = 0u;                  // fp16 scale, or the two E8M0 bytes
       if (i < n_mine) {
         float xh[16];
         smooth16(ring[b].x, ring[b].inv, xh);
-        // group absmax over this lane's 16 values, then across the 4 lanes of the row
-        float a = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(xh[j]));
-        a = quad_max(a);
-        // fp32(a / 7), correctly rounded, as one multiply by fp32(1/7) and one
-        // FMA correction (division by a constant known in advance: Brisebarre,
-        // Muller, Raina, IEEE Trans. Computers 2004); for the divisor 7 this is
-        // exact for every non-negative finite fp32 a, which was checked
-        // exhaustively against the IEEE division on the host.
-        const float q7 = a * kInv7;
-        const float s32 = fminf(__builtin_fmaf(__builtin_fmaf(-q7, 7.0f, a), kInv7, q7), 65504.0f);
-        s16 = f2h(s32);
-        const float sf = h2f(s16);
-        const float inv = (sf == 0.f) ? 0.f : 1.0f / sf;
-        // code = clamp(rint(xh * inv), -7, 7): clamping first gives the same
-        // result, and adding 1.5 * 2^23 rounds half-to-even to an integer whose
-        // low 4 bits are its two's-complement nibble.
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float c = __builtin_amdgcn_fmed3f(xh[j] * inv, -7.f, 7.f);
-          const uint32_t bits = __builtin_bit_cast(uint32_t, c + kMagicF);
-          packed[j >> 3] |= (bits & 0xFu) << (4 * (j & 7));
+        if constexpr (MX) {
+          quantize_mx(xh, packed, meta);
+        } else {
+          uint16_t s16;
+          quantize_int4(xh, packed, s16);
+          meta = s16;
         }
         if constexpr (NCB > 0) {
           // fp16 values to the matrix map through this wave's LDS tile
@@ -265,7 +324,7 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
       }
       if (i < n_mine && rvalid) {
         *reinterpret_cast<uint2*>(cblk + g * kGroupBytes + coff) = make_uint2(packed[0], packed[1]);
-        if (c4 == 0) sblk[g + soff] = s16;
+        if (c4 == 0) sblk[g + soff] = static_cast<uint16_t>(meta);
       }
       // Refill this slot only after the stores: issued right behind the matrix
       // instructions that read the slot's L1 operands, the loads corrupted
@@ -294,33 +353,38 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
 template <typename XT, int NCB>
 hipError_t launch_k1_t(const void* X, int64_t M, int64_t K, int64_t ldx,
                        const float* inv_smooth, const uint16_t* L1p, int R,
-                       uint8_t* a_codes, uint16_t* a_scales, float* D, hipStream_t stream) {
+                       uint8_t* a_codes, void* a_meta, bool mx, float* D, hipStream_t stream) {
   // groups in flight per wave, sized so the ring fits the register budget of
   // two resident workgroups
   constexpr int NB = 1;
   const dim3 block(64 * k1_waves<NCB>()), grid(static_cast<unsigned>((M + 15) / 16));
-  hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB>), grid, block, 0, stream,
-                     static_cast<const XT*>(X), M, K, ldx, inv_smooth, L1p, R, a_codes, a_scales,
-                     D);
+  if (mx)
+    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, true>), grid, block, 0, stream,
+                       static_cast<const XT*>(X), M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta,
+                       D);
+  else
+    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, false>), grid, block, 0, stream,
+                       static_cast<const XT*>(X), M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta,
+                       D);
   return hipGetLastError();
 }
 
 template <typename XT>
 hipError_t launch_k1_dtype(const void* X, int64_t M, int64_t K, int64_t ldx,
                                   const float* inv_smooth, const uint16_t* L1p, int R,
-                                  uint8_t* a_codes, uint16_t* a_scales, float* D,
+                                  uint8_t* a_codes, void* a_meta, bool mx, float* D,
                                   hipStream_t stream) {
   switch (R / 16) {
-    case 0: return launch_k1_t<XT, 0>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_scales, D, stream);
-    case 1: return launch_k1_t<XT, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_scales, D, stream);
-    case 2: return launch_k1_t<XT, 2>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_scales, D, stream);
-    case 3: return launch_k1_t<XT, 3>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_scales, D, stream);
-    case 4: return launch_k1_t<XT, 4>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_scales, D, stream);
-    case 5: return launch_k1_t<XT, 5>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_scales, D, stream);
-    case 6: return launch_k1_t<XT, 6>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_scales, D, stream);
+    case 0: return launch_k1_t<XT, 0>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
+    case 1: return launch_k1_t<XT, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
+    case 2: return launch_k1_t<XT, 2>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
+    case 3: return launch_k1_t<XT, 3>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
+    case 4: return launch_k1_t<XT, 4>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
+    case 5: return launch_k1_t<XT, 5>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
+    case 6: return launch_k1_t<XT, 6>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
     case 7:
-    case 8: return launch_k1_t<XT, 8>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_scales, D, stream);
-    default: return launch_k1_t<XT, 16>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_scales, D, stream);
+    case 8: return launch_k1_t<XT, 8>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
+    default: return launch_k1_t<XT, 16>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
   }
 }
 
@@ -328,10 +392,10 @@ hipError_t launch_k1_dtype(const void* X, int64_t M, int64_t K, int64_t ldx,
 
 hipError_t launch_k1(const void* X, bool x_f16, int64_t M, int64_t K, int64_t ldx,
                      const float* inv_smooth, const uint16_t* L1p, int R, uint8_t* a_codes,
-                     uint16_t* a_scales, float* D, hipStream_t stream) {
+                     void* a_meta, bool mx, float* D, hipStream_t stream) {
   if (x_f16)
-    return launch_k1_dtype<_Float16>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_scales, D, stream);
-  return launch_k1_dtype<float>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_scales, D, stream);
+    return launch_k1_dtype<_Float16>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
+  return launch_k1_dtype<float>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
 }
 
 }  // namespace svdq

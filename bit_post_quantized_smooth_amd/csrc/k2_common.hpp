@@ -1,0 +1,145 @@
+// Pieces shared by the two GEMM kernels (INT4 and MXFP4): the XCD-aware tile
+// order and the epilogue that adds the low-rank up-projection and the bias,
+// applies the optional GELU and stores Y.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+
+namespace svdq {
+
+// Resident workgroup slots of the current device (2 per compute unit).
+int resident_slots();
+
+namespace {
+
+// Tile order. Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs
+// on XCD b % 8), and each XCD has its own L2. Renumber so that every XCD works
+// through one contiguous run of tiles, and walk the tiles in bands of
+// kBandM tile rows, column by column: the tiles an XCD holds at one time then
+// share a few A row panels and B column panels, which stay in its L2.
+constexpr int kXcds = 8;
+constexpr int kBandM = 8;
+
+__device__ __forceinline__ int xcd_contiguous(int b, int T) {
+  const int per = T / kXcds, rem = T % kXcds;
+  const int x = b % kXcds, local = b / kXcds;
+  return x * per + (x < rem ? x : rem) + local;             // a bijection of [0, T)
+}
+
+__device__ __forceinline__ void banded_tile(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int band_tiles = kBandM * tiles_n;
+  const int band = t / band_tiles;
+  const int first_m = band * kBandM;
+  const int rows = tiles_m - first_m < kBandM ? tiles_m - first_m : kBandM;
+  const int r = t - band * band_tiles;
+  tm = first_m + r % rows;
+  tn = r / rows;
+}
+
+// Epilogue of a 2*WT x 2*WT tile whose 4 waves each hold a WT x WT quarter in
+// fp32 accumulators (wave w: rows wm = w/2, columns wn = w%2; in each 16 x 16
+// block a lane holds columns 4*(lane/16) .. +3 of row lane%16).
+// The low-rank branch (the Nunchaku engine fuses it into the low-bit kernel:
+// SVDQuant abstract; the disruptive-concepts.com post, section "Nunchaku:
+// Fusing Precision and Speed") runs as fp16 MFMAs on the same accumulators:
+// acc += fp16(D) . L2; then the bias, optionally the GELU, and one rounding
+// to the output type.
+template <int WT, bool Y_F16, bool GELU>
+__device__ __forceinline__ void lowrank_bias_store(
+    v4f (&acc)[WT / 16][WT / 16], const float* __restrict__ D, const uint16_t* __restrict__ L2t,
+    int R, const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N,
+    int64_t ldy, int64_t m0, int64_t n0) {
+  constexpr int NB = WT / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rl = lane & 15, q = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  // low-rank up-projection on the same accumulators: acc += fp16(D) . L2
+  for (int rc = 0; rc < R; rc += 32) {
+    const int kk = rc + 8 * q;                       // this lane's 8 rank indices
+    const bool kval = kk < R;                        // R % 16 == 0: whole 8-runs are valid or not
+    v8h Al[NB], Bl[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int64_t m = m0 + wm * WT + i * 16 + rl;
+      if (kval && m < M) {
+        const float4* dp = reinterpret_cast<const float4*>(D + m * R + kk);
+        const float4 u = dp[0], v = dp[1];
+        Al[i] = v8h{static_cast<_Float16>(u.x), static_cast<_Float16>(u.y),
+                    static_cast<_Float16>(u.z), static_cast<_Float16>(u.w),
+                    static_cast<_Float16>(v.x), static_cast<_Float16>(v.y),
+                    static_cast<_Float16>(v.z), static_cast<_Float16>(v.w)};
+      } else {
+        Al[i] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int64_t n = n0 + wn * WT + j * 16 + rl;
+      if (kval && n < N)
+        Bl[j] = *reinterpret_cast<const v8h*>(L2t + n * R + kk);
+      else
+        Bl[j] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[i][j] = mfma_f16_16x16x32(Bl[j], Al[i], acc[i][j]);
+  }
+
+  // bias and store; lane holds columns 4q .. 4q+3 of row rl in each 16 x 16
+  // block, written as one 8-byte (fp16) or 16-byte (fp32) store when Y's
+  // address and row stride allow it
+  constexpr int ES = Y_F16 ? 2 : 4;
+  const bool vec = ((reinterpret_cast<uintptr_t>(Y) | static_cast<uintptr_t>(ldy * ES)) %
+                    (4 * ES)) == 0;
+  float bv[NB][4];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t n = n0 + wn * WT + j * 16 + 4 * q + e;
+      bv[j][e] = (bias != nullptr && n < N) ? bias[n] : 0.f;
+    }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int64_t m = m0 + wm * WT + i * 16 + rl;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int64_t n = n0 + wn * WT + j * 16 + 4 * q;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = acc[i][j][e] + bv[j][e];
+        if constexpr (GELU) v[e] = gelu_tanh_f32(v[e]);
+      }
+      if (vec && n + 3 < N) {
+        if constexpr (Y_F16) {
+          const uint32_t lo = static_cast<uint32_t>(f2h(v[0])) | (static_cast<uint32_t>(f2h(v[1])) << 16);
+          const uint32_t hi = static_cast<uint32_t>(f2h(v[2])) | (static_cast<uint32_t>(f2h(v[3])) << 16);
+          *reinterpret_cast<uint2*>(static_cast<_Float16*>(Y) + m * ldy + n) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(Y) + m * ldy + n) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (n + e < N) {
+            if constexpr (Y_F16)
+              static_cast<_Float16*>(Y)[m * ldy + n + e] = static_cast<_Float16>(v[e]);
+            else
+              static_cast<float*>(Y)[m * ldy + n + e] = v[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+}  // namespace svdq

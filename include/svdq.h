@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 3
+#define SVDQ_ABI_VERSION 4
 
 /* status codes */
 enum {
@@ -95,6 +95,8 @@ enum { SVDQ_ACT_NONE = 0, SVDQ_ACT_GELU_TANH = 1 };
 
 /* The only group size implemented. */
 #define SVDQ_GROUP 64
+/* Values per shared scale in the MXFP4 format. */
+#define SVDQ_MX_BLOCK 32
 /* Largest rank the device kernels accept. */
 #define SVDQ_MAX_RANK 256
 
@@ -142,6 +144,16 @@ int svdq_smoothing_factors(const float* x_absmax, const float* W, int64_t K, int
 int svdq_prepare_weights(const float* W, const float* lambda, int64_t K, int64_t N,
                          int32_t rank, int32_t group, float* inv_smooth, uint16_t* L1t,
                          uint16_t* L2t, uint8_t* w_codes, uint16_t* w_scales, double* sigma);
+
+/* Offline weight preparation for the MXFP4 format (see "MXFP4 format" below):
+ * the same inv_smooth, SVD split, L1t, L2t and sigma as svdq_prepare_weights,
+ * then the fp32 residual R in MXFP4 down K for each output column n:
+ *   w_codes: N x K/2 bytes (E2M1 codes, element 2j in the low nibble),
+ *   w_e8m0:  N x K/32 bytes (shared exponents, biased by 127).
+ * Constraints: K % 64 == 0, 0 <= rank <= min(K, N), N >= 1. */
+int svdq_prepare_weights_mx(const float* W, const float* lambda, int64_t K, int64_t N,
+                            int32_t rank, float* inv_smooth, uint16_t* L1t, uint16_t* L2t,
+                            uint8_t* w_codes, uint8_t* w_e8m0, double* sigma);
 
 /* LoRA concatenation without re-quantization (chattools.cn overview, main
  * features, LoRA item; SVDQuant abstract). The branch multiplies Xhat, so row
@@ -216,6 +228,51 @@ int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth
                 const uint16_t* w_scales, const float* bias, void* Y, int y_dtype, int64_t ldy,
                 int64_t M, int64_t K, int64_t N, int32_t group, void* ws, size_t ws_bytes,
                 int32_t activation, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * MXFP4 format (the CDNA4 counterpart of the 4-bit floating-point version of
+ * the method that the taicenter.com news page names for the newest hardware,
+ * section on hardware co-design for Blackwell GPUs, NVFP4 item; the pages give
+ * no format details). Reading implemented, after OCP "Microscaling Formats
+ * (MX) Specification" v1.0, for Xhat rows and residual columns alike, over
+ * each block v of 32 consecutive values along K:
+ *     e = max(floor(log2(max|v|)) - 2, -127)   (-127 for an all-zero block;
+ *         as a byte: the biased exponent field of max|v| minus 2, floored at 0)
+ *     E8M0 byte = e + 127;  code = E2M1 nearest to v / 2^e, ties to the even
+ *     code, magnitudes above 6 saturating to 6, sign bit kept (-0 is code 8)
+ * E2M1 codes s e1 e0 m: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 for m|e = 0..7,
+ * bit 3 the sign; two per byte, element 2j in the low nibble.
+ * Layouts: a_codes M x K/2 and w_codes N x K/2 bytes as above; a_e8m0
+ * M x K/32 and w_e8m0 N x K/32 bytes, row-major. Smoothing, the low-rank
+ * factors and D are as in the INT4 functions. Constraints and alignment as for
+ * the device functions above (the exponent arrays 16-byte aligned); K % 64 == 0.
+ *
+ * K1-MX: as svdq_quantize_act_lowrank_down with the MXFP4 quantizer. */
+int svdq_quantize_act_lowrank_down_mx(const void* X, int x_dtype, int64_t M, int64_t K,
+                                      int64_t ldx, const float* inv_smooth, const uint16_t* L1p,
+                                      int32_t R, uint8_t* a_codes, uint8_t* a_e8m0, float* D,
+                                      hipStream_t stream);
+
+/* K2-MX: Y[m,n] = sum_k deq(a)[m,k] * deq(w)[n,k] (products and sums in the
+ * matrix core's fp32 accumulation, deq = E2M1 value * 2^e of its block)
+ *                 + sum_r fp16(D[m,r]) * L2[r,n] + bias[n]
+ * then the activation (SVDQ_ACT_*) in fp32, rounded once to y_dtype. */
+int svdq_mx_gemm_lowrank_up(const uint8_t* a_codes, const uint8_t* a_e8m0,
+                            const uint8_t* w_codes, const uint8_t* w_e8m0, const float* D,
+                            const uint16_t* L2t, int32_t R, const float* bias, void* Y,
+                            int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
+                            int32_t activation, hipStream_t stream);
+
+/* Bytes of workspace svdq_linear_mx needs: a_codes, a_e8m0 and D, each
+ * 256-byte aligned inside the workspace (0 for invalid sizes). */
+size_t svdq_linear_mx_workspace_bytes(int64_t M, int64_t K, int32_t R);
+
+/* The whole MXFP4 layer: K1-MX then K2-MX on `stream`, intermediates in `ws`. */
+int svdq_linear_mx(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
+                   const uint16_t* L1p, const uint16_t* L2t, int32_t R, const uint8_t* w_codes,
+                   const uint8_t* w_e8m0, const float* bias, void* Y, int y_dtype, int64_t ldy,
+                   int64_t M, int64_t K, int64_t N, void* ws, size_t ws_bytes,
+                   int32_t activation, hipStream_t stream);
 
 /* Test hook: the exact integer partials P[m, n, g] for rows row0 .. row0+rows-1,
  * computed with the same operand unpacking and int8 matrix-core instruction

@@ -1,0 +1,274 @@
+"""GPU parity of the MXFP4 path (K1-MX, K2-MX, the whole layer) through the C
+ABI against the CPU oracle's MXFP4 functions.
+
+Bit-exact: the activation codes and E8M0 exponents (whole tensors). Within
+2e-3 * max|Y| and within an element-wise rounding bound: the layer output on
+sampled rows at the full sizes of the workloads, and on every element for the
+small and edge-case shapes (K an odd multiple of 64, ragged M and N, rank 0,
+fp32 in and out, subnormal, zero and signed-zero blocks, the fused GELU)."""
+import functools
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as wl
+from gpu_common import TOL_Y, d_stat_bound, dev, rel_err, sample_rows, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+SPECS = [(0, 0), (1, 0), (2, 0), (2, 1), (3, 0), (3, 2), (3, 4), (4, 0)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_post_quantized_smooth_amd  # noqa: F401  (raises if the library is missing)
+
+
+@functools.lru_cache(maxsize=4)
+def _mx_layer(cfg: int, li: int):
+    import bit_post_quantized_smooth_amd as sq
+    L, X, W = wl.layer_inputs(cfg, li)
+    if X is None:
+        X = O.gelu_tanh(wl.preactivation(cfg, li, L.M, L.K, L.x_outlier_frac, L.x_outlier_scale))
+    lam = sq.smoothing_factors(sq.channel_absmax(X), W)
+    p = sq.prepare_weights_mx(W, lam, L.rank)
+    if L.lora_rank:
+        A, B = wl.lora(cfg, li, L.K, L.N, L.lora_rank)
+        p = sq.concat_lora(p, lam, A, B, 1.0)
+    return L, X, W, lam, p
+
+
+class MxDevice:
+    def __init__(self, X, p, bias, y_dtype="f16"):
+        torch = torch_mod()
+        self.M, self.K = X.shape
+        self.N, self.R = p.N, p.rank
+        self.X = dev(X)
+        self.inv = dev(p.inv_smooth)
+        self.L1p = dev(p.L1p) if self.R else None
+        self.L2t = dev(p.L2t) if self.R else None
+        self.wc = dev(p.w_codes)
+        self.we = dev(p.w_scales)
+        self.bias = dev(bias) if bias is not None else None
+        self.a_codes = torch.empty((self.M, self.K // 2), dtype=torch.uint8, device="cuda")
+        self.a_e8 = torch.empty((self.M, self.K // 32), dtype=torch.uint8, device="cuda")
+        self.D = torch.empty((self.M, max(self.R, 1)), dtype=torch.float32, device="cuda")
+        self.Y = torch.empty((self.M, self.N),
+                             dtype=torch.float16 if y_dtype == "f16" else torch.float32, device="cuda")
+
+    def k1(self):
+        import bit_post_quantized_smooth_amd as sq
+        sq.quantize_act_lowrank_down_mx(self.X, self.inv, self.L1p, self.R, self.a_codes, self.a_e8,
+                                        self.D if self.R else None)
+
+    def k2(self, activation=None):
+        import bit_post_quantized_smooth_amd as sq
+        sq.mx_gemm_lowrank_up(self.a_codes, self.a_e8, self.wc, self.we, self.D if self.R else None,
+                              self.L2t, self.R, self.bias, self.Y, self.K, activation=activation)
+
+
+def _oracle_w(X, W, p, base_rank):
+    """The oracle's own 1/lambda and MXFP4 residual for the library's fp16 factors
+    (with a LoRA concatenated, the residual belongs to the SVD columns only)."""
+    lam = O.smoothing_factors(O.channel_absmax(X), W)
+    inv = O.inv_smoothing(lam)
+    wc, we = O.mx_quantize_residual_from_factors(W, lam, p.L1[:, :base_rank], p.L2[:base_rank])
+    return inv, wc, we
+
+
+def _exact_rows(X, inv, p, wc, we, bias, rows, activation=None, chunk=16):
+    """Oracle Y for the rows in fp64 before its final rounding, the magnitude
+    envelope |A| . |B|^T + |fp16(D)| . |L2| + |b| (of the pre-activation sum),
+    and the largest legitimate change of the low-rank term (fp16(D) rounding
+    the other way where D lies within the pre-kernel's error bound of an fp16
+    rounding boundary)."""
+    Ys, envs, jumps = [], [], []
+    K = X.shape[1]
+    L2a = np.abs(np.asarray(p.L2, dtype=np.float64))
+    B = O.mx_dequantize_blocks(O.unpack_codes4(wc), we)
+    for i in range(0, len(rows), chunk):
+        r = rows[i:i + chunk]
+        _, parts = O.mx_linear(X[r], inv, p.L1, p.L2, wc, we, bias, "f32", return_parts=True)
+        A = O.mx_dequantize_blocks(O.unpack_codes4(parts["a_codes"]), parts["a_e8m0"])
+        y = parts["acc"] + parts["lr"]
+        env = np.abs(A) @ np.abs(B).T + np.abs(O.to_f16(parts["D"]).astype(np.float64)) @ L2a
+        if bias is not None:
+            y = y + np.asarray(bias, dtype=np.float64)[None, :]
+            env += np.abs(np.asarray(bias, dtype=np.float64))[None, :]
+        delta = d_stat_bound(parts["xhat"], p.L1, K)
+        D = parts["D"]
+        step = np.abs(O.to_f16(D + delta).astype(np.float64) - O.to_f16(D - delta).astype(np.float64))
+        Ys.append(y)
+        envs.append(env)
+        jumps.append(step @ L2a)
+    return np.concatenate(Ys), np.concatenate(envs), np.concatenate(jumps)
+
+
+def _assert_strict(Yg, Ye, env, jump, out_dtype, K, R, activation=None):
+    """One ulp of the output type plus, per element, two fp32 roundings per
+    128-chunk of the matrix-core sum and one per 16 ranks of the low-rank sum
+    (and a few more), each at most 2^-24 of the envelope, plus the low-rank
+    jump. With the GELU the bound on the sum is carried through the GELU's
+    slope (below 1.13 in magnitude) and the fp32 GELU's own few ulps."""
+    Yg = np.asarray(Yg, dtype=np.float64)
+    slack = (2 * (K // 128 + 1) + R / 16 + 4) * 2.0 ** -24 * env + jump
+    if activation == "gelu_tanh":
+        Yref = O.gelu_tanh_f64(Ye)
+        slack = 1.13 * slack + 8 * 2.0 ** -24 * np.abs(Yref) + 2.0 ** -30
+    else:
+        Yref = Ye
+    a = np.abs(Yref)
+    if out_dtype == "f16":
+        ulp = np.maximum(np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -14))) - 10), 2.0 ** -24)
+    else:
+        ulp = np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -126))) - 23)
+    ratio = np.abs(Yg - Yref) / (ulp + slack)
+    assert float(ratio.max()) <= 1.0, (int(np.count_nonzero(ratio > 1)), float(ratio.max()))
+
+
+@pytest.mark.parametrize("spec", SPECS, ids=lambda s: f"c{s[0]}l{s[1]}")
+def test_k1_mx_codes_exponents_bit_exact(spec):
+    torch = torch_mod()
+    L, X, W, lam, p = _mx_layer(*spec)
+    inv, wc, we = _oracle_w(X, W, p, L.rank)
+    assert np.array_equal(inv, p.inv_smooth)
+    assert np.array_equal(wc, p.w_codes) and np.array_equal(we, p.w_scales)
+    d = MxDevice(X, p, None, L.y_dtype)
+    d.k1()
+    torch.cuda.synchronize()
+    a_codes, a_e8, xh = O.mx_quantize_activation(X, inv)
+    got_c = d.a_codes.cpu().numpy()
+    nbad = int(np.count_nonzero(got_c != a_codes))
+    assert nbad == 0, f"{nbad} code bytes differ"
+    assert np.array_equal(d.a_e8.cpu().numpy(), a_e8)
+    if p.rank:
+        Dg = d.D.cpu().numpy()[:, :p.rank].astype(np.float64)
+        Do = O.down_projection(xh, p.L1)
+        worst = float(np.max(np.abs(Dg - Do) / (d_stat_bound(xh, p.L1, L.K) + 1e-30)))
+        assert worst <= 1.0, worst
+
+
+@pytest.mark.parametrize("spec", SPECS, ids=lambda s: f"c{s[0]}l{s[1]}")
+def test_mx_linear_matches_oracle(spec):
+    import bit_post_quantized_smooth_amd as sq
+    torch = torch_mod()
+    L, X, W, lam, p = _mx_layer(*spec)
+    bias = wl.bias(spec[0], spec[1], L.N)
+    inv, wc, we = _oracle_w(X, W, p, L.rank)
+    d = MxDevice(X, p, bias, L.y_dtype)
+    d.k1()
+    d.k2()
+    Y2 = torch.empty_like(d.Y)
+    wsb = torch.empty(sq.linear_mx_workspace_bytes(L.M, L.K, p.rank), dtype=torch.uint8, device="cuda")
+    sq.linear_mx(d.X, d.inv, d.L1p, d.L2t, p.rank, d.wc, d.we, d.bias, Y2, wsb)
+    torch.cuda.synchronize()
+    Yg = d.Y.cpu().numpy()
+    assert np.array_equal(Yg.view(np.uint8), Y2.cpu().numpy().view(np.uint8))
+    assert np.all(np.isfinite(Yg))
+    rows = sample_rows(L.M, seed=spec[0] * 100 + spec[1] + 7)
+    Yo = np.concatenate([O.mx_linear(X[rows[i:i + 16]], inv, p.L1, p.L2, wc, we, bias, L.y_dtype)
+                         for i in range(0, len(rows), 16)])
+    err = rel_err(Yg[rows], Yo)
+    assert err <= TOL_Y, err
+    Ye, env, jump = _exact_rows(X, inv, p, wc, we, bias, rows)
+    _assert_strict(Yg[rows], Ye, env, jump, L.y_dtype, L.K, p.rank)
+
+
+EDGE = [
+    # M, K, N, R, x_dtype, y_dtype, bias, activation
+    (1, 64, 1, 0, "f32", "f32", True, None),            # one half chunk
+    (17, 192, 130, 16, "f16", "f16", True, None),       # K % 128 == 64
+    (129, 320, 257, 48, "f16", "f32", False, None),
+    (200, 384, 320, 32, "f32", "f16", True, "gelu_tanh"),
+    (64, 1024, 512, 256, "f16", "f16", True, None),
+    (300, 640, 136, 80, "f16", "f16", False, "gelu_tanh"),
+    (33, 128, 600, 16, "f32", "f16", True, None),
+    (50, 256, 200, 112, "f16", "f16", True, None),
+]
+
+
+def _edge_inputs(M, K, N, xdt, seed):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((M, K))
+    X[:, rng.choice(K, max(1, K // 100), replace=False)] *= 20
+    # special blocks: all zero, signed zeros, tiny (subnormal Xhat for fp32 X)
+    X[M // 2, :32] = 0.0
+    if K >= 128:
+        X[M // 3, 64:96] = -0.0
+        X[M // 3, 96:128] *= 1e-40 if xdt == "f32" else 1e-7
+    X = X.astype(np.float16 if xdt == "f16" else np.float32)
+    W = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    W[rng.choice(K, max(1, K // 100), replace=False)] *= 10
+    b = (rng.standard_normal(N) * 0.1).astype(np.float32)
+    return X, W, b
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: "x".join(map(str, c[:4])) + f"_{c[4]}_{c[5]}_{c[7]}")
+def test_mx_edge_shapes_every_element(case):
+    import bit_post_quantized_smooth_amd as sq
+    torch = torch_mod()
+    M, K, N, R, xdt, ydt, use_bias, act = case
+    X, W, b = _edge_inputs(M, K, N, xdt, seed=M * 29 + K + N + R)
+    lam = sq.smoothing_factors(sq.channel_absmax(X), W)
+    p = sq.prepare_weights_mx(W, lam, R)
+    bias = b if use_bias else None
+    inv, wc, we = _oracle_w(X, W, p, R)
+    assert np.array_equal(wc, p.w_codes) and np.array_equal(we, p.w_scales)
+    d = MxDevice(X, p, bias, ydt)
+    d.k1()
+    d.k2(act)
+    torch.cuda.synchronize()
+    a_codes, a_e8, xh = O.mx_quantize_activation(X, inv)
+    assert np.array_equal(d.a_codes.cpu().numpy(), a_codes)
+    assert np.array_equal(d.a_e8.cpu().numpy(), a_e8)
+    Yg = d.Y.cpu().numpy()
+    Yo = O.mx_linear(X, inv, p.L1, p.L2, wc, we, bias, ydt, activation=act)
+    assert rel_err(Yg, Yo) <= TOL_Y
+    Ye, env, jump = _exact_rows(X, inv, p, wc, we, bias, np.arange(M))
+    _assert_strict(Yg, Ye, env, jump, ydt, K, R, act)
+
+
+def test_mx_and_int4_share_the_low_rank_branch():
+    """Both formats share the smoothing and the fp16 factors, so the difference of
+    their device outputs is the difference of their oracles' outputs (the
+    low-rank branch and the bias cancel)."""
+    import bit_post_quantized_smooth_amd as sq
+    torch = torch_mod()
+    M, K, N, R = 96, 256, 160, 32
+    X, W, b = _edge_inputs(M, K, N, "f16", seed=99)
+    lam = sq.smoothing_factors(sq.channel_absmax(X), W)
+    pm = sq.prepare_weights_mx(W, lam, R)
+    pi = sq.prepare_weights(W, lam, R)
+    assert np.array_equal(pm.L1t, pi.L1t) and np.array_equal(pm.L2t, pi.L2t)
+    Ym = sq.Linear(pm, b, out_dtype=torch.float32)(dev(X))
+    Yi = sq.Linear(pi, b, out_dtype=torch.float32)(dev(X))
+    torch.cuda.synchronize()
+    inv, wc, we = _oracle_w(X, W, pm, R)
+    Yo_m = O.mx_linear(X, inv, pm.L1, pm.L2, wc, we, b, "f32").astype(np.float64)
+    wci, wsi = O.quantize_residual_from_factors(W, lam, pi.L1, pi.L2)
+    Yo_i = O.linear(X, inv, pi.L1, pi.L2, wci, wsi, b, "f32").astype(np.float64)
+    diff_g = Ym.cpu().numpy().astype(np.float64) - Yi.cpu().numpy().astype(np.float64)
+    assert rel_err(diff_g, Yo_m - Yo_i) <= 1e-4
+
+
+def test_mx_repeatable_and_any_stream():
+    """Same bits on a second call, on a side stream, and through Linear."""
+    import bit_post_quantized_smooth_amd as sq
+    torch = torch_mod()
+    L, X, W, lam, p = _mx_layer(0, 0)
+    lin = sq.Linear(p, wl.bias(0, 0, L.N))
+    Xd = dev(X)
+    Y1 = lin(Xd)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        Y2 = lin(Xd)
+    s.synchronize()
+    Y3 = lin(Xd)
+    torch.cuda.synchronize()
+    b1 = Y1.cpu().numpy().view(np.uint16)
+    assert np.array_equal(b1, Y2.cpu().numpy().view(np.uint16))
+    assert np.array_equal(b1, Y3.cpu().numpy().view(np.uint16))

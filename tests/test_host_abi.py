@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert _lib.abi_version() == 3
+    assert _lib.abi_version() == 4
     for s in range(12):
         assert _lib.status_str(s) and _lib.status_str(s) != "unknown status"
     assert _lib.status_str(99) == "unknown status"
@@ -97,6 +97,49 @@ def test_prepare_codes_bit_exact(K, N, r):
         # canonical sign: the largest-magnitude entry of each column of L1 is positive
         idx = np.argmax(np.abs(L1), axis=0)
         assert np.all(L1[idx, np.arange(r)] > 0)
+
+
+@pytest.mark.parametrize("K,N,r", [(64, 16, 0), (128, 96, 16), (320, 40, 32), (512, 512, 16)])
+def test_prepare_mx_bit_exact(K, N, r):
+    """MXFP4 prep: the same factors as the INT4 prep, and residual codes and
+    E8M0 exponents equal to the oracle's for those factors."""
+    rng = np.random.default_rng(K * 5 + N + r)
+    X = rng.standard_normal((64, K)).astype(np.float32)
+    X[:, rng.choice(K, 3, replace=False)] *= 20
+    W = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    W[rng.choice(K, 2, replace=False)] *= 10
+    W[:, 3 % N] = 0.0                                  # an all-zero column: E8M0 0, codes 0
+    lam = O.smoothing_factors(O.channel_absmax(X), W)
+    p = sq.prepare_weights_mx(W, lam, r)
+    assert p.fmt == "mxfp4" and p.w_scales.shape == (N, K // 32) and p.w_codes.shape == (N, K // 2)
+    pi = sq.prepare_weights(W, lam, r)
+    assert np.array_equal(p.L1t, pi.L1t) and np.array_equal(p.L2t, pi.L2t)
+    assert np.array_equal(p.inv_smooth, pi.inv_smooth)
+    wc, we = O.mx_quantize_residual_from_factors(W, lam, p.L1, p.L2)
+    assert np.array_equal(p.w_codes, wc)
+    assert np.array_equal(p.w_scales, we)
+
+
+def test_prepare_mx_extreme_values():
+    """Columns that are tiny (subnormal fp32), huge, exactly on E2M1 midpoints, or
+    signed zeros: host codes equal the oracle's."""
+    K, N = 128, 6
+    W = np.zeros((K, N), dtype=np.float32)
+    rng = np.random.default_rng(77)
+    W[:, 0] = rng.standard_normal(K) * 1e-41          # subnormal
+    W[:, 1] = rng.standard_normal(K) * 1e37
+    W[:, 2] = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], K) * rng.choice([-1, 1], K)
+    W[:, 3] = -0.0
+    W[::2, 4] = -0.0
+    W[1::2, 4] = 1e-3
+    W[:, 5] = rng.standard_normal(K)
+    lam = np.ones(K, dtype=np.float32)
+    p = sq.prepare_weights_mx(W, lam, 0)
+    wc, we = O.mx_quantize_residual_from_factors(W, lam, np.zeros((K, 0), np.float16),
+                                                 np.zeros((0, N), np.float16))
+    assert np.array_equal(p.w_codes, wc)
+    assert np.array_equal(p.w_scales, we)
+    assert np.all(p.w_scales[3] == 0) and np.all(p.w_codes[3] == 0x88)   # -0 keeps its sign
 
 
 def test_prepare_full_rank_reconstructs():
@@ -178,6 +221,11 @@ def test_host_errors():
     assert L.svdq_pack_lowrank_down(bp, 96, 16, bp) == _lib.ERR_GROUP
     assert L.svdq_pack_lowrank_down(bp, 64, 24, bp) == _lib.ERR_RANK
     assert L.svdq_pack_lowrank_down(bp, 64, 0, bp) == _lib.ERR_RANK
+    # MXFP4 prep
+    assert L.svdq_prepare_weights_mx(W.ctypes.data, lam.ctypes.data, 128, 8, 4, bp, bp, bp, bp, None, None) == _lib.ERR_NULL
+    assert L.svdq_prepare_weights_mx(W.ctypes.data, lam.ctypes.data, 96, 8, 4, bp, bp, bp, bp, bp, None) == _lib.ERR_GROUP
+    assert L.svdq_prepare_weights_mx(W.ctypes.data, lam.ctypes.data, 128, 0, 0, bp, bp, bp, bp, bp, None) == _lib.ERR_SHAPE
+    assert L.svdq_prepare_weights_mx(W.ctypes.data, lam.ctypes.data, 128, 8, 9, bp, bp, bp, bp, bp, None) == _lib.ERR_RANK
 
 
 # Fake device addresses: never dereferenced because validation rejects the call
@@ -232,6 +280,35 @@ def test_device_entry_points_reject_bad_arguments():
     la[19] = 1
     la[17] = 0x10080
     assert L.svdq_linear(*la) == _lib.ERR_ALIGN
+    # MXFP4 K1 / K2 / layer
+    assert L.svdq_quantize_act_lowrank_down_mx(A16, 1, 16, 64, 64, A16, A16, 16, A16, None, A16, None) == _lib.ERR_NULL
+    assert L.svdq_quantize_act_lowrank_down_mx(A16, 1, 16, 96, 96, A16, A16, 16, A16, A16, A16, None) == _lib.ERR_GROUP
+    assert L.svdq_quantize_act_lowrank_down_mx(A16, 1, 16, 64, 64, A16, A16, 24, A16, A16, A16, None) == _lib.ERR_RANK
+    assert L.svdq_quantize_act_lowrank_down_mx(A16, 1, 16, 64, 64, A16, A16, 16, A16, MIS, A16, None) == _lib.ERR_ALIGN
+    assert L.svdq_quantize_act_lowrank_down_mx(A16, 3, 16, 64, 64, A16, A16, 16, A16, A16, A16, None) == _lib.ERR_DTYPE
+    mxa = [A16, A16, A16, A16, A16, A16, 16, None, A16, 1, 16, 16, 64, 16, 0, None]
+    bad = list(mxa); bad[3] = None
+    assert L.svdq_mx_gemm_lowrank_up(*bad) == _lib.ERR_NULL
+    bad = list(mxa); bad[1] = MIS                # activation exponents
+    assert L.svdq_mx_gemm_lowrank_up(*bad) == _lib.ERR_ALIGN
+    bad = list(mxa); bad[12] = 160
+    assert L.svdq_mx_gemm_lowrank_up(*bad) == _lib.ERR_GROUP
+    bad = list(mxa); bad[13] = 15
+    assert L.svdq_mx_gemm_lowrank_up(*bad) == _lib.ERR_SHAPE
+    bad = list(mxa); bad[14] = 3
+    assert L.svdq_mx_gemm_lowrank_up(*bad) == _lib.ERR_ACT
+    need_mx = L.svdq_linear_mx_workspace_bytes(16, 64, 16)
+    assert need_mx >= 16 * 32 + 16 * 2 + 16 * 16 * 4 and need_mx % 256 == 0
+    assert L.svdq_linear_mx_workspace_bytes(16, 96, 16) == 0
+    lm = [A16, 1, 64, A16, A16, A16, 16, A16, A16, None, A16, 1, 16, 16, 64, 16, A16, need_mx - 1, 0,
+          None]
+    assert L.svdq_linear_mx(*lm) == _lib.ERR_WORKSPACE
+    lm[17] = need_mx
+    lm[18] = 9
+    assert L.svdq_linear_mx(*lm) == _lib.ERR_ACT
+    lm[18] = 0
+    lm[16] = 0x10080
+    assert L.svdq_linear_mx(*lm) == _lib.ERR_ALIGN
     # partials hook: slice outside the rows
     assert L.svdq_debug_group_partials(A16, A16, 16, 16, 64, 64, 10, 7, A16, None) == _lib.ERR_SHAPE
     assert L.svdq_gelu_tanh_f16(A16, MIS, 8, None) == _lib.ERR_ALIGN
@@ -254,3 +331,5 @@ def test_device_entry_points_report_no_device():
     args = [A16, A16, A16, A16, A16, A16, 16, None, A16, 1, 16, 16, 64, 16, 64, 0, None]
     assert L.svdq_w4a4_gemm_lowrank_up(*args) == _lib.ERR_NO_DEVICE
     assert L.svdq_gelu_tanh_f16(A16, A16, 8, None) == _lib.ERR_NO_DEVICE
+    assert L.svdq_quantize_act_lowrank_down_mx(A16, 1, 16, 64, 64, A16, A16, 16, A16, A16, A16, None) == _lib.ERR_NO_DEVICE
+    assert L.svdq_mx_gemm_lowrank_up(A16, A16, A16, A16, A16, A16, 16, None, A16, 1, 16, 16, 64, 16, 0, None) == _lib.ERR_NO_DEVICE
