@@ -7,12 +7,14 @@ without a built library raises ImportError.
 from . import _lib  # noqa: F401  (fails loudly when libsvdq.so is missing)
 from .api import (Linear, Prepared, channel_absmax, concat_lora, debug_group_partials,  # noqa: F401
                   gelu_tanh_f16, linear, linear_mx, linear_mx_workspace_bytes,
-                  linear_workspace_bytes, mx_gemm_lowrank_up, pack_lowrank_down, prepare_weights,
+                  linear_workspace_bytes, mx_codes_tiled_bytes, mx_exps_tiled_bytes,
+                  mx_gemm_lowrank_up, pack_lowrank_down, pack_mx_tiles, prepare_weights,
                   prepare_weights_mx, quantize_act_lowrank_down, quantize_act_lowrank_down_mx,
                   smoothing_factors, w4a4_gemm_lowrank_up)
 
 __all__ = ["Linear", "Prepared", "channel_absmax", "concat_lora", "debug_group_partials",
            "gelu_tanh_f16", "linear", "linear_mx", "linear_mx_workspace_bytes",
-           "linear_workspace_bytes", "mx_gemm_lowrank_up", "pack_lowrank_down", "prepare_weights",
+           "linear_workspace_bytes", "mx_codes_tiled_bytes", "mx_exps_tiled_bytes",
+           "mx_gemm_lowrank_up", "pack_lowrank_down", "pack_mx_tiles", "prepare_weights",
            "prepare_weights_mx", "quantize_act_lowrank_down", "quantize_act_lowrank_down_mx",
            "smoothing_factors", "w4a4_gemm_lowrank_up"]

@@ -63,6 +63,9 @@ _SIGS = {
     "svdq_mx_gemm_lowrank_up": (_int, [_p, _p, _p, _p, _p, _p, _i32, _p, _p, _int, _i64, _i64,
                                        _i64, _i64, _i32, _p]),
     "svdq_linear_mx_workspace_bytes": (C.c_size_t, [_i64, _i64, _i32]),
+    "svdq_mx_codes_tiled_bytes": (C.c_size_t, [_i64, _i64]),
+    "svdq_mx_exps_tiled_bytes": (C.c_size_t, [_i64, _i64]),
+    "svdq_pack_mx_tiles": (_int, [_p, _p, _i64, _i64, _p, _p]),
     "svdq_linear_mx": (_int, [_p, _int, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _int, _i64, _i64,
                               _i64, _i64, _p, C.c_size_t, _i32, _p]),
     "svdq_debug_group_partials": (_int, [_p, _p, _i64, _i64, _i64, _i32, _i64, _i64, _p, _p]),

@@ -126,6 +126,27 @@ def prepare_weights_mx(W: np.ndarray, lam: np.ndarray, rank: int,
     return Prepared(K, N, rank, inv, L1t, L2t, wc, we, sig, fmt="mxfp4")
 
 
+def mx_codes_tiled_bytes(rows: int, K: int) -> int:
+    return int(lib.svdq_mx_codes_tiled_bytes(rows, K))
+
+
+def mx_exps_tiled_bytes(rows: int, K: int) -> int:
+    return int(lib.svdq_mx_exps_tiled_bytes(rows, K))
+
+
+def pack_mx_tiles(codes: np.ndarray, e8m0: np.ndarray, K: int):
+    """svdq_pack_mx_tiles: canonical MXFP4 codes (rows x K/2) and exponents
+    (rows x K/32) -> the tiled device layouts (flat uint8 arrays)."""
+    codes = _c(codes, np.uint8)
+    e8m0 = _c(e8m0, np.uint8)
+    rows = codes.shape[0]
+    ct = np.empty(mx_codes_tiled_bytes(rows, K), dtype=np.uint8)
+    et = np.empty(mx_exps_tiled_bytes(rows, K), dtype=np.uint8)
+    check(lib.svdq_pack_mx_tiles(_np_ptr(codes), _np_ptr(e8m0), rows, K, _np_ptr(ct), _np_ptr(et)),
+          "svdq_pack_mx_tiles")
+    return ct, et
+
+
 def concat_lora(prep: Prepared, lam: np.ndarray, A: np.ndarray, B: np.ndarray,
                 scale: float = 1.0) -> Prepared:
     A = _c(A, np.float16).view(np.uint16)
@@ -209,19 +230,22 @@ def linear(X, inv_smooth, L1p, L2t, R: int, w_codes, w_scales, bias, Y, ws, stre
                           _act(activation), _stream(stream)), "svdq_linear")
 
 
-def quantize_act_lowrank_down_mx(X, inv_smooth, L1p, R: int, a_codes, a_e8m0, D, stream=None):
+def quantize_act_lowrank_down_mx(X, inv_smooth, L1p, R: int, a_codes_t, a_exps_t, D, stream=None):
+    """K1-MX; a_codes_t / a_exps_t: device buffers of mx_codes_tiled_bytes(M, K) and
+    mx_exps_tiled_bytes(M, K) bytes (tiled layouts)."""
     M, K = X.shape
     check(lib.svdq_quantize_act_lowrank_down_mx(_tp(X), _dt(X), M, K, X.stride(0), _tp(inv_smooth),
-                                                _tp(L1p) if R else None, R, _tp(a_codes),
-                                                _tp(a_e8m0), _tp(D) if R else None,
+                                                _tp(L1p) if R else None, R, _tp(a_codes_t),
+                                                _tp(a_exps_t), _tp(D) if R else None,
                                                 _stream(stream)),
           "svdq_quantize_act_lowrank_down_mx")
 
 
-def mx_gemm_lowrank_up(a_codes, a_e8m0, w_codes, w_e8m0, D, L2t, R: int, bias, Y, K: int,
+def mx_gemm_lowrank_up(a_codes_t, a_exps_t, w_codes_t, w_exps_t, D, L2t, R: int, bias, Y, K: int,
                        stream=None, activation=None):
+    """K2-MX on the tiled activation and weight codes and exponents."""
     M, N = Y.shape
-    check(lib.svdq_mx_gemm_lowrank_up(_tp(a_codes), _tp(a_e8m0), _tp(w_codes), _tp(w_e8m0),
+    check(lib.svdq_mx_gemm_lowrank_up(_tp(a_codes_t), _tp(a_exps_t), _tp(w_codes_t), _tp(w_exps_t),
                                       _tp(D) if R else None, _tp(L2t) if R else None, R, _tp(bias),
                                       _tp(Y), _dt(Y), M, N, K, Y.stride(0), _act(activation),
                                       _stream(stream)),
@@ -232,13 +256,14 @@ def linear_mx_workspace_bytes(M: int, K: int, R: int) -> int:
     return int(lib.svdq_linear_mx_workspace_bytes(M, K, R))
 
 
-def linear_mx(X, inv_smooth, L1p, L2t, R: int, w_codes, w_e8m0, bias, Y, ws, stream=None,
+def linear_mx(X, inv_smooth, L1p, L2t, R: int, w_codes_t, w_exps_t, bias, Y, ws, stream=None,
               activation=None):
+    """The whole MXFP4 layer; the weights in the tiled layouts (pack_mx_tiles)."""
     M, K = X.shape
     N = Y.shape[1]
     check(lib.svdq_linear_mx(_tp(X), _dt(X), X.stride(0), _tp(inv_smooth),
-                             _tp(L1p) if R else None, _tp(L2t) if R else None, R, _tp(w_codes),
-                             _tp(w_e8m0), _tp(bias), _tp(Y), _dt(Y), Y.stride(0), M, K, N, _tp(ws),
+                             _tp(L1p) if R else None, _tp(L2t) if R else None, R, _tp(w_codes_t),
+                             _tp(w_exps_t), _tp(bias), _tp(Y), _dt(Y), Y.stride(0), M, K, N, _tp(ws),
                              ws.numel() * ws.element_size(), _act(activation), _stream(stream)),
           "svdq_linear_mx")
 
@@ -271,10 +296,12 @@ class Linear:
         self.L1p = torch.from_numpy(prep.L1p.view(np.int16)).to(dev) if self.R else None
         self.L2t = torch.from_numpy(prep.L2t.view(np.int16)).to(dev) if self.R else None
         self.fmt = prep.fmt
-        self.w_codes = torch.from_numpy(prep.w_codes).to(dev)
         if self.fmt == "mxfp4":
-            self.w_scales = torch.from_numpy(prep.w_scales).to(dev)
+            ct, et = pack_mx_tiles(prep.w_codes, prep.w_scales, prep.K)
+            self.w_codes = torch.from_numpy(ct).to(dev)
+            self.w_scales = torch.from_numpy(et).to(dev)
         else:
+            self.w_codes = torch.from_numpy(prep.w_codes).to(dev)
             self.w_scales = torch.from_numpy(prep.w_scales.view(np.int16)).to(dev)
         self.bias = None if bias is None else torch.from_numpy(_c(bias, np.float32)).to(dev)
         self.out_dtype = out_dtype

@@ -133,14 +133,20 @@ struct WsLayout {
   size_t codes, scales, d, total;
 };
 
-// INT4: fp16 scales, 2 bytes per 64 channels; MXFP4: 1 byte per 32 channels
+// INT4: codes M x K/2, fp16 scales M x K/64; MXFP4: the tiled codes and
+// exponents (ceil(M/16) and ceil(M/64) blocks of 1024 and 256 bytes per chunk
+// of 128 along K)
 WsLayout ws_layout(int64_t M, int64_t K, int32_t R, bool mx) {
   WsLayout w;
   w.codes = 0;
-  w.scales = round_up(static_cast<size_t>(M) * (K / 2), 256);
-  const size_t meta = mx ? static_cast<size_t>(M) * (K / SVDQ_MX_BLOCK)
-                         : static_cast<size_t>(M) * (K / SVDQ_GROUP) * 2;
-  w.d = w.scales + round_up(meta, 256);
+  if (mx) {
+    const size_t C = static_cast<size_t>((K + 127) / 128);
+    w.scales = round_up(static_cast<size_t>((M + 15) / 16) * C * 1024, 256);
+    w.d = w.scales + round_up(static_cast<size_t>((M + 63) / 64) * C * 256, 256);
+  } else {
+    w.scales = round_up(static_cast<size_t>(M) * (K / 2), 256);
+    w.d = w.scales + round_up(static_cast<size_t>(M) * (K / SVDQ_GROUP) * 2, 256);
+  }
   w.total = w.d + round_up(static_cast<size_t>(M) * R * 4, 256);
   return w;
 }

@@ -380,6 +380,58 @@ int svdq_prepare_weights_mx(const float* W, const float* lambda, int64_t K, int6
                         });
 }
 
+size_t svdq_mx_codes_tiled_bytes(int64_t rows, int64_t K) {
+  if (rows < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) return 0;
+  return static_cast<size_t>((rows + 15) / 16) * static_cast<size_t>((K + 127) / 128) * 1024;
+}
+
+size_t svdq_mx_exps_tiled_bytes(int64_t rows, int64_t K) {
+  if (rows < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) return 0;
+  return static_cast<size_t>((rows + 63) / 64) * static_cast<size_t>((K + 127) / 128) * 256;
+}
+
+int svdq_pack_mx_tiles(const uint8_t* codes, const uint8_t* e8m0, int64_t rows, int64_t K,
+                       uint8_t* codes_t, uint8_t* exps_t) {
+  clear_error();
+  if (!codes || !e8m0 || !codes_t || !exps_t) {
+    set_error("svdq_pack_mx_tiles: null pointer");
+    return SVDQ_ERR_NULL;
+  }
+  if (K < SVDQ_GROUP || K % SVDQ_GROUP != 0) {
+    set_error("svdq_pack_mx_tiles: K=%lld (need K %% 64 == 0)", (long long)K);
+    return SVDQ_ERR_GROUP;
+  }
+  if (rows < 1) {
+    set_error("svdq_pack_mx_tiles: rows=%lld", (long long)rows);
+    return SVDQ_ERR_SHAPE;
+  }
+  const int64_t C = (K + 127) / 128, kb = K / 2, ks = K / SVDQ_MX_BLOCK;
+  const int64_t nb = (rows + 15) / 16, ng = (rows + 63) / 64;
+  // codes: block (b, c), lane l = 16q + r: row 16b + r, bytes 64c + 16q .. +15
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nb; ++b)
+    for (int64_t c = 0; c < C; ++c)
+      for (int l = 0; l < 64; ++l) {
+        const int64_t row = 16 * b + (l & 15), off = 64 * c + 16 * (l >> 4);
+        uint8_t* dst = codes_t + ((b * C + c) * 64 + l) * 16;
+        if (row < rows && off < kb)
+          std::memcpy(dst, codes + row * kb + off, 16);
+        else
+          std::memset(dst, 0, 16);
+      }
+  // exponents: block (g, c), byte 4l + i: row 64g + 16i + r, 32-block 4c + q
+#pragma omp parallel for schedule(static)
+  for (int64_t g = 0; g < ng; ++g)
+    for (int64_t c = 0; c < C; ++c)
+      for (int l = 0; l < 64; ++l)
+        for (int i = 0; i < 4; ++i) {
+          const int64_t row = 64 * g + 16 * i + (l & 15), blk = 4 * c + (l >> 4);
+          exps_t[((g * C + c) * 64 + l) * 4 + i] =
+              (row < rows && blk < ks) ? e8m0[row * ks + blk] : uint8_t{127};
+        }
+  return SVDQ_OK;
+}
+
 int svdq_concat_lora(const uint16_t* L1t, const uint16_t* L2t, int64_t K, int64_t N, int32_t rank,
                      const float* lambda, const uint16_t* A, const uint16_t* B, int32_t rl,
                      float scale, uint16_t* L1t_out, uint16_t* L2t_out) {

@@ -200,7 +200,8 @@ struct GroupIn {
 
 constexpr int kXsStride = kGroup + 8;           // fp16 elements per row of the LDS tile
 
-// a_meta: the fp16 group scales (M x K/64) or, for MX, the E8M0 bytes (M x K/32)
+// a_codes, a_meta: INT4 codes (M x K/2) and fp16 group scales (M x K/64), or
+// for MX the tiled E2M1 codes and E8M0 exponents (see svdq.h)
 template <typename XT, int NCB, int NB, bool MX>
 __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
     const XT* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
@@ -237,6 +238,12 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
   // per row: G fp16 scales, or 2G E8M0 bytes (two per group, stored as one uint16)
   uint16_t* sblk = static_cast<uint16_t*>(a_meta) + row0 * G;
   const uint32_t soff = qr * static_cast<uint32_t>(G);
+  // MXFP4: the tiled code blocks of this workgroup's row block (one 1 KB block
+  // per chunk of 128) and the exponent blocks of its 64-row group, in which
+  // its rows are the byte ti = (row0 % 64) / 16 of each lane's dword
+  const int64_t nchunks = (K + 127) / 128;
+  uint8_t* tcode = a_codes + static_cast<int64_t>(blockIdx.x) * nchunks * 1024;
+  uint8_t* texp = static_cast<uint8_t*>(a_meta) + (row0 / 64) * nchunks * 256 + (row0 % 64) / 16;
 
   // packed operand (g, c, h) of this lane
   auto l1_operand = [&](int g, int c, int h) -> const v8h* {
@@ -323,8 +330,28 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
         }
       }
       if (i < n_mine && rvalid) {
-        *reinterpret_cast<uint2*>(cblk + g * kGroupBytes + coff) = make_uint2(packed[0], packed[1]);
-        if (c4 == 0) sblk[g + soff] = static_cast<uint16_t>(meta);
+        if constexpr (MX) {
+          // tiled layouts: group g is half h of chunk g/2; this lane's 16
+          // codes are the 8 bytes at 8*(c4%2) of lane 16*kq + qr of the chunk's
+          // block, kq = 2h + c4/2 (its 32-block within the chunk); the
+          // exponent of that 32-block (lanes c4 = 0, 2 hold the two) is byte
+          // ti of lane 16*kq + qr of the chunk's exponent block
+          const int c = g >> 1, h = g & 1;
+          const int kq = 2 * h + (c4 >> 1);
+          uint8_t* cb = tcode + static_cast<int64_t>(c) * 1024 + (16 * kq + qr) * 16 + 8 * (c4 & 1);
+          uint8_t* eb = texp + static_cast<int64_t>(c) * 256 + (16 * kq + qr) * 4;
+          *reinterpret_cast<uint2*>(cb) = make_uint2(packed[0], packed[1]);
+          if ((c4 & 1) == 0) eb[0] = static_cast<uint8_t>(meta & 0xFFu);
+          if (h == 0 && g == G - 1) {
+            // K % 128 == 64: the chunk's second half does not exist; zero codes
+            // and exponent 127 make it add exactly nothing
+            *reinterpret_cast<uint2*>(cb + 32 * 16) = make_uint2(0u, 0u);
+            if ((c4 & 1) == 0) eb[32 * 4] = 127;
+          }
+        } else {
+          *reinterpret_cast<uint2*>(cblk + g * kGroupBytes + coff) = make_uint2(packed[0], packed[1]);
+          if (c4 == 0) sblk[g + soff] = static_cast<uint16_t>(meta);
+        }
       }
       // Refill this slot only after the stores: issued right behind the matrix
       // instructions that read the slot's L1 operands, the loads corrupted

@@ -39,20 +39,20 @@ __device__ __forceinline__ void banded_tile(int t, int tiles_m, int tiles_n, int
   tn = r / rows;
 }
 
-// Epilogue of a 2*WT x 2*WT tile whose 4 waves each hold a WT x WT quarter in
-// fp32 accumulators (wave w: rows wm = w/2, columns wn = w%2; in each 16 x 16
+// Epilogue of a 2*WTM x 2*WTN tile whose 4 waves each hold a WTM x WTN quarter
+// in fp32 accumulators (wave w: rows wm = w/2, columns wn = w%2; in each 16 x 16
 // block a lane holds columns 4*(lane/16) .. +3 of row lane%16).
 // The low-rank branch (the Nunchaku engine fuses it into the low-bit kernel:
 // SVDQuant abstract; the disruptive-concepts.com post, section "Nunchaku:
 // Fusing Precision and Speed") runs as fp16 MFMAs on the same accumulators:
 // acc += fp16(D) . L2; then the bias, optionally the GELU, and one rounding
 // to the output type.
-template <int WT, bool Y_F16, bool GELU>
+template <int WTM, int WTN, bool Y_F16, bool GELU>
 __device__ __forceinline__ void lowrank_bias_store(
-    v4f (&acc)[WT / 16][WT / 16], const float* __restrict__ D, const uint16_t* __restrict__ L2t,
+    v4f (&acc)[WTM / 16][WTN / 16], const float* __restrict__ D, const uint16_t* __restrict__ L2t,
     int R, const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N,
     int64_t ldy, int64_t m0, int64_t n0) {
-  constexpr int NB = WT / 16;
+  constexpr int NBM = WTM / 16, NBN = WTN / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rl = lane & 15, q = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
@@ -60,10 +60,10 @@ __device__ __forceinline__ void lowrank_bias_store(
   for (int rc = 0; rc < R; rc += 32) {
     const int kk = rc + 8 * q;                       // this lane's 8 rank indices
     const bool kval = kk < R;                        // R % 16 == 0: whole 8-runs are valid or not
-    v8h Al[NB], Bl[NB];
+    v8h Al[NBM], Bl[NBN];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int64_t m = m0 + wm * WT + i * 16 + rl;
+    for (int i = 0; i < NBM; ++i) {
+      const int64_t m = m0 + wm * WTM + i * 16 + rl;
       if (kval && m < M) {
         const float4* dp = reinterpret_cast<const float4*>(D + m * R + kk);
         const float4 u = dp[0], v = dp[1];
@@ -76,17 +76,17 @@ __device__ __forceinline__ void lowrank_bias_store(
       }
     }
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int64_t n = n0 + wn * WT + j * 16 + rl;
+    for (int j = 0; j < NBN; ++j) {
+      const int64_t n = n0 + wn * WTN + j * 16 + rl;
       if (kval && n < N)
         Bl[j] = *reinterpret_cast<const v8h*>(L2t + n * R + kk);
       else
         Bl[j] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
     }
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
+    for (int i = 0; i < NBM; ++i)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) acc[i][j] = mfma_f16_16x16x32(Bl[j], Al[i], acc[i][j]);
+      for (int j = 0; j < NBN; ++j) acc[i][j] = mfma_f16_16x16x32(Bl[j], Al[i], acc[i][j]);
   }
 
   // bias and store; lane holds columns 4q .. 4q+3 of row rl in each 16 x 16
@@ -95,21 +95,21 @@ __device__ __forceinline__ void lowrank_bias_store(
   constexpr int ES = Y_F16 ? 2 : 4;
   const bool vec = ((reinterpret_cast<uintptr_t>(Y) | static_cast<uintptr_t>(ldy * ES)) %
                     (4 * ES)) == 0;
-  float bv[NB][4];
+  float bv[NBN][4];
 #pragma unroll
-  for (int j = 0; j < NB; ++j)
+  for (int j = 0; j < NBN; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int64_t n = n0 + wn * WT + j * 16 + 4 * q + e;
+      const int64_t n = n0 + wn * WTN + j * 16 + 4 * q + e;
       bv[j][e] = (bias != nullptr && n < N) ? bias[n] : 0.f;
     }
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int64_t m = m0 + wm * WT + i * 16 + rl;
+  for (int i = 0; i < NBM; ++i) {
+    const int64_t m = m0 + wm * WTM + i * 16 + rl;
     if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int64_t n = n0 + wn * WT + j * 16 + 4 * q;
+    for (int j = 0; j < NBN; ++j) {
+      const int64_t n = n0 + wn * WTN + j * 16 + 4 * q;
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {

@@ -285,7 +285,7 @@ __device__ __forceinline__ void gemm_tile(
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] *= 0.00390625f;
 
-  lowrank_bias_store<WT, Y_F16, GELU>(acc, D, L2t, R, bias, Y, M, N, ldy, m0, n0);
+  lowrank_bias_store<WT, WT, Y_F16, GELU>(acc, D, L2t, R, bias, Y, M, N, ldy, m0, n0);
 }
 
 // Workgroups 0 .. n_full-1 take the first n_full 128 x 128 tiles of the banded

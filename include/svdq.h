@@ -242,35 +242,64 @@ int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth
  *     code, magnitudes above 6 saturating to 6, sign bit kept (-0 is code 8)
  * E2M1 codes s e1 e0 m: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 for m|e = 0..7,
  * bit 3 the sign; two per byte, element 2j in the low nibble.
- * Layouts: a_codes M x K/2 and w_codes N x K/2 bytes as above; a_e8m0
- * M x K/32 and w_e8m0 N x K/32 bytes, row-major. Smoothing, the low-rank
- * factors and D are as in the INT4 functions. Constraints and alignment as for
- * the device functions above (the exponent arrays 16-byte aligned); K % 64 == 0.
+ * Canonical layouts (host side, as svdq_prepare_weights_mx writes them):
+ * codes rows x K/2 bytes and E8M0 exponents rows x K/32 bytes, row-major.
  *
- * K1-MX: as svdq_quantize_act_lowrank_down with the MXFP4 quantizer. */
+ * Tiled layouts (device side, what K1-MX writes and K2-MX reads): each load of
+ * the matrix instruction's operands becomes one contiguous run. With
+ * C = ceil(K/128) chunks of 128 values along K:
+ *   codes_t: ceil(rows/16) x C blocks of 1024 bytes; in block (b, c) lane
+ *     l = 16*q + r (q < 4, r < 16) holds bytes 16*l .. 16*l+15 =
+ *     canonical codes of row 16*b + r, bytes 64*c + 16*q .. +15;
+ *   exps_t: ceil(rows/64) x C blocks of 256 bytes; in block (g, c) byte
+ *     4*l + i (l = 16*q + r, i < 4) = E8M0 of row 64*g + 16*i + r, 32-block
+ *     4*c + q.
+ * Entries past the last row or past K (the second half of the last chunk when
+ * K % 128 == 64) hold zero codes and exponent 127 where svdq_pack_mx_tiles
+ * writes them; K1-MX writes the entries past K the same way and leaves rows
+ * past M unwritten (K2-MX never stores the outputs that depend on them).
+ * Smoothing, the low-rank factors and D are as in the INT4 functions.
+ * Constraints and alignment as for the device functions above (the tiled
+ * arrays 16-byte aligned); K % 64 == 0. */
+
+/* Bytes of the tiled layouts for `rows` rows of length K (0 for invalid sizes). */
+size_t svdq_mx_codes_tiled_bytes(int64_t rows, int64_t K);
+size_t svdq_mx_exps_tiled_bytes(int64_t rows, int64_t K);
+
+/* Host: canonical codes (rows x K/2) and exponents (rows x K/32) -> the tiled
+ * layouts above, padding included (a permutation, no arithmetic). Used for the
+ * weights, whose tiles are made once offline. Outputs must not overlap inputs. */
+int svdq_pack_mx_tiles(const uint8_t* codes, const uint8_t* e8m0, int64_t rows, int64_t K,
+                       uint8_t* codes_t, uint8_t* exps_t);
+
+/* K1-MX: as svdq_quantize_act_lowrank_down with the MXFP4 quantizer; a_codes_t
+ * and a_exps_t in the tiled layouts (svdq_mx_*_tiled_bytes(M, K) bytes). */
 int svdq_quantize_act_lowrank_down_mx(const void* X, int x_dtype, int64_t M, int64_t K,
                                       int64_t ldx, const float* inv_smooth, const uint16_t* L1p,
-                                      int32_t R, uint8_t* a_codes, uint8_t* a_e8m0, float* D,
+                                      int32_t R, uint8_t* a_codes_t, uint8_t* a_exps_t, float* D,
                                       hipStream_t stream);
 
 /* K2-MX: Y[m,n] = sum_k deq(a)[m,k] * deq(w)[n,k] (products and sums in the
  * matrix core's fp32 accumulation, deq = E2M1 value * 2^e of its block)
  *                 + sum_r fp16(D[m,r]) * L2[r,n] + bias[n]
- * then the activation (SVDQ_ACT_*) in fp32, rounded once to y_dtype. */
-int svdq_mx_gemm_lowrank_up(const uint8_t* a_codes, const uint8_t* a_e8m0,
-                            const uint8_t* w_codes, const uint8_t* w_e8m0, const float* D,
+ * then the activation (SVDQ_ACT_*) in fp32, rounded once to y_dtype.
+ * All four code and exponent arrays in the tiled layouts. */
+int svdq_mx_gemm_lowrank_up(const uint8_t* a_codes_t, const uint8_t* a_exps_t,
+                            const uint8_t* w_codes_t, const uint8_t* w_exps_t, const float* D,
                             const uint16_t* L2t, int32_t R, const float* bias, void* Y,
                             int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
                             int32_t activation, hipStream_t stream);
 
-/* Bytes of workspace svdq_linear_mx needs: a_codes, a_e8m0 and D, each
- * 256-byte aligned inside the workspace (0 for invalid sizes). */
+/* Bytes of workspace svdq_linear_mx needs: the tiled activation codes and
+ * exponents and D, each 256-byte aligned inside the workspace (0 for invalid
+ * sizes). */
 size_t svdq_linear_mx_workspace_bytes(int64_t M, int64_t K, int32_t R);
 
-/* The whole MXFP4 layer: K1-MX then K2-MX on `stream`, intermediates in `ws`. */
+/* The whole MXFP4 layer: K1-MX then K2-MX on `stream`, intermediates in `ws`;
+ * the weights in the tiled layouts. */
 int svdq_linear_mx(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
-                   const uint16_t* L1p, const uint16_t* L2t, int32_t R, const uint8_t* w_codes,
-                   const uint8_t* w_e8m0, const float* bias, void* Y, int y_dtype, int64_t ldy,
+                   const uint16_t* L1p, const uint16_t* L2t, int32_t R, const uint8_t* w_codes_t,
+                   const uint8_t* w_exps_t, const float* bias, void* Y, int y_dtype, int64_t ldy,
                    int64_t M, int64_t K, int64_t N, void* ws, size_t ws_bytes,
                    int32_t activation, hipStream_t stream);
 

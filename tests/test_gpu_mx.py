@@ -1,7 +1,9 @@
 """GPU parity of the MXFP4 path (K1-MX, K2-MX, the whole layer) through the C
 ABI against the CPU oracle's MXFP4 functions.
 
-Bit-exact: the activation codes and E8M0 exponents (whole tensors). Within
+Bit-exact: the activation codes and E8M0 exponents (whole tensors, read back
+from K1-MX's tiled layouts with the index formulas of svdq.h, including the
+zero half of the last chunk when K % 128 == 64). Within
 2e-3 * max|Y| and within an element-wise rounding bound: the layer output on
 sampled rows at the full sizes of the workloads, and on every element for the
 small and edge-case shapes (K an odd multiple of 64, ragged M and N, rank 0,
@@ -13,6 +15,7 @@ import pytest
 
 import oracle as O
 import workloads as wl
+import mx_tiles as T
 from gpu_common import TOL_Y, d_stat_bound, dev, rel_err, sample_rows, torch_mod
 
 pytestmark = pytest.mark.gpu
@@ -42,6 +45,24 @@ def _mx_layer(cfg: int, li: int):
     return L, X, W, lam, p
 
 
+def sq_mod():
+    import bit_post_quantized_smooth_amd as sq
+    return sq
+
+
+def read_act(d):
+    """K1-MX's tiled output as canonical codes (M x K/2) and exponents (M x K/32),
+    after checking the padding half of the last chunk (K % 128 == 64)."""
+    ct = d.a_codes.cpu().numpy()
+    et = d.a_e8.cpu().numpy()
+    c = T.untile_codes(ct, d.M, d.K)
+    e = T.untile_exps(et, d.M, d.K)
+    if d.K % 128:
+        assert not c[:d.M, d.K // 2:].any()
+        assert np.all(e[:d.M, d.K // 32:] == 127)
+    return c[:d.M, :d.K // 2], e[:d.M, :d.K // 32]
+
+
 class MxDevice:
     def __init__(self, X, p, bias, y_dtype="f16"):
         torch = torch_mod()
@@ -51,11 +72,15 @@ class MxDevice:
         self.inv = dev(p.inv_smooth)
         self.L1p = dev(p.L1p) if self.R else None
         self.L2t = dev(p.L2t) if self.R else None
-        self.wc = dev(p.w_codes)
-        self.we = dev(p.w_scales)
+        ct, et = sq_mod().pack_mx_tiles(p.w_codes, p.w_scales, self.K)
+        self.wc = dev(ct)
+        self.we = dev(et)
         self.bias = dev(bias) if bias is not None else None
-        self.a_codes = torch.empty((self.M, self.K // 2), dtype=torch.uint8, device="cuda")
-        self.a_e8 = torch.empty((self.M, self.K // 32), dtype=torch.uint8, device="cuda")
+        # K1-MX leaves rows past M unwritten: fill with a canary to show it
+        self.a_codes = torch.full((sq_mod().mx_codes_tiled_bytes(self.M, self.K),), 0x5A,
+                                  dtype=torch.uint8, device="cuda")
+        self.a_e8 = torch.full((sq_mod().mx_exps_tiled_bytes(self.M, self.K),), 0x5A,
+                               dtype=torch.uint8, device="cuda")
         self.D = torch.empty((self.M, max(self.R, 1)), dtype=torch.float32, device="cuda")
         self.Y = torch.empty((self.M, self.N),
                              dtype=torch.float16 if y_dtype == "f16" else torch.float32, device="cuda")
@@ -141,10 +166,10 @@ def test_k1_mx_codes_exponents_bit_exact(spec):
     d.k1()
     torch.cuda.synchronize()
     a_codes, a_e8, xh = O.mx_quantize_activation(X, inv)
-    got_c = d.a_codes.cpu().numpy()
+    got_c, got_e = read_act(d)
     nbad = int(np.count_nonzero(got_c != a_codes))
     assert nbad == 0, f"{nbad} code bytes differ"
-    assert np.array_equal(d.a_e8.cpu().numpy(), a_e8)
+    assert np.array_equal(got_e, a_e8)
     if p.rank:
         Dg = d.D.cpu().numpy()[:, :p.rank].astype(np.float64)
         Do = O.down_projection(xh, p.L1)
@@ -223,8 +248,9 @@ def test_mx_edge_shapes_every_element(case):
     d.k2(act)
     torch.cuda.synchronize()
     a_codes, a_e8, xh = O.mx_quantize_activation(X, inv)
-    assert np.array_equal(d.a_codes.cpu().numpy(), a_codes)
-    assert np.array_equal(d.a_e8.cpu().numpy(), a_e8)
+    got_c, got_e = read_act(d)
+    assert np.array_equal(got_c, a_codes)
+    assert np.array_equal(got_e, a_e8)
     Yg = d.Y.cpu().numpy()
     Yo = O.mx_linear(X, inv, p.L1, p.L2, wc, we, bias, ydt, activation=act)
     assert rel_err(Yg, Yo) <= TOL_Y

@@ -142,6 +142,33 @@ def test_prepare_mx_extreme_values():
     assert np.all(p.w_scales[3] == 0) and np.all(p.w_codes[3] == 0x88)   # -0 keeps its sign
 
 
+@pytest.mark.parametrize("rows,K", [(1, 64), (16, 128), (100, 320), (130, 1024), (64, 192)])
+def test_pack_mx_tiles_is_the_documented_layout(rows, K):
+    """svdq_pack_mx_tiles against the index formulas of svdq.h, written out in
+    numpy (tests/mx_tiles.py) and checked entry by entry on a sample; padding
+    rows and the missing half of the last chunk hold zero codes and exponent 127."""
+    import mx_tiles as T
+    rng = np.random.default_rng(rows * 7 + K)
+    c = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    e = rng.integers(0, 255, (rows, K // 32), dtype=np.uint8)
+    ct, et = sq.pack_mx_tiles(c, e, K)
+    C = (K + 127) // 128
+    assert ct.size == ((rows + 15) // 16) * C * 1024 == sq.mx_codes_tiled_bytes(rows, K)
+    assert et.size == ((rows + 63) // 64) * C * 256 == sq.mx_exps_tiled_bytes(rows, K)
+    assert np.array_equal(ct, T.tile_codes(c, K)) and np.array_equal(et, T.tile_exps(e, K))
+    assert np.array_equal(T.untile_codes(ct, rows, K)[:rows, :K // 2], c)
+    assert np.array_equal(T.untile_exps(et, rows, K)[:rows, :K // 32], e)
+    for _ in range(200):
+        b, cc, l = rng.integers(0, (rows + 15) // 16), rng.integers(0, C), rng.integers(0, 64)
+        j, g, i = rng.integers(0, 16), rng.integers(0, (rows + 63) // 64), rng.integers(0, 4)
+        row, byte = 16 * b + l % 16, 64 * cc + 16 * (l // 16) + j
+        want = c[row, byte] if row < rows and byte < K // 2 else 0
+        assert ct[((b * C + cc) * 64 + l) * 16 + j] == want
+        row, blk = 64 * g + 16 * i + l % 16, 4 * cc + l // 16
+        want = e[row, blk] if row < rows and blk < K // 32 else 127
+        assert et[((g * C + cc) * 64 + l) * 4 + i] == want
+
+
 def test_prepare_full_rank_reconstructs():
     rng = np.random.default_rng(5)
     K, N = 64, 48
@@ -221,6 +248,11 @@ def test_host_errors():
     assert L.svdq_pack_lowrank_down(bp, 96, 16, bp) == _lib.ERR_GROUP
     assert L.svdq_pack_lowrank_down(bp, 64, 24, bp) == _lib.ERR_RANK
     assert L.svdq_pack_lowrank_down(bp, 64, 0, bp) == _lib.ERR_RANK
+    # MXFP4 tiles
+    assert L.svdq_pack_mx_tiles(None, bp, 4, 64, bp, bp) == _lib.ERR_NULL
+    assert L.svdq_pack_mx_tiles(bp, bp, 4, 96, bp, bp) == _lib.ERR_GROUP
+    assert L.svdq_pack_mx_tiles(bp, bp, 0, 64, bp, bp) == _lib.ERR_SHAPE
+    assert L.svdq_mx_codes_tiled_bytes(0, 64) == 0 and L.svdq_mx_exps_tiled_bytes(4, 96) == 0
     # MXFP4 prep
     assert L.svdq_prepare_weights_mx(W.ctypes.data, lam.ctypes.data, 128, 8, 4, bp, bp, bp, bp, None, None) == _lib.ERR_NULL
     assert L.svdq_prepare_weights_mx(W.ctypes.data, lam.ctypes.data, 96, 8, 4, bp, bp, bp, bp, bp, None) == _lib.ERR_GROUP
