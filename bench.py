@@ -27,15 +27,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense FP4 / FP6 MFMA
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-PROFILE_PMC = os.path.join(ROOT, "profiles", "k2_dit_qkv_pmc.json")
-K2_SOURCES = ["bit_post_quantized_smooth_amd/csrc/k2_w4a4_gemm.hip",
-              "bit_post_quantized_smooth_amd/csrc/device_common.hpp"]
+# HBM traffic of the GEMM kernel from committed rocprofv3 FETCH/WRITE passes,
+# used only while the kernel's sources are unchanged since they were taken
+PROFILE_PMC = {"int4": os.path.join(ROOT, "profiles", "k2_dit_qkv_pmc.json"),
+               "mxfp4": os.path.join(ROOT, "profiles", "k2mx_dit_qkv_pmc.json")}
+_CSRC = "bit_post_quantized_smooth_amd/csrc/"
+K2_SOURCES = {"int4": [_CSRC + "k2_w4a4_gemm.hip", _CSRC + "k2_common.hpp",
+                       _CSRC + "device_common.hpp"],
+              "mxfp4": [_CSRC + "k2_mx_gemm.hip", _CSRC + "k2_common.hpp",
+                        _CSRC + "device_common.hpp"]}
 
 
-def k2_source_hash() -> str:
+def k2_source_hash(fmt: str = "int4") -> str:
     h = hashlib.sha256()
-    for p in K2_SOURCES:
+    for p in K2_SOURCES[fmt]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -57,6 +64,9 @@ def parse():
     ap.add_argument("--mlp", action="store_true",
                     help="time the DiT MLP pair instead: up-projection with the GELU fused into "
                          "its epilogue, then the down-projection")
+    ap.add_argument("--format", choices=["int4", "mxfp4"], default="int4",
+                    help="mxfp4: the MXFP4 variant (E2M1 codes, E8M0 exponent per 32) on the "
+                         "scaled FP4 matrix core")
     ap.add_argument("--unfused-gelu", action="store_true",
                     help="with --mlp: plain up-projection, then the separate GELU kernel")
     return ap.parse_args()
@@ -68,33 +78,44 @@ class Sets:
     def __init__(self, torch, X, prep, bias, n, y_dtype):
         import bit_post_quantized_smooth_amd as sq
         self.sq = sq
+        self.mx = prep.fmt == "mxfp4"
         M, K = X.shape
         self.M, self.K, self.N, self.R = M, K, prep.N, prep.rank
         G = K // 64
         d = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16
                                        else np.ascontiguousarray(a)).to("cuda")
+        if self.mx:
+            wct, wet = sq.pack_mx_tiles(prep.w_codes, prep.w_scales, K)
         self.sets = []
         for _ in range(n):
             s = dict(
                 X=d(X), inv=d(prep.inv_smooth),
                 L1p=d(prep.L1p) if self.R else None, L2t=d(prep.L2t) if self.R else None,
-                wc=d(prep.w_codes), ws=d(prep.w_scales), b=None if bias is None else d(bias),
-                ac=torch.empty((M, K // 2), dtype=torch.uint8, device="cuda"),
-                asc=torch.empty((M, G), dtype=torch.int16, device="cuda"),
+                b=None if bias is None else d(bias),
                 D=torch.empty((M, max(self.R, 1)), dtype=torch.float32, device="cuda"),
                 Y=torch.empty((M, self.N), dtype=torch.float16 if y_dtype == "f16" else torch.float32,
                               device="cuda"))
+            if self.mx:
+                s.update(wc=d(wct), ws=d(wet),
+                         ac=torch.empty(sq.mx_codes_tiled_bytes(M, K), dtype=torch.uint8, device="cuda"),
+                         asc=torch.empty(sq.mx_exps_tiled_bytes(M, K), dtype=torch.uint8, device="cuda"))
+            else:
+                s.update(wc=d(prep.w_codes), ws=d(prep.w_scales),
+                         ac=torch.empty((M, K // 2), dtype=torch.uint8, device="cuda"),
+                         asc=torch.empty((M, G), dtype=torch.int16, device="cuda"))
             self.sets.append(s)
 
     def k1(self, i):
         s = self.sets[i % len(self.sets)]
-        self.sq.quantize_act_lowrank_down(s["X"], s["inv"], s["L1p"], self.R, s["ac"], s["asc"],
-                                          s["D"] if self.R else None)
+        f = (self.sq.quantize_act_lowrank_down_mx if self.mx
+             else self.sq.quantize_act_lowrank_down)
+        f(s["X"], s["inv"], s["L1p"], self.R, s["ac"], s["asc"], s["D"] if self.R else None)
 
     def k2(self, i):
         s = self.sets[i % len(self.sets)]
-        self.sq.w4a4_gemm_lowrank_up(s["ac"], s["asc"], s["wc"], s["ws"], s["D"] if self.R else None,
-                                     s["L2t"], self.R, s["b"], s["Y"], self.K)
+        f = self.sq.mx_gemm_lowrank_up if self.mx else self.sq.w4a4_gemm_lowrank_up
+        f(s["ac"], s["asc"], s["wc"], s["ws"], s["D"] if self.R else None, s["L2t"], self.R, s["b"],
+          s["Y"], self.K)
 
 
 def time_steps(torch, sets, steps, warmup):
@@ -135,7 +156,8 @@ def event_gap(torch, reps=50):
 
 def cpu_baseline(X, W, prep, bias, budget_s):
     """The oracle's online part (quantize X, down-projection, integer partials,
-    scaled sum, up-projection, bias) on chunks of rows until ~budget_s seconds."""
+    scaled sum, up-projection, bias; or its MXFP4 counterpart) on chunks of rows
+    until ~budget_s seconds."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -144,7 +166,11 @@ def cpu_baseline(X, W, prep, bias, budget_s):
         cores = os.cpu_count()
     lam = O.smoothing_factors(O.channel_absmax(X), W)
     inv = O.inv_smoothing(lam)
-    wc, ws = O.quantize_residual_from_factors(W, lam, prep.L1, prep.L2)
+    mx = prep.fmt == "mxfp4"
+    if mx:
+        wc, ws = O.mx_quantize_residual_from_factors(W, lam, prep.L1, prep.L2)
+    else:
+        wc, ws = O.quantize_residual_from_factors(W, lam, prep.L1, prep.L2)
     M, K = X.shape
     N = W.shape[1]
     chunk = 32
@@ -152,7 +178,7 @@ def cpu_baseline(X, W, prep, bias, budget_s):
     t0 = time.perf_counter()
     while rows < M and time.perf_counter() - t0 < budget_s:
         r = slice(rows, min(M, rows + chunk))
-        O.linear(X[r], inv, prep.L1, prep.L2, wc, ws, bias, "f16")
+        (O.mx_linear if mx else O.linear)(X[r], inv, prep.L1, prep.L2, wc, ws, bias, "f16")
         rows = r.stop
     t = time.perf_counter() - t0
     return dict(value=2.0 * rows * N * K / t / 1e12, unit="TOPS", cores=int(cores), kind="oracle",
@@ -227,7 +253,9 @@ def main():
                                          L.x_outlier_scale))
     bias = None
     lam = sq.smoothing_factors(sq.channel_absmax(X), W)
-    prep = sq.prepare_weights(W, lam, L.rank)
+    mx = args.format == "mxfp4"
+    prepare = sq.prepare_weights_mx if mx else sq.prepare_weights
+    prep = prepare(W, lam, L.rank)
     if L.lora_rank:
         A, B = wl.lora(args.config, args.layer, L.K, L.N, L.lora_rank)
         prep = sq.concat_lora(prep, lam, A, B, 1.0)
@@ -241,21 +269,23 @@ def main():
     k2_avg = float(np.mean(k2)) - gap
     xb = 2 if L.x_dtype == "f16" else 4
     yb = 2 if L.y_dtype == "f16" else 4
-    k1_bytes = M * K * xb + M * K // 2 + 2 * M * (K // 64) + 4 * M * R + 2 * K * R + 4 * K
-    k2_bytes = (M + N) * K // 2 + 2 * (M + N) * (K // 64) + 4 * M * R + 2 * R * N + M * N * yb
+    meta = (K // 32) if mx else 2 * (K // 64)          # exponent or scale bytes per row
+    k1_bytes = M * K * xb + M * K // 2 + M * meta + 4 * M * R + 2 * K * R + 4 * K
+    k2_bytes = (M + N) * K // 2 + (M + N) * meta + 4 * M * R + 2 * R * N + M * N * yb
 
     traffic = None
-    if os.path.exists(PROFILE_PMC):
+    if os.path.exists(PROFILE_PMC[args.format]):
         try:
-            pm = json.load(open(PROFILE_PMC))
-            if pm.get("k2_source_hash") == k2_source_hash() and pm.get("config") == args.config:
+            pm = json.load(open(PROFILE_PMC[args.format]))
+            if (pm.get("k2_source_hash") == k2_source_hash(args.format)
+                    and pm.get("config") == args.config):
                 traffic = pm.get("hbm_bytes_per_launch")
         except Exception:
             traffic = None
 
     overhead = None
     if not args.no_overhead and R > 0:
-        prep0 = sq.prepare_weights(W, lam, 0)
+        prep0 = prepare(W, lam, 0)
         sets0 = Sets(torch, X, prep0, bias, args.sets, L.y_dtype)
         t0_step, _, k2_0 = time_steps(torch, sets0, args.steps, args.warmup)
         k2_0 = float(np.mean(k2_0)) - gap
@@ -271,10 +301,18 @@ def main():
             torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
 
+    if mx:
+        metric = "effective TFLOPS of the SVDQuant MXFP4+rank-32 linear, % of FP4 MFMA peak"
+        peak, unit, kname, dtype = FP4_PEAK_TFLOPS, "TFLOPS", "k2_mx_kernel", "fp4"
+        fmt_txt = "MXFP4 (E2M1, E8M0 per 32)"
+    else:
+        metric = "effective TOPS of SVDQuant W4A4+rank-32 linear, % of INT8 MFMA peak"
+        peak, unit, kname, dtype = INT8_PEAK_TOPS, "TOPS", "k2_w4a4_kernel", "int8"
+        fmt_txt = "INT4 per-64 groups"
     out = {
-        "metric": "effective TOPS of SVDQuant W4A4+rank-32 linear, % of INT8 MFMA peak",
+        "metric": metric,
         "value": round(value, 2),
-        "unit": "TOPS",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -282,15 +320,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": f"{cfg.name} layer {args.layer}: X {L.x_dtype} {M}x{K}, "
-                               f"W {K}x{N}, rank {R}, INT4 per-64 groups, Y {L.y_dtype}",
-                   "M": M, "K": K, "N": N, "rank": R, "group": 64, "buffer_sets": args.sets},
-        "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
-        "roofline": {"bound": "mfma", "kernel": "k2_w4a4_kernel",
-                     "achieved": round(ops / k2_avg / 1e12, 2), "peak": INT8_PEAK_TOPS,
-                     "unit": "TOPS", "frac": round(ops / k2_avg / 1e12 / INT8_PEAK_TOPS, 4),
+                               f"W {K}x{N}, rank {R}, {fmt_txt}, Y {L.y_dtype}",
+                   "M": M, "K": K, "N": N, "rank": R, "format": args.format,
+                   "buffer_sets": args.sets},
+        ("pct_fp4_peak" if mx else "pct_int8_peak"): round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "kernel": kname,
+                     "achieved": round(ops / k2_avg / 1e12, 2), "peak": peak,
+                     "unit": unit, "frac": round(ops / k2_avg / 1e12 / peak, 4),
                      "traffic": traffic, "algorithmic_bytes": k2_bytes,
                      "avg_ms": round(k2_avg * 1e3, 4),
                      "timing": "HIP events around each launch inside the timed steps, on the "
