@@ -181,7 +181,8 @@ def cpu_baseline(X, W, prep, bias, budget_s):
         (O.mx_linear if mx else O.linear)(X[r], inv, prep.L1, prep.L2, wc, ws, bias, "f16")
         rows = r.stop
     t = time.perf_counter() - t0
-    return dict(value=2.0 * rows * N * K / t / 1e12, unit="TOPS", cores=int(cores), kind="oracle",
+    return dict(value=2.0 * rows * N * K / t / 1e12, unit="TFLOPS" if mx else "TOPS",
+                cores=int(cores), kind="oracle",
                 sample=f"first {rows} of {M} rows of the same layer, online part only "
                        f"({t:.1f} s, numpy fp64, chunks of {chunk} rows)")
 

@@ -12,8 +12,9 @@
 // The MXFP4 instance (MX = true) replaces the quantizer step: per row and
 // block of 32 channels, the E8M0 exponent of the block's absmax and E2M1
 // codes (OCP Microscaling v1.0, the CDNA4 counterpart of the 4-bit float
-// version on the taicenter.com news page, hardware co-design section); the
-// rest of the kernel is the same.
+// version on the taicenter.com news page, hardware co-design section), and
+// the codes and exponents go out in the tiled layouts K2-MX reads (svdq.h);
+// the rest of the kernel is the same.
 //
 // Work split: a workgroup owns 16 rows; its waves (8, or 4 at high rank) take
 // the 64-channel groups round-robin.
