@@ -469,3 +469,42 @@ def mx_linear(X, inv_lam32, L1, L2, w_codes, w_e8m0, bias=None, out_dtype: str =
     if return_parts:
         return Y, dict(a_codes=a_codes, a_e8m0=a_e8, xhat=xh, D=D, acc=acc, lr=lr)
     return Y
+
+
+# --------------------------------------------------------------------------
+# 4-bit weight-only baseline (W4A16).
+#
+# The SVDQuant abstract (ai-digest.ru page) measures the method against a
+# baseline that quantizes only the weights to 4 bits, and gives no format for
+# it. The reading taken here: the same symmetric 4-bit group quantizer Q as
+# above, applied to W itself (per output column, groups of 64 along K; no
+# smoothing, no low-rank branch); activations stay fp16; each weight enters
+# the product dequantized to fp16, fp16(s * q), one rounding (what a fp16
+# weight-only kernel feeds its fp16 matrix unit); fp32-or-better accumulation,
+# one rounding of the output.
+
+
+def w4a16_prepare(W):
+    """(w_codes N x K/2, w_scales N x K/64 fp16): Q of W, down K per column."""
+    return quantize_weight(np.asarray(W, dtype=np.float64))
+
+
+def w4a16_dequant(w_codes, w_scales, group: int = GROUP) -> np.ndarray:
+    """N x K fp16 weights fp16(s * q) (the product is exact in fp64, then one
+    rounding to fp16)."""
+    q = unpack_nibbles(w_codes).astype(np.float64)
+    s = np.asarray(w_scales, dtype=np.float16).astype(np.float64)
+    N, K = q.shape
+    prod = q.reshape(N, K // group, group) * s[:, :, None]
+    return to_f16(prod.reshape(N, K))
+
+
+def w4a16_linear(X, w_codes, w_scales, bias=None, out_dtype: str = "f16") -> np.ndarray:
+    """Y = fp16(X) . fp16(s q)^T + b, exact in fp64 (each product of two fp16
+    values is exact, and so is their sum at these sizes), rounded once."""
+    Xh = to_f16(X).astype(np.float64)
+    Wd = w4a16_dequant(w_codes, w_scales).astype(np.float64)
+    y = Xh @ Wd.T
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    return y.astype(np.float16 if out_dtype == "f16" else np.float32)

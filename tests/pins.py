@@ -756,3 +756,91 @@ def check_mx_method_sanity(O):
 ALL_CHECKS += [check_golden_mx, check_golden_mx_linear, check_mx_bruteforce,
                check_mx_roundtrip_bound, check_mx_invariants, check_mx_linear_bruteforce,
                check_mx_method_sanity]
+
+
+# --------------------------------------------------------------------------
+# 4-bit weight-only baseline (W4A16): reading of the SVDQuant abstract's
+# comparison baseline (ai-digest.ru page)
+
+
+def check_golden_w4a16(O):
+    d = {}
+    with open(os.path.join(GOLDEN, "w4a16_tiny.txt")) as f:
+        for raw in f:
+            line = raw.split("#", 1)[0].strip()
+            if line:
+                tok = line.split()
+                d.setdefault(tok[0], []).append(tok[1:])
+    X = np.zeros((1, 64), dtype=np.float16)
+    for i, v in d["x"]:
+        X[0, int(i)] = float(v)
+    W = np.zeros((64, 1), dtype=np.float32)
+    for i, h in d["w"]:
+        W[int(i), 0] = bits_f32(int(h, 16))
+    wc, ws = O.w4a16_prepare(W)
+    deq = O.w4a16_dequant(wc, ws).astype(np.float64)
+    assert [float(deq[0, 0]), float(deq[0, 1])] == [float(t) for t in d["deq"][0]]
+    Y = O.w4a16_linear(X, wc, ws, None, "f32")
+    assert float(Y[0, 0]) == float(d["y"][0][0]), float(Y[0, 0])
+
+
+def check_w4a16_bruteforce(O, seed=61):
+    """Python loops: the group quantizer of pins.py, fp16(s q) by struct, exact sums."""
+    rng = np.random.default_rng(seed)
+    for (M, K, N) in [(3, 64, 5), (2, 128, 3)]:
+        X = (rng.standard_normal((M, K)) * 2).astype(np.float16)
+        W = (rng.standard_normal((K, N)) * 0.05).astype(np.float32)
+        W[3] *= 10
+        bias = (rng.standard_normal(N) * 0.1).astype(np.float32)
+        wc, ws = O.w4a16_prepare(W)
+        Y = O.w4a16_linear(X, wc, ws, bias, "f32")
+        for n in range(N):
+            deq = []
+            for g in range(K // 64):
+                q, s = py_quantize_group([float(W[k, n]) for k in range(64 * g, 64 * g + 64)])
+                deq += [py_f16(s * qq) for qq in q]
+            for m in range(M):
+                y = sum(float(X[m, k]) * deq[k] for k in range(K)) + float(bias[n])
+                assert abs(y - float(Y[m, n])) <= 1e-6 * max(1.0, abs(y)), (m, n, y, float(Y[m, n]))
+
+
+def check_w4a16_grid_identity(O, seed=67):
+    """Weights already on the quantization grid (fp16 scale times an integer in
+    -7..7, each product exact in fp16) come back unchanged, so the layer equals
+    fp16(X) . W exactly."""
+    rng = np.random.default_rng(seed)
+    K, N, M = 128, 6, 4
+    s = np.array([2.0 ** -6, 0.125, 0.75, 2.0 ** -10, 1.0, 0.5])
+    q = rng.integers(-7, 8, size=(K, N)).astype(np.float64)
+    q[0] = 7                                    # each group's absmax is 7 s ...
+    q[64] = -7
+    W = (q * s[None, :]).astype(np.float32)     # ... so Q recovers s and q exactly
+    wc, ws = O.w4a16_prepare(W)
+    deq = O.w4a16_dequant(wc, ws).astype(np.float64)
+    assert np.array_equal(deq, W.T.astype(np.float64))
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    Y = O.w4a16_linear(X, wc, ws, None, "f32").astype(np.float64)
+    ref = (X.astype(np.float64) @ W.astype(np.float64)).astype(np.float32).astype(np.float64)
+    assert np.array_equal(Y, ref)
+
+
+def check_w4a16_sanity(O):
+    """Against the W4A4 layer with lam = 1 and rank 0, whose weight codes are
+    the same (Q of W itself): the weight-only layer, which does not quantize
+    the activations, is closer to X.W on the tiny workload. (Against the
+    smoothed W4A4 layer it is not: the outlier rows of W dominate its groups.)"""
+    import workloads as wl
+    L, X, W = wl.layer_inputs(0, 0)
+    ref = X.astype(np.float16).astype(np.float64) @ W.astype(np.float64)
+    wc, ws = O.w4a16_prepare(W)
+    ones = np.ones(W.shape[0], dtype=np.float32)
+    p = O.prepare(W, ones, 0)
+    assert np.array_equal(p["w_codes"], wc) and np.array_equal(p["w_scales"], ws)
+    e16 = np.linalg.norm(O.w4a16_linear(X, wc, ws, None, "f32").astype(np.float64) - ref)
+    e44 = np.linalg.norm(O.linear(X, p["inv_smooth"], p["L1"], p["L2"], p["w_codes"],
+                                  p["w_scales"], None, "f32").astype(np.float64) - ref)
+    assert e16 < 0.8 * e44, (e16, e44)
+
+
+ALL_CHECKS += [check_golden_w4a16, check_w4a16_bruteforce, check_w4a16_grid_identity,
+               check_w4a16_sanity]

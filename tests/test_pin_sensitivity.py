@@ -217,6 +217,23 @@ def mut_mx_unsmoothed_activation(mp):
                lambda X, inv: orig(X, np.ones_like(np.asarray(inv, np.float32))))
 
 
+def mut_w4a16_unrounded_dequant(mp):
+    """The weight-only baseline's dequantized weights kept in fp64 (no fp16 rounding)."""
+    def f(wc, ws, group=64):
+        q = R.unpack_nibbles(wc).astype(np.float64)
+        s = np.asarray(ws, dtype=np.float16).astype(np.float64)
+        N, K = q.shape
+        return (q.reshape(N, K // group, group) * s[:, :, None]).reshape(N, K)
+    mp.setattr(R, "w4a16_dequant", f)
+
+
+def mut_w4a16_scale_group_shift(mp):
+    """Each group dequantized with its neighbour's scale."""
+    orig = _orig("w4a16_dequant")
+    mp.setattr(R, "w4a16_dequant",
+               lambda wc, ws, group=64: orig(wc, np.roll(np.asarray(ws), 1, axis=1), group))
+
+
 MUTATIONS = [mut_scale_div8, mut_ties_away, mut_nibble_order, mut_smoothing_inverted,
              mut_sigma_unsplit, mut_smallest_singulars, mut_residual_sign,
              mut_partials_group_shift, mut_drop_weight_scale, mut_drop_bias,
@@ -224,7 +241,8 @@ MUTATIONS = [mut_scale_div8, mut_ties_away, mut_nibble_order, mut_smoothing_inve
              mut_smooth_multiplies_lambda, mut_transposed_weight_groups, mut_clamp_8,
              mut_gelu_before_bias, mut_mx_ties_up, mut_mx_exponent_ceil,
              mut_mx_exponent_nearest, mut_mx_negative_zero_dropped, mut_mx_bias_128,
-             mut_mx_nibble_order, mut_mx_weight_blocks_along_n, mut_mx_unsmoothed_activation]
+             mut_mx_nibble_order, mut_mx_weight_blocks_along_n, mut_mx_unsmoothed_activation,
+             mut_w4a16_unrounded_dequant, mut_w4a16_scale_group_shift]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
