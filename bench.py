@@ -28,15 +28,19 @@ sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense FP4 / FP6 MFMA
+FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 # HBM traffic of the GEMM kernel from committed rocprofv3 FETCH/WRITE passes,
 # used only while the kernel's sources are unchanged since they were taken
 PROFILE_PMC = {"int4": os.path.join(ROOT, "profiles", "k2_dit_qkv_pmc.json"),
-               "mxfp4": os.path.join(ROOT, "profiles", "k2mx_dit_qkv_pmc.json")}
+               "mxfp4": os.path.join(ROOT, "profiles", "k2mx_dit_qkv_pmc.json"),
+               "w4a16": os.path.join(ROOT, "profiles", "k2w16_dit_qkv_pmc.json")}
 _CSRC = "bit_post_quantized_smooth_amd/csrc/"
 K2_SOURCES = {"int4": [_CSRC + "k2_w4a4_gemm.hip", _CSRC + "k2_common.hpp",
                        _CSRC + "device_common.hpp"],
               "mxfp4": [_CSRC + "k2_mx_gemm.hip", _CSRC + "k2_common.hpp",
+                        _CSRC + "device_common.hpp"],
+              "w4a16": [_CSRC + "k2_w4a16_gemm.hip", _CSRC + "k2_common.hpp",
                         _CSRC + "device_common.hpp"]}
 
 
@@ -64,9 +68,10 @@ def parse():
     ap.add_argument("--mlp", action="store_true",
                     help="time the DiT MLP pair instead: up-projection with the GELU fused into "
                          "its epilogue, then the down-projection")
-    ap.add_argument("--format", choices=["int4", "mxfp4"], default="int4",
+    ap.add_argument("--format", choices=["int4", "mxfp4", "w4a16"], default="int4",
                     help="mxfp4: the MXFP4 variant (E2M1 codes, E8M0 exponent per 32) on the "
-                         "scaled FP4 matrix core")
+                         "scaled FP4 matrix core; w4a16: the 4-bit weight-only baseline of the "
+                         "pages' speed comparison (fp16 activations, no low-rank branch)")
     ap.add_argument("--unfused-gelu", action="store_true",
                     help="with --mlp: plain up-projection, then the separate GELU kernel")
     return ap.parse_args()
@@ -79,6 +84,7 @@ class Sets:
         import bit_post_quantized_smooth_amd as sq
         self.sq = sq
         self.mx = prep.fmt == "mxfp4"
+        self.w16 = prep.fmt == "w4a16"
         M, K = X.shape
         self.M, self.K, self.N, self.R = M, K, prep.N, prep.rank
         G = K // 64
@@ -86,6 +92,8 @@ class Sets:
                                        else np.ascontiguousarray(a)).to("cuda")
         if self.mx:
             wct, wet = sq.pack_mx_tiles(prep.w_codes, prep.w_scales, K)
+        if self.w16:
+            wct, wet = sq.pack_w4a16_tiles(prep.w_codes, prep.w_scales, K)
         self.sets = []
         for _ in range(n):
             s = dict(
@@ -95,7 +103,11 @@ class Sets:
                 D=torch.empty((M, max(self.R, 1)), dtype=torch.float32, device="cuda"),
                 Y=torch.empty((M, self.N), dtype=torch.float16 if y_dtype == "f16" else torch.float32,
                               device="cuda"))
-            if self.mx:
+            if self.w16:
+                s.update(wc=d(wct), ws=d(wet),
+                         ac=torch.empty(sq.w4a16_x_tiled_bytes(M, K) // 2, dtype=torch.int16,
+                                        device="cuda"), asc=None)
+            elif self.mx:
                 s.update(wc=d(wct), ws=d(wet),
                          ac=torch.empty(sq.mx_codes_tiled_bytes(M, K), dtype=torch.uint8, device="cuda"),
                          asc=torch.empty(sq.mx_exps_tiled_bytes(M, K), dtype=torch.uint8, device="cuda"))
@@ -107,12 +119,18 @@ class Sets:
 
     def k1(self, i):
         s = self.sets[i % len(self.sets)]
+        if self.w16:
+            self.sq.w4a16_tile_activation(s["X"], s["ac"])
+            return
         f = (self.sq.quantize_act_lowrank_down_mx if self.mx
              else self.sq.quantize_act_lowrank_down)
         f(s["X"], s["inv"], s["L1p"], self.R, s["ac"], s["asc"], s["D"] if self.R else None)
 
     def k2(self, i):
         s = self.sets[i % len(self.sets)]
+        if self.w16:
+            self.sq.w4a16_gemm(s["ac"], s["wc"], s["ws"], s["b"], s["Y"], self.K)
+            return
         f = self.sq.mx_gemm_lowrank_up if self.mx else self.sq.w4a4_gemm_lowrank_up
         f(s["ac"], s["asc"], s["wc"], s["ws"], s["D"] if self.R else None, s["L2t"], self.R, s["b"],
           s["Y"], self.K)
@@ -167,7 +185,10 @@ def cpu_baseline(X, W, prep, bias, budget_s):
     lam = O.smoothing_factors(O.channel_absmax(X), W)
     inv = O.inv_smoothing(lam)
     mx = prep.fmt == "mxfp4"
-    if mx:
+    w16 = prep.fmt == "w4a16"
+    if w16:
+        wc, ws = O.w4a16_prepare(W)
+    elif mx:
         wc, ws = O.mx_quantize_residual_from_factors(W, lam, prep.L1, prep.L2)
     else:
         wc, ws = O.quantize_residual_from_factors(W, lam, prep.L1, prep.L2)
@@ -178,10 +199,13 @@ def cpu_baseline(X, W, prep, bias, budget_s):
     t0 = time.perf_counter()
     while rows < M and time.perf_counter() - t0 < budget_s:
         r = slice(rows, min(M, rows + chunk))
-        (O.mx_linear if mx else O.linear)(X[r], inv, prep.L1, prep.L2, wc, ws, bias, "f16")
+        if w16:
+            O.w4a16_linear(X[r], wc, ws, bias, "f16")
+        else:
+            (O.mx_linear if mx else O.linear)(X[r], inv, prep.L1, prep.L2, wc, ws, bias, "f16")
         rows = r.stop
     t = time.perf_counter() - t0
-    return dict(value=2.0 * rows * N * K / t / 1e12, unit="TFLOPS" if mx else "TOPS",
+    return dict(value=2.0 * rows * N * K / t / 1e12, unit="TFLOPS" if (mx or w16) else "TOPS",
                 cores=int(cores), kind="oracle",
                 sample=f"first {rows} of {M} rows of the same layer, online part only "
                        f"({t:.1f} s, numpy fp64, chunks of {chunk} rows)")
@@ -255,9 +279,10 @@ def main():
     bias = None
     lam = sq.smoothing_factors(sq.channel_absmax(X), W)
     mx = args.format == "mxfp4"
+    w16 = args.format == "w4a16"
     prepare = sq.prepare_weights_mx if mx else sq.prepare_weights
-    prep = prepare(W, lam, L.rank)
-    if L.lora_rank:
+    prep = sq.prepare_weights_w4a16(W) if w16 else prepare(W, lam, L.rank)
+    if L.lora_rank and not w16:
         A, B = wl.lora(args.config, args.layer, L.K, L.N, L.lora_rank)
         prep = sq.concat_lora(prep, lam, A, B, 1.0)
     M, K, N, R = L.M, L.K, L.N, prep.rank
@@ -271,8 +296,12 @@ def main():
     xb = 2 if L.x_dtype == "f16" else 4
     yb = 2 if L.y_dtype == "f16" else 4
     meta = (K // 32) if mx else 2 * (K // 64)          # exponent or scale bytes per row
-    k1_bytes = M * K * xb + M * K // 2 + M * meta + 4 * M * R + 2 * K * R + 4 * K
-    k2_bytes = (M + N) * K // 2 + (M + N) * meta + 4 * M * R + 2 * R * N + M * N * yb
+    if w16:   # tiling pass: read X, write fp16 tiles; GEMM: fp16 tiles, codes, scales, Y
+        k1_bytes = M * K * xb + 2 * M * K
+        k2_bytes = 2 * M * K + N * K // 2 + N * meta + M * N * yb
+    else:
+        k1_bytes = M * K * xb + M * K // 2 + M * meta + 4 * M * R + 2 * K * R + 4 * K
+        k2_bytes = (M + N) * K // 2 + (M + N) * meta + 4 * M * R + 2 * R * N + M * N * yb
 
     traffic = None
     if os.path.exists(PROFILE_PMC[args.format]):
@@ -285,7 +314,7 @@ def main():
             traffic = None
 
     overhead = None
-    if not args.no_overhead and R > 0:
+    if not args.no_overhead and R > 0 and not w16:
         prep0 = prepare(W, lam, 0)
         sets0 = Sets(torch, X, prep0, bias, args.sets, L.y_dtype)
         t0_step, _, k2_0 = time_steps(torch, sets0, args.steps, args.warmup)
@@ -302,7 +331,11 @@ def main():
             torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
 
-    if mx:
+    if w16:
+        metric = "effective TFLOPS of the 4-bit weight-only (W4A16) baseline linear, % of fp16 MFMA peak"
+        peak, unit, kname, dtype = FP16_PEAK_TFLOPS, "TFLOPS", "k2_w4a16_kernel", "fp16"
+        fmt_txt = "W4A16 baseline (INT4 weights per-64 groups, fp16 activations, no low-rank)"
+    elif mx:
         metric = "effective TFLOPS of the SVDQuant MXFP4+rank-32 linear, % of FP4 MFMA peak"
         peak, unit, kname, dtype = FP4_PEAK_TFLOPS, "TFLOPS", "k2_mx_kernel", "fp4"
         fmt_txt = "MXFP4 (E2M1, E8M0 per 32)"
@@ -327,7 +360,8 @@ def main():
                                f"W {K}x{N}, rank {R}, {fmt_txt}, Y {L.y_dtype}",
                    "M": M, "K": K, "N": N, "rank": R, "format": args.format,
                    "buffer_sets": args.sets},
-        ("pct_fp4_peak" if mx else "pct_int8_peak"): round(100.0 * value / peak, 2),
+        ("pct_fp16_peak" if w16 else "pct_fp4_peak" if mx else "pct_int8_peak"):
+            round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "kernel": kname,
                      "achieved": round(ops / k2_avg / 1e12, 2), "peak": peak,
                      "unit": unit, "frac": round(ops / k2_avg / 1e12 / peak, 4),
@@ -336,7 +370,8 @@ def main():
                      "timing": "HIP events around each launch inside the timed steps, on the "
                                "launch stream, less the gap of an empty event pair",
                      "event_gap_us": round(gap * 1e6, 2)},
-        "k1": {"kernel": "k1_quant_down_kernel", "avg_ms": round(k1_avg * 1e3, 4),
+        "k1": {"kernel": "tile_x_kernel" if w16 else "k1_quant_down_kernel",
+               "avg_ms": round(k1_avg * 1e3, 4),
                "algorithmic_bytes": k1_bytes, "achieved_gbs": round(k1_bytes / k1_avg / 1e9, 1),
                "peak_gbs": HBM_PEAK_GBS, "frac": round(k1_bytes / k1_avg / 1e9 / HBM_PEAK_GBS, 4)},
         "lowrank_overhead": None if overhead is None else {

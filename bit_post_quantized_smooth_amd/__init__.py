@@ -9,12 +9,16 @@ from .api import (Linear, Prepared, channel_absmax, concat_lora, debug_group_par
                   gelu_tanh_f16, linear, linear_mx, linear_mx_workspace_bytes,
                   linear_workspace_bytes, mx_codes_tiled_bytes, mx_exps_tiled_bytes,
                   mx_gemm_lowrank_up, pack_lowrank_down, pack_mx_tiles, prepare_weights,
-                  prepare_weights_mx, quantize_act_lowrank_down, quantize_act_lowrank_down_mx,
-                  smoothing_factors, w4a4_gemm_lowrank_up)
+                  prepare_weights_mx, prepare_weights_w4a16, pack_w4a16_tiles,
+                  quantize_act_lowrank_down, quantize_act_lowrank_down_mx, smoothing_factors,
+                  w4a4_gemm_lowrank_up, w4a16_gemm, w4a16_tile_activation, w4a16_x_tiled_bytes,
+                  linear_w4a16)
 
 __all__ = ["Linear", "Prepared", "channel_absmax", "concat_lora", "debug_group_partials",
            "gelu_tanh_f16", "linear", "linear_mx", "linear_mx_workspace_bytes",
            "linear_workspace_bytes", "mx_codes_tiled_bytes", "mx_exps_tiled_bytes",
            "mx_gemm_lowrank_up", "pack_lowrank_down", "pack_mx_tiles", "prepare_weights",
            "prepare_weights_mx", "quantize_act_lowrank_down", "quantize_act_lowrank_down_mx",
-           "smoothing_factors", "w4a4_gemm_lowrank_up"]
+           "smoothing_factors", "w4a4_gemm_lowrank_up", "prepare_weights_w4a16",
+           "pack_w4a16_tiles", "w4a16_gemm", "w4a16_tile_activation", "w4a16_x_tiled_bytes",
+           "linear_w4a16"]

@@ -68,6 +68,15 @@ _SIGS = {
     "svdq_pack_mx_tiles": (_int, [_p, _p, _i64, _i64, _p, _p]),
     "svdq_linear_mx": (_int, [_p, _int, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _int, _i64, _i64,
                               _i64, _i64, _p, C.c_size_t, _i32, _p]),
+    "svdq_prepare_weights_w4a16": (_int, [_p, _i64, _i64, _p, _p]),
+    "svdq_w4a16_codes_tiled_bytes": (C.c_size_t, [_i64, _i64]),
+    "svdq_w4a16_scales_tiled_bytes": (C.c_size_t, [_i64, _i64]),
+    "svdq_w4a16_x_tiled_bytes": (C.c_size_t, [_i64, _i64]),
+    "svdq_pack_w4a16_tiles": (_int, [_p, _p, _i64, _i64, _p, _p]),
+    "svdq_w4a16_tile_activation": (_int, [_p, _int, _i64, _i64, _i64, _p, _p]),
+    "svdq_w4a16_gemm": (_int, [_p, _p, _p, _p, _p, _int, _i64, _i64, _i64, _i64, _p]),
+    "svdq_linear_w4a16": (_int, [_p, _int, _i64, _p, _p, _p, _p, _int, _i64, _i64, _i64, _i64,
+                                 _p, C.c_size_t, _p]),
     "svdq_debug_group_partials": (_int, [_p, _p, _i64, _i64, _i64, _i32, _i64, _i64, _p, _p]),
     "svdq_gelu_tanh_f16": (_int, [_p, _p, _i64, _p]),
 }

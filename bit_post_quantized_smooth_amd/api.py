@@ -52,7 +52,8 @@ def smoothing_factors(x_absmax: np.ndarray, W: np.ndarray) -> np.ndarray:
 class Prepared:
     """Offline products for one layer, host side. L1t is R x K, L2t is N x R (fp16 bits).
     ``fmt`` "int4": w_scales are the fp16 group scales (N x K/64, as uint16 bits);
-    ``fmt`` "mxfp4": w_scales are the E8M0 block exponents (N x K/32, uint8)."""
+    ``fmt`` "mxfp4": w_scales are the E8M0 block exponents (N x K/32, uint8);
+    ``fmt`` "w4a16": the weight-only baseline, Q of W itself (rank 0, no smoothing)."""
     K: int
     N: int
     rank: int
@@ -145,6 +146,32 @@ def pack_mx_tiles(codes: np.ndarray, e8m0: np.ndarray, K: int):
     check(lib.svdq_pack_mx_tiles(_np_ptr(codes), _np_ptr(e8m0), rows, K, _np_ptr(ct), _np_ptr(et)),
           "svdq_pack_mx_tiles")
     return ct, et
+
+
+def prepare_weights_w4a16(W: np.ndarray) -> Prepared:
+    """svdq_prepare_weights_w4a16: the 4-bit weight-only baseline's weights
+    (the group quantizer on W itself; fmt "w4a16", rank 0)."""
+    W = _c(W, np.float32)
+    K, N = W.shape
+    wc = np.empty((N, K // 2), dtype=np.uint8)
+    ws = np.empty((N, K // GROUP), dtype=np.uint16)
+    check(lib.svdq_prepare_weights_w4a16(_np_ptr(W), K, N, _np_ptr(wc), _np_ptr(ws)),
+          "svdq_prepare_weights_w4a16")
+    return Prepared(K, N, 0, np.ones(K, dtype=np.float32), np.empty((0, K), np.uint16),
+                    np.empty((N, 0), np.uint16), wc, ws, None, fmt="w4a16")
+
+
+def pack_w4a16_tiles(w_codes: np.ndarray, w_scales: np.ndarray, K: int):
+    """svdq_pack_w4a16_tiles: canonical weight-only codes and fp16 scale bits ->
+    the tiled device layouts (flat uint8 codes, flat uint16 scale bits)."""
+    w_codes = _c(w_codes, np.uint8)
+    w_scales = _c(w_scales, np.uint16)
+    N = w_codes.shape[0]
+    ct = np.empty(int(lib.svdq_w4a16_codes_tiled_bytes(N, K)), dtype=np.uint8)
+    st = np.empty(int(lib.svdq_w4a16_scales_tiled_bytes(N, K)) // 2, dtype=np.uint16)
+    check(lib.svdq_pack_w4a16_tiles(_np_ptr(w_codes), _np_ptr(w_scales), N, K, _np_ptr(ct),
+                                    _np_ptr(st)), "svdq_pack_w4a16_tiles")
+    return ct, st
 
 
 def concat_lora(prep: Prepared, lam: np.ndarray, A: np.ndarray, B: np.ndarray,
@@ -268,6 +295,33 @@ def linear_mx(X, inv_smooth, L1p, L2t, R: int, w_codes_t, w_exps_t, bias, Y, ws,
           "svdq_linear_mx")
 
 
+def w4a16_x_tiled_bytes(M: int, K: int) -> int:
+    return int(lib.svdq_w4a16_x_tiled_bytes(M, K))
+
+
+def w4a16_tile_activation(X, x_t, stream=None):
+    """X (fp16 or fp32, M x K) -> x_t (w4a16_x_tiled_bytes(M, K) bytes), the tiled fp16 layout."""
+    M, K = X.shape
+    check(lib.svdq_w4a16_tile_activation(_tp(X), _dt(X), M, K, X.stride(0), _tp(x_t),
+                                         _stream(stream)), "svdq_w4a16_tile_activation")
+
+
+def w4a16_gemm(x_t, w_codes_t, w_scales_t, bias, Y, K: int, stream=None):
+    M, N = Y.shape
+    check(lib.svdq_w4a16_gemm(_tp(x_t), _tp(w_codes_t), _tp(w_scales_t), _tp(bias), _tp(Y), _dt(Y),
+                              M, N, K, Y.stride(0), _stream(stream)), "svdq_w4a16_gemm")
+
+
+def linear_w4a16(X, w_codes_t, w_scales_t, bias, Y, ws, stream=None):
+    """The weight-only baseline layer (tiling of X into ws, then the GEMM)."""
+    M, K = X.shape
+    N = Y.shape[1]
+    check(lib.svdq_linear_w4a16(_tp(X), _dt(X), X.stride(0), _tp(w_codes_t), _tp(w_scales_t),
+                                _tp(bias), _tp(Y), _dt(Y), Y.stride(0), M, K, N, _tp(ws),
+                                ws.numel() * ws.element_size(), _stream(stream)),
+          "svdq_linear_w4a16")
+
+
 def debug_group_partials(a_codes, w_codes, M: int, N: int, K: int, row0: int, rows: int, P,
                          stream=None):
     check(lib.svdq_debug_group_partials(_tp(a_codes), _tp(w_codes), M, N, K, GROUP, row0, rows,
@@ -296,7 +350,11 @@ class Linear:
         self.L1p = torch.from_numpy(prep.L1p.view(np.int16)).to(dev) if self.R else None
         self.L2t = torch.from_numpy(prep.L2t.view(np.int16)).to(dev) if self.R else None
         self.fmt = prep.fmt
-        if self.fmt == "mxfp4":
+        if self.fmt == "w4a16":
+            ct, st = pack_w4a16_tiles(prep.w_codes, prep.w_scales, prep.K)
+            self.w_codes = torch.from_numpy(ct).to(dev)
+            self.w_scales = torch.from_numpy(st.view(np.int16)).to(dev)
+        elif self.fmt == "mxfp4":
             ct, et = pack_mx_tiles(prep.w_codes, prep.w_scales, prep.K)
             self.w_codes = torch.from_numpy(ct).to(dev)
             self.w_scales = torch.from_numpy(et).to(dev)
@@ -311,8 +369,12 @@ class Linear:
 
     def workspace(self, M: int):
         torch = _torch()
-        need = (linear_mx_workspace_bytes(M, self.K, self.R) if self.fmt == "mxfp4"
-                else linear_workspace_bytes(M, self.K, self.R))
+        if self.fmt == "w4a16":
+            need = w4a16_x_tiled_bytes(M, self.K)
+        elif self.fmt == "mxfp4":
+            need = linear_mx_workspace_bytes(M, self.K, self.R)
+        else:
+            need = linear_workspace_bytes(M, self.K, self.R)
         if self.ws is None or self.ws.numel() < need:
             self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self.ws
@@ -322,6 +384,11 @@ class Linear:
         M = X.shape[0]
         if Y is None:
             Y = torch.empty((M, self.N), dtype=self.out_dtype or X.dtype, device=self.device)
+        if self.fmt == "w4a16":
+            if self.activation is not None:
+                raise ValueError("the weight-only baseline has no fused activation")
+            linear_w4a16(X, self.w_codes, self.w_scales, self.bias, Y, self.workspace(M), stream)
+            return Y
         run = linear_mx if self.fmt == "mxfp4" else linear
         run(X, self.inv_smooth, self.L1p, self.L2t, self.R, self.w_codes, self.w_scales,
             self.bias, Y, self.workspace(M), stream, self.activation)

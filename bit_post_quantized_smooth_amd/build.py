@@ -19,8 +19,8 @@ LIB = os.path.join(PKG, "libsvdq.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["k1_quant_down.hip", "k2_w4a4_gemm.hip", "k2_mx_gemm.hip", "gelu.hip",
-               "abi_device.hip"]
+HIP_SOURCES = ["k1_quant_down.hip", "k2_w4a4_gemm.hip", "k2_mx_gemm.hip", "k2_w4a16_gemm.hip",
+               "gelu.hip", "abi_device.hip"]
 HOST_SOURCES = {
     # the quantizer's fp32 divide/multiply must round exactly: no contraction
     "host_prep.cpp": ["-ffp-contract=off"],

@@ -314,6 +314,121 @@ int svdq_linear_mx(const void* X, int x_dtype, int64_t ldx, const float* inv_smo
                    "svdq_linear_mx K2 launch");
 }
 
+size_t svdq_w4a16_x_tiled_bytes(int64_t M, int64_t K) {
+  if (M < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) return 0;
+  return static_cast<size_t>((M + 15) / 16) * static_cast<size_t>(K / 32) * 1024;
+}
+
+namespace {
+
+int validate_w4a16_x(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                     const void* x_t, const char* fn) {
+  if (!X || !x_t) {
+    set_error("%s: null pointer", fn);
+    return SVDQ_ERR_NULL;
+  }
+  if (!known_dtype(x_dtype)) {
+    set_error("%s: x_dtype %d", fn, x_dtype);
+    return SVDQ_ERR_DTYPE;
+  }
+  if (int s = check_common(M, K, 0, SVDQ_GROUP, fn)) return s;
+  if (ldx < K || (M + 15) / 16 > 0x7FFFFFFF) {
+    set_error("%s: ldx=%lld < K=%lld", fn, (long long)ldx, (long long)K);
+    return SVDQ_ERR_SHAPE;
+  }
+  if (!aligned16(X) || !aligned16(x_t) || (ldx * esize(x_dtype)) % 16 != 0) {
+    set_error("%s: X, its row stride and x_t must be 16-byte aligned", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  return SVDQ_OK;
+}
+
+int validate_w4a16_gemm(const uint16_t* x_t, const uint8_t* wc, const uint16_t* ws,
+                        const float* bias, const void* Y, int y_dtype, int64_t M, int64_t N,
+                        int64_t K, int64_t ldy, const char* fn) {
+  if (!x_t || !wc || !ws || !Y) {
+    set_error("%s: null pointer", fn);
+    return SVDQ_ERR_NULL;
+  }
+  if (!known_dtype(y_dtype)) {
+    set_error("%s: y_dtype %d", fn, y_dtype);
+    return SVDQ_ERR_DTYPE;
+  }
+  if (int s = check_common(M, K, 0, SVDQ_GROUP, fn)) return s;
+  if (N < 1 || ldy < N || ((M + 127) / 128) * ((N + 255) / 256) > 0x7FFFFFFF) {
+    set_error("%s: N=%lld ldy=%lld", fn, (long long)N, (long long)ldy);
+    return SVDQ_ERR_SHAPE;
+  }
+  if (!aligned16(x_t) || !aligned16(wc) || !aligned16(ws)) {
+    set_error("%s: x_t and the tiled weights must be 16-byte aligned", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  if ((reinterpret_cast<uintptr_t>(Y) % esize(y_dtype)) != 0 ||
+      (bias && (reinterpret_cast<uintptr_t>(bias) & 3u) != 0)) {
+    set_error("%s: Y and bias must be aligned to their element size", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  return SVDQ_OK;
+}
+
+}  // namespace
+
+int svdq_w4a16_tile_activation(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                               uint16_t* x_t, hipStream_t stream) {
+  clear_error();
+  const char* fn = "svdq_w4a16_tile_activation";
+  if (int s = validate_w4a16_x(X, x_dtype, M, K, ldx, x_t, fn)) return s;
+  if (int s = device_ready()) return s;
+  return check_hip(launch_w4a16_tile_x(X, x_dtype == SVDQ_F16, M, K, ldx, x_t, stream),
+                   "svdq_w4a16_tile_activation launch");
+}
+
+int svdq_w4a16_gemm(const uint16_t* x_t, const uint8_t* w_codes_t, const uint16_t* w_scales_t,
+                    const float* bias, void* Y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                    int64_t ldy, hipStream_t stream) {
+  clear_error();
+  const char* fn = "svdq_w4a16_gemm";
+  if (int s = validate_w4a16_gemm(x_t, w_codes_t, w_scales_t, bias, Y, y_dtype, M, N, K, ldy, fn))
+    return s;
+  if (int s = device_ready()) return s;
+  return check_hip(launch_w4a16_gemm(x_t, w_codes_t, w_scales_t, bias, Y, y_dtype == SVDQ_F16, M,
+                                     N, K, ldy, stream),
+                   "svdq_w4a16_gemm launch");
+}
+
+int svdq_linear_w4a16(const void* X, int x_dtype, int64_t ldx, const uint8_t* w_codes_t,
+                      const uint16_t* w_scales_t, const float* bias, void* Y, int y_dtype,
+                      int64_t ldy, int64_t M, int64_t K, int64_t N, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  clear_error();
+  const char* fn = "svdq_linear_w4a16";
+  if (!ws) {
+    set_error("%s: null workspace", fn);
+    return SVDQ_ERR_NULL;
+  }
+  if (int s = check_common(M, K, 0, SVDQ_GROUP, fn)) return s;
+  const size_t need = svdq_w4a16_x_tiled_bytes(M, K);
+  if (ws_bytes < need) {
+    set_error("%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    return SVDQ_ERR_WORKSPACE;
+  }
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) {
+    set_error("%s: workspace must be 256-byte aligned", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  uint16_t* x_t = static_cast<uint16_t*>(ws);
+  if (int s = validate_w4a16_x(X, x_dtype, M, K, ldx, x_t, fn)) return s;
+  if (int s = validate_w4a16_gemm(x_t, w_codes_t, w_scales_t, bias, Y, y_dtype, M, N, K, ldy, fn))
+    return s;
+  if (int s = device_ready()) return s;
+  if (int s = check_hip(launch_w4a16_tile_x(X, x_dtype == SVDQ_F16, M, K, ldx, x_t, stream),
+                        "svdq_linear_w4a16 tiling launch"))
+    return s;
+  return check_hip(launch_w4a16_gemm(x_t, w_codes_t, w_scales_t, bias, Y, y_dtype == SVDQ_F16, M,
+                                     N, K, ldy, stream),
+                   "svdq_linear_w4a16 GEMM launch");
+}
+
 int svdq_debug_group_partials(const uint8_t* a_codes, const uint8_t* w_codes, int64_t M, int64_t N,
                               int64_t K, int32_t group, int64_t row0, int64_t rows, int32_t* P,
                               hipStream_t stream) {

@@ -22,6 +22,13 @@ hipError_t launch_k2_mx(const uint8_t* a_codes, const uint8_t* a_e8m0, const uin
                         const float* bias, void* Y, bool y_f16, int64_t M, int64_t N, int64_t K,
                         int64_t ldy, bool gelu, hipStream_t stream);
 
+hipError_t launch_w4a16_tile_x(const void* X, bool x_f16, int64_t M, int64_t K, int64_t ldx,
+                               uint16_t* x_t, hipStream_t stream);
+
+hipError_t launch_w4a16_gemm(const uint16_t* x_t, const uint8_t* w_codes_t,
+                             const uint16_t* w_scales_t, const float* bias, void* Y, bool y_f16,
+                             int64_t M, int64_t N, int64_t K, int64_t ldy, hipStream_t stream);
+
 hipError_t launch_debug_partials(const uint8_t* a_codes, const uint8_t* w_codes, int64_t M,
                                  int64_t N, int64_t K, int64_t row0, int64_t rows, int32_t* P,
                                  hipStream_t stream);

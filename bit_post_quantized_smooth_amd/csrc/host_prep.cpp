@@ -432,6 +432,83 @@ int svdq_pack_mx_tiles(const uint8_t* codes, const uint8_t* e8m0, int64_t rows, 
   return SVDQ_OK;
 }
 
+int svdq_prepare_weights_w4a16(const float* W, int64_t K, int64_t N, uint8_t* w_codes,
+                               uint16_t* w_scales) {
+  clear_error();
+  if (!W || !w_codes || !w_scales) {
+    set_error("svdq_prepare_weights_w4a16: null pointer");
+    return SVDQ_ERR_NULL;
+  }
+  const int st = check_prep_args("svdq_prepare_weights_w4a16", K, N, 0);
+  if (st != SVDQ_OK) return st;
+  SVDQ_TRY
+  const int64_t G = K / SVDQ_GROUP;
+#pragma omp parallel
+  {
+    std::vector<float> col(static_cast<size_t>(K));
+#pragma omp for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+      for (int64_t k = 0; k < K; ++k) col[k] = W[k * N + n];
+      for (int64_t g = 0; g < G; ++g)
+        quantize_group_f32(&col[g * SVDQ_GROUP], SVDQ_GROUP,
+                           &w_codes[n * (K / 2) + g * (SVDQ_GROUP / 2)], &w_scales[n * G + g]);
+    }
+  }
+  return SVDQ_OK;
+  SVDQ_CATCH
+}
+
+size_t svdq_w4a16_codes_tiled_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) return 0;
+  return static_cast<size_t>((N + 15) / 16) * static_cast<size_t>(K / 32) * 256;
+}
+
+size_t svdq_w4a16_scales_tiled_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) return 0;
+  return static_cast<size_t>((N + 63) / 64) * static_cast<size_t>(K / SVDQ_GROUP) * 128;
+}
+
+int svdq_pack_w4a16_tiles(const uint8_t* w_codes, const uint16_t* w_scales, int64_t N, int64_t K,
+                          uint8_t* codes_t, uint16_t* scales_t) {
+  clear_error();
+  if (!w_codes || !w_scales || !codes_t || !scales_t) {
+    set_error("svdq_pack_w4a16_tiles: null pointer");
+    return SVDQ_ERR_NULL;
+  }
+  if (K < SVDQ_GROUP || K % SVDQ_GROUP != 0) {
+    set_error("svdq_pack_w4a16_tiles: K=%lld (need K %% 64 == 0)", (long long)K);
+    return SVDQ_ERR_GROUP;
+  }
+  if (N < 1) {
+    set_error("svdq_pack_w4a16_tiles: N=%lld", (long long)N);
+    return SVDQ_ERR_SHAPE;
+  }
+  const int64_t S = K / 32, G = K / SVDQ_GROUP, kb = K / 2;
+  const int64_t nb = (N + 15) / 16, ng = (N + 63) / 64;
+  // codes: block (b, s), lane l = 16q + r: column 16b + r, bytes 16s + 4q .. +3,
+  // each nibble with bit 3 flipped (code + 8)
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nb; ++b)
+    for (int64_t s = 0; s < S; ++s)
+      for (int l = 0; l < 64; ++l) {
+        const int64_t n = 16 * b + (l & 15);
+        uint8_t* dst = codes_t + ((b * S + s) * 64 + l) * 4;
+        for (int j = 0; j < 4; ++j)
+          dst[j] = n < N ? static_cast<uint8_t>(w_codes[n * kb + 16 * s + 4 * (l >> 4) + j] ^ 0x88u)
+                         : uint8_t{0x88};
+      }
+  // scales: block (c, g), entry 4r + j: column 64c + 16j + r, group g (0 past N)
+#pragma omp parallel for schedule(static)
+  for (int64_t c = 0; c < ng; ++c)
+    for (int64_t g = 0; g < G; ++g)
+      for (int r = 0; r < 16; ++r)
+        for (int j = 0; j < 4; ++j) {
+          const int64_t n = 64 * c + 16 * j + r;
+          scales_t[(c * G + g) * 64 + 4 * r + j] = n < N ? w_scales[n * G + g] : uint16_t{0};
+        }
+  return SVDQ_OK;
+}
+
 int svdq_concat_lora(const uint16_t* L1t, const uint16_t* L2t, int64_t K, int64_t N, int32_t rank,
                      const float* lambda, const uint16_t* A, const uint16_t* B, int32_t rl,
                      float scale, uint16_t* L1t_out, uint16_t* L2t_out) {

@@ -303,6 +303,62 @@ int svdq_linear_mx(const void* X, int x_dtype, int64_t ldx, const float* inv_smo
                    int64_t M, int64_t K, int64_t N, void* ws, size_t ws_bytes,
                    int32_t activation, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * 4-bit weight-only baseline (W4A16): the comparison baseline of the SVDQuant
+ * abstract (ai-digest.ru page: 3.0x faster than a 4-bit weight-only baseline),
+ * which gives no format. Reading implemented: the quantizer above applied to W
+ * itself (per output column, groups of 64 along K; no smoothing, no low-rank
+ * branch), fp16 activations, each weight dequantized to fp16(s * q) with one
+ * rounding, fp32 accumulation:
+ *     Y = fp16(X) . fp16(s q)^T + bias, rounded once to y_dtype.
+ *
+ * Tiled device layouts (S = K/32 steps of 32 along K, G = K/64 groups):
+ *   x_t:      ceil(M/16) x S blocks of 1024 bytes (fp16): in block (b, s) lane
+ *             l = 16q + r holds 8 fp16 of row 16b + r at k = 32s + 8q + e,
+ *             in the order e = 0, 4, 1, 5, 2, 6, 3, 7;
+ *   codes_t:  ceil(N/16) x S blocks of 256 bytes: in block (b, s) lane l holds
+ *             the 4 bytes 16s + 4q .. +3 of column 16b + r (8 codes, element
+ *             2j in the low nibble of byte j), each nibble stored as code + 8;
+ *   scales_t: ceil(N/64) x G blocks of 64 fp16: entry 4r + j of block (c, g)
+ *             is the scale of column 64c + 16j + r in group g.
+ * Entries past N hold code 0 (stored as 8) and scale 0.
+ */
+
+/* Host: w_codes (N x K/2) and w_scales (N x K/64 fp16) = the quantizer on W
+ * (K x N fp32, Y = X . W), canonical layout. K % 64 == 0, N >= 1. */
+int svdq_prepare_weights_w4a16(const float* W, int64_t K, int64_t N, uint8_t* w_codes,
+                               uint16_t* w_scales);
+
+/* Bytes of the tiled weight layouts (0 for invalid sizes). */
+size_t svdq_w4a16_codes_tiled_bytes(int64_t N, int64_t K);
+size_t svdq_w4a16_scales_tiled_bytes(int64_t N, int64_t K);
+
+/* Host: canonical W4A16 weights -> the tiled layouts above (a permutation,
+ * and the +8 of the stored codes). Outputs must not overlap inputs. */
+int svdq_pack_w4a16_tiles(const uint8_t* w_codes, const uint16_t* w_scales, int64_t N, int64_t K,
+                          uint8_t* codes_t, uint16_t* scales_t);
+
+/* Bytes of the tiled fp16 activation (0 for invalid sizes). */
+size_t svdq_w4a16_x_tiled_bytes(int64_t M, int64_t K);
+
+/* Device: X (M x K fp16 or fp32, row stride ldx) -> x_t, the tiled fp16 layout
+ * above (fp32 values rounded to fp16, RNE). Rows past M in the last block are
+ * copies of row M-1. Constraints as for K1 (X 16-byte aligned rows). */
+int svdq_w4a16_tile_activation(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                               uint16_t* x_t, hipStream_t stream);
+
+/* Device: Y = x . deq(w)^T + bias on the tiled layouts, one rounding to y_dtype. */
+int svdq_w4a16_gemm(const uint16_t* x_t, const uint8_t* w_codes_t, const uint16_t* w_scales_t,
+                    const float* bias, void* Y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                    int64_t ldy, hipStream_t stream);
+
+/* Device: the whole baseline layer (tiling of X into `ws`, then the GEMM);
+ * ws >= svdq_w4a16_x_tiled_bytes(M, K) bytes, 256-byte aligned. */
+int svdq_linear_w4a16(const void* X, int x_dtype, int64_t ldx, const uint8_t* w_codes_t,
+                      const uint16_t* w_scales_t, const float* bias, void* Y, int y_dtype,
+                      int64_t ldy, int64_t M, int64_t K, int64_t N, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
 /* Test hook: the exact integer partials P[m, n, g] for rows row0 .. row0+rows-1,
  * computed with the same operand unpacking and int8 matrix-core instruction
  * as K2. P: rows x N x (K/group) int32, row-major. 0 <= row0, row0+rows <= M. */

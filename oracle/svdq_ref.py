@@ -501,10 +501,13 @@ def w4a16_dequant(w_codes, w_scales, group: int = GROUP) -> np.ndarray:
 
 def w4a16_linear(X, w_codes, w_scales, bias=None, out_dtype: str = "f16") -> np.ndarray:
     """Y = fp16(X) . fp16(s q)^T + b, exact in fp64 (each product of two fp16
-    values is exact, and so is their sum at these sizes), rounded once."""
+    values is exact, and so is their sum at these sizes), rounded once to
+    out_dtype ("f16", "f32", or "f64" for the unrounded value)."""
     Xh = to_f16(X).astype(np.float64)
     Wd = w4a16_dequant(w_codes, w_scales).astype(np.float64)
     y = Xh @ Wd.T
     if bias is not None:
         y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    if out_dtype == "f64":
+        return y
     return y.astype(np.float16 if out_dtype == "f16" else np.float32)

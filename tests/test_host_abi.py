@@ -169,6 +169,34 @@ def test_pack_mx_tiles_is_the_documented_layout(rows, K):
         assert et[((g * C + cc) * 64 + l) * 4 + i] == want
 
 
+@pytest.mark.parametrize("K,N", [(64, 1), (128, 40), (320, 70), (1024, 256)])
+def test_w4a16_prep_and_tiles(K, N):
+    """The weight-only baseline's weights equal the oracle's Q(W), and their tiled
+    layouts follow the index formulas of svdq.h (numpy statement in
+    tests/w16_tiles.py, spot-checked entry by entry)."""
+    import w16_tiles as T
+    rng = np.random.default_rng(K + 3 * N)
+    W = (rng.standard_normal((K, N)) * 0.05).astype(np.float32)
+    W[rng.integers(0, K)] *= 10
+    p = sq.prepare_weights_w4a16(W)
+    wc, ws = O.w4a16_prepare(W)
+    assert p.fmt == "w4a16" and np.array_equal(p.w_codes, wc)
+    assert np.array_equal(p.w_scales, ws.view(np.uint16))
+    ct, st = sq.pack_w4a16_tiles(p.w_codes, p.w_scales, K)
+    assert np.array_equal(ct, T.tile_w_codes(p.w_codes, K))
+    assert np.array_equal(st, T.tile_w_scales(p.w_scales, K))
+    S, G = K // 32, K // 64
+    for _ in range(100):
+        b, s, l, j = rng.integers(0, (N + 15) // 16), rng.integers(0, S), rng.integers(0, 64), rng.integers(0, 4)
+        n = 16 * b + l % 16
+        want = (p.w_codes[n, 16 * s + 4 * (l // 16) + j] ^ 0x88) if n < N else 0x88
+        assert ct[((b * S + s) * 64 + l) * 4 + j] == want
+        c, g, r = rng.integers(0, (N + 63) // 64), rng.integers(0, G), rng.integers(0, 16)
+        n = 64 * c + 16 * j + r
+        want = p.w_scales[n, g] if n < N else 0
+        assert st[(c * G + g) * 64 + 4 * r + j] == want
+
+
 def test_prepare_full_rank_reconstructs():
     rng = np.random.default_rng(5)
     K, N = 64, 48
@@ -248,6 +276,11 @@ def test_host_errors():
     assert L.svdq_pack_lowrank_down(bp, 96, 16, bp) == _lib.ERR_GROUP
     assert L.svdq_pack_lowrank_down(bp, 64, 24, bp) == _lib.ERR_RANK
     assert L.svdq_pack_lowrank_down(bp, 64, 0, bp) == _lib.ERR_RANK
+    # weight-only baseline
+    assert L.svdq_prepare_weights_w4a16(None, 64, 8, bp, bp) == _lib.ERR_NULL
+    assert L.svdq_prepare_weights_w4a16(W.ctypes.data, 96, 8, bp, bp) == _lib.ERR_GROUP
+    assert L.svdq_pack_w4a16_tiles(bp, bp, 0, 64, bp, bp) == _lib.ERR_SHAPE
+    assert L.svdq_w4a16_codes_tiled_bytes(4, 96) == 0 and L.svdq_w4a16_x_tiled_bytes(0, 64) == 0
     # MXFP4 tiles
     assert L.svdq_pack_mx_tiles(None, bp, 4, 64, bp, bp) == _lib.ERR_NULL
     assert L.svdq_pack_mx_tiles(bp, bp, 4, 96, bp, bp) == _lib.ERR_GROUP
@@ -341,6 +374,22 @@ def test_device_entry_points_reject_bad_arguments():
     lm[18] = 0
     lm[16] = 0x10080
     assert L.svdq_linear_mx(*lm) == _lib.ERR_ALIGN
+    # weight-only baseline, device side
+    assert L.svdq_w4a16_tile_activation(None, 1, 16, 64, 64, A16, None) == _lib.ERR_NULL
+    assert L.svdq_w4a16_tile_activation(A16, 9, 16, 64, 64, A16, None) == _lib.ERR_DTYPE
+    assert L.svdq_w4a16_tile_activation(A16, 1, 16, 64, 68, A16, None) == _lib.ERR_ALIGN
+    assert L.svdq_w4a16_tile_activation(A16, 1, 16, 96, 96, A16, None) == _lib.ERR_GROUP
+    wg = [A16, A16, A16, None, A16, 1, 16, 16, 64, 16, None]
+    bad = list(wg); bad[1] = None
+    assert L.svdq_w4a16_gemm(*bad) == _lib.ERR_NULL
+    bad = list(wg); bad[9] = 8
+    assert L.svdq_w4a16_gemm(*bad) == _lib.ERR_SHAPE
+    bad = list(wg); bad[2] = MIS
+    assert L.svdq_w4a16_gemm(*bad) == _lib.ERR_ALIGN
+    need16 = L.svdq_w4a16_x_tiled_bytes(16, 64)
+    assert need16 == 2 * 1024
+    lw = [A16, 1, 64, A16, A16, None, A16, 1, 16, 16, 64, 16, A16, need16 - 1, None]
+    assert L.svdq_linear_w4a16(*lw) == _lib.ERR_WORKSPACE
     # partials hook: slice outside the rows
     assert L.svdq_debug_group_partials(A16, A16, 16, 16, 64, 64, 10, 7, A16, None) == _lib.ERR_SHAPE
     assert L.svdq_gelu_tanh_f16(A16, MIS, 8, None) == _lib.ERR_ALIGN
