@@ -39,42 +39,30 @@ __device__ __forceinline__ void banded_tile(int t, int tiles_m, int tiles_n, int
   tn = r / rows;
 }
 
-// Epilogue of a 2*WTM x 2*WTN tile whose 4 waves each hold a WTM x WTN quarter
-// in fp32 accumulators (wave w: rows wm = w/2, columns wn = w%2; in each 16 x 16
-// block a lane holds columns 4*(lane/16) .. +3 of row lane%16).
+// Epilogue pieces of a 2*WTM x 2*WTN tile whose 4 waves each hold a WTM x WTN
+// quarter in fp32 accumulators (wave w: rows wm = w/2, columns wn = w%2; in
+// each 16 x 16 block a lane holds columns 4*(lane/16) .. +3 of row lane%16).
 // The low-rank branch (the Nunchaku engine fuses it into the low-bit kernel:
 // SVDQuant abstract; the disruptive-concepts.com post, section "Nunchaku:
 // Fusing Precision and Speed") runs as fp16 MFMAs on the same accumulators:
 // acc += fp16(D) . L2; then the bias, optionally the GELU, and one rounding
 // to the output type.
-template <int WTM, int WTN, bool Y_F16, bool GELU>
-__device__ __forceinline__ void lowrank_bias_store(
-    v4f (&acc)[WTM / 16][WTN / 16], const float* __restrict__ D, const uint16_t* __restrict__ L2t,
-    int R, const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N,
-    int64_t ldy, int64_t m0, int64_t n0) {
+// The low-rank up-projection on the accumulators: acc += fp16(D) . L2.
+template <int WTM, int WTN>
+__device__ __forceinline__ void lowrank_up(v4f (&acc)[WTM / 16][WTN / 16],
+                                           const float* __restrict__ D,
+                                           const uint16_t* __restrict__ L2t, int R, int64_t M,
+                                           int64_t N, int64_t m0, int64_t n0) {
   constexpr int NBM = WTM / 16, NBN = WTN / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rl = lane & 15, q = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
-  // low-rank up-projection on the same accumulators: acc += fp16(D) . L2
   for (int rc = 0; rc < R; rc += 32) {
     const int kk = rc + 8 * q;                       // this lane's 8 rank indices
     const bool kval = kk < R;                        // R % 16 == 0: whole 8-runs are valid or not
-    v8h Al[NBM], Bl[NBN];
-#pragma unroll
-    for (int i = 0; i < NBM; ++i) {
-      const int64_t m = m0 + wm * WTM + i * 16 + rl;
-      if (kval && m < M) {
-        const float4* dp = reinterpret_cast<const float4*>(D + m * R + kk);
-        const float4 u = dp[0], v = dp[1];
-        Al[i] = v8h{static_cast<_Float16>(u.x), static_cast<_Float16>(u.y),
-                    static_cast<_Float16>(u.z), static_cast<_Float16>(u.w),
-                    static_cast<_Float16>(v.x), static_cast<_Float16>(v.y),
-                    static_cast<_Float16>(v.z), static_cast<_Float16>(v.w)};
-      } else {
-        Al[i] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-    }
+    // the L2 fragments of all column blocks, then one row block of D at a time
+    // (few registers live at once: the caller may hold loads in flight)
+    v8h Bl[NBN];
 #pragma unroll
     for (int j = 0; j < NBN; ++j) {
       const int64_t n = n0 + wn * WTN + j * 16 + rl;
@@ -84,14 +72,36 @@ __device__ __forceinline__ void lowrank_bias_store(
         Bl[j] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
     }
 #pragma unroll
-    for (int i = 0; i < NBM; ++i)
+    for (int i = 0; i < NBM; ++i) {
+      const int64_t m = m0 + wm * WTM + i * 16 + rl;
+      v8h Al = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+      if (kval && m < M) {
+        const float4* dp = reinterpret_cast<const float4*>(D + m * R + kk);
+        const float4 u = dp[0], v = dp[1];
+        Al = v8h{static_cast<_Float16>(u.x), static_cast<_Float16>(u.y),
+                 static_cast<_Float16>(u.z), static_cast<_Float16>(u.w),
+                 static_cast<_Float16>(v.x), static_cast<_Float16>(v.y),
+                 static_cast<_Float16>(v.z), static_cast<_Float16>(v.w)};
+      }
 #pragma unroll
-      for (int j = 0; j < NBN; ++j) acc[i][j] = mfma_f16_16x16x32(Bl[j], Al[i], acc[i][j]);
+      for (int j = 0; j < NBN; ++j) acc[i][j] = mfma_f16_16x16x32(Bl[j], Al, acc[i][j]);
+    }
   }
+}
 
-  // bias and store; lane holds columns 4q .. 4q+3 of row rl in each 16 x 16
-  // block, written as one 8-byte (fp16) or 16-byte (fp32) store when Y's
-  // address and row stride allow it
+// Bias, the optional GELU, one rounding to the output type, and the stores: a
+// lane holds columns 4q .. 4q+3 of row rl in each 16 x 16 block, written as
+// one 8-byte (fp16) or 16-byte (fp32) store when Y's address and row stride
+// allow it.
+template <int WTM, int WTN, bool Y_F16, bool GELU>
+__device__ __forceinline__ void bias_store(v4f (&acc)[WTM / 16][WTN / 16],
+                                           const float* __restrict__ bias, void* __restrict__ Y,
+                                           int64_t M, int64_t N, int64_t ldy, int64_t m0,
+                                           int64_t n0) {
+  constexpr int NBM = WTM / 16, NBN = WTN / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rl = lane & 15, q = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
   constexpr int ES = Y_F16 ? 2 : 4;
   const bool vec = ((reinterpret_cast<uintptr_t>(Y) | static_cast<uintptr_t>(ldy * ES)) %
                     (4 * ES)) == 0;
@@ -138,6 +148,16 @@ __device__ __forceinline__ void lowrank_bias_store(
       }
     }
   }
+}
+
+// Both, in that order (the INT4 and weight-only kernels' epilogue).
+template <int WTM, int WTN, bool Y_F16, bool GELU>
+__device__ __forceinline__ void lowrank_bias_store(
+    v4f (&acc)[WTM / 16][WTN / 16], const float* __restrict__ D, const uint16_t* __restrict__ L2t,
+    int R, const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N,
+    int64_t ldy, int64_t m0, int64_t n0) {
+  lowrank_up<WTM, WTN>(acc, D, L2t, R, M, N, m0, n0);
+  bias_store<WTM, WTN, Y_F16, GELU>(acc, bias, Y, M, N, ldy, m0, n0);
 }
 
 }  // namespace

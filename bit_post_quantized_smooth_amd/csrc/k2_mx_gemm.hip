@@ -16,8 +16,9 @@
 // packed codes, plus one E8M0 byte for that 32-block, chosen from a 32-bit
 // register by the op_sel immediate. The weight fragment is the first operand,
 // so a lane ends up with 4 consecutive columns of one row of each 16 x 16
-// output block, as in the INT4 kernel, and the same epilogue (k2_common.hpp)
-// finishes the tile.
+// output block, as in the INT4 kernel, and the same epilogue pieces
+// (k2_common.hpp) finish the tile: the low-rank up-projection seeds the
+// accumulators before the K loop, the bias and the stores follow it.
 //
 // Data movement. One instruction takes 16 cycles on a SIMD and consumes 2 KB
 // of operands, so operand delivery, not arithmetic, bounds this kernel. Both
@@ -159,14 +160,22 @@ __device__ __forceinline__ void mx_tile(
     if constexpr (WTN < 64) f.sb[0] >>= shb;
   };
 
+  // The first chunk's loads go out first; the low-rank up-projection then
+  // starts the accumulators (acc = fp16(D) . L2) while they are in flight,
+  // instead of exposing its own loads after the K loop; the second chunk's
+  // loads follow (issuing them earlier would hold more registers than there
+  // are next to the branch's operands).
+  static_assert(NS == 2, "the prologue below is written for two chunks in flight");
+  Frags f[NS];
+  load(f[0], 0);
+
   v4f acc[NBM][NBN];
 #pragma unroll
   for (int i = 0; i < NBM; ++i)
 #pragma unroll
     for (int j = 0; j < NBN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  Frags f[NS];
-  static_for<NS>([&](auto S) { load(f[S.value], S.value); });
+  lowrank_up<WTM, WTN>(acc, D, L2t, R, M, N, m0, n0);
+  load(f[1], 1);
   int64_t c0 = 0;
   for (; c0 + NS <= C; c0 += NS) {
     static_for<NS>([&](auto S) {
@@ -186,7 +195,7 @@ __device__ __forceinline__ void mx_tile(
     }
   });
 
-  lowrank_bias_store<WTM, WTN, Y_F16, GELU>(acc, D, L2t, R, bias, Y, M, N, ldy, m0, n0);
+  bias_store<WTM, WTN, Y_F16, GELU>(acc, bias, Y, M, N, ldy, m0, n0);
 }
 
 constexpr int kFullM = 256, kFullN = 128;     // full tile; quarters are 128 x 64
