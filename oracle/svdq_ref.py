@@ -511,3 +511,41 @@ def w4a16_linear(X, w_codes, w_scales, bias=None, out_dtype: str = "f16") -> np.
     if out_dtype == "f64":
         return y
     return y.astype(np.float16 if out_dtype == "f16" else np.float32)
+
+
+# --------------------------------------------------------------------------
+# Convolutions as implicit GEMMs (UNet layers).
+#
+# The pages say the method applies to UNet backbones as well as DiT ones
+# (chattools.cn overview, main features, architectures item;
+# disruptive-concepts.com post) without saying how a convolution is treated.
+# Reading: a KH x KW convolution over an NHWC image (zero padding, one stride
+# for both axes) is the linear layer applied to the matrix of its patches,
+# X_col (batch*OH*OW x KH*KW*C), whose row (b, oh, ow) holds, at column
+# (kh*KW + kw)*C + c, the input value at (b, oh*stride + kh - pad,
+# ow*stride + kw - pad, c), or 0 outside the image; the weight (KH, KW, C, N)
+# becomes the (KH*KW*C) x N matrix in the same order. Smoothing, the split,
+# quantization and everything else are those of the linear layer on X_col.
+
+
+def im2col_nhwc(X, KH: int, KW: int, stride: int, pad: int) -> np.ndarray:
+    """The patch matrix X_col of an NHWC image, in the image's dtype."""
+    X = np.asarray(X)
+    B, H, W, C = X.shape
+    OH = (H + 2 * pad - KH) // stride + 1
+    OW = (W + 2 * pad - KW) // stride + 1
+    Xp = np.zeros((B, H + 2 * pad, W + 2 * pad, C), dtype=X.dtype)
+    Xp[:, pad:pad + H, pad:pad + W, :] = X
+    cols = np.empty((B, OH, OW, KH, KW, C), dtype=X.dtype)
+    for kh in range(KH):
+        for kw in range(KW):
+            cols[:, :, :, kh, kw, :] = Xp[:, kh:kh + stride * (OH - 1) + 1:stride,
+                                          kw:kw + stride * (OW - 1) + 1:stride, :]
+    return cols.reshape(B * OH * OW, KH * KW * C)
+
+
+def conv_weight_matrix(Wc) -> np.ndarray:
+    """(KH, KW, C, N) -> (KH*KW*C) x N, rows in the order of X_col's columns."""
+    Wc = np.asarray(Wc)
+    KH, KW, C, N = Wc.shape
+    return Wc.reshape(KH * KW * C, N)

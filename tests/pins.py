@@ -844,3 +844,56 @@ def check_w4a16_sanity(O):
 
 ALL_CHECKS += [check_golden_w4a16, check_w4a16_bruteforce, check_w4a16_grid_identity,
                check_w4a16_sanity]
+
+
+# --------------------------------------------------------------------------
+# Convolutions as implicit GEMMs (reading of the pages' UNet applicability)
+
+
+def _py_conv_direct(X, Wc, stride, pad):
+    """Direct convolution by loops (Python floats)."""
+    B, H, W, C = X.shape
+    KH, KW, _, N = Wc.shape
+    OH = (H + 2 * pad - KH) // stride + 1
+    OW = (W + 2 * pad - KW) // stride + 1
+    Y = np.zeros((B, OH, OW, N))
+    for b in range(B):
+        for oh in range(OH):
+            for ow in range(OW):
+                for n in range(N):
+                    acc = 0.0
+                    for kh in range(KH):
+                        ih = oh * stride + kh - pad
+                        if ih < 0 or ih >= H:
+                            continue
+                        for kw in range(KW):
+                            iw = ow * stride + kw - pad
+                            if iw < 0 or iw >= W:
+                                continue
+                            for c in range(C):
+                                acc += float(X[b, ih, iw, c]) * float(Wc[kh, kw, c, n])
+                    Y[b, oh, ow, n] = acc
+    return Y
+
+
+def check_im2col_is_the_convolution(O, seed=71):
+    """X_col . W equals a direct convolution by loops (zero padding, strides 1
+    and 2, odd sizes), and a 1 x 1 stride-1 convolution's X_col is X itself."""
+    rng = np.random.default_rng(seed)
+    for (B, H, W, C, N, KH, KW, s, p) in [(1, 5, 4, 3, 2, 3, 3, 1, 1), (2, 6, 7, 2, 3, 3, 3, 2, 1),
+                                          (1, 4, 5, 2, 2, 2, 3, 1, 0)]:
+        X = rng.standard_normal((B, H, W, C))
+        Wc = rng.standard_normal((KH, KW, C, N))
+        Y = O.im2col_nhwc(X, KH, KW, s, p) @ O.conv_weight_matrix(Wc)
+        ref = _py_conv_direct(X, Wc, s, p).reshape(Y.shape)
+        assert np.allclose(Y, ref, rtol=0, atol=1e-12 * max(1.0, np.abs(ref).max()))
+    X = rng.standard_normal((2, 3, 5, 4))
+    assert np.array_equal(O.im2col_nhwc(X, 1, 1, 1, 0), X.reshape(-1, 4))
+    # padding entries are exact zeros, and the column order is (kh, kw, c)
+    cols = O.im2col_nhwc(np.ones((1, 2, 2, 1)), 3, 3, 1, 1)
+    assert cols.shape == (4, 9)
+    assert list(cols[0]) == [0, 0, 0, 0, 1, 1, 0, 1, 1]     # output (0, 0): taps hit rows/cols -1
+    assert list(cols[3]) == [1, 1, 0, 1, 1, 0, 0, 0, 0]     # output (1, 1)
+
+
+ALL_CHECKS += [check_im2col_is_the_convolution]

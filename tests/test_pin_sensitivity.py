@@ -234,6 +234,31 @@ def mut_w4a16_scale_group_shift(mp):
                lambda wc, ws, group=64: orig(wc, np.roll(np.asarray(ws), 1, axis=1), group))
 
 
+def mut_im2col_channel_major(mp):
+    """Patch columns ordered (c, kh, kw) instead of (kh, kw, c)."""
+    orig = _orig("im2col_nhwc")
+
+    def f(X, KH, KW, stride, pad):
+        cols = orig(X, KH, KW, stride, pad)
+        C = np.asarray(X).shape[3]
+        return cols.reshape(cols.shape[0], KH * KW, C).transpose(0, 2, 1).reshape(cols.shape[0], -1)
+    mp.setattr(R, "im2col_nhwc", f)
+
+
+def mut_im2col_no_padding_shift(mp):
+    """Taps not shifted by the padding (output (oh, ow) reads from (oh + kh, ow + kw) - 0)."""
+    orig = _orig("im2col_nhwc")
+
+    def f(X, KH, KW, stride, pad):
+        X = np.asarray(X)
+        if pad == 0:
+            return orig(X, KH, KW, stride, pad)
+        Xs = np.zeros_like(X)
+        Xs[:, pad:, pad:, :] = X[:, :X.shape[1] - pad, :X.shape[2] - pad, :]
+        return orig(Xs, KH, KW, stride, pad)
+    mp.setattr(R, "im2col_nhwc", f)
+
+
 MUTATIONS = [mut_scale_div8, mut_ties_away, mut_nibble_order, mut_smoothing_inverted,
              mut_sigma_unsplit, mut_smallest_singulars, mut_residual_sign,
              mut_partials_group_shift, mut_drop_weight_scale, mut_drop_bias,
@@ -242,7 +267,8 @@ MUTATIONS = [mut_scale_div8, mut_ties_away, mut_nibble_order, mut_smoothing_inve
              mut_gelu_before_bias, mut_mx_ties_up, mut_mx_exponent_ceil,
              mut_mx_exponent_nearest, mut_mx_negative_zero_dropped, mut_mx_bias_128,
              mut_mx_nibble_order, mut_mx_weight_blocks_along_n, mut_mx_unsmoothed_activation,
-             mut_w4a16_unrounded_dequant, mut_w4a16_scale_group_shift]
+             mut_w4a16_unrounded_dequant, mut_w4a16_scale_group_shift,
+             mut_im2col_channel_major, mut_im2col_no_padding_shift]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)

@@ -145,3 +145,63 @@ def layer_inputs(cfg: int, layer_idx: int = 0):
         return L, None, W
     X = activation(cfg, layer_idx, L.M, L.K, L.x_dtype, L.x_outlier_frac, L.x_outlier_scale)
     return L, X, W
+
+
+# --------------------------------------------------------------------------
+# UNet convolutions (NHWC), run as implicit GEMMs: M = batch * OH * OW output
+# pixels, K = KH * KW * C, N = output channels. Shapes are those of an SDXL-
+# style UNet at 128x128 latents, batch 2 (3x3 convolutions at each level, a
+# stride-2 downsample); the pages say SVDQuant applies to UNet backbones
+# (chattools.cn overview, main features; disruptive-concepts.com post).
+
+@dataclasses.dataclass(frozen=True)
+class ConvLayer:
+    batch: int
+    H: int
+    W: int
+    C: int
+    N: int
+    KH: int
+    KW: int
+    stride: int
+    pad: int
+    rank: int
+    x_dtype: str = "f16"
+    y_dtype: str = "f16"
+    name: str = ""
+
+    @property
+    def OH(self) -> int:
+        return (self.H + 2 * self.pad - self.KH) // self.stride + 1
+
+    @property
+    def OW(self) -> int:
+        return (self.W + 2 * self.pad - self.KW) // self.stride + 1
+
+    @property
+    def M(self) -> int:
+        return self.batch * self.OH * self.OW
+
+    @property
+    def K(self) -> int:
+        return self.KH * self.KW * self.C
+
+
+CONV_LAYERS: List[ConvLayer] = [
+    ConvLayer(1, 8, 8, 64, 64, 3, 3, 1, 1, 16, "f32", "f32", "tiny 3x3"),
+    ConvLayer(2, 128, 128, 320, 320, 3, 3, 1, 1, 32, name="unet 128x128 3x3 320->320"),
+    ConvLayer(2, 64, 64, 640, 640, 3, 3, 1, 1, 32, name="unet 64x64 3x3 640->640"),
+    ConvLayer(2, 32, 32, 1280, 1280, 3, 3, 1, 1, 32, name="unet 32x32 3x3 1280->1280"),
+    ConvLayer(2, 128, 128, 320, 320, 3, 3, 2, 1, 32, name="unet downsample 128->64 3x3 s2"),
+]
+CONV_CFG = 10          # seed stream of the convolution layers
+
+
+def conv_inputs(idx: int):
+    """(ConvLayer, X NHWC (batch x H x W x C), Wc (KH x KW x C x N) fp32), seeded like the
+    linear layers: X N(0,1) with 1% of channels x20, Wc N(0, 0.02^2) with 1% of its
+    KH*KW*C input rows x10."""
+    L = CONV_LAYERS[idx]
+    X = activation(CONV_CFG, idx, L.batch * L.H * L.W, L.C, L.x_dtype)
+    Wc = weight(CONV_CFG, idx, L.K, L.N)
+    return L, X.reshape(L.batch, L.H, L.W, L.C), Wc.reshape(L.KH, L.KW, L.C, L.N)
