@@ -74,6 +74,9 @@ def parse():
                          "pages' speed comparison (fp16 activations, no low-rank branch)")
     ap.add_argument("--unfused-gelu", action="store_true",
                     help="with --mlp: plain up-projection, then the separate GELU kernel")
+    ap.add_argument("--conv", type=int, default=None,
+                    help="time UNet convolution I instead (NHWC, K1 on the implicit patch matrix, "
+                         "then K2; INT4 format)")
     return ap.parse_args()
 
 
@@ -255,6 +258,114 @@ def mlp_main(args, torch, sq, wl):
         "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2)}), flush=True)
 
 
+def conv_cpu_baseline(L, X, Wm, prep, bias, budget_s):
+    """The oracle's convolution (im2col of the whole image, then its linear layer
+    on chunks of patch rows) until ~budget_s seconds."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    t0 = time.perf_counter()
+    Xcol = O.im2col_nhwc(X, L.KH, L.KW, L.stride, L.pad)
+    lam = O.smoothing_factors(O.channel_absmax(Xcol), Wm)
+    inv = O.inv_smoothing(lam)
+    wc, ws = O.quantize_residual_from_factors(Wm, lam, prep.L1, prep.L2)
+    t_setup = time.perf_counter() - t0
+    chunk, rows = 32, 0
+    t0 = time.perf_counter()
+    while rows < L.M and time.perf_counter() - t0 < budget_s:
+        r = slice(rows, min(L.M, rows + chunk))
+        O.linear(Xcol[r], inv, prep.L1, prep.L2, wc, ws, bias, L.y_dtype)
+        rows = r.stop
+    t = time.perf_counter() - t0
+    return dict(value=2.0 * rows * L.N * L.K / t / 1e12, unit="TOPS", cores=int(cores),
+                kind="oracle",
+                sample=f"first {rows} of {L.M} output pixels of the same convolution, online "
+                       f"part only ({t:.1f} s, numpy fp64, chunks of {chunk}; the im2col and "
+                       f"calibration before it took {t_setup:.1f} s and are not counted)")
+
+
+def conv_main(args, torch, sq, wl):
+    """Step = one UNet convolution on one batch: K1 on the implicit patch matrix
+    of the NHWC image, then K2 (the same kernels as svdq_conv2d)."""
+    L, X, Wc = wl.conv_inputs(args.conv)
+    Wm = Wc.reshape(L.K, L.N)
+    bias = wl.bias(wl.CONV_CFG, args.conv, L.N)
+    lam = sq.smoothing_factors(sq.conv_patch_absmax(X, L.KH, L.KW, L.stride, L.pad), Wm)
+    prep = sq.prepare_weights(Wm, lam, L.rank)
+    M, K, N, R = L.M, L.K, L.N, prep.rank
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16
+                                   else np.ascontiguousarray(a)).to("cuda")
+    ydt = torch.float16 if L.y_dtype == "f16" else torch.float32
+    sets = []
+    for _ in range(args.sets):
+        sets.append(dict(
+            X=d(X), inv=d(prep.inv_smooth), L1p=d(prep.L1p), L2t=d(prep.L2t), wc=d(prep.w_codes),
+            ws=d(prep.w_scales), b=d(bias),
+            ac=torch.empty((M, K // 2), dtype=torch.uint8, device="cuda"),
+            asc=torch.empty((M, K // 64), dtype=torch.int16, device="cuda"),
+            D=torch.empty((M, R), dtype=torch.float32, device="cuda"),
+            Y=torch.empty((L.batch, L.OH, L.OW, N), dtype=ydt, device="cuda")))
+
+    def k1(i):
+        s = sets[i % len(sets)]
+        sq.quantize_act_lowrank_down_conv(s["X"], L.KH, L.KW, L.stride, L.pad, s["inv"], s["L1p"],
+                                          R, s["ac"], s["asc"], s["D"])
+
+    def k2(i):
+        s = sets[i % len(sets)]
+        sq.w4a4_gemm_lowrank_up(s["ac"], s["asc"], s["wc"], s["ws"], s["D"], s["L2t"], R, s["b"],
+                                s["Y"].view(M, N), K)
+
+    class _S:
+        pass
+    st = _S()
+    st.k1, st.k2 = k1, k2
+    t_step, t1, t2 = time_steps(torch, st, args.steps, args.warmup)
+    gap = event_gap(torch)
+    k1_avg = float(np.mean(t1)) - gap
+    k2_avg = float(np.mean(t2)) - gap
+    ops = 2.0 * M * N * K
+    value = ops / t_step / 1e12
+    xb = 2 if L.x_dtype == "f16" else 4
+    yb = 2 if L.y_dtype == "f16" else 4
+    img = L.batch * L.H * L.W * L.C
+    # K1: the image once, the patch matrix's codes, scales and D out
+    k1_bytes = img * xb + M * K // 2 + M * 2 * (K // 64) + 4 * M * R + 2 * K * R + 4 * K
+    k2_bytes = (M + N) * K // 2 + (M + N) * 2 * (K // 64) + 4 * M * R + 2 * R * N + M * N * yb
+    out = {
+        "metric": "effective TOPS of an SVDQuant W4A4+rank-32 UNet convolution "
+                  "(implicit GEMM), % of INT8 MFMA peak",
+        "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"{L.name}: X {L.x_dtype} NHWC {L.batch}x{L.H}x{L.W}x{L.C}, "
+                               f"{L.KH}x{L.KW} stride {L.stride} pad {L.pad} -> {N} channels "
+                               f"(patch matrix {M}x{K}), rank {R}, INT4 per-64 groups, "
+                               f"Y {L.y_dtype}",
+                   "M": M, "K": K, "N": N, "rank": R, "format": "int4",
+                   "buffer_sets": args.sets},
+        "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": "k2_w4a4_kernel",
+                     "achieved": round(ops / k2_avg / 1e12, 2), "peak": INT8_PEAK_TOPS,
+                     "unit": "TOPS", "frac": round(ops / k2_avg / 1e12 / INT8_PEAK_TOPS, 4),
+                     "traffic": None, "algorithmic_bytes": k2_bytes,
+                     "avg_ms": round(k2_avg * 1e3, 4),
+                     "timing": "HIP events around each launch inside the timed steps, on the "
+                               "launch stream, less the gap of an empty event pair",
+                     "event_gap_us": round(gap * 1e6, 2)},
+        "k1": {"kernel": "k1_quant_down_kernel (convolution instance)",
+               "avg_ms": round(k1_avg * 1e3, 4), "algorithmic_bytes": k1_bytes,
+               "achieved_gbs": round(k1_bytes / k1_avg / 1e9, 1), "peak_gbs": HBM_PEAK_GBS,
+               "frac": round(k1_bytes / k1_avg / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = conv_cpu_baseline(L, X, Wm, prep, bias, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -268,6 +379,9 @@ def main():
 
     if args.mlp:
         mlp_main(args, torch, sq, wl)
+        return
+    if args.conv is not None:
+        conv_main(args, torch, sq, wl)
         return
     cfg = wl.CONFIGS[args.config]
     L = cfg.layers[args.layer]

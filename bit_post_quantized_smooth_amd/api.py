@@ -322,6 +322,50 @@ def linear_w4a16(X, w_codes_t, w_scales_t, bias, Y, ws, stream=None):
           "svdq_linear_w4a16")
 
 
+# --------------------------------------------------------------------------
+# convolutions: the linear layer on the implicit patch matrix of an NHWC image
+
+
+def conv_out_size(n: int, k: int, stride: int, pad: int) -> int:
+    """Output extent of a convolution along one axis."""
+    return (n + 2 * pad - k) // stride + 1
+
+
+def conv_patch_absmax(X: np.ndarray, KH: int, KW: int, stride: int, pad: int) -> np.ndarray:
+    """Column maxima of |patch matrix| (length KH*KW*C) for an NHWC image X."""
+    X = np.ascontiguousarray(X)
+    dt = F16 if X.dtype == np.float16 else F32
+    if dt == F32:
+        X = _c(X, np.float32)
+    B, H, W, Cc = X.shape
+    out = np.empty(KH * KW * Cc, dtype=np.float32)
+    check(lib.svdq_conv_patch_absmax(_np_ptr(X), dt, B, H, W, Cc, KH, KW, stride, pad,
+                                     _np_ptr(out)), "svdq_conv_patch_absmax")
+    return out
+
+
+def quantize_act_lowrank_down_conv(X, KH: int, KW: int, stride: int, pad: int, inv_smooth, L1p,
+                                   R: int, a_codes, a_scales, D, stream=None):
+    """K1 on the patch matrix of the NHWC image X (batch x H x W x C, contiguous)."""
+    B, H, W, Cc = X.shape
+    check(lib.svdq_quantize_act_lowrank_down_conv(
+        _tp(X), _dt(X), B, H, W, Cc, KH, KW, stride, pad, _tp(inv_smooth),
+        _tp(L1p) if R else None, R, _tp(a_codes), _tp(a_scales), _tp(D) if R else None,
+        _stream(stream)), "svdq_quantize_act_lowrank_down_conv")
+
+
+def conv2d(X, KH: int, KW: int, stride: int, pad: int, inv_smooth, L1p, L2t, R: int, w_codes,
+           w_scales, bias, Y, ws, stream=None, activation=None):
+    """The whole convolution: Y (batch x OH x OW x N, contiguous) from the NHWC image X."""
+    B, H, W, Cc = X.shape
+    N = Y.shape[-1]
+    check(lib.svdq_conv2d(_tp(X), _dt(X), B, H, W, Cc, KH, KW, stride, pad, _tp(inv_smooth),
+                          _tp(L1p) if R else None, _tp(L2t) if R else None, R, _tp(w_codes),
+                          _tp(w_scales), _tp(bias), _tp(Y), _dt(Y), N, _tp(ws),
+                          ws.numel() * ws.element_size(), _act(activation), _stream(stream)),
+          "svdq_conv2d")
+
+
 def debug_group_partials(a_codes, w_codes, M: int, N: int, K: int, row0: int, rows: int, P,
                          stream=None):
     check(lib.svdq_debug_group_partials(_tp(a_codes), _tp(w_codes), M, N, K, GROUP, row0, rows,
@@ -392,4 +436,40 @@ class Linear:
         run = linear_mx if self.fmt == "mxfp4" else linear
         run(X, self.inv_smooth, self.L1p, self.L2t, self.R, self.w_codes, self.w_scales,
             self.bias, Y, self.workspace(M), stream, self.activation)
+        return Y
+
+
+class Conv2d:
+    """One prepared SVDQuant convolution resident on a device.
+
+    ``prep`` is the INT4 prep of the K x N weight matrix whose row
+    (kh*KW + kw)*C + c is filter tap (kh, kw, c) (a KH x KW x C x N filter
+    reshaped). ``Conv2d(prep, KH, KW, stride, pad, bias)(X)`` maps an NHWC
+    image to the NHWC output (batch x OH x OW x N)."""
+
+    def __init__(self, prep: Prepared, KH: int, KW: int, stride: int = 1, pad: int = 0,
+                 bias: Optional[np.ndarray] = None, device="cuda", out_dtype=None,
+                 activation=None):
+        if prep.fmt != "int4":
+            raise ValueError("convolutions run in the INT4 format only")
+        if prep.K % (KH * KW) != 0:
+            raise ValueError(f"K={prep.K} is not KH*KW*C for a {KH}x{KW} kernel")
+        self.lin = Linear(prep, bias, device, out_dtype, activation)
+        self.KH, self.KW, self.stride, self.pad = KH, KW, stride, pad
+        self.C = prep.K // (KH * KW)
+
+    def __call__(self, X, Y=None, stream=None):
+        torch = _torch()
+        lin = self.lin
+        B, H, W, Cc = X.shape
+        if Cc != self.C:
+            raise ValueError(f"image has {Cc} channels, the filter {self.C}")
+        OH = conv_out_size(H, self.KH, self.stride, self.pad)
+        OW = conv_out_size(W, self.KW, self.stride, self.pad)
+        if Y is None:
+            Y = torch.empty((B, OH, OW, lin.N), dtype=lin.out_dtype or X.dtype,
+                            device=lin.device)
+        ws = lin.workspace(max(B * OH * OW, 1))
+        conv2d(X, self.KH, self.KW, self.stride, self.pad, lin.inv_smooth, lin.L1p, lin.L2t,
+               lin.R, lin.w_codes, lin.w_scales, lin.bias, Y, ws, stream, lin.activation)
         return Y

@@ -7,10 +7,21 @@
 
 namespace svdq {
 
-// a_meta: fp16 group scales (mx = false) or E8M0 block exponents (mx = true)
+// A KH x KW convolution over an NHWC image (batch x H x W x C), run by K1 as
+// the linear layer on its patch matrix: row (b, oh, ow), column
+// (kh*KW + kw)*C + c (zero outside the image). C % 64 == 0, so a 64-channel
+// group lies within one tap.
+struct ConvGeom {
+  int32_t H, W, C, KH, KW, stride, pad, OH, OW;
+};
+
+// a_meta: fp16 group scales (mx = false) or E8M0 block exponents (mx = true).
+// conv: null for a linear layer; else X is the NHWC image and M, K are the
+// patch matrix's (INT4 only).
 hipError_t launch_k1(const void* X, bool x_f16, int64_t M, int64_t K, int64_t ldx,
                      const float* inv_smooth, const uint16_t* L1p, int R, uint8_t* a_codes,
-                     void* a_meta, bool mx, float* D, hipStream_t stream);
+                     void* a_meta, bool mx, float* D, hipStream_t stream,
+                     const ConvGeom* conv = nullptr);
 
 hipError_t launch_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* w_codes,
                      const uint16_t* w_scales, const float* D, const uint16_t* L2t, int R,

@@ -95,6 +95,36 @@ static void quantize_block_mx(const float* v, uint8_t* codes, uint8_t* e8m0) {
   *e8m0 = static_cast<uint8_t>(e8);
 }
 
+int check_conv(int64_t batch, int64_t H, int64_t W, int64_t C, int32_t KH, int32_t KW,
+               int32_t stride, int32_t pad, ConvShape& cs, const char* fn) {
+  const int64_t lim = int64_t{1} << 31;
+  if (batch < 1 || H < 1 || W < 1 || H >= lim || W >= lim || C < SVDQ_GROUP ||
+      C % SVDQ_GROUP != 0 || KH < 1 || KH > 64 || KW < 1 || KW > 64 || stride < 1 ||
+      stride > 64 || pad < 0 || pad > 64 || H + 2 * pad < KH || W + 2 * pad < KW) {
+    set_error("%s: convolution batch=%lld H=%lld W=%lld C=%lld kernel %dx%d stride %d pad %d "
+              "(need C a positive multiple of 64, kernel and stride in [1, 64], pad in [0, 64], "
+              "kernel within the padded image)",
+              fn, (long long)batch, (long long)H, (long long)W, (long long)C, KH, KW, stride, pad);
+    return SVDQ_ERR_SHAPE;
+  }
+  cs.batch = batch; cs.H = H; cs.W = W; cs.C = C;
+  cs.KH = KH; cs.KW = KW; cs.stride = stride; cs.pad = pad;
+  cs.OH = (H + 2 * pad - KH) / stride + 1;
+  cs.OW = (W + 2 * pad - KW) / stride + 1;
+  cs.K = static_cast<int64_t>(KH) * KW * C;
+  // element counts of the image and the number of output pixels, each below
+  // 2^31 (checked factor by factor so the products cannot overflow)
+  if (batch > lim / H || batch * H > lim / W || batch * H * W > (lim - 1) / C ||
+      batch > lim / cs.OH || batch * cs.OH > (lim - 1) / cs.OW || cs.K > (int64_t{1} << 25)) {
+    set_error("%s: image %lldx%lldx%lldx%lld or its %lld x %lld patch matrix too large", fn,
+              (long long)batch, (long long)H, (long long)W, (long long)C,
+              (long long)(batch * cs.OH * cs.OW), (long long)cs.K);
+    return SVDQ_ERR_SHAPE;
+  }
+  cs.M = batch * cs.OH * cs.OW;
+  return SVDQ_OK;
+}
+
 }  // namespace svdq
 
 using namespace svdq;
@@ -307,6 +337,53 @@ int svdq_channel_absmax(const void* X, int x_dtype, int64_t M, int64_t K, int64_
     float a = 0.0f;
     for (int t = 0; t < nt; ++t) a = std::max(a, part[static_cast<size_t>(t) * K + k]);
     out[k] = a;
+  }
+  return SVDQ_OK;
+  SVDQ_CATCH
+}
+
+int svdq_conv_patch_absmax(const void* X, int x_dtype, int64_t batch, int64_t H, int64_t W,
+                           int64_t C, int32_t KH, int32_t KW, int32_t stride, int32_t pad,
+                           float* out) {
+  clear_error();
+  const char* fn = "svdq_conv_patch_absmax";
+  if (!X || !out) {
+    set_error("%s: null pointer", fn);
+    return SVDQ_ERR_NULL;
+  }
+  if (x_dtype != SVDQ_F16 && x_dtype != SVDQ_F32) {
+    set_error("%s: x_dtype %d", fn, x_dtype);
+    return SVDQ_ERR_DTYPE;
+  }
+  ConvShape cs;
+  if (int s = check_conv(batch, H, W, C, KH, KW, stride, pad, cs, fn)) return s;
+  SVDQ_TRY
+  // column (kh, kw, c) of the patch matrix holds pixel (oh*stride + kh - pad,
+  // ow*stride + kw - pad) of every image, or 0 outside it (which never raises
+  // a maximum of magnitudes)
+  const int64_t taps = static_cast<int64_t>(KH) * KW;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < taps; ++t) {
+    const int64_t kh = t / KW, kw = t % KW;
+    float* o = out + t * C;
+    for (int64_t c = 0; c < C; ++c) o[c] = 0.0f;
+    for (int64_t b = 0; b < batch; ++b)
+      for (int64_t oh = 0; oh < cs.OH; ++oh) {
+        const int64_t ih = oh * stride + kh - pad;
+        if (ih < 0 || ih >= H) continue;
+        for (int64_t ow = 0; ow < cs.OW; ++ow) {
+          const int64_t iw = ow * stride + kw - pad;
+          if (iw < 0 || iw >= W) continue;
+          const int64_t px = ((b * H + ih) * W + iw) * C;
+          if (x_dtype == SVDQ_F32) {
+            const float* row = static_cast<const float*>(X) + px;
+            for (int64_t c = 0; c < C; ++c) o[c] = std::max(o[c], std::fabs(row[c]));
+          } else {
+            const uint16_t* row = static_cast<const uint16_t*>(X) + px;
+            for (int64_t c = 0; c < C; ++c) o[c] = std::max(o[c], std::fabs(f16_to_f32(row[c])));
+          }
+        }
+      }
   }
   return SVDQ_OK;
   SVDQ_CATCH

@@ -195,6 +195,7 @@ constexpr int k1_waves() { return NCB <= 4 ? 8 : 4; }
 template <typename XT, int NCB>
 struct GroupIn {
   Raw<XT> x;
+  bool valid;            // convolution: the tap lies inside the image (else the values are 0)
   float4 inv[4];
   v8h l1[ring_l1_blocks<NCB>() > 0 ? ring_l1_blocks<NCB>() : 1][2];
 };
@@ -202,12 +203,20 @@ struct GroupIn {
 constexpr int kXsStride = kGroup + 8;           // fp16 elements per row of the LDS tile
 
 // a_codes, a_meta: INT4 codes (M x K/2) and fp16 group scales (M x K/64), or
-// for MX the tiled E2M1 codes and E8M0 exponents (see svdq.h)
-template <typename XT, int NCB, int NB, bool MX>
+// for MX the tiled E2M1 codes and E8M0 exponents (see svdq.h).
+// CONV: X is an NHWC image and the rows are the patches of the convolution cg
+// (the chattools.cn overview says the method applies to UNet backbones; the
+// convolution is the linear layer on its patch matrix): row p is the output
+// pixel (b, oh, ow), group g the 64 channels cb*64 .. +63 of tap (kh, kw) with
+// g = (kh*KW + kw)*C/64 + cb. A lane reads its 16 channels at input pixel
+// (oh*stride + kh - pad, ow*stride + kw - pad) or, outside the image, loads a
+// clamped pixel and uses zeros, so every load stays unconditional.
+template <typename XT, int NCB, int NB, bool MX, bool CONV>
 __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
     const XT* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
     const float* __restrict__ inv_smooth, const uint16_t* __restrict__ L1p, int R,
-    uint8_t* __restrict__ a_codes, void* __restrict__ a_meta, float* __restrict__ D) {
+    uint8_t* __restrict__ a_codes, void* __restrict__ a_meta, float* __restrict__ D,
+    ConvGeom cg) {
 #pragma clang fp contract(off)
   constexpr int WAVES = k1_waves<NCB>();
   constexpr int NCBA = NCB > 0 ? NCB : 1;
@@ -252,11 +261,39 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
     return l1b + static_cast<int64_t>((g * ncb + cc) * 2 + h) * 64 + lane;
   };
 
+  // convolution: this lane's output pixel (its first input pixel and the
+  // pixel offset of its image)
+  int pix0 = 0, ih0 = 0, iw0 = 0;
+  if constexpr (CONV) {
+    const int p = static_cast<int>(row0) + static_cast<int>(lq);
+    const int ohw = cg.OH * cg.OW;
+    const int img = p / ohw, rem = p - img * ohw;
+    const int oh = rem / cg.OW, ow = rem - oh * cg.OW;
+    pix0 = img * cg.H * cg.W;
+    ih0 = oh * cg.stride - cg.pad;
+    iw0 = ow * cg.stride - cg.pad;
+  }
+
   auto load_group = [&](GroupIn<XT, NCB>& in, int i) {
     int g = wave + WAVES * i;
     g = g < G ? g : G - 1;
     const int k0 = g * kGroup;
-    load_raw<XT>(in.x, xblk + k0 + xoff);
+    if constexpr (CONV) {
+      const int cbs = cg.C / kGroup;                  // channel groups per tap (uniform)
+      const int t = g / cbs, cb = g - t * cbs;
+      const int kh = t / cg.KW, kw = t - kh * cg.KW;
+      const int ih = ih0 + kh, iw = iw0 + kw;
+      in.valid = static_cast<unsigned>(ih) < static_cast<unsigned>(cg.H) &&
+                 static_cast<unsigned>(iw) < static_cast<unsigned>(cg.W);
+      const int ihc = ih < 0 ? 0 : (ih >= cg.H ? cg.H - 1 : ih);
+      const int iwc = iw < 0 ? 0 : (iw >= cg.W ? cg.W - 1 : iw);
+      const uint32_t off = static_cast<uint32_t>(pix0 + ihc * cg.W + iwc) *
+                               static_cast<uint32_t>(cg.C) + cb * kGroup + c4 * 16;
+      load_raw<XT>(in.x, X + off);
+    } else {
+      in.valid = true;
+      load_raw<XT>(in.x, xblk + k0 + xoff);
+    }
     const float4* ip = reinterpret_cast<const float4*>(inv_smooth + k0 + ioff);
 #pragma unroll
     for (int j = 0; j < 4; ++j) in.inv[j] = ip[j];
@@ -287,6 +324,11 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
       if (i < n_mine) {
         float xh[16];
         smooth16(ring[b].x, ring[b].inv, xh);
+        if constexpr (CONV) {
+          // a tap outside the image: the patch matrix holds zeros there
+#pragma unroll
+          for (int j = 0; j < 16; ++j) xh[j] = ring[b].valid ? xh[j] : 0.f;
+        }
         if constexpr (MX) {
           quantize_mx(xh, packed, meta);
         } else {
@@ -381,19 +423,23 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
 template <typename XT, int NCB>
 hipError_t launch_k1_t(const void* X, int64_t M, int64_t K, int64_t ldx,
                        const float* inv_smooth, const uint16_t* L1p, int R,
-                       uint8_t* a_codes, void* a_meta, bool mx, float* D, hipStream_t stream) {
+                       uint8_t* a_codes, void* a_meta, bool mx, float* D, hipStream_t stream,
+                       const ConvGeom* conv) {
   // groups in flight per wave, sized so the ring fits the register budget of
   // two resident workgroups
   constexpr int NB = 1;
   const dim3 block(64 * k1_waves<NCB>()), grid(static_cast<unsigned>((M + 15) / 16));
-  if (mx)
-    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, true>), grid, block, 0, stream,
-                       static_cast<const XT*>(X), M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta,
-                       D);
+  const XT* x = static_cast<const XT*>(X);
+  const ConvGeom cg = conv ? *conv : ConvGeom{};
+  if (conv)
+    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, false, true>), grid, block, 0, stream,
+                       x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
+  else if (mx)
+    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, true, false>), grid, block, 0, stream,
+                       x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
   else
-    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, false>), grid, block, 0, stream,
-                       static_cast<const XT*>(X), M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta,
-                       D);
+    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, false, false>), grid, block, 0, stream,
+                       x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
   return hipGetLastError();
 }
 
@@ -401,18 +447,18 @@ template <typename XT>
 hipError_t launch_k1_dtype(const void* X, int64_t M, int64_t K, int64_t ldx,
                                   const float* inv_smooth, const uint16_t* L1p, int R,
                                   uint8_t* a_codes, void* a_meta, bool mx, float* D,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, const ConvGeom* conv) {
   switch (R / 16) {
-    case 0: return launch_k1_t<XT, 0>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
-    case 1: return launch_k1_t<XT, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
-    case 2: return launch_k1_t<XT, 2>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
-    case 3: return launch_k1_t<XT, 3>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
-    case 4: return launch_k1_t<XT, 4>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
-    case 5: return launch_k1_t<XT, 5>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
-    case 6: return launch_k1_t<XT, 6>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
+    case 0: return launch_k1_t<XT, 0>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
+    case 1: return launch_k1_t<XT, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
+    case 2: return launch_k1_t<XT, 2>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
+    case 3: return launch_k1_t<XT, 3>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
+    case 4: return launch_k1_t<XT, 4>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
+    case 5: return launch_k1_t<XT, 5>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
+    case 6: return launch_k1_t<XT, 6>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
     case 7:
-    case 8: return launch_k1_t<XT, 8>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
-    default: return launch_k1_t<XT, 16>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
+    case 8: return launch_k1_t<XT, 8>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
+    default: return launch_k1_t<XT, 16>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
   }
 }
 
@@ -420,10 +466,10 @@ hipError_t launch_k1_dtype(const void* X, int64_t M, int64_t K, int64_t ldx,
 
 hipError_t launch_k1(const void* X, bool x_f16, int64_t M, int64_t K, int64_t ldx,
                      const float* inv_smooth, const uint16_t* L1p, int R, uint8_t* a_codes,
-                     void* a_meta, bool mx, float* D, hipStream_t stream) {
+                     void* a_meta, bool mx, float* D, hipStream_t stream, const ConvGeom* conv) {
   if (x_f16)
-    return launch_k1_dtype<_Float16>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
-  return launch_k1_dtype<float>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream);
+    return launch_k1_dtype<_Float16>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
+  return launch_k1_dtype<float>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
 }
 
 }  // namespace svdq

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 4
+#define SVDQ_ABI_VERSION 5
 
 /* status codes */
 enum {
@@ -358,6 +358,50 @@ int svdq_linear_w4a16(const void* X, int x_dtype, int64_t ldx, const uint8_t* w_
                       const uint16_t* w_scales_t, const float* bias, void* Y, int y_dtype,
                       int64_t ldy, int64_t M, int64_t K, int64_t N, void* ws, size_t ws_bytes,
                       hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Convolutions (the chattools.cn overview, section "SVDQuant的技术原理", says
+ * the method serves UNet backbones as well as DiT ones; the pages give no
+ * convolution-specific rule). Reading implemented: a KH x KW convolution with
+ * square stride and zero padding is the linear layer above on its patch
+ * matrix, with no patch matrix in memory:
+ *   X      NHWC image, batch x H x W x C, contiguous, fp16 or fp32;
+ *          C a positive multiple of 64 (a group of 64 never straddles taps);
+ *   M = batch * OH * OW patches (row p = (b, oh, ow), b-major),
+ *          OH = (H + 2 pad - KH) / stride + 1, OW likewise;
+ *   K = KH * KW * C, column (kh * KW + kw) * C + c holding channel c of pixel
+ *          (oh * stride + kh - pad, ow * stride + kw - pad), 0 outside the image;
+ *   lam, L1, L2, the residual: those of the K x N weight matrix Wm whose row
+ *          (kh * KW + kw) * C + c is the filter tap (kh, kw, c), i.e. a
+ *          KH x KW x C x N (HWIO) filter reshaped; svdq_prepare_weights on Wm;
+ *   Y      M x N row-major = the NHWC output batch x OH x OW x N.
+ * Limits: KH, KW, stride in [1, 64], pad in [0, 64], KH <= H + 2 pad (and W),
+ * batch*H*W*C and M below 2^31, K at most 2^25. INT4 format only.
+ */
+
+/* Host: out[k] (k < K) = max over the M patches of |patch matrix entry k|,
+ * the calibration statistic of the convolution's smoothing factors. */
+int svdq_conv_patch_absmax(const void* X, int x_dtype, int64_t batch, int64_t H, int64_t W,
+                           int64_t C, int32_t KH, int32_t KW, int32_t stride, int32_t pad,
+                           float* out);
+
+/* Device: K1 on the patch matrix: a_codes (M x K/2), a_scales (M x K/64) and
+ * D (M x R) as svdq_quantize_act_lowrank_down would give for the patch matrix
+ * in memory (bit-exact). X 16-byte aligned. */
+int svdq_quantize_act_lowrank_down_conv(const void* X, int x_dtype, int64_t batch, int64_t H,
+                                        int64_t W, int64_t C, int32_t KH, int32_t KW,
+                                        int32_t stride, int32_t pad, const float* inv_smooth,
+                                        const uint16_t* L1p, int32_t R, uint8_t* a_codes,
+                                        uint16_t* a_scales, float* D, hipStream_t stream);
+
+/* Device: the whole convolution, K1 on the patch matrix into `ws`, then K2
+ * (svdq_w4a4_gemm_lowrank_up) into Y (ldy = N). ws: 256-byte aligned, at
+ * least svdq_linear_workspace_bytes(M, K, R, 64) bytes. */
+int svdq_conv2d(const void* X, int x_dtype, int64_t batch, int64_t H, int64_t W, int64_t C,
+                int32_t KH, int32_t KW, int32_t stride, int32_t pad, const float* inv_smooth,
+                const uint16_t* L1p, const uint16_t* L2t, int32_t R, const uint8_t* w_codes,
+                const uint16_t* w_scales, const float* bias, void* Y, int y_dtype, int64_t N,
+                void* ws, size_t ws_bytes, int32_t activation, hipStream_t stream);
 
 /* Test hook: the exact integer partials P[m, n, g] for rows row0 .. row0+rows-1,
  * computed with the same operand unpacking and int8 matrix-core instruction

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert _lib.abi_version() == 4
+    assert _lib.abi_version() == 5
     for s in range(12):
         assert _lib.status_str(s) and _lib.status_str(s) != "unknown status"
     assert _lib.status_str(99) == "unknown status"
@@ -60,6 +60,24 @@ def test_channel_absmax_and_smoothing_bit_exact():
         lam = sq.smoothing_factors(xa, W)
         assert np.array_equal(lam, O.smoothing_factors(O.channel_absmax(Xd), W))
     assert lam[5] == 1.0 and lam[7] == 1.0
+
+
+@pytest.mark.parametrize("geom", [
+    # batch, H, W, C, KH, KW, stride, pad
+    (1, 8, 8, 64, 3, 3, 1, 1), (2, 5, 7, 128, 3, 3, 2, 1), (1, 6, 4, 64, 1, 1, 1, 0),
+    (1, 4, 4, 64, 5, 5, 1, 2), (3, 9, 5, 192, 3, 2, 3, 0), (1, 2, 2, 64, 1, 1, 1, 2)])
+def test_conv_patch_absmax_bit_exact(geom):
+    """Column maxima of the implicit patch matrix = those of the oracle's im2col."""
+    B, H, W, Cc, KH, KW, st, pad = geom
+    rng = np.random.default_rng(sum(geom))
+    X = rng.standard_normal((B, H, W, Cc)).astype(np.float32)
+    X[..., 3] *= 30
+    for Xd in (X, X.astype(np.float16)):
+        got = sq.conv_patch_absmax(Xd, KH, KW, st, pad)
+        ref = O.channel_absmax(O.im2col_nhwc(Xd, KH, KW, st, pad)).astype(np.float32)
+        assert got.shape == (KH * KW * Cc,)
+        assert np.array_equal(got, ref)
+    assert sq.conv_out_size(H, KH, st, pad) == (H + 2 * pad - KH) // st + 1
 
 
 @pytest.mark.parametrize("K,N,r", [(64, 16, 0), (128, 96, 16), (256, 64, 32), (192, 300, 48),
@@ -390,6 +408,38 @@ def test_device_entry_points_reject_bad_arguments():
     assert need16 == 2 * 1024
     lw = [A16, 1, 64, A16, A16, None, A16, 1, 16, 16, 64, 16, A16, need16 - 1, None]
     assert L.svdq_linear_w4a16(*lw) == _lib.ERR_WORKSPACE
+    # convolutions: geometry checks come before any pointer is used
+    geo = [1, 8, 8, 64, 3, 3, 1, 1]
+    assert L.svdq_conv_patch_absmax(None, 2, *geo, A16) == _lib.ERR_NULL
+    for bad_geo in ([1, 8, 8, 96, 3, 3, 1, 1],     # C not a multiple of 64
+                    [1, 8, 8, 0, 3, 3, 1, 1],
+                    [0, 8, 8, 64, 3, 3, 1, 1],
+                    [1, 8, 8, 64, 3, 3, 0, 1],     # stride 0
+                    [1, 8, 8, 64, 3, 3, 1, -1],    # negative pad
+                    [1, 2, 8, 64, 5, 3, 1, 1],     # kernel taller than the padded image
+                    [1, 8, 8, 64, 65, 1, 1, 40],   # kernel beyond 64
+                    [1 << 16, 128, 128, 64, 3, 3, 1, 1]):   # image past 2^31 elements
+        assert L.svdq_conv_patch_absmax(A16, 2, *bad_geo, A16) == _lib.ERR_SHAPE, bad_geo
+        assert L.svdq_quantize_act_lowrank_down_conv(A16, 1, *bad_geo, A16, A16, 16, A16, A16, A16,
+                                                     None) == _lib.ERR_SHAPE, bad_geo
+        assert L.svdq_conv2d(A16, 1, *bad_geo, A16, A16, A16, 16, A16, A16, None, A16, 1, 16, A16,
+                             1 << 20, 0, None) == _lib.ERR_SHAPE, bad_geo
+    assert L.svdq_conv_patch_absmax(A16, 5, *geo, A16) == _lib.ERR_DTYPE
+    assert L.svdq_quantize_act_lowrank_down_conv(MIS, 1, *geo, A16, A16, 16, A16, A16, A16, None) == _lib.ERR_ALIGN
+    assert L.svdq_quantize_act_lowrank_down_conv(A16, 1, *geo, A16, A16, 24, A16, A16, A16, None) == _lib.ERR_RANK
+    assert L.svdq_quantize_act_lowrank_down_conv(A16, 1, *geo, A16, None, 16, A16, A16, A16, None) == _lib.ERR_NULL
+    # patch matrix 64 x 576: the workspace is that of the linear layer
+    need_c = L.svdq_linear_workspace_bytes(64, 576, 16, 64)
+    ca = [A16, 1, *geo, A16, A16, A16, 16, A16, A16, None, A16, 1, 16, A16, need_c - 1, 0, None]
+    assert L.svdq_conv2d(*ca) == _lib.ERR_WORKSPACE
+    ca[21] = need_c
+    ca[22] = 4
+    assert L.svdq_conv2d(*ca) == _lib.ERR_ACT
+    ca[22] = 0
+    ca[20] = 0x10080
+    assert L.svdq_conv2d(*ca) == _lib.ERR_ALIGN
+    ca[20] = None
+    assert L.svdq_conv2d(*ca) == _lib.ERR_NULL
     # partials hook: slice outside the rows
     assert L.svdq_debug_group_partials(A16, A16, 16, 16, 64, 64, 10, 7, A16, None) == _lib.ERR_SHAPE
     assert L.svdq_gelu_tanh_f16(A16, MIS, 8, None) == _lib.ERR_ALIGN
@@ -414,3 +464,8 @@ def test_device_entry_points_report_no_device():
     assert L.svdq_gelu_tanh_f16(A16, A16, 8, None) == _lib.ERR_NO_DEVICE
     assert L.svdq_quantize_act_lowrank_down_mx(A16, 1, 16, 64, 64, A16, A16, 16, A16, A16, A16, None) == _lib.ERR_NO_DEVICE
     assert L.svdq_mx_gemm_lowrank_up(A16, A16, A16, A16, A16, A16, 16, None, A16, 1, 16, 16, 64, 16, 0, None) == _lib.ERR_NO_DEVICE
+    geo = [1, 8, 8, 64, 3, 3, 1, 1]
+    assert L.svdq_quantize_act_lowrank_down_conv(A16, 1, *geo, A16, A16, 16, A16, A16, A16, None) == _lib.ERR_NO_DEVICE
+    need_c = L.svdq_linear_workspace_bytes(64, 576, 16, 64)
+    assert L.svdq_conv2d(A16, 1, *geo, A16, A16, A16, 16, A16, A16, None, A16, 1, 16, 0x10000,
+                         need_c, 0, None) == _lib.ERR_NO_DEVICE
