@@ -19,16 +19,14 @@
 // Work split: a workgroup owns 16 rows; its waves (8, or 4 at high rank) take
 // the 64-channel groups round-robin.
 //
-// Two lane maps per wave and group:
-// - quantizer map: lane l holds row l/4 and channels 16*(l%4) .. +15, so each
-//   group of 16 lanes reads 4 whole 128-byte row segments of X (coalesced),
-//   the row's absmax is a reduction over 4 neighbouring lanes (quad DPP), and
-//   the 4 lanes of a row write its 32 bytes of codes side by side;
-// - matrix map: v_mfma_f32_16x16x32_f16 wants lane l to hold row l%16 and 8
-//   consecutive channels per operand. The fp16 values go from one map to the
-//   other through a small per-wave LDS tile (the row stride is padded by 16
-//   bytes so both the stores and the loads are spread over all banks).
-// L1 arrives packed in the matrix instruction's operand order (see
+// Lane map per wave and group: lane l holds row l%16 and channels
+// 16*(l/16) .. +15, which is exactly what v_mfma_f32_16x16x32_f16 wants for
+// its two K-halves (8 consecutive channels per operand), so the fp16 values
+// of the down-projection never leave the registers. A row's group is spread
+// over the lanes r, r+16, r+32, r+48: its absmax is a reduction over those
+// four lanes with the gfx950 lane-swap instructions (v_permlane16_swap,
+// v_permlane32_swap), and the four lanes write its 32 bytes of codes side by
+// side. L1 arrives packed in the matrix instruction's operand order (see
 // svdq_pack_lowrank_down), so each operand is one contiguous 1 KB load per
 // wave. The per-wave partial D tiles are summed in LDS in a fixed order.
 //
@@ -76,8 +74,13 @@ __device__ __forceinline__ void load_raw<float>(Raw<float>& r, const float* p) {
   for (int i = 0; i < 4; ++i) r.v[i] = q[i];
 }
 
-// xh[i] = fp32(x[i]) * inv[i], rounded once to fp32.
-__device__ __forceinline__ void smooth16(const Raw<_Float16>& r, const float4* inv, float* xh) {
+// xh[i] = fp32(x[i]) * inv[i], rounded once to fp32. For fp16 X this is one
+// v_fma_mix_f32 per value: fma(fp32(x), inv, -0) equals the product exactly
+// (adding -0 changes no value, not even a zero's sign); `nz` is -0 in a
+// register the compiler cannot see through, which keeps it from rewriting the
+// fma as a conversion plus a multiply.
+__device__ __forceinline__ void smooth16(const Raw<_Float16>& r, const float4* inv, float* xh,
+                                         float nz) {
   const uint32_t w[8] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w,
                          r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
   const float iv[16] = {inv[0].x, inv[0].y, inv[0].z, inv[0].w, inv[1].x, inv[1].y,
@@ -85,12 +88,13 @@ __device__ __forceinline__ void smooth16(const Raw<_Float16>& r, const float4* i
                         inv[3].x, inv[3].y, inv[3].z, inv[3].w};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    xh[2 * i] = h2f(static_cast<uint16_t>(w[i] & 0xFFFFu)) * iv[2 * i];
-    xh[2 * i + 1] = h2f(static_cast<uint16_t>(w[i] >> 16)) * iv[2 * i + 1];
+    xh[2 * i] = __builtin_fmaf(h2f(static_cast<uint16_t>(w[i] & 0xFFFFu)), iv[2 * i], nz);
+    xh[2 * i + 1] = __builtin_fmaf(h2f(static_cast<uint16_t>(w[i] >> 16)), iv[2 * i + 1], nz);
   }
 }
 
-__device__ __forceinline__ void smooth16(const Raw<float>& r, const float4* inv, float* xh) {
+__device__ __forceinline__ void smooth16(const Raw<float>& r, const float4* inv, float* xh,
+                                         float) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     xh[4 * i] = r.v[i].x * inv[i].x;
@@ -100,34 +104,47 @@ __device__ __forceinline__ void smooth16(const Raw<float>& r, const float4* inv,
   }
 }
 
-// max over the 4 lanes of a quad (lanes 4r .. 4r+3), via DPP quad permutes
-__device__ __forceinline__ float quad_max(float a) {
-  const int xor1 = 0xB1;            // quad_perm [1, 0, 3, 2]
-  const int xor2 = 0x4E;            // quad_perm [2, 3, 0, 1]
-  a = fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a),
-                                                                  xor1, 0xF, 0xF, false)));
-  a = fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a),
-                                                                  xor2, 0xF, 0xF, false)));
-  return a;
+// Maxima of non-negative floats across lanes, on their bit patterns (for
+// values >= 0 the unsigned order of the bits is the order of the values, and
+// no NaN quieting is involved). permlane16_swap(v, v) hands every lane the
+// value of lane l^16 in one of its two results, permlane32_swap(v, v) that of
+// lane l^32.
+__device__ __forceinline__ float max_xor16(float a) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, a);
+  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  return __builtin_bit_cast(float, r[0] > r[1] ? r[0] : r[1]);
+}
+__device__ __forceinline__ float max_xor32(float a) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, a);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __builtin_bit_cast(float, r[0] > r[1] ? r[0] : r[1]);
 }
 
-// max with the other lane of the pair (lanes 2r, 2r+1): the two lanes that
-// hold one 32-channel block
-__device__ __forceinline__ float pair_max(float a) {
-  return fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a),
-                                                                     0xB1, 0xF, 0xF, false)));
+// Codes of 8 values from the fp32 bit patterns of (value + 1.5 * 2^23), whose
+// low byte is the value's two's-complement integer: byte j of the result is
+// code 2j in its low nibble and code 2j+1 in its high nibble. Byte permutes
+// gather the even and the odd codes, a bit-field insert merges them.
+__device__ __forceinline__ uint32_t pack8_codes(const uint32_t* b) {
+  constexpr uint32_t kLow2 = 0x0C0C0400u;        // [S1.byte0, S0.byte0, 0, 0]
+  constexpr uint32_t kCat = 0x05040100u;         // [S1.byte0, S1.byte1, S0.byte0, S0.byte1]
+  const uint32_t ev = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[6], b[4], kLow2),
+                                            __builtin_amdgcn_perm(b[2], b[0], kLow2), kCat);
+  const uint32_t od = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[5], kLow2),
+                                            __builtin_amdgcn_perm(b[3], b[1], kLow2), kCat);
+  return (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
 }
 
 constexpr float kInv7 = 0.142857149f;           // fp32(1/7) = 0x3E124925
 
-// INT4 quantizer of one row's group of 64 (4 lanes, 16 values each): packed
-// codes of this lane's 16 values and the group's fp16 scale.
+// INT4 quantizer of one row's group of 64 (lanes r, r+16, r+32, r+48, 16
+// values each): packed codes of this lane's 16 values and the group's fp16
+// scale.
 __device__ __forceinline__ void quantize_int4(const float* xh, uint32_t packed[2], uint16_t& s16) {
   // group absmax over this lane's 16 values, then across the 4 lanes of the row
   float a = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(xh[j]));
-  a = quad_max(a);
+  a = max_xor32(max_xor16(a));
   // fp32(a / 7), correctly rounded, as one multiply by fp32(1/7) and one
   // FMA correction (division by a constant known in advance: Brisebarre,
   // Muller, Raina, IEEE Trans. Computers 2004); for the divisor 7 this is
@@ -137,33 +154,39 @@ __device__ __forceinline__ void quantize_int4(const float* xh, uint32_t packed[2
   const float s32 = fminf(__builtin_fmaf(__builtin_fmaf(-q7, 7.0f, a), kInv7, q7), 65504.0f);
   s16 = f2h(s32);
   const float sf = h2f(s16);
-  const float inv = (sf == 0.f) ? 0.f : 1.0f / sf;
+  // 1/s correctly rounded: the hardware reciprocal (within one ulp) and one
+  // Newton step give exactly the IEEE quotient for every fp16 s (checked
+  // exhaustively on the host, for any start within two floats of it)
+  const float r0 = __builtin_amdgcn_rcpf(sf);
+  const float rc = __builtin_fmaf(__builtin_fmaf(-sf, r0, 1.0f), r0, r0);
+  const float inv = (sf == 0.f) ? 0.f : rc;
   // code = clamp(rint(xh * inv), -7, 7): clamping first gives the same
   // result, and adding 1.5 * 2^23 rounds half-to-even to an integer whose
   // low 4 bits are its two's-complement nibble.
-  packed[0] = packed[1] = 0u;
+  uint32_t bits[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const float c = __builtin_amdgcn_fmed3f(xh[j] * inv, -7.f, 7.f);
-    const uint32_t bits = __builtin_bit_cast(uint32_t, c + kMagicF);
-    packed[j >> 3] |= (bits & 0xFu) << (4 * (j & 7));
+    bits[j] = __builtin_bit_cast(uint32_t, c + kMagicF);
   }
+  packed[0] = pack8_codes(bits);
+  packed[1] = pack8_codes(bits + 8);
 }
 
-// MXFP4 quantizer of one row's two 32-channel blocks (lanes 0, 1 of the quad
-// hold the first, lanes 2, 3 the second): packed E2M1 codes of this lane's 16
-// values, and in lane 0 of the quad both E8M0 bytes (first block low).
+// MXFP4 quantizer of one row's two 32-channel blocks (lanes r, r+16 hold the
+// first, lanes r+32, r+48 the second): packed E2M1 codes of this lane's 16
+// values and the E8M0 byte of its block.
 // The shared exponent is e = floor(log2 amax) - 2, at least -127, i.e. the
 // E8M0 byte is amax's biased exponent field minus 2, floored at 0. Values are
 // first multiplied by 2^-e (exact: a power of two, and every product that is
 // not a normal fp32 is below 0.25 and gives a zero code of the same sign),
 // then converted with scale 1 by v_cvt_scalef32_pk_fp4_f32, which rounds to
 // the nearest E2M1 value, ties to even, and saturates at 6.
-__device__ __forceinline__ void quantize_mx(const float* xh, uint32_t packed[2], uint32_t& e8pair) {
+__device__ __forceinline__ void quantize_mx(const float* xh, uint32_t packed[2], uint32_t& e8out) {
   float a = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(xh[j]));
-  a = pair_max(a);
+  a = max_xor16(a);
   const int ex = static_cast<int>(__builtin_bit_cast(uint32_t, a) >> 23);
   const int e8 = ex > 2 ? ex - 2 : 0;
   const float mult = __builtin_bit_cast(float, static_cast<uint32_t>(254 - e8) << 23);
@@ -176,8 +199,7 @@ __device__ __forceinline__ void quantize_mx(const float* xh, uint32_t packed[2],
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xh[8 * d + 6] * mult, xh[8 * d + 7] * mult, 1.0f, 3);
     packed[d] = w;
   }
-  const int e8_next = __builtin_amdgcn_mov_dpp(e8, 0x4E, 0xF, 0xF, false);   // lane + 2 of the quad
-  e8pair = static_cast<uint32_t>(e8) | (static_cast<uint32_t>(e8_next) << 8);
+  e8out = static_cast<uint32_t>(e8);
 }
 
 // L1 operands travel in the ring up to rank 128; above that they would not fit
@@ -200,8 +222,6 @@ struct GroupIn {
   v8h l1[ring_l1_blocks<NCB>() > 0 ? ring_l1_blocks<NCB>() : 1][2];
 };
 
-constexpr int kXsStride = kGroup + 8;           // fp16 elements per row of the LDS tile
-
 // a_codes, a_meta: INT4 codes (M x K/2) and fp16 group scales (M x K/64), or
 // for MX the tiled E2M1 codes and E8M0 exponents (see svdq.h).
 // CONV: X is an NHWC image and the rows are the patches of the convolution cg
@@ -221,13 +241,13 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
   constexpr int WAVES = k1_waves<NCB>();
   constexpr int NCBA = NCB > 0 ? NCB : 1;
   __shared__ float dpart[WAVES][16][NCBA * 16];
-  __shared__ __attribute__((aligned(16))) uint16_t xs[WAVES][16][kXsStride];
   const int lane = threadIdx.x & 63;
   // the wave index is the same in all lanes: keep it (and everything derived
   // from it: group numbers, group offsets) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int qr = lane >> 2, c4 = lane & 3;         // quantizer map
-  const int rl = lane & 15, q = lane >> 4;          // matrix map
+  // lane map: row qr = rl of the tile, channels 16*c4 .. +15 of each group
+  const int rl = lane & 15, q = lane >> 4;
+  const int qr = rl, c4 = q;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int nrows = M - row0 < 16 ? static_cast<int>(M - row0) : 16;
   const bool rvalid = qr < nrows;
@@ -310,6 +330,10 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
 #pragma unroll
   for (int c = 0; c < NCBA; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // -0 in a register the compiler cannot see through (see smooth16)
+  float nz;
+  __asm__("v_mov_b32 %0, 0x80000000" : "=v"(nz));
+
   GroupIn<XT, NCB> ring[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) load_group(ring[b], b);
@@ -320,10 +344,10 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
       const int i = i0 + b;
       const int g = wave + WAVES * i;
       uint32_t packed[2] = {0u, 0u};
-      uint32_t meta = 0u;                  // fp16 scale, or the two E8M0 bytes
+      uint32_t meta = 0u;                  // fp16 scale, or the E8M0 byte
       if (i < n_mine) {
         float xh[16];
-        smooth16(ring[b].x, ring[b].inv, xh);
+        smooth16(ring[b].x, ring[b].inv, xh, nz);
         if constexpr (CONV) {
           // a tap outside the image: the patch matrix holds zeros there
 #pragma unroll
@@ -337,26 +361,20 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
           meta = s16;
         }
         if constexpr (NCB > 0) {
-          // fp16 values to the matrix map through this wave's LDS tile
-          // Xhat is rounded to fp32 first and then to fp16. The empty asm hands
-          // the conversion an opaque fp32 value: otherwise the backend folds
+          // the lane's 16 values, rounded to fp16, are its two matrix
+          // operands. Xhat is rounded to fp32 first and then to fp16 (RNE).
+          // The conversion is written out: as plain code the backend folds
           // the product and the conversion into one v_fma_mixlo_f16, which
           // rounds only once and differs in rare double-rounding cases.
-          uint32_t h[8];
+          v2h hp[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            float lo = xh[2 * j], hi = xh[2 * j + 1];
-            __asm__ volatile("" : "+v"(lo), "+v"(hi));
-            h[j] = static_cast<uint32_t>(f2h(lo)) | (static_cast<uint32_t>(f2h(hi)) << 16);
+            uint32_t r;
+            __asm__("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(xh[2 * j]), "v"(xh[2 * j + 1]));
+            hp[j] = __builtin_bit_cast(v2h, r);
           }
-          uint4* wp = reinterpret_cast<uint4*>(&xs[wave][qr][c4 * 16]);
-          wp[0] = make_uint4(h[0], h[1], h[2], h[3]);
-          wp[1] = make_uint4(h[4], h[5], h[6], h[7]);
-          __asm__ volatile("" ::: "memory");          // LDS of one wave is in order
-          const uint4* rp = reinterpret_cast<const uint4*>(&xs[wave][rl][q * 16]);
-          const v8h x0 = __builtin_bit_cast(v8h, rp[0]);
-          const v8h x1 = __builtin_bit_cast(v8h, rp[1]);
-          __asm__ volatile("" ::: "memory");
+          const v8h x0 = {hp[0][0], hp[0][1], hp[1][0], hp[1][1], hp[2][0], hp[2][1], hp[3][0], hp[3][1]};
+          const v8h x1 = {hp[4][0], hp[4][1], hp[5][0], hp[5][1], hp[6][0], hp[6][1], hp[7][0], hp[7][1]};
           if constexpr (ring_l1_blocks<NCB>() > 0) {
 #pragma unroll
             for (int c = 0; c < NCB; ++c) {
