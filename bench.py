@@ -271,16 +271,22 @@ def conv_cpu_baseline(L, X, Wm, prep, bias, budget_s):
     Xcol = O.im2col_nhwc(X, L.KH, L.KW, L.stride, L.pad)
     lam = O.smoothing_factors(O.channel_absmax(Xcol), Wm)
     inv = O.inv_smoothing(lam)
-    wc, ws = O.quantize_residual_from_factors(Wm, lam, prep.L1, prep.L2)
+    mx = prep.fmt == "mxfp4"
+    if mx:
+        wc, ws = O.mx_quantize_residual_from_factors(Wm, lam, prep.L1, prep.L2)
+    else:
+        wc, ws = O.quantize_residual_from_factors(Wm, lam, prep.L1, prep.L2)
     t_setup = time.perf_counter() - t0
     chunk, rows = 32, 0
     t0 = time.perf_counter()
     while rows < L.M and time.perf_counter() - t0 < budget_s:
         r = slice(rows, min(L.M, rows + chunk))
-        O.linear(Xcol[r], inv, prep.L1, prep.L2, wc, ws, bias, L.y_dtype)
+        (O.mx_linear if mx else O.linear)(Xcol[r], inv, prep.L1, prep.L2, wc, ws, bias,
+                                          L.y_dtype)
         rows = r.stop
     t = time.perf_counter() - t0
-    return dict(value=2.0 * rows * L.N * L.K / t / 1e12, unit="TOPS", cores=int(cores),
+    return dict(value=2.0 * rows * L.N * L.K / t / 1e12, unit="TFLOPS" if mx else "TOPS",
+                cores=int(cores),
                 kind="oracle",
                 sample=f"first {rows} of {L.M} output pixels of the same convolution, online "
                        f"part only ({t:.1f} s, numpy fp64, chunks of {chunk}; the im2col and "
@@ -289,41 +295,51 @@ def conv_cpu_baseline(L, X, Wm, prep, bias, budget_s):
 
 def conv_main(args, torch, sq, wl):
     """Step = one UNet convolution on one batch: K1 on the implicit patch matrix
-    of the NHWC image, then K2 (the same kernels as svdq_conv2d)."""
+    of the NHWC image, then K2 (the same kernels as svdq_conv2d, or with
+    --format mxfp4 their MXFP4 versions, as svdq_conv2d_mx)."""
     L, X, Wc = wl.conv_inputs(args.conv)
+    mx = args.format == "mxfp4"
+    if args.format == "w4a16":
+        raise SystemExit("--conv runs the INT4 or MXFP4 format")
     Wm = Wc.reshape(L.K, L.N)
     bias = wl.bias(wl.CONV_CFG, args.conv, L.N)
     lam = sq.smoothing_factors(sq.conv_patch_absmax(X, L.KH, L.KW, L.stride, L.pad), Wm)
-    prep = sq.prepare_weights(Wm, lam, L.rank)
+    prep = (sq.prepare_weights_mx if mx else sq.prepare_weights)(Wm, lam, L.rank)
     M, K, N, R = L.M, L.K, L.N, prep.rank
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16
                                    else np.ascontiguousarray(a)).to("cuda")
+    if mx:
+        wct, wet = sq.pack_mx_tiles(prep.w_codes, prep.w_scales, K)
+    else:
+        wct, wet = prep.w_codes, prep.w_scales
     ydt = torch.float16 if L.y_dtype == "f16" else torch.float32
     sets = []
     for _ in range(args.sets):
-        sets.append(dict(
-            X=d(X), inv=d(prep.inv_smooth), L1p=d(prep.L1p), L2t=d(prep.L2t), wc=d(prep.w_codes),
-            ws=d(prep.w_scales), b=d(bias),
-            ac=torch.empty((M, K // 2), dtype=torch.uint8, device="cuda"),
-            asc=torch.empty((M, K // 64), dtype=torch.int16, device="cuda"),
-            D=torch.empty((M, R), dtype=torch.float32, device="cuda"),
-            Y=torch.empty((L.batch, L.OH, L.OW, N), dtype=ydt, device="cuda")))
+        s = dict(X=d(X), inv=d(prep.inv_smooth), L1p=d(prep.L1p), L2t=d(prep.L2t), wc=d(wct),
+                 ws=d(wet), b=d(bias), D=torch.empty((M, R), dtype=torch.float32, device="cuda"),
+                 Y=torch.empty((L.batch, L.OH, L.OW, N), dtype=ydt, device="cuda"))
+        if mx:
+            s.update(ac=torch.empty(sq.mx_codes_tiled_bytes(M, K), dtype=torch.uint8, device="cuda"),
+                     asc=torch.empty(sq.mx_exps_tiled_bytes(M, K), dtype=torch.uint8, device="cuda"))
+        else:
+            s.update(ac=torch.empty((M, K // 2), dtype=torch.uint8, device="cuda"),
+                     asc=torch.empty((M, K // 64), dtype=torch.int16, device="cuda"))
+        sets.append(s)
+    k1f = sq.quantize_act_lowrank_down_conv_mx if mx else sq.quantize_act_lowrank_down_conv
+    k2f = sq.mx_gemm_lowrank_up if mx else sq.w4a4_gemm_lowrank_up
 
-    def k1(i):
-        s = sets[i % len(sets)]
-        sq.quantize_act_lowrank_down_conv(s["X"], L.KH, L.KW, L.stride, L.pad, s["inv"], s["L1p"],
-                                          R, s["ac"], s["asc"], s["D"])
+    class _Step:
+        def k1(self, i):
+            s = sets[i % len(sets)]
+            k1f(s["X"], L.KH, L.KW, L.stride, L.pad, s["inv"], s["L1p"], R, s["ac"], s["asc"],
+                s["D"])
 
-    def k2(i):
-        s = sets[i % len(sets)]
-        sq.w4a4_gemm_lowrank_up(s["ac"], s["asc"], s["wc"], s["ws"], s["D"], s["L2t"], R, s["b"],
-                                s["Y"].view(M, N), K)
+        def k2(self, i):
+            s = sets[i % len(sets)]
+            k2f(s["ac"], s["asc"], s["wc"], s["ws"], s["D"], s["L2t"], R, s["b"],
+                s["Y"].view(M, N), K)
 
-    class _S:
-        pass
-    st = _S()
-    st.k1, st.k2 = k1, k2
-    t_step, t1, t2 = time_steps(torch, st, args.steps, args.warmup)
+    t_step, t1, t2 = time_steps(torch, _Step(), args.steps, args.warmup)
     gap = event_gap(torch)
     k1_avg = float(np.mean(t1)) - gap
     k2_avg = float(np.mean(t2)) - gap
@@ -332,25 +348,28 @@ def conv_main(args, torch, sq, wl):
     xb = 2 if L.x_dtype == "f16" else 4
     yb = 2 if L.y_dtype == "f16" else 4
     img = L.batch * L.H * L.W * L.C
-    # K1: the image once, the patch matrix's codes, scales and D out
-    k1_bytes = img * xb + M * K // 2 + M * 2 * (K // 64) + 4 * M * R + 2 * K * R + 4 * K
-    k2_bytes = (M + N) * K // 2 + (M + N) * 2 * (K // 64) + 4 * M * R + 2 * R * N + M * N * yb
+    meta = (K // 32) if mx else 2 * (K // 64)           # exponent or scale bytes per row
+    # K1: the image once, the patch matrix's codes, scales (or exponents) and D out
+    k1_bytes = img * xb + M * K // 2 + M * meta + 4 * M * R + 2 * K * R + 4 * K
+    k2_bytes = (M + N) * K // 2 + (M + N) * meta + 4 * M * R + 2 * R * N + M * N * yb
+    peak, unit, kname, dtype = ((FP4_PEAK_TFLOPS, "TFLOPS", "k2_mx_kernel", "fp4") if mx else
+                                (INT8_PEAK_TOPS, "TOPS", "k2_w4a4_kernel", "int8"))
+    fmt_txt = "MXFP4 (E2M1, E8M0 per 32)" if mx else "INT4 per-64 groups"
     out = {
-        "metric": "effective TOPS of an SVDQuant W4A4+rank-32 UNet convolution "
-                  "(implicit GEMM), % of INT8 MFMA peak",
-        "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "metric": (f"effective {unit} of an SVDQuant {'MXFP4' if mx else 'W4A4'}+rank-32 UNet "
+                   f"convolution (implicit GEMM), % of {'FP4' if mx else 'INT8'} MFMA peak"),
+        "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": f"{L.name}: X {L.x_dtype} NHWC {L.batch}x{L.H}x{L.W}x{L.C}, "
                                f"{L.KH}x{L.KW} stride {L.stride} pad {L.pad} -> {N} channels "
-                               f"(patch matrix {M}x{K}), rank {R}, INT4 per-64 groups, "
-                               f"Y {L.y_dtype}",
-                   "M": M, "K": K, "N": N, "rank": R, "format": "int4",
+                               f"(patch matrix {M}x{K}), rank {R}, {fmt_txt}, Y {L.y_dtype}",
+                   "M": M, "K": K, "N": N, "rank": R, "format": args.format,
                    "buffer_sets": args.sets},
-        "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
-        "roofline": {"bound": "mfma", "kernel": "k2_w4a4_kernel",
-                     "achieved": round(ops / k2_avg / 1e12, 2), "peak": INT8_PEAK_TOPS,
-                     "unit": "TOPS", "frac": round(ops / k2_avg / 1e12 / INT8_PEAK_TOPS, 4),
+        ("pct_fp4_peak" if mx else "pct_int8_peak"): round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "kernel": kname,
+                     "achieved": round(ops / k2_avg / 1e12, 2), "peak": peak,
+                     "unit": unit, "frac": round(ops / k2_avg / 1e12 / peak, 4),
                      "traffic": None, "algorithmic_bytes": k2_bytes,
                      "avg_ms": round(k2_avg * 1e3, 4),
                      "timing": "HIP events around each launch inside the timed steps, on the "

@@ -6,21 +6,22 @@ without a built library raises ImportError.
 """
 from . import _lib  # noqa: F401  (fails loudly when libsvdq.so is missing)
 from .api import (Conv2d, Linear, Prepared, channel_absmax, concat_lora,  # noqa: F401
-                  conv2d, conv_out_size, conv_patch_absmax, debug_group_partials,
+                  conv2d, conv2d_mx, conv_out_size, conv_patch_absmax, debug_group_partials,
                   gelu_tanh_f16, linear, linear_mx, linear_mx_workspace_bytes,
                   linear_workspace_bytes, mx_codes_tiled_bytes, mx_exps_tiled_bytes,
                   mx_gemm_lowrank_up, pack_lowrank_down, pack_mx_tiles, prepare_weights,
                   prepare_weights_mx, prepare_weights_w4a16, pack_w4a16_tiles,
                   quantize_act_lowrank_down, quantize_act_lowrank_down_conv,
+                  quantize_act_lowrank_down_conv_mx,
                   quantize_act_lowrank_down_mx, smoothing_factors, w4a4_gemm_lowrank_up,
                   w4a16_gemm, w4a16_tile_activation, w4a16_x_tiled_bytes, linear_w4a16)
 
-__all__ = ["Conv2d", "Linear", "Prepared", "channel_absmax", "concat_lora", "conv2d",
+__all__ = ["Conv2d", "Linear", "Prepared", "channel_absmax", "concat_lora", "conv2d", "conv2d_mx",
            "conv_out_size", "conv_patch_absmax", "debug_group_partials",
            "gelu_tanh_f16", "linear", "linear_mx", "linear_mx_workspace_bytes",
            "linear_workspace_bytes", "mx_codes_tiled_bytes", "mx_exps_tiled_bytes",
            "mx_gemm_lowrank_up", "pack_lowrank_down", "pack_mx_tiles", "prepare_weights",
            "prepare_weights_mx", "quantize_act_lowrank_down", "quantize_act_lowrank_down_conv",
-           "quantize_act_lowrank_down_mx", "smoothing_factors", "w4a4_gemm_lowrank_up",
+           "quantize_act_lowrank_down_conv_mx", "quantize_act_lowrank_down_mx", "smoothing_factors", "w4a4_gemm_lowrank_up",
            "prepare_weights_w4a16", "pack_w4a16_tiles", "w4a16_gemm", "w4a16_tile_activation",
            "w4a16_x_tiled_bytes", "linear_w4a16"]

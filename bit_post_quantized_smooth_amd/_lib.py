@@ -83,6 +83,10 @@ _SIGS = {
                                                    _i32, _i32, _p, _p, _i32, _p, _p, _p, _p]),
     "svdq_conv2d": (_int, [_p, _int, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _p, _p, _p,
                            _i32, _p, _p, _p, _p, _int, _i64, _p, C.c_size_t, _i32, _p]),
+    "svdq_quantize_act_lowrank_down_conv_mx": (_int, [_p, _int, _i64, _i64, _i64, _i64, _i32, _i32,
+                                                      _i32, _i32, _p, _p, _i32, _p, _p, _p, _p]),
+    "svdq_conv2d_mx": (_int, [_p, _int, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _p, _p,
+                              _p, _i32, _p, _p, _p, _p, _int, _i64, _p, C.c_size_t, _i32, _p]),
     "svdq_debug_group_partials": (_int, [_p, _p, _i64, _i64, _i64, _i32, _i64, _i64, _p, _p]),
     "svdq_gelu_tanh_f16": (_int, [_p, _p, _i64, _p]),
 }

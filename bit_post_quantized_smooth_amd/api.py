@@ -366,6 +366,28 @@ def conv2d(X, KH: int, KW: int, stride: int, pad: int, inv_smooth, L1p, L2t, R: 
           "svdq_conv2d")
 
 
+def quantize_act_lowrank_down_conv_mx(X, KH: int, KW: int, stride: int, pad: int, inv_smooth,
+                                      L1p, R: int, a_codes_t, a_exps_t, D, stream=None):
+    """K1-MX on the patch matrix of the NHWC image X: tiled codes and exponents, D."""
+    B, H, W, Cc = X.shape
+    check(lib.svdq_quantize_act_lowrank_down_conv_mx(
+        _tp(X), _dt(X), B, H, W, Cc, KH, KW, stride, pad, _tp(inv_smooth),
+        _tp(L1p) if R else None, R, _tp(a_codes_t), _tp(a_exps_t), _tp(D) if R else None,
+        _stream(stream)), "svdq_quantize_act_lowrank_down_conv_mx")
+
+
+def conv2d_mx(X, KH: int, KW: int, stride: int, pad: int, inv_smooth, L1p, L2t, R: int,
+              w_codes_t, w_exps_t, bias, Y, ws, stream=None, activation=None):
+    """The whole convolution in MXFP4 (tiled weights): Y (batch x OH x OW x N) from X."""
+    B, H, W, Cc = X.shape
+    N = Y.shape[-1]
+    check(lib.svdq_conv2d_mx(_tp(X), _dt(X), B, H, W, Cc, KH, KW, stride, pad, _tp(inv_smooth),
+                             _tp(L1p) if R else None, _tp(L2t) if R else None, R, _tp(w_codes_t),
+                             _tp(w_exps_t), _tp(bias), _tp(Y), _dt(Y), N, _tp(ws),
+                             ws.numel() * ws.element_size(), _act(activation), _stream(stream)),
+          "svdq_conv2d_mx")
+
+
 def debug_group_partials(a_codes, w_codes, M: int, N: int, K: int, row0: int, rows: int, P,
                          stream=None):
     check(lib.svdq_debug_group_partials(_tp(a_codes), _tp(w_codes), M, N, K, GROUP, row0, rows,
@@ -442,7 +464,7 @@ class Linear:
 class Conv2d:
     """One prepared SVDQuant convolution resident on a device.
 
-    ``prep`` is the INT4 prep of the K x N weight matrix whose row
+    ``prep`` is the INT4 or MXFP4 prep of the K x N weight matrix whose row
     (kh*KW + kw)*C + c is filter tap (kh, kw, c) (a KH x KW x C x N filter
     reshaped). ``Conv2d(prep, KH, KW, stride, pad, bias)(X)`` maps an NHWC
     image to the NHWC output (batch x OH x OW x N)."""
@@ -450,8 +472,8 @@ class Conv2d:
     def __init__(self, prep: Prepared, KH: int, KW: int, stride: int = 1, pad: int = 0,
                  bias: Optional[np.ndarray] = None, device="cuda", out_dtype=None,
                  activation=None):
-        if prep.fmt != "int4":
-            raise ValueError("convolutions run in the INT4 format only")
+        if prep.fmt not in ("int4", "mxfp4"):
+            raise ValueError("convolutions run in the INT4 and MXFP4 formats")
         if prep.K % (KH * KW) != 0:
             raise ValueError(f"K={prep.K} is not KH*KW*C for a {KH}x{KW} kernel")
         self.lin = Linear(prep, bias, device, out_dtype, activation)
@@ -470,6 +492,7 @@ class Conv2d:
             Y = torch.empty((B, OH, OW, lin.N), dtype=lin.out_dtype or X.dtype,
                             device=lin.device)
         ws = lin.workspace(max(B * OH * OW, 1))
-        conv2d(X, self.KH, self.KW, self.stride, self.pad, lin.inv_smooth, lin.L1p, lin.L2t,
-               lin.R, lin.w_codes, lin.w_scales, lin.bias, Y, ws, stream, lin.activation)
+        run = conv2d_mx if lin.fmt == "mxfp4" else conv2d
+        run(X, self.KH, self.KW, self.stride, self.pad, lin.inv_smooth, lin.L1p, lin.L2t, lin.R,
+            lin.w_codes, lin.w_scales, lin.bias, Y, ws, stream, lin.activation)
         return Y

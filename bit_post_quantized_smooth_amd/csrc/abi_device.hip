@@ -385,6 +385,71 @@ int svdq_conv2d(const void* X, int x_dtype, int64_t batch, int64_t H, int64_t W,
                    "svdq_conv2d K2 launch");
 }
 
+int svdq_quantize_act_lowrank_down_conv_mx(const void* X, int x_dtype, int64_t batch, int64_t H,
+                                           int64_t W, int64_t C, int32_t KH, int32_t KW,
+                                           int32_t stride, int32_t pad, const float* inv_smooth,
+                                           const uint16_t* L1p, int32_t R, uint8_t* a_codes_t,
+                                           uint8_t* a_exps_t, float* D, hipStream_t stream) {
+  clear_error();
+  const char* fn = "svdq_quantize_act_lowrank_down_conv_mx";
+  ConvShape cs;
+  if (int s = check_conv(batch, H, W, C, KH, KW, stride, pad, cs, fn)) return s;
+  if (int s = validate_k1(X, x_dtype, cs.M, cs.K, cs.K, inv_smooth, L1p, R, SVDQ_GROUP, a_codes_t,
+                          a_exps_t, D, fn))
+    return s;
+  if (int s = device_ready()) return s;
+  const ConvGeom g = conv_geom(cs);
+  return check_hip(launch_k1(X, x_dtype == SVDQ_F16, cs.M, cs.K, cs.K, inv_smooth, L1p, R,
+                             a_codes_t, a_exps_t, true, D, stream, &g),
+                   "svdq_quantize_act_lowrank_down_conv_mx launch");
+}
+
+int svdq_conv2d_mx(const void* X, int x_dtype, int64_t batch, int64_t H, int64_t W, int64_t C,
+                   int32_t KH, int32_t KW, int32_t stride, int32_t pad, const float* inv_smooth,
+                   const uint16_t* L1p, const uint16_t* L2t, int32_t R, const uint8_t* w_codes_t,
+                   const uint8_t* w_exps_t, const float* bias, void* Y, int y_dtype, int64_t N,
+                   void* ws, size_t ws_bytes, int32_t activation, hipStream_t stream) {
+  clear_error();
+  const char* fn = "svdq_conv2d_mx";
+  if (int s = check_activation(activation, fn)) return s;
+  if (!ws) {
+    set_error("%s: null workspace", fn);
+    return SVDQ_ERR_NULL;
+  }
+  ConvShape cs;
+  if (int s = check_conv(batch, H, W, C, KH, KW, stride, pad, cs, fn)) return s;
+  if (int s = check_common(cs.M, cs.K, R, SVDQ_GROUP, fn)) return s;
+  const WsLayout L = ws_layout(cs.M, cs.K, R, true);
+  if (ws_bytes < L.total) {
+    set_error("%s: workspace %zu bytes < %zu needed", fn, ws_bytes, L.total);
+    return SVDQ_ERR_WORKSPACE;
+  }
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) {
+    set_error("%s: workspace must be 256-byte aligned", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* a_codes = base + L.codes;
+  uint8_t* a_exps = base + L.scales;
+  float* D = R > 0 ? reinterpret_cast<float*>(base + L.d) : nullptr;
+  if (int s = validate_k1(X, x_dtype, cs.M, cs.K, cs.K, inv_smooth, L1p, R, SVDQ_GROUP, a_codes,
+                          a_exps, D, fn))
+    return s;
+  if (int s = validate_k2(a_codes, a_exps, w_codes_t, w_exps_t, D, L2t, R, bias, Y, y_dtype, cs.M,
+                          N, cs.K, N, SVDQ_GROUP, fn))
+    return s;
+  if (int s = device_ready()) return s;
+  const ConvGeom g = conv_geom(cs);
+  if (int s = check_hip(launch_k1(X, x_dtype == SVDQ_F16, cs.M, cs.K, cs.K, inv_smooth, L1p, R,
+                                  a_codes, a_exps, true, D, stream, &g),
+                        "svdq_conv2d_mx K1 launch"))
+    return s;
+  return check_hip(launch_k2_mx(a_codes, a_exps, w_codes_t, w_exps_t, D, L2t, R, bias, Y,
+                                y_dtype == SVDQ_F16, cs.M, N, cs.K, N,
+                                activation == SVDQ_ACT_GELU_TANH, stream),
+                   "svdq_conv2d_mx K2 launch");
+}
+
 size_t svdq_w4a16_x_tiled_bytes(int64_t M, int64_t K) {
   if (M < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) return 0;
   return static_cast<size_t>((M + 15) / 16) * static_cast<size_t>(K / 32) * 1024;

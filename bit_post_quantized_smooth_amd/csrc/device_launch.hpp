@@ -17,7 +17,7 @@ struct ConvGeom {
 
 // a_meta: fp16 group scales (mx = false) or E8M0 block exponents (mx = true).
 // conv: null for a linear layer; else X is the NHWC image and M, K are the
-// patch matrix's (INT4 only).
+// patch matrix's.
 hipError_t launch_k1(const void* X, bool x_f16, int64_t M, int64_t K, int64_t ldx,
                      const float* inv_smooth, const uint16_t* L1p, int R, uint8_t* a_codes,
                      void* a_meta, bool mx, float* D, hipStream_t stream,

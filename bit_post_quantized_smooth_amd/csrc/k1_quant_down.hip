@@ -449,7 +449,10 @@ hipError_t launch_k1_t(const void* X, int64_t M, int64_t K, int64_t ldx,
   const dim3 block(64 * k1_waves<NCB>()), grid(static_cast<unsigned>((M + 15) / 16));
   const XT* x = static_cast<const XT*>(X);
   const ConvGeom cg = conv ? *conv : ConvGeom{};
-  if (conv)
+  if (conv && mx)
+    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, true, true>), grid, block, 0, stream,
+                       x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
+  else if (conv)
     hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, false, true>), grid, block, 0, stream,
                        x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
   else if (mx)

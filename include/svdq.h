@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 5
+#define SVDQ_ABI_VERSION 6
 
 /* status codes */
 enum {
@@ -376,7 +376,9 @@ int svdq_linear_w4a16(const void* X, int x_dtype, int64_t ldx, const uint8_t* w_
  *          KH x KW x C x N (HWIO) filter reshaped; svdq_prepare_weights on Wm;
  *   Y      M x N row-major = the NHWC output batch x OH x OW x N.
  * Limits: KH, KW, stride in [1, 64], pad in [0, 64], KH <= H + 2 pad (and W),
- * batch*H*W*C and M below 2^31, K at most 2^25. INT4 format only.
+ * batch*H*W*C and M below 2^31, K at most 2^25. Both formats: the INT4
+ * entry points below, and their MXFP4 counterparts (the tiled layouts of the
+ * MXFP4 section, prep by svdq_prepare_weights_mx on Wm).
  */
 
 /* Host: out[k] (k < K) = max over the M patches of |patch matrix entry k|,
@@ -402,6 +404,24 @@ int svdq_conv2d(const void* X, int x_dtype, int64_t batch, int64_t H, int64_t W,
                 const uint16_t* L1p, const uint16_t* L2t, int32_t R, const uint8_t* w_codes,
                 const uint16_t* w_scales, const float* bias, void* Y, int y_dtype, int64_t N,
                 void* ws, size_t ws_bytes, int32_t activation, hipStream_t stream);
+
+/* Device: K1-MX on the patch matrix: the tiled E2M1 codes and E8M0 exponents
+ * and D, as svdq_quantize_act_lowrank_down_mx would give for the patch matrix
+ * in memory (bit-exact). */
+int svdq_quantize_act_lowrank_down_conv_mx(const void* X, int x_dtype, int64_t batch, int64_t H,
+                                           int64_t W, int64_t C, int32_t KH, int32_t KW,
+                                           int32_t stride, int32_t pad, const float* inv_smooth,
+                                           const uint16_t* L1p, int32_t R, uint8_t* a_codes_t,
+                                           uint8_t* a_exps_t, float* D, hipStream_t stream);
+
+/* Device: the whole convolution in MXFP4: K1-MX on the patch matrix into
+ * `ws`, then K2-MX into Y (ldy = N). ws: 256-byte aligned, at least
+ * svdq_linear_mx_workspace_bytes(M, K, R) bytes. */
+int svdq_conv2d_mx(const void* X, int x_dtype, int64_t batch, int64_t H, int64_t W, int64_t C,
+                   int32_t KH, int32_t KW, int32_t stride, int32_t pad, const float* inv_smooth,
+                   const uint16_t* L1p, const uint16_t* L2t, int32_t R, const uint8_t* w_codes_t,
+                   const uint8_t* w_exps_t, const float* bias, void* Y, int y_dtype, int64_t N,
+                   void* ws, size_t ws_bytes, int32_t activation, hipStream_t stream);
 
 /* Test hook: the exact integer partials P[m, n, g] for rows row0 .. row0+rows-1,
  * computed with the same operand unpacking and int8 matrix-core instruction

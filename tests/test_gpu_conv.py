@@ -6,7 +6,9 @@ patch matrix, and codes, scales, D and Y against the linear entry points run
 on the same patch matrix materialised in device memory (the two must agree to
 the bit: the same values reach the same arithmetic). Within 2e-3 * max|Y| and
 the strict element-wise bound: Y against the oracle, on every element for the
-small cases and on sampled output pixels at the UNet sizes."""
+small cases and on sampled output pixels at the UNet sizes. The MXFP4
+convolution (K1-MX on the patches, K2-MX) is held to the same bar against the
+oracle's MXFP4 functions."""
 import numpy as np
 import pytest
 
@@ -202,3 +204,115 @@ def test_conv_workspace_reuse_smaller_image():
     wc, ws = O.quantize_residual_from_factors(O.conv_weight_matrix(Wc), lam, p.L1, p.L2)
     Yo = O.linear(Xcol, inv, p.L1, p.L2, wc, ws, b, "f16")
     assert rel_err(Ys.cpu().numpy().reshape(small.M, 64), Yo) <= TOL_Y
+
+
+# ---------------------------------------------------------------------------
+# the MXFP4 convolution: K1-MX on the implicit patch matrix, then K2-MX
+
+import mx_tiles as T  # noqa: E402
+from test_gpu_mx import _assert_strict, _exact_rows  # noqa: E402
+
+
+def _setup_mx(L: wl.ConvLayer, X, Wc):
+    import bit_post_quantized_smooth_amd as sq
+    Wm = O.conv_weight_matrix(Wc)
+    lam = sq.smoothing_factors(sq.conv_patch_absmax(X, L.KH, L.KW, L.stride, L.pad), Wm)
+    p = sq.prepare_weights_mx(Wm, lam, L.rank)
+    Xcol = O.im2col_nhwc(X, L.KH, L.KW, L.stride, L.pad)
+    lam_o = O.smoothing_factors(O.channel_absmax(Xcol), Wm)
+    inv = O.inv_smoothing(lam_o)
+    wc, we = O.mx_quantize_residual_from_factors(Wm, lam_o, p.L1, p.L2)
+    assert np.array_equal(inv, p.inv_smooth)
+    assert np.array_equal(wc, p.w_codes) and np.array_equal(we, p.w_scales)
+    return p, Xcol, inv, wc, we
+
+
+def _run_mx(L: wl.ConvLayer, X, p, bias):
+    """K1-MX on the patches (tiled outputs read back as canonical codes and
+    exponents), and the whole MXFP4 convolution."""
+    import bit_post_quantized_smooth_amd as sq
+    torch = torch_mod()
+    M, K, R = L.M, L.K, p.rank
+    Xd = dev(X)
+    ct = torch.full((sq.mx_codes_tiled_bytes(M, K),), 0x5A, dtype=torch.uint8, device="cuda")
+    et = torch.full((sq.mx_exps_tiled_bytes(M, K),), 0x5A, dtype=torch.uint8, device="cuda")
+    D = torch.empty((M, max(R, 1)), dtype=torch.float32, device="cuda")
+    sq.quantize_act_lowrank_down_conv_mx(Xd, L.KH, L.KW, L.stride, L.pad, dev(p.inv_smooth),
+                                         dev(p.L1p) if R else None, R, ct, et, D if R else None)
+    conv = sq.Conv2d(p, L.KH, L.KW, L.stride, L.pad, bias,
+                     out_dtype=torch.float16 if L.y_dtype == "f16" else torch.float32)
+    Y = conv(Xd)
+    torch.cuda.synchronize()
+    c = T.untile_codes(ct.cpu().numpy(), M, K)
+    e = T.untile_exps(et.cpu().numpy(), M, K)
+    if K % 128:
+        assert not c[:M, K // 2:].any() and np.all(e[:M, K // 32:] == 127)
+    return c[:M, :K // 2], e[:M, :K // 32], D, Y, (ct, et)
+
+
+def _check_mx_against_linear(L, Xcol, p, bias, tiles, D, Y):
+    """K1-MX and the MXFP4 linear layer on the materialised patch matrix give the same bits."""
+    import bit_post_quantized_smooth_amd as sq
+    torch = torch_mod()
+    M, K, R = L.M, L.K, p.rank
+    Xd = dev(Xcol)
+    ct = torch.full((sq.mx_codes_tiled_bytes(M, K),), 0x5A, dtype=torch.uint8, device="cuda")
+    et = torch.full((sq.mx_exps_tiled_bytes(M, K),), 0x5A, dtype=torch.uint8, device="cuda")
+    D2 = torch.empty((M, max(R, 1)), dtype=torch.float32, device="cuda")
+    sq.quantize_act_lowrank_down_mx(Xd, dev(p.inv_smooth), dev(p.L1p) if R else None, R, ct, et,
+                                    D2 if R else None)
+    lin = sq.Linear(p, bias, out_dtype=torch.float16 if L.y_dtype == "f16" else torch.float32)
+    Y2 = lin(Xd)
+    torch.cuda.synchronize()
+    assert torch.equal(ct, tiles[0]) and torch.equal(et, tiles[1])
+    if R:
+        assert torch.equal(D[:, :R], D2[:, :R])
+    assert torch.equal(Y.reshape(M, p.N).view(torch.uint8), Y2.view(torch.uint8))
+
+
+MX_EDGE = [EDGE[0], EDGE[1], EDGE[3], EDGE[4], EDGE[5], EDGE[6]]
+
+
+@pytest.mark.parametrize("L", MX_EDGE, ids=lambda L: "mx_" + L.name.replace(" ", "_"))
+def test_conv_mx_edge_every_element(L):
+    X, Wc, b = _edge_inputs(L, seed=L.H * 131 + L.W * 7 + L.C + L.KH + L.stride + 1)
+    p, Xcol, inv, wc, we = _setup_mx(L, X, Wc)
+    c, e, D, Y, tiles = _run_mx(L, X, p, b)
+    oc, oe, xh = O.mx_quantize_activation(Xcol, inv)
+    assert np.array_equal(c, oc)
+    assert np.array_equal(e, oe)
+    if p.rank:
+        Dg = D.cpu().numpy()[:, :p.rank].astype(np.float64)
+        Do = O.down_projection(xh, p.L1)
+        assert float(np.max(np.abs(Dg - Do) / (d_stat_bound(xh, p.L1, L.K) + 1e-30))) <= 1.0
+    Yg = Y.cpu().numpy().reshape(L.M, L.N)
+    Yo = O.mx_linear(Xcol, inv, p.L1, p.L2, wc, we, b, L.y_dtype)
+    assert rel_err(Yg, Yo) <= TOL_Y
+    Ye, env, jump = _exact_rows(Xcol, inv, p, wc, we, b, np.arange(L.M))
+    _assert_strict(Yg, Ye, env, jump, L.y_dtype, L.K, p.rank)
+    _check_mx_against_linear(L, Xcol, p, b, tiles, D, Y)
+
+
+@pytest.mark.parametrize("idx", [1, 3], ids=lambda i: "mx_" + wl.CONV_LAYERS[i].name.replace(" ", "_"))
+def test_conv_mx_unet_sizes(idx):
+    L, X, Wc = wl.conv_inputs(idx)
+    b = wl.bias(wl.CONV_CFG, idx, L.N)
+    p, Xcol, inv, wc, we = _setup_mx(L, X, Wc)
+    c, e, D, Y, tiles = _run_mx(L, X, p, b)
+    rows = sample_rows(L.M, seed=idx + 50)
+    border = [0, L.OW - 1, (L.OH - 1) * L.OW, L.OH * L.OW - 1, L.OH * L.OW, L.M - 1]
+    rows = np.unique(np.concatenate([rows, border]))
+    oc, oe, xh = O.mx_quantize_activation(Xcol[rows], inv)
+    assert np.array_equal(c[rows], oc)
+    assert np.array_equal(e[rows], oe)
+    Dg = D.cpu().numpy()[rows, :p.rank].astype(np.float64)
+    Do = O.down_projection(xh, p.L1)
+    assert float(np.max(np.abs(Dg - Do) / (d_stat_bound(xh, p.L1, L.K) + 1e-30))) <= 1.0
+    Yg = Y.cpu().numpy().reshape(L.M, L.N)
+    Yo = np.concatenate([O.mx_linear(Xcol[rows[i:i + 16]], inv, p.L1, p.L2, wc, we, b, L.y_dtype)
+                         for i in range(0, len(rows), 16)])
+    assert rel_err(Yg[rows], Yo) <= TOL_Y
+    Ye, env, jump = _exact_rows(Xcol, inv, p, wc, we, b, rows)
+    _assert_strict(Yg[rows], Ye, env, jump, L.y_dtype, L.K, p.rank)
+    assert np.all(np.isfinite(Yg))
+    _check_mx_against_linear(L, Xcol, p, b, tiles, D, Y)

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert _lib.abi_version() == 5
+    assert _lib.abi_version() == 6
     for s in range(12):
         assert _lib.status_str(s) and _lib.status_str(s) != "unknown status"
     assert _lib.status_str(99) == "unknown status"
@@ -440,6 +440,18 @@ def test_device_entry_points_reject_bad_arguments():
     assert L.svdq_conv2d(*ca) == _lib.ERR_ALIGN
     ca[20] = None
     assert L.svdq_conv2d(*ca) == _lib.ERR_NULL
+    # the MXFP4 convolution: same geometry checks, the MXFP4 workspace
+    assert L.svdq_quantize_act_lowrank_down_conv_mx(A16, 1, 1, 8, 8, 96, 3, 3, 1, 1, A16, A16, 16, A16, A16, A16, None) == _lib.ERR_SHAPE
+    assert L.svdq_quantize_act_lowrank_down_conv_mx(A16, 1, *geo, A16, A16, 16, A16, MIS, A16, None) == _lib.ERR_ALIGN
+    need_cm = L.svdq_linear_mx_workspace_bytes(64, 576, 16)
+    cm = [A16, 1, *geo, A16, A16, A16, 16, A16, A16, None, A16, 1, 16, A16, need_cm - 1, 0, None]
+    assert L.svdq_conv2d_mx(*cm) == _lib.ERR_WORKSPACE
+    cm[21] = need_cm
+    cm[22] = 5
+    assert L.svdq_conv2d_mx(*cm) == _lib.ERR_ACT
+    cm[2] = 0
+    cm[22] = 0
+    assert L.svdq_conv2d_mx(*cm) == _lib.ERR_SHAPE
     # partials hook: slice outside the rows
     assert L.svdq_debug_group_partials(A16, A16, 16, 16, 64, 64, 10, 7, A16, None) == _lib.ERR_SHAPE
     assert L.svdq_gelu_tanh_f16(A16, MIS, 8, None) == _lib.ERR_ALIGN
@@ -469,3 +481,7 @@ def test_device_entry_points_report_no_device():
     need_c = L.svdq_linear_workspace_bytes(64, 576, 16, 64)
     assert L.svdq_conv2d(A16, 1, *geo, A16, A16, A16, 16, A16, A16, None, A16, 1, 16, 0x10000,
                          need_c, 0, None) == _lib.ERR_NO_DEVICE
+    assert L.svdq_quantize_act_lowrank_down_conv_mx(A16, 1, *geo, A16, A16, 16, A16, A16, A16, None) == _lib.ERR_NO_DEVICE
+    need_cm = L.svdq_linear_mx_workspace_bytes(64, 576, 16)
+    assert L.svdq_conv2d_mx(A16, 1, *geo, A16, A16, A16, 16, A16, A16, None, A16, 1, 16, 0x10000,
+                            need_cm, 0, None) == _lib.ERR_NO_DEVICE
