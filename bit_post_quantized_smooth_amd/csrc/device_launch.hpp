@@ -15,6 +15,9 @@ struct ConvGeom {
   int32_t H, W, C, KH, KW, stride, pad, OH, OW;
 };
 
+// Resident workgroup slots of the current device (2 per compute unit).
+int resident_slots();
+
 // a_meta: fp16 group scales (mx = false) or E8M0 block exponents (mx = true).
 // conv: null for a linear layer; else X is the NHWC image and M, K are the
 // patch matrix's.

@@ -212,18 +212,23 @@ constexpr int ring_l1_blocks() { return NCB <= 8 ? NCB : 0; }
 template <int NCB>
 constexpr int k1_waves() { return NCB <= 4 ? 8 : 4; }
 
-// Everything one lane reads for one group: its 16 X values, the 16 matching
-// smoothing factors and, per column block of D, its two packed L1 operands.
-template <typename XT, int NCB>
+// Everything one lane reads for one group: its 16 X values in each of the
+// workgroup's RT row tiles, the 16 matching smoothing factors and, per column
+// block of D, its two packed L1 operands (both shared by the row tiles).
+template <typename XT, int NCB, int RT>
 struct GroupIn {
-  Raw<XT> x;
-  bool valid;            // convolution: the tap lies inside the image (else the values are 0)
+  Raw<XT> x[RT];
+  bool valid[RT];        // convolution: the tap lies inside the image (else the values are 0)
   float4 inv[4];
   v8h l1[ring_l1_blocks<NCB>() > 0 ? ring_l1_blocks<NCB>() : 1][2];
 };
 
 // a_codes, a_meta: INT4 codes (M x K/2) and fp16 group scales (M x K/64), or
 // for MX the tiled E2M1 codes and E8M0 exponents (see svdq.h).
+// RT: row tiles of 16 per workgroup. With RT = 2 every wave quantizes the same
+// group of two row tiles with one set of smoothing factors and L1 operands,
+// which halves their (cached) traffic per row; used when there are rows
+// enough to keep every compute unit busy.
 // CONV: X is an NHWC image and the rows are the patches of the convolution cg
 // (the chattools.cn overview says the method applies to UNet backbones; the
 // convolution is the linear layer on its patch matrix): row p is the output
@@ -231,7 +236,7 @@ struct GroupIn {
 // g = (kh*KW + kw)*C/64 + cb. A lane reads its 16 channels at input pixel
 // (oh*stride + kh - pad, ow*stride + kw - pad) or, outside the image, loads a
 // clamped pixel and uses zeros, so every load stays unconditional.
-template <typename XT, int NCB, int NB, bool MX, bool CONV>
+template <typename XT, int NCB, int NB, bool MX, bool CONV, int RT>
 __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
     const XT* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
     const float* __restrict__ inv_smooth, const uint16_t* __restrict__ L1p, int R,
@@ -240,40 +245,60 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
 #pragma clang fp contract(off)
   constexpr int WAVES = k1_waves<NCB>();
   constexpr int NCBA = NCB > 0 ? NCB : 1;
-  __shared__ float dpart[WAVES][16][NCBA * 16];
+  __shared__ float dpart[WAVES][16 * RT][NCBA * 16];
   const int lane = threadIdx.x & 63;
   // the wave index is the same in all lanes: keep it (and everything derived
   // from it: group numbers, group offsets) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  // lane map: row qr = rl of the tile, channels 16*c4 .. +15 of each group
+  // lane map: row qr = rl of each row tile, channels 16*c4 .. +15 of each group
   const int rl = lane & 15, q = lane >> 4;
   const int qr = rl, c4 = q;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * 16;
-  const int nrows = M - row0 < 16 ? static_cast<int>(M - row0) : 16;
-  const bool rvalid = qr < nrows;
-  const uint32_t lq = rvalid ? qr : nrows - 1;      // clamped row of the tile for loads
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * (16 * RT);
   const int G = static_cast<int>(K / kGroup);
   const int ncb = R / 16;                            // real column blocks (<= NCB)
   // this wave's groups are wave, wave+WAVES, ...: n_mine of them
   const int n_mine = (G > wave) ? (G - wave + WAVES - 1) / WAVES : 0;
+  const int64_t nchunks = (K + 127) / 128;
 
-  // Addresses: a base shared by the workgroup plus a 32-bit per-lane offset
-  // (the host bounds 16 rows of X and of the codes below 2^31 bytes)
-  const XT* xblk = X + row0 * ldx;
-  const uint32_t xoff = lq * static_cast<uint32_t>(ldx) + c4 * 16;
+  // Per row tile: this lane's row (clamped to the last row for loads: rows
+  // past M are computed and never stored, so every load is unconditional),
+  // its X row, and where its codes and scales (or tiled codes and exponents) go
+  const XT* xrow[RT];
+  bool rvalid[RT];
+  uint8_t* crow[RT];
+  uint16_t* srow[RT];
+  uint8_t* tcode[RT];
+  uint8_t* texp[RT];
+  int pix0[RT], ih0[RT], iw0[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int64_t r0 = row0 + 16 * rt;
+    const int64_t row = r0 + qr;
+    rvalid[rt] = row < M;
+    const int64_t rowc = rvalid[rt] ? row : M - 1;
+    xrow[rt] = X + rowc * ldx + c4 * 16;
+    crow[rt] = a_codes + row * (K / 2) + c4 * 8;
+    srow[rt] = static_cast<uint16_t*>(a_meta) + row * G;
+    // MXFP4: the tile's 1 KB code block per chunk of 128, and its 64-row
+    // group's exponent blocks, in which its rows are byte (r0 % 64) / 16 of
+    // each lane's dword
+    tcode[rt] = a_codes + (r0 / 16) * nchunks * 1024;
+    texp[rt] = static_cast<uint8_t*>(a_meta) + (r0 / 64) * nchunks * 256 + (r0 % 64) / 16;
+    pix0[rt] = ih0[rt] = iw0[rt] = 0;
+    if constexpr (CONV) {
+      // convolution: this lane's output pixel (its first input pixel and the
+      // pixel offset of its image)
+      const int p = static_cast<int>(rowc);
+      const int ohw = cg.OH * cg.OW;
+      const int img = p / ohw, rem = p - img * ohw;
+      const int oh = rem / cg.OW, ow = rem - oh * cg.OW;
+      pix0[rt] = img * cg.H * cg.W;
+      ih0[rt] = oh * cg.stride - cg.pad;
+      iw0[rt] = ow * cg.stride - cg.pad;
+    }
+  }
   const uint32_t ioff = c4 * 16;
   const v8h* l1b = reinterpret_cast<const v8h*>(L1p);
-  uint8_t* cblk = a_codes + row0 * (K / 2);
-  const uint32_t coff = qr * static_cast<uint32_t>(K / 2) + c4 * 8;
-  // per row: G fp16 scales, or 2G E8M0 bytes (two per group, stored as one uint16)
-  uint16_t* sblk = static_cast<uint16_t*>(a_meta) + row0 * G;
-  const uint32_t soff = qr * static_cast<uint32_t>(G);
-  // MXFP4: the tiled code blocks of this workgroup's row block (one 1 KB block
-  // per chunk of 128) and the exponent blocks of its 64-row group, in which
-  // its rows are the byte ti = (row0 % 64) / 16 of each lane's dword
-  const int64_t nchunks = (K + 127) / 128;
-  uint8_t* tcode = a_codes + static_cast<int64_t>(blockIdx.x) * nchunks * 1024;
-  uint8_t* texp = static_cast<uint8_t*>(a_meta) + (row0 / 64) * nchunks * 256 + (row0 % 64) / 16;
 
   // packed operand (g, c, h) of this lane
   auto l1_operand = [&](int g, int c, int h) -> const v8h* {
@@ -281,38 +306,28 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
     return l1b + static_cast<int64_t>((g * ncb + cc) * 2 + h) * 64 + lane;
   };
 
-  // convolution: this lane's output pixel (its first input pixel and the
-  // pixel offset of its image)
-  int pix0 = 0, ih0 = 0, iw0 = 0;
-  if constexpr (CONV) {
-    const int p = static_cast<int>(row0) + static_cast<int>(lq);
-    const int ohw = cg.OH * cg.OW;
-    const int img = p / ohw, rem = p - img * ohw;
-    const int oh = rem / cg.OW, ow = rem - oh * cg.OW;
-    pix0 = img * cg.H * cg.W;
-    ih0 = oh * cg.stride - cg.pad;
-    iw0 = ow * cg.stride - cg.pad;
-  }
-
-  auto load_group = [&](GroupIn<XT, NCB>& in, int i) {
+  auto load_group = [&](GroupIn<XT, NCB, RT>& in, int i) {
     int g = wave + WAVES * i;
     g = g < G ? g : G - 1;
     const int k0 = g * kGroup;
-    if constexpr (CONV) {
-      const int cbs = cg.C / kGroup;                  // channel groups per tap (uniform)
-      const int t = g / cbs, cb = g - t * cbs;
-      const int kh = t / cg.KW, kw = t - kh * cg.KW;
-      const int ih = ih0 + kh, iw = iw0 + kw;
-      in.valid = static_cast<unsigned>(ih) < static_cast<unsigned>(cg.H) &&
-                 static_cast<unsigned>(iw) < static_cast<unsigned>(cg.W);
-      const int ihc = ih < 0 ? 0 : (ih >= cg.H ? cg.H - 1 : ih);
-      const int iwc = iw < 0 ? 0 : (iw >= cg.W ? cg.W - 1 : iw);
-      const uint32_t off = static_cast<uint32_t>(pix0 + ihc * cg.W + iwc) *
-                               static_cast<uint32_t>(cg.C) + cb * kGroup + c4 * 16;
-      load_raw<XT>(in.x, X + off);
-    } else {
-      in.valid = true;
-      load_raw<XT>(in.x, xblk + k0 + xoff);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if constexpr (CONV) {
+        const int cbs = cg.C / kGroup;                  // channel groups per tap (uniform)
+        const int t = g / cbs, cb = g - t * cbs;
+        const int kh = t / cg.KW, kw = t - kh * cg.KW;
+        const int ih = ih0[rt] + kh, iw = iw0[rt] + kw;
+        in.valid[rt] = static_cast<unsigned>(ih) < static_cast<unsigned>(cg.H) &&
+                       static_cast<unsigned>(iw) < static_cast<unsigned>(cg.W);
+        const int ihc = ih < 0 ? 0 : (ih >= cg.H ? cg.H - 1 : ih);
+        const int iwc = iw < 0 ? 0 : (iw >= cg.W ? cg.W - 1 : iw);
+        const uint32_t off = static_cast<uint32_t>(pix0[rt] + ihc * cg.W + iwc) *
+                                 static_cast<uint32_t>(cg.C) + cb * kGroup + c4 * 16;
+        load_raw<XT>(in.x[rt], X + off);
+      } else {
+        in.valid[rt] = true;
+        load_raw<XT>(in.x[rt], xrow[rt] + k0);
+      }
     }
     const float4* ip = reinterpret_cast<const float4*>(inv_smooth + k0 + ioff);
 #pragma unroll
@@ -326,15 +341,17 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
     }
   };
 
-  v4f acc[NCBA];
+  v4f acc[RT][NCBA];
 #pragma unroll
-  for (int c = 0; c < NCBA; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int c = 0; c < NCBA; ++c) acc[rt][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // -0 in a register the compiler cannot see through (see smooth16)
   float nz;
   __asm__("v_mov_b32 %0, 0x80000000" : "=v"(nz));
 
-  GroupIn<XT, NCB> ring[NB];
+  GroupIn<XT, NCB, RT> ring[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) load_group(ring[b], b);
 
@@ -343,75 +360,78 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
     for (int b = 0; b < NB; ++b) {
       const int i = i0 + b;
       const int g = wave + WAVES * i;
-      uint32_t packed[2] = {0u, 0u};
-      uint32_t meta = 0u;                  // fp16 scale, or the E8M0 byte
-      if (i < n_mine) {
-        float xh[16];
-        smooth16(ring[b].x, ring[b].inv, xh, nz);
-        if constexpr (CONV) {
-          // a tap outside the image: the patch matrix holds zeros there
 #pragma unroll
-          for (int j = 0; j < 16; ++j) xh[j] = ring[b].valid ? xh[j] : 0.f;
-        }
-        if constexpr (MX) {
-          quantize_mx(xh, packed, meta);
-        } else {
-          uint16_t s16;
-          quantize_int4(xh, packed, s16);
-          meta = s16;
-        }
-        if constexpr (NCB > 0) {
-          // the lane's 16 values, rounded to fp16, are its two matrix
-          // operands. Xhat is rounded to fp32 first and then to fp16 (RNE).
-          // The conversion is written out: as plain code the backend folds
-          // the product and the conversion into one v_fma_mixlo_f16, which
-          // rounds only once and differs in rare double-rounding cases.
-          v2h hp[8];
+      for (int rt = 0; rt < RT; ++rt) {
+        uint32_t packed[2] = {0u, 0u};
+        uint32_t meta = 0u;                  // fp16 scale, or the E8M0 byte
+        if (i < n_mine) {
+          float xh[16];
+          smooth16(ring[b].x[rt], ring[b].inv, xh, nz);
+          if constexpr (CONV) {
+            // a tap outside the image: the patch matrix holds zeros there
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            uint32_t r;
-            __asm__("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(xh[2 * j]), "v"(xh[2 * j + 1]));
-            hp[j] = __builtin_bit_cast(v2h, r);
+            for (int j = 0; j < 16; ++j) xh[j] = ring[b].valid[rt] ? xh[j] : 0.f;
           }
-          const v8h x0 = {hp[0][0], hp[0][1], hp[1][0], hp[1][1], hp[2][0], hp[2][1], hp[3][0], hp[3][1]};
-          const v8h x1 = {hp[4][0], hp[4][1], hp[5][0], hp[5][1], hp[6][0], hp[6][1], hp[7][0], hp[7][1]};
-          if constexpr (ring_l1_blocks<NCB>() > 0) {
+          if constexpr (MX) {
+            quantize_mx(xh, packed, meta);
+          } else {
+            uint16_t s16;
+            quantize_int4(xh, packed, s16);
+            meta = s16;
+          }
+          if constexpr (NCB > 0) {
+            // the lane's 16 values, rounded to fp16, are its two matrix
+            // operands. Xhat is rounded to fp32 first and then to fp16 (RNE).
+            // The conversion is written out: as plain code the backend folds
+            // the product and the conversion into one v_fma_mixlo_f16, which
+            // rounds only once and differs in rare double-rounding cases.
+            v2h hp[8];
 #pragma unroll
-            for (int c = 0; c < NCB; ++c) {
-              acc[c] = mfma_f16_16x16x32(x0, ring[b].l1[c][0], acc[c]);
-              acc[c] = mfma_f16_16x16x32(x1, ring[b].l1[c][1], acc[c]);
+            for (int j = 0; j < 8; ++j) {
+              uint32_t r;
+              __asm__("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(xh[2 * j]), "v"(xh[2 * j + 1]));
+              hp[j] = __builtin_bit_cast(v2h, r);
+            }
+            const v8h x0 = {hp[0][0], hp[0][1], hp[1][0], hp[1][1], hp[2][0], hp[2][1], hp[3][0], hp[3][1]};
+            const v8h x1 = {hp[4][0], hp[4][1], hp[5][0], hp[5][1], hp[6][0], hp[6][1], hp[7][0], hp[7][1]};
+            if constexpr (ring_l1_blocks<NCB>() > 0) {
+#pragma unroll
+              for (int c = 0; c < NCB; ++c) {
+                acc[rt][c] = mfma_f16_16x16x32(x0, ring[b].l1[c][0], acc[rt][c]);
+                acc[rt][c] = mfma_f16_16x16x32(x1, ring[b].l1[c][1], acc[rt][c]);
+              }
+            } else {
+#pragma unroll
+              for (int c = 0; c < NCB; ++c) {
+                acc[rt][c] = mfma_f16_16x16x32(x0, *l1_operand(g, c, 0), acc[rt][c]);
+                acc[rt][c] = mfma_f16_16x16x32(x1, *l1_operand(g, c, 1), acc[rt][c]);
+              }
+            }
+          }
+        }
+        if (i < n_mine && rvalid[rt]) {
+          if constexpr (MX) {
+            // tiled layouts: group g is half h of chunk g/2; this lane's 16
+            // codes are the 8 bytes at 8*(c4%2) of lane 16*kq + qr of the
+            // chunk's block, kq = 2h + c4/2 (its 32-block within the chunk);
+            // the exponent of that 32-block (lanes c4 = 0, 2 hold the two) is
+            // byte ti of lane 16*kq + qr of the chunk's exponent block
+            const int c = g >> 1, h = g & 1;
+            const int kq = 2 * h + (c4 >> 1);
+            uint8_t* cb = tcode[rt] + static_cast<int64_t>(c) * 1024 + (16 * kq + qr) * 16 + 8 * (c4 & 1);
+            uint8_t* eb = texp[rt] + static_cast<int64_t>(c) * 256 + (16 * kq + qr) * 4;
+            *reinterpret_cast<uint2*>(cb) = make_uint2(packed[0], packed[1]);
+            if ((c4 & 1) == 0) eb[0] = static_cast<uint8_t>(meta & 0xFFu);
+            if (h == 0 && g == G - 1) {
+              // K % 128 == 64: the chunk's second half does not exist; zero
+              // codes and exponent 127 make it add exactly nothing
+              *reinterpret_cast<uint2*>(cb + 32 * 16) = make_uint2(0u, 0u);
+              if ((c4 & 1) == 0) eb[32 * 4] = 127;
             }
           } else {
-#pragma unroll
-            for (int c = 0; c < NCB; ++c) {
-              acc[c] = mfma_f16_16x16x32(x0, *l1_operand(g, c, 0), acc[c]);
-              acc[c] = mfma_f16_16x16x32(x1, *l1_operand(g, c, 1), acc[c]);
-            }
+            *reinterpret_cast<uint2*>(crow[rt] + g * kGroupBytes) = make_uint2(packed[0], packed[1]);
+            if (c4 == 0) srow[rt][g] = static_cast<uint16_t>(meta);
           }
-        }
-      }
-      if (i < n_mine && rvalid) {
-        if constexpr (MX) {
-          // tiled layouts: group g is half h of chunk g/2; this lane's 16
-          // codes are the 8 bytes at 8*(c4%2) of lane 16*kq + qr of the chunk's
-          // block, kq = 2h + c4/2 (its 32-block within the chunk); the
-          // exponent of that 32-block (lanes c4 = 0, 2 hold the two) is byte
-          // ti of lane 16*kq + qr of the chunk's exponent block
-          const int c = g >> 1, h = g & 1;
-          const int kq = 2 * h + (c4 >> 1);
-          uint8_t* cb = tcode + static_cast<int64_t>(c) * 1024 + (16 * kq + qr) * 16 + 8 * (c4 & 1);
-          uint8_t* eb = texp + static_cast<int64_t>(c) * 256 + (16 * kq + qr) * 4;
-          *reinterpret_cast<uint2*>(cb) = make_uint2(packed[0], packed[1]);
-          if ((c4 & 1) == 0) eb[0] = static_cast<uint8_t>(meta & 0xFFu);
-          if (h == 0 && g == G - 1) {
-            // K % 128 == 64: the chunk's second half does not exist; zero codes
-            // and exponent 127 make it add exactly nothing
-            *reinterpret_cast<uint2*>(cb + 32 * 16) = make_uint2(0u, 0u);
-            if ((c4 & 1) == 0) eb[32 * 4] = 127;
-          }
-        } else {
-          *reinterpret_cast<uint2*>(cblk + g * kGroupBytes + coff) = make_uint2(packed[0], packed[1]);
-          if (c4 == 0) sblk[g + soff] = static_cast<uint16_t>(meta);
         }
       }
       // Refill this slot only after the stores: issued right behind the matrix
@@ -424,11 +444,13 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
   if constexpr (NCB > 0) {
     // partial D of this wave -> LDS; lane holds rows 4q+j of column c*16+rl
 #pragma unroll
-    for (int c = 0; c < NCB; ++c)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dpart[wave][4 * q + j][c * 16 + rl] = acc[c][j];
+      for (int c = 0; c < NCB; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dpart[wave][16 * rt + 4 * q + j][c * 16 + rl] = acc[rt][c][j];
     __syncthreads();
-    for (int t = threadIdx.x; t < 16 * R; t += blockDim.x) {
+    for (int t = threadIdx.x; t < 16 * RT * R; t += blockDim.x) {
       const int r_ = t / R, c_ = t - r_ * R;
       float s = 0.f;
 #pragma unroll
@@ -438,30 +460,48 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
   }
 }
 
+template <typename XT, int NCB, int RT>
+hipError_t launch_k1_rt(const void* X, int64_t M, int64_t K, int64_t ldx,
+                        const float* inv_smooth, const uint16_t* L1p, int R,
+                        uint8_t* a_codes, void* a_meta, bool mx, float* D, hipStream_t stream,
+                        const ConvGeom* conv) {
+  // groups in flight per wave, sized so the ring fits the register budget of
+  // two resident workgroups
+  constexpr int NB = 1;
+  const dim3 block(64 * k1_waves<NCB>()),
+      grid(static_cast<unsigned>((M + 16 * RT - 1) / (16 * RT)));
+  const XT* x = static_cast<const XT*>(X);
+  const ConvGeom cg = conv ? *conv : ConvGeom{};
+  if (conv && mx)
+    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, true, true, RT>), grid, block, 0,
+                       stream, x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
+  else if (conv)
+    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, false, true, RT>), grid, block, 0,
+                       stream, x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
+  else if (mx)
+    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, true, false, RT>), grid, block, 0,
+                       stream, x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
+  else
+    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, false, false, RT>), grid, block, 0,
+                       stream, x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
+  return hipGetLastError();
+}
+
+// Two row tiles per workgroup once there are at least two of them per
+// resident workgroup slot (every compute unit still gets several workgroups),
+// up to rank 32 (beyond it the second tile's registers cost occupancy).
 template <typename XT, int NCB>
 hipError_t launch_k1_t(const void* X, int64_t M, int64_t K, int64_t ldx,
                        const float* inv_smooth, const uint16_t* L1p, int R,
                        uint8_t* a_codes, void* a_meta, bool mx, float* D, hipStream_t stream,
                        const ConvGeom* conv) {
-  // groups in flight per wave, sized so the ring fits the register budget of
-  // two resident workgroups
-  constexpr int NB = 1;
-  const dim3 block(64 * k1_waves<NCB>()), grid(static_cast<unsigned>((M + 15) / 16));
-  const XT* x = static_cast<const XT*>(X);
-  const ConvGeom cg = conv ? *conv : ConvGeom{};
-  if (conv && mx)
-    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, true, true>), grid, block, 0, stream,
-                       x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
-  else if (conv)
-    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, false, true>), grid, block, 0, stream,
-                       x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
-  else if (mx)
-    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, true, false>), grid, block, 0, stream,
-                       x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
-  else
-    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, false, false>), grid, block, 0, stream,
-                       x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
-  return hipGetLastError();
+  if constexpr (NCB <= 2) {
+    if ((M + 15) / 16 >= 2 * static_cast<int64_t>(resident_slots()))
+      return launch_k1_rt<XT, NCB, 2>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D,
+                                      stream, conv);
+  }
+  return launch_k1_rt<XT, NCB, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D,
+                                  stream, conv);
 }
 
 template <typename XT>
