@@ -26,7 +26,10 @@
 // over the lanes r, r+16, r+32, r+48: its absmax is a reduction over those
 // four lanes with the gfx950 lane-swap instructions (v_permlane16_swap,
 // v_permlane32_swap), and the four lanes write its 32 bytes of codes side by
-// side. L1 arrives packed in the matrix instruction's operand order (see
+// side. Each lane loads one smoothing factor per group (lane l: channel l of
+// the group, one coalesced 256-byte load per wave) and takes the 16 it needs
+// from the lanes of its 16-lane row with DPP row broadcasts. L1 arrives packed
+// in the matrix instruction's operand order (see
 // svdq_pack_lowrank_down), so each operand is one contiguous 1 KB load per
 // wave. The per-wave partial D tiles are summed in LDS in a fixed order.
 //
@@ -102,6 +105,22 @@ __device__ __forceinline__ void smooth16(const Raw<float>& r, const float4* inv,
     xh[4 * i + 2] = r.v[i].z * inv[i].z;
     xh[4 * i + 3] = r.v[i].w * inv[i].w;
   }
+}
+
+// Lane J of each 16-lane row, in every lane of that row (DPP row_newbcast).
+template <int J>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + J,
+                                                            0xF, 0xF, false));
+}
+
+// The 16 smoothing factors of a lane's channels 16q .. 16q+15, from one value
+// per lane (lane 16q + j holds channel 16q + j's).
+__device__ __forceinline__ void expand_inv(float v, float4 inv[4]) {
+  inv[0] = make_float4(row_bcast<0>(v), row_bcast<1>(v), row_bcast<2>(v), row_bcast<3>(v));
+  inv[1] = make_float4(row_bcast<4>(v), row_bcast<5>(v), row_bcast<6>(v), row_bcast<7>(v));
+  inv[2] = make_float4(row_bcast<8>(v), row_bcast<9>(v), row_bcast<10>(v), row_bcast<11>(v));
+  inv[3] = make_float4(row_bcast<12>(v), row_bcast<13>(v), row_bcast<14>(v), row_bcast<15>(v));
 }
 
 // Maxima of non-negative floats across lanes, on their bit patterns (for
@@ -213,13 +232,14 @@ template <int NCB>
 constexpr int k1_waves() { return NCB <= 4 ? 8 : 4; }
 
 // Everything one lane reads for one group: its 16 X values in each of the
-// workgroup's RT row tiles, the 16 matching smoothing factors and, per column
-// block of D, its two packed L1 operands (both shared by the row tiles).
+// workgroup's RT row tiles, one smoothing factor (the lane's 16 come from its
+// row's lanes) and, per column block of D, its two packed L1 operands (both
+// shared by the row tiles).
 template <typename XT, int NCB, int RT>
 struct GroupIn {
   Raw<XT> x[RT];
   bool valid[RT];        // convolution: the tap lies inside the image (else the values are 0)
-  float4 inv[4];
+  float inv1;            // smoothing factor of channel 16*(lane/16) + lane%16 of the group
   v8h l1[ring_l1_blocks<NCB>() > 0 ? ring_l1_blocks<NCB>() : 1][2];
 };
 
@@ -297,7 +317,6 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
       iw0[rt] = ow * cg.stride - cg.pad;
     }
   }
-  const uint32_t ioff = c4 * 16;
   const v8h* l1b = reinterpret_cast<const v8h*>(L1p);
 
   // packed operand (g, c, h) of this lane
@@ -329,9 +348,7 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
         load_raw<XT>(in.x[rt], xrow[rt] + k0);
       }
     }
-    const float4* ip = reinterpret_cast<const float4*>(inv_smooth + k0 + ioff);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) in.inv[j] = ip[j];
+    in.inv1 = inv_smooth[k0 + lane];
     if constexpr (ring_l1_blocks<NCB>() > 0) {
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
@@ -366,7 +383,9 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
         uint32_t meta = 0u;                  // fp16 scale, or the E8M0 byte
         if (i < n_mine) {
           float xh[16];
-          smooth16(ring[b].x[rt], ring[b].inv, xh, nz);
+          float4 iv[4];
+          expand_inv(ring[b].inv1, iv);
+          smooth16(ring[b].x[rt], iv, xh, nz);
           if constexpr (CONV) {
             // a tap outside the image: the patch matrix holds zeros there
 #pragma unroll
@@ -489,13 +508,13 @@ hipError_t launch_k1_rt(const void* X, int64_t M, int64_t K, int64_t ldx,
 
 // Two row tiles per workgroup once there are at least two of them per
 // resident workgroup slot (every compute unit still gets several workgroups),
-// up to rank 32 (beyond it the second tile's registers cost occupancy).
+// up to rank 64 (beyond it the second tile's registers cost occupancy).
 template <typename XT, int NCB>
 hipError_t launch_k1_t(const void* X, int64_t M, int64_t K, int64_t ldx,
                        const float* inv_smooth, const uint16_t* L1p, int R,
                        uint8_t* a_codes, void* a_meta, bool mx, float* D, hipStream_t stream,
                        const ConvGeom* conv) {
-  if constexpr (NCB <= 2) {
+  if constexpr (NCB <= 4) {
     if ((M + 15) / 16 >= 2 * static_cast<int64_t>(resident_slots()))
       return launch_k1_rt<XT, NCB, 2>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D,
                                       stream, conv);
