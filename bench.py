@@ -161,6 +161,18 @@ def time_steps(torch, sets, steps, warmup):
     return (t1 - t0) / steps, k1, k2
 
 
+def copy_probe(torch):
+    """A plain copy of known size (256 Mi fp32: 1 GiB read + 1 GiB written, more
+    than the last-level cache), whose FETCH_SIZE and WRITE_SIZE counters scale
+    the GEMM's and the pre-kernel's to bytes."""
+    n = 256 << 20
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+
+
 def event_gap(torch, reps=50):
     """Median time between two HIP events recorded back to back on the current
     stream with nothing between them: the overhead one event pair adds to a
@@ -380,6 +392,8 @@ def conv_main(args, torch, sq, wl):
                "achieved_gbs": round(k1_bytes / k1_avg / 1e9, 1), "peak_gbs": HBM_PEAK_GBS,
                "frac": round(k1_bytes / k1_avg / 1e9 / HBM_PEAK_GBS, 4)},
     }
+    if args.copy_probe:
+        copy_probe(torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = conv_cpu_baseline(L, X, Wm, prep, bias, args.cpu_seconds)
     print(json.dumps(out), flush=True)
@@ -457,12 +471,7 @@ def main():
         del sets0
 
     if args.copy_probe:
-        n = 256 << 20                     # 256 Mi fp32 = 1 GiB read + 1 GiB written (> MALL)
-        a = torch.ones(n, dtype=torch.float32, device="cuda")
-        b = torch.empty_like(a)
-        for _ in range(5):
-            torch.mul(a, 1.0, out=b)
-        torch.cuda.synchronize()
+        copy_probe(torch)
 
     if w16:
         metric = "effective TFLOPS of the 4-bit weight-only (W4A16) baseline linear, % of fp16 MFMA peak"
