@@ -43,6 +43,7 @@
 
 #include "device_common.hpp"
 #include "device_launch.hpp"
+#include "k2_common.hpp"
 
 namespace svdq {
 
@@ -273,7 +274,12 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
   // lane map: row qr = rl of each row tile, channels 16*c4 .. +15 of each group
   const int rl = lane & 15, q = lane >> 4;
   const int qr = rl, c4 = q;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * (16 * RT);
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin; renumber
+  // so each XCD takes one contiguous run of row tiles (neighbouring output
+  // pixels of a convolution read the same input rows, which then stay in
+  // that XCD's L2)
+  const int tile = xcd_contiguous(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+  const int64_t row0 = static_cast<int64_t>(tile) * (16 * RT);
   const int G = static_cast<int>(K / kGroup);
   const int ncb = R / 16;                            // real column blocks (<= NCB)
   // this wave's groups are wave, wave+WAVES, ...: n_mine of them

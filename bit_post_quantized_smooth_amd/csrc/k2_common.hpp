@@ -1,6 +1,7 @@
-// Pieces shared by the two GEMM kernels (INT4 and MXFP4): the XCD-aware tile
-// order and the epilogue that adds the low-rank up-projection and the bias,
-// applies the optional GELU and stores Y.
+// Pieces shared by the GEMM kernels (INT4, MXFP4 and the weight-only
+// baseline): the XCD-aware tile order (which the pre-kernel uses too) and the
+// epilogue that adds the low-rank up-projection and the bias, applies the
+// optional GELU and stores Y.
 #pragma once
 
 #include <hip/hip_runtime.h>
