@@ -25,13 +25,21 @@
 // operands arrive in the tiled layouts of svdq.h: the 16 bytes every lane needs
 // for one 16-row block and one chunk of 128 form one contiguous 1 KB run, and
 // the exponent bytes for four such blocks one contiguous 256-byte run (a
-// 32-bit word per lane whose byte i belongs to block i). Each wave therefore
-// loads its operands straight into registers, one coalesced 1 KB load per
-// block and chunk, with no LDS staging and no barrier; the two waves that
-// share a row (or column) panel read it through the same L1. The K loop keeps
-// NS chunks in flight and has no branch, so the wait counter only ever waits
-// for the oldest chunk; chunk numbers past the end are clamped to the last
-// chunk (repeated loads, never used).
+// 32-bit word per lane whose byte i belongs to block i).
+// - Full tiles copy every block of a chunk from global memory into LDS once
+//   per workgroup, with direct-to-LDS loads (global_load_lds: no registers),
+//   and each wave reads its blocks from LDS. Loading them per wave instead
+//   fetched each block twice (two waves share every row and column panel)
+//   and kept the vector memory address unit 72% busy. Three LDS stages: while
+//   chunk c's matrix instructions run, chunk c+1 is read into registers and
+//   chunk c+2 is copied into the stage chunk c-1 left; one barrier per chunk.
+//   The waits are written out (s_waitcnt with the count of one chunk's copies,
+//   then s_barrier) because the compiler's own would wait for every copy.
+// - Quarter tiles (a thin last round) load straight into registers, one
+//   coalesced 1 KB load per block and chunk; the K loop keeps NS chunks in
+//   flight and has no branch, so the wait counter only ever waits for the
+//   oldest chunk; chunk numbers past the end are clamped to the last chunk
+//   (repeated loads, never used).
 //
 // Tiling: a 256-thread workgroup computes a 2*WTM x 2*WTN tile, each wave a
 // WTM x WTN quarter: 256 x 128 tiles of 128 x 64 waves (128 fp32 accumulators
@@ -198,6 +206,120 @@ __device__ __forceinline__ void mx_tile(
   bias_store<WTM, WTN, Y_F16, GELU>(acc, bias, Y, M, N, ldy, m0, n0);
 }
 
+// Full 256 x 128 tile with the operands shared through LDS (see the top of
+// the file): each wave copies 4 activation blocks, 2 weight blocks and one
+// exponent block of each (waves 2 and 3 copy the weight exponents again,
+// which keeps every wave's copy count at 8), and reads its 8 activation and 4
+// weight blocks and their exponent words.
+struct MxStage {
+  uint8_t a[16][kCodeBlock];        // activation blocks of the tile's 256 rows
+  uint8_t b[8][kCodeBlock];         // weight blocks of its 128 columns
+  uint8_t ea[4][kExpBlock];         // activation exponent blocks (64 rows each)
+  uint8_t eb[2][kExpBlock];         // weight exponent blocks
+};
+
+#define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <bool Y_F16, bool GELU>
+__device__ __forceinline__ void mx_tile_lds(
+    MxStage (&st)[3], const uint8_t* __restrict__ a_codes_t, const uint8_t* __restrict__ a_exps_t,
+    const uint8_t* __restrict__ w_codes_t, const uint8_t* __restrict__ w_exps_t,
+    const float* __restrict__ D, const uint16_t* __restrict__ L2t, int R,
+    const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N, int64_t K,
+    int64_t ldy, int64_t m0, int64_t n0) {
+  constexpr int WTM = 128, WTN = 64, NBM = 8, NBN = 4;
+  using Frags = MxFrags<NBM, NBN>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t C = (K + kChunk - 1) / kChunk;
+  const int64_t mb_last = (M + 15) / 16 - 1, nb_last = (N + 15) / 16 - 1;
+  const int64_t mg_last = (M + 63) / 64 - 1, ng_last = (N + 63) / 64 - 1;
+  // this wave's share of the copies: activation blocks 4w .. 4w+3, weight
+  // blocks 2w, 2w+1, activation exponent block w and weight exponent block
+  // w % 2 (waves 2 and 3 copy the same bytes as 0 and 1)
+  const uint8_t* ga[4];
+  const uint8_t* gb[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t b = m0 / 16 + 4 * wave + i;
+    ga[i] = a_codes_t + (b < mb_last ? b : mb_last) * C * kCodeBlock + 16 * lane;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t b = n0 / 16 + 2 * wave + j;
+    gb[j] = w_codes_t + (b < nb_last ? b : nb_last) * C * kCodeBlock + 16 * lane;
+  }
+  const int64_t gea_b = m0 / 64 + wave, geb_b = n0 / 64 + (wave & 1);
+  const uint8_t* gea = a_exps_t + (gea_b < mg_last ? gea_b : mg_last) * C * kExpBlock + 4 * lane;
+  const uint8_t* geb = w_exps_t + (geb_b < ng_last ? geb_b : ng_last) * C * kExpBlock + 4 * lane;
+
+  auto copy = [&](MxStage& s, int64_t c) {
+    c = c < C ? c : C - 1;
+    const int64_t co = c * kCodeBlock, eo = c * kExpBlock;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(ga[i] + co, LDSP(&s.a[4 * wave + i][0]), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_global_load_lds(gb[j] + co, LDSP(&s.b[2 * wave + j][0]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(gea + eo, LDSP(&s.ea[wave][0]), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(geb + eo, LDSP(&s.eb[wave & 1][0]), 4, 0, 0);
+  };
+  auto read = [&](Frags& f, const MxStage& s) {
+#pragma unroll
+    for (int i = 0; i < NBM; ++i) f.A[i] = *reinterpret_cast<const uint4*>(&s.a[NBM * wm + i][16 * lane]);
+#pragma unroll
+    for (int j = 0; j < NBN; ++j) f.B[j] = *reinterpret_cast<const uint4*>(&s.b[NBN * wn + j][16 * lane]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) f.sa[t] = *reinterpret_cast<const uint32_t*>(&s.ea[2 * wm + t][4 * lane]);
+    f.sb[0] = *reinterpret_cast<const uint32_t*>(&s.eb[wn][4 * lane]);
+  };
+  // all of this wave's copies and LDS reads done, then every wave's
+  constexpr int kWaitAll = 0x0070;   // vmcnt(0) expcnt(7) lgkmcnt(0)
+  auto sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __builtin_amdgcn_s_barrier();
+  };
+
+  copy(st[0], 0);
+  copy(st[1], 1);
+  v4f acc[NBM][NBN];
+#pragma unroll
+  for (int i = 0; i < NBM; ++i)
+#pragma unroll
+    for (int j = 0; j < NBN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  lowrank_up<WTM, WTN>(acc, D, L2t, R, M, N, m0, n0);
+  sync();                            // chunks 0 and 1 in stages 0 and 1
+  Frags f[2];
+  read(f[0], st[0]);
+  // iteration c: chunk c's operands are in f[c % 2]; chunk c+1 is in stage
+  // (c+1) % 3; chunk c+2 is copied into stage (c+2) % 3, which held chunk
+  // c-1 (read two iterations ago, before the last barrier)
+  constexpr int kWaitCopies = 0x0078;  // vmcnt(8) expcnt(7) lgkmcnt(0): one chunk's copies may fly
+  int64_t c = 0;
+  int s1 = 1, s2 = 2;                // stages of chunks c+1 and c+2
+  for (; c + 2 <= C; c += 2) {
+    static_for<2>([&](auto S) {
+      constexpr int P = S.value;
+      copy(st[s2], c + P + 2);
+      __builtin_amdgcn_s_waitcnt(kWaitCopies);
+      __builtin_amdgcn_s_barrier();  // chunk c+P+1 copied by all waves
+      read(f[P ^ 1], st[s1]);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_chunk<NBM, NBN>(acc, f[P]);
+      __builtin_amdgcn_sched_barrier(0);
+      s1 = s2;
+      s2 = s2 == 2 ? 0 : s2 + 1;
+    });
+  }
+  if (c < C) mfma_chunk<NBM, NBN>(acc, f[0]);
+  // the copies of chunks past the end land in LDS no later wave reads; wait
+  // for them before the workgroup's LDS can be handed on
+  sync();
+  bias_store<WTM, WTN, Y_F16, GELU>(acc, bias, Y, M, N, ldy, m0, n0);
+}
+
 constexpr int kFullM = 256, kFullN = 128;     // full tile; quarters are 128 x 64
 
 // Workgroups 0 .. n_full-1 take the first n_full full tiles of the banded
@@ -209,14 +331,15 @@ __global__ __launch_bounds__(NT, 2) void k2_mx_kernel(
     const float* __restrict__ D, const uint16_t* __restrict__ L2t, int R,
     const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N, int64_t K,
     int64_t ldy, int tiles_m, int tiles_n, int n_full) {
+  __shared__ MxStage st[3];
   const int b = static_cast<int>(blockIdx.x);
   int tm, tn;
   if (b < n_full) {
     banded_tile(xcd_contiguous(b, n_full), tiles_m, tiles_n, tm, tn);
-    mx_tile<kFullM / 2, kFullN / 2, Y_F16, GELU>(a_codes_t, a_exps_t, w_codes_t, w_exps_t, D, L2t,
-                                                 R, bias, Y, M, N, K, ldy,
-                                                 static_cast<int64_t>(tm) * kFullM,
-                                                 static_cast<int64_t>(tn) * kFullN);
+    mx_tile_lds<Y_F16, GELU>(st, a_codes_t, a_exps_t, w_codes_t, w_exps_t, D, L2t,
+                             R, bias, Y, M, N, K, ldy,
+                             static_cast<int64_t>(tm) * kFullM,
+                             static_cast<int64_t>(tn) * kFullN);
   } else {
     const int qb = b - n_full;
     const int quarter = qb & 3;
