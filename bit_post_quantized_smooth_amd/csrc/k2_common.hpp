@@ -151,6 +151,68 @@ __device__ __forceinline__ void bias_store(v4f (&acc)[WTM / 16][WTN / 16],
   }
 }
 
+// The same epilogue for an fp16 Y through LDS, for a wave whose WTM x 64
+// quarter lies inside Y, with Y and its row stride 16-byte aligned. The wave
+// writes its rounded values (bias and GELU applied) into its own region of
+// LDS (WTM rows of 128 bytes, the 16-byte units of row r XOR-swizzled by
+// r % 8), then reads them back 16 bytes per lane: 8 lanes cover one 128-byte
+// row, so every store instruction writes 8 whole cache lines of Y instead of
+// 32-byte pieces of 16. `lds` is this wave's region (WTM * 128 bytes, 16-byte
+// aligned); the caller makes sure no other wave still reads it.
+template <int WTM, int WTN, bool GELU>
+__device__ __forceinline__ void bias_store_lds_f16(v4f (&acc)[WTM / 16][WTN / 16],
+                                                   const float* __restrict__ bias,
+                                                   _Float16* __restrict__ Y, int64_t ldy,
+                                                   int64_t m0, int64_t n0, uint8_t* lds) {
+  static_assert(WTN == 64, "one 128-byte LDS row per output row");
+  constexpr int NBM = WTM / 16, NBN = WTN / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rl = lane & 15, q = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t mw = m0 + wm * WTM, nw = n0 + wn * WTN;
+  float bv[NBN][4];
+#pragma unroll
+  for (int j = 0; j < NBN; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bv[j][e] = bias != nullptr ? bias[nw + j * 16 + 4 * q + e] : 0.f;
+#pragma unroll
+  for (int i = 0; i < NBM; ++i) {
+    const int row = i * 16 + rl;
+#pragma unroll
+    for (int j = 0; j < NBN; ++j) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = acc[i][j][e] + bv[j][e];
+        if constexpr (GELU) v[e] = gelu_tanh_f32(v[e]);
+      }
+      const uint32_t lo = static_cast<uint32_t>(f2h(v[0])) | (static_cast<uint32_t>(f2h(v[1])) << 16);
+      const uint32_t hi = static_cast<uint32_t>(f2h(v[2])) | (static_cast<uint32_t>(f2h(v[3])) << 16);
+      const int unit = 2 * j + (q >> 1);              // 16-byte unit of columns 16j + 4q .. +3
+      *reinterpret_cast<uint2*>(lds + row * 128 + ((unit ^ (row & 7)) << 4) + ((q & 1) << 3)) =
+          make_uint2(lo, hi);
+    }
+  }
+  const int u = lane & 7, r8 = lane >> 3;
+#pragma unroll
+  for (int it = 0; it < WTM / 8; ++it) {
+    const int row = it * 8 + r8;
+    const uint4 v = *reinterpret_cast<const uint4*>(lds + row * 128 + ((u ^ r8) << 4));
+    *reinterpret_cast<uint4*>(Y + (mw + row) * ldy + nw + 8 * u) = v;
+  }
+}
+
+// Whether this wave's WTM x WTN quarter of the tile at (m0, n0) may take the
+// LDS-staged fp16 store: inside Y, Y and its row stride 16-byte aligned.
+template <int WTM, int WTN>
+__device__ __forceinline__ bool lds_store_ok(const void* Y, int64_t ldy, int64_t M, int64_t N,
+                                             int64_t m0, int64_t n0) {
+  const int wave = threadIdx.x >> 6;
+  const int64_t mw = m0 + (wave >> 1) * WTM, nw = n0 + (wave & 1) * WTN;
+  return mw + WTM <= M && nw + WTN <= N &&
+         ((reinterpret_cast<uintptr_t>(Y) | static_cast<uintptr_t>(ldy * 2)) % 16) == 0;
+}
+
 // Both, in that order (the INT4 and weight-only kernels' epilogue).
 template <int WTM, int WTN, bool Y_F16, bool GELU>
 __device__ __forceinline__ void lowrank_bias_store(

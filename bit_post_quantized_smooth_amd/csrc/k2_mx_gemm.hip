@@ -211,7 +211,7 @@ __device__ __forceinline__ void mx_tile(
 // exponent block of each (waves 2 and 3 copy the weight exponents again,
 // which keeps every wave's copy count at 8), and reads its 8 activation and 4
 // weight blocks and their exponent words.
-struct MxStage {
+struct alignas(16) MxStage {
   uint8_t a[16][kCodeBlock];        // activation blocks of the tile's 256 rows
   uint8_t b[8][kCodeBlock];         // weight blocks of its 128 columns
   uint8_t ea[4][kExpBlock];         // activation exponent blocks (64 rows each)
@@ -317,7 +317,12 @@ __device__ __forceinline__ void mx_tile_lds(
   // the copies of chunks past the end land in LDS no later wave reads; wait
   // for them before the workgroup's LDS can be handed on
   sync();
-  bias_store<WTM, WTN, Y_F16, GELU>(acc, bias, Y, M, N, ldy, m0, n0);
+  static_assert(sizeof(MxStage) * 3 >= 4 * WTM * 128, "each wave stages a WTM x 64 fp16 tile");
+  if (Y_F16 && lds_store_ok<WTM, WTN>(Y, ldy, M, N, m0, n0))
+    bias_store_lds_f16<WTM, WTN, GELU>(acc, bias, static_cast<_Float16*>(Y), ldy, m0, n0,
+                                       reinterpret_cast<uint8_t*>(&st[0]) + wave * WTM * 128);
+  else
+    bias_store<WTM, WTN, Y_F16, GELU>(acc, bias, Y, M, N, ldy, m0, n0);
 }
 
 constexpr int kFullM = 256, kFullN = 128;     // full tile; quarters are 128 x 64

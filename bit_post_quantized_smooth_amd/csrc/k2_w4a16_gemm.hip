@@ -125,7 +125,7 @@ __device__ __forceinline__ void w16_tile(const uint16_t* __restrict__ x_t,
                                          const uint16_t* __restrict__ w_scales_t,
                                          const float* __restrict__ bias, void* __restrict__ Y,
                                          int64_t M, int64_t N, int64_t K, int64_t ldy, int64_t m0,
-                                         int64_t n0) {
+                                         int64_t n0, uint8_t* ystage) {
   constexpr int NBM = WTM / 16, NBN = WTN / 16;
   using Frags = W16Frags<NBM, NBN>;
   const int lane = threadIdx.x & 63;
@@ -208,6 +208,16 @@ __device__ __forceinline__ void w16_tile(const uint16_t* __restrict__ x_t,
     if (s0 + P.value < S) step(f[P.value]);
   });
 
+  // full quarters of an fp16 Y go out through LDS in whole cache lines; the
+  // staging area is used by nothing else, so no wave waits for another
+  if constexpr (Y_F16 && WTN == 64) {
+    if (ystage != nullptr && lds_store_ok<WTM, WTN>(Y, ldy, M, N, m0, n0)) {
+      const int wave = threadIdx.x >> 6;
+      bias_store_lds_f16<WTM, WTN, false>(acc, bias, static_cast<_Float16*>(Y), ldy, m0, n0,
+                                          ystage + wave * WTM * 128);
+      return;
+    }
+  }
   lowrank_bias_store<WTM, WTN, Y_F16, false>(acc, nullptr, nullptr, 0, bias, Y, M, N, ldy, m0,
                                              n0);
 }
@@ -227,20 +237,23 @@ __global__ __launch_bounds__(NT, 2) void k2_w4a16_kernel(
     const uint16_t* __restrict__ w_scales_t, const float* __restrict__ bias,
     void* __restrict__ Y, int64_t M, int64_t N, int64_t K, int64_t ldy, int tiles_m, int tiles_n,
     int n_full) {
+  // Y staging of a full tile (fp16 only)
+  __shared__ __attribute__((aligned(16))) uint8_t ystage[Y_F16 ? 4 * kWtm * 128 : 16];
   const int b = static_cast<int>(blockIdx.x);
   int tm, tn;
   if (b < n_full) {
     banded_tile(xcd_contiguous(b, n_full), tiles_m, tiles_n, tm, tn);
     w16_tile<kWtm, kWtn, Y_F16>(x_t, w_codes_t, w_scales_t, bias, Y, M, N, K, ldy,
                                 static_cast<int64_t>(tm) * kFullM,
-                                static_cast<int64_t>(tn) * kFullN);
+                                static_cast<int64_t>(tn) * kFullN, Y_F16 ? ystage : nullptr);
   } else {
     const int qb = b - n_full;
     const int quarter = qb & 3;
     banded_tile(n_full + (qb >> 2), tiles_m, tiles_n, tm, tn);
     w16_tile<kWtm / 2, kWtn / 2, Y_F16>(x_t, w_codes_t, w_scales_t, bias, Y, M, N, K, ldy,
                                         static_cast<int64_t>(tm) * kFullM + kWtm * (quarter >> 1),
-                                        static_cast<int64_t>(tn) * kFullN + kWtn * (quarter & 1));
+                                        static_cast<int64_t>(tn) * kFullN + kWtn * (quarter & 1),
+                                        nullptr);
   }
 }
 

@@ -285,7 +285,17 @@ __device__ __forceinline__ void gemm_tile(
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] *= 0.00390625f;
 
-  lowrank_bias_store<WT, WT, Y_F16, GELU>(acc, D, L2t, R, bias, Y, M, N, ldy, m0, n0);
+  lowrank_up<WT, WT>(acc, D, L2t, R, M, N, m0, n0);
+  if constexpr (Y_F16 && WT == 64) {
+    static_assert(sizeof(Smem<WT>) >= 4 * WT * 128, "each wave stages a WT x 64 fp16 tile");
+    __syncthreads();                 // every wave is done reading the operands in LDS
+    if (lds_store_ok<WT, WT>(Y, ldy, M, N, m0, n0)) {
+      bias_store_lds_f16<WT, WT, GELU>(acc, bias, static_cast<_Float16*>(Y), ldy, m0, n0,
+                                       reinterpret_cast<uint8_t*>(&sm) + wave * WT * 128);
+      return;
+    }
+  }
+  bias_store<WT, WT, Y_F16, GELU>(acc, bias, Y, M, N, ldy, m0, n0);
 }
 
 // Workgroups 0 .. n_full-1 take the first n_full 128 x 128 tiles of the banded
