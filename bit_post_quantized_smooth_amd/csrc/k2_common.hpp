@@ -49,6 +49,10 @@ __device__ __forceinline__ void banded_tile(int t, int tiles_m, int tiles_n, int
 // acc += fp16(D) . L2; then the bias, optionally the GELU, and one rounding
 // to the output type.
 // The low-rank up-projection on the accumulators: acc += fp16(D) . L2.
+// Every load is unconditional, from a clamped in-bounds address, and
+// out-of-range operands are zeroed after it arrives; a load under a branch
+// whose other side zeroes the same registers would have to complete before
+// anything else is issued.
 template <int WTM, int WTN>
 __device__ __forceinline__ void lowrank_up(v4f (&acc)[WTM / 16][WTN / 16],
                                            const float* __restrict__ D,
@@ -58,32 +62,29 @@ __device__ __forceinline__ void lowrank_up(v4f (&acc)[WTM / 16][WTN / 16],
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rl = lane & 15, q = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
+  const v8h zero = v8h{0, 0, 0, 0, 0, 0, 0, 0};
   for (int rc = 0; rc < R; rc += 32) {
     const int kk = rc + 8 * q;                       // this lane's 8 rank indices
     const bool kval = kk < R;                        // R % 16 == 0: whole 8-runs are valid or not
-    // the L2 fragments of all column blocks, then one row block of D at a time
-    // (few registers live at once: the caller may hold loads in flight)
     v8h Bl[NBN];
 #pragma unroll
     for (int j = 0; j < NBN; ++j) {
       const int64_t n = n0 + wn * WTN + j * 16 + rl;
-      if (kval && n < N)
-        Bl[j] = *reinterpret_cast<const v8h*>(L2t + n * R + kk);
-      else
-        Bl[j] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+      const bool ok = kval && n < N;
+      const v8h b = *reinterpret_cast<const v8h*>(L2t + (ok ? n * R + kk : 0));
+      Bl[j] = ok ? b : zero;
     }
 #pragma unroll
     for (int i = 0; i < NBM; ++i) {
       const int64_t m = m0 + wm * WTM + i * 16 + rl;
-      v8h Al = v8h{0, 0, 0, 0, 0, 0, 0, 0};
-      if (kval && m < M) {
-        const float4* dp = reinterpret_cast<const float4*>(D + m * R + kk);
-        const float4 u = dp[0], v = dp[1];
-        Al = v8h{static_cast<_Float16>(u.x), static_cast<_Float16>(u.y),
-                 static_cast<_Float16>(u.z), static_cast<_Float16>(u.w),
-                 static_cast<_Float16>(v.x), static_cast<_Float16>(v.y),
-                 static_cast<_Float16>(v.z), static_cast<_Float16>(v.w)};
-      }
+      const bool ok = kval && m < M;
+      const float4* dp = reinterpret_cast<const float4*>(D + (ok ? m * R + kk : 0));
+      const float4 u = dp[0], v = dp[1];
+      const v8h a = v8h{static_cast<_Float16>(u.x), static_cast<_Float16>(u.y),
+                        static_cast<_Float16>(u.z), static_cast<_Float16>(u.w),
+                        static_cast<_Float16>(v.x), static_cast<_Float16>(v.y),
+                        static_cast<_Float16>(v.z), static_cast<_Float16>(v.w)};
+      const v8h Al = ok ? a : zero;
 #pragma unroll
       for (int j = 0; j < NBN; ++j) acc[i][j] = mfma_f16_16x16x32(Bl[j], Al, acc[i][j]);
     }
