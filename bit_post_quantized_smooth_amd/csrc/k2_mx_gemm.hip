@@ -18,7 +18,9 @@
 // so a lane ends up with 4 consecutive columns of one row of each 16 x 16
 // output block, as in the INT4 kernel, and the same epilogue pieces
 // (k2_common.hpp) finish the tile: the low-rank up-projection seeds the
-// accumulators before the K loop, the bias and the stores follow it.
+// accumulators before the K loop, the bias and the stores follow it (a full
+// quarter of an fp16 Y goes through the then idle operand LDS and out in
+// whole cache lines).
 //
 // Data movement. One instruction takes 16 cycles on a SIMD and consumes 2 KB
 // of operands, so operand delivery, not arithmetic, bounds this kernel. Both
