@@ -277,9 +277,11 @@ hipError_t launch_w4a16_gemm(const uint16_t* x_t, const uint8_t* w_codes_t,
   const int tiles_m = static_cast<int>((M + kFullM - 1) / kFullM);
   const int tiles_n = static_cast<int>((N + kFullN - 1) / kFullN);
   const int T = tiles_m * tiles_n;
+  // leftover tiles of the last round; quartered when they would fill at most
+  // a quarter of the resident slots
   const int S = resident_slots();
   const int left = T < S ? T : T % S;
-  const int n_quarter_tiles = (left > 0 && 2 * left <= S) ? left : 0;
+  const int n_quarter_tiles = (left > 0 && 4 * left <= S) ? left : 0;
   const int n_full = T - n_quarter_tiles;
   const dim3 grid(static_cast<unsigned>(n_full + 4 * n_quarter_tiles)), block(NT);
   if (y_f16)
