@@ -22,7 +22,7 @@ namespace {
 // kBandM tile rows, column by column: the tiles an XCD holds at one time then
 // share a few A row panels and B column panels, which stay in its L2.
 constexpr int kXcds = 8;
-constexpr int kBandM = 8;
+constexpr int kBandM = 4;   // measured against 2, 8, 16 and 36: 1-2% ahead of 8
 
 __device__ __forceinline__ int xcd_contiguous(int b, int T) {
   const int per = T / kXcds, rem = T % kXcds;
