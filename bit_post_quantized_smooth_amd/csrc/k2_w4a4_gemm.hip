@@ -65,7 +65,9 @@ template <int WT>
 struct Smem {
   v4i a[2][2 * WT / 16][64];        // widened A operands of one group [buf][row block][lane]
   v4i b[2][2 * WT / 16][64];        // widened B operands
-  uint16_t sx[2][2][16][WT / 16];   // activation scales [buf][row/WT][row%16][(row%WT)/16]
+  float sx[2][2][16][WT / 16];      // activation scales [buf][row/WT][row%16][(row%WT)/16], fp32
+  float be[2][2][16][WT / 16];      // -12582912 * each activation scale, same layout
+                                    // (converted once by the loader, not by every wave)
   uint16_t sw[2][2 * WT];           // weight scales [buf][col]
 };
 
@@ -136,8 +138,11 @@ struct Loader {
       dst[rb][e0] = widen_codes(make_uint2(c[0].x, c[0].y));
       dst[rb][e1] = widen_codes(make_uint2(c[0].z, c[0].w));
     }
-    if (t < BT)
-      sm.sx[buf][t / WT][t & 15][(t % WT) >> 4] = sc;
+    if (t < BT) {
+      const float sxf = h2f(sc);
+      sm.sx[buf][t / WT][t & 15][(t % WT) >> 4] = sxf;
+      sm.be[buf][t / WT][t & 15][(t % WT) >> 4] = sxf * -kMagicF;   // exact: 3 * 2^22 * s_x
+    }
     else if (t < 2 * BT)
       sm.sw[buf][t - BT] = sc;
   }
@@ -156,32 +161,29 @@ struct Scales {
 };
 
 template <int WT>
-__device__ __forceinline__ void read_group(Frags<WT / 16>& f, Scales<WT / 16>& sc,
-                                           const Smem<WT>& sm, int buf, int wm, int wn,
-                                           int lane) {
+__device__ __forceinline__ void read_frags(Frags<WT / 16>& f, const Smem<WT>& sm, int buf, int wm,
+                                           int wn, int lane) {
   constexpr int NB = WT / 16;
-  const int q = lane >> 4, rl = lane & 15;
   const int sl = swz(lane);
 #pragma unroll
   for (int i = 0; i < NB; ++i) f.A[i] = sm.a[buf][wm * NB + i][sl];
 #pragma unroll
   for (int j = 0; j < NB; ++j) f.B[j] = sm.b[buf][wn * NB + j][sl];
+}
+
+template <int WT>
+__device__ __forceinline__ void read_scales(Scales<WT / 16>& sc, const Smem<WT>& sm, int buf,
+                                            int wm, int wn, int lane) {
+  constexpr int NB = WT / 16;
+  const int q = lane >> 4, rl = lane & 15;
 #pragma unroll
   for (int j = 0; j < NB; ++j)
     sc.swp[j] = *reinterpret_cast<const uint2*>(&sm.sw[buf][wn * WT + j * 16 + 4 * q]);
-  if constexpr (NB == 4) {
-    const uint2 sxp = *reinterpret_cast<const uint2*>(&sm.sx[buf][wm][rl][0]);
-    sc.sx[0] = h2f(static_cast<uint16_t>(sxp.x & 0xFFFFu));
-    sc.sx[1] = h2f(static_cast<uint16_t>(sxp.x >> 16));
-    sc.sx[2] = h2f(static_cast<uint16_t>(sxp.y & 0xFFFFu));
-    sc.sx[3] = h2f(static_cast<uint16_t>(sxp.y >> 16));
-  } else {
-    const uint32_t sxp = *reinterpret_cast<const uint32_t*>(&sm.sx[buf][wm][rl][0]);
-    sc.sx[0] = h2f(static_cast<uint16_t>(sxp & 0xFFFFu));
-    sc.sx[1] = h2f(static_cast<uint16_t>(sxp >> 16));
-  }
 #pragma unroll
-  for (int i = 0; i < NB; ++i) sc.be[i] = sc.sx[i] * -kMagicF;     // exact: 3 * 2^22 * s_x
+  for (int i = 0; i < NB; ++i) {
+    sc.sx[i] = sm.sx[buf][wm][rl][i];
+    sc.be[i] = sm.be[buf][wm][rl][i];
+  }
 }
 
 template <int NB>
@@ -242,8 +244,9 @@ __device__ __forceinline__ void gemm_tile(
 
   v4i P[NB][NB];
   Frags<NB> f;
-  Scales<NB> cur, nxt;
-  read_group<WT>(f, cur, sm, 0, wm, wn, lane);
+  Scales<NB> cur;
+  read_frags<WT>(f, sm, 0, wm, wn, lane);
+  read_scales<WT>(cur, sm, 0, wm, wn, lane);
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
@@ -256,7 +259,7 @@ __device__ __forceinline__ void gemm_tile(
       ld.store(sm, buf);             // group g+2 replaces group g
       if (g + 3 < G) ld.load(g + 3);
     }
-    read_group<WT>(f, nxt, sm, buf ^ 1, wm, wn, lane);
+    read_frags<WT>(f, sm, buf ^ 1, wm, wn, lane);
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
 #pragma unroll
@@ -272,7 +275,11 @@ __device__ __forceinline__ void gemm_tile(
       __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    cur = nxt;
+    __builtin_amdgcn_sched_barrier(0);
+    // group g+1's scales, read into the same registers once group g's are
+    // used up (no second set, no copies at the end of the iteration; the
+    // barrier ahead of the next iteration's stores waits for these reads)
+    read_scales<WT>(cur, sm, buf ^ 1, wm, wn, lane);
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i)
