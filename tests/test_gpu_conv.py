@@ -110,6 +110,9 @@ EDGE = [
     wl.ConvLayer(1, 4, 4, 64, 33, 5, 5, 1, 2, 16, "f32", "f16", "5x5 on 4x4"),
     wl.ConvLayer(3, 9, 7, 192, 70, 3, 2, 3, 1, 48, "f16", "f16", "s3 3x2"),
     wl.ConvLayer(1, 2, 2, 64, 16, 1, 1, 1, 2, 16, "f32", "f32", "pad only rows"),
+    # 4225 patch rows: more 16-row tiles than CUs, so K1 takes 32 rows per
+    # workgroup, and the last workgroup holds a single row
+    wl.ConvLayer(1, 65, 65, 64, 32, 3, 3, 1, 1, 32, "f16", "f16", "two row tiles"),
 ]
 
 
@@ -270,7 +273,7 @@ def _check_mx_against_linear(L, Xcol, p, bias, tiles, D, Y):
     assert torch.equal(Y.reshape(M, p.N).view(torch.uint8), Y2.view(torch.uint8))
 
 
-MX_EDGE = [EDGE[0], EDGE[1], EDGE[3], EDGE[4], EDGE[5], EDGE[6]]
+MX_EDGE = [EDGE[0], EDGE[1], EDGE[3], EDGE[4], EDGE[5], EDGE[6], EDGE[7]]
 
 
 @pytest.mark.parametrize("L", MX_EDGE, ids=lambda L: "mx_" + L.name.replace(" ", "_"))
