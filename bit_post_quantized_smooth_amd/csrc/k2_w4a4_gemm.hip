@@ -30,18 +30,20 @@
 // Tiling: a 256-thread workgroup computes a square tile of Y; each of its 4
 // waves owns a WT x WT quarter of it (WT/16 x WT/16 blocks of 16 x 16). The
 // matrix instruction takes the weight fragment as its first operand, so a lane
-// ends up holding 4 consecutive columns of one row of each block, which leave
-// in one 8-byte store. The K loop stages one group at a time through
+// ends up holding 4 consecutive columns of one row of each block (a full
+// quarter of an fp16 Y goes out through the then idle LDS in whole cache
+// lines, any other in 8-byte stores). The K loop stages one group at a time through
 // double-buffered LDS; the loader widens the codes once, as it stores them, in
 // operand order: the 16 bytes a lane feeds to the matrix instruction for
 // (row block, group) sit at [buffer][row block][lane], so each operand is one
-// contiguous 16-byte LDS read per lane. The next group's operands are read
+// contiguous 16-byte LDS read per lane; it also converts each activation scale
+// to fp32 once, next to -1.5*2^23 times it. The next group's operands are read
 // while the current group computes.
 //
 // Most tiles are 128 x 128 (WT = 64). When the last round of tiles would
-// leave most of the chip idle (fewer leftover tiles than half the resident
-// workgroup slots), the leftover tiles are cut into 64 x 64 tiles (WT = 32) in
-// the same launch, so the tail takes about a quarter of a round. Every output
+// leave most of the chip idle (leftover tiles filling at most a quarter of the
+// resident workgroup slots), the leftover tiles are cut into 64 x 64 tiles
+// (WT = 32) in the same launch, so the tail takes about a quarter of a round. Every output
 // element goes through the same arithmetic in either size.
 #include <hip/hip_runtime.h>
 
