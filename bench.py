@@ -10,7 +10,13 @@ weights are prepared on the host by the library before timing.
 Prints one JSON line. ``value`` is the effective throughput 2*M*N*K / t of the
 whole step (TOPS); ``roofline`` reports the dominant kernel (K2) against the
 dense INT8 matrix-core peak, timed with HIP events on the stream it runs on;
-``cpu_baseline`` times the CPU oracle on a bounded row sample.
+``clock`` is the shader clock sampled during the timed steps; ``cpu_baseline``
+times the CPU oracle on a bounded row sample.
+
+``--layer all`` times a whole workload instead of one layer: the five UNet
+linears back to back (config 3), the 19-layer LoRA stack as a chain in which
+each layer's output is the next one's input (config 4), or the DiT MLP pair
+(config 2, the same as ``--mlp``).
 """
 from __future__ import annotations
 
@@ -42,6 +48,8 @@ K2_SOURCES = {"int4": [_CSRC + "k2_w4a4_gemm.hip", _CSRC + "k2_common.hpp",
                         _CSRC + "device_common.hpp"],
               "w4a16": [_CSRC + "k2_w4a16_gemm.hip", _CSRC + "k2_common.hpp",
                         _CSRC + "device_common.hpp"]}
+TIMING_NOTE = ("HIP events around each launch in a second pass of the same steps, on the "
+               "launch stream, less the gap of an empty event pair")
 
 
 def k2_source_hash(fmt: str = "int4") -> str:
@@ -58,13 +66,20 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=1, help="workload index (1 = DiT QKV)")
-    ap.add_argument("--layer", type=int, default=0)
+    ap.add_argument("--layer", default="0",
+                    help="layer index, or 'all': the whole workload (config 2: the MLP pair, "
+                         "3: the five UNet linears back to back, 4: the 19-layer chain)")
     ap.add_argument("--sets", type=int, default=4, help="rotating buffer sets (cold MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overhead", action="store_true", help="skip the rank-0 comparison run")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="no shader-clock probe beside the timed steps")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain fp32 copy kernel of known size (for PMC scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="run the step for this long before the counted warm-up steps, so the "
+                         "shader clock has left its idle level (reported as settle_ms)")
     ap.add_argument("--mlp", action="store_true",
                     help="time the DiT MLP pair instead: up-projection with the GELU fused into "
                          "its epilogue, then the down-projection")
@@ -78,6 +93,184 @@ def parse():
                     help="time UNet convolution I instead (NHWC, K1 on the implicit patch matrix, "
                          "then K2; INT4 format)")
     return ap.parse_args()
+
+
+# --------------------------------------------------------------------------
+# timing
+
+
+class ClockProbe:
+    """The shader clock during the timed steps: svdq_clock_probe (one wave on a
+    side stream, sampling the shader-clock cycle counter against the constant
+    wall counter every INTERVAL_US) runs from just before the first timed
+    launch until svdq_clock_mark, queued behind the last timed launch, sets its
+    stop flag. The mark is a one-wave kernel inside the timed window, and the
+    final synchronize waits for the probe to see the flag (at most one
+    interval)."""
+    INTERVAL_US = 10.0
+
+    def __init__(self, torch, sq):
+        self.torch, self.sq = torch, sq
+        self.wall_khz, self.peak_khz = sq.clock_rates()
+        self.ticks = max(1, int(round(self.INTERVAL_US * self.wall_khz / 1000.0)))
+        n = 1 << 18                                       # 2.6 s of samples at 10 us
+        self.samples = torch.zeros(1 + 2 * n, dtype=torch.int64, device="cuda")
+        self.stop = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.stamp = torch.zeros(1, dtype=torch.int64, device="cuda")
+        self.side = torch.cuda.Stream()                   # default priority
+
+    def arm(self):
+        """Before the synchronize that opens the timed window."""
+        self.stop.zero_()
+        self.samples[0].zero_()
+
+    def launch(self):
+        """Right after that synchronize, before the first timed launch."""
+        self.sq.clock_probe(self.samples, self.stop, self.ticks, stream=self.side)
+
+    def end(self):
+        """Right after the last timed launch, before the closing synchronize."""
+        self.sq.clock_mark(self.stamp, self.stop)
+
+    def result(self):
+        s = self.samples.cpu().numpy().view(np.uint64)
+        n = int(s[0])
+        if n < 2:
+            return {"sclk_mhz": None, "samples": n}
+        c = s[1:1 + 2 * n:2].astype(np.float64)
+        w = s[2:2 + 2 * n:2].astype(np.float64)
+        wall_mhz = self.wall_khz / 1000.0
+        mean = (c[-1] - c[0]) / (w[-1] - w[0]) * wall_mhz
+        # per-millisecond windows for the spread
+        step = max(1, int(round(1000.0 / self.INTERVAL_US)))
+        idx = np.arange(0, n, step)
+        if idx[-1] != n - 1:
+            idx = np.append(idx, n - 1)
+        dc, dw = np.diff(c[idx]), np.diff(w[idx])
+        per = dc[dw > 0] / dw[dw > 0] * wall_mhz
+        return {"sclk_mhz": round(float(mean), 1),
+                "sclk_mhz_min_1ms": round(float(per.min()), 1) if per.size else None,
+                "sclk_mhz_max_1ms": round(float(per.max()), 1) if per.size else None,
+                "peak_mhz": round(self.peak_khz / 1000.0, 1),
+                "window_ms": round((w[-1] - w[0]) / self.wall_khz, 3), "samples": n,
+                "how": "shader-clock counter against the constant wall counter, one wave on a "
+                       "side stream during the timed steps"}
+
+
+def settle(torch, runner, ms):
+    """Run whole steps for about `ms` milliseconds (untimed, before the counted
+    warm-up): right after idle the shader clock sits well below its loaded
+    level for longer than a few steps (measured on c1: 1.85 GHz averaged over
+    the first 7 ms against 2.2 GHz once settled)."""
+    if ms <= 0:
+        return 0.0
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for _, f in runner.launches(i):
+            f()
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= ms:
+                break
+    return (time.perf_counter() - t0) * 1e3
+
+
+def time_steps(torch, runner, steps, warmup, probe=None):
+    """Two passes of `steps` steps after `warmup` untimed ones. The first,
+    bracketed by synchronizations, is the step time: plain launches and
+    nothing else on the stream (plus the clock probe's one-wave mark). The
+    second records HIP events around each launch on the launch stream for the
+    per-kernel durations; an event record costs the stream a few microseconds,
+    so that pass is not the step time. Returns (step seconds, launch names,
+    per-launch seconds as a steps x launches array)."""
+    for i in range(warmup):
+        for _, f in runner.launches(i):
+            f()
+    if probe is not None:
+        probe.arm()
+    torch.cuda.synchronize()
+    if probe is not None:
+        probe.launch()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for _, f in runner.launches(i):
+            f()
+    if probe is not None:
+        probe.end()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    names = [n for n, _ in runner.launches(0)]
+    evs = []
+    for i in range(steps):
+        ls = runner.launches(i)
+        es = [torch.cuda.Event(enable_timing=True) for _ in range(len(ls) + 1)]
+        for j, (_, f) in enumerate(ls):
+            es[j].record()
+            f()
+        es[-1].record()
+        evs.append(es)
+    torch.cuda.synchronize()
+    per = np.array([[es[j].elapsed_time(es[j + 1]) for j in range(len(names))] for es in evs])
+    return (t1 - t0) / steps, names, per * 1e-3
+
+
+def event_gap(torch, reps=50):
+    """Median time between two HIP events recorded back to back on the current
+    stream with nothing between them: the overhead one event pair adds to a
+    kernel timed between them."""
+    gaps = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        b.record()
+        gaps.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in gaps])) * 1e-3
+
+
+def kernel_stats(per_col, gap):
+    """(mean, median) seconds of one launch over the event pass, less the event gap."""
+    return float(np.mean(per_col)) - gap, float(np.median(per_col)) - gap
+
+
+def copy_probe(torch):
+    """A plain copy of known size (256 Mi fp32: 1 GiB read + 1 GiB written, more
+    than the last-level cache), whose FETCH_SIZE and WRITE_SIZE counters scale
+    the GEMM's and the pre-kernel's to bytes."""
+    n = 256 << 20
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+
+
+def host_cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return os.cpu_count()
+
+
+# --------------------------------------------------------------------------
+# algorithmic bytes (per launch)
+
+
+def k1_bytes(M, K, R, xb, meta_per_row):
+    """Read X once; write codes, scales (or exponents) and D; read L1 and 1/lambda."""
+    return M * K * xb + M * K // 2 + M * meta_per_row + 4 * M * R + 2 * K * R + 4 * K
+
+
+def k2_bytes(M, N, K, R, yb, meta_per_row):
+    """Codes and scales of both operands, D, L2, Y (bias not counted: zero in the configs)."""
+    return (M + N) * K // 2 + (M + N) * meta_per_row + 4 * M * R + 2 * R * N + M * N * yb
+
+
+# --------------------------------------------------------------------------
+# one layer
 
 
 class Sets:
@@ -120,92 +313,35 @@ class Sets:
                          asc=torch.empty((M, G), dtype=torch.int16, device="cuda"))
             self.sets.append(s)
 
-    def k1(self, i):
+    def k1(self, i, X=None):
         s = self.sets[i % len(self.sets)]
+        X = s["X"] if X is None else X
         if self.w16:
-            self.sq.w4a16_tile_activation(s["X"], s["ac"])
+            self.sq.w4a16_tile_activation(X, s["ac"])
             return
         f = (self.sq.quantize_act_lowrank_down_mx if self.mx
              else self.sq.quantize_act_lowrank_down)
-        f(s["X"], s["inv"], s["L1p"], self.R, s["ac"], s["asc"], s["D"] if self.R else None)
+        f(X, s["inv"], s["L1p"], self.R, s["ac"], s["asc"], s["D"] if self.R else None)
 
-    def k2(self, i):
+    def k2(self, i, Y=None):
         s = self.sets[i % len(self.sets)]
+        Y = s["Y"] if Y is None else Y
         if self.w16:
-            self.sq.w4a16_gemm(s["ac"], s["wc"], s["ws"], s["b"], s["Y"], self.K)
+            self.sq.w4a16_gemm(s["ac"], s["wc"], s["ws"], s["b"], Y, self.K)
             return
         f = self.sq.mx_gemm_lowrank_up if self.mx else self.sq.w4a4_gemm_lowrank_up
         f(s["ac"], s["asc"], s["wc"], s["ws"], s["D"] if self.R else None, s["L2t"], self.R, s["b"],
-          s["Y"], self.K)
+          Y, self.K)
+
+    def launches(self, i):
+        return [("k1", lambda: self.k1(i)), ("k2", lambda: self.k2(i))]
 
 
-def time_steps(torch, sets, steps, warmup):
-    """Two passes of `steps` steps after `warmup` untimed ones. The first,
-    bracketed by synchronizations, is the step time: plain launches and
-    nothing else on the stream. The second records HIP events around each
-    launch on the launch stream for the per-kernel durations; an event record
-    costs the stream a few microseconds, so that pass is not the step time."""
-    for i in range(warmup):
-        sets.k1(i)
-        sets.k2(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        sets.k1(i)
-        sets.k2(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        e0, e1, e2 = ev[i]
-        e0.record()
-        sets.k1(i)
-        e1.record()
-        sets.k2(i)
-        e2.record()
-    torch.cuda.synchronize()
-    k1 = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e-3
-    k2 = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e-3
-    return (t1 - t0) / steps, k1, k2
-
-
-def copy_probe(torch):
-    """A plain copy of known size (256 Mi fp32: 1 GiB read + 1 GiB written, more
-    than the last-level cache), whose FETCH_SIZE and WRITE_SIZE counters scale
-    the GEMM's and the pre-kernel's to bytes."""
-    n = 256 << 20
-    a = torch.ones(n, dtype=torch.float32, device="cuda")
-    b = torch.empty_like(a)
-    for _ in range(5):
-        torch.mul(a, 1.0, out=b)
-    torch.cuda.synchronize()
-
-
-def event_gap(torch, reps=50):
-    """Median time between two HIP events recorded back to back on the current
-    stream with nothing between them: the overhead one event pair adds to a
-    kernel timed between them."""
-    gaps = []
-    for _ in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        b.record()
-        gaps.append((a, b))
-    torch.cuda.synchronize()
-    return float(np.median([a.elapsed_time(b) for a, b in gaps])) * 1e-3
-
-
-def cpu_baseline(X, W, prep, bias, budget_s):
+def cpu_baseline(X, W, prep, bias, budget_s, out_dtype="f16"):
     """The oracle's online part (quantize X, down-projection, integer partials,
     scaled sum, up-projection, bias; or its MXFP4 counterpart) on chunks of rows
-    until ~budget_s seconds."""
+    until ~budget_s seconds. Returns (dict, seconds per row)."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count()
     lam = O.smoothing_factors(O.channel_absmax(X), W)
     inv = O.inv_smoothing(lam)
     mx = prep.fmt == "mxfp4"
@@ -215,7 +351,8 @@ def cpu_baseline(X, W, prep, bias, budget_s):
     elif mx:
         wc, ws = O.mx_quantize_residual_from_factors(W, lam, prep.L1, prep.L2)
     else:
-        wc, ws = O.quantize_residual_from_factors(W, lam, prep.L1, prep.L2)
+        base = prep.rank if getattr(prep, "base_rank", None) is None else prep.base_rank
+        wc, ws = O.quantize_residual_from_factors(W, lam, prep.L1[:, :base], prep.L2[:base])
     M, K = X.shape
     N = W.shape[1]
     chunk = 32
@@ -224,23 +361,272 @@ def cpu_baseline(X, W, prep, bias, budget_s):
     while rows < M and time.perf_counter() - t0 < budget_s:
         r = slice(rows, min(M, rows + chunk))
         if w16:
-            O.w4a16_linear(X[r], wc, ws, bias, "f16")
+            O.w4a16_linear(X[r], wc, ws, bias, out_dtype)
         else:
-            (O.mx_linear if mx else O.linear)(X[r], inv, prep.L1, prep.L2, wc, ws, bias, "f16")
+            (O.mx_linear if mx else O.linear)(X[r], inv, prep.L1, prep.L2, wc, ws, bias, out_dtype)
         rows = r.stop
     t = time.perf_counter() - t0
-    return dict(value=2.0 * rows * N * K / t / 1e12, unit="TFLOPS" if (mx or w16) else "TOPS",
-                cores=int(cores), kind="oracle",
-                sample=f"first {rows} of {M} rows of the same layer, online part only "
-                       f"({t:.1f} s, numpy fp64, chunks of {chunk} rows)")
+    return (dict(value=2.0 * rows * N * K / t / 1e12, unit="TFLOPS" if (mx or w16) else "TOPS",
+                 cores=int(host_cores()), kind="oracle",
+                 sample=f"first {rows} of {M} rows of the same layer, online part only "
+                        f"({t:.1f} s, numpy fp64, chunks of {chunk} rows)"), t / rows)
 
 
-def mlp_main(args, torch, sq, wl):
+def prepare_layer(sq, wl, cfg, li, fmt, rank=None):
+    """(Layer, X, W, lam, prep) with the library's host prep (LoRA concatenated
+    for the configs that carry one); rank overrides the SVD rank (0: bare GEMM)."""
+    L, X, W = wl.layer_inputs(cfg, li)
+    lam = sq.smoothing_factors(sq.channel_absmax(X), W)
+    r = L.rank if rank is None else rank
+    if fmt == "w4a16":
+        return L, X, W, lam, sq.prepare_weights_w4a16(W)
+    prep = (sq.prepare_weights_mx if fmt == "mxfp4" else sq.prepare_weights)(W, lam, r)
+    if L.lora_rank and rank is None:
+        A, B = wl.lora(cfg, li, L.K, L.N, L.lora_rank)
+        base = prep.rank
+        prep = sq.concat_lora(prep, lam, A, B, 1.0)
+        prep.base_rank = base
+    return L, X, W, lam, prep
+
+
+FORMATS = {
+    "int4": dict(metric="effective TOPS of SVDQuant W4A4+rank-32 linear, % of INT8 MFMA peak",
+                 peak=INT8_PEAK_TOPS, unit="TOPS", kname="k2_w4a4_kernel", dtype="int8",
+                 text="INT4 per-64 groups", pct="pct_int8_peak"),
+    "mxfp4": dict(metric="effective TFLOPS of the SVDQuant MXFP4+rank-32 linear, % of FP4 MFMA peak",
+                  peak=FP4_PEAK_TFLOPS, unit="TFLOPS", kname="k2_mx_kernel", dtype="fp4",
+                  text="MXFP4 (E2M1, E8M0 per 32)", pct="pct_fp4_peak"),
+    "w4a16": dict(metric="effective TFLOPS of the 4-bit weight-only (W4A16) baseline linear, "
+                         "% of fp16 MFMA peak",
+                  peak=FP16_PEAK_TFLOPS, unit="TFLOPS", kname="k2_w4a16_kernel", dtype="fp16",
+                  text="W4A16 baseline (INT4 weights per-64 groups, fp16 activations, no "
+                       "low-rank)", pct="pct_fp16_peak"),
+}
+
+
+def meta_bytes(K, fmt):
+    return (K // 32) if fmt == "mxfp4" else 2 * (K // 64)
+
+
+def single_layer_main(args, torch, sq, wl, probe):
+    cfg = wl.CONFIGS[args.config]
+    li = int(args.layer)
+    fmt = args.format
+    F = FORMATS[fmt]
+    L, X, W, lam, prep = prepare_layer(sq, wl, args.config, li, fmt)
+    bias = None
+    M, K, N, R = L.M, L.K, L.N, prep.rank
+    sets = Sets(torch, X, prep, bias, args.sets, L.y_dtype)
+    settled = settle(torch, sets, args.settle_ms)
+    t_step, _, per = time_steps(torch, sets, args.steps, args.warmup, probe)
+    clock = probe.result() if probe is not None else None
+    ops = 2.0 * M * N * K
+    value = ops / t_step / 1e12
+    gap = event_gap(torch)
+    k1_avg, k1_med = kernel_stats(per[:, 0], gap)
+    k2_avg, k2_med = kernel_stats(per[:, 1], gap)
+    xb = 2 if L.x_dtype == "f16" else 4
+    yb = 2 if L.y_dtype == "f16" else 4
+    meta = meta_bytes(K, fmt)
+    if fmt == "w4a16":   # tiling pass: read X, write fp16 tiles; GEMM: fp16 tiles, codes, scales, Y
+        b1 = M * K * xb + 2 * M * K
+        b2 = 2 * M * K + N * K // 2 + N * meta + M * N * yb
+    else:
+        b1 = k1_bytes(M, K, R, xb, meta)
+        b2 = k2_bytes(M, N, K, R, yb, meta)
+
+    traffic = None
+    if os.path.exists(PROFILE_PMC[fmt]):
+        try:
+            with open(PROFILE_PMC[fmt]) as f:
+                pm = json.load(f)
+            if (pm.get("k2_source_hash") == k2_source_hash(fmt)
+                    and pm.get("config") == args.config):
+                traffic = pm.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    overhead = None
+    if not args.no_overhead and R > 0 and fmt != "w4a16":
+        _, _, _, _, prep0 = prepare_layer(sq, wl, args.config, li, fmt, rank=0)
+        sets0 = Sets(torch, X, prep0, bias, args.sets, L.y_dtype)
+        t0_step, _, per0 = time_steps(torch, sets0, args.steps, args.warmup)
+        k2_0 = float(np.median(per0[:, 1])) - gap
+        overhead = dict(step_ms_rank0=t0_step * 1e3, k2_ms_rank0=k2_0 * 1e3,
+                        frac=(t_step - t0_step) / k2_0)
+        del sets0
+
+    if args.copy_probe:
+        copy_probe(torch)
+
+    out = {
+        "metric": F["metric"],
+        "value": round(value, 2),
+        "unit": F["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "settle_ms": round(settled, 1),
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": F["dtype"],
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} layer {li}: X {L.x_dtype} {M}x{K}, "
+                               f"W {K}x{N}, rank {R}, {F['text']}, Y {L.y_dtype}",
+                   "M": M, "K": K, "N": N, "rank": R, "format": fmt,
+                   "buffer_sets": args.sets},
+        F["pct"]: round(100.0 * value / F["peak"], 2),
+        "roofline": {"bound": "mfma", "kernel": F["kname"],
+                     "achieved": round(ops / k2_avg / 1e12, 2), "peak": F["peak"],
+                     "unit": F["unit"], "frac": round(ops / k2_avg / 1e12 / F["peak"], 4),
+                     "traffic": traffic, "algorithmic_bytes": b2,
+                     "avg_ms": round(k2_avg * 1e3, 4), "median_ms": round(k2_med * 1e3, 4),
+                     "frac_median": round(ops / k2_med / 1e12 / F["peak"], 4),
+                     "timing": TIMING_NOTE, "event_gap_us": round(gap * 1e6, 2)},
+        "k1": {"kernel": "tile_x_kernel" if fmt == "w4a16" else "k1_quant_down_kernel",
+               "avg_ms": round(k1_avg * 1e3, 4), "median_ms": round(k1_med * 1e3, 4),
+               "algorithmic_bytes": b1, "achieved_gbs": round(b1 / k1_avg / 1e9, 1),
+               "peak_gbs": HBM_PEAK_GBS, "frac": round(b1 / k1_avg / 1e9 / HBM_PEAK_GBS, 4),
+               "frac_median": round(b1 / k1_med / 1e9 / HBM_PEAK_GBS, 4)},
+        "lowrank_overhead": None if overhead is None else {
+            k: round(v, 4) for k, v in overhead.items()},
+        "clock": clock,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(X, W, prep, bias, args.cpu_seconds, L.y_dtype)[0]
+    return out
+
+
+# --------------------------------------------------------------------------
+# whole workloads
+
+
+class Chain:
+    """A whole workload as one step. chain=True: layer l reads layer l-1's output
+    (the LoRA stack, K = N for every layer); else every layer has its own input
+    (the UNet batch, run back to back)."""
+
+    def __init__(self, torch, layers, n_sets, chain):
+        self.chain = chain
+        self.layers = [Sets(torch, X, prep, None, n_sets if (li == 0 or not chain) else 1,
+                            L.y_dtype) for li, (L, X, prep) in enumerate(layers)]
+        if chain:
+            M, N = layers[0][0].M, layers[0][0].N
+            self.act = [torch.empty((M, N), dtype=torch.float16, device="cuda") for _ in range(2)]
+
+    def launches(self, i):
+        out = []
+        for li, s in enumerate(self.layers):
+            if self.chain and li > 0:
+                x_in, y_out = self.act[(li - 1) % 2], self.act[li % 2]
+                out.append((f"k1[{li}]", lambda s=s, x=x_in: s.k1(0, X=x)))
+                out.append((f"k2[{li}]", lambda s=s, y=y_out: s.k2(0, Y=y)))
+            elif self.chain:
+                y0 = self.act[0]
+                out.append((f"k1[{li}]", lambda s=s, i=i: s.k1(i)))
+                out.append((f"k2[{li}]", lambda s=s, i=i, y=y0: s.k2(i, Y=y)))
+            else:
+                out.append((f"k1[{li}]", lambda s=s, i=i: s.k1(i)))
+                out.append((f"k2[{li}]", lambda s=s, i=i: s.k2(i)))
+        return out
+
+
+def whole_config_main(args, torch, sq, wl, probe):
+    cfg = wl.CONFIGS[args.config]
+    fmt = args.format
+    if fmt == "w4a16":
+        raise SystemExit("--layer all runs the INT4 or MXFP4 format")
+    F = FORMATS[fmt]
+    chain = args.config == 4
+    prepped = [prepare_layer(sq, wl, args.config, li, fmt) for li in range(len(cfg.layers))]
+    layers = [(L, X, prep) for (L, X, W, lam, prep) in prepped]
+    runner = Chain(torch, layers, args.sets, chain)
+    settled = settle(torch, runner, args.settle_ms)
+    t_step, names, per = time_steps(torch, runner, args.steps, args.warmup, probe)
+    clock = probe.result() if probe is not None else None
+    gap = event_gap(torch)
+    ops_total = sum(2.0 * L.M * L.N * L.K for L, _, _ in layers)
+    rows, k2_total, k2_total_med = [], 0.0, 0.0
+    for li, (L, X, prep) in enumerate(layers):
+        M, K, N, R = L.M, L.K, L.N, prep.rank
+        k1_avg, k1_med = kernel_stats(per[:, 2 * li], gap)
+        k2_avg, k2_med = kernel_stats(per[:, 2 * li + 1], gap)
+        k2_total += k2_avg
+        k2_total_med += k2_med
+        xb = 2 if L.x_dtype == "f16" else 4
+        yb = 2 if L.y_dtype == "f16" else 4
+        meta = meta_bytes(K, fmt)
+        b1 = k1_bytes(M, K, R, xb, meta)
+        b2 = k2_bytes(M, N, K, R, yb, meta)
+        ops = 2.0 * M * N * K
+        attainable = min(F["peak"], ops / b2 * HBM_PEAK_GBS / 1e3)   # TOPS at 8 TB/s
+        rows.append({"layer": li, "M": M, "K": K, "N": N, "rank": R,
+                     "k1_us": round(k1_med * 1e6, 2), "k2_us": round(k2_med * 1e6, 2),
+                     "k2_tops": round(ops / k2_med / 1e12, 1),
+                     "k2_pct_peak": round(100.0 * ops / k2_med / 1e12 / F["peak"], 2),
+                     "k2_attainable": round(attainable, 1),
+                     "k2_pct_attainable": round(100.0 * ops / k2_med / 1e12 / attainable, 2),
+                     "k1_gbs": round(b1 / k1_med / 1e9, 1),
+                     "k1_pct_hbm": round(100.0 * b1 / k1_med / 1e9 / HBM_PEAK_GBS, 2)})
+    overhead = None
+    if not args.no_overhead:
+        p0 = [prepare_layer(sq, wl, args.config, li, fmt, rank=0) for li in range(len(cfg.layers))]
+        runner0 = Chain(torch, [(L, X, prep) for (L, X, W, lam, prep) in p0], args.sets, chain)
+        t0_step, _, per0 = time_steps(torch, runner0, args.steps, args.warmup)
+        k2_0 = sum(float(np.median(per0[:, 2 * li + 1])) - gap for li in range(len(p0)))
+        overhead = dict(step_ms_rank0=t0_step * 1e3, k2_ms_rank0=k2_0 * 1e3,
+                        frac=(t_step - t0_step) / k2_0)
+        del runner0
+    value = ops_total / t_step / 1e12
+    desc = ("19 chained layers (each output is the next input)" if chain else
+            f"{len(layers)} layers back to back")
+    out = {
+        "metric": F["metric"].replace("linear", f"workload ({desc})"),
+        "value": round(value, 2), "unit": F["unit"], "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "settle_ms": round(settled, 1),
+        "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": F["dtype"], "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {desc}; {cfg.note}", "format": fmt,
+                   "layers": len(layers), "buffer_sets": args.sets},
+        F["pct"]: round(100.0 * value / F["peak"], 2),
+        "roofline": {"bound": "mfma", "kernel": F["kname"] + " (all layers)",
+                     "achieved": round(ops_total / k2_total / 1e12, 2), "peak": F["peak"],
+                     "unit": F["unit"], "frac": round(ops_total / k2_total / 1e12 / F["peak"], 4),
+                     "frac_median": round(ops_total / k2_total_med / 1e12 / F["peak"], 4),
+                     "traffic": None, "timing": TIMING_NOTE,
+                     "event_gap_us": round(gap * 1e6, 2)},
+        "layers": rows,
+        "lowrank_overhead": None if overhead is None else {
+            k: round(v, 4) for k, v in overhead.items()},
+        "clock": clock,
+    }
+    if not args.no_cpu_baseline:
+        # the oracle on a row sample of each distinct layer shape, scaled to the whole workload
+        t_cpu, desc_cpu, seen = 0.0, [], {}
+        budget = args.cpu_seconds / (1 if chain else len(prepped))
+        for li, (L, X, W, lam, prep) in enumerate(prepped):
+            key = (L.M, L.K, L.N)
+            if chain and key in seen:
+                t_cpu += seen[key]
+                continue
+            d, per_row = cpu_baseline(X, W, prep, None, budget, L.y_dtype)
+            seen[key] = per_row * L.M
+            t_cpu += per_row * L.M
+            desc_cpu.append(d["sample"])
+        out["cpu_baseline"] = dict(value=ops_total / t_cpu / 1e12, unit=F["unit"],
+                                   cores=int(host_cores()), kind="oracle",
+                                   sample="; ".join(desc_cpu) + " -- scaled to every row of every "
+                                          "layer (rows are independent)")
+    return out
+
+
+def mlp_main(args, torch, sq, wl, probe):
     """Step = the DiT MLP pair on one batch: K1 + K2 (+GELU) of the up-projection
     4608 x 3072 -> 12288, then K1 + K2 of the down-projection 12288 -> 3072."""
-    (Lu, Xu, Wu), (Ld, _, Wd) = wl.layer_inputs(2, 0), wl.layer_inputs(2, 1)
-    import oracle as O   # input synthesis only: GELU of the seeded pre-activations
-    Xd_cal = O.gelu_tanh(wl.preactivation(2, 1, Ld.M, Ld.K, Ld.x_outlier_frac, Ld.x_outlier_scale))
+    Lu, Xu, Wu = wl.layer_inputs(2, 0)
+    Ld, Xd_cal, Wd = wl.layer_inputs(2, 1)
     lam_u = sq.smoothing_factors(sq.channel_absmax(Xu), Wu)
     lam_d = sq.smoothing_factors(sq.channel_absmax(Xd_cal), Wd)
     up = sq.Linear(sq.prepare_weights(Wu, lam_u, Lu.rank),
@@ -251,43 +637,40 @@ def mlp_main(args, torch, sq, wl):
     H = [torch.empty((Lu.M, Lu.N), dtype=torch.float16, device="cuda") for _ in range(n)]
     Y = [torch.empty((Ld.M, Ld.N), dtype=torch.float16, device="cuda") for _ in range(n)]
 
-    def step(i):
-        j = i % n
-        up(X[j], H[j])
-        if args.unfused_gelu:
-            sq.gelu_tanh_f16(H[j], H[j])
-        down(H[j], Y[j])
+    class _Runner:
+        def launches(self, i):
+            j = i % n
+            ls = [("up", lambda: up(X[j], H[j]))]
+            if args.unfused_gelu:
+                ls.append(("gelu", lambda: sq.gelu_tanh_f16(H[j], H[j])))
+            ls.append(("down", lambda: down(H[j], Y[j])))
+            return ls
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    t = (time.perf_counter() - t0) / args.steps
+    settled = settle(torch, _Runner(), args.settle_ms)
+    t, names, per = time_steps(torch, _Runner(), args.steps, args.warmup, probe)
+    clock = probe.result() if probe is not None else None
+    gap = event_gap(torch)
     ops = 2.0 * Lu.M * Lu.N * Lu.K + 2.0 * Ld.M * Ld.N * Ld.K
     value = ops / t / 1e12
-    print(json.dumps({
+    return {
         "metric": "effective TOPS of the DiT MLP pair (SVDQuant W4A4+rank-32 up, GELU, down)",
         "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(t * 1e3, 4), "higher_is_better": True,
+        "warmup": args.warmup, "settle_ms": round(settled, 1),
+        "ms_per_step": round(t * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
         "config": {"workload": "dit_mlp: X f16 4608x3072 -> 12288 (GELU-tanh) -> 3072, rank 32",
                    "gelu": "separate kernel" if args.unfused_gelu else "fused into the up epilogue",
                    "buffer_sets": n},
-        "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2)}), flush=True)
+        "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
+        "launch_median_us": {nm: round((float(np.median(per[:, j])) - gap) * 1e6, 2)
+                             for j, nm in enumerate(names)},
+        "clock": clock}
 
 
 def conv_cpu_baseline(L, X, Wm, prep, bias, budget_s):
     """The oracle's convolution (im2col of the whole image, then its linear layer
     on chunks of patch rows) until ~budget_s seconds."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count()
     t0 = time.perf_counter()
     Xcol = O.im2col_nhwc(X, L.KH, L.KW, L.stride, L.pad)
     lam = O.smoothing_factors(O.channel_absmax(Xcol), Wm)
@@ -307,14 +690,14 @@ def conv_cpu_baseline(L, X, Wm, prep, bias, budget_s):
         rows = r.stop
     t = time.perf_counter() - t0
     return dict(value=2.0 * rows * L.N * L.K / t / 1e12, unit="TFLOPS" if mx else "TOPS",
-                cores=int(cores),
+                cores=int(host_cores()),
                 kind="oracle",
                 sample=f"first {rows} of {L.M} output pixels of the same convolution, online "
                        f"part only ({t:.1f} s, numpy fp64, chunks of {chunk}; the im2col and "
                        f"calibration before it took {t_setup:.1f} s and are not counted)")
 
 
-def conv_main(args, torch, sq, wl):
+def conv_main(args, torch, sq, wl, probe):
     """Step = one UNet convolution on one batch: K1 on the implicit patch matrix
     of the NHWC image, then K2 (the same kernels as svdq_conv2d, or with
     --format mxfp4 their MXFP4 versions, as svdq_conv2d_mx)."""
@@ -349,64 +732,62 @@ def conv_main(args, torch, sq, wl):
     k1f = sq.quantize_act_lowrank_down_conv_mx if mx else sq.quantize_act_lowrank_down_conv
     k2f = sq.mx_gemm_lowrank_up if mx else sq.w4a4_gemm_lowrank_up
 
-    class _Step:
-        def k1(self, i):
+    class _Runner:
+        def launches(self, i):
             s = sets[i % len(sets)]
-            k1f(s["X"], L.KH, L.KW, L.stride, L.pad, s["inv"], s["L1p"], R, s["ac"], s["asc"],
-                s["D"])
+            return [("k1", lambda: k1f(s["X"], L.KH, L.KW, L.stride, L.pad, s["inv"], s["L1p"], R,
+                                       s["ac"], s["asc"], s["D"])),
+                    ("k2", lambda: k2f(s["ac"], s["asc"], s["wc"], s["ws"], s["D"], s["L2t"], R,
+                                       s["b"], s["Y"].view(M, N), K))]
 
-        def k2(self, i):
-            s = sets[i % len(sets)]
-            k2f(s["ac"], s["asc"], s["wc"], s["ws"], s["D"], s["L2t"], R, s["b"],
-                s["Y"].view(M, N), K)
-
-    t_step, t1, t2 = time_steps(torch, _Step(), args.steps, args.warmup)
+    settled = settle(torch, _Runner(), args.settle_ms)
+    t_step, _, per = time_steps(torch, _Runner(), args.steps, args.warmup, probe)
+    clock = probe.result() if probe is not None else None
     gap = event_gap(torch)
-    k1_avg = float(np.mean(t1)) - gap
-    k2_avg = float(np.mean(t2)) - gap
+    k1_avg, k1_med = kernel_stats(per[:, 0], gap)
+    k2_avg, k2_med = kernel_stats(per[:, 1], gap)
     ops = 2.0 * M * N * K
     value = ops / t_step / 1e12
     xb = 2 if L.x_dtype == "f16" else 4
     yb = 2 if L.y_dtype == "f16" else 4
     img = L.batch * L.H * L.W * L.C
-    meta = (K // 32) if mx else 2 * (K // 64)           # exponent or scale bytes per row
+    meta = meta_bytes(K, args.format)
     # K1: the image once, the patch matrix's codes, scales (or exponents) and D out
-    k1_bytes = img * xb + M * K // 2 + M * meta + 4 * M * R + 2 * K * R + 4 * K
-    k2_bytes = (M + N) * K // 2 + (M + N) * meta + 4 * M * R + 2 * R * N + M * N * yb
-    peak, unit, kname, dtype = ((FP4_PEAK_TFLOPS, "TFLOPS", "k2_mx_kernel", "fp4") if mx else
-                                (INT8_PEAK_TOPS, "TOPS", "k2_w4a4_kernel", "int8"))
-    fmt_txt = "MXFP4 (E2M1, E8M0 per 32)" if mx else "INT4 per-64 groups"
+    b1 = img * xb + M * K // 2 + M * meta + 4 * M * R + 2 * K * R + 4 * K
+    b2 = k2_bytes(M, N, K, R, yb, meta)
+    F = FORMATS[args.format]
+    fmt_txt = F["text"]
     out = {
-        "metric": (f"effective {unit} of an SVDQuant {'MXFP4' if mx else 'W4A4'}+rank-32 UNet "
+        "metric": (f"effective {F['unit']} of an SVDQuant {'MXFP4' if mx else 'W4A4'}+rank-32 UNet "
                    f"convolution (implicit GEMM), % of {'FP4' if mx else 'INT8'} MFMA peak"),
-        "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "value": round(value, 2), "unit": F["unit"], "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "settle_ms": round(settled, 1),
+        "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": F["dtype"], "data": "synthetic",
         "config": {"workload": f"{L.name}: X {L.x_dtype} NHWC {L.batch}x{L.H}x{L.W}x{L.C}, "
                                f"{L.KH}x{L.KW} stride {L.stride} pad {L.pad} -> {N} channels "
                                f"(patch matrix {M}x{K}), rank {R}, {fmt_txt}, Y {L.y_dtype}",
                    "M": M, "K": K, "N": N, "rank": R, "format": args.format,
                    "buffer_sets": args.sets},
-        ("pct_fp4_peak" if mx else "pct_int8_peak"): round(100.0 * value / peak, 2),
-        "roofline": {"bound": "mfma", "kernel": kname,
-                     "achieved": round(ops / k2_avg / 1e12, 2), "peak": peak,
-                     "unit": unit, "frac": round(ops / k2_avg / 1e12 / peak, 4),
-                     "traffic": None, "algorithmic_bytes": k2_bytes,
-                     "avg_ms": round(k2_avg * 1e3, 4),
-                     "timing": "HIP events around each launch in a second pass of the same "
-                               "steps, on the launch stream, less the gap of an empty "
-                               "event pair",
-                     "event_gap_us": round(gap * 1e6, 2)},
+        F["pct"]: round(100.0 * value / F["peak"], 2),
+        "roofline": {"bound": "mfma", "kernel": F["kname"],
+                     "achieved": round(ops / k2_avg / 1e12, 2), "peak": F["peak"],
+                     "unit": F["unit"], "frac": round(ops / k2_avg / 1e12 / F["peak"], 4),
+                     "traffic": None, "algorithmic_bytes": b2,
+                     "avg_ms": round(k2_avg * 1e3, 4), "median_ms": round(k2_med * 1e3, 4),
+                     "timing": TIMING_NOTE, "event_gap_us": round(gap * 1e6, 2)},
         "k1": {"kernel": "k1_quant_down_kernel (convolution instance)",
-               "avg_ms": round(k1_avg * 1e3, 4), "algorithmic_bytes": k1_bytes,
-               "achieved_gbs": round(k1_bytes / k1_avg / 1e9, 1), "peak_gbs": HBM_PEAK_GBS,
-               "frac": round(k1_bytes / k1_avg / 1e9 / HBM_PEAK_GBS, 4)},
+               "avg_ms": round(k1_avg * 1e3, 4), "median_ms": round(k1_med * 1e3, 4),
+               "algorithmic_bytes": b1,
+               "achieved_gbs": round(b1 / k1_avg / 1e9, 1), "peak_gbs": HBM_PEAK_GBS,
+               "frac": round(b1 / k1_avg / 1e9 / HBM_PEAK_GBS, 4)},
+        "clock": clock,
     }
     if args.copy_probe:
         copy_probe(torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = conv_cpu_baseline(L, X, Wm, prep, bias, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    return out
 
 
 def main():
@@ -420,119 +801,19 @@ def main():
     import bit_post_quantized_smooth_amd as sq
     import workloads as wl
 
-    if args.mlp:
-        mlp_main(args, torch, sq, wl)
-        return
-    if args.conv is not None:
-        conv_main(args, torch, sq, wl)
-        return
-    cfg = wl.CONFIGS[args.config]
-    L = cfg.layers[args.layer]
-    Lx, X, W = wl.layer_inputs(args.config, args.layer)
-    if X is None:
-        import oracle as O   # input synthesis only: GELU of the seeded pre-activations
-        X = O.gelu_tanh(wl.preactivation(args.config, args.layer, L.M, L.K, L.x_outlier_frac,
-                                         L.x_outlier_scale))
-    bias = None
-    lam = sq.smoothing_factors(sq.channel_absmax(X), W)
-    mx = args.format == "mxfp4"
-    w16 = args.format == "w4a16"
-    prepare = sq.prepare_weights_mx if mx else sq.prepare_weights
-    prep = sq.prepare_weights_w4a16(W) if w16 else prepare(W, lam, L.rank)
-    if L.lora_rank and not w16:
-        A, B = wl.lora(args.config, args.layer, L.K, L.N, L.lora_rank)
-        prep = sq.concat_lora(prep, lam, A, B, 1.0)
-    M, K, N, R = L.M, L.K, L.N, prep.rank
-    sets = Sets(torch, X, prep, bias, args.sets, L.y_dtype)
-    t_step, k1, k2 = time_steps(torch, sets, args.steps, args.warmup)
-    ops = 2.0 * M * N * K
-    value = ops / t_step / 1e12
-    gap = event_gap(torch)
-    k1_avg = float(np.mean(k1)) - gap
-    k2_avg = float(np.mean(k2)) - gap
-    xb = 2 if L.x_dtype == "f16" else 4
-    yb = 2 if L.y_dtype == "f16" else 4
-    meta = (K // 32) if mx else 2 * (K // 64)          # exponent or scale bytes per row
-    if w16:   # tiling pass: read X, write fp16 tiles; GEMM: fp16 tiles, codes, scales, Y
-        k1_bytes = M * K * xb + 2 * M * K
-        k2_bytes = 2 * M * K + N * K // 2 + N * meta + M * N * yb
+    probe = None if args.no_clock else ClockProbe(torch, sq)
+    if args.mlp or (args.layer == "all" and args.config == 2):
+        out = mlp_main(args, torch, sq, wl, probe)
+    elif args.conv is not None:
+        out = conv_main(args, torch, sq, wl, probe)
+    elif args.layer == "all" and len(wl.CONFIGS[args.config].layers) > 1:
+        out = whole_config_main(args, torch, sq, wl, probe)
     else:
-        k1_bytes = M * K * xb + M * K // 2 + M * meta + 4 * M * R + 2 * K * R + 4 * K
-        k2_bytes = (M + N) * K // 2 + (M + N) * meta + 4 * M * R + 2 * R * N + M * N * yb
-
-    traffic = None
-    if os.path.exists(PROFILE_PMC[args.format]):
-        try:
-            pm = json.load(open(PROFILE_PMC[args.format]))
-            if (pm.get("k2_source_hash") == k2_source_hash(args.format)
-                    and pm.get("config") == args.config):
-                traffic = pm.get("hbm_bytes_per_launch")
-        except Exception:
-            traffic = None
-
-    overhead = None
-    if not args.no_overhead and R > 0 and not w16:
-        prep0 = prepare(W, lam, 0)
-        sets0 = Sets(torch, X, prep0, bias, args.sets, L.y_dtype)
-        t0_step, _, k2_0 = time_steps(torch, sets0, args.steps, args.warmup)
-        k2_0 = float(np.mean(k2_0)) - gap
-        overhead = dict(step_ms_rank0=t0_step * 1e3, k2_ms_rank0=k2_0 * 1e3,
-                        frac=(t_step - t0_step) / k2_0)
-        del sets0
-
-    if args.copy_probe:
-        copy_probe(torch)
-
-    if w16:
-        metric = "effective TFLOPS of the 4-bit weight-only (W4A16) baseline linear, % of fp16 MFMA peak"
-        peak, unit, kname, dtype = FP16_PEAK_TFLOPS, "TFLOPS", "k2_w4a16_kernel", "fp16"
-        fmt_txt = "W4A16 baseline (INT4 weights per-64 groups, fp16 activations, no low-rank)"
-    elif mx:
-        metric = "effective TFLOPS of the SVDQuant MXFP4+rank-32 linear, % of FP4 MFMA peak"
-        peak, unit, kname, dtype = FP4_PEAK_TFLOPS, "TFLOPS", "k2_mx_kernel", "fp4"
-        fmt_txt = "MXFP4 (E2M1, E8M0 per 32)"
-    else:
-        metric = "effective TOPS of SVDQuant W4A4+rank-32 linear, % of INT8 MFMA peak"
-        peak, unit, kname, dtype = INT8_PEAK_TOPS, "TOPS", "k2_w4a4_kernel", "int8"
-        fmt_txt = "INT4 per-64 groups"
-    out = {
-        "metric": metric,
-        "value": round(value, 2),
-        "unit": unit,
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(t_step * 1e3, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": dtype,
-        "data": "synthetic",
-        "config": {"workload": f"{cfg.name} layer {args.layer}: X {L.x_dtype} {M}x{K}, "
-                               f"W {K}x{N}, rank {R}, {fmt_txt}, Y {L.y_dtype}",
-                   "M": M, "K": K, "N": N, "rank": R, "format": args.format,
-                   "buffer_sets": args.sets},
-        ("pct_fp16_peak" if w16 else "pct_fp4_peak" if mx else "pct_int8_peak"):
-            round(100.0 * value / peak, 2),
-        "roofline": {"bound": "mfma", "kernel": kname,
-                     "achieved": round(ops / k2_avg / 1e12, 2), "peak": peak,
-                     "unit": unit, "frac": round(ops / k2_avg / 1e12 / peak, 4),
-                     "traffic": traffic, "algorithmic_bytes": k2_bytes,
-                     "avg_ms": round(k2_avg * 1e3, 4),
-                     "timing": "HIP events around each launch in a second pass of the same "
-                               "steps, on the launch stream, less the gap of an empty "
-                               "event pair",
-                     "event_gap_us": round(gap * 1e6, 2)},
-        "k1": {"kernel": "tile_x_kernel" if w16 else "k1_quant_down_kernel",
-               "avg_ms": round(k1_avg * 1e3, 4),
-               "algorithmic_bytes": k1_bytes, "achieved_gbs": round(k1_bytes / k1_avg / 1e9, 1),
-               "peak_gbs": HBM_PEAK_GBS, "frac": round(k1_bytes / k1_avg / 1e9 / HBM_PEAK_GBS, 4)},
-        "lowrank_overhead": None if overhead is None else {
-            k: round(v, 4) for k, v in overhead.items()},
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(X, W, prep, bias, args.cpu_seconds)
+        if args.layer == "all":
+            args.layer = "0"
+        out = single_layer_main(args, torch, sq, wl, probe)
     print(json.dumps(out), flush=True)
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

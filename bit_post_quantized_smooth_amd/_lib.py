@@ -89,6 +89,9 @@ _SIGS = {
                               _p, _i32, _p, _p, _p, _p, _int, _i64, _p, C.c_size_t, _i32, _p]),
     "svdq_debug_group_partials": (_int, [_p, _p, _i64, _i64, _i64, _i32, _i64, _i64, _p, _p]),
     "svdq_gelu_tanh_f16": (_int, [_p, _p, _i64, _p]),
+    "svdq_clock_rates": (_int, [_p, _p]),
+    "svdq_clock_probe": (_int, [_p, _i32, _i64, _p, _p]),
+    "svdq_clock_mark": (_int, [_p, _p, _p]),
 }
 
 for _name, (_res, _args) in _SIGS.items():

@@ -205,11 +205,11 @@ int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth
   clear_error();
   const char* fn = "svdq_linear";
   if (int s = check_activation(activation, fn)) return s;
+  if (int s = check_common(M, K, R, group, fn)) return s;
   if (!ws) {
     set_error("%s: null workspace", fn);
     return SVDQ_ERR_NULL;
   }
-  if (int s = check_common(M, K, R, group, fn)) return s;
   const WsLayout L = ws_layout(M, K, R, false);
   if (ws_bytes < L.total) {
     set_error("%s: workspace %zu bytes < %zu needed", fn, ws_bytes, L.total);
@@ -588,6 +588,69 @@ int svdq_debug_group_partials(const uint8_t* a_codes, const uint8_t* w_codes, in
   if (int s = device_ready()) return s;
   return check_hip(launch_debug_partials(a_codes, w_codes, M, N, K, row0, rows, P, stream),
                    "svdq_debug_group_partials launch");
+}
+
+int svdq_clock_rates(int32_t* wall_khz, int32_t* peak_khz) {
+  clear_error();
+  if (!wall_khz || !peak_khz) {
+    set_error("svdq_clock_rates: null pointer");
+    return SVDQ_ERR_NULL;
+  }
+  if (int s = device_ready()) return s;
+  int dev = 0;
+  if (int s = check_hip(hipGetDevice(&dev), "svdq_clock_rates")) return s;
+  int w = 0, c = 0;
+  if (int s = check_hip(hipDeviceGetAttribute(&w, hipDeviceAttributeWallClockRate, dev),
+                        "svdq_clock_rates wall clock"))
+    return s;
+  if (int s = check_hip(hipDeviceGetAttribute(&c, hipDeviceAttributeClockRate, dev),
+                        "svdq_clock_rates shader clock"))
+    return s;
+  *wall_khz = w;
+  *peak_khz = c;
+  return SVDQ_OK;
+}
+
+int svdq_clock_probe(uint64_t* samples, int32_t max_samples, int64_t interval_ticks,
+                     const int32_t* stop, hipStream_t stream) {
+  clear_error();
+  const char* fn = "svdq_clock_probe";
+  if (!samples || !stop) {
+    set_error("%s: null pointer", fn);
+    return SVDQ_ERR_NULL;
+  }
+  if ((reinterpret_cast<uintptr_t>(samples) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(stop) & 3u) != 0) {
+    set_error("%s: samples must be 8-byte and stop 4-byte aligned", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  int32_t wall = 0, peak = 0;
+  if (int s = svdq_clock_rates(&wall, &peak)) return s;
+  // at most 10 ms between samples and 60 s in all, in ticks of the wall counter
+  const int64_t per_ms = wall > 0 ? wall : 100000;
+  if (max_samples < 1 || max_samples > (1 << 20) || interval_ticks < 1 ||
+      interval_ticks > 10 * per_ms || interval_ticks * max_samples > 60000 * per_ms) {
+    set_error("%s: max_samples=%d interval=%lld out of range", fn, max_samples,
+              (long long)interval_ticks);
+    return SVDQ_ERR_SHAPE;
+  }
+  return check_hip(launch_clock_probe(samples, max_samples, interval_ticks, stop, stream),
+                   "svdq_clock_probe launch");
+}
+
+int svdq_clock_mark(uint64_t* stamp, int32_t* stop, hipStream_t stream) {
+  clear_error();
+  if (!stamp) {
+    set_error("svdq_clock_mark: null pointer");
+    return SVDQ_ERR_NULL;
+  }
+  if ((reinterpret_cast<uintptr_t>(stamp) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(stop) & 3u) != 0) {
+    set_error("svdq_clock_mark: stamp must be 8-byte and stop 4-byte aligned");
+    return SVDQ_ERR_ALIGN;
+  }
+  if (int s = device_ready()) return s;
+  return check_hip(launch_clock_mark(stamp, stop, stream), "svdq_clock_mark launch");
 }
 
 int svdq_gelu_tanh_f16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream) {

@@ -49,4 +49,9 @@ hipError_t launch_debug_partials(const uint8_t* a_codes, const uint8_t* w_codes,
 
 hipError_t launch_gelu_f16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream);
 
+// Measurement utility: shader-clock samples (see clock_probe.hip).
+hipError_t launch_clock_probe(uint64_t* samples, int32_t max_samples, int64_t interval,
+                              const int32_t* stop, hipStream_t stream);
+hipError_t launch_clock_mark(uint64_t* stamp, int32_t* stop, hipStream_t stream);
+
 }  // namespace svdq

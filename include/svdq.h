@@ -435,6 +435,32 @@ int svdq_debug_group_partials(const uint8_t* a_codes, const uint8_t* w_codes, in
  * in fp32 from fp16 and rounded to fp16. x and y may be the same buffer. */
 int svdq_gelu_tanh_f16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Measurement utilities (not part of the method): the shader clock during a
+ * timed region. The pages give no hardware figures; the rooflines are priced
+ * at the chip's peak clock, so a benchmark reports the clock it actually ran at.
+ */
+
+/* Host: the constant rate of the device's wall counter and the peak shader
+ * clock, both in kHz (HIP device attributes of the current device). */
+int svdq_clock_rates(int32_t* wall_khz, int32_t* peak_khz);
+
+/* Device: one wave that, every `interval_ticks` ticks of the wall counter,
+ * stores the pair (shader-clock cycle counter, wall counter) at
+ * samples[1 + 2i], samples[2 + 2i], until *stop is nonzero (read with
+ * agent-scope atomics) or max_samples pairs are stored; samples[0] = the
+ * number stored. samples: device memory of 1 + 2*max_samples uint64 (8-byte
+ * aligned); stop: device int32 (4-byte aligned), zero before the launch.
+ * Limits: 1 <= max_samples <= 2^20, interval at most 10 ms and
+ * max_samples * interval at most 60 s of wall ticks, so the wave always ends.
+ * Launch it on a stream other than the timed one. */
+int svdq_clock_probe(uint64_t* samples, int32_t max_samples, int64_t interval_ticks,
+                     const int32_t* stop, hipStream_t stream);
+
+/* Device: one wave that stores the wall counter at *stamp and, if stop is not
+ * NULL, sets *stop = 1 (ending a running svdq_clock_probe). */
+int svdq_clock_mark(uint64_t* stamp, int32_t* stop, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,8 +41,6 @@ def layer(cfg: int, li: int, with_bias: bool = False, use_lora: bool = True):
 def _layer(cfg: int, li: int, use_lora: bool):
     import bit_post_quantized_smooth_amd as sq
     L, X, W = wl.layer_inputs(cfg, li)
-    if X is None:          # input of a down-projection: GELU of seeded pre-activations
-        X = O.gelu_tanh(wl.preactivation(cfg, li, L.M, L.K, L.x_outlier_frac, L.x_outlier_scale))
     lam = sq.smoothing_factors(sq.channel_absmax(X), W)
     p = sq.prepare_weights(W, lam, L.rank)
     if L.lora_rank and use_lora:

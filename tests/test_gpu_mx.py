@@ -35,8 +35,6 @@ def _gpu():
 def _mx_layer(cfg: int, li: int):
     import bit_post_quantized_smooth_amd as sq
     L, X, W = wl.layer_inputs(cfg, li)
-    if X is None:
-        X = O.gelu_tanh(wl.preactivation(cfg, li, L.M, L.K, L.x_outlier_frac, L.x_outlier_scale))
     lam = sq.smoothing_factors(sq.channel_absmax(X), W)
     p = sq.prepare_weights_mx(W, lam, L.rank)
     if L.lora_rank:

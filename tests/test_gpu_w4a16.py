@@ -35,8 +35,6 @@ def _gpu():
 def _layer(cfg: int, li: int):
     import bit_post_quantized_smooth_amd as sq
     L, X, W = wl.layer_inputs(cfg, li)
-    if X is None:
-        X = O.gelu_tanh(wl.preactivation(cfg, li, L.M, L.K, L.x_outlier_frac, L.x_outlier_scale))
     return L, X, W, sq.prepare_weights_w4a16(W)
 
 

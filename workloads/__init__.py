@@ -18,8 +18,8 @@ item on supported architectures):
   drawn without replacement, multiplied by an outlier factor (x20 at 1%);
 * weights W ~ N(0, 0.02^2) in fp32, with the same count of input rows
   (drawn independently of X's channels) multiplied by x10;
-* pre-activations for a down-projection: N(0, 1) with 0.5% channels x15
-  (the consumer applies GELU-tanh to them);
+* pre-activations for a down-projection: N(0, 1) with 0.5% channels x15,
+  passed through GELU-tanh (``post_gelu_activation``);
 * LoRA factors A (K x rl) and B (rl x N) ~ N(0, 0.01^2), stored as fp16.
 """
 from __future__ import annotations
@@ -47,7 +47,7 @@ class Layer:
     w_outlier_frac: float = 0.01
     w_outlier_scale: float = 10.0
     lora_rank: int = 0            # extra rank concatenated onto the SVD factors
-    preact: bool = False          # X = GELU_tanh(Z) with Z drawn by ``preactivation``
+    preact: bool = False          # X = post_gelu_activation(...): GELU_tanh of ``preactivation``
 
 
 @dataclasses.dataclass(frozen=True)
@@ -113,6 +113,18 @@ def preactivation(cfg: int, layer: int, M: int, K: int, frac: float = 0.005,
     return z.astype(np.float16)
 
 
+def post_gelu_activation(cfg: int, layer: int, M: int, K: int, frac: float = 0.005,
+                         scale: float = 15.0) -> np.ndarray:
+    """X (M x K) fp16 for the down-projection of an MLP: the seeded pre-activations
+    of ``preactivation`` through the tanh form of GELU, evaluated in fp64 and
+    rounded once to fp16. This is only the input distribution (a heavy positive
+    tail from the outlier channels, negatives bounded near -0.17); the GELU the
+    layers run between them is the library's."""
+    z = preactivation(cfg, layer, M, K, frac, scale).astype(np.float64)
+    u = np.sqrt(2.0 / np.pi) * (z + 0.044715 * z * z * z)
+    return (0.5 * z * (1.0 + np.tanh(u))).astype(np.float16)
+
+
 def weight(cfg: int, layer: int, K: int, N: int, frac: float = 0.01,
            scale: float = 10.0) -> np.ndarray:
     """W (K x N) fp32: N(0, 0.02^2) with ``outlier_count(K, frac)`` input rows times ``scale``."""
@@ -135,14 +147,13 @@ def lora(cfg: int, layer: int, K: int, N: int, rl: int = 64, std: float = 0.01):
 
 
 def layer_inputs(cfg: int, layer_idx: int = 0):
-    """Convenience: (Layer, X or None, W) for one layer of a config.
-
-    For a layer whose input is a GELU output, X is None: the caller draws
-    ``preactivation`` and applies its own GELU."""
+    """Convenience: (Layer, X, W) for one layer of a config. For a layer whose
+    input is a GELU output, X is ``post_gelu_activation``."""
     L = CONFIGS[cfg].layers[layer_idx]
     W = weight(cfg, layer_idx, L.K, L.N, L.w_outlier_frac, L.w_outlier_scale)
     if L.preact:
-        return L, None, W
+        return L, post_gelu_activation(cfg, layer_idx, L.M, L.K, L.x_outlier_frac,
+                                       L.x_outlier_scale), W
     X = activation(cfg, layer_idx, L.M, L.K, L.x_dtype, L.x_outlier_frac, L.x_outlier_scale)
     return L, X, W
 
