@@ -5,7 +5,8 @@ include/svdq.h); this package is its thin Python binding. Importing it
 without a built library raises ImportError.
 """
 from . import _lib  # noqa: F401  (fails loudly when libsvdq.so is missing)
-from .api import (Conv2d, Linear, Prepared, channel_absmax, concat_lora,  # noqa: F401
+from .api import (Conv2d, Linear, Prepared, channel_absmax, clock_mark, clock_probe,  # noqa: F401
+                  clock_rates, concat_lora,
                   conv2d, conv2d_mx, conv_out_size, conv_patch_absmax, debug_group_partials,
                   gelu_tanh_f16, linear, linear_mx, linear_mx_workspace_bytes,
                   linear_workspace_bytes, mx_codes_tiled_bytes, mx_exps_tiled_bytes,
@@ -16,7 +17,8 @@ from .api import (Conv2d, Linear, Prepared, channel_absmax, concat_lora,  # noqa
                   quantize_act_lowrank_down_mx, smoothing_factors, w4a4_gemm_lowrank_up,
                   w4a16_gemm, w4a16_tile_activation, w4a16_x_tiled_bytes, linear_w4a16)
 
-__all__ = ["Conv2d", "Linear", "Prepared", "channel_absmax", "concat_lora", "conv2d", "conv2d_mx",
+__all__ = ["Conv2d", "Linear", "Prepared", "channel_absmax", "clock_mark", "clock_probe",
+           "clock_rates", "concat_lora", "conv2d", "conv2d_mx",
            "conv_out_size", "conv_patch_absmax", "debug_group_partials",
            "gelu_tanh_f16", "linear", "linear_mx", "linear_mx_workspace_bytes",
            "linear_workspace_bytes", "mx_codes_tiled_bytes", "mx_exps_tiled_bytes",

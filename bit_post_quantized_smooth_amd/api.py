@@ -191,6 +191,13 @@ def concat_lora(prep: Prepared, lam: np.ndarray, A: np.ndarray, B: np.ndarray,
 
 # --------------------------------------------------------------------------
 # device entry points (torch tensors)
+#
+# The kernels trust the shapes they are given: a weight buffer shorter than
+# K and N imply, or an output narrower than the layer, would be read or
+# written past its end. So every entry point checks, before the library call,
+# that each tensor's shape, dtype, size and strides agree with the others,
+# then that all of them sit on one GPU (that check comes last, so the others
+# can be exercised without a GPU). Violations raise ValueError or TypeError.
 
 
 def _torch():
@@ -217,8 +224,106 @@ def _dt(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+_BYTES = ("uint8", "int8")
+_HALF = ("float16", "int16", "uint16")        # fp16 values or their bit patterns
+_F32 = ("float32",)
+_XY = ("float16", "float32")
+
+
+def _dtname(t) -> str:
+    return str(t.dtype).replace("torch.", "")
+
+
+def _buf(name, t, dtypes, nbytes=None, min_bytes=None, contiguous=True):
+    """A flat buffer: dtype in `dtypes`, exactly `nbytes` or at least `min_bytes`."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if _dtname(t) not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    size = t.numel() * t.element_size()
+    if nbytes is not None and size != nbytes:
+        raise ValueError(f"{name}: {size} bytes, expected {nbytes}")
+    if min_bytes is not None and size < min_bytes:
+        raise ValueError(f"{name}: {size} bytes, at least {min_bytes} needed")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t
+
+
+def _mat(name, t, rows, cols, dtypes=_XY):
+    """A row-major matrix of `rows` x `cols` with unit inner stride (any row stride >= cols)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if _dtname(t) not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() != 2 or (rows is not None and t.shape[0] != rows) or (
+            cols is not None and t.shape[1] != cols):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected ({rows}, {cols})")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name}: the inner stride must be 1, got {t.stride(1)}")
+    if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+        raise ValueError(f"{name}: row stride {t.stride(0)} < {t.shape[1]} columns")
+    return t
+
+
+def _on_gpu(*ts):
+    devs = {(t.device.type, t.device.index) for t in ts if t is not None}
+    if any(d[0] != "cuda" for d in devs):
+        raise ValueError("every tensor must be on a GPU (device memory)")
+    if len(devs) > 1:
+        raise ValueError(f"tensors on several devices: {sorted(devs)}")
+
+
+def _groups(K: int) -> int:
+    if K < GROUP or K % GROUP:
+        raise ValueError(f"K={K}: need a positive multiple of {GROUP}")
+    return K // GROUP
+
+
+def _bias(bias, N):
+    if bias is not None:
+        _buf("bias", bias, _F32, nbytes=4 * N)
+
+
+def _act_side(M, K, R, a_codes, a_scales, D, mx=False):
+    """Checks of the activation-side buffers written by K1 and read by K2."""
+    G = _groups(K)
+    if mx:
+        _buf("a_codes_t", a_codes, _BYTES, min_bytes=mx_codes_tiled_bytes(M, K))
+        _buf("a_exps_t", a_scales, _BYTES, min_bytes=mx_exps_tiled_bytes(M, K))
+    else:
+        _buf("a_codes", a_codes, _BYTES, min_bytes=M * K // 2)
+        _buf("a_scales", a_scales, _HALF, min_bytes=2 * M * G)
+    if R:
+        _buf("D", D, _F32, min_bytes=4 * M * R)
+
+
+def _weights(N, K, R, w_codes, w_scales, L2t, mx=False):
+    G = _groups(K)
+    if mx:
+        _buf("w_codes_t", w_codes, _BYTES, nbytes=mx_codes_tiled_bytes(N, K))
+        _buf("w_exps_t", w_scales, _BYTES, nbytes=mx_exps_tiled_bytes(N, K))
+    else:
+        _buf("w_codes", w_codes, _BYTES, nbytes=N * K // 2)
+        _buf("w_scales", w_scales, _HALF, nbytes=2 * N * G)
+    if R:
+        _buf("L2t", L2t, _HALF, nbytes=2 * N * R)
+
+
+def _down(K, R, inv_smooth, L1p):
+    _buf("inv_smooth", inv_smooth, _F32, nbytes=4 * K)
+    if R:
+        _buf("L1p", L1p, _HALF, nbytes=2 * R * K)
+
+
 def quantize_act_lowrank_down(X, inv_smooth, L1p, R: int, a_codes, a_scales, D, stream=None):
+    _mat("X", X, None, None)
     M, K = X.shape
+    _down(K, R, inv_smooth, L1p)
+    _act_side(M, K, R, a_codes, a_scales, D)
+    _on_gpu(X, inv_smooth, L1p if R else None, a_codes, a_scales, D if R else None)
     check(lib.svdq_quantize_act_lowrank_down(_tp(X), _dt(X), M, K, X.stride(0), _tp(inv_smooth),
                                              _tp(L1p) if R else None, R, GROUP, _tp(a_codes),
                                              _tp(a_scales), _tp(D) if R else None, _stream(stream)),
@@ -235,7 +340,12 @@ def _act(activation) -> int:
 
 def w4a4_gemm_lowrank_up(a_codes, a_scales, w_codes, w_scales, D, L2t, R: int, bias, Y, K: int,
                          stream=None, activation=None):
+    _mat("Y", Y, None, None)
     M, N = Y.shape
+    _act_side(M, K, R, a_codes, a_scales, D)
+    _weights(N, K, R, w_codes, w_scales, L2t)
+    _bias(bias, N)
+    _on_gpu(a_codes, a_scales, w_codes, w_scales, D if R else None, L2t if R else None, bias, Y)
     check(lib.svdq_w4a4_gemm_lowrank_up(_tp(a_codes), _tp(a_scales), _tp(w_codes), _tp(w_scales),
                                         _tp(D) if R else None, _tp(L2t) if R else None, R, _tp(bias),
                                         _tp(Y), _dt(Y), M, N, K, Y.stride(0), GROUP,
@@ -247,10 +357,21 @@ def linear_workspace_bytes(M: int, K: int, R: int) -> int:
     return int(lib.svdq_linear_workspace_bytes(M, K, R, GROUP))
 
 
+def _layer_io(X, Y, K=None, N=None):
+    _mat("X", X, None, K)
+    M = X.shape[0]
+    _mat("Y", Y, M, N)
+    return M, X.shape[1], Y.shape[1]
+
+
 def linear(X, inv_smooth, L1p, L2t, R: int, w_codes, w_scales, bias, Y, ws, stream=None,
            activation=None):
-    M, K = X.shape
-    N = Y.shape[1]
+    M, K, N = _layer_io(X, Y)
+    _down(K, R, inv_smooth, L1p)
+    _weights(N, K, R, w_codes, w_scales, L2t)
+    _bias(bias, N)
+    _buf("ws", ws, _BYTES + _HALF + _F32, min_bytes=linear_workspace_bytes(M, K, R))
+    _on_gpu(X, inv_smooth, L1p if R else None, L2t if R else None, w_codes, w_scales, bias, Y, ws)
     check(lib.svdq_linear(_tp(X), _dt(X), X.stride(0), _tp(inv_smooth), _tp(L1p) if R else None,
                           _tp(L2t) if R else None, R, _tp(w_codes), _tp(w_scales), _tp(bias), _tp(Y),
                           _dt(Y), Y.stride(0), M, K, N, GROUP, _tp(ws), ws.numel() * ws.element_size(),
@@ -260,7 +381,11 @@ def linear(X, inv_smooth, L1p, L2t, R: int, w_codes, w_scales, bias, Y, ws, stre
 def quantize_act_lowrank_down_mx(X, inv_smooth, L1p, R: int, a_codes_t, a_exps_t, D, stream=None):
     """K1-MX; a_codes_t / a_exps_t: device buffers of mx_codes_tiled_bytes(M, K) and
     mx_exps_tiled_bytes(M, K) bytes (tiled layouts)."""
+    _mat("X", X, None, None)
     M, K = X.shape
+    _down(K, R, inv_smooth, L1p)
+    _act_side(M, K, R, a_codes_t, a_exps_t, D, mx=True)
+    _on_gpu(X, inv_smooth, L1p if R else None, a_codes_t, a_exps_t, D if R else None)
     check(lib.svdq_quantize_act_lowrank_down_mx(_tp(X), _dt(X), M, K, X.stride(0), _tp(inv_smooth),
                                                 _tp(L1p) if R else None, R, _tp(a_codes_t),
                                                 _tp(a_exps_t), _tp(D) if R else None,
@@ -271,7 +396,12 @@ def quantize_act_lowrank_down_mx(X, inv_smooth, L1p, R: int, a_codes_t, a_exps_t
 def mx_gemm_lowrank_up(a_codes_t, a_exps_t, w_codes_t, w_exps_t, D, L2t, R: int, bias, Y, K: int,
                        stream=None, activation=None):
     """K2-MX on the tiled activation and weight codes and exponents."""
+    _mat("Y", Y, None, None)
     M, N = Y.shape
+    _act_side(M, K, R, a_codes_t, a_exps_t, D, mx=True)
+    _weights(N, K, R, w_codes_t, w_exps_t, L2t, mx=True)
+    _bias(bias, N)
+    _on_gpu(a_codes_t, a_exps_t, w_codes_t, w_exps_t, D if R else None, L2t if R else None, bias, Y)
     check(lib.svdq_mx_gemm_lowrank_up(_tp(a_codes_t), _tp(a_exps_t), _tp(w_codes_t), _tp(w_exps_t),
                                       _tp(D) if R else None, _tp(L2t) if R else None, R, _tp(bias),
                                       _tp(Y), _dt(Y), M, N, K, Y.stride(0), _act(activation),
@@ -286,8 +416,13 @@ def linear_mx_workspace_bytes(M: int, K: int, R: int) -> int:
 def linear_mx(X, inv_smooth, L1p, L2t, R: int, w_codes_t, w_exps_t, bias, Y, ws, stream=None,
               activation=None):
     """The whole MXFP4 layer; the weights in the tiled layouts (pack_mx_tiles)."""
-    M, K = X.shape
-    N = Y.shape[1]
+    M, K, N = _layer_io(X, Y)
+    _down(K, R, inv_smooth, L1p)
+    _weights(N, K, R, w_codes_t, w_exps_t, L2t, mx=True)
+    _bias(bias, N)
+    _buf("ws", ws, _BYTES + _HALF + _F32, min_bytes=linear_mx_workspace_bytes(M, K, R))
+    _on_gpu(X, inv_smooth, L1p if R else None, L2t if R else None, w_codes_t, w_exps_t, bias, Y,
+            ws)
     check(lib.svdq_linear_mx(_tp(X), _dt(X), X.stride(0), _tp(inv_smooth),
                              _tp(L1p) if R else None, _tp(L2t) if R else None, R, _tp(w_codes_t),
                              _tp(w_exps_t), _tp(bias), _tp(Y), _dt(Y), Y.stride(0), M, K, N, _tp(ws),
@@ -299,23 +434,43 @@ def w4a16_x_tiled_bytes(M: int, K: int) -> int:
     return int(lib.svdq_w4a16_x_tiled_bytes(M, K))
 
 
+def _w4a16_weights(N, K, w_codes_t, w_scales_t):
+    _groups(K)
+    _buf("w_codes_t", w_codes_t, _BYTES, nbytes=int(lib.svdq_w4a16_codes_tiled_bytes(N, K)))
+    _buf("w_scales_t", w_scales_t, _HALF, nbytes=int(lib.svdq_w4a16_scales_tiled_bytes(N, K)))
+
+
 def w4a16_tile_activation(X, x_t, stream=None):
     """X (fp16 or fp32, M x K) -> x_t (w4a16_x_tiled_bytes(M, K) bytes), the tiled fp16 layout."""
+    _mat("X", X, None, None)
     M, K = X.shape
+    _groups(K)
+    _buf("x_t", x_t, _BYTES + _HALF, min_bytes=w4a16_x_tiled_bytes(M, K))
+    _on_gpu(X, x_t)
     check(lib.svdq_w4a16_tile_activation(_tp(X), _dt(X), M, K, X.stride(0), _tp(x_t),
                                          _stream(stream)), "svdq_w4a16_tile_activation")
 
 
 def w4a16_gemm(x_t, w_codes_t, w_scales_t, bias, Y, K: int, stream=None):
+    _mat("Y", Y, None, None)
     M, N = Y.shape
+    _groups(K)
+    _buf("x_t", x_t, _BYTES + _HALF, min_bytes=w4a16_x_tiled_bytes(M, K))
+    _w4a16_weights(N, K, w_codes_t, w_scales_t)
+    _bias(bias, N)
+    _on_gpu(x_t, w_codes_t, w_scales_t, bias, Y)
     check(lib.svdq_w4a16_gemm(_tp(x_t), _tp(w_codes_t), _tp(w_scales_t), _tp(bias), _tp(Y), _dt(Y),
                               M, N, K, Y.stride(0), _stream(stream)), "svdq_w4a16_gemm")
 
 
 def linear_w4a16(X, w_codes_t, w_scales_t, bias, Y, ws, stream=None):
     """The weight-only baseline layer (tiling of X into ws, then the GEMM)."""
-    M, K = X.shape
-    N = Y.shape[1]
+    M, K, N = _layer_io(X, Y)
+    _groups(K)
+    _w4a16_weights(N, K, w_codes_t, w_scales_t)
+    _bias(bias, N)
+    _buf("ws", ws, _BYTES + _HALF + _F32, min_bytes=w4a16_x_tiled_bytes(M, K))
+    _on_gpu(X, w_codes_t, w_scales_t, bias, Y, ws)
     check(lib.svdq_linear_w4a16(_tp(X), _dt(X), X.stride(0), _tp(w_codes_t), _tp(w_scales_t),
                                 _tp(bias), _tp(Y), _dt(Y), Y.stride(0), M, K, N, _tp(ws),
                                 ws.numel() * ws.element_size(), _stream(stream)),
@@ -344,10 +499,47 @@ def conv_patch_absmax(X: np.ndarray, KH: int, KW: int, stride: int, pad: int) ->
     return out
 
 
+def _image(X):
+    torch = _torch()
+    if not isinstance(X, torch.Tensor):
+        raise TypeError(f"X: expected a torch tensor, got {type(X).__name__}")
+    if _dtname(X) not in _XY:
+        raise ValueError(f"X: dtype {X.dtype}, expected one of {_XY}")
+    if X.dim() != 4 or not X.is_contiguous():
+        raise ValueError(f"X: expected a contiguous NHWC image, got shape {tuple(X.shape)}")
+    return X.shape
+
+
+def _conv_shape(X, KH, KW, stride, pad):
+    B, H, W, Cc = _image(X)
+    if min(KH, KW, stride) < 1 or pad < 0:
+        raise ValueError(f"kernel {KH}x{KW}, stride {stride}, pad {pad}")
+    OH, OW = conv_out_size(H, KH, stride, pad), conv_out_size(W, KW, stride, pad)
+    if OH < 1 or OW < 1:
+        raise ValueError(f"empty output: {OH} x {OW}")
+    return B, H, W, Cc, OH, OW, B * OH * OW, KH * KW * Cc
+
+
+def _conv_out(Y, B, OH, OW, N=None):
+    torch = _torch()
+    if not isinstance(Y, torch.Tensor):
+        raise TypeError(f"Y: expected a torch tensor, got {type(Y).__name__}")
+    if _dtname(Y) not in _XY:
+        raise ValueError(f"Y: dtype {Y.dtype}, expected one of {_XY}")
+    if Y.dim() != 4 or tuple(Y.shape[:3]) != (B, OH, OW) or (N is not None and Y.shape[3] != N) \
+            or not Y.is_contiguous():
+        raise ValueError(f"Y: expected a contiguous ({B}, {OH}, {OW}, N) output, got "
+                         f"{tuple(Y.shape)}")
+    return Y.shape[3]
+
+
 def quantize_act_lowrank_down_conv(X, KH: int, KW: int, stride: int, pad: int, inv_smooth, L1p,
                                    R: int, a_codes, a_scales, D, stream=None):
     """K1 on the patch matrix of the NHWC image X (batch x H x W x C, contiguous)."""
-    B, H, W, Cc = X.shape
+    B, H, W, Cc, OH, OW, M, K = _conv_shape(X, KH, KW, stride, pad)
+    _down(K, R, inv_smooth, L1p)
+    _act_side(M, K, R, a_codes, a_scales, D)
+    _on_gpu(X, inv_smooth, L1p if R else None, a_codes, a_scales, D if R else None)
     check(lib.svdq_quantize_act_lowrank_down_conv(
         _tp(X), _dt(X), B, H, W, Cc, KH, KW, stride, pad, _tp(inv_smooth),
         _tp(L1p) if R else None, R, _tp(a_codes), _tp(a_scales), _tp(D) if R else None,
@@ -357,8 +549,13 @@ def quantize_act_lowrank_down_conv(X, KH: int, KW: int, stride: int, pad: int, i
 def conv2d(X, KH: int, KW: int, stride: int, pad: int, inv_smooth, L1p, L2t, R: int, w_codes,
            w_scales, bias, Y, ws, stream=None, activation=None):
     """The whole convolution: Y (batch x OH x OW x N, contiguous) from the NHWC image X."""
-    B, H, W, Cc = X.shape
-    N = Y.shape[-1]
+    B, H, W, Cc, OH, OW, M, K = _conv_shape(X, KH, KW, stride, pad)
+    N = _conv_out(Y, B, OH, OW)
+    _down(K, R, inv_smooth, L1p)
+    _weights(N, K, R, w_codes, w_scales, L2t)
+    _bias(bias, N)
+    _buf("ws", ws, _BYTES + _HALF + _F32, min_bytes=linear_workspace_bytes(M, K, R))
+    _on_gpu(X, inv_smooth, L1p if R else None, L2t if R else None, w_codes, w_scales, bias, Y, ws)
     check(lib.svdq_conv2d(_tp(X), _dt(X), B, H, W, Cc, KH, KW, stride, pad, _tp(inv_smooth),
                           _tp(L1p) if R else None, _tp(L2t) if R else None, R, _tp(w_codes),
                           _tp(w_scales), _tp(bias), _tp(Y), _dt(Y), N, _tp(ws),
@@ -369,7 +566,10 @@ def conv2d(X, KH: int, KW: int, stride: int, pad: int, inv_smooth, L1p, L2t, R: 
 def quantize_act_lowrank_down_conv_mx(X, KH: int, KW: int, stride: int, pad: int, inv_smooth,
                                       L1p, R: int, a_codes_t, a_exps_t, D, stream=None):
     """K1-MX on the patch matrix of the NHWC image X: tiled codes and exponents, D."""
-    B, H, W, Cc = X.shape
+    B, H, W, Cc, OH, OW, M, K = _conv_shape(X, KH, KW, stride, pad)
+    _down(K, R, inv_smooth, L1p)
+    _act_side(M, K, R, a_codes_t, a_exps_t, D, mx=True)
+    _on_gpu(X, inv_smooth, L1p if R else None, a_codes_t, a_exps_t, D if R else None)
     check(lib.svdq_quantize_act_lowrank_down_conv_mx(
         _tp(X), _dt(X), B, H, W, Cc, KH, KW, stride, pad, _tp(inv_smooth),
         _tp(L1p) if R else None, R, _tp(a_codes_t), _tp(a_exps_t), _tp(D) if R else None,
@@ -379,8 +579,14 @@ def quantize_act_lowrank_down_conv_mx(X, KH: int, KW: int, stride: int, pad: int
 def conv2d_mx(X, KH: int, KW: int, stride: int, pad: int, inv_smooth, L1p, L2t, R: int,
               w_codes_t, w_exps_t, bias, Y, ws, stream=None, activation=None):
     """The whole convolution in MXFP4 (tiled weights): Y (batch x OH x OW x N) from X."""
-    B, H, W, Cc = X.shape
-    N = Y.shape[-1]
+    B, H, W, Cc, OH, OW, M, K = _conv_shape(X, KH, KW, stride, pad)
+    N = _conv_out(Y, B, OH, OW)
+    _down(K, R, inv_smooth, L1p)
+    _weights(N, K, R, w_codes_t, w_exps_t, L2t, mx=True)
+    _bias(bias, N)
+    _buf("ws", ws, _BYTES + _HALF + _F32, min_bytes=linear_mx_workspace_bytes(M, K, R))
+    _on_gpu(X, inv_smooth, L1p if R else None, L2t if R else None, w_codes_t, w_exps_t, bias, Y,
+            ws)
     check(lib.svdq_conv2d_mx(_tp(X), _dt(X), B, H, W, Cc, KH, KW, stride, pad, _tp(inv_smooth),
                              _tp(L1p) if R else None, _tp(L2t) if R else None, R, _tp(w_codes_t),
                              _tp(w_exps_t), _tp(bias), _tp(Y), _dt(Y), N, _tp(ws),
@@ -390,11 +596,47 @@ def conv2d_mx(X, KH: int, KW: int, stride: int, pad: int, inv_smooth, L1p, L2t, 
 
 def debug_group_partials(a_codes, w_codes, M: int, N: int, K: int, row0: int, rows: int, P,
                          stream=None):
+    G = _groups(K)
+    _buf("a_codes", a_codes, _BYTES, min_bytes=M * K // 2)
+    _buf("w_codes", w_codes, _BYTES, min_bytes=N * K // 2)
+    _buf("P", P, ("int32",), min_bytes=4 * max(rows, 0) * N * G)
+    _on_gpu(a_codes, w_codes, P)
     check(lib.svdq_debug_group_partials(_tp(a_codes), _tp(w_codes), M, N, K, GROUP, row0, rows,
                                         _tp(P), _stream(stream)), "svdq_debug_group_partials")
 
 
+def clock_rates():
+    """(wall counter rate, peak shader clock), both in kHz, of the current device."""
+    import ctypes as C
+    w, c = C.c_int32(0), C.c_int32(0)
+    check(lib.svdq_clock_rates(C.byref(w), C.byref(c)), "svdq_clock_rates")
+    return int(w.value), int(c.value)
+
+
+def clock_probe(samples, stop, interval_ticks: int, stream=None):
+    """Shader-clock sampler (one wave) on `stream`; samples: int64 device tensor of
+    1 + 2*n entries, stop: int32 device tensor (zero), see svdq_clock_probe."""
+    _buf("samples", samples, ("int64", "uint64"), min_bytes=24)
+    _buf("stop", stop, ("int32",), min_bytes=4)
+    _on_gpu(samples, stop)
+    n = (samples.numel() - 1) // 2
+    check(lib.svdq_clock_probe(_tp(samples), n, int(interval_ticks), _tp(stop), _stream(stream)),
+          "svdq_clock_probe")
+
+
+def clock_mark(stamp, stop=None, stream=None):
+    """Store the wall counter at stamp[0] and, if given, set stop to end a probe."""
+    _buf("stamp", stamp, ("int64", "uint64"), min_bytes=8)
+    if stop is not None:
+        _buf("stop", stop, ("int32",), min_bytes=4)
+    _on_gpu(stamp, stop)
+    check(lib.svdq_clock_mark(_tp(stamp), _tp(stop), _stream(stream)), "svdq_clock_mark")
+
+
 def gelu_tanh_f16(x, y, stream=None):
+    _buf("x", x, ("float16",))
+    _buf("y", y, ("float16",), min_bytes=2 * x.numel())
+    _on_gpu(x, y)
     check(lib.svdq_gelu_tanh_f16(_tp(x), _tp(y), x.numel(), _stream(stream)), "svdq_gelu_tanh_f16")
 
 
@@ -447,7 +689,10 @@ class Linear:
 
     def __call__(self, X, Y=None, stream=None):
         torch = _torch()
+        _mat("X", X, None, self.K)
         M = X.shape[0]
+        if Y is not None:
+            _mat("Y", Y, M, self.N)
         if Y is None:
             Y = torch.empty((M, self.N), dtype=self.out_dtype or X.dtype, device=self.device)
         if self.fmt == "w4a16":
