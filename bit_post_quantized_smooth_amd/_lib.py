@@ -35,6 +35,7 @@ F16, F32 = 1, 2
 GROUP = 64
 MX_BLOCK = 32
 MAX_RANK = 256
+NOALLOC_MAX_BYTES = 64 << 20
 
 _p = C.c_void_p
 _i64 = C.c_int64
@@ -62,6 +63,8 @@ _SIGS = {
                                                  _p, _p]),
     "svdq_mx_gemm_lowrank_up": (_int, [_p, _p, _p, _p, _p, _p, _i32, _p, _p, _int, _i64, _i64,
                                        _i64, _i64, _i32, _p]),
+    "svdq_linear_noalloc": (_int, [_p, _int, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _int, _i64,
+                                   _i64, _i64, _i64, _i32, _i32, _p]),
     "svdq_linear_mx_workspace_bytes": (C.c_size_t, [_i64, _i64, _i32]),
     "svdq_mx_codes_tiled_bytes": (C.c_size_t, [_i64, _i64]),
     "svdq_mx_exps_tiled_bytes": (C.c_size_t, [_i64, _i64]),

@@ -378,6 +378,22 @@ def linear(X, inv_smooth, L1p, L2t, R: int, w_codes, w_scales, bias, Y, ws, stre
                           _act(activation), _stream(stream)), "svdq_linear")
 
 
+def linear_noalloc(X, inv_smooth, L1p, L2t, R: int, w_codes, w_scales, bias, Y, stream=None,
+                   activation=None):
+    """svdq_linear with the intermediates in the library's static device buffer
+    (no workspace, no allocation; calls that overlap on one GPU race)."""
+    M, K, N = _layer_io(X, Y)
+    _down(K, R, inv_smooth, L1p)
+    _weights(N, K, R, w_codes, w_scales, L2t)
+    _bias(bias, N)
+    _on_gpu(X, inv_smooth, L1p if R else None, L2t if R else None, w_codes, w_scales, bias, Y)
+    check(lib.svdq_linear_noalloc(_tp(X), _dt(X), X.stride(0), _tp(inv_smooth),
+                                  _tp(L1p) if R else None, _tp(L2t) if R else None, R,
+                                  _tp(w_codes), _tp(w_scales), _tp(bias), _tp(Y), _dt(Y),
+                                  Y.stride(0), M, K, N, GROUP, _act(activation), _stream(stream)),
+          "svdq_linear_noalloc")
+
+
 def quantize_act_lowrank_down_mx(X, inv_smooth, L1p, R: int, a_codes_t, a_exps_t, D, stream=None):
     """K1-MX; a_codes_t / a_exps_t: device buffers of mx_codes_tiled_bytes(M, K) and
     mx_exps_tiled_bytes(M, K) bytes (tiled layouts)."""

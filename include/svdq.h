@@ -229,6 +229,28 @@ int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth
                 int64_t M, int64_t K, int64_t N, int32_t group, void* ws, size_t ws_bytes,
                 int32_t activation, hipStream_t stream);
 
+/* Largest intermediate size svdq_linear_noalloc handles (bytes of
+ * svdq_linear_workspace_bytes): 64 MiB, enough for every layer shape used
+ * here (the DiT MLP down-projection needs 31 MB, the largest UNet
+ * convolution 54 MB). */
+#define SVDQ_NOALLOC_MAX_BYTES (64u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): svdq_linear
+ * with its intermediates (activation codes, scales, D) in a static device
+ * buffer of SVDQ_NOALLOC_MAX_BYTES that the library holds on each GPU it runs
+ * on until the process ends, instead of a caller workspace. Same arguments,
+ * results and checks as svdq_linear otherwise. Returns SVDQ_ERR_WORKSPACE (and
+ * launches nothing) when svdq_linear_workspace_bytes(M, K, R, group) exceeds
+ * the buffer. It calls no allocator. Every call on one GPU shares that GPU's
+ * buffer: calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialized by the caller. */
+int svdq_linear_noalloc(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
+                        const uint16_t* L1p, const uint16_t* L2t, int32_t R,
+                        const uint8_t* w_codes, const uint16_t* w_scales, const float* bias,
+                        void* Y, int y_dtype, int64_t ldy, int64_t M, int64_t K, int64_t N,
+                        int32_t group, int32_t activation, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * MXFP4 format (the CDNA4 counterpart of the 4-bit floating-point version of
  * the method that the taicenter.com news page names for the newest hardware,

@@ -485,3 +485,17 @@ def test_device_entry_points_report_no_device():
     need_cm = L.svdq_linear_mx_workspace_bytes(64, 576, 16)
     assert L.svdq_conv2d_mx(A16, 1, *geo, A16, A16, A16, 16, A16, A16, None, A16, 1, 16, 0x10000,
                             need_cm, 0, None) == _lib.ERR_NO_DEVICE
+
+
+def test_noalloc_rejects_layers_beyond_its_buffer():
+    """svdq_linear_noalloc refuses, before any HIP call, a layer whose
+    intermediates exceed its static buffer, and reports bad sizes as svdq_linear."""
+    lib = _lib.lib
+    M, K = 1 << 20, 4096                       # 2 GiB of codes alone
+    assert lib.svdq_linear_workspace_bytes(M, K, 0, 64) > _lib.NOALLOC_MAX_BYTES
+    s = lib.svdq_linear_noalloc(None, _lib.F16, K, None, None, None, 0, None, None, None, None,
+                                _lib.F16, 64, M, K, 64, 64, 0, None)
+    assert s == _lib.ERR_WORKSPACE and "static buffer" in _lib.last_error()
+    s = lib.svdq_linear_noalloc(None, _lib.F16, 64, None, None, None, 0, None, None, None, None,
+                                _lib.F16, 64, 16, 60, 64, 64, 0, None)
+    assert s == _lib.ERR_GROUP and _lib.last_error().startswith("svdq_linear_noalloc")
