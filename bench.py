@@ -39,11 +39,14 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 # HBM traffic of the GEMM kernel from committed rocprofv3 FETCH/WRITE passes,
 # used only while the kernel's sources are unchanged since they were taken
 PROFILE_PMC = {"int4": os.path.join(ROOT, "profiles", "k2_dit_qkv_pmc.json"),
+               "int4t": os.path.join(ROOT, "profiles", "k2t_dit_qkv_pmc.json"),
                "mxfp4": os.path.join(ROOT, "profiles", "k2mx_dit_qkv_pmc.json"),
                "w4a16": os.path.join(ROOT, "profiles", "k2w16_dit_qkv_pmc.json")}
 _CSRC = "bit_post_quantized_smooth_amd/csrc/"
 K2_SOURCES = {"int4": [_CSRC + "k2_w4a4_gemm.hip", _CSRC + "k2_common.hpp",
                        _CSRC + "device_common.hpp"],
+              "int4t": [_CSRC + "k2_w4a4_tiled.hip", _CSRC + "k2_common.hpp",
+                        _CSRC + "device_common.hpp"],
               "mxfp4": [_CSRC + "k2_mx_gemm.hip", _CSRC + "k2_common.hpp",
                         _CSRC + "device_common.hpp"],
               "w4a16": [_CSRC + "k2_w4a16_gemm.hip", _CSRC + "k2_common.hpp",
@@ -87,6 +90,9 @@ def parse():
                     help="mxfp4: the MXFP4 variant (E2M1 codes, E8M0 exponent per 32) on the "
                          "scaled FP4 matrix core; w4a16: the 4-bit weight-only baseline of the "
                          "pages' speed comparison (fp16 activations, no low-rank branch)")
+    ap.add_argument("--path", choices=["tiled", "canonical"], default="tiled",
+                    help="INT4 only: the tiled path (pre-kernel writing the GEMM's operand "
+                         "tiles, svdq_linear_tiled) or the canonical-layout kernels")
     ap.add_argument("--unfused-gelu", action="store_true",
                     help="with --mlp: plain up-projection, then the separate GELU kernel")
     ap.add_argument("--conv", type=int, default=None,
@@ -259,14 +265,18 @@ def host_cores():
 # algorithmic bytes (per launch)
 
 
-def k1_bytes(M, K, R, xb, meta_per_row):
-    """Read X once; write codes, scales (or exponents) and D; read L1 and 1/lambda."""
-    return M * K * xb + M * K // 2 + M * meta_per_row + 4 * M * R + 2 * K * R + 4 * K
+def k1_bytes(M, K, R, xb, meta_per_row, tiled=False):
+    """Read X once; write codes, scales (or exponents) and D; read L1 and 1/lambda.
+    tiled: the activation side as the tiled path stores it (one int8 operand byte
+    per code, an 8-byte fp32 scale pair per row and group)."""
+    act = M * K + 8 * M * (K // 64) if tiled else M * K // 2 + M * meta_per_row
+    return M * K * xb + act + 4 * M * R + 2 * K * R + 4 * K
 
 
-def k2_bytes(M, N, K, R, yb, meta_per_row):
+def k2_bytes(M, N, K, R, yb, meta_per_row, tiled=False):
     """Codes and scales of both operands, D, L2, Y (bias not counted: zero in the configs)."""
-    return (M + N) * K // 2 + (M + N) * meta_per_row + 4 * M * R + 2 * R * N + M * N * yb
+    act = M * K + 8 * M * (K // 64) if tiled else M * K // 2 + M * meta_per_row
+    return act + N * K // 2 + N * meta_per_row + 4 * M * R + 2 * R * N + M * N * yb
 
 
 # --------------------------------------------------------------------------
@@ -276,11 +286,12 @@ def k2_bytes(M, N, K, R, yb, meta_per_row):
 class Sets:
     """`n` independent device copies of one layer's inputs, weights and outputs."""
 
-    def __init__(self, torch, X, prep, bias, n, y_dtype):
+    def __init__(self, torch, X, prep, bias, n, y_dtype, tiled=False):
         import bit_post_quantized_smooth_amd as sq
         self.sq = sq
         self.mx = prep.fmt == "mxfp4"
         self.w16 = prep.fmt == "w4a16"
+        self.tiled = tiled and prep.fmt == "int4"
         M, K = X.shape
         self.M, self.K, self.N, self.R = M, K, prep.N, prep.rank
         G = K // 64
@@ -290,6 +301,8 @@ class Sets:
             wct, wet = sq.pack_mx_tiles(prep.w_codes, prep.w_scales, K)
         if self.w16:
             wct, wet = sq.pack_w4a16_tiles(prep.w_codes, prep.w_scales, K)
+        if self.tiled:
+            wct, wet = sq.pack_w4a4_tiles(prep.w_codes, prep.w_scales, K)
         self.sets = []
         for _ in range(n):
             s = dict(
@@ -303,6 +316,12 @@ class Sets:
                 s.update(wc=d(wct), ws=d(wet),
                          ac=torch.empty(sq.w4a16_x_tiled_bytes(M, K) // 2, dtype=torch.int16,
                                         device="cuda"), asc=None)
+            elif self.tiled:
+                s.update(wc=d(wct), ws=d(wet),
+                         ac=torch.empty(sq.int4_act_tiled_bytes(M, K), dtype=torch.uint8,
+                                        device="cuda"),
+                         asc=torch.empty(sq.int4_pairs_tiled_bytes(M, K) // 4, dtype=torch.float32,
+                                         device="cuda"))
             elif self.mx:
                 s.update(wc=d(wct), ws=d(wet),
                          ac=torch.empty(sq.mx_codes_tiled_bytes(M, K), dtype=torch.uint8, device="cuda"),
@@ -320,6 +339,7 @@ class Sets:
             self.sq.w4a16_tile_activation(X, s["ac"])
             return
         f = (self.sq.quantize_act_lowrank_down_mx if self.mx
+             else self.sq.quantize_act_lowrank_down_tiled if self.tiled
              else self.sq.quantize_act_lowrank_down)
         f(X, s["inv"], s["L1p"], self.R, s["ac"], s["asc"], s["D"] if self.R else None)
 
@@ -329,7 +349,9 @@ class Sets:
         if self.w16:
             self.sq.w4a16_gemm(s["ac"], s["wc"], s["ws"], s["b"], Y, self.K)
             return
-        f = self.sq.mx_gemm_lowrank_up if self.mx else self.sq.w4a4_gemm_lowrank_up
+        f = (self.sq.mx_gemm_lowrank_up if self.mx
+             else self.sq.w4a4_gemm_lowrank_up_tiled if self.tiled
+             else self.sq.w4a4_gemm_lowrank_up)
         f(s["ac"], s["asc"], s["wc"], s["ws"], s["D"] if self.R else None, s["L2t"], self.R, s["b"],
           Y, self.K)
 
@@ -416,7 +438,8 @@ def single_layer_main(args, torch, sq, wl, probe):
     L, X, W, lam, prep = prepare_layer(sq, wl, args.config, li, fmt)
     bias = None
     M, K, N, R = L.M, L.K, L.N, prep.rank
-    sets = Sets(torch, X, prep, bias, args.sets, L.y_dtype)
+    tiled = args.path == "tiled" and fmt == "int4"
+    sets = Sets(torch, X, prep, bias, args.sets, L.y_dtype, tiled)
     settled = settle(torch, sets, args.settle_ms)
     t_step, _, per = time_steps(torch, sets, args.steps, args.warmup, probe)
     clock = probe.result() if probe is not None else None
@@ -434,13 +457,18 @@ def single_layer_main(args, torch, sq, wl, probe):
     else:
         b1 = k1_bytes(M, K, R, xb, meta)
         b2 = k2_bytes(M, N, K, R, yb, meta)
+    # the bytes the tiled path's layouts move (the fractions use the method's
+    # algorithmic bytes above, which are fewer)
+    b1_layout = k1_bytes(M, K, R, xb, meta, tiled) if tiled else b1
+    b2_layout = k2_bytes(M, N, K, R, yb, meta, tiled) if tiled else b2
 
     traffic = None
-    if os.path.exists(PROFILE_PMC[fmt]):
+    pkey = "int4t" if tiled else fmt
+    if os.path.exists(PROFILE_PMC[pkey]):
         try:
-            with open(PROFILE_PMC[fmt]) as f:
+            with open(PROFILE_PMC[pkey]) as f:
                 pm = json.load(f)
-            if (pm.get("k2_source_hash") == k2_source_hash(fmt)
+            if (pm.get("k2_source_hash") == k2_source_hash(pkey)
                     and pm.get("config") == args.config):
                 traffic = pm.get("hbm_bytes_per_launch")
         except Exception:
@@ -449,7 +477,7 @@ def single_layer_main(args, torch, sq, wl, probe):
     overhead = None
     if not args.no_overhead and R > 0 and fmt != "w4a16":
         _, _, _, _, prep0 = prepare_layer(sq, wl, args.config, li, fmt, rank=0)
-        sets0 = Sets(torch, X, prep0, bias, args.sets, L.y_dtype)
+        sets0 = Sets(torch, X, prep0, bias, args.sets, L.y_dtype, tiled)
         t0_step, _, per0 = time_steps(torch, sets0, args.steps, args.warmup)
         k2_0 = float(np.median(per0[:, 1])) - gap
         overhead = dict(step_ms_rank0=t0_step * 1e3, k2_ms_rank0=k2_0 * 1e3,
@@ -476,17 +504,18 @@ def single_layer_main(args, torch, sq, wl, probe):
         "config": {"workload": f"{cfg.name} layer {li}: X {L.x_dtype} {M}x{K}, "
                                f"W {K}x{N}, rank {R}, {F['text']}, Y {L.y_dtype}",
                    "M": M, "K": K, "N": N, "rank": R, "format": fmt,
-                   "buffer_sets": args.sets},
+                   "path": "tiled" if tiled else "canonical", "buffer_sets": args.sets},
         F["pct"]: round(100.0 * value / F["peak"], 2),
-        "roofline": {"bound": "mfma", "kernel": F["kname"],
+        "roofline": {"bound": "mfma", "kernel": "k2t_w4a4_kernel" if tiled else F["kname"],
                      "achieved": round(ops / k2_avg / 1e12, 2), "peak": F["peak"],
                      "unit": F["unit"], "frac": round(ops / k2_avg / 1e12 / F["peak"], 4),
-                     "traffic": traffic, "algorithmic_bytes": b2,
+                     "traffic": traffic, "algorithmic_bytes": b2, "layout_bytes": b2_layout,
                      "avg_ms": round(k2_avg * 1e3, 4), "median_ms": round(k2_med * 1e3, 4),
                      "frac_median": round(ops / k2_med / 1e12 / F["peak"], 4),
                      "timing": TIMING_NOTE, "event_gap_us": round(gap * 1e6, 2)},
         "k1": {"kernel": "tile_x_kernel" if fmt == "w4a16" else "k1_quant_down_kernel",
                "avg_ms": round(k1_avg * 1e3, 4), "median_ms": round(k1_med * 1e3, 4),
+               "layout_bytes": b1_layout,
                "algorithmic_bytes": b1, "achieved_gbs": round(b1 / k1_avg / 1e9, 1),
                "peak_gbs": HBM_PEAK_GBS, "frac": round(b1 / k1_avg / 1e9 / HBM_PEAK_GBS, 4),
                "frac_median": round(b1 / k1_med / 1e9 / HBM_PEAK_GBS, 4)},
@@ -508,10 +537,10 @@ class Chain:
     (the LoRA stack, K = N for every layer); else every layer has its own input
     (the UNet batch, run back to back)."""
 
-    def __init__(self, torch, layers, n_sets, chain):
+    def __init__(self, torch, layers, n_sets, chain, tiled=False):
         self.chain = chain
         self.layers = [Sets(torch, X, prep, None, n_sets if (li == 0 or not chain) else 1,
-                            L.y_dtype) for li, (L, X, prep) in enumerate(layers)]
+                            L.y_dtype, tiled) for li, (L, X, prep) in enumerate(layers)]
         if chain:
             M, N = layers[0][0].M, layers[0][0].N
             self.act = [torch.empty((M, N), dtype=torch.float16, device="cuda") for _ in range(2)]
@@ -540,9 +569,13 @@ def whole_config_main(args, torch, sq, wl, probe):
         raise SystemExit("--layer all runs the INT4 or MXFP4 format")
     F = FORMATS[fmt]
     chain = args.config == 4
-    prepped = [prepare_layer(sq, wl, args.config, li, fmt) for li in range(len(cfg.layers))]
+    prepped = []
+    for li in range(len(cfg.layers)):
+        prepped.append(prepare_layer(sq, wl, args.config, li, fmt))
+        print(f"prepared layer {li + 1} of {len(cfg.layers)}", file=sys.stderr, flush=True)
     layers = [(L, X, prep) for (L, X, W, lam, prep) in prepped]
-    runner = Chain(torch, layers, args.sets, chain)
+    tiled = args.path == "tiled" and fmt == "int4"
+    runner = Chain(torch, layers, args.sets, chain, tiled)
     settled = settle(torch, runner, args.settle_ms)
     t_step, names, per = time_steps(torch, runner, args.steps, args.warmup, probe)
     clock = probe.result() if probe is not None else None
@@ -573,7 +606,8 @@ def whole_config_main(args, torch, sq, wl, probe):
     overhead = None
     if not args.no_overhead:
         p0 = [prepare_layer(sq, wl, args.config, li, fmt, rank=0) for li in range(len(cfg.layers))]
-        runner0 = Chain(torch, [(L, X, prep) for (L, X, W, lam, prep) in p0], args.sets, chain)
+        runner0 = Chain(torch, [(L, X, prep) for (L, X, W, lam, prep) in p0], args.sets, chain,
+                        tiled)
         t0_step, _, per0 = time_steps(torch, runner0, args.steps, args.warmup)
         k2_0 = sum(float(np.median(per0[:, 2 * li + 1])) - gap for li in range(len(p0)))
         overhead = dict(step_ms_rank0=t0_step * 1e3, k2_ms_rank0=k2_0 * 1e3,

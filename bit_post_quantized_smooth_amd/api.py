@@ -378,6 +378,105 @@ def linear(X, inv_smooth, L1p, L2t, R: int, w_codes, w_scales, bias, Y, ws, stre
                           _act(activation), _stream(stream)), "svdq_linear")
 
 
+def int4_act_tiled_bytes(M: int, K: int) -> int:
+    return int(lib.svdq_int4_act_tiled_bytes(M, K))
+
+
+def int4_pairs_tiled_bytes(M: int, K: int) -> int:
+    return int(lib.svdq_int4_pairs_tiled_bytes(M, K))
+
+
+def int4_w_codes_tiled_bytes(N: int, K: int) -> int:
+    return int(lib.svdq_int4_w_codes_tiled_bytes(N, K))
+
+
+def int4_w_scales_tiled_bytes(N: int, K: int) -> int:
+    return int(lib.svdq_int4_w_scales_tiled_bytes(N, K))
+
+
+def pack_w4a4_tiles(w_codes: np.ndarray, w_scales: np.ndarray, K: int):
+    """svdq_pack_w4a4_tiles: canonical INT4 weight codes and fp16 scale bits -> the
+    tiled layouts of the tiled path (flat uint8 codes, flat uint16 scale bits)."""
+    w_codes = _c(w_codes, np.uint8)
+    w_scales = _c(w_scales, np.uint16)
+    N = w_codes.shape[0]
+    ct = np.empty(int4_w_codes_tiled_bytes(N, K), dtype=np.uint8)
+    st = np.empty(int4_w_scales_tiled_bytes(N, K) // 2, dtype=np.uint16)
+    check(lib.svdq_pack_w4a4_tiles(_np_ptr(w_codes), _np_ptr(w_scales), N, K, _np_ptr(ct),
+                                   _np_ptr(st)), "svdq_pack_w4a4_tiles")
+    return ct, st
+
+
+def _act_side_tiled(M, K, R, a_ops_t, a_pairs_t, D):
+    _groups(K)
+    _buf("a_ops_t", a_ops_t, _BYTES, min_bytes=int4_act_tiled_bytes(M, K))
+    _buf("a_pairs_t", a_pairs_t, _F32, min_bytes=int4_pairs_tiled_bytes(M, K))
+    if R:
+        _buf("D", D, _F32, min_bytes=4 * M * R)
+
+
+def _weights_tiled(N, K, R, w_codes_t, w_scales_t, L2t):
+    _groups(K)
+    _buf("w_codes_t", w_codes_t, _BYTES, nbytes=int4_w_codes_tiled_bytes(N, K))
+    _buf("w_scales_t", w_scales_t, _HALF, nbytes=int4_w_scales_tiled_bytes(N, K))
+    if R:
+        _buf("L2t", L2t, _HALF, nbytes=2 * N * R)
+
+
+def quantize_act_lowrank_down_tiled(X, inv_smooth, L1p, R: int, a_ops_t, a_pairs_t, D,
+                                    stream=None):
+    """K1 writing the tiled activation operands and scale pairs."""
+    _mat("X", X, None, None)
+    M, K = X.shape
+    _down(K, R, inv_smooth, L1p)
+    _act_side_tiled(M, K, R, a_ops_t, a_pairs_t, D)
+    _on_gpu(X, inv_smooth, L1p if R else None, a_ops_t, a_pairs_t, D if R else None)
+    check(lib.svdq_quantize_act_lowrank_down_tiled(_tp(X), _dt(X), M, K, X.stride(0),
+                                                   _tp(inv_smooth), _tp(L1p) if R else None, R,
+                                                   _tp(a_ops_t), _tp(a_pairs_t),
+                                                   _tp(D) if R else None, _stream(stream)),
+          "svdq_quantize_act_lowrank_down_tiled")
+
+
+def w4a4_gemm_lowrank_up_tiled(a_ops_t, a_pairs_t, w_codes_t, w_scales_t, D, L2t, R: int, bias, Y,
+                               K: int, stream=None, activation=None):
+    """K2 on the tiled layouts."""
+    _mat("Y", Y, None, None)
+    M, N = Y.shape
+    _act_side_tiled(M, K, R, a_ops_t, a_pairs_t, D)
+    _weights_tiled(N, K, R, w_codes_t, w_scales_t, L2t)
+    _bias(bias, N)
+    _on_gpu(a_ops_t, a_pairs_t, w_codes_t, w_scales_t, D if R else None, L2t if R else None, bias,
+            Y)
+    check(lib.svdq_w4a4_gemm_lowrank_up_tiled(_tp(a_ops_t), _tp(a_pairs_t), _tp(w_codes_t),
+                                              _tp(w_scales_t), _tp(D) if R else None,
+                                              _tp(L2t) if R else None, R, _tp(bias), _tp(Y),
+                                              _dt(Y), M, N, K, Y.stride(0), _act(activation),
+                                              _stream(stream)),
+          "svdq_w4a4_gemm_lowrank_up_tiled")
+
+
+def linear_tiled_workspace_bytes(M: int, K: int, R: int) -> int:
+    return int(lib.svdq_linear_tiled_workspace_bytes(M, K, R))
+
+
+def linear_tiled(X, inv_smooth, L1p, L2t, R: int, w_codes_t, w_scales_t, bias, Y, ws, stream=None,
+                 activation=None):
+    """The whole INT4 layer on the tiled path (weights from pack_w4a4_tiles)."""
+    M, K, N = _layer_io(X, Y)
+    _down(K, R, inv_smooth, L1p)
+    _weights_tiled(N, K, R, w_codes_t, w_scales_t, L2t)
+    _bias(bias, N)
+    _buf("ws", ws, _BYTES + _HALF + _F32, min_bytes=linear_tiled_workspace_bytes(M, K, R))
+    _on_gpu(X, inv_smooth, L1p if R else None, L2t if R else None, w_codes_t, w_scales_t, bias, Y,
+            ws)
+    check(lib.svdq_linear_tiled(_tp(X), _dt(X), X.stride(0), _tp(inv_smooth),
+                                _tp(L1p) if R else None, _tp(L2t) if R else None, R,
+                                _tp(w_codes_t), _tp(w_scales_t), _tp(bias), _tp(Y), _dt(Y),
+                                Y.stride(0), M, K, N, _tp(ws), ws.numel() * ws.element_size(),
+                                _act(activation), _stream(stream)), "svdq_linear_tiled")
+
+
 def linear_noalloc(X, inv_smooth, L1p, L2t, R: int, w_codes, w_scales, bias, Y, stream=None,
                    activation=None):
     """svdq_linear with the intermediates in the library's static device buffer
@@ -660,13 +759,14 @@ class Linear:
     """One prepared SVDQuant layer resident on a device.
 
     ``Linear(prep, bias)(X)`` runs K1 then K2 (their MXFP4 versions for a
-    prep of fmt "mxfp4") on the current stream and
+    prep of fmt "mxfp4"; with ``tiled=True`` an INT4 prep runs the tiled path,
+    svdq_linear_tiled) on the current stream and
     returns Y (M x N, ``out_dtype``), optionally through the fused activation
     (``"gelu_tanh"``). The workspace is kept between calls and grown when a
     larger M arrives."""
 
     def __init__(self, prep: Prepared, bias: Optional[np.ndarray] = None, device="cuda",
-                 out_dtype=None, activation=None):
+                 out_dtype=None, activation=None, tiled: bool = False):
         torch = _torch()
         self.K, self.N, self.R = prep.K, prep.N, prep.rank
         dev = torch.device(device)
@@ -674,7 +774,12 @@ class Linear:
         self.L1p = torch.from_numpy(prep.L1p.view(np.int16)).to(dev) if self.R else None
         self.L2t = torch.from_numpy(prep.L2t.view(np.int16)).to(dev) if self.R else None
         self.fmt = prep.fmt
-        if self.fmt == "w4a16":
+        self.tiled = bool(tiled) and self.fmt == "int4"
+        if self.tiled:
+            ct, st = pack_w4a4_tiles(prep.w_codes, prep.w_scales, prep.K)
+            self.w_codes = torch.from_numpy(ct).to(dev)
+            self.w_scales = torch.from_numpy(st.view(np.int16)).to(dev)
+        elif self.fmt == "w4a16":
             ct, st = pack_w4a16_tiles(prep.w_codes, prep.w_scales, prep.K)
             self.w_codes = torch.from_numpy(ct).to(dev)
             self.w_scales = torch.from_numpy(st.view(np.int16)).to(dev)
@@ -697,6 +802,8 @@ class Linear:
             need = w4a16_x_tiled_bytes(M, self.K)
         elif self.fmt == "mxfp4":
             need = linear_mx_workspace_bytes(M, self.K, self.R)
+        elif self.tiled:
+            need = linear_tiled_workspace_bytes(M, self.K, self.R)
         else:
             need = linear_workspace_bytes(M, self.K, self.R)
         if self.ws is None or self.ws.numel() < need:
@@ -716,7 +823,7 @@ class Linear:
                 raise ValueError("the weight-only baseline has no fused activation")
             linear_w4a16(X, self.w_codes, self.w_scales, self.bias, Y, self.workspace(M), stream)
             return Y
-        run = linear_mx if self.fmt == "mxfp4" else linear
+        run = linear_mx if self.fmt == "mxfp4" else linear_tiled if self.tiled else linear
         run(X, self.inv_smooth, self.L1p, self.L2t, self.R, self.w_codes, self.w_scales,
             self.bias, Y, self.workspace(M), stream, self.activation)
         return Y

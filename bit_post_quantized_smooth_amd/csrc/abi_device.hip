@@ -151,6 +151,18 @@ WsLayout ws_layout(int64_t M, int64_t K, int32_t R, bool mx) {
   return w;
 }
 
+// The tiled INT4 path: operand blocks ceil(M/16) x K/64 of 1 KB, scale pairs
+// ceil(M/128) x K/64 of 1 KB, D.
+WsLayout tiled_ws_layout(int64_t M, int64_t K, int32_t R) {
+  WsLayout w;
+  const size_t G = static_cast<size_t>(K / SVDQ_GROUP);
+  w.codes = 0;
+  w.scales = round_up(static_cast<size_t>((M + 15) / 16) * G * 1024, 256);
+  w.d = w.scales + round_up(static_cast<size_t>((M + 127) / 128) * G * 1024, 256);
+  w.total = w.d + round_up(static_cast<size_t>(M) * R * 4, 256);
+  return w;
+}
+
 ConvGeom conv_geom(const ConvShape& cs) {
   return ConvGeom{static_cast<int32_t>(cs.H), static_cast<int32_t>(cs.W),
                   static_cast<int32_t>(cs.C), cs.KH, cs.KW, cs.stride, cs.pad,
@@ -237,6 +249,88 @@ int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth
   return check_hip(launch_k2(a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y,
                              y_dtype == SVDQ_F16, M, N, K, ldy, activation == SVDQ_ACT_GELU_TANH, stream),
                    "svdq_linear K2 launch");
+}
+
+int svdq_quantize_act_lowrank_down_tiled(const void* X, int x_dtype, int64_t M, int64_t K,
+                                         int64_t ldx, const float* inv_smooth,
+                                         const uint16_t* L1p, int32_t R, uint8_t* a_ops_t,
+                                         float* a_pairs_t, float* D, hipStream_t stream) {
+  clear_error();
+  const char* fn = "svdq_quantize_act_lowrank_down_tiled";
+  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, SVDQ_GROUP, a_ops_t,
+                          a_pairs_t, D, fn))
+    return s;
+  if (int s = device_ready()) return s;
+  return check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1p, R, a_ops_t,
+                             a_pairs_t, kK1Int4Tiled, D, stream),
+                   "svdq_quantize_act_lowrank_down_tiled launch");
+}
+
+int svdq_w4a4_gemm_lowrank_up_tiled(const uint8_t* a_ops_t, const float* a_pairs_t,
+                                    const uint8_t* w_codes_t, const uint16_t* w_scales_t,
+                                    const float* D, const uint16_t* L2t, int32_t R,
+                                    const float* bias, void* Y, int y_dtype, int64_t M, int64_t N,
+                                    int64_t K, int64_t ldy, int32_t activation,
+                                    hipStream_t stream) {
+  clear_error();
+  const char* fn = "svdq_w4a4_gemm_lowrank_up_tiled";
+  if (int s = validate_k2(a_ops_t, a_pairs_t, w_codes_t, w_scales_t, D, L2t, R, bias, Y, y_dtype,
+                          M, N, K, ldy, SVDQ_GROUP, fn))
+    return s;
+  if (int s = check_activation(activation, fn)) return s;
+  if (int s = device_ready()) return s;
+  return check_hip(launch_k2t(a_ops_t, a_pairs_t, w_codes_t, w_scales_t, D, L2t, R, bias, Y,
+                              y_dtype == SVDQ_F16, M, N, K, ldy,
+                              activation == SVDQ_ACT_GELU_TANH, stream),
+                   "svdq_w4a4_gemm_lowrank_up_tiled launch");
+}
+
+size_t svdq_linear_tiled_workspace_bytes(int64_t M, int64_t K, int32_t R) {
+  if (M < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0 || R < 0) return 0;
+  return tiled_ws_layout(M, K, R).total;
+}
+
+int svdq_linear_tiled(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
+                      const uint16_t* L1p, const uint16_t* L2t, int32_t R,
+                      const uint8_t* w_codes_t, const uint16_t* w_scales_t, const float* bias,
+                      void* Y, int y_dtype, int64_t ldy, int64_t M, int64_t K, int64_t N,
+                      void* ws, size_t ws_bytes, int32_t activation, hipStream_t stream) {
+  clear_error();
+  const char* fn = "svdq_linear_tiled";
+  if (int s = check_activation(activation, fn)) return s;
+  if (int s = check_common(M, K, R, SVDQ_GROUP, fn)) return s;
+  if (!ws) {
+    set_error("%s: null workspace", fn);
+    return SVDQ_ERR_NULL;
+  }
+  const WsLayout L = tiled_ws_layout(M, K, R);
+  if (ws_bytes < L.total) {
+    set_error("%s: workspace %zu bytes < %zu needed", fn, ws_bytes, L.total);
+    return SVDQ_ERR_WORKSPACE;
+  }
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) {
+    set_error("%s: workspace must be 256-byte aligned", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* a_ops = base + L.codes;
+  float* a_pairs = reinterpret_cast<float*>(base + L.scales);
+  float* D = R > 0 ? reinterpret_cast<float*>(base + L.d) : nullptr;
+  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, SVDQ_GROUP, a_ops, a_pairs,
+                          D, fn))
+    return s;
+  if (int s = validate_k2(a_ops, a_pairs, w_codes_t, w_scales_t, D, L2t, R, bias, Y, y_dtype, M,
+                          N, K, ldy, SVDQ_GROUP, fn))
+    return s;
+  if (int s = device_ready()) return s;
+  if (int s = check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1p, R, a_ops,
+                                  a_pairs, kK1Int4Tiled, D, stream),
+                        "svdq_linear_tiled K1 launch"))
+    return s;
+  return check_hip(launch_k2t(a_ops, a_pairs, w_codes_t, w_scales_t, D, L2t, R, bias, Y,
+                              y_dtype == SVDQ_F16, M, N, K, ldy, activation == SVDQ_ACT_GELU_TANH,
+                              stream),
+                   "svdq_linear_tiled K2 launch");
 }
 
 int svdq_quantize_act_lowrank_down_mx(const void* X, int x_dtype, int64_t M, int64_t K,

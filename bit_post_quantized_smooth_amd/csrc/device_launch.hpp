@@ -18,18 +18,30 @@ struct ConvGeom {
 // Resident workgroup slots of the current device (2 per compute unit).
 int resident_slots();
 
-// a_meta: fp16 group scales (mx = false) or E8M0 block exponents (mx = true).
+// Output format of the pre-kernel: canonical INT4 codes and fp16 scales;
+// MXFP4 tiled codes and E8M0 exponents; INT4 operand tiles and fp32 scale
+// pairs for the tiled GEMM (K2T). a_codes / a_meta are the codes / the scales,
+// exponents or scale pairs of that format.
+enum K1Fmt { kK1Int4 = 0, kK1Mx = 1, kK1Int4Tiled = 2 };
+
 // conv: null for a linear layer; else X is the NHWC image and M, K are the
 // patch matrix's.
 hipError_t launch_k1(const void* X, bool x_f16, int64_t M, int64_t K, int64_t ldx,
                      const float* inv_smooth, const uint16_t* L1p, int R, uint8_t* a_codes,
-                     void* a_meta, bool mx, float* D, hipStream_t stream,
+                     void* a_meta, int fmt, float* D, hipStream_t stream,
                      const ConvGeom* conv = nullptr);
 
 hipError_t launch_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* w_codes,
                      const uint16_t* w_scales, const float* D, const uint16_t* L2t, int R,
                      const float* bias, void* Y, bool y_f16, int64_t M, int64_t N, int64_t K,
                      int64_t ldy, bool gelu, hipStream_t stream);
+
+// K2T on the tiled INT4 layouts (svdq.h): a_ops / a_pairs from the pre-kernel's
+// kK1Int4Tiled output, w_codes_t / w_scales_t from svdq_pack_w4a4_tiles.
+hipError_t launch_k2t(const uint8_t* a_ops, const float* a_pairs, const uint8_t* w_codes_t,
+                      const uint16_t* w_scales_t, const float* D, const uint16_t* L2t, int R,
+                      const float* bias, void* Y, bool y_f16, int64_t M, int64_t N, int64_t K,
+                      int64_t ldy, bool gelu, hipStream_t stream);
 
 hipError_t launch_k2_mx(const uint8_t* a_codes, const uint8_t* a_e8m0, const uint8_t* w_codes,
                         const uint8_t* w_e8m0, const float* D, const uint16_t* L2t, int R,

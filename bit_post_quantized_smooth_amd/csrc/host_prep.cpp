@@ -586,6 +586,69 @@ int svdq_pack_w4a16_tiles(const uint8_t* w_codes, const uint16_t* w_scales, int6
   return SVDQ_OK;
 }
 
+size_t svdq_int4_act_tiled_bytes(int64_t M, int64_t K) {
+  if (M < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) return 0;
+  return static_cast<size_t>((M + 15) / 16) * static_cast<size_t>(K / SVDQ_GROUP) * 1024;
+}
+
+size_t svdq_int4_pairs_tiled_bytes(int64_t M, int64_t K) {
+  if (M < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) return 0;
+  return static_cast<size_t>((M + 127) / 128) * static_cast<size_t>(K / SVDQ_GROUP) * 1024;
+}
+
+size_t svdq_int4_w_codes_tiled_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) return 0;
+  return static_cast<size_t>((N + 31) / 32) * static_cast<size_t>(K / SVDQ_GROUP) * 1024;
+}
+
+size_t svdq_int4_w_scales_tiled_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) return 0;
+  return static_cast<size_t>((N + 31) / 32) * static_cast<size_t>(K / SVDQ_GROUP) * 64;
+}
+
+int svdq_pack_w4a4_tiles(const uint8_t* w_codes, const uint16_t* w_scales, int64_t N, int64_t K,
+                         uint8_t* w_codes_t, uint16_t* w_scales_t) {
+  clear_error();
+  if (!w_codes || !w_scales || !w_codes_t || !w_scales_t) {
+    set_error("svdq_pack_w4a4_tiles: null pointer");
+    return SVDQ_ERR_NULL;
+  }
+  if (K < SVDQ_GROUP || K % SVDQ_GROUP != 0) {
+    set_error("svdq_pack_w4a4_tiles: K=%lld (need K %% 64 == 0)", (long long)K);
+    return SVDQ_ERR_GROUP;
+  }
+  if (N < 1) {
+    set_error("svdq_pack_w4a4_tiles: N=%lld", (long long)N);
+    return SVDQ_ERR_SHAPE;
+  }
+  const int64_t G = K / SVDQ_GROUP, kb = K / 2, ns = (N + 31) / 32;
+  // codes: block (s, g), lane l = 16q + r: bytes 0..7 = codes of column
+  // 32s + r, bytes 8..15 = codes of column 32s + 16 + r, each the 8 bytes
+  // 32g + 8q .. +7 of the column's row (0 past N)
+#pragma omp parallel for schedule(static)
+  for (int64_t s = 0; s < ns; ++s)
+    for (int64_t g = 0; g < G; ++g)
+      for (int l = 0; l < 64; ++l)
+        for (int j = 0; j < 2; ++j) {
+          const int64_t n = 32 * s + 16 * j + (l & 15);
+          uint8_t* dst = w_codes_t + ((s * G + g) * 64 + l) * 16 + 8 * j;
+          for (int t = 0; t < 8; ++t)
+            dst[t] = n < N ? w_codes[n * kb + 32 * g + 8 * (l >> 4) + t] : uint8_t{0};
+        }
+  // scales: block (s, g), entry 8q + 4j + e: column 32s + 16j + 4q + e (0 past N)
+#pragma omp parallel for schedule(static)
+  for (int64_t s = 0; s < ns; ++s)
+    for (int64_t g = 0; g < G; ++g)
+      for (int q = 0; q < 4; ++q)
+        for (int j = 0; j < 2; ++j)
+          for (int e = 0; e < 4; ++e) {
+            const int64_t n = 32 * s + 16 * j + 4 * q + e;
+            w_scales_t[(s * G + g) * 32 + 8 * q + 4 * j + e] =
+                n < N ? w_scales[n * G + g] : uint16_t{0};
+          }
+  return SVDQ_OK;
+}
+
 int svdq_concat_lora(const uint16_t* L1t, const uint16_t* L2t, int64_t K, int64_t N, int32_t rank,
                      const float* lambda, const uint16_t* A, const uint16_t* B, int32_t rl,
                      float scale, uint16_t* L1t_out, uint16_t* L2t_out) {

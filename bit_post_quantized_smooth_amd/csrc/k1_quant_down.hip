@@ -257,13 +257,21 @@ struct GroupIn {
 // g = (kh*KW + kw)*C/64 + cb. A lane reads its 16 channels at input pixel
 // (oh*stride + kh - pad, ow*stride + kw - pad) or, outside the image, loads a
 // clamped pixel and uses zeros, so every load stays unconditional.
-template <typename XT, int NCB, int NB, bool MX, bool CONV, int RT>
+// FMT: what the quantizer step writes (K1Fmt): the canonical INT4 codes and
+// fp16 scales, the MXFP4 tiled codes and exponents, or the INT4 operands of
+// the tiled GEMM (K2T): per 16-row block and group one 1 KB block in the
+// matrix instruction's lane order (lane 16q + r: row r, codes 16q .. 16q+15
+// of the group, widened to int8 16*q in widen_codes' order) and the scale as
+// the fp32 pair (s/256, -12582912 s/256) in the 128-row band layout of svdq.h.
+template <typename XT, int NCB, int NB, int FMT, bool CONV, int RT>
 __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
     const XT* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
     const float* __restrict__ inv_smooth, const uint16_t* __restrict__ L1p, int R,
     uint8_t* __restrict__ a_codes, void* __restrict__ a_meta, float* __restrict__ D,
     ConvGeom cg) {
 #pragma clang fp contract(off)
+  constexpr bool MX = FMT == kK1Mx;
+  constexpr bool TILED = FMT == kK1Int4Tiled;
   constexpr int WAVES = k1_waves<NCB>();
   constexpr int NCBA = NCB > 0 ? NCB : 1;
   __shared__ float dpart[WAVES][16 * RT][NCBA * 16];
@@ -434,7 +442,23 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
             }
           }
         }
-        if (i < n_mine && rvalid[rt]) {
+        if constexpr (TILED) {
+          // the row block exists (rows past M inside it carry the clamped
+          // row's values, so the block is fully written)
+          if (i < n_mine && row0 + 16 * rt < M) {
+            const int64_t b = row0 / 16 + rt;
+            *reinterpret_cast<v4i*>(a_codes + (b * G + g) * 1024 + 16 * lane) =
+                widen_codes(make_uint2(packed[0], packed[1]));
+            if (c4 == 0) {
+              // (s/256, -12582912 s/256), both exact
+              const float sx = h2f(static_cast<uint16_t>(meta)) * 0.00390625f;
+              const int ib = static_cast<int>(b % 8);
+              float* pp = static_cast<float*>(a_meta) + ((b / 8) * G + g) * 256 +
+                          ((ib >> 1) * 16 + qr) * 4 + (ib & 1) * 2;
+              *reinterpret_cast<float2*>(pp) = make_float2(sx, sx * -kMagicF);
+            }
+          }
+        } else if (i < n_mine && rvalid[rt]) {
           if constexpr (MX) {
             // tiled layouts: group g is half h of chunk g/2; this lane's 16
             // codes are the 8 bytes at 8*(c4%2) of lane 16*kq + qr of the
@@ -488,7 +512,7 @@ __global__ __launch_bounds__(64 * k1_waves<NCB>(), 2) void k1_quant_down_kernel(
 template <typename XT, int NCB, int RT>
 hipError_t launch_k1_rt(const void* X, int64_t M, int64_t K, int64_t ldx,
                         const float* inv_smooth, const uint16_t* L1p, int R,
-                        uint8_t* a_codes, void* a_meta, bool mx, float* D, hipStream_t stream,
+                        uint8_t* a_codes, void* a_meta, int fmt, float* D, hipStream_t stream,
                         const ConvGeom* conv) {
   // groups in flight per wave, sized so the ring fits the register budget of
   // two resident workgroups
@@ -497,18 +521,19 @@ hipError_t launch_k1_rt(const void* X, int64_t M, int64_t K, int64_t ldx,
       grid(static_cast<unsigned>((M + 16 * RT - 1) / (16 * RT)));
   const XT* x = static_cast<const XT*>(X);
   const ConvGeom cg = conv ? *conv : ConvGeom{};
-  if (conv && mx)
-    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, true, true, RT>), grid, block, 0,
-                       stream, x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
-  else if (conv)
-    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, false, true, RT>), grid, block, 0,
-                       stream, x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
-  else if (mx)
-    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, true, false, RT>), grid, block, 0,
-                       stream, x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
-  else
-    hipLaunchKernelGGL((k1_quant_down_kernel<XT, NCB, NB, false, false, RT>), grid, block, 0,
-                       stream, x, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, D, cg);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, x, M, K, ldx, inv_smooth, L1p, R, a_codes,
+                       a_meta, D, cg);
+  };
+  if (conv) {
+    if (fmt == kK1Mx) go(k1_quant_down_kernel<XT, NCB, NB, kK1Mx, true, RT>);
+    else if (fmt == kK1Int4Tiled) go(k1_quant_down_kernel<XT, NCB, NB, kK1Int4Tiled, true, RT>);
+    else go(k1_quant_down_kernel<XT, NCB, NB, kK1Int4, true, RT>);
+  } else {
+    if (fmt == kK1Mx) go(k1_quant_down_kernel<XT, NCB, NB, kK1Mx, false, RT>);
+    else if (fmt == kK1Int4Tiled) go(k1_quant_down_kernel<XT, NCB, NB, kK1Int4Tiled, false, RT>);
+    else go(k1_quant_down_kernel<XT, NCB, NB, kK1Int4, false, RT>);
+  }
   return hipGetLastError();
 }
 
@@ -523,33 +548,33 @@ hipError_t launch_k1_rt(const void* X, int64_t M, int64_t K, int64_t ldx,
 template <typename XT, int NCB>
 hipError_t launch_k1_t(const void* X, int64_t M, int64_t K, int64_t ldx,
                        const float* inv_smooth, const uint16_t* L1p, int R,
-                       uint8_t* a_codes, void* a_meta, bool mx, float* D, hipStream_t stream,
+                       uint8_t* a_codes, void* a_meta, int fmt, float* D, hipStream_t stream,
                        const ConvGeom* conv) {
   if constexpr (NCB <= 4) {
     if (2 * ((M + 15) / 16) > static_cast<int64_t>(resident_slots()))
-      return launch_k1_rt<XT, NCB, 2>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D,
+      return launch_k1_rt<XT, NCB, 2>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D,
                                       stream, conv);
   }
-  return launch_k1_rt<XT, NCB, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D,
+  return launch_k1_rt<XT, NCB, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D,
                                   stream, conv);
 }
 
 template <typename XT>
 hipError_t launch_k1_dtype(const void* X, int64_t M, int64_t K, int64_t ldx,
                                   const float* inv_smooth, const uint16_t* L1p, int R,
-                                  uint8_t* a_codes, void* a_meta, bool mx, float* D,
+                                  uint8_t* a_codes, void* a_meta, int fmt, float* D,
                                   hipStream_t stream, const ConvGeom* conv) {
   switch (R / 16) {
-    case 0: return launch_k1_t<XT, 0>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
-    case 1: return launch_k1_t<XT, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
-    case 2: return launch_k1_t<XT, 2>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
-    case 3: return launch_k1_t<XT, 3>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
-    case 4: return launch_k1_t<XT, 4>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
-    case 5: return launch_k1_t<XT, 5>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
-    case 6: return launch_k1_t<XT, 6>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
+    case 0: return launch_k1_t<XT, 0>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
+    case 1: return launch_k1_t<XT, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
+    case 2: return launch_k1_t<XT, 2>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
+    case 3: return launch_k1_t<XT, 3>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
+    case 4: return launch_k1_t<XT, 4>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
+    case 5: return launch_k1_t<XT, 5>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
+    case 6: return launch_k1_t<XT, 6>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
     case 7:
-    case 8: return launch_k1_t<XT, 8>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
-    default: return launch_k1_t<XT, 16>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
+    case 8: return launch_k1_t<XT, 8>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
+    default: return launch_k1_t<XT, 16>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
   }
 }
 
@@ -557,10 +582,10 @@ hipError_t launch_k1_dtype(const void* X, int64_t M, int64_t K, int64_t ldx,
 
 hipError_t launch_k1(const void* X, bool x_f16, int64_t M, int64_t K, int64_t ldx,
                      const float* inv_smooth, const uint16_t* L1p, int R, uint8_t* a_codes,
-                     void* a_meta, bool mx, float* D, hipStream_t stream, const ConvGeom* conv) {
+                     void* a_meta, int fmt, float* D, hipStream_t stream, const ConvGeom* conv) {
   if (x_f16)
-    return launch_k1_dtype<_Float16>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
-  return launch_k1_dtype<float>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, mx, D, stream, conv);
+    return launch_k1_dtype<_Float16>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
+  return launch_k1_dtype<float>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
 }
 
 }  // namespace svdq

@@ -53,15 +53,19 @@ __device__ __forceinline__ void banded_tile(int t, int tiles_m, int tiles_n, int
 // out-of-range operands are zeroed after it arrives; a load under a branch
 // whose other side zeroes the same registers would have to complete before
 // anything else is issued.
+// lowrank_up_at: for a wave whose WTM x WTN region of Y starts at row mw and
+// column nw; lowrank_up: for the wave's quarter of a 2*WTM x 2*WTN tile at
+// (m0, n0) (wave w: rows w/2, columns w%2).
 template <int WTM, int WTN>
-__device__ __forceinline__ void lowrank_up(v4f (&acc)[WTM / 16][WTN / 16],
-                                           const float* __restrict__ D,
-                                           const uint16_t* __restrict__ L2t, int R, int64_t M,
-                                           int64_t N, int64_t m0, int64_t n0) {
+__device__ __forceinline__ void lowrank_up_at(v4f (&acc)[WTM / 16][WTN / 16],
+                                              const float* __restrict__ D,
+                                              const uint16_t* __restrict__ L2t, int R, int64_t M,
+                                              int64_t N, int64_t mw, int64_t nw) {
   constexpr int NBM = WTM / 16, NBN = WTN / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int rl = lane & 15, q = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = mw, n0 = nw;
+  constexpr int wm = 0, wn = 0;
   const v8h zero = v8h{0, 0, 0, 0, 0, 0, 0, 0};
   for (int rc = 0; rc < R; rc += 32) {
     const int kk = rc + 8 * q;                       // this lane's 8 rank indices
@@ -91,19 +95,31 @@ __device__ __forceinline__ void lowrank_up(v4f (&acc)[WTM / 16][WTN / 16],
   }
 }
 
+template <int WTM, int WTN>
+__device__ __forceinline__ void lowrank_up(v4f (&acc)[WTM / 16][WTN / 16],
+                                           const float* __restrict__ D,
+                                           const uint16_t* __restrict__ L2t, int R, int64_t M,
+                                           int64_t N, int64_t m0, int64_t n0) {
+  const int wave = threadIdx.x >> 6;
+  lowrank_up_at<WTM, WTN>(acc, D, L2t, R, M, N, m0 + (wave >> 1) * WTM,
+                          n0 + (wave & 1) * WTN);
+}
+
 // Bias, the optional GELU, one rounding to the output type, and the stores: a
 // lane holds columns 4q .. 4q+3 of row rl in each 16 x 16 block, written as
 // one 8-byte (fp16) or 16-byte (fp32) store when Y's address and row stride
-// allow it.
+// allow it. bias_store_at: the wave's region starts at (mw, nw); bias_store:
+// the wave's quarter of the tile at (m0, n0), as lowrank_up.
 template <int WTM, int WTN, bool Y_F16, bool GELU>
-__device__ __forceinline__ void bias_store(v4f (&acc)[WTM / 16][WTN / 16],
-                                           const float* __restrict__ bias, void* __restrict__ Y,
-                                           int64_t M, int64_t N, int64_t ldy, int64_t m0,
-                                           int64_t n0) {
+__device__ __forceinline__ void bias_store_at(v4f (&acc)[WTM / 16][WTN / 16],
+                                              const float* __restrict__ bias,
+                                              void* __restrict__ Y, int64_t M, int64_t N,
+                                              int64_t ldy, int64_t mw, int64_t nw) {
   constexpr int NBM = WTM / 16, NBN = WTN / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int rl = lane & 15, q = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = mw, n0 = nw;
+  constexpr int wm = 0, wn = 0;
   constexpr int ES = Y_F16 ? 2 : 4;
   const bool vec = ((reinterpret_cast<uintptr_t>(Y) | static_cast<uintptr_t>(ldy * ES)) %
                     (4 * ES)) == 0;
@@ -150,6 +166,16 @@ __device__ __forceinline__ void bias_store(v4f (&acc)[WTM / 16][WTN / 16],
       }
     }
   }
+}
+
+template <int WTM, int WTN, bool Y_F16, bool GELU>
+__device__ __forceinline__ void bias_store(v4f (&acc)[WTM / 16][WTN / 16],
+                                           const float* __restrict__ bias, void* __restrict__ Y,
+                                           int64_t M, int64_t N, int64_t ldy, int64_t m0,
+                                           int64_t n0) {
+  const int wave = threadIdx.x >> 6;
+  bias_store_at<WTM, WTN, Y_F16, GELU>(acc, bias, Y, M, N, ldy, m0 + (wave >> 1) * WTM,
+                                       n0 + (wave & 1) * WTN);
 }
 
 // The same epilogue for an fp16 Y through LDS, for a wave whose WTM x 64

@@ -1,0 +1,307 @@
+// K2T: the W4A4 GEMM of the SVDQuant linear layer on tiled operands, with the
+// low-rank up-projection and the bias fused in (gfx950).
+//
+// The arithmetic is K2's (k2_w4a4_gemm.hip): both operands are 4-bit codes
+// (SVDQuant abstract: weights and activations at 4 bits), widened to int8
+// lanes holding 16*q for v_mfma_i32_16x16x64_i8, whose int32 result over one
+// 64-channel group is the exact group partial P (times 256, read through the
+// 1.5*2^23 accumulator seed as the float f = 12582912 + 256 P); per output
+// and group two fp32 ops
+//     t   = fma(f, s_x/256, -12582912 s_x/256) = P s_x   (exact)
+//     acc = fma(t, s_w, acc)                            (the one rounding)
+// and the low-rank branch fp16(D) . L2 and the bias in the same kernel (the
+// Nunchaku engine fuses the low-rank kernels into the low-bit ones:
+// SVDQuant abstract; the disruptive-concepts.com post, section "Nunchaku:
+// Fusing Precision and Speed").
+//
+// Those two fp32 ops per output and group bound the kernel: the vector ALU
+// needs twice the matrix core's time for them. So this kernel keeps every
+// other vector op out of the K loop:
+// - the activation operand arrives already widened, in the matrix
+//   instruction's lane order, from the pre-kernel (svdq.h, tiled INT4
+//   layouts), with its scale as the fp32 pair (s_x/256, -12582912 s_x/256);
+// - the weights stay 4-bit (the 4-bit weight memory is the method's point)
+//   in a lane-order tiling per 32-column strip, so a wave's weight fragment
+//   for one group is one 16-byte read per lane, widened once (12 bit ops);
+// - every operand goes from global memory straight into LDS
+//   (global_load_lds: no register round trip), KSTAGES groups deep, with one
+//   barrier per group; addresses advance by scalar offsets.
+// What remains per group and wave: 16 matrix instructions, 128 rescale ops,
+// 12 widening ops, 14 LDS reads and 5 copies.
+//
+// Tiling: a 256-thread workgroup computes a 128 x 128 tile of Y; wave w owns
+// all 128 rows and columns 32w .. 32w+31 (8 x 2 blocks of 16 x 16), so its
+// weight strip is its own and only the activation operands are shared. The
+// weight fragment is the matrix instruction's first operand, so a lane holds 4
+// consecutive columns of one row of each block (as in K2). Tiles run in K2's
+// XCD-aware banded order.
+#include <hip/hip_runtime.h>
+
+#include "device_common.hpp"
+#include "device_launch.hpp"
+#include "k2_common.hpp"
+
+namespace svdq {
+
+namespace {
+
+constexpr int NT = 256;             // threads per workgroup
+constexpr int kBlk = 1024;          // one operand block: 64 lanes x 16 bytes
+constexpr int kPairBlk = 256;       // scale pairs of one 128-row band and group (floats)
+constexpr int kWsBlk = 32;          // fp16 weight scales of one 32-column strip and group
+constexpr int KSTAGES = 4;          // LDS ring depth
+constexpr int KAHEAD = KSTAGES - 1; // groups copied ahead of the one computed
+constexpr int kCopiesPerGroup = 5;  // direct-to-LDS loads per wave and group
+
+// One group's operands for the whole tile.
+struct alignas(16) TStage {
+  uint8_t a[8][kBlk];               // activation operands of the 8 row blocks (int8 16q)
+  uint8_t b[4][kBlk];               // 4-bit weight codes of the 4 waves' strips
+  float p[kPairBlk];                // scale pairs of the 128 rows
+  uint16_t w[4][kWsBlk];            // fp16 weight scales of the 4 strips
+};
+
+#define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
+
+// The 16 bytes of 4-bit codes a lane holds for its strip (8 for each of its
+// two column blocks) -> the two int8 operands (16*q, the order of
+// widen_codes, which the pre-kernel used for the activation operands).
+__device__ __forceinline__ void widen_strip(uint4 raw, v4i (&B)[2]) {
+  B[0] = widen_codes(make_uint2(raw.x, raw.y));
+  B[1] = widen_codes(make_uint2(raw.z, raw.w));
+}
+
+struct TScales {
+  float sx[8], be[8];               // (s_x/256, -12582912 s_x/256) of the lane's row per row block
+  uint2 swp[2];                     // fp16 s_w of the lane's 4 columns per column block
+};
+
+__device__ __forceinline__ float sw_of(const TScales& sc, int j, int e) {
+  const uint32_t w = (e < 2) ? sc.swp[j].x : sc.swp[j].y;
+  return h2f(static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xFFFFu)));
+}
+
+__device__ __forceinline__ void rescale(v4f& acc, const v4i& p, const TScales& sc, int i, int j) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int pe = p[e];                     // scalar copy: see as_float()
+    const float t = __builtin_fmaf(as_float(pe), sc.sx[i], sc.be[i]);
+    acc[e] = __builtin_fmaf(t, sw_of(sc, j, e), acc[e]);
+  }
+}
+
+// All of this wave's copies and LDS reads done, then every wave's.
+constexpr int kWaitAll = 0x0070;                                   // vmcnt(0) lgkmcnt(0)
+// Copies of the newest KAHEAD-1 groups may still be in flight.
+constexpr int kWaitAhead = 0x0070 | (kCopiesPerGroup * (KAHEAD - 1));
+static_assert(kCopiesPerGroup * (KAHEAD - 1) < 16, "vmcnt field");
+
+template <bool Y_F16, bool GELU>
+__device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __restrict__ a_ops,
+                                       const float* __restrict__ a_pairs,
+                                       const uint8_t* __restrict__ w_codes,
+                                       const uint16_t* __restrict__ w_scales,
+                                       const float* __restrict__ D,
+                                       const uint16_t* __restrict__ L2t, int R,
+                                       const float* __restrict__ bias, void* __restrict__ Y,
+                                       int64_t M, int64_t N, int64_t K, int64_t ldy, int64_t m0,
+                                       int64_t n0) {
+  constexpr int RB = 8, CB = 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int rl = lane & 15, q = lane >> 4;
+  const int G = static_cast<int>(K / kGroup);
+  const int64_t Mb = (M + 15) / 16, Ns = (N + 31) / 32;
+  const int64_t band = m0 / 128;
+  // this wave's copies: activation row blocks 2w and 2w+1 of the band (blocks
+  // past the last row clamped to it: their outputs are never stored), its own
+  // weight strip, a quarter of the band's scale pairs, and the scales of all
+  // four strips (every wave writes the same 256 bytes, which keeps the copy
+  // count of all waves equal)
+  auto clamp_b = [&](int64_t b) { return b < Mb ? b : Mb - 1; };
+  auto clamp_s = [&](int64_t s) { return s < Ns ? s : Ns - 1; };
+  const uint8_t* ga0 = a_ops + clamp_b(m0 / 16 + 2 * wave) * G * kBlk + 16 * lane;
+  const uint8_t* ga1 = a_ops + clamp_b(m0 / 16 + 2 * wave + 1) * G * kBlk + 16 * lane;
+  const uint8_t* gb = w_codes + clamp_s(n0 / 32 + wave) * G * kBlk + 16 * lane;
+  const float* gp = a_pairs + band * G * kPairBlk + 64 * wave + lane;
+  const uint16_t* gw = w_scales + clamp_s(n0 / 32 + q) * G * kWsBlk + 2 * rl;
+
+  auto copy = [&](TStage& s, int g) {
+    g = g < G ? g : G - 1;
+    const int64_t o = static_cast<int64_t>(g) * kBlk;
+    __builtin_amdgcn_global_load_lds(ga0 + o, LDSP(&s.a[2 * wave][0]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(ga1 + o, LDSP(&s.a[2 * wave + 1][0]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(gb + o, LDSP(&s.b[wave][0]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(gp + static_cast<int64_t>(g) * kPairBlk,
+                                     LDSP(&s.p[64 * wave]), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(gw + static_cast<int64_t>(g) * kWsBlk, LDSP(&s.w[0][0]), 4,
+                                     0, 0);
+  };
+  auto read_ops = [&](v4i (&A)[RB], v4i (&B)[CB], const TStage& s) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) A[i] = *reinterpret_cast<const v4i*>(&s.a[i][16 * lane]);
+    widen_strip(*reinterpret_cast<const uint4*>(&s.b[wave][16 * lane]), B);
+  };
+  // pairs: row block i of the lane's row at ((i/2)*16 + rl)*4 + (i%2)*2
+  auto read_scales = [&](TScales& sc, const TStage& s) {
+#pragma unroll
+    for (int h = 0; h < RB / 2; ++h) {
+      const float4 v = *reinterpret_cast<const float4*>(&s.p[(h * 16 + rl) * 4]);
+      sc.sx[2 * h] = v.x;
+      sc.be[2 * h] = v.y;
+      sc.sx[2 * h + 1] = v.z;
+      sc.be[2 * h + 1] = v.w;
+    }
+    const uint4 w = *reinterpret_cast<const uint4*>(&s.w[wave][8 * q]);
+    sc.swp[0] = make_uint2(w.x, w.y);
+    sc.swp[1] = make_uint2(w.z, w.w);
+  };
+
+#pragma unroll
+  for (int c = 0; c < KAHEAD; ++c) copy(st[c], c);
+
+  // the low-rank branch starts the accumulators while the first groups copy
+  v4f acc[RB][CB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  lowrank_up_at<16 * RB, 16 * CB>(acc, D, L2t, R, M, N, m0, n0 + 32 * wave);
+
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  __builtin_amdgcn_s_barrier();
+  const v4i seed = v4i{kMagicSeed, kMagicSeed, kMagicSeed, kMagicSeed};
+  v4i A[RB], B[CB], P[RB][CB];
+  TScales cur;
+  read_ops(A, B, st[0]);
+  read_scales(cur, st[0]);
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j) P[i][j] = mfma_i8_16x16x64(B[j], A[i], seed);
+
+  // iteration g: rescale group g's partials block by block and, behind each
+  // block, issue group g+1's matrix instruction into the same registers.
+  // Group g+KAHEAD is copied into the stage group g-1 left (every wave read
+  // it before the previous barrier); group g+1's copies, issued KAHEAD-1
+  // iterations ago, are waited for before this iteration's barrier.
+  int s1 = 1;                                   // stage of group g+1
+  for (int g = 0; g + 1 < G; ++g) {
+    const int sc_ = (s1 + KAHEAD - 1) & (KSTAGES - 1);   // stage of group g+KAHEAD
+    copy(st[sc_], g + KAHEAD);
+    __builtin_amdgcn_s_waitcnt(kWaitAhead);
+    __builtin_amdgcn_s_barrier();
+    read_ops(A, B, st[s1]);
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+#pragma unroll
+      for (int j = 0; j < CB; ++j) {
+        rescale(acc[i][j], P[i][j], cur, i, j);
+        P[i][j] = mfma_i8_16x16x64(B[j], A[i], seed);
+      }
+    }
+    // four blocks' rescale (32 ops) cover the LDS reads of the first
+    // operands; then one matrix instruction behind each block's 8 ops
+#pragma unroll
+    for (int b = 0; b < 4; ++b) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+    for (int b = 0; b < RB * CB - 4; ++b) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    read_scales(cur, st[s1]);
+    s1 = (s1 + 1) & (KSTAGES - 1);
+  }
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j) rescale(acc[i][j], P[i][j], cur, i, j);
+
+  // copies of groups past the end land in stages nobody reads; wait for them
+  // before the LDS is used for the output
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  __builtin_amdgcn_s_barrier();
+  if constexpr (Y_F16) {
+    static_assert(sizeof(TStage) * KSTAGES >= 128 * 256, "a 128 x 128 fp16 tile in LDS");
+    if (m0 + 128 <= M && n0 + 128 <= N &&
+        ((reinterpret_cast<uintptr_t>(Y) | static_cast<uintptr_t>(ldy * 2)) % 16) == 0) {
+      // the whole tile through LDS: 128 rows of 256 bytes, the 16-byte
+      // units of row r XOR-swizzled by r % 16; then every store instruction
+      // writes 4 rows of 256 bytes (8 whole cache lines)
+      uint8_t* lds = reinterpret_cast<uint8_t*>(&st[0]);
+      float bv[CB][4];
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          bv[j][e] = bias != nullptr ? bias[n0 + 32 * wave + 16 * j + 4 * q + e] : 0.f;
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int row = 16 * i + rl;
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = acc[i][j][e] + bv[j][e];
+            if constexpr (GELU) v[e] = gelu_tanh_f32(v[e]);
+          }
+          const uint32_t lo = static_cast<uint32_t>(f2h(v[0])) | (static_cast<uint32_t>(f2h(v[1])) << 16);
+          const uint32_t hi = static_cast<uint32_t>(f2h(v[2])) | (static_cast<uint32_t>(f2h(v[3])) << 16);
+          const int unit = 4 * wave + 2 * j + (q >> 1);     // 16-byte unit of the 4 columns
+          *reinterpret_cast<uint2*>(lds + row * 256 + ((unit ^ (row & 15)) << 4) + ((q & 1) << 3)) =
+              make_uint2(lo, hi);
+        }
+      }
+      __syncthreads();
+      _Float16* Yh = static_cast<_Float16*>(Y);
+      const int u = lane & 15, r4 = lane >> 4;
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int row = 32 * wave + 4 * it + r4;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + row * 256 + ((u ^ (row & 15)) << 4));
+        *reinterpret_cast<uint4*>(Yh + (m0 + row) * ldy + n0 + 8 * u) = v;
+      }
+      return;
+    }
+  }
+  bias_store_at<16 * RB, 16 * CB, Y_F16, GELU>(acc, bias, Y, M, N, ldy, m0, n0 + 32 * wave);
+}
+
+template <bool Y_F16, bool GELU>
+__global__ __launch_bounds__(NT, 2) void k2t_w4a4_kernel(
+    const uint8_t* __restrict__ a_ops, const float* __restrict__ a_pairs,
+    const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales,
+    const float* __restrict__ D, const uint16_t* __restrict__ L2t, int R,
+    const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N, int64_t K,
+    int64_t ldy, int tiles_m, int tiles_n) {
+  __shared__ TStage st[KSTAGES];
+  const int T = tiles_m * tiles_n;
+  int tm, tn;
+  banded_tile(xcd_contiguous(static_cast<int>(blockIdx.x), T), tiles_m, tiles_n, tm, tn);
+  tile_t<Y_F16, GELU>(st, a_ops, a_pairs, w_codes, w_scales, D, L2t, R, bias, Y, M, N, K, ldy,
+                      static_cast<int64_t>(tm) * 128, static_cast<int64_t>(tn) * 128);
+}
+
+}  // namespace
+
+hipError_t launch_k2t(const uint8_t* a_ops, const float* a_pairs, const uint8_t* w_codes_t,
+                      const uint16_t* w_scales_t, const float* D, const uint16_t* L2t, int R,
+                      const float* bias, void* Y, bool y_f16, int64_t M, int64_t N, int64_t K,
+                      int64_t ldy, bool gelu, hipStream_t stream) {
+  const int tiles_m = static_cast<int>((M + 127) / 128);
+  const int tiles_n = static_cast<int>((N + 127) / 128);
+  const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n)), block(NT);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, a_ops, a_pairs, w_codes_t, w_scales_t, D,
+                       L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n);
+  };
+  if (y_f16)
+    gelu ? go(k2t_w4a4_kernel<true, true>) : go(k2t_w4a4_kernel<true, false>);
+  else
+    gelu ? go(k2t_w4a4_kernel<false, true>) : go(k2t_w4a4_kernel<false, false>);
+  return hipGetLastError();
+}
+
+}  // namespace svdq

@@ -1,0 +1,83 @@
+"""The tiled INT4 layouts of include/svdq.h ("Tiled INT4 path"), written out in
+numpy from the documented index formulas, for the tests: to check the host
+packing of the weights and to read back (and build) the activation operands
+and scale pairs of the tiled kernels."""
+from __future__ import annotations
+
+import numpy as np
+
+# order of the 16 codes of a lane's k-chunk inside its 16 operand bytes:
+# byte t holds code PERM[t] (even codes of each 8, then the odd ones)
+PERM = np.array([0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15])
+
+
+def unpack(codes: np.ndarray) -> np.ndarray:
+    """rows x K/2 canonical bytes -> rows x K int8 codes (two's complement nibbles)."""
+    b = np.asarray(codes, dtype=np.int16)
+    lo, hi = b & 15, (b >> 4) & 15
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int16)
+    out[..., 0::2] = np.where(lo >= 8, lo - 16, lo)
+    out[..., 1::2] = np.where(hi >= 8, hi - 16, hi)
+    return out.astype(np.int8)
+
+
+def tile_act_ops(codes: np.ndarray, M: int, K: int) -> np.ndarray:
+    """canonical activation codes (M x K/2) -> a_ops_t bytes (rows past M in the
+    last block repeat row M-1)."""
+    G, nb = K // 64, (M + 15) // 16
+    q = unpack(codes).astype(np.int16)                       # M x K
+    rows = np.minimum(np.arange(nb * 16), M - 1)
+    q = q[rows]                                              # nb*16 x K
+    # [b, r, g, chunk, 16] -> [b, g, chunk, r, 16] (lane = 16*chunk + r)
+    t = q.reshape(nb, 16, G, 4, 16)[..., PERM].transpose(0, 2, 3, 1, 4)
+    return ((16 * t) & 0xFF).astype(np.uint8).reshape(-1)
+
+
+def untile_act_ops(ops: np.ndarray, M: int, K: int) -> np.ndarray:
+    """a_ops_t bytes -> (nb*16) x K int8 codes, after checking every byte is 16*q."""
+    G, nb = K // 64, (M + 15) // 16
+    v = np.asarray(ops, dtype=np.uint8)[:nb * G * 1024].view(np.int8).astype(np.int16)
+    assert np.all(v % 16 == 0), "operand bytes must be multiples of 16"
+    v = (v // 16).reshape(nb, G, 4, 16, 16)                  # [b, g, chunk, r, byte]
+    inv = np.argsort(PERM)
+    v = v[..., inv].transpose(0, 3, 1, 2, 4)                 # [b, r, g, chunk, code]
+    return v.reshape(nb * 16, K).astype(np.int8)
+
+
+def pair_index(M: int, K: int):
+    """(row, group) -> flat float index of the row's s/256 in a_pairs_t."""
+    G = K // 64
+    rows = np.arange(((M + 127) // 128) * 128)
+    t, i, r = rows // 128, (rows % 128) // 16, rows % 16
+    base = ((i // 2) * 16 + r) * 4 + (i % 2) * 2
+    return t[:, None] * G * 256 + np.arange(G)[None, :] * 256 + base[:, None]
+
+
+def tile_pairs(scales: np.ndarray, M: int, K: int) -> np.ndarray:
+    """fp16 activation scales (M x G) -> a_pairs_t floats (s/256, -12582912 s/256);
+    rows past M get zeros."""
+    G = K // 64
+    nt = (M + 127) // 128
+    s = np.zeros((nt * 128, G), dtype=np.float64)
+    s[:M] = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    out = np.zeros(nt * G * 256, dtype=np.float32)
+    idx = pair_index(M, K)
+    out[idx] = (s / 256.0).astype(np.float32)
+    out[idx + 1] = (s * (-12582912.0 / 256.0)).astype(np.float32)
+    return out
+
+
+def tile_w(w_codes: np.ndarray, w_scales: np.ndarray, N: int, K: int):
+    """canonical weight codes (N x K/2) and fp16 scale bits (N x G) -> (w_codes_t
+    bytes, w_scales_t uint16), zero past N."""
+    G, ns = K // 64, (N + 31) // 32
+    c = np.zeros((ns * 32, K // 2), dtype=np.uint8)
+    c[:N] = w_codes
+    # [s, j, r, g, q, 8] -> [s, g, q, r, j, 8]  (lane = 16q + r, bytes 8j .. 8j+7)
+    ct = c.reshape(ns, 2, 16, G, 4, 8).transpose(0, 3, 4, 2, 1, 5)
+    sc = np.zeros((ns * 32, G), dtype=np.uint16)
+    sc[:N] = np.asarray(w_scales).view(np.uint16) if np.asarray(w_scales).dtype != np.uint16 \
+        else w_scales
+    # column 32s + 16j + 4q + e -> entry 8q + 4j + e of block (s, g)
+    st = sc.reshape(ns, 2, 4, 4, G).transpose(0, 4, 2, 1, 3)
+    return np.ascontiguousarray(ct).reshape(-1), np.ascontiguousarray(st).reshape(-1)

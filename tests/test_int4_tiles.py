@@ -1,0 +1,42 @@
+"""The tiled INT4 weight layouts on the CPU: the library's packer against the
+layout formulas of svdq.h written out in numpy (tests/int4_tiles.py), and the
+numpy helpers' own round trips (they build and read the GPU tests' operands)."""
+import numpy as np
+import pytest
+
+import int4_tiles as T
+
+sq = pytest.importorskip("bit_post_quantized_smooth_amd")
+
+
+@pytest.mark.parametrize("N,K", [(1, 64), (31, 192), (32, 64), (33, 128), (100, 320), (257, 640)])
+def test_pack_w4a4_tiles_matches_the_layout(N, K):
+    rng = np.random.default_rng(N * 1000 + K)
+    wc = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    ws = rng.integers(0, 1 << 16, size=(N, K // 64), dtype=np.uint16)
+    ct, st = sq.pack_w4a4_tiles(wc, ws, K)
+    ect, est = T.tile_w(wc, ws, N, K)
+    assert ct.size == sq.int4_w_codes_tiled_bytes(N, K) == ect.size
+    assert st.size * 2 == sq.int4_w_scales_tiled_bytes(N, K) == est.size * 2
+    assert np.array_equal(ct, ect) and np.array_equal(st, est)
+    # a permutation with zero padding: every canonical byte appears exactly once
+    assert np.array_equal(np.sort(ct)[-wc.size:], np.sort(wc.reshape(-1)))
+    assert np.count_nonzero(ct) <= np.count_nonzero(wc)
+
+
+@pytest.mark.parametrize("M,K", [(1, 64), (17, 128), (129, 192), (300, 640)])
+def test_activation_tile_helpers_round_trip(M, K):
+    rng = np.random.default_rng(M + K)
+    q = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    codes = ((q[:, 0::2] & 15) | ((q[:, 1::2] & 15) << 4)).astype(np.uint8)
+    ops = T.tile_act_ops(codes, M, K)
+    assert ops.size == sq.int4_act_tiled_bytes(M, K)
+    back = T.untile_act_ops(ops, M, K)
+    assert np.array_equal(back[:M], q)
+    assert np.all(back[M:] == q[M - 1])
+    s = rng.standard_normal((M, K // 64)).astype(np.float16)
+    p = T.tile_pairs(s, M, K)
+    assert p.size * 4 == sq.int4_pairs_tiled_bytes(M, K)
+    idx = T.pair_index(M, K)[:M]
+    assert np.array_equal(p[idx], (s.astype(np.float64) / 256).astype(np.float32))
+    assert np.array_equal(p[idx + 1], (s.astype(np.float64) * -49152.0).astype(np.float32))
