@@ -266,6 +266,19 @@ int svdq_quantize_act_lowrank_down_tiled(const void* X, int x_dtype, int64_t M, 
                    "svdq_quantize_act_lowrank_down_tiled launch");
 }
 
+namespace {
+// K2T adds each lane's offset into the tiled weight scales in 32 bits, and
+// its grid can hold up to 3 x 1024 more workgroups than tiles (split tails).
+int check_k2t_shape(int64_t M, int64_t N, int64_t K, const char* fn) {
+  if (((N + 31) / 32) * (K / SVDQ_GROUP) * 64 > int64_t{0xFFFFFFFF} ||
+      ((M + 127) / 128) * ((N + 127) / 128) > 0x7FFFFFFF - 4096) {
+    set_error("%s: N=%lld K=%lld too large for the tiled kernel", fn, (long long)N, (long long)K);
+    return SVDQ_ERR_SHAPE;
+  }
+  return SVDQ_OK;
+}
+}  // namespace
+
 int svdq_w4a4_gemm_lowrank_up_tiled(const uint8_t* a_ops_t, const float* a_pairs_t,
                                     const uint8_t* w_codes_t, const uint16_t* w_scales_t,
                                     const float* D, const uint16_t* L2t, int32_t R,
@@ -277,6 +290,7 @@ int svdq_w4a4_gemm_lowrank_up_tiled(const uint8_t* a_ops_t, const float* a_pairs
   if (int s = validate_k2(a_ops_t, a_pairs_t, w_codes_t, w_scales_t, D, L2t, R, bias, Y, y_dtype,
                           M, N, K, ldy, SVDQ_GROUP, fn))
     return s;
+  if (int s = check_k2t_shape(M, N, K, fn)) return s;
   if (int s = check_activation(activation, fn)) return s;
   if (int s = device_ready()) return s;
   return check_hip(launch_k2t(a_ops_t, a_pairs_t, w_codes_t, w_scales_t, D, L2t, R, bias, Y,
@@ -322,6 +336,7 @@ int svdq_linear_tiled(const void* X, int x_dtype, int64_t ldx, const float* inv_
   if (int s = validate_k2(a_ops, a_pairs, w_codes_t, w_scales_t, D, L2t, R, bias, Y, y_dtype, M,
                           N, K, ldy, SVDQ_GROUP, fn))
     return s;
+  if (int s = check_k2t_shape(M, N, K, fn)) return s;
   if (int s = device_ready()) return s;
   if (int s = check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1p, R, a_ops,
                                   a_pairs, kK1Int4Tiled, D, stream),

@@ -34,7 +34,8 @@
 // weight strip is its own and only the activation operands are shared. The
 // weight fragment is the matrix instruction's first operand, so a lane holds 4
 // consecutive columns of one row of each block (as in K2). Tiles run in K2's
-// XCD-aware banded order.
+// XCD-aware banded order; when the last round would leave most workgroup
+// slots idle its tiles are cut into 64 x 128 halves or 64 x 64 quarters.
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -51,37 +52,49 @@ constexpr int kPairBlk = 256;       // scale pairs of one 128-row band and group
 constexpr int kWsBlk = 32;          // fp16 weight scales of one 32-column strip and group
 constexpr int KSTAGES = 4;          // LDS ring depth
 constexpr int KAHEAD = KSTAGES - 1; // groups copied ahead of the one computed
-constexpr int kCopiesPerGroup = 5;  // direct-to-LDS loads per wave and group
 
-// One group's operands for the whole tile.
+// One group's operands for the whole tile (a 128 x 128 tile uses all of it).
 struct alignas(16) TStage {
-  uint8_t a[8][kBlk];               // activation operands of the 8 row blocks (int8 16q)
+  uint8_t a[8][kBlk];               // activation operands of the tile's row blocks (int8 16q)
   uint8_t b[4][kBlk];               // 4-bit weight codes of the 4 waves' strips
-  float p[kPairBlk];                // scale pairs of the 128 rows
-  uint16_t w[4][kWsBlk];            // fp16 weight scales of the 4 strips
+  float p[kPairBlk];                // scale pairs of the 128-row band
+  uint16_t w[4][kWsBlk];            // fp16 weight scales of 4 strips
 };
 
 #define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
 
-// The 16 bytes of 4-bit codes a lane holds for its strip (8 for each of its
-// two column blocks) -> the two int8 operands (16*q, the order of
-// widen_codes, which the pre-kernel used for the activation operands).
-__device__ __forceinline__ void widen_strip(uint4 raw, v4i (&B)[2]) {
-  B[0] = widen_codes(make_uint2(raw.x, raw.y));
-  B[1] = widen_codes(make_uint2(raw.z, raw.w));
-}
+// Tile shapes: RB row blocks of 16 (every wave holds all of them) and CB
+// column blocks of 16 per wave. 8 x 2: the 128 x 128 tile; 4 x 2 (64 x 128)
+// and 4 x 1 (64 x 64): the pieces a thin last round is cut into.
+template <int RB, int CB>
+struct Shape {
+  static constexpr int ROWS = 16 * RB;
+  static constexpr int WCOLS = 16 * CB;             // columns per wave
+  static constexpr int COLS = 4 * WCOLS;
+  static constexpr int ACOPY = RB / 4;              // activation blocks each wave copies
+  static constexpr int COPIES = ACOPY + 3;          // direct loads per wave and group
+  static constexpr int NBLK = RB * CB;              // 16 x 16 blocks per wave
+  // wait until the copies of the newest KAHEAD-1 groups are the only ones in flight
+  static constexpr int WAIT_AHEAD = 0x0070 | (COPIES * (KAHEAD - 1));
+  static_assert(COPIES * (KAHEAD - 1) < 16, "vmcnt field");
+};
+constexpr int kWaitAll = 0x0070;                    // vmcnt(0) lgkmcnt(0)
 
+template <int RB, int CB>
 struct TScales {
-  float sx[8], be[8];               // (s_x/256, -12582912 s_x/256) of the lane's row per row block
-  uint2 swp[2];                     // fp16 s_w of the lane's 4 columns per column block
+  float sx[RB], be[RB];             // (s_x/256, -12582912 s_x/256) of the lane's row per row block
+  uint2 swp[CB];                    // fp16 s_w of the lane's 4 columns per column block
 };
 
-__device__ __forceinline__ float sw_of(const TScales& sc, int j, int e) {
+template <int RB, int CB>
+__device__ __forceinline__ float sw_of(const TScales<RB, CB>& sc, int j, int e) {
   const uint32_t w = (e < 2) ? sc.swp[j].x : sc.swp[j].y;
   return h2f(static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xFFFFu)));
 }
 
-__device__ __forceinline__ void rescale(v4f& acc, const v4i& p, const TScales& sc, int i, int j) {
+template <int RB, int CB>
+__device__ __forceinline__ void rescale(v4f& acc, const v4i& p, const TScales<RB, CB>& sc, int i,
+                                        int j) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int pe = p[e];                     // scalar copy: see as_float()
@@ -90,13 +103,8 @@ __device__ __forceinline__ void rescale(v4f& acc, const v4i& p, const TScales& s
   }
 }
 
-// All of this wave's copies and LDS reads done, then every wave's.
-constexpr int kWaitAll = 0x0070;                                   // vmcnt(0) lgkmcnt(0)
-// Copies of the newest KAHEAD-1 groups may still be in flight.
-constexpr int kWaitAhead = 0x0070 | (kCopiesPerGroup * (KAHEAD - 1));
-static_assert(kCopiesPerGroup * (KAHEAD - 1) < 16, "vmcnt field");
-
-template <bool Y_F16, bool GELU>
+// One tile of Y: rows m0 .. m0 + 16*RB - 1, columns n0 .. n0 + 64*CB - 1.
+template <int RB, int CB, bool Y_F16, bool GELU>
 __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __restrict__ a_ops,
                                        const float* __restrict__ a_pairs,
                                        const uint8_t* __restrict__ w_codes,
@@ -106,55 +114,77 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
                                        const float* __restrict__ bias, void* __restrict__ Y,
                                        int64_t M, int64_t N, int64_t K, int64_t ldy, int64_t m0,
                                        int64_t n0) {
-  constexpr int RB = 8, CB = 2;
+  using S = Shape<RB, CB>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int rl = lane & 15, q = lane >> 4;
   const int G = static_cast<int>(K / kGroup);
   const int64_t Mb = (M + 15) / 16, Ns = (N + 31) / 32;
-  const int64_t band = m0 / 128;
-  // this wave's copies: activation row blocks 2w and 2w+1 of the band (blocks
-  // past the last row clamped to it: their outputs are never stored), its own
-  // weight strip, a quarter of the band's scale pairs, and the scales of all
-  // four strips (every wave writes the same 256 bytes, which keeps the copy
-  // count of all waves equal)
+  const int64_t nw = n0 + S::WCOLS * wave;          // the wave's first column
+  const int rb0 = static_cast<int>((m0 % 128) / 16);   // the tile's first row block in its band
+  const int rs = (S::WCOLS * wave) / 32;            // the wave's strip among the 4 copied
+  const int hb = CB == 1 ? static_cast<int>((nw / 16) & 1) : 0;   // its half of that strip
+  // this wave's copies: activation row blocks ACOPY*w .. +ACOPY-1 of the tile
+  // (clamped to the last row block: their outputs are never stored), the
+  // strip holding its columns, a quarter of the band's scale pairs, and the
+  // scales of the 4 strips from n0/32 on (every wave writes the same bytes,
+  // which keeps the copy counts equal). Bases are wave-uniform; each lane
+  // adds a 32-bit offset.
   auto clamp_b = [&](int64_t b) { return b < Mb ? b : Mb - 1; };
   auto clamp_s = [&](int64_t s) { return s < Ns ? s : Ns - 1; };
-  const uint8_t* ga0 = a_ops + clamp_b(m0 / 16 + 2 * wave) * G * kBlk + 16 * lane;
-  const uint8_t* ga1 = a_ops + clamp_b(m0 / 16 + 2 * wave + 1) * G * kBlk + 16 * lane;
-  const uint8_t* gb = w_codes + clamp_s(n0 / 32 + wave) * G * kBlk + 16 * lane;
-  const float* gp = a_pairs + band * G * kPairBlk + 64 * wave + lane;
-  const uint16_t* gw = w_scales + clamp_s(n0 / 32 + q) * G * kWsBlk + 2 * rl;
+  const uint8_t* ga[S::ACOPY];
+#pragma unroll
+  for (int c = 0; c < S::ACOPY; ++c)
+    ga[c] = a_ops + clamp_b(m0 / 16 + S::ACOPY * wave + c) * G * kBlk;
+  const uint8_t* gb = w_codes + clamp_s(nw / 32) * G * kBlk;
+  const float* gp = a_pairs + (m0 / 128) * G * kPairBlk + 64 * wave;
+  const uint32_t lo16 = 16u * static_cast<uint32_t>(lane);
+  const uint32_t lo4 = 4u * static_cast<uint32_t>(lane);
+  const uint32_t low = static_cast<uint32_t>((clamp_s(n0 / 32 + q) * G * kWsBlk + 2 * rl) * 2);
 
   auto copy = [&](TStage& s, int g) {
     g = g < G ? g : G - 1;
     const int64_t o = static_cast<int64_t>(g) * kBlk;
-    __builtin_amdgcn_global_load_lds(ga0 + o, LDSP(&s.a[2 * wave][0]), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(ga1 + o, LDSP(&s.a[2 * wave + 1][0]), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(gb + o, LDSP(&s.b[wave][0]), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(gp + static_cast<int64_t>(g) * kPairBlk,
-                                     LDSP(&s.p[64 * wave]), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds(gw + static_cast<int64_t>(g) * kWsBlk, LDSP(&s.w[0][0]), 4,
-                                     0, 0);
+#pragma unroll
+    for (int c = 0; c < S::ACOPY; ++c)
+      __builtin_amdgcn_global_load_lds(ga[c] + o + lo16, LDSP(&s.a[S::ACOPY * wave + c][0]), 16, 0,
+                                       0);
+    __builtin_amdgcn_global_load_lds(gb + o + lo16, LDSP(&s.b[wave][0]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const uint8_t*>(gp + static_cast<int64_t>(g) * kPairBlk) + lo4,
+        LDSP(&s.p[64 * wave]), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const uint8_t*>(w_scales + static_cast<int64_t>(g) * kWsBlk) + low,
+        LDSP(&s.w[0][0]), 4, 0, 0);
   };
   auto read_ops = [&](v4i (&A)[RB], v4i (&B)[CB], const TStage& s) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) A[i] = *reinterpret_cast<const v4i*>(&s.a[i][16 * lane]);
-    widen_strip(*reinterpret_cast<const uint4*>(&s.b[wave][16 * lane]), B);
+    const uint4 raw = *reinterpret_cast<const uint4*>(&s.b[wave][16 * lane]);
+    if constexpr (CB == 2) {
+      B[0] = widen_codes(make_uint2(raw.x, raw.y));
+      B[1] = widen_codes(make_uint2(raw.z, raw.w));
+    } else {
+      B[0] = widen_codes(hb ? make_uint2(raw.z, raw.w) : make_uint2(raw.x, raw.y));
+    }
   };
-  // pairs: row block i of the lane's row at ((i/2)*16 + rl)*4 + (i%2)*2
-  auto read_scales = [&](TScales& sc, const TStage& s) {
+  // pairs: row block i of the band, row r, at ((i/2)*16 + r)*4 + (i%2)*2
+  auto read_scales = [&](TScales<RB, CB>& sc, const TStage& s) {
 #pragma unroll
     for (int h = 0; h < RB / 2; ++h) {
-      const float4 v = *reinterpret_cast<const float4*>(&s.p[(h * 16 + rl) * 4]);
+      const float4 v = *reinterpret_cast<const float4*>(&s.p[((rb0 / 2 + h) * 16 + rl) * 4]);
       sc.sx[2 * h] = v.x;
       sc.be[2 * h] = v.y;
       sc.sx[2 * h + 1] = v.z;
       sc.be[2 * h + 1] = v.w;
     }
-    const uint4 w = *reinterpret_cast<const uint4*>(&s.w[wave][8 * q]);
-    sc.swp[0] = make_uint2(w.x, w.y);
-    sc.swp[1] = make_uint2(w.z, w.w);
+    const uint4 w = *reinterpret_cast<const uint4*>(&s.w[rs][8 * q]);
+    if constexpr (CB == 2) {
+      sc.swp[0] = make_uint2(w.x, w.y);
+      sc.swp[1] = make_uint2(w.z, w.w);
+    } else {
+      sc.swp[0] = hb ? make_uint2(w.z, w.w) : make_uint2(w.x, w.y);
+    }
   };
 
 #pragma unroll
@@ -166,13 +196,13 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
   for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int j = 0; j < CB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  lowrank_up_at<16 * RB, 16 * CB>(acc, D, L2t, R, M, N, m0, n0 + 32 * wave);
+  lowrank_up_at<16 * RB, 16 * CB>(acc, D, L2t, R, M, N, m0, nw);
 
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __builtin_amdgcn_s_barrier();
   const v4i seed = v4i{kMagicSeed, kMagicSeed, kMagicSeed, kMagicSeed};
   v4i A[RB], B[CB], P[RB][CB];
-  TScales cur;
+  TScales<RB, CB> cur;
   read_ops(A, B, st[0]);
   read_scales(cur, st[0]);
 #pragma unroll
@@ -185,11 +215,11 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
   // Group g+KAHEAD is copied into the stage group g-1 left (every wave read
   // it before the previous barrier); group g+1's copies, issued KAHEAD-1
   // iterations ago, are waited for before this iteration's barrier.
+  constexpr int LEAD = S::NBLK < 4 ? S::NBLK : 4;
   int s1 = 1;                                   // stage of group g+1
   for (int g = 0; g + 1 < G; ++g) {
-    const int sc_ = (s1 + KAHEAD - 1) & (KSTAGES - 1);   // stage of group g+KAHEAD
-    copy(st[sc_], g + KAHEAD);
-    __builtin_amdgcn_s_waitcnt(kWaitAhead);
+    copy(st[(s1 + KAHEAD - 1) & (KSTAGES - 1)], g + KAHEAD);
+    __builtin_amdgcn_s_waitcnt(S::WAIT_AHEAD);
     __builtin_amdgcn_s_barrier();
     read_ops(A, B, st[s1]);
 #pragma unroll
@@ -200,15 +230,17 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
         P[i][j] = mfma_i8_16x16x64(B[j], A[i], seed);
       }
     }
-    // four blocks' rescale (32 ops) cover the LDS reads of the first
-    // operands; then one matrix instruction behind each block's 8 ops
+    // the first blocks' rescale covers the LDS reads of the first operands;
+    // then one matrix instruction behind each block's 8 ops
 #pragma unroll
-    for (int b = 0; b < 4; ++b) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    for (int b = 0; b < LEAD; ++b) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
 #pragma unroll
-    for (int b = 0; b < RB * CB - 4; ++b) {
+    for (int b = 0; b < S::NBLK - LEAD; ++b) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
     }
+#pragma unroll
+    for (int b = 0; b < LEAD; ++b) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_barrier(0);
     read_scales(cur, st[s1]);
     s1 = (s1 + 1) & (KSTAGES - 1);
@@ -222,7 +254,7 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
   // before the LDS is used for the output
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __builtin_amdgcn_s_barrier();
-  if constexpr (Y_F16) {
+  if constexpr (Y_F16 && RB == 8 && CB == 2) {
     static_assert(sizeof(TStage) * KSTAGES >= 128 * 256, "a 128 x 128 fp16 tile in LDS");
     if (m0 + 128 <= M && n0 + 128 <= N &&
         ((reinterpret_cast<uintptr_t>(Y) | static_cast<uintptr_t>(ldy * 2)) % 16) == 0) {
@@ -235,7 +267,7 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
       for (int j = 0; j < CB; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          bv[j][e] = bias != nullptr ? bias[n0 + 32 * wave + 16 * j + 4 * q + e] : 0.f;
+          bv[j][e] = bias != nullptr ? bias[nw + 16 * j + 4 * q + e] : 0.f;
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
         const int row = 16 * i + rl;
@@ -266,22 +298,41 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
       return;
     }
   }
-  bias_store_at<16 * RB, 16 * CB, Y_F16, GELU>(acc, bias, Y, M, N, ldy, m0, n0 + 32 * wave);
+  bias_store_at<16 * RB, 16 * CB, Y_F16, GELU>(acc, bias, Y, M, N, ldy, m0, nw);
 }
 
+// Workgroups 0 .. n_full-1 take the first n_full 128 x 128 tiles of the
+// banded order; the rest take the remaining tiles in `split` pieces (2: 64 x
+// 128 halves, 4: 64 x 64 quarters). A piece wholly outside Y returns at once
+// (the same for every wave of the workgroup, before any barrier).
 template <bool Y_F16, bool GELU>
 __global__ __launch_bounds__(NT, 2) void k2t_w4a4_kernel(
     const uint8_t* __restrict__ a_ops, const float* __restrict__ a_pairs,
     const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales,
     const float* __restrict__ D, const uint16_t* __restrict__ L2t, int R,
     const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N, int64_t K,
-    int64_t ldy, int tiles_m, int tiles_n) {
+    int64_t ldy, int tiles_m, int tiles_n, int n_full, int split) {
   __shared__ TStage st[KSTAGES];
-  const int T = tiles_m * tiles_n;
+  const int b = static_cast<int>(blockIdx.x);
   int tm, tn;
-  banded_tile(xcd_contiguous(static_cast<int>(blockIdx.x), T), tiles_m, tiles_n, tm, tn);
-  tile_t<Y_F16, GELU>(st, a_ops, a_pairs, w_codes, w_scales, D, L2t, R, bias, Y, M, N, K, ldy,
-                      static_cast<int64_t>(tm) * 128, static_cast<int64_t>(tn) * 128);
+  if (b < n_full) {
+    banded_tile(xcd_contiguous(b, n_full), tiles_m, tiles_n, tm, tn);
+    tile_t<8, 2, Y_F16, GELU>(st, a_ops, a_pairs, w_codes, w_scales, D, L2t, R, bias, Y, M, N, K,
+                              ldy, static_cast<int64_t>(tm) * 128, static_cast<int64_t>(tn) * 128);
+    return;
+  }
+  const int u = b - n_full;
+  banded_tile(n_full + u / split, tiles_m, tiles_n, tm, tn);
+  const int part = u % split;
+  const int64_t m0 = static_cast<int64_t>(tm) * 128 + 64 * (split == 2 ? part : part >> 1);
+  const int64_t n0 = static_cast<int64_t>(tn) * 128 + (split == 4 ? 64 * (part & 1) : 0);
+  if (m0 >= M || n0 >= N) return;
+  if (split == 2)
+    tile_t<4, 2, Y_F16, GELU>(st, a_ops, a_pairs, w_codes, w_scales, D, L2t, R, bias, Y, M, N, K,
+                              ldy, m0, n0);
+  else
+    tile_t<4, 1, Y_F16, GELU>(st, a_ops, a_pairs, w_codes, w_scales, D, L2t, R, bias, Y, M, N, K,
+                              ldy, m0, n0);
 }
 
 }  // namespace
@@ -292,10 +343,18 @@ hipError_t launch_k2t(const uint8_t* a_ops, const float* a_pairs, const uint8_t*
                       int64_t ldy, bool gelu, hipStream_t stream) {
   const int tiles_m = static_cast<int>((M + 127) / 128);
   const int tiles_n = static_cast<int>((N + 127) / 128);
-  const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n)), block(NT);
+  const int T = tiles_m * tiles_n;
+  // the tiles of a thin last round are cut into halves or quarters, so that
+  // they fill more of the resident workgroup slots
+  const int S = resident_slots();
+  const int left = T < S ? T : T % S;
+  const int split = (left > 0 && 4 * left <= S) ? 4 : (left > 0 && 2 * left <= S) ? 2 : 1;
+  const int n_split = split > 1 ? left : 0;
+  const int n_full = T - n_split;
+  const dim3 grid(static_cast<unsigned>(n_full + split * n_split)), block(NT);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, a_ops, a_pairs, w_codes_t, w_scales_t, D,
-                       L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n);
+                       L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n, n_full, split);
   };
   if (y_f16)
     gelu ? go(k2t_w4a4_kernel<true, true>) : go(k2t_w4a4_kernel<true, false>);
