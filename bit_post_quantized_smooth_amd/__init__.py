@@ -11,7 +11,8 @@ from .api import (Conv2d, Linear, Prepared, channel_absmax, clock_mark, clock_pr
                   linear_tiled_workspace_bytes, pack_w4a4_tiles, quantize_act_lowrank_down_tiled,
                   w4a4_gemm_lowrank_up_tiled,
                   conv2d, conv2d_mx, conv_out_size, conv_patch_absmax, debug_group_partials,
-                  gelu_tanh_f16, linear, linear_mx, linear_mx_workspace_bytes,
+                  gelu_tanh_f16, linear, linear_canonical, linear_canonical_workspace_bytes,
+                  linear_mx, linear_mx_workspace_bytes, pack_lowrank,
                   linear_noalloc, linear_workspace_bytes, mx_codes_tiled_bytes, mx_exps_tiled_bytes,
                   mx_gemm_lowrank_up, pack_lowrank_down, pack_mx_tiles, prepare_weights,
                   prepare_weights_mx, prepare_weights_w4a16, pack_w4a16_tiles,
@@ -26,7 +27,8 @@ __all__ = ["Conv2d", "Linear", "Prepared", "channel_absmax", "clock_mark", "cloc
            "linear_tiled_workspace_bytes", "pack_w4a4_tiles", "quantize_act_lowrank_down_tiled",
            "w4a4_gemm_lowrank_up_tiled", "conv2d", "conv2d_mx",
            "conv_out_size", "conv_patch_absmax", "debug_group_partials",
-           "gelu_tanh_f16", "linear", "linear_mx", "linear_mx_workspace_bytes",
+           "gelu_tanh_f16", "linear", "linear_canonical", "linear_canonical_workspace_bytes",
+           "linear_mx", "linear_mx_workspace_bytes", "pack_lowrank",
            "linear_noalloc", "linear_workspace_bytes", "mx_codes_tiled_bytes", "mx_exps_tiled_bytes",
            "mx_gemm_lowrank_up", "pack_lowrank_down", "pack_mx_tiles", "prepare_weights",
            "prepare_weights_mx", "quantize_act_lowrank_down", "quantize_act_lowrank_down_conv",

@@ -51,6 +51,7 @@ _SIGS = {
     "svdq_prepare_weights": (_int, [_p, _p, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p]),
     "svdq_concat_lora": (_int, [_p, _p, _i64, _i64, _i32, _p, _p, _p, _i32, C.c_float, _p, _p]),
     "svdq_pack_lowrank_down": (_int, [_p, _i64, _i32, _p]),
+    "svdq_pack_lowrank": (_int, [_p, _p, _i64, _i64, _i32, _p, _p]),
     "svdq_quantize_act_lowrank_down": (_int, [_p, _int, _i64, _i64, _i64, _p, _p, _i32, _i32,
                                               _p, _p, _p, _p]),
     "svdq_w4a4_gemm_lowrank_up": (_int, [_p, _p, _p, _p, _p, _p, _i32, _p, _p, _int, _i64, _i64,
@@ -58,6 +59,9 @@ _SIGS = {
     "svdq_linear_workspace_bytes": (C.c_size_t, [_i64, _i64, _i32, _i32]),
     "svdq_linear": (_int, [_p, _int, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _int, _i64, _i64,
                            _i64, _i64, _i32, _p, C.c_size_t, _i32, _p]),
+    "svdq_linear_canonical_workspace_bytes": (C.c_size_t, [_i64, _i64, _i64, _i32, _i32]),
+    "svdq_linear_canonical": (_int, [_p, _int, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _int,
+                                     _i64, _i64, _i64, _i64, _i32, _p, C.c_size_t, _i32, _p]),
     "svdq_prepare_weights_mx": (_int, [_p, _p, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p]),
     "svdq_quantize_act_lowrank_down_mx": (_int, [_p, _int, _i64, _i64, _i64, _p, _p, _i32, _p, _p,
                                                  _p, _p]),

@@ -90,6 +90,22 @@ def pack_lowrank_down(L1t: np.ndarray) -> np.ndarray:
     return out
 
 
+def pack_lowrank(L1: np.ndarray, L2: np.ndarray):
+    """svdq_pack_lowrank: the canonical factors L1 (K x R) and L2 (R x N), fp16 bits
+    -> (L1p, R*K fp16 bits in K1's operand order; L2t, N x R fp16 bits)."""
+    L1 = _c(L1, np.uint16)
+    L2 = _c(L2, np.uint16)
+    K, R = L1.shape
+    R2, N = L2.shape
+    if R2 != R:
+        raise ValueError(f"L1 is {K} x {R} but L2 is {R2} x {N}")
+    L1p = np.empty(R * K, dtype=np.uint16)
+    L2t = np.empty((N, R), dtype=np.uint16)
+    check(lib.svdq_pack_lowrank(_np_ptr(L1), _np_ptr(L2), K, N, R, _np_ptr(L1p), _np_ptr(L2t)),
+          "svdq_pack_lowrank")
+    return L1p, L2t
+
+
 def prepare_weights(W: np.ndarray, lam: np.ndarray, rank: int, want_sigma: bool = False) -> Prepared:
     W = _c(W, np.float32)
     lam = _c(lam, np.float32)
@@ -376,6 +392,31 @@ def linear(X, inv_smooth, L1p, L2t, R: int, w_codes, w_scales, bias, Y, ws, stre
                           _tp(L2t) if R else None, R, _tp(w_codes), _tp(w_scales), _tp(bias), _tp(Y),
                           _dt(Y), Y.stride(0), M, K, N, GROUP, _tp(ws), ws.numel() * ws.element_size(),
                           _act(activation), _stream(stream)), "svdq_linear")
+
+
+def linear_canonical_workspace_bytes(M: int, K: int, N: int, R: int) -> int:
+    return int(lib.svdq_linear_canonical_workspace_bytes(M, K, N, R, GROUP))
+
+
+def linear_canonical(X, inv_smooth, L1, L2, R: int, w_codes, w_scales, bias, Y, ws, stream=None,
+                     activation=None):
+    """svdq_linear_canonical: the layer with the low-rank factors as L1 (K x R) and
+    L2 (R x N) fp16 device arrays."""
+    M, K, N = _layer_io(X, Y)
+    _buf("inv_smooth", inv_smooth, _F32, nbytes=4 * K)
+    if R:
+        _buf("L1", L1, _HALF, nbytes=2 * K * R)
+        _buf("L2", L2, _HALF, nbytes=2 * R * N)
+    _weights(N, K, 0, w_codes, w_scales, None)
+    _bias(bias, N)
+    _buf("ws", ws, _BYTES + _HALF + _F32, min_bytes=linear_canonical_workspace_bytes(M, K, N, R))
+    _on_gpu(X, inv_smooth, L1 if R else None, L2 if R else None, w_codes, w_scales, bias, Y, ws)
+    check(lib.svdq_linear_canonical(_tp(X), _dt(X), X.stride(0), _tp(inv_smooth),
+                                    _tp(L1) if R else None, _tp(L2) if R else None, R,
+                                    _tp(w_codes), _tp(w_scales), _tp(bias), _tp(Y), _dt(Y),
+                                    Y.stride(0), M, K, N, GROUP, _tp(ws),
+                                    ws.numel() * ws.element_size(), _act(activation),
+                                    _stream(stream)), "svdq_linear_canonical")
 
 
 def int4_act_tiled_bytes(M: int, K: int) -> int:

@@ -20,7 +20,8 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["k1_quant_down.hip", "k2_w4a4_gemm.hip", "k2_mx_gemm.hip", "k2_w4a16_gemm.hip",
-               "k2_w4a4_tiled.hip", "gelu.hip", "clock_probe.hip", "abi_device.hip",
+               "k2_w4a4_tiled.hip", "gelu.hip", "lowrank_pack.hip", "clock_probe.hip",
+               "abi_device.hip",
                "abi_noalloc.hip"]
 HOST_SOURCES = {
     # the quantizer's fp32 divide/multiply must round exactly: no contraction

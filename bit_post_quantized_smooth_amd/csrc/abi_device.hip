@@ -251,6 +251,92 @@ int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth
                    "svdq_linear K2 launch");
 }
 
+namespace {
+// svdq_linear's workspace, then the packed factors L1p (R*K fp16) and L2t
+// (N*R fp16)
+struct CanonWs {
+  WsLayout base;
+  size_t l1p, l2t, total;
+};
+CanonWs canon_ws_layout(int64_t M, int64_t K, int64_t N, int32_t R) {
+  CanonWs c;
+  c.base = ws_layout(M, K, R, false);
+  c.l1p = c.base.total;
+  c.l2t = c.l1p + round_up(static_cast<size_t>(R) * K * 2, 256);
+  c.total = c.l2t + round_up(static_cast<size_t>(N) * R * 2, 256);
+  return c;
+}
+}  // namespace
+
+size_t svdq_linear_canonical_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t R,
+                                             int32_t group) {
+  if (M < 1 || N < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0 || group != SVDQ_GROUP || R < 0)
+    return 0;
+  return canon_ws_layout(M, K, N, R).total;
+}
+
+int svdq_linear_canonical(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
+                          const uint16_t* L1, const uint16_t* L2, int32_t R,
+                          const uint8_t* w_codes, const uint16_t* w_scales, const float* bias,
+                          void* Y, int y_dtype, int64_t ldy, int64_t M, int64_t K, int64_t N,
+                          int32_t group, void* ws, size_t ws_bytes, int32_t activation,
+                          hipStream_t stream) {
+  clear_error();
+  const char* fn = "svdq_linear_canonical";
+  if (int s = check_activation(activation, fn)) return s;
+  if (int s = check_common(M, K, R, group, fn)) return s;
+  if (N < 1) {
+    set_error("%s: N=%lld", fn, (long long)N);
+    return SVDQ_ERR_SHAPE;
+  }
+  if (R > 0 && (!L1 || !L2)) {
+    set_error("%s: null low-rank factor", fn);
+    return SVDQ_ERR_NULL;
+  }
+  if (R > 0 && (!aligned16(L1) || !aligned16(L2))) {
+    set_error("%s: L1 and L2 must be 16-byte aligned", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  if (!ws) {
+    set_error("%s: null workspace", fn);
+    return SVDQ_ERR_NULL;
+  }
+  const CanonWs L = canon_ws_layout(M, K, N, R);
+  if (ws_bytes < L.total) {
+    set_error("%s: workspace %zu bytes < %zu needed", fn, ws_bytes, L.total);
+    return SVDQ_ERR_WORKSPACE;
+  }
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) {
+    set_error("%s: workspace must be 256-byte aligned", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* a_codes = base + L.base.codes;
+  uint16_t* a_scales = reinterpret_cast<uint16_t*>(base + L.base.scales);
+  float* D = R > 0 ? reinterpret_cast<float*>(base + L.base.d) : nullptr;
+  uint16_t* L1p = R > 0 ? reinterpret_cast<uint16_t*>(base + L.l1p) : nullptr;
+  uint16_t* L2t = R > 0 ? reinterpret_cast<uint16_t*>(base + L.l2t) : nullptr;
+  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, group, a_codes, a_scales, D,
+                          fn))
+    return s;
+  if (int s = validate_k2(a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y, y_dtype, M, N,
+                          K, ldy, group, fn))
+    return s;
+  if (int s = device_ready()) return s;
+  if (R > 0) {
+    if (int s = check_hip(launch_pack_lowrank(L1, L2, K, N, R, L1p, L2t, stream),
+                          "svdq_linear_canonical factor packing launch"))
+      return s;
+  }
+  if (int s = check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1p, R, a_codes,
+                                  a_scales, false, D, stream),
+                        "svdq_linear_canonical K1 launch"))
+    return s;
+  return check_hip(launch_k2(a_codes, a_scales, w_codes, w_scales, D, L2t, R, bias, Y,
+                             y_dtype == SVDQ_F16, M, N, K, ldy, activation == SVDQ_ACT_GELU_TANH, stream),
+                   "svdq_linear_canonical K2 launch");
+}
+
 int svdq_quantize_act_lowrank_down_tiled(const void* X, int x_dtype, int64_t M, int64_t K,
                                          int64_t ldx, const float* inv_smooth,
                                          const uint16_t* L1p, int32_t R, uint8_t* a_ops_t,

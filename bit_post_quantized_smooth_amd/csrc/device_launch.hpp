@@ -61,6 +61,11 @@ hipError_t launch_debug_partials(const uint8_t* a_codes, const uint8_t* w_codes,
 
 hipError_t launch_gelu_f16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream);
 
+// The canonical low-rank factors L1 (K x R) and L2 (R x N) -> L1p and L2t
+// (see lowrank_pack.hip).
+hipError_t launch_pack_lowrank(const uint16_t* L1, const uint16_t* L2, int64_t K, int64_t N,
+                               int R, uint16_t* L1p, uint16_t* L2t, hipStream_t stream);
+
 // Measurement utility: shader-clock samples (see clock_probe.hip).
 hipError_t launch_clock_probe(uint64_t* samples, int32_t max_samples, int64_t interval,
                               const int32_t* stop, hipStream_t stream);

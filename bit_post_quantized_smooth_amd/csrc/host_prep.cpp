@@ -717,6 +717,45 @@ int svdq_pack_lowrank_down(const uint16_t* L1t, int64_t K, int32_t R, uint16_t* 
   return SVDQ_OK;
 }
 
+int svdq_pack_lowrank(const uint16_t* L1, const uint16_t* L2, int64_t K, int64_t N, int32_t R,
+                      uint16_t* L1p, uint16_t* L2t) {
+  clear_error();
+  if (!L1 || !L2 || !L1p || !L2t) {
+    set_error("svdq_pack_lowrank: null pointer");
+    return SVDQ_ERR_NULL;
+  }
+  if (K < SVDQ_GROUP || K % SVDQ_GROUP != 0) {
+    set_error("svdq_pack_lowrank: K=%lld is not a positive multiple of %d", (long long)K,
+              SVDQ_GROUP);
+    return SVDQ_ERR_GROUP;
+  }
+  if (N < 1) {
+    set_error("svdq_pack_lowrank: N=%lld", (long long)N);
+    return SVDQ_ERR_SHAPE;
+  }
+  if (R < 16 || R % 16 != 0 || R > SVDQ_MAX_RANK) {
+    set_error("svdq_pack_lowrank: R=%d", R);
+    return SVDQ_ERR_RANK;
+  }
+  // operand (g, c, h), lane = q*16 + rl, element j  <-  L1[g*64 + q*16 + h*8 + j][c*16 + rl]
+  const int64_t G = K / SVDQ_GROUP, ncb = R / 16;
+#pragma omp parallel for schedule(static)
+  for (int64_t g = 0; g < G; ++g)
+    for (int64_t c = 0; c < ncb; ++c)
+      for (int h = 0; h < 2; ++h)
+        for (int lane = 0; lane < 64; ++lane) {
+          const int rl = lane & 15, q = lane >> 4;
+          const int64_t k0 = g * SVDQ_GROUP + q * 16 + h * 8, r = c * 16 + rl;
+          uint16_t* dst = L1p + (((g * ncb + c) * 2 + h) * 64 + lane) * 8;
+          for (int j = 0; j < 8; ++j) dst[j] = L1[(k0 + j) * R + r];
+        }
+  // L2t[n][r] = L2[r][n]
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int32_t r = 0; r < R; ++r) L2t[n * R + r] = L2[static_cast<int64_t>(r) * N + n];
+  return SVDQ_OK;
+}
+
 int svdq_abi_version(void) { return SVDQ_ABI_VERSION; }
 
 const char* svdq_status_str(int status) {

@@ -39,11 +39,14 @@
  *   - a_codes: M x K/2 bytes, row-major (row m holds token m along K).
  *     w_codes: N x K/2 bytes, row-major (row n holds output column n along K).
  *   - a_scales: M x K/group fp16, w_scales: N x K/group fp16, row-major.
- *   - L1t: R x K fp16 row-major  (the transpose of the K x R factor L1), as
- *     the host functions produce it; the device side takes it packed in
- *     operand order (L1p, svdq_pack_lowrank_down).
- *     L2t: N x R fp16 row-major  (the transpose of the R x N factor L2),
- *     contiguous along the rank, which is what a matrix-core operand lane loads.
+ *   - The low-rank factors as the method states them (X . L1 . L2):
+ *     L1: K x R fp16 row-major, L2: R x N fp16 row-major. svdq_linear_canonical
+ *     takes them so; svdq_pack_lowrank turns them into the two packings the
+ *     kernels read:
+ *     L1p: L1 in K1's operand order (svdq_pack_lowrank_down gives the formula);
+ *     L2t: N x R fp16 row-major (the transpose of L2), contiguous along the
+ *     rank, which is what a matrix-core operand lane loads.
+ *     The offline preparation writes L1t (R x K, the transpose of L1) and L2t.
  *   - D: M x R fp32 row-major.  X: M x K row-major with row stride ldx
  *     (elements).  Y: M x N row-major with row stride ldy (elements).
  *
@@ -66,7 +69,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 6
+#define SVDQ_ABI_VERSION 7
 
 /* status codes */
 enum {
@@ -181,6 +184,16 @@ int svdq_concat_lora(const uint16_t* L1t, const uint16_t* L2t, int64_t K, int64_
  * L1p: R*K fp16. K % 64 == 0, 16 <= R <= SVDQ_MAX_RANK, R % 16 == 0. */
 int svdq_pack_lowrank_down(const uint16_t* L1t, int64_t K, int32_t R, uint16_t* L1p);
 
+/* The canonical low-rank factors -> the device packings (a layout, no
+ * arithmetic): L1 (K x R fp16, row-major) -> L1p as svdq_pack_lowrank_down
+ * writes it (L1p[...] = L1[64g + 16q + 8h + j][16c + rl] in its formula), and
+ * L2 (R x N fp16, row-major) -> L2t[n][r] = L2[r][n] (N x R). The factors are
+ * those of the 16-bit low-rank branch of the SVD split (chattools.cn overview,
+ * section "SVDQuant的技术原理"). K % 64 == 0, N >= 1, 16 <= R <= SVDQ_MAX_RANK,
+ * R % 16 == 0. Outputs must not overlap inputs. */
+int svdq_pack_lowrank(const uint16_t* L1, const uint16_t* L2, int64_t K, int64_t N, int32_t R,
+                      uint16_t* L1p, uint16_t* L2t);
+
 /* ---------------------------------------------------------------------------
  * Device functions: pointers are device memory; the work is enqueued on
  * `stream` (0 = the null stream) and the call returns without waiting. They
@@ -203,7 +216,13 @@ int svdq_quantize_act_lowrank_down(const void* X, int x_dtype, int64_t M, int64_
                                    int32_t R, int32_t group, uint8_t* a_codes,
                                    uint16_t* a_scales, float* D, hipStream_t stream);
 
-/* K2: W4A4 GEMM with the low-rank up-projection and bias fused in.
+/* K2: W4A4 GEMM with the low-rank up-projection and bias fused in. Both
+ * operands 4-bit (SVDQuant abstract, ai-digest.ru page: weights and
+ * activations quantized to 4 bits); the low-rank branch's second product runs
+ * inside the low-bit GEMM rather than as a kernel of its own (the Nunchaku
+ * engine fuses the low-rank kernels into the low-bit ones: chattools.cn
+ * overview, section "SVDQuant的技术原理", Nunchaku item; disruptive-concepts.com
+ * post, section "Nunchaku: Fusing Precision and Speed").
  *   P[m,n,g] = sum over k in group g of qx[m,k] * qw[n,k]   (exact int32)
  *   Y[m,n]   = sum_g s_x[m,g] * s_w[n,g] * P[m,n,g]   (fp32)
  *              + sum_r fp16(D[m,r]) * L2[r,n]          (fp16 products, fp32 sum)
@@ -220,14 +239,42 @@ int svdq_w4a4_gemm_lowrank_up(const uint8_t* a_codes, const uint16_t* a_scales,
  * 256-byte aligned inside the workspace. */
 size_t svdq_linear_workspace_bytes(int64_t M, int64_t K, int32_t R, int32_t group);
 
-/* The whole layer: K1 then K2 on `stream`, intermediates in `ws`
- * (>= svdq_linear_workspace_bytes(M, K, R, group) bytes, 256-byte aligned).
- * L1p: packed by svdq_pack_lowrank_down, L2t: N x R. activation: SVDQ_ACT_*. */
+/* The whole layer Y = Xhat . L1 . L2 + Q(Xhat) . Q(R) + b (chattools.cn
+ * overview, section "SVDQuant的技术原理": the low-rank branch beside the 4-bit
+ * residual branch), as the Nunchaku engine runs it: two kernels, the low-rank
+ * down-projection fused into the activation quantizer and the up-projection
+ * into the W4A4 GEMM (chattools.cn overview, Nunchaku item; disruptive-
+ * concepts.com post, section "Nunchaku: Fusing Precision and Speed"; the
+ * SVDQuant abstract: the activation is not moved a second time). K1 then K2 on
+ * `stream`, intermediates in `ws` (>= svdq_linear_workspace_bytes(M, K, R,
+ * group) bytes, 256-byte aligned). L1p: packed by svdq_pack_lowrank_down or
+ * svdq_pack_lowrank, L2t: N x R. activation: SVDQ_ACT_*. */
 int svdq_linear(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
                 const uint16_t* L1p, const uint16_t* L2t, int32_t R, const uint8_t* w_codes,
                 const uint16_t* w_scales, const float* bias, void* Y, int y_dtype, int64_t ldy,
                 int64_t M, int64_t K, int64_t N, int32_t group, void* ws, size_t ws_bytes,
                 int32_t activation, hipStream_t stream);
+
+/* Bytes of workspace svdq_linear_canonical needs: svdq_linear's, then room
+ * for the packed factors (R*K and N*R fp16), each 256-byte aligned. */
+size_t svdq_linear_canonical_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t R,
+                                             int32_t group);
+
+/* svdq_linear taking the low-rank factors as the method states them: L1
+ * (K x R) and L2 (R x N), fp16 row-major device arrays (the SVD split of the
+ * smoothed weight into a 16-bit low-rank branch and a 4-bit residual:
+ * chattools.cn overview, section "SVDQuant的技术原理"). A layout kernel first
+ * writes L1p and L2t into `ws` (>= svdq_linear_canonical_workspace_bytes),
+ * then the same K1 and K2 as svdq_linear: the result is bit-identical to
+ * svdq_linear on the packed factors. The packing is repeated on every call;
+ * callers that run a layer many times pack once (svdq_pack_lowrank) and call
+ * svdq_linear. L1, L2: 16-byte aligned; may be NULL when R == 0. */
+int svdq_linear_canonical(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
+                          const uint16_t* L1, const uint16_t* L2, int32_t R,
+                          const uint8_t* w_codes, const uint16_t* w_scales, const float* bias,
+                          void* Y, int y_dtype, int64_t ldy, int64_t M, int64_t K, int64_t N,
+                          int32_t group, void* ws, size_t ws_bytes, int32_t activation,
+                          hipStream_t stream);
 
 /* Largest intermediate size svdq_linear_noalloc handles (bytes of
  * svdq_linear_workspace_bytes): 64 MiB, enough for every layer shape used

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert _lib.abi_version() == 6
+    assert _lib.abi_version() == 7
     for s in range(12):
         assert _lib.status_str(s) and _lib.status_str(s) != "unknown status"
     assert _lib.status_str(99) == "unknown status"
@@ -275,6 +275,40 @@ def test_pack_lowrank_down_is_the_documented_permutation(K, R):
     assert got[idx] == L1t[c * 16 + rl, g * 64 + q * 16 + h * 8 + j]
 
 
+@pytest.mark.parametrize("K,N,R", [(64, 1, 16), (192, 130, 48), (1024, 300, 112)])
+def test_pack_lowrank_takes_the_canonical_factors(K, N, R):
+    """svdq_pack_lowrank on L1 (K x R) and L2 (R x N), the oracle's shapes: L1p by
+    the header's index formula (a reshape of L1's transpose), L2t = L2 transposed;
+    the factors of an oracle preparation go through unchanged."""
+    rng = np.random.default_rng(K + N + R)
+    L1 = rng.integers(0, 1 << 16, size=(K, R), dtype=np.uint16)
+    L2 = rng.integers(0, 1 << 16, size=(R, N), dtype=np.uint16)
+    L1p, L2t = sq.pack_lowrank(L1, L2)
+    ref = (L1.T.reshape(R // 16, 16, K // 64, 4, 2, 8)    # c, rl, g, q, h, j
+              .transpose(2, 0, 4, 3, 1, 5)                 # g, c, h, q, rl, j
+              .reshape(-1))
+    assert np.array_equal(L1p, ref)
+    g, c, h, q, rl, j = K // 64 - 1, R // 16 - 1, 1, 3, 14, 7
+    idx = (((g * (R // 16) + c) * 2 + h) * 64 + q * 16 + rl) * 8 + j
+    assert L1p[idx] == L1[g * 64 + q * 16 + h * 8 + j, c * 16 + rl]
+    assert L2t.shape == (N, R) and np.array_equal(L2t, L2.T)
+    # the same packing as svdq_pack_lowrank_down on the transpose
+    assert np.array_equal(L1p, sq.pack_lowrank_down(np.ascontiguousarray(L1.T)))
+
+
+def test_pack_lowrank_of_an_oracle_preparation():
+    rng = np.random.default_rng(11)
+    K, N, R = 128, 96, 16
+    W = rng.standard_normal((K, N)).astype(np.float32)
+    X = rng.standard_normal((32, K)).astype(np.float32)
+    lam = O.smoothing_factors(O.channel_absmax(X), W)
+    pr = O.prepare(W, lam, R)
+    assert pr["L1"].shape == (K, R) and pr["L2"].shape == (R, N)
+    L1p, L2t = sq.pack_lowrank(pr["L1"].view(np.uint16), pr["L2"].view(np.uint16))
+    assert np.array_equal(L2t.view(np.float16), pr["L2"].T)
+    assert L1p[0] == pr["L1"].view(np.uint16)[0, 0]
+
+
 def test_host_errors():
     L = _lib.lib
     W = np.zeros((128, 8), dtype=np.float32)
@@ -294,6 +328,10 @@ def test_host_errors():
     assert L.svdq_pack_lowrank_down(bp, 96, 16, bp) == _lib.ERR_GROUP
     assert L.svdq_pack_lowrank_down(bp, 64, 24, bp) == _lib.ERR_RANK
     assert L.svdq_pack_lowrank_down(bp, 64, 0, bp) == _lib.ERR_RANK
+    assert L.svdq_pack_lowrank(None, bp, 64, 8, 16, bp, bp) == _lib.ERR_NULL
+    assert L.svdq_pack_lowrank(bp, bp, 96, 8, 16, bp, bp) == _lib.ERR_GROUP
+    assert L.svdq_pack_lowrank(bp, bp, 64, 0, 16, bp, bp) == _lib.ERR_SHAPE
+    assert L.svdq_pack_lowrank(bp, bp, 64, 8, 24, bp, bp) == _lib.ERR_RANK
     # weight-only baseline
     assert L.svdq_prepare_weights_w4a16(None, 64, 8, bp, bp) == _lib.ERR_NULL
     assert L.svdq_prepare_weights_w4a16(W.ctypes.data, 96, 8, bp, bp) == _lib.ERR_GROUP
