@@ -14,20 +14,30 @@
 // SVDQuant abstract; the disruptive-concepts.com post, section "Nunchaku:
 // Fusing Precision and Speed").
 //
-// Those two fp32 ops per output and group bound the kernel: the vector ALU
-// needs twice the matrix core's time for them. So this kernel keeps every
-// other vector op out of the K loop:
+// Those two fp32 ops per output and group bound the kernel. Measured on this
+// chip, a wave64 v_fma_f32 occupies a SIMD for about 2.5 cycles once two or
+// more waves share it (one wave alone issues one every ~5 cycles), an i8
+// 16x16x64 matrix instruction for about 17, and the two do not overlap: a
+// SIMD running both spends the sum. Per group and wave that is 16 matrix
+// instructions (272 cycles) against 128 rescale FMAs (~320 cycles), so the
+// kernel keeps every other vector op out of the K loop:
 // - the activation operand arrives already widened, in the matrix
 //   instruction's lane order, from the pre-kernel (svdq.h, tiled INT4
 //   layouts), with its scale as the fp32 pair (s_x/256, -12582912 s_x/256);
 // - the weights stay 4-bit (the 4-bit weight memory is the method's point)
 //   in a lane-order tiling per 32-column strip, so a wave's weight fragment
 //   for one group is one 16-byte read per lane, widened once (12 bit ops);
+// - the weight scales are converted to fp32 once per group (8 conversions):
+//   folded into the FMAs instead, as v_fma_mix_f32, they would cost 64 ops
+//   at half the rate of v_fma_f32;
 // - every operand goes from global memory straight into LDS
 //   (global_load_lds: no register round trip), KSTAGES groups deep, with one
 //   barrier per group; addresses advance by scalar offsets.
 // What remains per group and wave: 16 matrix instructions, 128 rescale ops,
-// 12 widening ops, 14 LDS reads and 5 copies.
+// 8 conversions, 12 widening ops, 9 address and other ops, 14 LDS reads and
+// 5 copies. Three workgroups share a compute unit (168 registers, 40.7 KB of
+// LDS), so a wave waiting at the barrier or on LDS leaves the SIMD to two
+// others.
 //
 // Tiling: a 256-thread workgroup computes a 128 x 128 tile of Y; wave w owns
 // all 128 rows and columns 32w .. 32w+31 (8 x 2 blocks of 16 x 16), so its
@@ -50,7 +60,10 @@ constexpr int NT = 256;             // threads per workgroup
 constexpr int kBlk = 1024;          // one operand block: 64 lanes x 16 bytes
 constexpr int kPairBlk = 256;       // scale pairs of one 128-row band and group (floats)
 constexpr int kWsBlk = 32;          // fp16 weight scales of one 32-column strip and group
-constexpr int KSTAGES = 4;          // LDS ring depth
+// LDS ring depth. Three stages (40.7 KB) let three workgroups share a
+// compute unit; with four (54.3 KB) only two were resident, measured, though
+// three times 54.3 KB is below the 160 KB of LDS (the allocation granularity).
+constexpr int KSTAGES = 3;
 constexpr int KAHEAD = KSTAGES - 1; // groups copied ahead of the one computed
 
 // One group's operands for the whole tile (a 128 x 128 tile uses all of it).
@@ -62,6 +75,7 @@ struct alignas(16) TStage {
 };
 
 #define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
+
 
 // Tile shapes: RB row blocks of 16 (every wave holds all of them) and CB
 // column blocks of 16 per wave. 8 x 2: the 128 x 128 tile; 4 x 2 (64 x 128)
@@ -83,14 +97,8 @@ constexpr int kWaitAll = 0x0070;                    // vmcnt(0) lgkmcnt(0)
 template <int RB, int CB>
 struct TScales {
   float sx[RB], be[RB];             // (s_x/256, -12582912 s_x/256) of the lane's row per row block
-  uint2 swp[CB];                    // fp16 s_w of the lane's 4 columns per column block
+  float sw[CB][4];                  // s_w of the lane's 4 columns per column block
 };
-
-template <int RB, int CB>
-__device__ __forceinline__ float sw_of(const TScales<RB, CB>& sc, int j, int e) {
-  const uint32_t w = (e < 2) ? sc.swp[j].x : sc.swp[j].y;
-  return h2f(static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xFFFFu)));
-}
 
 template <int RB, int CB>
 __device__ __forceinline__ void rescale(v4f& acc, const v4i& p, const TScales<RB, CB>& sc, int i,
@@ -99,8 +107,18 @@ __device__ __forceinline__ void rescale(v4f& acc, const v4i& p, const TScales<RB
   for (int e = 0; e < 4; ++e) {
     const int pe = p[e];                     // scalar copy: see as_float()
     const float t = __builtin_fmaf(as_float(pe), sc.sx[i], sc.be[i]);
-    acc[e] = __builtin_fmaf(t, sw_of(sc, j, e), acc[e]);
+    acc[e] = __builtin_fmaf(t, sc.sw[j][e], acc[e]);
   }
+}
+
+// fp16 -> fp32 kept as an instruction of its own. Left visible, the compiler
+// folds the conversion into each of the 4*RB rescale ops that use the value
+// (v_fma_mix_f32), and that form issues at half the rate of v_fma_f32 here
+// (a measured 4 against 2 cycles per wave64 instruction).
+__device__ __forceinline__ float h2f_opaque(uint32_t bits16) {
+  float f = h2f(static_cast<uint16_t>(bits16));
+  asm("" : "+v"(f));
+  return f;
 }
 
 // One tile of Y: rows m0 .. m0 + 16*RB - 1, columns n0 .. n0 + 64*CB - 1.
@@ -157,34 +175,8 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
         reinterpret_cast<const uint8_t*>(w_scales + static_cast<int64_t>(g) * kWsBlk) + low,
         LDSP(&s.w[0][0]), 4, 0, 0);
   };
-  auto read_ops = [&](v4i (&A)[RB], v4i (&B)[CB], const TStage& s) {
-#pragma unroll
-    for (int i = 0; i < RB; ++i) A[i] = *reinterpret_cast<const v4i*>(&s.a[i][16 * lane]);
-    const uint4 raw = *reinterpret_cast<const uint4*>(&s.b[wave][16 * lane]);
-    if constexpr (CB == 2) {
-      B[0] = widen_codes(make_uint2(raw.x, raw.y));
-      B[1] = widen_codes(make_uint2(raw.z, raw.w));
-    } else {
-      B[0] = widen_codes(hb ? make_uint2(raw.z, raw.w) : make_uint2(raw.x, raw.y));
-    }
-  };
-  // pairs: row block i of the band, row r, at ((i/2)*16 + r)*4 + (i%2)*2
-  auto read_scales = [&](TScales<RB, CB>& sc, const TStage& s) {
-#pragma unroll
-    for (int h = 0; h < RB / 2; ++h) {
-      const float4 v = *reinterpret_cast<const float4*>(&s.p[((rb0 / 2 + h) * 16 + rl) * 4]);
-      sc.sx[2 * h] = v.x;
-      sc.be[2 * h] = v.y;
-      sc.sx[2 * h + 1] = v.z;
-      sc.be[2 * h + 1] = v.w;
-    }
-    const uint4 w = *reinterpret_cast<const uint4*>(&s.w[rs][8 * q]);
-    if constexpr (CB == 2) {
-      sc.swp[0] = make_uint2(w.x, w.y);
-      sc.swp[1] = make_uint2(w.z, w.w);
-    } else {
-      sc.swp[0] = hb ? make_uint2(w.z, w.w) : make_uint2(w.x, w.y);
-    }
+  auto read_a = [&](const TStage& s, int i) {
+    return *reinterpret_cast<const v4i*>(&s.a[i][16 * lane]);
   };
 
 #pragma unroll
@@ -198,57 +190,69 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
     for (int j = 0; j < CB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   lowrank_up_at<16 * RB, 16 * CB>(acc, D, L2t, R, M, N, m0, nw);
 
-  __builtin_amdgcn_s_waitcnt(kWaitAll);
-  __builtin_amdgcn_s_barrier();
+  // Iteration g computes group g from stage g % KSTAGES. Its barrier follows
+  // this wave's wait for its own copies of group g, so after it every copy of
+  // group g has landed and every wave is done with group g-1, whose stage then
+  // takes group g+KAHEAD. Inside the group the matrix instructions of row
+  // block i go out before the rescale of row block i-1, so the partials of
+  // only two row blocks are live (and two activation operands), which keeps
+  // the kernel at three waves per SIMD.
   const v4i seed = v4i{kMagicSeed, kMagicSeed, kMagicSeed, kMagicSeed};
-  v4i A[RB], B[CB], P[RB][CB];
-  TScales<RB, CB> cur;
-  read_ops(A, B, st[0]);
-  read_scales(cur, st[0]);
-#pragma unroll
-  for (int i = 0; i < RB; ++i)
-#pragma unroll
-    for (int j = 0; j < CB; ++j) P[i][j] = mfma_i8_16x16x64(B[j], A[i], seed);
-
-  // iteration g: rescale group g's partials block by block and, behind each
-  // block, issue group g+1's matrix instruction into the same registers.
-  // Group g+KAHEAD is copied into the stage group g-1 left (every wave read
-  // it before the previous barrier); group g+1's copies, issued KAHEAD-1
-  // iterations ago, are waited for before this iteration's barrier.
-  constexpr int LEAD = S::NBLK < 4 ? S::NBLK : 4;
-  int s1 = 1;                                   // stage of group g+1
-  for (int g = 0; g + 1 < G; ++g) {
-    copy(st[(s1 + KAHEAD - 1) & (KSTAGES - 1)], g + KAHEAD);
+  int sg = 0, sp = KSTAGES - 1;                 // stages of groups g and g-1
+  for (int g = 0; g < G; ++g) {
+    const TStage& s = st[sg];
     __builtin_amdgcn_s_waitcnt(S::WAIT_AHEAD);
     __builtin_amdgcn_s_barrier();
-    read_ops(A, B, st[s1]);
+    copy(st[sp], g + KAHEAD);                   // group g-1's stage takes group g+KAHEAD
+    sp = sg;
+    sg = sg + 1 == KSTAGES ? 0 : sg + 1;
+
+    const uint4 braw = *reinterpret_cast<const uint4*>(&s.b[wave][16 * lane]);
+    const uint4 wraw = *reinterpret_cast<const uint4*>(&s.w[rs][8 * q]);
+    v4i A[2];
+    A[0] = read_a(s, 0);
+    // pairs: row block i of the band, row r, at ((i/2)*16 + r)*4 + (i%2)*2
+    TScales<RB, CB> sc;
+#pragma unroll
+    for (int h = 0; h < RB / 2; ++h) {
+      const float4 v = *reinterpret_cast<const float4*>(&s.p[((rb0 / 2 + h) * 16 + rl) * 4]);
+      sc.sx[2 * h] = v.x;
+      sc.be[2 * h] = v.y;
+      sc.sx[2 * h + 1] = v.z;
+      sc.be[2 * h + 1] = v.w;
+    }
+    v4i B[CB];
+    if constexpr (CB == 2) {
+      B[0] = widen_codes(make_uint2(braw.x, braw.y));
+      B[1] = widen_codes(make_uint2(braw.z, braw.w));
+      const uint32_t w4[4] = {wraw.x, wraw.y, wraw.z, wraw.w};
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sc.sw[j][e] = h2f_opaque((e & 1) ? (w4[2 * j + e / 2] >> 16) : w4[2 * j + e / 2]);
+    } else {
+      B[0] = widen_codes(hb ? make_uint2(braw.z, braw.w) : make_uint2(braw.x, braw.y));
+      const uint32_t w0 = hb ? wraw.z : wraw.x, w1 = hb ? wraw.w : wraw.y;
+      sc.sw[0][0] = h2f_opaque(w0);
+      sc.sw[0][1] = h2f_opaque(w0 >> 16);
+      sc.sw[0][2] = h2f_opaque(w1);
+      sc.sw[0][3] = h2f_opaque(w1 >> 16);
+    }
+    v4i P[2][CB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
+      if (i + 1 < RB) A[(i + 1) & 1] = read_a(s, i + 1);
 #pragma unroll
-      for (int j = 0; j < CB; ++j) {
-        rescale(acc[i][j], P[i][j], cur, i, j);
-        P[i][j] = mfma_i8_16x16x64(B[j], A[i], seed);
+      for (int j = 0; j < CB; ++j) P[i & 1][j] = mfma_i8_16x16x64(B[j], A[i & 1], seed);
+      if (i > 0) {
+#pragma unroll
+        for (int j = 0; j < CB; ++j) rescale(acc[i - 1][j], P[(i - 1) & 1][j], sc, i - 1, j);
       }
     }
-    // the first blocks' rescale covers the LDS reads of the first operands;
-    // then one matrix instruction behind each block's 8 ops
 #pragma unroll
-    for (int b = 0; b < LEAD; ++b) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-#pragma unroll
-    for (int b = 0; b < S::NBLK - LEAD; ++b) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    }
-#pragma unroll
-    for (int b = 0; b < LEAD; ++b) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    read_scales(cur, st[s1]);
-    s1 = (s1 + 1) & (KSTAGES - 1);
+    for (int j = 0; j < CB; ++j) rescale(acc[RB - 1][j], P[(RB - 1) & 1][j], sc, RB - 1, j);
   }
-#pragma unroll
-  for (int i = 0; i < RB; ++i)
-#pragma unroll
-    for (int j = 0; j < CB; ++j) rescale(acc[i][j], P[i][j], cur, i, j);
 
   // copies of groups past the end land in stages nobody reads; wait for them
   // before the LDS is used for the output
@@ -306,7 +310,7 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
 // 128 halves, 4: 64 x 64 quarters). A piece wholly outside Y returns at once
 // (the same for every wave of the workgroup, before any barrier).
 template <bool Y_F16, bool GELU>
-__global__ __launch_bounds__(NT, 2) void k2t_w4a4_kernel(
+__global__ __launch_bounds__(NT, 3) void k2t_w4a4_kernel(
     const uint8_t* __restrict__ a_ops, const float* __restrict__ a_pairs,
     const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales,
     const float* __restrict__ D, const uint16_t* __restrict__ L2t, int R,
@@ -335,6 +339,26 @@ __global__ __launch_bounds__(NT, 2) void k2t_w4a4_kernel(
                               ldy, m0, n0);
 }
 
+// Workgroups of this kernel resident at once on the current device (compute
+// units times the occupancy its registers and LDS allow), cached per device.
+int k2t_slots() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return resident_slots();
+  if (cache[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0 ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(k2t_w4a4_kernel<true, false>), NT, 0) !=
+            hipSuccess ||
+        per_cu <= 0)
+      return resident_slots();
+    cache[dev] = cus * per_cu;
+  }
+  return cache[dev];
+}
+
 }  // namespace
 
 hipError_t launch_k2t(const uint8_t* a_ops, const float* a_pairs, const uint8_t* w_codes_t,
@@ -346,7 +370,7 @@ hipError_t launch_k2t(const uint8_t* a_ops, const float* a_pairs, const uint8_t*
   const int T = tiles_m * tiles_n;
   // the tiles of a thin last round are cut into halves or quarters, so that
   // they fill more of the resident workgroup slots
-  const int S = resident_slots();
+  const int S = k2t_slots();
   const int left = T < S ? T : T % S;
   const int split = (left > 0 && 4 * left <= S) ? 4 : (left > 0 && 2 * left <= S) ? 2 : 1;
   const int n_split = split > 1 ? left : 0;

@@ -41,6 +41,55 @@ def test_every_declared_symbol_is_exported():
         getattr(_lib.lib, n)
 
 
+def header_prototypes():
+    """{name: (return type, [parameter types])} parsed from include/svdq.h."""
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    out = {}
+    for m in re.finditer(r"^\s*((?:const\s+)?[\w]+\s*\**)\s*\b(svdq_\w+)\s*\(([^)]*)\)\s*;",
+                         src, flags=re.M):
+        ret, name, params = m.group(1), m.group(2), m.group(3)
+        plist = [] if params.strip() in ("", "void") else [p.strip() for p in params.split(",")]
+        types = [re.sub(r"\s*\b\w+$", "", p) if not p.endswith("*") else p for p in plist]
+        out[name] = (ret.strip(), types)
+    return out
+
+
+def _ctype_of(t: str):
+    """The ctypes type a C parameter of type t is passed as."""
+    t = t.replace("const ", "").strip()
+    if t.endswith("*") or t == "hipStream_t":
+        return C.c_void_p
+    return {"int": C.c_int, "int32_t": C.c_int32, "int64_t": C.c_int64, "size_t": C.c_size_t,
+            "float": C.c_float}[t]
+
+
+def test_ctypes_signatures_match_the_header():
+    """Every binding signature agrees with the header's prototype in arity, order
+    and kind of each argument (an argument out of step would pass a size where a
+    pointer is expected, or the reverse)."""
+    protos = header_prototypes()
+    assert set(protos) == set(header_functions())
+    for name, (res, args) in _lib._SIGS.items():
+        assert name in protos, name
+        ret, ptypes = protos[name]
+        want = [_ctype_of(t) for t in ptypes]
+        assert list(args) == want, (name, ptypes)
+        if ret.endswith("*"):
+            assert res in (C.c_char_p, C.c_void_p), name
+        else:
+            assert res == _ctype_of(ret), (name, ret)
+    assert set(protos) == set(_lib._SIGS), set(protos) ^ set(_lib._SIGS)
+
+
+def test_one_hip_runtime_is_mapped():
+    """The library and torch share one HIP runtime (a second copy would be handed
+    the other's stream and device-memory handles)."""
+    maps = open("/proc/self/maps").read()
+    paths = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(paths) <= 1, paths
+
+
 def test_version_and_status_strings():
     assert _lib.abi_version() == 7
     for s in range(12):
