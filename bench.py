@@ -268,14 +268,20 @@ def host_cores():
 def k1_bytes(M, K, R, xb, meta_per_row, tiled=False):
     """Read X once; write codes, scales (or exponents) and D; read L1 and 1/lambda.
     tiled: the activation side as the tiled path stores it (one int8 operand byte
-    per code, an 8-byte fp32 scale pair per row and group)."""
-    act = M * K + 8 * M * (K // 64) if tiled else M * K // 2 + M * meta_per_row
+    per code, an fp32 scale per row and group)."""
+    act = M * K + 4 * M * (K // 64) if tiled else M * K // 2 + M * meta_per_row
     return M * K * xb + act + 4 * M * R + 2 * K * R + 4 * K
 
 
 def k2_bytes(M, N, K, R, yb, meta_per_row, tiled=False):
-    """Codes and scales of both operands, D, L2, Y (bias not counted: zero in the configs)."""
-    act = M * K + 8 * M * (K // 64) if tiled else M * K // 2 + M * meta_per_row
+    """Codes and scales of both operands, D, L2, Y (bias not counted: zero in the configs).
+    tiled: as the tiled path stores them (int8 activation operands and fp32 scales,
+    the weight scales as 8-byte fp32 pairs)."""
+    if tiled:
+        G = K // 64
+        return (M * K + 4 * M * G + N * K // 2 + 8 * N * G + 4 * M * R + 2 * R * N
+                + M * N * yb)
+    act = M * K // 2 + M * meta_per_row
     return act + N * K // 2 + N * meta_per_row + 4 * M * R + 2 * R * N + M * N * yb
 
 
@@ -320,7 +326,7 @@ class Sets:
                 s.update(wc=d(wct), ws=d(wet),
                          ac=torch.empty(sq.int4_act_tiled_bytes(M, K), dtype=torch.uint8,
                                         device="cuda"),
-                         asc=torch.empty(sq.int4_pairs_tiled_bytes(M, K) // 4, dtype=torch.float32,
+                         asc=torch.empty(sq.int4_act_scales_tiled_bytes(M, K) // 4, dtype=torch.float32,
                                          device="cuda"))
             elif self.mx:
                 s.update(wc=d(wct), ws=d(wet),

@@ -70,7 +70,7 @@ _SIGS = {
     "svdq_linear_noalloc": (_int, [_p, _int, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _int, _i64,
                                    _i64, _i64, _i64, _i32, _i32, _p]),
     "svdq_int4_act_tiled_bytes": (C.c_size_t, [_i64, _i64]),
-    "svdq_int4_pairs_tiled_bytes": (C.c_size_t, [_i64, _i64]),
+    "svdq_int4_act_scales_tiled_bytes": (C.c_size_t, [_i64, _i64]),
     "svdq_int4_w_codes_tiled_bytes": (C.c_size_t, [_i64, _i64]),
     "svdq_int4_w_scales_tiled_bytes": (C.c_size_t, [_i64, _i64]),
     "svdq_pack_w4a4_tiles": (_int, [_p, _p, _i64, _i64, _p, _p]),

@@ -423,8 +423,8 @@ def int4_act_tiled_bytes(M: int, K: int) -> int:
     return int(lib.svdq_int4_act_tiled_bytes(M, K))
 
 
-def int4_pairs_tiled_bytes(M: int, K: int) -> int:
-    return int(lib.svdq_int4_pairs_tiled_bytes(M, K))
+def int4_act_scales_tiled_bytes(M: int, K: int) -> int:
+    return int(lib.svdq_int4_act_scales_tiled_bytes(M, K))
 
 
 def int4_w_codes_tiled_bytes(N: int, K: int) -> int:
@@ -437,21 +437,21 @@ def int4_w_scales_tiled_bytes(N: int, K: int) -> int:
 
 def pack_w4a4_tiles(w_codes: np.ndarray, w_scales: np.ndarray, K: int):
     """svdq_pack_w4a4_tiles: canonical INT4 weight codes and fp16 scale bits -> the
-    tiled layouts of the tiled path (flat uint8 codes, flat uint16 scale bits)."""
+    tiled layouts of the tiled path (flat uint8 codes, flat fp32 scale pairs)."""
     w_codes = _c(w_codes, np.uint8)
     w_scales = _c(w_scales, np.uint16)
     N = w_codes.shape[0]
     ct = np.empty(int4_w_codes_tiled_bytes(N, K), dtype=np.uint8)
-    st = np.empty(int4_w_scales_tiled_bytes(N, K) // 2, dtype=np.uint16)
+    st = np.empty(int4_w_scales_tiled_bytes(N, K) // 4, dtype=np.float32)
     check(lib.svdq_pack_w4a4_tiles(_np_ptr(w_codes), _np_ptr(w_scales), N, K, _np_ptr(ct),
                                    _np_ptr(st)), "svdq_pack_w4a4_tiles")
     return ct, st
 
 
-def _act_side_tiled(M, K, R, a_ops_t, a_pairs_t, D):
+def _act_side_tiled(M, K, R, a_ops_t, a_scales_t, D):
     _groups(K)
     _buf("a_ops_t", a_ops_t, _BYTES, min_bytes=int4_act_tiled_bytes(M, K))
-    _buf("a_pairs_t", a_pairs_t, _F32, min_bytes=int4_pairs_tiled_bytes(M, K))
+    _buf("a_scales_t", a_scales_t, _F32, min_bytes=int4_act_scales_tiled_bytes(M, K))
     if R:
         _buf("D", D, _F32, min_bytes=4 * M * R)
 
@@ -459,37 +459,37 @@ def _act_side_tiled(M, K, R, a_ops_t, a_pairs_t, D):
 def _weights_tiled(N, K, R, w_codes_t, w_scales_t, L2t):
     _groups(K)
     _buf("w_codes_t", w_codes_t, _BYTES, nbytes=int4_w_codes_tiled_bytes(N, K))
-    _buf("w_scales_t", w_scales_t, _HALF, nbytes=int4_w_scales_tiled_bytes(N, K))
+    _buf("w_scales_t", w_scales_t, _F32, nbytes=int4_w_scales_tiled_bytes(N, K))
     if R:
         _buf("L2t", L2t, _HALF, nbytes=2 * N * R)
 
 
-def quantize_act_lowrank_down_tiled(X, inv_smooth, L1p, R: int, a_ops_t, a_pairs_t, D,
+def quantize_act_lowrank_down_tiled(X, inv_smooth, L1p, R: int, a_ops_t, a_scales_t, D,
                                     stream=None):
-    """K1 writing the tiled activation operands and scale pairs."""
+    """K1 writing the tiled activation operands and fp32 scales."""
     _mat("X", X, None, None)
     M, K = X.shape
     _down(K, R, inv_smooth, L1p)
-    _act_side_tiled(M, K, R, a_ops_t, a_pairs_t, D)
-    _on_gpu(X, inv_smooth, L1p if R else None, a_ops_t, a_pairs_t, D if R else None)
+    _act_side_tiled(M, K, R, a_ops_t, a_scales_t, D)
+    _on_gpu(X, inv_smooth, L1p if R else None, a_ops_t, a_scales_t, D if R else None)
     check(lib.svdq_quantize_act_lowrank_down_tiled(_tp(X), _dt(X), M, K, X.stride(0),
                                                    _tp(inv_smooth), _tp(L1p) if R else None, R,
-                                                   _tp(a_ops_t), _tp(a_pairs_t),
+                                                   _tp(a_ops_t), _tp(a_scales_t),
                                                    _tp(D) if R else None, _stream(stream)),
           "svdq_quantize_act_lowrank_down_tiled")
 
 
-def w4a4_gemm_lowrank_up_tiled(a_ops_t, a_pairs_t, w_codes_t, w_scales_t, D, L2t, R: int, bias, Y,
+def w4a4_gemm_lowrank_up_tiled(a_ops_t, a_scales_t, w_codes_t, w_scales_t, D, L2t, R: int, bias, Y,
                                K: int, stream=None, activation=None):
     """K2 on the tiled layouts."""
     _mat("Y", Y, None, None)
     M, N = Y.shape
-    _act_side_tiled(M, K, R, a_ops_t, a_pairs_t, D)
+    _act_side_tiled(M, K, R, a_ops_t, a_scales_t, D)
     _weights_tiled(N, K, R, w_codes_t, w_scales_t, L2t)
     _bias(bias, N)
-    _on_gpu(a_ops_t, a_pairs_t, w_codes_t, w_scales_t, D if R else None, L2t if R else None, bias,
+    _on_gpu(a_ops_t, a_scales_t, w_codes_t, w_scales_t, D if R else None, L2t if R else None, bias,
             Y)
-    check(lib.svdq_w4a4_gemm_lowrank_up_tiled(_tp(a_ops_t), _tp(a_pairs_t), _tp(w_codes_t),
+    check(lib.svdq_w4a4_gemm_lowrank_up_tiled(_tp(a_ops_t), _tp(a_scales_t), _tp(w_codes_t),
                                               _tp(w_scales_t), _tp(D) if R else None,
                                               _tp(L2t) if R else None, R, _tp(bias), _tp(Y),
                                               _dt(Y), M, N, K, Y.stride(0), _act(activation),
@@ -819,7 +819,7 @@ class Linear:
         if self.tiled:
             ct, st = pack_w4a4_tiles(prep.w_codes, prep.w_scales, prep.K)
             self.w_codes = torch.from_numpy(ct).to(dev)
-            self.w_scales = torch.from_numpy(st.view(np.int16)).to(dev)
+            self.w_scales = torch.from_numpy(st).to(dev)
         elif self.fmt == "w4a16":
             ct, st = pack_w4a16_tiles(prep.w_codes, prep.w_scales, prep.K)
             self.w_codes = torch.from_numpy(ct).to(dev)

@@ -151,14 +151,14 @@ WsLayout ws_layout(int64_t M, int64_t K, int32_t R, bool mx) {
   return w;
 }
 
-// The tiled INT4 path: operand blocks ceil(M/16) x K/64 of 1 KB, scale pairs
-// ceil(M/128) x K/64 of 1 KB, D.
+// The tiled INT4 path: operand blocks ceil(M/16) x K/64 of 1 KB, scales
+// ceil(M/128) x K/64 of 512 bytes, D.
 WsLayout tiled_ws_layout(int64_t M, int64_t K, int32_t R) {
   WsLayout w;
   const size_t G = static_cast<size_t>(K / SVDQ_GROUP);
   w.codes = 0;
   w.scales = round_up(static_cast<size_t>((M + 15) / 16) * G * 1024, 256);
-  w.d = w.scales + round_up(static_cast<size_t>((M + 127) / 128) * G * 1024, 256);
+  w.d = w.scales + round_up(static_cast<size_t>((M + 127) / 128) * G * 512, 256);
   w.total = w.d + round_up(static_cast<size_t>(M) * R * 4, 256);
   return w;
 }
@@ -340,15 +340,15 @@ int svdq_linear_canonical(const void* X, int x_dtype, int64_t ldx, const float* 
 int svdq_quantize_act_lowrank_down_tiled(const void* X, int x_dtype, int64_t M, int64_t K,
                                          int64_t ldx, const float* inv_smooth,
                                          const uint16_t* L1p, int32_t R, uint8_t* a_ops_t,
-                                         float* a_pairs_t, float* D, hipStream_t stream) {
+                                         float* a_scales_t, float* D, hipStream_t stream) {
   clear_error();
   const char* fn = "svdq_quantize_act_lowrank_down_tiled";
   if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, SVDQ_GROUP, a_ops_t,
-                          a_pairs_t, D, fn))
+                          a_scales_t, D, fn))
     return s;
   if (int s = device_ready()) return s;
   return check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1p, R, a_ops_t,
-                             a_pairs_t, kK1Int4Tiled, D, stream),
+                             a_scales_t, kK1Int4Tiled, D, stream),
                    "svdq_quantize_act_lowrank_down_tiled launch");
 }
 
@@ -356,7 +356,7 @@ namespace {
 // K2T adds each lane's offset into the tiled weight scales in 32 bits, and
 // its grid can hold up to 3 x 1024 more workgroups than tiles (split tails).
 int check_k2t_shape(int64_t M, int64_t N, int64_t K, const char* fn) {
-  if (((N + 31) / 32) * (K / SVDQ_GROUP) * 64 > int64_t{0xFFFFFFFF} ||
+  if (((N + 31) / 32) * (K / SVDQ_GROUP) * 256 > int64_t{0xFFFFFFFF} ||
       ((M + 127) / 128) * ((N + 127) / 128) > 0x7FFFFFFF - 4096) {
     set_error("%s: N=%lld K=%lld too large for the tiled kernel", fn, (long long)N, (long long)K);
     return SVDQ_ERR_SHAPE;
@@ -365,21 +365,21 @@ int check_k2t_shape(int64_t M, int64_t N, int64_t K, const char* fn) {
 }
 }  // namespace
 
-int svdq_w4a4_gemm_lowrank_up_tiled(const uint8_t* a_ops_t, const float* a_pairs_t,
-                                    const uint8_t* w_codes_t, const uint16_t* w_scales_t,
+int svdq_w4a4_gemm_lowrank_up_tiled(const uint8_t* a_ops_t, const float* a_scales_t,
+                                    const uint8_t* w_codes_t, const float* w_scales_t,
                                     const float* D, const uint16_t* L2t, int32_t R,
                                     const float* bias, void* Y, int y_dtype, int64_t M, int64_t N,
                                     int64_t K, int64_t ldy, int32_t activation,
                                     hipStream_t stream) {
   clear_error();
   const char* fn = "svdq_w4a4_gemm_lowrank_up_tiled";
-  if (int s = validate_k2(a_ops_t, a_pairs_t, w_codes_t, w_scales_t, D, L2t, R, bias, Y, y_dtype,
+  if (int s = validate_k2(a_ops_t, a_scales_t, w_codes_t, w_scales_t, D, L2t, R, bias, Y, y_dtype,
                           M, N, K, ldy, SVDQ_GROUP, fn))
     return s;
   if (int s = check_k2t_shape(M, N, K, fn)) return s;
   if (int s = check_activation(activation, fn)) return s;
   if (int s = device_ready()) return s;
-  return check_hip(launch_k2t(a_ops_t, a_pairs_t, w_codes_t, w_scales_t, D, L2t, R, bias, Y,
+  return check_hip(launch_k2t(a_ops_t, a_scales_t, w_codes_t, w_scales_t, D, L2t, R, bias, Y,
                               y_dtype == SVDQ_F16, M, N, K, ldy,
                               activation == SVDQ_ACT_GELU_TANH, stream),
                    "svdq_w4a4_gemm_lowrank_up_tiled launch");
@@ -392,7 +392,7 @@ size_t svdq_linear_tiled_workspace_bytes(int64_t M, int64_t K, int32_t R) {
 
 int svdq_linear_tiled(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
                       const uint16_t* L1p, const uint16_t* L2t, int32_t R,
-                      const uint8_t* w_codes_t, const uint16_t* w_scales_t, const float* bias,
+                      const uint8_t* w_codes_t, const float* w_scales_t, const float* bias,
                       void* Y, int y_dtype, int64_t ldy, int64_t M, int64_t K, int64_t N,
                       void* ws, size_t ws_bytes, int32_t activation, hipStream_t stream) {
   clear_error();
@@ -414,21 +414,21 @@ int svdq_linear_tiled(const void* X, int x_dtype, int64_t ldx, const float* inv_
   }
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint8_t* a_ops = base + L.codes;
-  float* a_pairs = reinterpret_cast<float*>(base + L.scales);
+  float* a_scales = reinterpret_cast<float*>(base + L.scales);
   float* D = R > 0 ? reinterpret_cast<float*>(base + L.d) : nullptr;
-  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, SVDQ_GROUP, a_ops, a_pairs,
+  if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, SVDQ_GROUP, a_ops, a_scales,
                           D, fn))
     return s;
-  if (int s = validate_k2(a_ops, a_pairs, w_codes_t, w_scales_t, D, L2t, R, bias, Y, y_dtype, M,
+  if (int s = validate_k2(a_ops, a_scales, w_codes_t, w_scales_t, D, L2t, R, bias, Y, y_dtype, M,
                           N, K, ldy, SVDQ_GROUP, fn))
     return s;
   if (int s = check_k2t_shape(M, N, K, fn)) return s;
   if (int s = device_ready()) return s;
   if (int s = check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1p, R, a_ops,
-                                  a_pairs, kK1Int4Tiled, D, stream),
+                                  a_scales, kK1Int4Tiled, D, stream),
                         "svdq_linear_tiled K1 launch"))
     return s;
-  return check_hip(launch_k2t(a_ops, a_pairs, w_codes_t, w_scales_t, D, L2t, R, bias, Y,
+  return check_hip(launch_k2t(a_ops, a_scales, w_codes_t, w_scales_t, D, L2t, R, bias, Y,
                               y_dtype == SVDQ_F16, M, N, K, ldy, activation == SVDQ_ACT_GELU_TANH,
                               stream),
                    "svdq_linear_tiled K2 launch");

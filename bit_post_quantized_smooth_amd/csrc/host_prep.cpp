@@ -591,9 +591,9 @@ size_t svdq_int4_act_tiled_bytes(int64_t M, int64_t K) {
   return static_cast<size_t>((M + 15) / 16) * static_cast<size_t>(K / SVDQ_GROUP) * 1024;
 }
 
-size_t svdq_int4_pairs_tiled_bytes(int64_t M, int64_t K) {
+size_t svdq_int4_act_scales_tiled_bytes(int64_t M, int64_t K) {
   if (M < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) return 0;
-  return static_cast<size_t>((M + 127) / 128) * static_cast<size_t>(K / SVDQ_GROUP) * 1024;
+  return static_cast<size_t>((M + 127) / 128) * static_cast<size_t>(K / SVDQ_GROUP) * 512;
 }
 
 size_t svdq_int4_w_codes_tiled_bytes(int64_t N, int64_t K) {
@@ -603,11 +603,11 @@ size_t svdq_int4_w_codes_tiled_bytes(int64_t N, int64_t K) {
 
 size_t svdq_int4_w_scales_tiled_bytes(int64_t N, int64_t K) {
   if (N < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) return 0;
-  return static_cast<size_t>((N + 31) / 32) * static_cast<size_t>(K / SVDQ_GROUP) * 64;
+  return static_cast<size_t>((N + 31) / 32) * static_cast<size_t>(K / SVDQ_GROUP) * 256;
 }
 
 int svdq_pack_w4a4_tiles(const uint8_t* w_codes, const uint16_t* w_scales, int64_t N, int64_t K,
-                         uint8_t* w_codes_t, uint16_t* w_scales_t) {
+                         uint8_t* w_codes_t, float* w_scales_t) {
   clear_error();
   if (!w_codes || !w_scales || !w_codes_t || !w_scales_t) {
     set_error("svdq_pack_w4a4_tiles: null pointer");
@@ -635,7 +635,10 @@ int svdq_pack_w4a4_tiles(const uint8_t* w_codes, const uint16_t* w_scales, int64
           for (int t = 0; t < 8; ++t)
             dst[t] = n < N ? w_codes[n * kb + 32 * g + 8 * (l >> 4) + t] : uint8_t{0};
         }
-  // scales: block (s, g), entry 8q + 4j + e: column 32s + 16j + 4q + e (0 past N)
+  // scales: block (s, g), entries 16q + 8j + 2e and +1: the pair
+  // (s/256, -12582912 s/256) of column 32s + 16j + 4q + e (0 past N); both
+  // products are exact in fp32 (a power of two; 12582912/256 = 3 * 2^14 adds
+  // two bits to the 11 of an fp16 significand)
 #pragma omp parallel for schedule(static)
   for (int64_t s = 0; s < ns; ++s)
     for (int64_t g = 0; g < G; ++g)
@@ -643,8 +646,10 @@ int svdq_pack_w4a4_tiles(const uint8_t* w_codes, const uint16_t* w_scales, int64
         for (int j = 0; j < 2; ++j)
           for (int e = 0; e < 4; ++e) {
             const int64_t n = 32 * s + 16 * j + 4 * q + e;
-            w_scales_t[(s * G + g) * 32 + 8 * q + 4 * j + e] =
-                n < N ? w_scales[n * G + g] : uint16_t{0};
+            const float sw = n < N ? f16_to_f32(w_scales[n * G + g]) : 0.f;
+            float* dst = w_scales_t + (s * G + g) * 64 + 16 * q + 8 * j + 2 * e;
+            dst[0] = sw * 0.00390625f;
+            dst[1] = sw * -49152.0f;
           }
   return SVDQ_OK;
 }

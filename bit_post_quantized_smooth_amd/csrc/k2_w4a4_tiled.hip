@@ -7,8 +7,8 @@
 // 64-channel group is the exact group partial P (times 256, read through the
 // 1.5*2^23 accumulator seed as the float f = 12582912 + 256 P); per output
 // and group two fp32 ops
-//     t   = fma(f, s_x/256, -12582912 s_x/256) = P s_x   (exact)
-//     acc = fma(t, s_w, acc)                            (the one rounding)
+//     t   = fma(f, s_w/256, -12582912 s_w/256) = P s_w   (exact)
+//     acc = fma(t, s_x, acc)                            (the one rounding)
 // and the low-rank branch fp16(D) . L2 and the bias in the same kernel (the
 // Nunchaku engine fuses the low-rank kernels into the low-bit ones:
 // SVDQuant abstract; the disruptive-concepts.com post, section "Nunchaku:
@@ -23,21 +23,21 @@
 // kernel keeps every other vector op out of the K loop:
 // - the activation operand arrives already widened, in the matrix
 //   instruction's lane order, from the pre-kernel (svdq.h, tiled INT4
-//   layouts), with its scale as the fp32 pair (s_x/256, -12582912 s_x/256);
+//   layouts), with its scale in fp32;
 // - the weights stay 4-bit (the 4-bit weight memory is the method's point)
 //   in a lane-order tiling per 32-column strip, so a wave's weight fragment
 //   for one group is one 16-byte read per lane, widened once (12 bit ops);
-// - the weight scales are converted to fp32 once per group (8 conversions):
-//   folded into the FMAs instead, as v_fma_mix_f32, they would cost 64 ops
-//   at half the rate of v_fma_f32;
+//   their scales arrive as the exact fp32 pairs (s_w/256, -12582912 s_w/256),
+//   made once offline, so no scale is converted in the loop (an fp16 scale
+//   folded into the FMAs as v_fma_mix_f32 would cost ~4.4 cycles an op
+//   against ~2.5 for v_fma_f32);
 // - every operand goes from global memory straight into LDS
 //   (global_load_lds: no register round trip), KSTAGES groups deep, with one
 //   barrier per group; addresses advance by scalar offsets.
 // What remains per group and wave: 16 matrix instructions, 128 rescale ops,
-// 8 conversions, 12 widening ops, 9 address and other ops, 14 LDS reads and
-// 5 copies. Three workgroups share a compute unit (168 registers, 40.7 KB of
-// LDS), so a wave waiting at the barrier or on LDS leaves the SIMD to two
-// others.
+// 12 widening ops, 9 address and other ops, 15 LDS reads and 5 copies. Three
+// workgroups share a compute unit (142 registers, 41.5 KB of LDS), so a wave
+// waiting at the barrier or on LDS leaves the SIMD to two others.
 //
 // Tiling: a 256-thread workgroup computes a 128 x 128 tile of Y; wave w owns
 // all 128 rows and columns 32w .. 32w+31 (8 x 2 blocks of 16 x 16), so its
@@ -58,11 +58,12 @@ namespace {
 
 constexpr int NT = 256;             // threads per workgroup
 constexpr int kBlk = 1024;          // one operand block: 64 lanes x 16 bytes
-constexpr int kPairBlk = 256;       // scale pairs of one 128-row band and group (floats)
-constexpr int kWsBlk = 32;          // fp16 weight scales of one 32-column strip and group
-// LDS ring depth. Three stages (40.7 KB) let three workgroups share a
-// compute unit; with four (54.3 KB) only two were resident, measured, though
-// three times 54.3 KB is below the 160 KB of LDS (the allocation granularity).
+constexpr int kSxBlk = 128;         // activation scales of one 128-row band and group (floats)
+constexpr int kWpBlk = 64;          // weight scale pairs of one 32-column strip and group (floats)
+// LDS ring depth. Three stages (41.5 KB) let three workgroups share a
+// compute unit; with four (54.3 KB at the time) only two were resident,
+// measured, though three times 54.3 KB is below the 160 KB of LDS (the
+// allocation granularity).
 constexpr int KSTAGES = 3;
 constexpr int KAHEAD = KSTAGES - 1; // groups copied ahead of the one computed
 
@@ -70,8 +71,8 @@ constexpr int KAHEAD = KSTAGES - 1; // groups copied ahead of the one computed
 struct alignas(16) TStage {
   uint8_t a[8][kBlk];               // activation operands of the tile's row blocks (int8 16q)
   uint8_t b[4][kBlk];               // 4-bit weight codes of the 4 waves' strips
-  float p[kPairBlk];                // scale pairs of the 128-row band
-  uint16_t w[4][kWsBlk];            // fp16 weight scales of 4 strips
+  float sx[kSxBlk];                 // activation scales of the 128-row band
+  float wp[4][kWpBlk];              // weight scale pairs of the 4 strips
 };
 
 #define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
@@ -96,37 +97,29 @@ constexpr int kWaitAll = 0x0070;                    // vmcnt(0) lgkmcnt(0)
 
 template <int RB, int CB>
 struct TScales {
-  float sx[RB], be[RB];             // (s_x/256, -12582912 s_x/256) of the lane's row per row block
-  float sw[CB][4];                  // s_w of the lane's 4 columns per column block
+  float sx[RB];                     // s_x of the lane's row per row block
+  float ws[CB][4], wb[CB][4];       // (s_w/256, -12582912 s_w/256) of the lane's 4 columns per block
 };
 
+// t = P s_w exactly (see the file comment), then acc += t s_x with one
+// rounding: the same value as P s_x s_w + acc rounded once.
 template <int RB, int CB>
 __device__ __forceinline__ void rescale(v4f& acc, const v4i& p, const TScales<RB, CB>& sc, int i,
                                         int j) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int pe = p[e];                     // scalar copy: see as_float()
-    const float t = __builtin_fmaf(as_float(pe), sc.sx[i], sc.be[i]);
-    acc[e] = __builtin_fmaf(t, sc.sw[j][e], acc[e]);
+    const float t = __builtin_fmaf(as_float(pe), sc.ws[j][e], sc.wb[j][e]);
+    acc[e] = __builtin_fmaf(t, sc.sx[i], acc[e]);
   }
-}
-
-// fp16 -> fp32 kept as an instruction of its own. Left visible, the compiler
-// folds the conversion into each of the 4*RB rescale ops that use the value
-// (v_fma_mix_f32), and that form issues at half the rate of v_fma_f32 here
-// (a measured 4 against 2 cycles per wave64 instruction).
-__device__ __forceinline__ float h2f_opaque(uint32_t bits16) {
-  float f = h2f(static_cast<uint16_t>(bits16));
-  asm("" : "+v"(f));
-  return f;
 }
 
 // One tile of Y: rows m0 .. m0 + 16*RB - 1, columns n0 .. n0 + 64*CB - 1.
 template <int RB, int CB, bool Y_F16, bool GELU>
 __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __restrict__ a_ops,
-                                       const float* __restrict__ a_pairs,
+                                       const float* __restrict__ a_scales,
                                        const uint8_t* __restrict__ w_codes,
-                                       const uint16_t* __restrict__ w_scales,
+                                       const float* __restrict__ w_scales,
                                        const float* __restrict__ D,
                                        const uint16_t* __restrict__ L2t, int R,
                                        const float* __restrict__ bias, void* __restrict__ Y,
@@ -144,10 +137,9 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
   const int hb = CB == 1 ? static_cast<int>((nw / 16) & 1) : 0;   // its half of that strip
   // this wave's copies: activation row blocks ACOPY*w .. +ACOPY-1 of the tile
   // (clamped to the last row block: their outputs are never stored), the
-  // strip holding its columns, a quarter of the band's scale pairs, and the
-  // scales of the 4 strips from n0/32 on (every wave writes the same bytes,
-  // which keeps the copy counts equal). Bases are wave-uniform; each lane
-  // adds a 32-bit offset.
+  // strip holding its columns and that strip's scale pairs, and half of the
+  // band's activation scales. Every wave issues the same number of copies.
+  // Bases are wave-uniform; each lane adds a 32-bit offset.
   auto clamp_b = [&](int64_t b) { return b < Mb ? b : Mb - 1; };
   auto clamp_s = [&](int64_t s) { return s < Ns ? s : Ns - 1; };
   const uint8_t* ga[S::ACOPY];
@@ -155,10 +147,10 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
   for (int c = 0; c < S::ACOPY; ++c)
     ga[c] = a_ops + clamp_b(m0 / 16 + S::ACOPY * wave + c) * G * kBlk;
   const uint8_t* gb = w_codes + clamp_s(nw / 32) * G * kBlk;
-  const float* gp = a_pairs + (m0 / 128) * G * kPairBlk + 64 * wave;
+  const float* gx = a_scales + (m0 / 128) * G * kSxBlk + 64 * (wave & 1);
+  const float* gw = w_scales + clamp_s(nw / 32) * G * kWpBlk;
   const uint32_t lo16 = 16u * static_cast<uint32_t>(lane);
   const uint32_t lo4 = 4u * static_cast<uint32_t>(lane);
-  const uint32_t low = static_cast<uint32_t>((clamp_s(n0 / 32 + q) * G * kWsBlk + 2 * rl) * 2);
 
   auto copy = [&](TStage& s, int g) {
     g = g < G ? g : G - 1;
@@ -168,12 +160,16 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
       __builtin_amdgcn_global_load_lds(ga[c] + o + lo16, LDSP(&s.a[S::ACOPY * wave + c][0]), 16, 0,
                                        0);
     __builtin_amdgcn_global_load_lds(gb + o + lo16, LDSP(&s.b[wave][0]), 16, 0, 0);
+    // half of the band's activation scales (waves 2 and 3 write the same
+    // bytes as waves 0 and 1: a direct-to-LDS load of fewer than 4 bytes per
+    // lane still takes a 4-byte LDS slot per lane, so a quarter per wave
+    // would need 2-byte slots, which do not exist)
     __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const uint8_t*>(gp + static_cast<int64_t>(g) * kPairBlk) + lo4,
-        LDSP(&s.p[64 * wave]), 4, 0, 0);
+        reinterpret_cast<const uint8_t*>(gx + static_cast<int64_t>(g) * kSxBlk) + lo4,
+        LDSP(&s.sx[64 * (wave & 1)]), 4, 0, 0);
     __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const uint8_t*>(w_scales + static_cast<int64_t>(g) * kWsBlk) + low,
-        LDSP(&s.w[0][0]), 4, 0, 0);
+        reinterpret_cast<const uint8_t*>(gw + static_cast<int64_t>(g) * kWpBlk) + lo4,
+        LDSP(&s.wp[rs][0]), 4, 0, 0);
   };
   auto read_a = [&](const TStage& s, int i) {
     return *reinterpret_cast<const v4i*>(&s.a[i][16 * lane]);
@@ -208,36 +204,39 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
     sg = sg + 1 == KSTAGES ? 0 : sg + 1;
 
     const uint4 braw = *reinterpret_cast<const uint4*>(&s.b[wave][16 * lane]);
-    const uint4 wraw = *reinterpret_cast<const uint4*>(&s.w[rs][8 * q]);
     v4i A[2];
     A[0] = read_a(s, 0);
-    // pairs: row block i of the band, row r, at ((i/2)*16 + r)*4 + (i%2)*2
     TScales<RB, CB> sc;
+    // activation scales: row block i of the band, row r, at 8r + i
 #pragma unroll
-    for (int h = 0; h < RB / 2; ++h) {
-      const float4 v = *reinterpret_cast<const float4*>(&s.p[((rb0 / 2 + h) * 16 + rl) * 4]);
-      sc.sx[2 * h] = v.x;
-      sc.be[2 * h] = v.y;
-      sc.sx[2 * h + 1] = v.z;
-      sc.be[2 * h + 1] = v.w;
+    for (int h = 0; h < RB / 4; ++h) {
+      const float4 v = *reinterpret_cast<const float4*>(&s.sx[rl * 8 + rb0 + 4 * h]);
+      sc.sx[4 * h] = v.x;
+      sc.sx[4 * h + 1] = v.y;
+      sc.sx[4 * h + 2] = v.z;
+      sc.sx[4 * h + 3] = v.w;
+    }
+    // weight pairs: column 16j + 4q + e of the strip at 16q + 8j + 2e
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int jj = CB == 2 ? j : hb;
+      const float4 u = *reinterpret_cast<const float4*>(&s.wp[rs][16 * q + 8 * jj]);
+      const float4 v = *reinterpret_cast<const float4*>(&s.wp[rs][16 * q + 8 * jj + 4]);
+      sc.ws[j][0] = u.x;
+      sc.wb[j][0] = u.y;
+      sc.ws[j][1] = u.z;
+      sc.wb[j][1] = u.w;
+      sc.ws[j][2] = v.x;
+      sc.wb[j][2] = v.y;
+      sc.ws[j][3] = v.z;
+      sc.wb[j][3] = v.w;
     }
     v4i B[CB];
     if constexpr (CB == 2) {
       B[0] = widen_codes(make_uint2(braw.x, braw.y));
       B[1] = widen_codes(make_uint2(braw.z, braw.w));
-      const uint32_t w4[4] = {wraw.x, wraw.y, wraw.z, wraw.w};
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sc.sw[j][e] = h2f_opaque((e & 1) ? (w4[2 * j + e / 2] >> 16) : w4[2 * j + e / 2]);
     } else {
       B[0] = widen_codes(hb ? make_uint2(braw.z, braw.w) : make_uint2(braw.x, braw.y));
-      const uint32_t w0 = hb ? wraw.z : wraw.x, w1 = hb ? wraw.w : wraw.y;
-      sc.sw[0][0] = h2f_opaque(w0);
-      sc.sw[0][1] = h2f_opaque(w0 >> 16);
-      sc.sw[0][2] = h2f_opaque(w1);
-      sc.sw[0][3] = h2f_opaque(w1 >> 16);
     }
     v4i P[2][CB];
 #pragma unroll
@@ -311,8 +310,8 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
 // (the same for every wave of the workgroup, before any barrier).
 template <bool Y_F16, bool GELU>
 __global__ __launch_bounds__(NT, 3) void k2t_w4a4_kernel(
-    const uint8_t* __restrict__ a_ops, const float* __restrict__ a_pairs,
-    const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales,
+    const uint8_t* __restrict__ a_ops, const float* __restrict__ a_scales,
+    const uint8_t* __restrict__ w_codes, const float* __restrict__ w_scales,
     const float* __restrict__ D, const uint16_t* __restrict__ L2t, int R,
     const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N, int64_t K,
     int64_t ldy, int tiles_m, int tiles_n, int n_full, int split) {
@@ -321,7 +320,7 @@ __global__ __launch_bounds__(NT, 3) void k2t_w4a4_kernel(
   int tm, tn;
   if (b < n_full) {
     banded_tile(xcd_contiguous(b, n_full), tiles_m, tiles_n, tm, tn);
-    tile_t<8, 2, Y_F16, GELU>(st, a_ops, a_pairs, w_codes, w_scales, D, L2t, R, bias, Y, M, N, K,
+    tile_t<8, 2, Y_F16, GELU>(st, a_ops, a_scales, w_codes, w_scales, D, L2t, R, bias, Y, M, N, K,
                               ldy, static_cast<int64_t>(tm) * 128, static_cast<int64_t>(tn) * 128);
     return;
   }
@@ -332,10 +331,10 @@ __global__ __launch_bounds__(NT, 3) void k2t_w4a4_kernel(
   const int64_t n0 = static_cast<int64_t>(tn) * 128 + (split == 4 ? 64 * (part & 1) : 0);
   if (m0 >= M || n0 >= N) return;
   if (split == 2)
-    tile_t<4, 2, Y_F16, GELU>(st, a_ops, a_pairs, w_codes, w_scales, D, L2t, R, bias, Y, M, N, K,
+    tile_t<4, 2, Y_F16, GELU>(st, a_ops, a_scales, w_codes, w_scales, D, L2t, R, bias, Y, M, N, K,
                               ldy, m0, n0);
   else
-    tile_t<4, 1, Y_F16, GELU>(st, a_ops, a_pairs, w_codes, w_scales, D, L2t, R, bias, Y, M, N, K,
+    tile_t<4, 1, Y_F16, GELU>(st, a_ops, a_scales, w_codes, w_scales, D, L2t, R, bias, Y, M, N, K,
                               ldy, m0, n0);
 }
 
@@ -361,8 +360,8 @@ int k2t_slots() {
 
 }  // namespace
 
-hipError_t launch_k2t(const uint8_t* a_ops, const float* a_pairs, const uint8_t* w_codes_t,
-                      const uint16_t* w_scales_t, const float* D, const uint16_t* L2t, int R,
+hipError_t launch_k2t(const uint8_t* a_ops, const float* a_scales, const uint8_t* w_codes_t,
+                      const float* w_scales_t, const float* D, const uint16_t* L2t, int R,
                       const float* bias, void* Y, bool y_f16, int64_t M, int64_t N, int64_t K,
                       int64_t ldy, bool gelu, hipStream_t stream) {
   const int tiles_m = static_cast<int>((M + 127) / 128);
@@ -377,7 +376,7 @@ hipError_t launch_k2t(const uint8_t* a_ops, const float* a_pairs, const uint8_t*
   const int n_full = T - n_split;
   const dim3 grid(static_cast<unsigned>(n_full + split * n_split)), block(NT);
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, block, 0, stream, a_ops, a_pairs, w_codes_t, w_scales_t, D,
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, a_ops, a_scales, w_codes_t, w_scales_t, D,
                        L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n, n_full, split);
   };
   if (y_f16)

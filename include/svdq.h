@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 7
+#define SVDQ_ABI_VERSION 8
 
 /* status codes */
 enum {
@@ -311,54 +311,55 @@ int svdq_linear_noalloc(const void* X, int x_dtype, int64_t ldx, const float* in
  *             0..3 = 16*(c0, c2, c4, c6), 4..7 = 16*(c1, c3, c5, c7),
  *             8..11 = 16*(c8, c10, c12, c14), 12..15 = 16*(c9, c11, c13, c15).
  *             Rows past M inside the last block hold row M-1's values.
- *   a_pairs_t activation scales, ceil(M/128) x G blocks of 256 fp32; block
- *             (t, g) holds, for row 128t + 16i + r, the pair
- *             (s/256, -12582912 s/256) with s = fp32(the row's fp16 group
- *             scale) at index ((i/2)*16 + r)*4 + (i%2)*2 (both values exact).
+ *   a_scales_t activation scales, ceil(M/128) x G blocks of 128 fp32; block
+ *             (t, g) holds s = fp32(the fp16 group scale) of row 128t + 16i + r
+ *             (i < 8, r < 16) at index 8r + i.
  *   w_codes_t weight codes, 4-bit as in the canonical layout, ceil(N/32) x G
  *             blocks of 1024 bytes; block (s, g) lane l = 16q + r holds bytes
  *             32g + 8q .. +7 of the canonical rows of columns 32s + r (bytes
  *             0..7) and 32s + 16 + r (bytes 8..15); 0 past N.
- *   w_scales_t weight scales, ceil(N/32) x G blocks of 32 fp16; entry
- *             8q + 4j + e of block (s, g) is the scale of column
- *             32s + 16j + 4q + e in group g; 0 past N.
+ *   w_scales_t weight scales as fp32 pairs, ceil(N/32) x G blocks of 64 fp32;
+ *             entries 16q + 8j + 2e and 16q + 8j + 2e + 1 of block (s, g) are
+ *             (s/256, -12582912 s/256), s = fp32(the fp16 scale of column
+ *             32s + 16j + 4q + e in group g), both exact; 0 past N. The pair
+ *             turns the matrix instruction's biased result into P s exactly.
  * The weight layouts are a permutation of the canonical w_codes / w_scales
  * (svdq_pack_w4a4_tiles), made once offline; the weights stay at 4 bits.
  */
 
 /* Bytes of the tiled INT4 layouts (0 for invalid sizes). */
 size_t svdq_int4_act_tiled_bytes(int64_t M, int64_t K);
-size_t svdq_int4_pairs_tiled_bytes(int64_t M, int64_t K);
+size_t svdq_int4_act_scales_tiled_bytes(int64_t M, int64_t K);
 size_t svdq_int4_w_codes_tiled_bytes(int64_t N, int64_t K);
 size_t svdq_int4_w_scales_tiled_bytes(int64_t N, int64_t K);
 
 /* Host: canonical w_codes (N x K/2) and w_scales (N x K/64 fp16) -> the tiled
- * weight layouts above (a permutation, zero padding). K % 64 == 0, N >= 1.
- * Outputs must not overlap inputs. */
+ * weight layouts above (a permutation of the codes, the scales as exact fp32
+ * pairs, zero padding). K % 64 == 0, N >= 1. Outputs must not overlap inputs. */
 int svdq_pack_w4a4_tiles(const uint8_t* w_codes, const uint16_t* w_scales, int64_t N, int64_t K,
-                         uint8_t* w_codes_t, uint16_t* w_scales_t);
+                         uint8_t* w_codes_t, float* w_scales_t);
 
 /* Device: K1 (svdq_quantize_act_lowrank_down: the same smoothing, quantizer
- * and D) writing the codes and scales as a_ops_t and a_pairs_t
- * (svdq_int4_act_tiled_bytes(M, K) and svdq_int4_pairs_tiled_bytes(M, K)
+ * and D) writing the codes and scales as a_ops_t and a_scales_t
+ * (svdq_int4_act_tiled_bytes(M, K) and svdq_int4_act_scales_tiled_bytes(M, K)
  * bytes, 16-byte aligned). */
 int svdq_quantize_act_lowrank_down_tiled(const void* X, int x_dtype, int64_t M, int64_t K,
                                          int64_t ldx, const float* inv_smooth,
                                          const uint16_t* L1p, int32_t R, uint8_t* a_ops_t,
-                                         float* a_pairs_t, float* D, hipStream_t stream);
+                                         float* a_scales_t, float* D, hipStream_t stream);
 
 /* Device: K2 (svdq_w4a4_gemm_lowrank_up: the same exact int32 group partials,
  * fp32 rescale, low-rank up-projection, bias and activation) on the tiled
  * layouts. The order of the fp32 sums differs from K2's (the low-rank term
  * first), within the same rounding bound. */
-int svdq_w4a4_gemm_lowrank_up_tiled(const uint8_t* a_ops_t, const float* a_pairs_t,
-                                    const uint8_t* w_codes_t, const uint16_t* w_scales_t,
+int svdq_w4a4_gemm_lowrank_up_tiled(const uint8_t* a_ops_t, const float* a_scales_t,
+                                    const uint8_t* w_codes_t, const float* w_scales_t,
                                     const float* D, const uint16_t* L2t, int32_t R,
                                     const float* bias, void* Y, int y_dtype, int64_t M, int64_t N,
                                     int64_t K, int64_t ldy, int32_t activation,
                                     hipStream_t stream);
 
-/* Bytes of workspace svdq_linear_tiled needs: a_ops_t, a_pairs_t and D, each
+/* Bytes of workspace svdq_linear_tiled needs: a_ops_t, a_scales_t and D, each
  * 256-byte aligned inside the workspace. */
 size_t svdq_linear_tiled_workspace_bytes(int64_t M, int64_t K, int32_t R);
 
@@ -367,7 +368,7 @@ size_t svdq_linear_tiled_workspace_bytes(int64_t M, int64_t K, int32_t R);
  * svdq_pack_w4a4_tiles. */
 int svdq_linear_tiled(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
                       const uint16_t* L1p, const uint16_t* L2t, int32_t R,
-                      const uint8_t* w_codes_t, const uint16_t* w_scales_t, const float* bias,
+                      const uint8_t* w_codes_t, const float* w_scales_t, const float* bias,
                       void* Y, int y_dtype, int64_t ldy, int64_t M, int64_t K, int64_t N,
                       void* ws, size_t ws_bytes, int32_t activation, hipStream_t stream);
 

@@ -44,40 +44,38 @@ def untile_act_ops(ops: np.ndarray, M: int, K: int) -> np.ndarray:
     return v.reshape(nb * 16, K).astype(np.int8)
 
 
-def pair_index(M: int, K: int):
-    """(row, group) -> flat float index of the row's s/256 in a_pairs_t."""
+def act_scale_index(M: int, K: int):
+    """(row, group) -> flat float index of the row's scale in a_scales_t."""
     G = K // 64
     rows = np.arange(((M + 127) // 128) * 128)
     t, i, r = rows // 128, (rows % 128) // 16, rows % 16
-    base = ((i // 2) * 16 + r) * 4 + (i % 2) * 2
-    return t[:, None] * G * 256 + np.arange(G)[None, :] * 256 + base[:, None]
+    return t[:, None] * G * 128 + np.arange(G)[None, :] * 128 + (8 * r + i)[:, None]
 
 
-def tile_pairs(scales: np.ndarray, M: int, K: int) -> np.ndarray:
-    """fp16 activation scales (M x G) -> a_pairs_t floats (s/256, -12582912 s/256);
-    rows past M get zeros."""
+def tile_act_scales(scales: np.ndarray, M: int, K: int) -> np.ndarray:
+    """fp16 activation scales (M x G) -> a_scales_t floats; rows past M get zeros."""
     G = K // 64
     nt = (M + 127) // 128
-    s = np.zeros((nt * 128, G), dtype=np.float64)
-    s[:M] = np.asarray(scales, dtype=np.float16).astype(np.float64)
-    out = np.zeros(nt * G * 256, dtype=np.float32)
-    idx = pair_index(M, K)
-    out[idx] = (s / 256.0).astype(np.float32)
-    out[idx + 1] = (s * (-12582912.0 / 256.0)).astype(np.float32)
+    s = np.zeros((nt * 128, G), dtype=np.float32)
+    s[:M] = np.asarray(scales, dtype=np.float16).astype(np.float32)
+    out = np.zeros(nt * G * 128, dtype=np.float32)
+    out[act_scale_index(M, K)] = s
     return out
 
 
 def tile_w(w_codes: np.ndarray, w_scales: np.ndarray, N: int, K: int):
     """canonical weight codes (N x K/2) and fp16 scale bits (N x G) -> (w_codes_t
-    bytes, w_scales_t uint16), zero past N."""
+    bytes, w_scales_t fp32 pairs (s/256, -12582912 s/256)), zero past N."""
     G, ns = K // 64, (N + 31) // 32
     c = np.zeros((ns * 32, K // 2), dtype=np.uint8)
     c[:N] = w_codes
     # [s, j, r, g, q, 8] -> [s, g, q, r, j, 8]  (lane = 16q + r, bytes 8j .. 8j+7)
     ct = c.reshape(ns, 2, 16, G, 4, 8).transpose(0, 3, 4, 2, 1, 5)
-    sc = np.zeros((ns * 32, G), dtype=np.uint16)
-    sc[:N] = np.asarray(w_scales).view(np.uint16) if np.asarray(w_scales).dtype != np.uint16 \
-        else w_scales
-    # column 32s + 16j + 4q + e -> entry 8q + 4j + e of block (s, g)
-    st = sc.reshape(ns, 2, 4, 4, G).transpose(0, 4, 2, 1, 3)
-    return np.ascontiguousarray(ct).reshape(-1), np.ascontiguousarray(st).reshape(-1)
+    sc = np.zeros((ns * 32, G), dtype=np.float64)
+    bits = np.asarray(w_scales)
+    bits = bits if bits.dtype == np.uint16 else bits.view(np.uint16)
+    sc[:N] = bits.view(np.float16).astype(np.float64)
+    # column 32s + 16j + 4q + e -> entries 16q + 8j + 2e (+1) of block (s, g)
+    st = sc.reshape(ns, 2, 4, 4, G).transpose(0, 4, 2, 1, 3)      # s, g, q, j, e
+    pairs = np.stack([st / 256.0, st * (-12582912.0 / 256.0)], axis=-1).astype(np.float32)
+    return np.ascontiguousarray(ct).reshape(-1), np.ascontiguousarray(pairs).reshape(-1)

@@ -454,6 +454,26 @@ def check_method_sanity(O):
     assert errs[L.rank] < 0.9 * errs[0], errs
 
 
+def check_method_sanity_dit(O):
+    """E8 on the DiT fused-QKV workload (4608 x 3072 x 9216, r = 32): the
+    low-rank branch lowers the error against the exact X.W on the same sampled
+    rows. Smoothing is calibrated on all rows; one SVD serves both ranks."""
+    import workloads as wl
+    L, X, W = wl.layer_inputs(1, 0)
+    lam = O.smoothing_factors(O.channel_absmax(X), W)
+    svd = O.svd_canonical(O.smooth_weight(W, lam))
+    rows = np.random.default_rng(8).choice(L.M, 48, replace=False)
+    Xs = X[rows]
+    ref = Xs.astype(np.float64) @ W.astype(np.float64)
+    errs = {}
+    for r in (0, L.rank):
+        p = O.prepare(W, lam, r, svd=svd)
+        Y = O.linear(Xs, p["inv_smooth"], p["L1"], p["L2"], p["w_codes"], p["w_scales"], None,
+                     "f32")
+        errs[r] = float(np.linalg.norm(Y.astype(np.float64) - ref) / np.linalg.norm(ref))
+    assert errs[L.rank] < 0.95 * errs[0], errs
+
+
 def check_gelu(O):
     x = np.array([0.0, 1.0, -1.0, 3.0, -3.0, 20.0, -20.0], dtype=np.float64)
     g = O.gelu_tanh(x).astype(np.float64)
@@ -496,7 +516,7 @@ ALL_CHECKS = [
     check_golden_tiny_linear, check_quantizer_bruteforce, check_roundtrip_bound,
     check_invariants, check_pack_roundtrip, check_eym, check_sigma_split, check_full_rank,
     check_reconstruction, check_partials_bruteforce, check_dense_identity, check_lora,
-    check_method_sanity, check_gelu, check_linear_gelu,
+    check_method_sanity, check_method_sanity_dit, check_gelu, check_linear_gelu,
 ]
 
 

@@ -2,7 +2,7 @@
 svdq_w4a4_gemm_lowrank_up_tiled, svdq_linear_tiled) through the C ABI against
 the CPU oracle.
 
-Bit-exact: the activation operands and scale pairs the tiled pre-kernel
+Bit-exact: the activation operands and fp32 scales the tiled pre-kernel
 writes (read back with the layout formulas of svdq.h, tests/int4_tiles.py),
 and the tiled GEMM's own int32 group partials, exposed through Y with
 power-of-two scales as in test_gpu_k2_partials.py. Within 2e-3 of max|Y| and
@@ -51,8 +51,8 @@ class TiledLayer:
         self.bias = dev(bias) if bias is not None else None
         self.ops = torch.full((sq.int4_act_tiled_bytes(self.M, self.K),), 0x5A, dtype=torch.uint8,
                               device="cuda")
-        self.pairs = torch.full((sq.int4_pairs_tiled_bytes(self.M, self.K) // 4,), float("nan"),
-                                dtype=torch.float32, device="cuda")
+        self.scales = torch.full((sq.int4_act_scales_tiled_bytes(self.M, self.K) // 4,),
+                                 float("nan"), dtype=torch.float32, device="cuda")
         self.D = torch.empty((self.M, max(self.R, 1)), dtype=torch.float32, device="cuda")
         self.Y = torch.full((self.M, self.N), float("nan"),
                             dtype=torch.float16 if y_dtype == "f16" else torch.float32,
@@ -60,10 +60,10 @@ class TiledLayer:
 
     def k1(self):
         sq_mod().quantize_act_lowrank_down_tiled(self.X, self.inv, self.L1p, self.R, self.ops,
-                                                 self.pairs, self.D if self.R else None)
+                                                 self.scales, self.D if self.R else None)
 
     def k2(self, activation=None):
-        sq_mod().w4a4_gemm_lowrank_up_tiled(self.ops, self.pairs, self.wc, self.ws,
+        sq_mod().w4a4_gemm_lowrank_up_tiled(self.ops, self.scales, self.wc, self.ws,
                                             self.D if self.R else None, self.L2t, self.R,
                                             self.bias, self.Y, self.K, activation=activation)
 
@@ -77,14 +77,13 @@ def _check_k1_tiled(X, inv_o, p, K, d):
     nbad = int(np.count_nonzero(q[:M] != ref))
     assert nbad == 0, f"{nbad} activation operands differ"
     assert np.all(q[M:] == ref[M - 1]), "rows past M must repeat the last row"
-    pairs = d.pairs.cpu().numpy()
-    idx = T.pair_index(M, K)
-    exp = T.tile_pairs(a_scales, M, K)
-    assert np.array_equal(pairs[idx[:M]].view(np.uint32), exp[idx[:M]].view(np.uint32))
-    assert np.array_equal(pairs[idx[:M] + 1].view(np.uint32), exp[idx[:M] + 1].view(np.uint32))
+    sc = d.scales.cpu().numpy()
+    idx = T.act_scale_index(M, K)
+    exp = T.tile_act_scales(a_scales, M, K)
+    assert np.array_equal(sc[idx[:M]].view(np.uint32), exp[idx[:M]].view(np.uint32))
     Mb16 = ((M + 15) // 16) * 16
     if Mb16 > M:
-        assert np.array_equal(pairs[idx[M:Mb16]], np.repeat(pairs[idx[M - 1:M]], Mb16 - M, 0))
+        assert np.array_equal(sc[idx[M:Mb16]], np.repeat(sc[idx[M - 1:M]], Mb16 - M, 0))
     if p.rank:
         Dg = d.D.cpu().numpy()[:, :p.rank].astype(np.float64)
         Do = O.down_projection(xh, p.L1)
@@ -110,7 +109,7 @@ def _run_k2t(a_codes, w_codes, sx, sw, M, N, K, pad=3):
     Ybig[:, N:] = -3.0
     ct, st = T.tile_w(w_codes, np.asarray(sw, dtype=np.float16).view(np.uint16), N, K)
     sq_mod().w4a4_gemm_lowrank_up_tiled(dev(T.tile_act_ops(a_codes, M, K)),
-                                        dev(T.tile_pairs(sx, M, K)), dev(ct), dev(st), None, None,
+                                        dev(T.tile_act_scales(sx, M, K)), dev(ct), dev(st), None, None,
                                         0, None, Ybig[:, :N], K)
     torch.cuda.synchronize()
     Yh = Ybig.cpu().numpy()

@@ -13,12 +13,19 @@ sq = pytest.importorskip("bit_post_quantized_smooth_amd")
 def test_pack_w4a4_tiles_matches_the_layout(N, K):
     rng = np.random.default_rng(N * 1000 + K)
     wc = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
-    ws = rng.integers(0, 1 << 16, size=(N, K // 64), dtype=np.uint16)
+    # every finite non-negative fp16 scale pattern is possible (zero and subnormals included)
+    ws = rng.integers(0, 0x7C00, size=(N, K // 64), dtype=np.uint16)
+    ws[0, 0] = 0x7BFF                                   # 65504, the largest scale
     ct, st = sq.pack_w4a4_tiles(wc, ws, K)
     ect, est = T.tile_w(wc, ws, N, K)
     assert ct.size == sq.int4_w_codes_tiled_bytes(N, K) == ect.size
-    assert st.size * 2 == sq.int4_w_scales_tiled_bytes(N, K) == est.size * 2
-    assert np.array_equal(ct, ect) and np.array_equal(st, est)
+    assert st.dtype == np.float32
+    assert st.size * 4 == sq.int4_w_scales_tiled_bytes(N, K) == est.size * 4
+    assert np.array_equal(ct, ect) and np.array_equal(st.view(np.uint32), est.view(np.uint32))
+    # the pair is exact: s/256 and -12582912 s/256 times 256 give back s and -12582912 s
+    s64 = ws.view(np.float16).astype(np.float64)
+    col = 0
+    assert st[0] * 256.0 == s64[col, 0] and st[1] == s64[col, 0] * -49152.0
     # a permutation with zero padding: every canonical byte appears exactly once
     assert np.array_equal(np.sort(ct)[-wc.size:], np.sort(wc.reshape(-1)))
     assert np.count_nonzero(ct) <= np.count_nonzero(wc)
@@ -34,9 +41,15 @@ def test_activation_tile_helpers_round_trip(M, K):
     back = T.untile_act_ops(ops, M, K)
     assert np.array_equal(back[:M], q)
     assert np.all(back[M:] == q[M - 1])
-    s = rng.standard_normal((M, K // 64)).astype(np.float16)
-    p = T.tile_pairs(s, M, K)
-    assert p.size * 4 == sq.int4_pairs_tiled_bytes(M, K)
-    idx = T.pair_index(M, K)[:M]
-    assert np.array_equal(p[idx], (s.astype(np.float64) / 256).astype(np.float32))
-    assert np.array_equal(p[idx + 1], (s.astype(np.float64) * -49152.0).astype(np.float32))
+    s = np.abs(rng.standard_normal((M, K // 64))).astype(np.float16)
+    p = T.tile_act_scales(s, M, K)
+    assert p.size * 4 == sq.int4_act_scales_tiled_bytes(M, K)
+    idx = T.act_scale_index(M, K)
+    assert np.array_equal(p[idx[:M]], s.astype(np.float32))
+    assert np.all(p[idx[M:]] == 0)
+    # the index formula is a bijection onto the blocks
+    assert np.array_equal(np.sort(idx.reshape(-1)), np.arange(p.size))
+    # row 128t + 16i + r, group g at (t G + g) 128 + 8 r + i
+    r_, g_ = min(M - 1, 137), K // 64 - 1
+    t, i, r = r_ // 128, (r_ % 128) // 16, r_ % 16
+    assert idx[r_, g_] == (t * (K // 64) + g_) * 128 + 8 * r + i
