@@ -268,18 +268,20 @@ def host_cores():
 def k1_bytes(M, K, R, xb, meta_per_row, tiled=False):
     """Read X once; write codes, scales (or exponents) and D; read L1 and 1/lambda.
     tiled: the activation side as the tiled path stores it (one int8 operand byte
-    per code, an fp32 scale per row and group)."""
-    act = M * K + 4 * M * (K // 64) if tiled else M * K // 2 + M * meta_per_row
+    per code, an fp32 scale per row and group, D in fp16)."""
+    if tiled:
+        return M * K * xb + M * K + 4 * M * (K // 64) + 2 * M * R + 2 * K * R + 4 * K
+    act = M * K // 2 + M * meta_per_row
     return M * K * xb + act + 4 * M * R + 2 * K * R + 4 * K
 
 
 def k2_bytes(M, N, K, R, yb, meta_per_row, tiled=False):
     """Codes and scales of both operands, D, L2, Y (bias not counted: zero in the configs).
     tiled: as the tiled path stores them (int8 activation operands and fp32 scales,
-    the weight scales as 8-byte fp32 pairs)."""
+    the weight scales as 8-byte fp32 pairs, D in fp16)."""
     if tiled:
         G = K // 64
-        return (M * K + 4 * M * G + N * K // 2 + 8 * N * G + 4 * M * R + 2 * R * N
+        return (M * K + 4 * M * G + N * K // 2 + 8 * N * G + 2 * M * R + 2 * R * N
                 + M * N * yb)
     act = M * K // 2 + M * meta_per_row
     return act + N * K // 2 + N * meta_per_row + 4 * M * R + 2 * R * N + M * N * yb
@@ -315,7 +317,9 @@ class Sets:
                 X=d(X), inv=d(prep.inv_smooth),
                 L1p=d(prep.L1p) if self.R else None, L2t=d(prep.L2t) if self.R else None,
                 b=None if bias is None else d(bias),
-                D=torch.empty((M, max(self.R, 1)), dtype=torch.float32, device="cuda"),
+                D=(torch.empty(max(sq.int4_d_tiled_bytes(M, self.R), 2) // 2, dtype=torch.int16,
+                               device="cuda") if self.tiled else
+                   torch.empty((M, max(self.R, 1)), dtype=torch.float32, device="cuda")),
                 Y=torch.empty((M, self.N), dtype=torch.float16 if y_dtype == "f16" else torch.float32,
                               device="cuda"))
             if self.w16:

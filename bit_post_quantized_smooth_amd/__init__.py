@@ -6,7 +6,7 @@ without a built library raises ImportError.
 """
 from . import _lib  # noqa: F401  (fails loudly when libsvdq.so is missing)
 from .api import (Conv2d, Linear, Prepared, channel_absmax, clock_mark, clock_probe,  # noqa: F401
-                  clock_rates, concat_lora, int4_act_tiled_bytes, int4_act_scales_tiled_bytes,
+                  clock_rates, concat_lora, int4_act_tiled_bytes, int4_act_scales_tiled_bytes, int4_d_tiled_bytes,
                   int4_w_codes_tiled_bytes, int4_w_scales_tiled_bytes, linear_tiled,
                   linear_tiled_workspace_bytes, pack_w4a4_tiles, quantize_act_lowrank_down_tiled,
                   w4a4_gemm_lowrank_up_tiled,
@@ -22,7 +22,7 @@ from .api import (Conv2d, Linear, Prepared, channel_absmax, clock_mark, clock_pr
                   w4a16_gemm, w4a16_tile_activation, w4a16_x_tiled_bytes, linear_w4a16)
 
 __all__ = ["Conv2d", "Linear", "Prepared", "channel_absmax", "clock_mark", "clock_probe",
-           "clock_rates", "concat_lora", "int4_act_tiled_bytes", "int4_act_scales_tiled_bytes",
+           "clock_rates", "concat_lora", "int4_act_tiled_bytes", "int4_act_scales_tiled_bytes", "int4_d_tiled_bytes",
            "int4_w_codes_tiled_bytes", "int4_w_scales_tiled_bytes", "linear_tiled",
            "linear_tiled_workspace_bytes", "pack_w4a4_tiles", "quantize_act_lowrank_down_tiled",
            "w4a4_gemm_lowrank_up_tiled", "conv2d", "conv2d_mx",

@@ -71,6 +71,7 @@ _SIGS = {
                                    _i64, _i64, _i64, _i32, _i32, _p]),
     "svdq_int4_act_tiled_bytes": (C.c_size_t, [_i64, _i64]),
     "svdq_int4_act_scales_tiled_bytes": (C.c_size_t, [_i64, _i64]),
+    "svdq_int4_d_tiled_bytes": (C.c_size_t, [_i64, _i32]),
     "svdq_int4_w_codes_tiled_bytes": (C.c_size_t, [_i64, _i64]),
     "svdq_int4_w_scales_tiled_bytes": (C.c_size_t, [_i64, _i64]),
     "svdq_pack_w4a4_tiles": (_int, [_p, _p, _i64, _i64, _p, _p]),

@@ -427,6 +427,10 @@ def int4_act_scales_tiled_bytes(M: int, K: int) -> int:
     return int(lib.svdq_int4_act_scales_tiled_bytes(M, K))
 
 
+def int4_d_tiled_bytes(M: int, R: int) -> int:
+    return int(lib.svdq_int4_d_tiled_bytes(M, R))
+
+
 def int4_w_codes_tiled_bytes(N: int, K: int) -> int:
     return int(lib.svdq_int4_w_codes_tiled_bytes(N, K))
 
@@ -448,12 +452,12 @@ def pack_w4a4_tiles(w_codes: np.ndarray, w_scales: np.ndarray, K: int):
     return ct, st
 
 
-def _act_side_tiled(M, K, R, a_ops_t, a_scales_t, D):
+def _act_side_tiled(M, K, R, a_ops_t, a_scales_t, D_t):
     _groups(K)
     _buf("a_ops_t", a_ops_t, _BYTES, min_bytes=int4_act_tiled_bytes(M, K))
     _buf("a_scales_t", a_scales_t, _F32, min_bytes=int4_act_scales_tiled_bytes(M, K))
     if R:
-        _buf("D", D, _F32, min_bytes=4 * M * R)
+        _buf("D_t", D_t, _HALF, min_bytes=int4_d_tiled_bytes(M, R))
 
 
 def _weights_tiled(N, K, R, w_codes_t, w_scales_t, L2t):
@@ -464,9 +468,10 @@ def _weights_tiled(N, K, R, w_codes_t, w_scales_t, L2t):
         _buf("L2t", L2t, _HALF, nbytes=2 * N * R)
 
 
-def quantize_act_lowrank_down_tiled(X, inv_smooth, L1p, R: int, a_ops_t, a_scales_t, D,
+def quantize_act_lowrank_down_tiled(X, inv_smooth, L1p, R: int, a_ops_t, a_scales_t, D_t,
                                     stream=None):
-    """K1 writing the tiled activation operands and fp32 scales."""
+    """K1 writing the tiled activation operands, fp32 scales and fp16 D_t."""
+    D = D_t
     _mat("X", X, None, None)
     M, K = X.shape
     _down(K, R, inv_smooth, L1p)
@@ -479,9 +484,10 @@ def quantize_act_lowrank_down_tiled(X, inv_smooth, L1p, R: int, a_ops_t, a_scale
           "svdq_quantize_act_lowrank_down_tiled")
 
 
-def w4a4_gemm_lowrank_up_tiled(a_ops_t, a_scales_t, w_codes_t, w_scales_t, D, L2t, R: int, bias, Y,
-                               K: int, stream=None, activation=None):
-    """K2 on the tiled layouts."""
+def w4a4_gemm_lowrank_up_tiled(a_ops_t, a_scales_t, w_codes_t, w_scales_t, D_t, L2t, R: int, bias,
+                               Y, K: int, stream=None, activation=None):
+    """K2 on the tiled layouts (D_t: the pre-kernel's fp16 D in operand order)."""
+    D = D_t
     _mat("Y", Y, None, None)
     M, N = Y.shape
     _act_side_tiled(M, K, R, a_ops_t, a_scales_t, D)

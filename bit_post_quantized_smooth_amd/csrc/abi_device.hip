@@ -152,14 +152,15 @@ WsLayout ws_layout(int64_t M, int64_t K, int32_t R, bool mx) {
 }
 
 // The tiled INT4 path: operand blocks ceil(M/16) x K/64 of 1 KB, scales
-// ceil(M/128) x K/64 of 512 bytes, D.
+// ceil(M/128) x K/64 of 512 bytes, fp16 D in operand order ceil(M/16) x
+// ceil(R/32) blocks of 1 KB.
 WsLayout tiled_ws_layout(int64_t M, int64_t K, int32_t R) {
   WsLayout w;
   const size_t G = static_cast<size_t>(K / SVDQ_GROUP);
   w.codes = 0;
   w.scales = round_up(static_cast<size_t>((M + 15) / 16) * G * 1024, 256);
   w.d = w.scales + round_up(static_cast<size_t>((M + 127) / 128) * G * 512, 256);
-  w.total = w.d + round_up(static_cast<size_t>(M) * R * 4, 256);
+  w.total = w.d + round_up(static_cast<size_t>((M + 15) / 16) * ((R + 31) / 32) * 1024, 256);
   return w;
 }
 
@@ -340,9 +341,11 @@ int svdq_linear_canonical(const void* X, int x_dtype, int64_t ldx, const float* 
 int svdq_quantize_act_lowrank_down_tiled(const void* X, int x_dtype, int64_t M, int64_t K,
                                          int64_t ldx, const float* inv_smooth,
                                          const uint16_t* L1p, int32_t R, uint8_t* a_ops_t,
-                                         float* a_scales_t, float* D, hipStream_t stream) {
+                                         float* a_scales_t, uint16_t* D_t, hipStream_t stream) {
   clear_error();
   const char* fn = "svdq_quantize_act_lowrank_down_tiled";
+  // D_t is checked (null, alignment) and passed as an untyped device pointer
+  float* D = reinterpret_cast<float*>(D_t);
   if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, SVDQ_GROUP, a_ops_t,
                           a_scales_t, D, fn))
     return s;
@@ -367,19 +370,20 @@ int check_k2t_shape(int64_t M, int64_t N, int64_t K, const char* fn) {
 
 int svdq_w4a4_gemm_lowrank_up_tiled(const uint8_t* a_ops_t, const float* a_scales_t,
                                     const uint8_t* w_codes_t, const float* w_scales_t,
-                                    const float* D, const uint16_t* L2t, int32_t R,
+                                    const uint16_t* D_t, const uint16_t* L2t, int32_t R,
                                     const float* bias, void* Y, int y_dtype, int64_t M, int64_t N,
                                     int64_t K, int64_t ldy, int32_t activation,
                                     hipStream_t stream) {
   clear_error();
   const char* fn = "svdq_w4a4_gemm_lowrank_up_tiled";
-  if (int s = validate_k2(a_ops_t, a_scales_t, w_codes_t, w_scales_t, D, L2t, R, bias, Y, y_dtype,
+  if (int s = validate_k2(a_ops_t, a_scales_t, w_codes_t, w_scales_t,
+                          reinterpret_cast<const float*>(D_t), L2t, R, bias, Y, y_dtype,
                           M, N, K, ldy, SVDQ_GROUP, fn))
     return s;
   if (int s = check_k2t_shape(M, N, K, fn)) return s;
   if (int s = check_activation(activation, fn)) return s;
   if (int s = device_ready()) return s;
-  return check_hip(launch_k2t(a_ops_t, a_scales_t, w_codes_t, w_scales_t, D, L2t, R, bias, Y,
+  return check_hip(launch_k2t(a_ops_t, a_scales_t, w_codes_t, w_scales_t, D_t, L2t, R, bias, Y,
                               y_dtype == SVDQ_F16, M, N, K, ldy,
                               activation == SVDQ_ACT_GELU_TANH, stream),
                    "svdq_w4a4_gemm_lowrank_up_tiled launch");
@@ -428,7 +432,8 @@ int svdq_linear_tiled(const void* X, int x_dtype, int64_t ldx, const float* inv_
                                   a_scales, kK1Int4Tiled, D, stream),
                         "svdq_linear_tiled K1 launch"))
     return s;
-  return check_hip(launch_k2t(a_ops, a_scales, w_codes_t, w_scales_t, D, L2t, R, bias, Y,
+  return check_hip(launch_k2t(a_ops, a_scales, w_codes_t, w_scales_t,
+                              reinterpret_cast<const uint16_t*>(D), L2t, R, bias, Y,
                               y_dtype == SVDQ_F16, M, N, K, ldy, activation == SVDQ_ACT_GELU_TANH,
                               stream),
                    "svdq_linear_tiled K2 launch");

@@ -40,7 +40,7 @@ hipError_t launch_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uin
 // pre-kernel's tiled instance, the weight codes and scale pairs from
 // svdq_pack_w4a4_tiles.
 hipError_t launch_k2t(const uint8_t* a_ops, const float* a_scales, const uint8_t* w_codes_t,
-                      const float* w_scales_t, const float* D, const uint16_t* L2t, int R,
+                      const float* w_scales_t, const uint16_t* Dt, const uint16_t* L2t, int R,
                       const float* bias, void* Y, bool y_f16, int64_t M, int64_t N, int64_t K,
                       int64_t ldy, bool gelu, hipStream_t stream);
 

@@ -596,6 +596,11 @@ size_t svdq_int4_act_scales_tiled_bytes(int64_t M, int64_t K) {
   return static_cast<size_t>((M + 127) / 128) * static_cast<size_t>(K / SVDQ_GROUP) * 512;
 }
 
+size_t svdq_int4_d_tiled_bytes(int64_t M, int32_t R) {
+  if (M < 1 || R < 1) return 0;
+  return static_cast<size_t>((M + 15) / 16) * static_cast<size_t>((R + 31) / 32) * 1024;
+}
+
 size_t svdq_int4_w_codes_tiled_bytes(int64_t N, int64_t K) {
   if (N < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) return 0;
   return static_cast<size_t>((N + 31) / 32) * static_cast<size_t>(K / SVDQ_GROUP) * 1024;

@@ -450,9 +450,11 @@ __global__ __launch_bounds__(64 * WV, WV >= 16 ? 1 : 2) void k1_quant_down_kerne
             *reinterpret_cast<v4i*>(a_codes + (b * G + g) * 1024 + 16 * lane) =
                 widen_codes(make_uint2(packed[0], packed[1]));
             if (c4 == 0) {
-              // the scale in fp32, row block b % 8 of its 128-row band at 8 qr + b % 8
-              static_cast<float*>(a_meta)[((b / 8) * G + g) * 128 + qr * 8 + b % 8] =
-                  h2f(static_cast<uint16_t>(meta));
+              // the scale in fp32: row block i = b % 8 of its 128-row band, row
+              // qr, at 64 (i/4) + 4 qr + i%4
+              const int64_t ib = b % 8;
+              static_cast<float*>(a_meta)[((b / 8) * G + g) * 128 + 64 * (ib / 4) + 4 * qr +
+                                          ib % 4] = h2f(static_cast<uint16_t>(meta));
             }
           }
         } else if (i < n_mine && rvalid[rt]) {
@@ -501,7 +503,19 @@ __global__ __launch_bounds__(64 * WV, WV >= 16 ? 1 : 2) void k1_quant_down_kerne
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) s += dpart[w][r_][c_];
-      if (row0 + r_ < M) D[(row0 + r_) * R + c_] = s;
+      if (row0 + r_ < M) {
+        if constexpr (TILED) {
+          // fp16(D) in the up-projection's operand order: per 16-row block
+          // and 32-rank chunk one 1 KB block, lane 16q + r holding row r,
+          // ranks 8q .. 8q+7 of the chunk (svdq.h, tiled INT4 layouts)
+          const int64_t m = row0 + r_;
+          const int64_t blk = (m / 16) * ((R + 31) / 32) + c_ / 32;
+          reinterpret_cast<uint16_t*>(D)[(blk * 64 + 16 * ((c_ % 32) / 8) + m % 16) * 8 + c_ % 8] =
+              f2h(s);
+        } else {
+          D[(row0 + r_) * R + c_] = s;
+        }
+      }
     }
   }
 }

@@ -114,13 +114,82 @@ __device__ __forceinline__ void rescale(v4f& acc, const v4i& p, const TScales<RB
   }
 }
 
+// The low-rank up-projection acc += fp16(D) . L2 for a wave whose region of Y
+// starts at row m0 (16*RB rows) and column nw (16*CB columns), from the
+// pre-kernel's fp16 D in operand order (D_t: per 16-row block and 32-rank
+// chunk one 1 KB block; lane 16q + r holds row r, ranks 8q .. 8q+7), so an
+// operand is one 16-byte load with nothing to convert. Work goes in units of
+// 4 row blocks of one chunk; the next unit's loads are issued before this
+// unit's matrix instructions. Every load is from a clamped in-bounds address;
+// operands past R or M are zeroed after they arrive (selected, never
+// multiplied in).
+template <int RB, int CB>
+__device__ __forceinline__ void lowrank_up_tiled(v4f (&acc)[RB][CB],
+                                                 const uint16_t* __restrict__ Dt,
+                                                 const uint16_t* __restrict__ L2t, int R,
+                                                 int64_t M, int64_t N, int64_t m0, int64_t nw) {
+  constexpr int NH = RB / 4;                        // units of 4 row blocks per chunk
+  if (R <= 0) return;
+  const int lane = threadIdx.x & 63;
+  const int rl = lane & 15, q = lane >> 4;
+  const int RC = (R + 31) / 32;
+  const int NU = RC * NH;
+  const int64_t Mb = (M + 15) / 16;
+  const v8h zero = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+  auto load = [&](int u, v8h (&A)[4], v8h (&B)[CB]) {
+    const int c = u / NH, h = u - c * NH;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int64_t b = m0 / 16 + 4 * h + i;
+      b = b < Mb ? b : Mb - 1;
+      A[i] = *reinterpret_cast<const v8h*>(Dt + ((b * RC + c) * 64 + lane) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int64_t n = nw + 16 * j + rl;
+      const int kk = 32 * c + 8 * q;
+      const bool ok = kk < R && n < N;
+      B[j] = *reinterpret_cast<const v8h*>(L2t + (ok ? n * R + kk : 0));
+    }
+  };
+  auto step = [&](int u, v8h (&A)[4], v8h (&B)[CB]) {
+    const int c = u / NH, h = u - c * NH;
+    const bool kval = 32 * c + 8 * q < R;
+#pragma unroll
+    for (int j = 0; j < CB; ++j) B[j] = (kval && nw + 16 * j + rl < N) ? B[j] : zero;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v8h a = (kval && m0 + 16 * (4 * h + i) + rl < M) ? A[i] : zero;
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) {
+        if (hh == h) {
+#pragma unroll
+          for (int j = 0; j < CB; ++j)
+            acc[4 * hh + i][j] = mfma_f16_16x16x32(B[j], a, acc[4 * hh + i][j]);
+        }
+      }
+    }
+  };
+  v8h A0[4], B0[CB], A1[4], B1[CB];
+  load(0, A0, B0);
+  // NU is the same for every lane, so loads past the last unit are skipped
+  // by the whole wave
+  for (int u = 0; u < NU; u += 2) {
+    if (u + 1 < NU) load(u + 1, A1, B1);
+    step(u, A0, B0);
+    if (u + 1 >= NU) break;
+    if (u + 2 < NU) load(u + 2, A0, B0);
+    step(u + 1, A1, B1);
+  }
+}
+
 // One tile of Y: rows m0 .. m0 + 16*RB - 1, columns n0 .. n0 + 64*CB - 1.
 template <int RB, int CB, bool Y_F16, bool GELU>
 __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __restrict__ a_ops,
                                        const float* __restrict__ a_scales,
                                        const uint8_t* __restrict__ w_codes,
                                        const float* __restrict__ w_scales,
-                                       const float* __restrict__ D,
+                                       const uint16_t* __restrict__ Dt,
                                        const uint16_t* __restrict__ L2t, int R,
                                        const float* __restrict__ bias, void* __restrict__ Y,
                                        int64_t M, int64_t N, int64_t K, int64_t ldy, int64_t m0,
@@ -184,7 +253,7 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
   for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int j = 0; j < CB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  lowrank_up_at<16 * RB, 16 * CB>(acc, D, L2t, R, M, N, m0, nw);
+  lowrank_up_tiled<RB, CB>(acc, Dt, L2t, R, M, N, m0, nw);
 
   // Iteration g computes group g from stage g % KSTAGES. Its barrier follows
   // this wave's wait for its own copies of group g, so after it every copy of
@@ -207,10 +276,11 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
     v4i A[2];
     A[0] = read_a(s, 0);
     TScales<RB, CB> sc;
-    // activation scales: row block i of the band, row r, at 8r + i
+    // activation scales: row block i of the band, row r, at 64 (i/4) + 4r + i%4
+    // (the 16 rows' float4 of one instruction are 256 contiguous bytes)
 #pragma unroll
     for (int h = 0; h < RB / 4; ++h) {
-      const float4 v = *reinterpret_cast<const float4*>(&s.sx[rl * 8 + rb0 + 4 * h]);
+      const float4 v = *reinterpret_cast<const float4*>(&s.sx[64 * (rb0 / 4 + h) + 4 * rl]);
       sc.sx[4 * h] = v.x;
       sc.sx[4 * h + 1] = v.y;
       sc.sx[4 * h + 2] = v.z;
@@ -312,7 +382,7 @@ template <bool Y_F16, bool GELU>
 __global__ __launch_bounds__(NT, 3) void k2t_w4a4_kernel(
     const uint8_t* __restrict__ a_ops, const float* __restrict__ a_scales,
     const uint8_t* __restrict__ w_codes, const float* __restrict__ w_scales,
-    const float* __restrict__ D, const uint16_t* __restrict__ L2t, int R,
+    const uint16_t* __restrict__ Dt, const uint16_t* __restrict__ L2t, int R,
     const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N, int64_t K,
     int64_t ldy, int tiles_m, int tiles_n, int n_full, int split) {
   __shared__ TStage st[KSTAGES];
@@ -320,7 +390,7 @@ __global__ __launch_bounds__(NT, 3) void k2t_w4a4_kernel(
   int tm, tn;
   if (b < n_full) {
     banded_tile(xcd_contiguous(b, n_full), tiles_m, tiles_n, tm, tn);
-    tile_t<8, 2, Y_F16, GELU>(st, a_ops, a_scales, w_codes, w_scales, D, L2t, R, bias, Y, M, N, K,
+    tile_t<8, 2, Y_F16, GELU>(st, a_ops, a_scales, w_codes, w_scales, Dt, L2t, R, bias, Y, M, N, K,
                               ldy, static_cast<int64_t>(tm) * 128, static_cast<int64_t>(tn) * 128);
     return;
   }
@@ -331,10 +401,10 @@ __global__ __launch_bounds__(NT, 3) void k2t_w4a4_kernel(
   const int64_t n0 = static_cast<int64_t>(tn) * 128 + (split == 4 ? 64 * (part & 1) : 0);
   if (m0 >= M || n0 >= N) return;
   if (split == 2)
-    tile_t<4, 2, Y_F16, GELU>(st, a_ops, a_scales, w_codes, w_scales, D, L2t, R, bias, Y, M, N, K,
+    tile_t<4, 2, Y_F16, GELU>(st, a_ops, a_scales, w_codes, w_scales, Dt, L2t, R, bias, Y, M, N, K,
                               ldy, m0, n0);
   else
-    tile_t<4, 1, Y_F16, GELU>(st, a_ops, a_scales, w_codes, w_scales, D, L2t, R, bias, Y, M, N, K,
+    tile_t<4, 1, Y_F16, GELU>(st, a_ops, a_scales, w_codes, w_scales, Dt, L2t, R, bias, Y, M, N, K,
                               ldy, m0, n0);
 }
 
@@ -361,7 +431,7 @@ int k2t_slots() {
 }  // namespace
 
 hipError_t launch_k2t(const uint8_t* a_ops, const float* a_scales, const uint8_t* w_codes_t,
-                      const float* w_scales_t, const float* D, const uint16_t* L2t, int R,
+                      const float* w_scales_t, const uint16_t* Dt, const uint16_t* L2t, int R,
                       const float* bias, void* Y, bool y_f16, int64_t M, int64_t N, int64_t K,
                       int64_t ldy, bool gelu, hipStream_t stream) {
   const int tiles_m = static_cast<int>((M + 127) / 128);
@@ -376,7 +446,7 @@ hipError_t launch_k2t(const uint8_t* a_ops, const float* a_scales, const uint8_t
   const int n_full = T - n_split;
   const dim3 grid(static_cast<unsigned>(n_full + split * n_split)), block(NT);
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, block, 0, stream, a_ops, a_scales, w_codes_t, w_scales_t, D,
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, a_ops, a_scales, w_codes_t, w_scales_t, Dt,
                        L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n, n_full, split);
   };
   if (y_f16)

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 8
+#define SVDQ_ABI_VERSION 9
 
 /* status codes */
 enum {
@@ -313,7 +313,7 @@ int svdq_linear_noalloc(const void* X, int x_dtype, int64_t ldx, const float* in
  *             Rows past M inside the last block hold row M-1's values.
  *   a_scales_t activation scales, ceil(M/128) x G blocks of 128 fp32; block
  *             (t, g) holds s = fp32(the fp16 group scale) of row 128t + 16i + r
- *             (i < 8, r < 16) at index 8r + i.
+ *             (i < 8, r < 16) at index 64*(i/4) + 4r + i%4.
  *   w_codes_t weight codes, 4-bit as in the canonical layout, ceil(N/32) x G
  *             blocks of 1024 bytes; block (s, g) lane l = 16q + r holds bytes
  *             32g + 8q .. +7 of the canonical rows of columns 32s + r (bytes
@@ -323,6 +323,11 @@ int svdq_linear_noalloc(const void* X, int x_dtype, int64_t ldx, const float* in
  *             (s/256, -12582912 s/256), s = fp32(the fp16 scale of column
  *             32s + 16j + 4q + e in group g), both exact; 0 past N. The pair
  *             turns the matrix instruction's biased result into P s exactly.
+ *   D_t       the down-projection D in fp16 (rounded once from its fp32
+ *             sum, as the up-projection of K2 rounds it), ceil(M/16) x
+ *             ceil(R/32) blocks of 512 fp16; element 8l + j of block (b, c),
+ *             lane l = 16q + r, is fp16(D[16b + r][32c + 8q + j]). Entries past
+ *             M or past R are not written and not read.
  * The weight layouts are a permutation of the canonical w_codes / w_scales
  * (svdq_pack_w4a4_tiles), made once offline; the weights stay at 4 bits.
  */
@@ -330,6 +335,7 @@ int svdq_linear_noalloc(const void* X, int x_dtype, int64_t ldx, const float* in
 /* Bytes of the tiled INT4 layouts (0 for invalid sizes). */
 size_t svdq_int4_act_tiled_bytes(int64_t M, int64_t K);
 size_t svdq_int4_act_scales_tiled_bytes(int64_t M, int64_t K);
+size_t svdq_int4_d_tiled_bytes(int64_t M, int32_t R);
 size_t svdq_int4_w_codes_tiled_bytes(int64_t N, int64_t K);
 size_t svdq_int4_w_scales_tiled_bytes(int64_t N, int64_t K);
 
@@ -340,13 +346,14 @@ int svdq_pack_w4a4_tiles(const uint8_t* w_codes, const uint16_t* w_scales, int64
                          uint8_t* w_codes_t, float* w_scales_t);
 
 /* Device: K1 (svdq_quantize_act_lowrank_down: the same smoothing, quantizer
- * and D) writing the codes and scales as a_ops_t and a_scales_t
- * (svdq_int4_act_tiled_bytes(M, K) and svdq_int4_act_scales_tiled_bytes(M, K)
- * bytes, 16-byte aligned). */
+ * and D) writing the codes, scales and D as a_ops_t, a_scales_t and D_t
+ * (svdq_int4_act_tiled_bytes(M, K), svdq_int4_act_scales_tiled_bytes(M, K) and
+ * svdq_int4_d_tiled_bytes(M, R) bytes, 16-byte aligned; D_t may be NULL when
+ * R == 0). */
 int svdq_quantize_act_lowrank_down_tiled(const void* X, int x_dtype, int64_t M, int64_t K,
                                          int64_t ldx, const float* inv_smooth,
                                          const uint16_t* L1p, int32_t R, uint8_t* a_ops_t,
-                                         float* a_scales_t, float* D, hipStream_t stream);
+                                         float* a_scales_t, uint16_t* D_t, hipStream_t stream);
 
 /* Device: K2 (svdq_w4a4_gemm_lowrank_up: the same exact int32 group partials,
  * fp32 rescale, low-rank up-projection, bias and activation) on the tiled
@@ -354,12 +361,12 @@ int svdq_quantize_act_lowrank_down_tiled(const void* X, int x_dtype, int64_t M, 
  * first), within the same rounding bound. */
 int svdq_w4a4_gemm_lowrank_up_tiled(const uint8_t* a_ops_t, const float* a_scales_t,
                                     const uint8_t* w_codes_t, const float* w_scales_t,
-                                    const float* D, const uint16_t* L2t, int32_t R,
+                                    const uint16_t* D_t, const uint16_t* L2t, int32_t R,
                                     const float* bias, void* Y, int y_dtype, int64_t M, int64_t N,
                                     int64_t K, int64_t ldy, int32_t activation,
                                     hipStream_t stream);
 
-/* Bytes of workspace svdq_linear_tiled needs: a_ops_t, a_scales_t and D, each
+/* Bytes of workspace svdq_linear_tiled needs: a_ops_t, a_scales_t and D_t, each
  * 256-byte aligned inside the workspace. */
 size_t svdq_linear_tiled_workspace_bytes(int64_t M, int64_t K, int32_t R);
 

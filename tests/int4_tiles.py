@@ -49,7 +49,7 @@ def act_scale_index(M: int, K: int):
     G = K // 64
     rows = np.arange(((M + 127) // 128) * 128)
     t, i, r = rows // 128, (rows % 128) // 16, rows % 16
-    return t[:, None] * G * 128 + np.arange(G)[None, :] * 128 + (8 * r + i)[:, None]
+    return t[:, None] * G * 128 + np.arange(G)[None, :] * 128 + (64 * (i // 4) + 4 * r + i % 4)[:, None]
 
 
 def tile_act_scales(scales: np.ndarray, M: int, K: int) -> np.ndarray:
@@ -79,3 +79,20 @@ def tile_w(w_codes: np.ndarray, w_scales: np.ndarray, N: int, K: int):
     st = sc.reshape(ns, 2, 4, 4, G).transpose(0, 4, 2, 1, 3)      # s, g, q, j, e
     pairs = np.stack([st / 256.0, st * (-12582912.0 / 256.0)], axis=-1).astype(np.float32)
     return np.ascontiguousarray(ct).reshape(-1), np.ascontiguousarray(pairs).reshape(-1)
+
+
+def untile_d(dt: np.ndarray, M: int, R: int) -> np.ndarray:
+    """D_t (fp16 bits, the tiled low-rank down-projection) -> M x R fp16."""
+    nb, rc = (M + 15) // 16, (R + 31) // 32
+    v = np.asarray(dt).view(np.uint16)[:nb * rc * 512].reshape(nb, rc, 4, 16, 8)  # b, c, q, r, j
+    v = v.transpose(0, 3, 1, 2, 4).reshape(nb * 16, rc * 32)                      # [16b + r][32c + 8q + j]
+    return v[:M, :R].view(np.float16)
+
+
+def tile_d(d16: np.ndarray, M: int, R: int) -> np.ndarray:
+    """M x R fp16 -> D_t fp16 bits (entries past M or R zero)."""
+    nb, rc = (M + 15) // 16, (R + 31) // 32
+    full = np.zeros((nb * 16, rc * 32), dtype=np.float16)
+    full[:M, :R] = d16
+    v = full.view(np.uint16).reshape(nb, 16, rc, 4, 8).transpose(0, 2, 3, 1, 4)   # b, c, q, r, j
+    return np.ascontiguousarray(v).reshape(-1)

@@ -49,7 +49,22 @@ def test_activation_tile_helpers_round_trip(M, K):
     assert np.all(p[idx[M:]] == 0)
     # the index formula is a bijection onto the blocks
     assert np.array_equal(np.sort(idx.reshape(-1)), np.arange(p.size))
-    # row 128t + 16i + r, group g at (t G + g) 128 + 8 r + i
-    r_, g_ = min(M - 1, 137), K // 64 - 1
-    t, i, r = r_ // 128, (r_ % 128) // 16, r_ % 16
-    assert idx[r_, g_] == (t * (K // 64) + g_) * 128 + 8 * r + i
+    # row 128t + 16i + r, group g at (t G + g) 128 + 64 (i/4) + 4 r + i%4
+    for r_ in {min(M - 1, 137), min(M - 1, 77), M - 1}:
+        g_ = K // 64 - 1
+        t, i, r = r_ // 128, (r_ % 128) // 16, r_ % 16
+        assert idx[r_, g_] == (t * (K // 64) + g_) * 128 + 64 * (i // 4) + 4 * r + i % 4
+
+
+@pytest.mark.parametrize("M,R", [(1, 16), (17, 32), (130, 48), (300, 96)])
+def test_d_tile_helpers(M, R):
+    """D_t: element 8l + j of block (b, c), l = 16q + r, is D[16b + r][32c + 8q + j]."""
+    rng = np.random.default_rng(M * 7 + R)
+    d = rng.standard_normal((M, R)).astype(np.float16)
+    t = T.tile_d(d, M, R)
+    assert t.size * 2 == sq.int4_d_tiled_bytes(M, R)
+    assert np.array_equal(T.untile_d(t, M, R).view(np.uint16), d.view(np.uint16))
+    rc = (R + 31) // 32
+    for m, k in {(0, 0), (M - 1, R - 1), (min(M - 1, 21), min(R - 1, 13))}:
+        b, r, c, q, j = m // 16, m % 16, k // 32, (k % 32) // 8, k % 8
+        assert t[((b * rc + c) * 64 + 16 * q + r) * 8 + j] == d.view(np.uint16)[m, k]
