@@ -550,22 +550,28 @@ hipError_t launch_k1_rt(const void* X, int64_t M, int64_t K, int64_t ldx,
 // registers cost occupancy). A row tile takes about the same time whatever
 // else runs, so with 16-row workgroups some compute units would run two of
 // them back to back; a 32-row workgroup costs less than that, and its waves
-// share one set of smoothing factors and L1 operands (measured: 4608 rows
-// +4.5%, the 12288-channel down-projection +12%; at 4096 rows, one 16-row tile
-// per compute unit, it would be 37% slower).
+// share one set of smoothing factors and L1 operands (measured on the
+// 12288-channel down-projection at 4608 rows: 41.0 us against 46.1 us; at
+// 4096 rows, one 16-row tile per compute unit, it would be 37% slower).
 template <typename XT, int NCB>
 hipError_t launch_k1_t(const void* X, int64_t M, int64_t K, int64_t ldx,
                        const float* inv_smooth, const uint16_t* L1p, int R,
                        uint8_t* a_codes, void* a_meta, int fmt, float* D, hipStream_t stream,
                        const ConvGeom* conv) {
   if constexpr (NCB <= 4) {
-    if (2 * ((M + 15) / 16) > static_cast<int64_t>(resident_slots())) {
+    const int64_t tiles = (M + 15) / 16, slots = static_cast<int64_t>(resident_slots());
+    // short rows (fewer than 12 groups of 64 channels per wave) with every
+    // 16-row tile resident at once: the 32-row tile's shared operands do not
+    // pay for its longer reduction (measured on the DiT QKV pre-kernel, 4608
+    // x 3072: 14.0 us against 15.6 us)
+    const bool short_rows = K / 64 < 12 * k1_waves<NCB>() && tiles <= slots;
+    if (2 * tiles > slots && !short_rows) {
       // at most one 32-row workgroup per compute unit: each wave keeps three
       // groups in flight (the registers of a second resident workgroup are
       // not needed); measured 4% faster on the DiT QKV pre-kernel and 11% on
       // the 12288-channel down-projection than one group in flight (16 waves
       // with two groups each were slower than either)
-      if ((M + 31) / 32 <= static_cast<int64_t>(resident_slots()) / 2)
+      if ((M + 31) / 32 <= slots / 2)
         return launch_k1_rt<XT, NCB, 2, 3>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt,
                                            D, stream, conv);
       return launch_k1_rt<XT, NCB, 2, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D,
