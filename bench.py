@@ -76,7 +76,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overhead", action="store_true", help="skip the rank-0 comparison run")
     ap.add_argument("--no-clock", action="store_true",
-                    help="no shader-clock probe beside the timed steps")
+                    help="no shader-clock probe (a replica of the timed steps)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain fp32 copy kernel of known size (for PMC scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -106,13 +106,14 @@ def parse():
 
 
 class ClockProbe:
-    """The shader clock during the timed steps: svdq_clock_probe (one wave on a
-    side stream, sampling the shader-clock cycle counter against the constant
-    wall counter every INTERVAL_US) runs from just before the first timed
-    launch until svdq_clock_mark, queued behind the last timed launch, sets its
-    stop flag. The mark is a one-wave kernel inside the timed window, and the
-    final synchronize waits for the probe to see the flag (at most one
-    interval)."""
+    """The shader clock over a replica of the timed steps: svdq_clock_probe
+    (one wave on a side stream, sampling the shader-clock cycle counter
+    against the constant wall counter every INTERVAL_US) runs from just before
+    the replica's first launch until svdq_clock_mark, queued behind its last
+    launch, sets the stop flag; the final synchronize waits for the probe to
+    see the flag (at most one interval). The replica runs right after the
+    timed pass, with the same launches: run beside the timed pass itself, the
+    probe wave slowed its steps (c1: 240 against 222 us per step on one box)."""
     INTERVAL_US = 10.0
 
     def __init__(self, torch, sq):
@@ -155,12 +156,14 @@ class ClockProbe:
         dc, dw = np.diff(c[idx]), np.diff(w[idx])
         per = dc[dw > 0] / dw[dw > 0] * wall_mhz
         return {"sclk_mhz": round(float(mean), 1),
+                "ms_per_step_replica": (round(self.step_s * 1e3, 4)
+                                        if getattr(self, "step_s", None) else None),
                 "sclk_mhz_min_1ms": round(float(per.min()), 1) if per.size else None,
                 "sclk_mhz_max_1ms": round(float(per.max()), 1) if per.size else None,
                 "peak_mhz": round(self.peak_khz / 1000.0, 1),
                 "window_ms": round((w[-1] - w[0]) / self.wall_khz, 3), "samples": n,
                 "how": "shader-clock counter against the constant wall counter, one wave on a "
-                       "side stream during the timed steps"}
+                       "side stream during a replica of the timed steps run right after them"}
 
 
 def settle(torch, runner, ms):
@@ -184,29 +187,35 @@ def settle(torch, runner, ms):
 
 
 def time_steps(torch, runner, steps, warmup, probe=None):
-    """Two passes of `steps` steps after `warmup` untimed ones. The first,
+    """Passes of `steps` steps after `warmup` untimed ones. The first,
     bracketed by synchronizations, is the step time: plain launches and
-    nothing else on the stream (plus the clock probe's one-wave mark). The
-    second records HIP events around each launch on the launch stream for the
-    per-kernel durations; an event record costs the stream a few microseconds,
-    so that pass is not the step time. Returns (step seconds, launch names,
-    per-launch seconds as a steps x launches array)."""
+    nothing else on the GPU. With a clock probe, a replica of it follows with
+    the probe beside it (ClockProbe). The last records HIP events around each
+    launch on the launch stream for the per-kernel durations; an event record
+    costs the stream a few microseconds, so that pass is not the step time.
+    Returns (step seconds, launch names, per-launch seconds as a steps x
+    launches array)."""
     for i in range(warmup):
         for _, f in runner.launches(i):
             f()
-    if probe is not None:
-        probe.arm()
     torch.cuda.synchronize()
-    if probe is not None:
-        probe.launch()
     t0 = time.perf_counter()
     for i in range(steps):
         for _, f in runner.launches(i):
             f()
-    if probe is not None:
-        probe.end()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if probe is not None:
+        probe.arm()
+        torch.cuda.synchronize()
+        probe.launch()
+        r0 = time.perf_counter()
+        for i in range(steps):
+            for _, f in runner.launches(i):
+                f()
+        probe.end()
+        torch.cuda.synchronize()
+        probe.step_s = (time.perf_counter() - r0) / steps
     names = [n for n, _ in runner.launches(0)]
     evs = []
     for i in range(steps):

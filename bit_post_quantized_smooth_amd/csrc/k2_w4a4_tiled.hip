@@ -60,10 +60,9 @@ constexpr int NT = 256;             // threads per workgroup
 constexpr int kBlk = 1024;          // one operand block: 64 lanes x 16 bytes
 constexpr int kSxBlk = 128;         // activation scales of one 128-row band and group (floats)
 constexpr int kWpBlk = 64;          // weight scale pairs of one 32-column strip and group (floats)
-// LDS ring depth. Three stages (41.5 KB) let three workgroups share a
-// compute unit; with four (54.3 KB at the time) only two were resident,
-// measured, though three times 54.3 KB is below the 160 KB of LDS (the
-// allocation granularity).
+// LDS ring depth. Three stages (41,472 bytes) let three workgroups share a
+// compute unit; four (55,296 bytes) leave room for two (three would need
+// more than the 163,840 bytes of a compute unit's LDS).
 constexpr int KSTAGES = 3;
 constexpr int KAHEAD = KSTAGES - 1; // groups copied ahead of the one computed
 
