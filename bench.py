@@ -53,6 +53,8 @@ K2_SOURCES = {"int4": [_CSRC + "k2_w4a4_gemm.hip", _CSRC + "k2_common.hpp",
                         _CSRC + "device_common.hpp"]}
 TIMING_NOTE = ("HIP events around each launch in a second pass of the same steps, on the "
                "launch stream, less the gap of an empty event pair")
+GRAPH_TIMING_NOTE = ("HIP events around replays of a graph of one launch over the buffer sets, "
+                     "less the gap of an empty event pair, per launch")
 
 
 def k2_source_hash(fmt: str = "int4") -> str:
@@ -73,6 +75,9 @@ def parse():
                     help="layer index, or 'all': the whole workload (config 2: the MLP pair, "
                          "3: the five UNet linears back to back, 4: the 19-layer chain)")
     ap.add_argument("--sets", type=int, default=4, help="rotating buffer sets (cold MALL)")
+    ap.add_argument("--graph", action="store_true",
+                    help="run the steps as replays of a HIP graph of --sets steps (one host "
+                         "call per graph instead of one per kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overhead", action="store_true", help="skip the rank-0 comparison run")
     ap.add_argument("--no-clock", action="store_true",
@@ -186,19 +191,70 @@ def settle(torch, runner, ms):
     return (time.perf_counter() - t0) * 1e3
 
 
-def time_steps(torch, runner, steps, warmup, probe=None):
+def time_steps(torch, runner, steps, warmup, probe=None, graph_period=0):
     """Passes of `steps` steps after `warmup` untimed ones. The first,
     bracketed by synchronizations, is the step time: plain launches and
     nothing else on the GPU. With a clock probe, a replica of it follows with
     the probe beside it (ClockProbe). The last records HIP events around each
     launch on the launch stream for the per-kernel durations; an event record
     costs the stream a few microseconds, so that pass is not the step time.
-    Returns (step seconds, launch names, per-launch seconds as a steps x
-    launches array)."""
+    With graph_period = P > 0 the steps run as replays of one HIP graph of P
+    consecutive steps (every buffer set once), captured after the warm-up, so
+    the host issues one call per P steps instead of one per kernel; the
+    per-kernel pass then replays, for each launch of a step, a graph of that
+    launch over the P steps between two events. Returns (step seconds, launch
+    names, per-launch seconds as a rows x launches array)."""
     for i in range(warmup):
         for _, f in runner.launches(i):
             f()
     torch.cuda.synchronize()
+    names = [n for n, _ in runner.launches(0)]
+    if graph_period > 0:
+        P = graph_period
+        reps = max(1, steps // P)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(P):
+                for _, f in runner.launches(i):
+                    f()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        if probe is not None:
+            probe.arm()
+            torch.cuda.synchronize()
+            probe.launch()
+            r0 = time.perf_counter()
+            for _ in range(reps):
+                g.replay()
+            probe.end()
+            torch.cuda.synchronize()
+            probe.step_s = (time.perf_counter() - r0) / (reps * P)
+        gap = event_gap(torch)
+        per = np.zeros((reps, len(names)))
+        for j in range(len(names)):
+            gj = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gj):
+                for i in range(P):
+                    runner.launches(i)[j][1]()
+            gj.replay()
+            evs = []
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                gj.replay()
+                b.record()
+                evs.append((a, b))
+            torch.cuda.synchronize()
+            # the callers subtract one event gap per launch: leave it in once
+            per[:, j] = [(a.elapsed_time(b) * 1e-3 - gap) / P + gap for a, b in evs]
+            del gj
+        del g
+        return (t1 - t0) / (reps * P), names, per
     t0 = time.perf_counter()
     for i in range(steps):
         for _, f in runner.launches(i):
@@ -216,7 +272,6 @@ def time_steps(torch, runner, steps, warmup, probe=None):
         probe.end()
         torch.cuda.synchronize()
         probe.step_s = (time.perf_counter() - r0) / steps
-    names = [n for n, _ in runner.launches(0)]
     evs = []
     for i in range(steps):
         ls = runner.launches(i)
@@ -460,7 +515,8 @@ def single_layer_main(args, torch, sq, wl, probe):
     tiled = args.path == "tiled" and fmt == "int4"
     sets = Sets(torch, X, prep, bias, args.sets, L.y_dtype, tiled)
     settled = settle(torch, sets, args.settle_ms)
-    t_step, _, per = time_steps(torch, sets, args.steps, args.warmup, probe)
+    t_step, _, per = time_steps(torch, sets, args.steps, args.warmup, probe,
+                                 args.sets if args.graph else 0)
     clock = probe.result() if probe is not None else None
     ops = 2.0 * M * N * K
     value = ops / t_step / 1e12
@@ -498,7 +554,8 @@ def single_layer_main(args, torch, sq, wl, probe):
         _, _, _, _, prep0 = prepare_layer(sq, wl, args.config, li, fmt, rank=0)
         sets0 = Sets(torch, X, prep0, bias, args.sets, L.y_dtype, tiled)
         settle(torch, sets0, args.settle_ms)     # the clock fell while the rank-0 layer was made
-        t0_step, _, per0 = time_steps(torch, sets0, args.steps, args.warmup)
+        t0_step, _, per0 = time_steps(torch, sets0, args.steps, args.warmup, None,
+                                       args.sets if args.graph else 0)
         k2_0 = float(np.median(per0[:, 1])) - gap
         overhead = dict(step_ms_rank0=t0_step * 1e3, k2_ms_rank0=k2_0 * 1e3,
                         frac=(t_step - t0_step) / k2_0)
@@ -524,7 +581,8 @@ def single_layer_main(args, torch, sq, wl, probe):
         "config": {"workload": f"{cfg.name} layer {li}: X {L.x_dtype} {M}x{K}, "
                                f"W {K}x{N}, rank {R}, {F['text']}, Y {L.y_dtype}",
                    "M": M, "K": K, "N": N, "rank": R, "format": fmt,
-                   "path": "tiled" if tiled else "canonical", "buffer_sets": args.sets},
+                   "path": "tiled" if tiled else "canonical", "buffer_sets": args.sets,
+                   "launch": "hip graph" if args.graph else "eager"},
         F["pct"]: round(100.0 * value / F["peak"], 2),
         "roofline": {"bound": "mfma", "kernel": "k2t_w4a4_kernel" if tiled else F["kname"],
                      "achieved": round(ops / k2_avg / 1e12, 2), "peak": F["peak"],
@@ -532,7 +590,8 @@ def single_layer_main(args, torch, sq, wl, probe):
                      "traffic": traffic, "algorithmic_bytes": b2, "layout_bytes": b2_layout,
                      "avg_ms": round(k2_avg * 1e3, 4), "median_ms": round(k2_med * 1e3, 4),
                      "frac_median": round(ops / k2_med / 1e12 / F["peak"], 4),
-                     "timing": TIMING_NOTE, "event_gap_us": round(gap * 1e6, 2)},
+                     "timing": GRAPH_TIMING_NOTE if args.graph else TIMING_NOTE,
+                     "event_gap_us": round(gap * 1e6, 2)},
         "k1": {"kernel": "tile_x_kernel" if fmt == "w4a16" else "k1_quant_down_kernel",
                "avg_ms": round(k1_avg * 1e3, 4), "median_ms": round(k1_med * 1e3, 4),
                "layout_bytes": b1_layout,
@@ -597,7 +656,8 @@ def whole_config_main(args, torch, sq, wl, probe):
     tiled = args.path == "tiled" and fmt == "int4"
     runner = Chain(torch, layers, args.sets, chain, tiled)
     settled = settle(torch, runner, args.settle_ms)
-    t_step, names, per = time_steps(torch, runner, args.steps, args.warmup, probe)
+    t_step, names, per = time_steps(torch, runner, args.steps, args.warmup, probe,
+                                     args.sets if args.graph else 0)
     clock = probe.result() if probe is not None else None
     gap = event_gap(torch)
     ops_total = sum(2.0 * L.M * L.N * L.K for L, _, _ in layers)
@@ -629,7 +689,8 @@ def whole_config_main(args, torch, sq, wl, probe):
         runner0 = Chain(torch, [(L, X, prep) for (L, X, W, lam, prep) in p0], args.sets, chain,
                         tiled)
         settle(torch, runner0, args.settle_ms)   # the clock fell while the rank-0 layers were made
-        t0_step, _, per0 = time_steps(torch, runner0, args.steps, args.warmup)
+        t0_step, _, per0 = time_steps(torch, runner0, args.steps, args.warmup, None,
+                                       args.sets if args.graph else 0)
         k2_0 = sum(float(np.median(per0[:, 2 * li + 1])) - gap for li in range(len(p0)))
         overhead = dict(step_ms_rank0=t0_step * 1e3, k2_ms_rank0=k2_0 * 1e3,
                         frac=(t_step - t0_step) / k2_0)
@@ -644,13 +705,15 @@ def whole_config_main(args, torch, sq, wl, probe):
         "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": F["dtype"], "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {desc}; {cfg.note}", "format": fmt,
-                   "layers": len(layers), "buffer_sets": args.sets},
+                   "layers": len(layers), "buffer_sets": args.sets,
+                   "launch": "hip graph" if args.graph else "eager"},
         F["pct"]: round(100.0 * value / F["peak"], 2),
         "roofline": {"bound": "mfma", "kernel": F["kname"] + " (all layers)",
                      "achieved": round(ops_total / k2_total / 1e12, 2), "peak": F["peak"],
                      "unit": F["unit"], "frac": round(ops_total / k2_total / 1e12 / F["peak"], 4),
                      "frac_median": round(ops_total / k2_total_med / 1e12 / F["peak"], 4),
-                     "traffic": None, "timing": TIMING_NOTE,
+                     "traffic": None,
+                     "timing": GRAPH_TIMING_NOTE if args.graph else TIMING_NOTE,
                      "event_gap_us": round(gap * 1e6, 2)},
         "layers": rows,
         "lowrank_overhead": None if overhead is None else {
