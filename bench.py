@@ -329,18 +329,20 @@ def host_cores():
 # algorithmic bytes (per launch)
 
 
-def k1_bytes(M, K, R, xb, meta_per_row, tiled=False):
-    """Read X once; write codes, scales (or exponents) and D; read L1 and 1/lambda.
+def k1_bytes(M, K, R, xb, meta_per_row, tiled=False, db=4):
+    """Read X once; write codes, scales (or exponents) and D (db bytes an entry:
+    fp32, or fp16 on the MXFP4 path); read L1 and 1/lambda.
     tiled: the activation side as the tiled path stores it (one int8 operand byte
     per code, an fp32 scale per row and group, D in fp16)."""
     if tiled:
         return M * K * xb + M * K + 4 * M * (K // 64) + 2 * M * R + 2 * K * R + 4 * K
     act = M * K // 2 + M * meta_per_row
-    return M * K * xb + act + 4 * M * R + 2 * K * R + 4 * K
+    return M * K * xb + act + db * M * R + 2 * K * R + 4 * K
 
 
-def k2_bytes(M, N, K, R, yb, meta_per_row, tiled=False):
-    """Codes and scales of both operands, D, L2, Y (bias not counted: zero in the configs).
+def k2_bytes(M, N, K, R, yb, meta_per_row, tiled=False, db=4):
+    """Codes and scales of both operands, D (db bytes an entry), L2, Y (bias not
+    counted: zero in the configs).
     tiled: as the tiled path stores them (int8 activation operands and fp32 scales,
     the weight scales as 8-byte fp32 pairs, D in fp16)."""
     if tiled:
@@ -348,7 +350,7 @@ def k2_bytes(M, N, K, R, yb, meta_per_row, tiled=False):
         return (M * K + 4 * M * G + N * K // 2 + 8 * N * G + 2 * M * R + 2 * R * N
                 + M * N * yb)
     act = M * K // 2 + M * meta_per_row
-    return act + N * K // 2 + N * meta_per_row + 4 * M * R + 2 * R * N + M * N * yb
+    return act + N * K // 2 + N * meta_per_row + db * M * R + 2 * R * N + M * N * yb
 
 
 # --------------------------------------------------------------------------
@@ -382,7 +384,7 @@ class Sets:
                 L1p=d(prep.L1p) if self.R else None, L2t=d(prep.L2t) if self.R else None,
                 b=None if bias is None else d(bias),
                 D=(torch.empty(max(sq.int4_d_tiled_bytes(M, self.R), 2) // 2, dtype=torch.int16,
-                               device="cuda") if self.tiled else
+                               device="cuda") if self.tiled or self.mx else
                    torch.empty((M, max(self.R, 1)), dtype=torch.float32, device="cuda")),
                 Y=torch.empty((M, self.N), dtype=torch.float16 if y_dtype == "f16" else torch.float32,
                               device="cuda"))
@@ -530,8 +532,9 @@ def single_layer_main(args, torch, sq, wl, probe):
         b1 = M * K * xb + 2 * M * K
         b2 = 2 * M * K + N * K // 2 + N * meta + M * N * yb
     else:
-        b1 = k1_bytes(M, K, R, xb, meta)
-        b2 = k2_bytes(M, N, K, R, yb, meta)
+        db = 2 if fmt == "mxfp4" else 4
+        b1 = k1_bytes(M, K, R, xb, meta, db=db)
+        b2 = k2_bytes(M, N, K, R, yb, meta, db=db)
     # the bytes the tiled path's layouts move (the fractions use the method's
     # algorithmic bytes above, which are fewer)
     b1_layout = k1_bytes(M, K, R, xb, meta, tiled) if tiled else b1
@@ -671,8 +674,9 @@ def whole_config_main(args, torch, sq, wl, probe):
         xb = 2 if L.x_dtype == "f16" else 4
         yb = 2 if L.y_dtype == "f16" else 4
         meta = meta_bytes(K, fmt)
-        b1 = k1_bytes(M, K, R, xb, meta)
-        b2 = k2_bytes(M, N, K, R, yb, meta)
+        db = 2 if fmt == "mxfp4" else 4
+        b1 = k1_bytes(M, K, R, xb, meta, db=db)
+        b2 = k2_bytes(M, N, K, R, yb, meta, db=db)
         ops = 2.0 * M * N * K
         attainable = min(F["peak"], ops / b2 * HBM_PEAK_GBS / 1e3)   # TOPS at 8 TB/s
         rows.append({"layer": li, "M": M, "K": K, "N": N, "rank": R,
@@ -838,7 +842,10 @@ def conv_main(args, torch, sq, wl, probe):
     sets = []
     for _ in range(args.sets):
         s = dict(X=d(X), inv=d(prep.inv_smooth), L1p=d(prep.L1p), L2t=d(prep.L2t), wc=d(wct),
-                 ws=d(wet), b=d(bias), D=torch.empty((M, R), dtype=torch.float32, device="cuda"),
+                 ws=d(wet), b=d(bias),
+                 D=(torch.empty(max(sq.int4_d_tiled_bytes(M, R), 2) // 2, dtype=torch.int16,
+                                device="cuda") if mx else
+                    torch.empty((M, R), dtype=torch.float32, device="cuda")),
                  Y=torch.empty((L.batch, L.OH, L.OW, N), dtype=ydt, device="cuda"))
         if mx:
             s.update(ac=torch.empty(sq.mx_codes_tiled_bytes(M, K), dtype=torch.uint8, device="cuda"),
@@ -871,8 +878,9 @@ def conv_main(args, torch, sq, wl, probe):
     img = L.batch * L.H * L.W * L.C
     meta = meta_bytes(K, args.format)
     # K1: the image once, the patch matrix's codes, scales (or exponents) and D out
-    b1 = img * xb + M * K // 2 + M * meta + 4 * M * R + 2 * K * R + 4 * K
-    b2 = k2_bytes(M, N, K, R, yb, meta)
+    db = 2 if args.format == "mxfp4" else 4
+    b1 = img * xb + M * K // 2 + M * meta + db * M * R + 2 * K * R + 4 * K
+    b2 = k2_bytes(M, N, K, R, yb, meta, db=db)
     F = FORMATS[args.format]
     fmt_txt = F["text"]
     out = {

@@ -313,7 +313,10 @@ def _act_side(M, K, R, a_codes, a_scales, D, mx=False):
         _buf("a_codes", a_codes, _BYTES, min_bytes=M * K // 2)
         _buf("a_scales", a_scales, _HALF, min_bytes=2 * M * G)
     if R:
-        _buf("D", D, _F32, min_bytes=4 * M * R)
+        if mx:
+            _buf("D_t", D, _HALF, min_bytes=int4_d_tiled_bytes(M, R))
+        else:
+            _buf("D", D, _F32, min_bytes=4 * M * R)
 
 
 def _weights(N, K, R, w_codes, w_scales, L2t, mx=False):
@@ -542,7 +545,8 @@ def linear_noalloc(X, inv_smooth, L1p, L2t, R: int, w_codes, w_scales, bias, Y, 
 
 def quantize_act_lowrank_down_mx(X, inv_smooth, L1p, R: int, a_codes_t, a_exps_t, D, stream=None):
     """K1-MX; a_codes_t / a_exps_t: device buffers of mx_codes_tiled_bytes(M, K) and
-    mx_exps_tiled_bytes(M, K) bytes (tiled layouts)."""
+    mx_exps_tiled_bytes(M, K) bytes (tiled layouts); D: D_t, fp16 in the
+    up-projection's operand order (int4_d_tiled_bytes(M, R) bytes)."""
     _mat("X", X, None, None)
     M, K = X.shape
     _down(K, R, inv_smooth, L1p)

@@ -147,7 +147,10 @@ WsLayout ws_layout(int64_t M, int64_t K, int32_t R, bool mx) {
     w.scales = round_up(static_cast<size_t>(M) * (K / 2), 256);
     w.d = w.scales + round_up(static_cast<size_t>(M) * (K / SVDQ_GROUP) * 2, 256);
   }
-  w.total = w.d + round_up(static_cast<size_t>(M) * R * 4, 256);
+  // D: fp32 M x R, or for MXFP4 fp16 in operand order (ceil(M/16) x
+  // ceil(R/32) blocks of 1 KB)
+  w.total = w.d + (mx ? round_up(static_cast<size_t>((M + 15) / 16) * ((R + 31) / 32) * 1024, 256)
+                      : round_up(static_cast<size_t>(M) * R * 4, 256));
   return w;
 }
 
@@ -441,10 +444,11 @@ int svdq_linear_tiled(const void* X, int x_dtype, int64_t ldx, const float* inv_
 
 int svdq_quantize_act_lowrank_down_mx(const void* X, int x_dtype, int64_t M, int64_t K,
                                       int64_t ldx, const float* inv_smooth, const uint16_t* L1p,
-                                      int32_t R, uint8_t* a_codes, uint8_t* a_e8m0, float* D,
-                                      hipStream_t stream) {
+                                      int32_t R, uint8_t* a_codes, uint8_t* a_e8m0,
+                                      uint16_t* D_t, hipStream_t stream) {
   clear_error();
   const char* fn = "svdq_quantize_act_lowrank_down_mx";
+  float* D = reinterpret_cast<float*>(D_t);   // checked for null and alignment only
   if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, SVDQ_GROUP, a_codes, a_e8m0,
                           D, fn))
     return s;
@@ -455,18 +459,18 @@ int svdq_quantize_act_lowrank_down_mx(const void* X, int x_dtype, int64_t M, int
 }
 
 int svdq_mx_gemm_lowrank_up(const uint8_t* a_codes, const uint8_t* a_e8m0,
-                            const uint8_t* w_codes, const uint8_t* w_e8m0, const float* D,
+                            const uint8_t* w_codes, const uint8_t* w_e8m0, const uint16_t* D_t,
                             const uint16_t* L2t, int32_t R, const float* bias, void* Y,
                             int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
                             int32_t activation, hipStream_t stream) {
   clear_error();
   const char* fn = "svdq_mx_gemm_lowrank_up";
-  if (int s = validate_k2(a_codes, a_e8m0, w_codes, w_e8m0, D, L2t, R, bias, Y, y_dtype, M, N, K,
-                          ldy, SVDQ_GROUP, fn))
+  if (int s = validate_k2(a_codes, a_e8m0, w_codes, w_e8m0, reinterpret_cast<const float*>(D_t),
+                          L2t, R, bias, Y, y_dtype, M, N, K, ldy, SVDQ_GROUP, fn))
     return s;
   if (int s = check_activation(activation, fn)) return s;
   if (int s = device_ready()) return s;
-  return check_hip(launch_k2_mx(a_codes, a_e8m0, w_codes, w_e8m0, D, L2t, R, bias, Y,
+  return check_hip(launch_k2_mx(a_codes, a_e8m0, w_codes, w_e8m0, D_t, L2t, R, bias, Y,
                                 y_dtype == SVDQ_F16, M, N, K, ldy,
                                 activation == SVDQ_ACT_GELU_TANH, stream),
                    "svdq_mx_gemm_lowrank_up launch");
@@ -514,7 +518,8 @@ int svdq_linear_mx(const void* X, int x_dtype, int64_t ldx, const float* inv_smo
                                   a_e8m0, true, D, stream),
                         "svdq_linear_mx K1 launch"))
     return s;
-  return check_hip(launch_k2_mx(a_codes, a_e8m0, w_codes, w_e8m0, D, L2t, R, bias, Y,
+  return check_hip(launch_k2_mx(a_codes, a_e8m0, w_codes, w_e8m0,
+                                reinterpret_cast<const uint16_t*>(D), L2t, R, bias, Y,
                                 y_dtype == SVDQ_F16, M, N, K, ldy,
                                 activation == SVDQ_ACT_GELU_TANH, stream),
                    "svdq_linear_mx K2 launch");
@@ -589,9 +594,10 @@ int svdq_quantize_act_lowrank_down_conv_mx(const void* X, int x_dtype, int64_t b
                                            int64_t W, int64_t C, int32_t KH, int32_t KW,
                                            int32_t stride, int32_t pad, const float* inv_smooth,
                                            const uint16_t* L1p, int32_t R, uint8_t* a_codes_t,
-                                           uint8_t* a_exps_t, float* D, hipStream_t stream) {
+                                           uint8_t* a_exps_t, uint16_t* D_t, hipStream_t stream) {
   clear_error();
   const char* fn = "svdq_quantize_act_lowrank_down_conv_mx";
+  float* D = reinterpret_cast<float*>(D_t);   // checked for null and alignment only
   ConvShape cs;
   if (int s = check_conv(batch, H, W, C, KH, KW, stride, pad, cs, fn)) return s;
   if (int s = validate_k1(X, x_dtype, cs.M, cs.K, cs.K, inv_smooth, L1p, R, SVDQ_GROUP, a_codes_t,
@@ -644,7 +650,8 @@ int svdq_conv2d_mx(const void* X, int x_dtype, int64_t batch, int64_t H, int64_t
                                   a_codes, a_exps, true, D, stream, &g),
                         "svdq_conv2d_mx K1 launch"))
     return s;
-  return check_hip(launch_k2_mx(a_codes, a_exps, w_codes_t, w_exps_t, D, L2t, R, bias, Y,
+  return check_hip(launch_k2_mx(a_codes, a_exps, w_codes_t, w_exps_t,
+                                reinterpret_cast<const uint16_t*>(D), L2t, R, bias, Y,
                                 y_dtype == SVDQ_F16, cs.M, N, cs.K, N,
                                 activation == SVDQ_ACT_GELU_TANH, stream),
                    "svdq_conv2d_mx K2 launch");

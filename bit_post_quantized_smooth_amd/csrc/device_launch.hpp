@@ -45,7 +45,7 @@ hipError_t launch_k2t(const uint8_t* a_ops, const float* a_scales, const uint8_t
                       int64_t ldy, bool gelu, hipStream_t stream);
 
 hipError_t launch_k2_mx(const uint8_t* a_codes, const uint8_t* a_e8m0, const uint8_t* w_codes,
-                        const uint8_t* w_e8m0, const float* D, const uint16_t* L2t, int R,
+                        const uint8_t* w_e8m0, const uint16_t* Dt, const uint16_t* L2t, int R,
                         const float* bias, void* Y, bool y_f16, int64_t M, int64_t N, int64_t K,
                         int64_t ldy, bool gelu, hipStream_t stream);
 

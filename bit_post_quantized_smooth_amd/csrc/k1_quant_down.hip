@@ -504,10 +504,11 @@ __global__ __launch_bounds__(64 * WV, WV >= 16 ? 1 : 2) void k1_quant_down_kerne
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) s += dpart[w][r_][c_];
       if (row0 + r_ < M) {
-        if constexpr (TILED) {
+        if constexpr (TILED || MX) {
           // fp16(D) in the up-projection's operand order: per 16-row block
           // and 32-rank chunk one 1 KB block, lane 16q + r holding row r,
-          // ranks 8q .. 8q+7 of the chunk (svdq.h, tiled INT4 layouts)
+          // ranks 8q .. 8q+7 of the chunk (svdq.h, tiled layouts of both
+          // formats)
           const int64_t m = row0 + r_;
           const int64_t blk = (m / 16) * ((R + 31) / 32) + c_ / 32;
           reinterpret_cast<uint16_t*>(D)[(blk * 64 + 16 * ((c_ % 32) / 8) + m % 16) * 8 + c_ % 8] =

@@ -105,6 +105,59 @@ __device__ __forceinline__ void lowrank_up(v4f (&acc)[WTM / 16][WTN / 16],
                           n0 + (wave & 1) * WTN);
 }
 
+// The same up-projection from the pre-kernel's fp16 D in operand order (D_t:
+// per 16-row block and 32-rank chunk one 1 KB block, lane 16q + r holding row
+// r, ranks 8q .. 8q+7; svdq.h, tiled layouts): one 16-byte load per row block
+// and chunk, nothing converted. The same sums as lowrank_up_at, whose operand
+// is the same fp16(D).
+template <int WTM, int WTN>
+__device__ __forceinline__ void lowrank_up_dt_at(v4f (&acc)[WTM / 16][WTN / 16],
+                                                 const uint16_t* __restrict__ Dt,
+                                                 const uint16_t* __restrict__ L2t, int R,
+                                                 int64_t M, int64_t N, int64_t mw, int64_t nw) {
+  constexpr int NBM = WTM / 16, NBN = WTN / 16;
+  const int lane = threadIdx.x & 63;
+  const int rl = lane & 15, q = lane >> 4;
+  const int RC = (R + 31) / 32;
+  const int64_t Mb = (M + 15) / 16;
+  const v8h zero = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+  for (int c = 0; c < RC; ++c) {
+    const int kk = 32 * c + 8 * q;                   // this lane's 8 rank indices
+    const bool kval = kk < R;                        // R % 16 == 0: whole 8-runs are valid or not
+    v8h Bl[NBN], Ar[NBM];
+#pragma unroll
+    for (int j = 0; j < NBN; ++j) {
+      const int64_t n = nw + j * 16 + rl;
+      const bool ok = kval && n < N;
+      Bl[j] = *reinterpret_cast<const v8h*>(L2t + (ok ? n * R + kk : 0));
+    }
+#pragma unroll
+    for (int i = 0; i < NBM; ++i) {
+      int64_t b = mw / 16 + i;
+      b = b < Mb ? b : Mb - 1;
+      Ar[i] = *reinterpret_cast<const v8h*>(Dt + ((b * RC + c) * 64 + lane) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < NBN; ++j) Bl[j] = (kval && nw + j * 16 + rl < N) ? Bl[j] : zero;
+#pragma unroll
+    for (int i = 0; i < NBM; ++i) {
+      const v8h Al = (kval && mw + i * 16 + rl < M) ? Ar[i] : zero;
+#pragma unroll
+      for (int j = 0; j < NBN; ++j) acc[i][j] = mfma_f16_16x16x32(Bl[j], Al, acc[i][j]);
+    }
+  }
+}
+
+template <int WTM, int WTN>
+__device__ __forceinline__ void lowrank_up_dt(v4f (&acc)[WTM / 16][WTN / 16],
+                                              const uint16_t* __restrict__ Dt,
+                                              const uint16_t* __restrict__ L2t, int R, int64_t M,
+                                              int64_t N, int64_t m0, int64_t n0) {
+  const int wave = threadIdx.x >> 6;
+  lowrank_up_dt_at<WTM, WTN>(acc, Dt, L2t, R, M, N, m0 + (wave >> 1) * WTM,
+                             n0 + (wave & 1) * WTN);
+}
+
 // Bias, the optional GELU, one rounding to the output type, and the stores: a
 // lane holds columns 4q .. 4q+3 of row rl in each 16 x 16 block, written as
 // one 8-byte (fp16) or 16-byte (fp32) store when Y's address and row stride

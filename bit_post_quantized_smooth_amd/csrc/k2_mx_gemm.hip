@@ -18,9 +18,10 @@
 // so a lane ends up with 4 consecutive columns of one row of each 16 x 16
 // output block, as in the INT4 kernel, and the same epilogue pieces
 // (k2_common.hpp) finish the tile: the low-rank up-projection seeds the
-// accumulators before the K loop, the bias and the stores follow it (a full
-// quarter of an fp16 Y goes through the then idle operand LDS and out in
-// whole cache lines).
+// accumulators before the K loop (from the pre-kernel's fp16 D in operand
+// order: one 16-byte load per row block and 32 ranks, nothing converted), the
+// bias and the stores follow it (a full quarter of an fp16 Y goes through the
+// then idle operand LDS and out in whole cache lines).
 //
 // Data movement. One instruction takes 16 cycles on a SIMD and consumes 2 KB
 // of operands, so operand delivery, not arithmetic, bounds this kernel. Both
@@ -109,7 +110,7 @@ template <int WTM, int WTN, bool Y_F16, bool GELU>
 __device__ __forceinline__ void mx_tile(
     const uint8_t* __restrict__ a_codes_t, const uint8_t* __restrict__ a_exps_t,
     const uint8_t* __restrict__ w_codes_t, const uint8_t* __restrict__ w_exps_t,
-    const float* __restrict__ D, const uint16_t* __restrict__ L2t, int R,
+    const uint16_t* __restrict__ Dt, const uint16_t* __restrict__ L2t, int R,
     const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N, int64_t K,
     int64_t ldy, int64_t m0, int64_t n0) {
   constexpr int NBM = WTM / 16, NBN = WTN / 16;
@@ -184,7 +185,7 @@ __device__ __forceinline__ void mx_tile(
   for (int i = 0; i < NBM; ++i)
 #pragma unroll
     for (int j = 0; j < NBN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  lowrank_up<WTM, WTN>(acc, D, L2t, R, M, N, m0, n0);
+  lowrank_up_dt<WTM, WTN>(acc, Dt, L2t, R, M, N, m0, n0);
   load(f[1], 1);
   int64_t c0 = 0;
   for (; c0 + NS <= C; c0 += NS) {
@@ -226,7 +227,7 @@ template <bool Y_F16, bool GELU>
 __device__ __forceinline__ void mx_tile_lds(
     MxStage (&st)[3], const uint8_t* __restrict__ a_codes_t, const uint8_t* __restrict__ a_exps_t,
     const uint8_t* __restrict__ w_codes_t, const uint8_t* __restrict__ w_exps_t,
-    const float* __restrict__ D, const uint16_t* __restrict__ L2t, int R,
+    const uint16_t* __restrict__ Dt, const uint16_t* __restrict__ L2t, int R,
     const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N, int64_t K,
     int64_t ldy, int64_t m0, int64_t n0) {
   constexpr int WTM = 128, WTN = 64, NBM = 8, NBN = 4;
@@ -291,7 +292,7 @@ __device__ __forceinline__ void mx_tile_lds(
   for (int i = 0; i < NBM; ++i)
 #pragma unroll
     for (int j = 0; j < NBN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  lowrank_up<WTM, WTN>(acc, D, L2t, R, M, N, m0, n0);
+  lowrank_up_dt<WTM, WTN>(acc, Dt, L2t, R, M, N, m0, n0);
   sync();                            // chunks 0 and 1 in stages 0 and 1
   Frags f[2];
   read(f[0], st[0]);
@@ -335,7 +336,7 @@ template <bool Y_F16, bool GELU>
 __global__ __launch_bounds__(NT, 2) void k2_mx_kernel(
     const uint8_t* __restrict__ a_codes_t, const uint8_t* __restrict__ a_exps_t,
     const uint8_t* __restrict__ w_codes_t, const uint8_t* __restrict__ w_exps_t,
-    const float* __restrict__ D, const uint16_t* __restrict__ L2t, int R,
+    const uint16_t* __restrict__ Dt, const uint16_t* __restrict__ L2t, int R,
     const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N, int64_t K,
     int64_t ldy, int tiles_m, int tiles_n, int n_full) {
   __shared__ MxStage st[3];
@@ -343,7 +344,7 @@ __global__ __launch_bounds__(NT, 2) void k2_mx_kernel(
   int tm, tn;
   if (b < n_full) {
     banded_tile(xcd_contiguous(b, n_full), tiles_m, tiles_n, tm, tn);
-    mx_tile_lds<Y_F16, GELU>(st, a_codes_t, a_exps_t, w_codes_t, w_exps_t, D, L2t,
+    mx_tile_lds<Y_F16, GELU>(st, a_codes_t, a_exps_t, w_codes_t, w_exps_t, Dt, L2t,
                              R, bias, Y, M, N, K, ldy,
                              static_cast<int64_t>(tm) * kFullM,
                              static_cast<int64_t>(tn) * kFullN);
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(NT, 2) void k2_mx_kernel(
     const int quarter = qb & 3;
     banded_tile(n_full + (qb >> 2), tiles_m, tiles_n, tm, tn);
     mx_tile<kFullM / 4, kFullN / 4, Y_F16, GELU>(
-        a_codes_t, a_exps_t, w_codes_t, w_exps_t, D, L2t, R, bias, Y, M, N, K, ldy,
+        a_codes_t, a_exps_t, w_codes_t, w_exps_t, Dt, L2t, R, bias, Y, M, N, K, ldy,
         static_cast<int64_t>(tm) * kFullM + (kFullM / 2) * (quarter >> 1),
         static_cast<int64_t>(tn) * kFullN + (kFullN / 2) * (quarter & 1));
   }
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(NT, 2) void k2_mx_kernel(
 }  // namespace
 
 hipError_t launch_k2_mx(const uint8_t* a_codes_t, const uint8_t* a_exps_t,
-                        const uint8_t* w_codes_t, const uint8_t* w_exps_t, const float* D,
+                        const uint8_t* w_codes_t, const uint8_t* w_exps_t, const uint16_t* Dt,
                         const uint16_t* L2t, int R, const float* bias, void* Y, bool y_f16,
                         int64_t M, int64_t N, int64_t K, int64_t ldy, bool gelu,
                         hipStream_t stream) {
@@ -378,7 +379,7 @@ hipError_t launch_k2_mx(const uint8_t* a_codes_t, const uint8_t* a_exps_t,
   const dim3 grid(static_cast<unsigned>(n_full + 4 * n_quarter_tiles)), block(NT);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, a_codes_t, a_exps_t, w_codes_t, w_exps_t,
-                       D, L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n, n_full);
+                       Dt, L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n, n_full);
   };
   if (y_f16)
     gelu ? go(k2_mx_kernel<true, true>) : go(k2_mx_kernel<true, false>);

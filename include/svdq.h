@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 9
+#define SVDQ_ABI_VERSION 10
 
 /* status codes */
 enum {
@@ -408,7 +408,9 @@ int svdq_linear_tiled(const void* X, int x_dtype, int64_t ldx, const float* inv_
  * K % 128 == 64) hold zero codes and exponent 127 where svdq_pack_mx_tiles
  * writes them; K1-MX writes the entries past K the same way and leaves rows
  * past M unwritten (K2-MX never stores the outputs that depend on them).
- * Smoothing, the low-rank factors and D are as in the INT4 functions.
+ * Smoothing and the low-rank factors are as in the INT4 functions; D travels
+ * from K1-MX to K2-MX as D_t, fp16 in the up-projection's operand order, as on
+ * the tiled INT4 path (svdq_int4_d_tiled_bytes(M, R) bytes, 16-byte aligned).
  * Constraints and alignment as for the device functions above (the tiled
  * arrays 16-byte aligned); K % 64 == 0. */
 
@@ -423,25 +425,28 @@ int svdq_pack_mx_tiles(const uint8_t* codes, const uint8_t* e8m0, int64_t rows, 
                        uint8_t* codes_t, uint8_t* exps_t);
 
 /* K1-MX: as svdq_quantize_act_lowrank_down with the MXFP4 quantizer; a_codes_t
- * and a_exps_t in the tiled layouts (svdq_mx_*_tiled_bytes(M, K) bytes). */
+ * and a_exps_t in the tiled layouts (svdq_mx_*_tiled_bytes(M, K) bytes); D as
+ * D_t (fp16 D in operand order, the layout of the tiled INT4 path; NULL when
+ * R == 0). */
 int svdq_quantize_act_lowrank_down_mx(const void* X, int x_dtype, int64_t M, int64_t K,
                                       int64_t ldx, const float* inv_smooth, const uint16_t* L1p,
-                                      int32_t R, uint8_t* a_codes_t, uint8_t* a_exps_t, float* D,
-                                      hipStream_t stream);
+                                      int32_t R, uint8_t* a_codes_t, uint8_t* a_exps_t,
+                                      uint16_t* D_t, hipStream_t stream);
 
 /* K2-MX: Y[m,n] = sum_k deq(a)[m,k] * deq(w)[n,k] (products and sums in the
  * matrix core's fp32 accumulation, deq = E2M1 value * 2^e of its block)
  *                 + sum_r fp16(D[m,r]) * L2[r,n] + bias[n]
  * then the activation (SVDQ_ACT_*) in fp32, rounded once to y_dtype.
- * All four code and exponent arrays in the tiled layouts. */
+ * All four code and exponent arrays in the tiled layouts; fp16(D) as D_t, as
+ * K1-MX writes it. */
 int svdq_mx_gemm_lowrank_up(const uint8_t* a_codes_t, const uint8_t* a_exps_t,
-                            const uint8_t* w_codes_t, const uint8_t* w_exps_t, const float* D,
+                            const uint8_t* w_codes_t, const uint8_t* w_exps_t, const uint16_t* D_t,
                             const uint16_t* L2t, int32_t R, const float* bias, void* Y,
                             int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
                             int32_t activation, hipStream_t stream);
 
 /* Bytes of workspace svdq_linear_mx needs: the tiled activation codes and
- * exponents and D, each 256-byte aligned inside the workspace (0 for invalid
+ * exponents and D_t, each 256-byte aligned inside the workspace (0 for invalid
  * sizes). */
 size_t svdq_linear_mx_workspace_bytes(int64_t M, int64_t K, int32_t R);
 
@@ -556,13 +561,13 @@ int svdq_conv2d(const void* X, int x_dtype, int64_t batch, int64_t H, int64_t W,
                 void* ws, size_t ws_bytes, int32_t activation, hipStream_t stream);
 
 /* Device: K1-MX on the patch matrix: the tiled E2M1 codes and E8M0 exponents
- * and D, as svdq_quantize_act_lowrank_down_mx would give for the patch matrix
- * in memory (bit-exact). */
+ * and D_t, as svdq_quantize_act_lowrank_down_mx would give for the patch
+ * matrix in memory (bit-exact). */
 int svdq_quantize_act_lowrank_down_conv_mx(const void* X, int x_dtype, int64_t batch, int64_t H,
                                            int64_t W, int64_t C, int32_t KH, int32_t KW,
                                            int32_t stride, int32_t pad, const float* inv_smooth,
                                            const uint16_t* L1p, int32_t R, uint8_t* a_codes_t,
-                                           uint8_t* a_exps_t, float* D, hipStream_t stream);
+                                           uint8_t* a_exps_t, uint16_t* D_t, hipStream_t stream);
 
 /* Device: the whole convolution in MXFP4: K1-MX on the patch matrix into
  * `ws`, then K2-MX into Y (ldy = N). ws: 256-byte aligned, at least

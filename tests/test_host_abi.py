@@ -91,7 +91,7 @@ def test_one_hip_runtime_is_mapped():
 
 
 def test_version_and_status_strings():
-    assert _lib.abi_version() == 9
+    assert _lib.abi_version() == 10
     for s in range(12):
         assert _lib.status_str(s) and _lib.status_str(s) != "unknown status"
     assert _lib.status_str(99) == "unknown status"
