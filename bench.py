@@ -407,6 +407,10 @@ class Sets:
                          ac=torch.empty((M, K // 2), dtype=torch.uint8, device="cuda"),
                          asc=torch.empty((M, G), dtype=torch.int16, device="cuda"))
             self.sets.append(s)
+        # the pre-kernel's optional workspace (long rows run split), shared by
+        # the sets: the launches of one stream never overlap
+        need = sq.quantize_act_workspace_bytes(M, K, self.R) if (self.tiled or self.mx) else 0
+        self.k1ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
 
     def k1(self, i, X=None):
         s = self.sets[i % len(self.sets)]
@@ -417,7 +421,11 @@ class Sets:
         f = (self.sq.quantize_act_lowrank_down_mx if self.mx
              else self.sq.quantize_act_lowrank_down_tiled if self.tiled
              else self.sq.quantize_act_lowrank_down)
-        f(X, s["inv"], s["L1p"], self.R, s["ac"], s["asc"], s["D"] if self.R else None)
+        if self.tiled or self.mx:
+            f(X, s["inv"], s["L1p"], self.R, s["ac"], s["asc"], s["D"] if self.R else None,
+              workspace=self.k1ws)
+        else:
+            f(X, s["inv"], s["L1p"], self.R, s["ac"], s["asc"], s["D"] if self.R else None)
 
     def k2(self, i, Y=None):
         s = self.sets[i % len(self.sets)]
@@ -746,14 +754,21 @@ def whole_config_main(args, torch, sq, wl, probe):
 
 def mlp_main(args, torch, sq, wl, probe):
     """Step = the DiT MLP pair on one batch: K1 + K2 (+GELU) of the up-projection
-    4608 x 3072 -> 12288, then K1 + K2 of the down-projection 12288 -> 3072."""
+    4608 x 3072 -> 12288, then K1 + K2 of the down-projection 12288 -> 3072, each
+    one call of the layer's fused entry point (svdq_linear_tiled on the tiled
+    INT4 path, svdq_linear on the canonical one, svdq_linear_mx for MXFP4)."""
+    if args.format == "w4a16":
+        raise SystemExit("the MLP pair runs the INT4 or MXFP4 format")
+    mx = args.format == "mxfp4"
+    tiled = args.path == "tiled" and not mx
+    prep_fn = sq.prepare_weights_mx if mx else sq.prepare_weights
     Lu, Xu, Wu = wl.layer_inputs(2, 0)
     Ld, Xd_cal, Wd = wl.layer_inputs(2, 1)
     lam_u = sq.smoothing_factors(sq.channel_absmax(Xu), Wu)
     lam_d = sq.smoothing_factors(sq.channel_absmax(Xd_cal), Wd)
-    up = sq.Linear(sq.prepare_weights(Wu, lam_u, Lu.rank),
-                   activation=None if args.unfused_gelu else "gelu_tanh")
-    down = sq.Linear(sq.prepare_weights(Wd, lam_d, Ld.rank))
+    up = sq.Linear(prep_fn(Wu, lam_u, Lu.rank),
+                   activation=None if args.unfused_gelu else "gelu_tanh", tiled=tiled)
+    down = sq.Linear(prep_fn(Wd, lam_d, Ld.rank), tiled=tiled)
     n = args.sets
     X = [torch.from_numpy(Xu).to("cuda") for _ in range(n)]
     H = [torch.empty((Lu.M, Lu.N), dtype=torch.float16, device="cuda") for _ in range(n)]
@@ -774,16 +789,20 @@ def mlp_main(args, torch, sq, wl, probe):
     gap = event_gap(torch)
     ops = 2.0 * Lu.M * Lu.N * Lu.K + 2.0 * Ld.M * Ld.N * Ld.K
     value = ops / t / 1e12
+    F = FORMATS[args.format]
     return {
-        "metric": "effective TOPS of the DiT MLP pair (SVDQuant W4A4+rank-32 up, GELU, down)",
-        "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "metric": (f"effective {F['unit']} of the DiT MLP pair (SVDQuant "
+                   f"{'MXFP4' if mx else 'W4A4'}+rank-32 up, GELU, down)"),
+        "value": round(value, 2), "unit": F["unit"], "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "settle_ms": round(settled, 1),
         "ms_per_step": round(t * 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": F["dtype"], "data": "synthetic",
         "config": {"workload": "dit_mlp: X f16 4608x3072 -> 12288 (GELU-tanh) -> 3072, rank 32",
                    "gelu": "separate kernel" if args.unfused_gelu else "fused into the up epilogue",
+                   "format": args.format,
+                   "path": "tiled" if tiled else ("mxfp4" if mx else "canonical"),
                    "buffer_sets": n},
-        "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
+        F["pct"]: round(100.0 * value / F["peak"], 2),
         "launch_median_us": {nm: round((float(np.median(per[:, j])) - gap) * 1e6, 2)
                              for j, nm in enumerate(names)},
         "clock": clock}

@@ -64,7 +64,7 @@ _SIGS = {
                                      _i64, _i64, _i64, _i64, _i32, _p, C.c_size_t, _i32, _p]),
     "svdq_prepare_weights_mx": (_int, [_p, _p, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p]),
     "svdq_quantize_act_lowrank_down_mx": (_int, [_p, _int, _i64, _i64, _i64, _p, _p, _i32, _p, _p,
-                                                 _p, _p]),
+                                                 _p, _p, C.c_size_t, _p]),
     "svdq_mx_gemm_lowrank_up": (_int, [_p, _p, _p, _p, _p, _p, _i32, _p, _p, _int, _i64, _i64,
                                        _i64, _i64, _i32, _p]),
     "svdq_linear_noalloc": (_int, [_p, _int, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _int, _i64,
@@ -75,8 +75,9 @@ _SIGS = {
     "svdq_int4_w_codes_tiled_bytes": (C.c_size_t, [_i64, _i64]),
     "svdq_int4_w_scales_tiled_bytes": (C.c_size_t, [_i64, _i64]),
     "svdq_pack_w4a4_tiles": (_int, [_p, _p, _i64, _i64, _p, _p]),
+    "svdq_quantize_act_workspace_bytes": (C.c_size_t, [_i64, _i64, _i32]),
     "svdq_quantize_act_lowrank_down_tiled": (_int, [_p, _int, _i64, _i64, _i64, _p, _p, _i32,
-                                                    _p, _p, _p, _p]),
+                                                    _p, _p, _p, _p, C.c_size_t, _p]),
     "svdq_w4a4_gemm_lowrank_up_tiled": (_int, [_p, _p, _p, _p, _p, _p, _i32, _p, _p, _int, _i64,
                                                _i64, _i64, _i64, _i32, _p]),
     "svdq_linear_tiled_workspace_bytes": (C.c_size_t, [_i64, _i64, _i32]),

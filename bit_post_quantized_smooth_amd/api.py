@@ -471,19 +471,38 @@ def _weights_tiled(N, K, R, w_codes_t, w_scales_t, L2t):
         _buf("L2t", L2t, _HALF, nbytes=2 * N * R)
 
 
+def quantize_act_workspace_bytes(M: int, K: int, R: int) -> int:
+    """Bytes of the optional pre-kernel workspace (tiled INT4 and MXFP4) on the
+    current device; 0 when the shape does not split."""
+    return int(lib.svdq_quantize_act_workspace_bytes(M, K, R))
+
+
+def _k1_ws(workspace):
+    """(pointer, bytes) of the optional pre-kernel workspace."""
+    if workspace is None:
+        return None, 0
+    if workspace.dtype != _torch().uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace: a contiguous uint8 tensor")
+    return _tp(workspace), workspace.numel()
+
+
 def quantize_act_lowrank_down_tiled(X, inv_smooth, L1p, R: int, a_ops_t, a_scales_t, D_t,
-                                    stream=None):
-    """K1 writing the tiled activation operands, fp32 scales and fp16 D_t."""
+                                    stream=None, workspace=None):
+    """K1 writing the tiled activation operands, fp32 scales and fp16 D_t.
+    workspace: None, or quantize_act_workspace_bytes(M, K, R) bytes (uint8) on
+    the same device, with which long rows run split."""
     D = D_t
     _mat("X", X, None, None)
     M, K = X.shape
     _down(K, R, inv_smooth, L1p)
     _act_side_tiled(M, K, R, a_ops_t, a_scales_t, D)
-    _on_gpu(X, inv_smooth, L1p if R else None, a_ops_t, a_scales_t, D if R else None)
+    _on_gpu(X, inv_smooth, L1p if R else None, a_ops_t, a_scales_t, D if R else None, workspace)
+    wp, wb = _k1_ws(workspace)
     check(lib.svdq_quantize_act_lowrank_down_tiled(_tp(X), _dt(X), M, K, X.stride(0),
                                                    _tp(inv_smooth), _tp(L1p) if R else None, R,
                                                    _tp(a_ops_t), _tp(a_scales_t),
-                                                   _tp(D) if R else None, _stream(stream)),
+                                                   _tp(D) if R else None, wp, wb,
+                                                   _stream(stream)),
           "svdq_quantize_act_lowrank_down_tiled")
 
 
@@ -543,18 +562,21 @@ def linear_noalloc(X, inv_smooth, L1p, L2t, R: int, w_codes, w_scales, bias, Y, 
           "svdq_linear_noalloc")
 
 
-def quantize_act_lowrank_down_mx(X, inv_smooth, L1p, R: int, a_codes_t, a_exps_t, D, stream=None):
+def quantize_act_lowrank_down_mx(X, inv_smooth, L1p, R: int, a_codes_t, a_exps_t, D, stream=None,
+                                 workspace=None):
     """K1-MX; a_codes_t / a_exps_t: device buffers of mx_codes_tiled_bytes(M, K) and
     mx_exps_tiled_bytes(M, K) bytes (tiled layouts); D: D_t, fp16 in the
-    up-projection's operand order (int4_d_tiled_bytes(M, R) bytes)."""
+    up-projection's operand order (int4_d_tiled_bytes(M, R) bytes); workspace:
+    as for quantize_act_lowrank_down_tiled."""
     _mat("X", X, None, None)
     M, K = X.shape
     _down(K, R, inv_smooth, L1p)
     _act_side(M, K, R, a_codes_t, a_exps_t, D, mx=True)
-    _on_gpu(X, inv_smooth, L1p if R else None, a_codes_t, a_exps_t, D if R else None)
+    _on_gpu(X, inv_smooth, L1p if R else None, a_codes_t, a_exps_t, D if R else None, workspace)
+    wp, wb = _k1_ws(workspace)
     check(lib.svdq_quantize_act_lowrank_down_mx(_tp(X), _dt(X), M, K, X.stride(0), _tp(inv_smooth),
                                                 _tp(L1p) if R else None, R, _tp(a_codes_t),
-                                                _tp(a_exps_t), _tp(D) if R else None,
+                                                _tp(a_exps_t), _tp(D) if R else None, wp, wb,
                                                 _stream(stream)),
           "svdq_quantize_act_lowrank_down_mx")
 

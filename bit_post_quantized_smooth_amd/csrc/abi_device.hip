@@ -130,8 +130,14 @@ int validate_k2(const uint8_t* a_codes, const void* a_scales, const uint8_t* w_c
 }
 
 struct WsLayout {
-  size_t codes, scales, d, total;
+  size_t codes, scales, d, part, total;
 };
+
+// The split pre-kernel's partial D tiles (k1_split_bytes; 0 when the shape is
+// not split on this device).
+size_t part_bytes(int64_t M, int64_t K, int32_t R, int fmt) {
+  return round_up(k1_split_bytes(M, K, R, fmt, false), 256);
+}
 
 // INT4: codes M x K/2, fp16 scales M x K/64; MXFP4: the tiled codes and
 // exponents (ceil(M/16) and ceil(M/64) blocks of 1024 and 256 bytes per chunk
@@ -148,22 +154,24 @@ WsLayout ws_layout(int64_t M, int64_t K, int32_t R, bool mx) {
     w.d = w.scales + round_up(static_cast<size_t>(M) * (K / SVDQ_GROUP) * 2, 256);
   }
   // D: fp32 M x R, or for MXFP4 fp16 in operand order (ceil(M/16) x
-  // ceil(R/32) blocks of 1 KB)
-  w.total = w.d + (mx ? round_up(static_cast<size_t>((M + 15) / 16) * ((R + 31) / 32) * 1024, 256)
-                      : round_up(static_cast<size_t>(M) * R * 4, 256));
+  // ceil(R/32) blocks of 1 KB); MXFP4 then the split pre-kernel's partials
+  w.part = w.d + (mx ? round_up(static_cast<size_t>((M + 15) / 16) * ((R + 31) / 32) * 1024, 256)
+                     : round_up(static_cast<size_t>(M) * R * 4, 256));
+  w.total = w.part + (mx ? part_bytes(M, K, R, kK1Mx) : 0);
   return w;
 }
 
 // The tiled INT4 path: operand blocks ceil(M/16) x K/64 of 1 KB, scales
 // ceil(M/128) x K/64 of 512 bytes, fp16 D in operand order ceil(M/16) x
-// ceil(R/32) blocks of 1 KB.
+// ceil(R/32) blocks of 1 KB, then the split pre-kernel's partials.
 WsLayout tiled_ws_layout(int64_t M, int64_t K, int32_t R) {
   WsLayout w;
   const size_t G = static_cast<size_t>(K / SVDQ_GROUP);
   w.codes = 0;
   w.scales = round_up(static_cast<size_t>((M + 15) / 16) * G * 1024, 256);
   w.d = w.scales + round_up(static_cast<size_t>((M + 127) / 128) * G * 512, 256);
-  w.total = w.d + round_up(static_cast<size_t>((M + 15) / 16) * ((R + 31) / 32) * 1024, 256);
+  w.part = w.d + round_up(static_cast<size_t>((M + 15) / 16) * ((R + 31) / 32) * 1024, 256);
+  w.total = w.part + part_bytes(M, K, R, kK1Int4Tiled);
   return w;
 }
 
@@ -341,10 +349,40 @@ int svdq_linear_canonical(const void* X, int x_dtype, int64_t ldx, const float* 
                    "svdq_linear_canonical K2 launch");
 }
 
+size_t svdq_quantize_act_workspace_bytes(int64_t M, int64_t K, int32_t R) {
+  if (M < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0 || R < 0 || R > SVDQ_MAX_RANK ||
+      R % 16 != 0)
+    return 0;
+  return k1_split_bytes(M, K, R, kK1Int4Tiled, false);
+}
+
+namespace {
+// The optional workspace of the tiled and MXFP4 pre-kernels: null, or at least
+// svdq_quantize_act_workspace_bytes and 256-byte aligned. Returns the partial
+// buffer to hand to the launcher (null: run unsplit).
+int k1_workspace(void* ws, size_t ws_bytes, int64_t M, int64_t K, int32_t R, int fmt,
+                 const char* fn, float** part) {
+  *part = nullptr;
+  if (ws == nullptr) return SVDQ_OK;
+  const size_t need = k1_split_bytes(M, K, R, fmt, false);
+  if (ws_bytes < need) {
+    set_error("%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    return SVDQ_ERR_WORKSPACE;
+  }
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) {
+    set_error("%s: workspace must be 256-byte aligned", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  *part = need > 0 ? static_cast<float*>(ws) : nullptr;
+  return SVDQ_OK;
+}
+}  // namespace
+
 int svdq_quantize_act_lowrank_down_tiled(const void* X, int x_dtype, int64_t M, int64_t K,
                                          int64_t ldx, const float* inv_smooth,
                                          const uint16_t* L1p, int32_t R, uint8_t* a_ops_t,
-                                         float* a_scales_t, uint16_t* D_t, hipStream_t stream) {
+                                         float* a_scales_t, uint16_t* D_t, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
   clear_error();
   const char* fn = "svdq_quantize_act_lowrank_down_tiled";
   // D_t is checked (null, alignment) and passed as an untyped device pointer
@@ -352,9 +390,12 @@ int svdq_quantize_act_lowrank_down_tiled(const void* X, int x_dtype, int64_t M, 
   if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, SVDQ_GROUP, a_ops_t,
                           a_scales_t, D, fn))
     return s;
+  float* part = nullptr;
+  if (int s = k1_workspace(workspace, workspace_bytes, M, K, R, kK1Int4Tiled, fn, &part))
+    return s;
   if (int s = device_ready()) return s;
   return check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1p, R, a_ops_t,
-                             a_scales_t, kK1Int4Tiled, D, stream),
+                             a_scales_t, kK1Int4Tiled, D, stream, nullptr, part),
                    "svdq_quantize_act_lowrank_down_tiled launch");
 }
 
@@ -423,6 +464,7 @@ int svdq_linear_tiled(const void* X, int x_dtype, int64_t ldx, const float* inv_
   uint8_t* a_ops = base + L.codes;
   float* a_scales = reinterpret_cast<float*>(base + L.scales);
   float* D = R > 0 ? reinterpret_cast<float*>(base + L.d) : nullptr;
+  float* part = L.total > L.part ? reinterpret_cast<float*>(base + L.part) : nullptr;
   if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, SVDQ_GROUP, a_ops, a_scales,
                           D, fn))
     return s;
@@ -432,7 +474,7 @@ int svdq_linear_tiled(const void* X, int x_dtype, int64_t ldx, const float* inv_
   if (int s = check_k2t_shape(M, N, K, fn)) return s;
   if (int s = device_ready()) return s;
   if (int s = check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1p, R, a_ops,
-                                  a_scales, kK1Int4Tiled, D, stream),
+                                  a_scales, kK1Int4Tiled, D, stream, nullptr, part),
                         "svdq_linear_tiled K1 launch"))
     return s;
   return check_hip(launch_k2t(a_ops, a_scales, w_codes_t, w_scales_t,
@@ -445,16 +487,19 @@ int svdq_linear_tiled(const void* X, int x_dtype, int64_t ldx, const float* inv_
 int svdq_quantize_act_lowrank_down_mx(const void* X, int x_dtype, int64_t M, int64_t K,
                                       int64_t ldx, const float* inv_smooth, const uint16_t* L1p,
                                       int32_t R, uint8_t* a_codes, uint8_t* a_e8m0,
-                                      uint16_t* D_t, hipStream_t stream) {
+                                      uint16_t* D_t, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
   clear_error();
   const char* fn = "svdq_quantize_act_lowrank_down_mx";
   float* D = reinterpret_cast<float*>(D_t);   // checked for null and alignment only
   if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, SVDQ_GROUP, a_codes, a_e8m0,
                           D, fn))
     return s;
+  float* part = nullptr;
+  if (int s = k1_workspace(workspace, workspace_bytes, M, K, R, kK1Mx, fn, &part)) return s;
   if (int s = device_ready()) return s;
   return check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1p, R, a_codes,
-                             a_e8m0, true, D, stream),
+                             a_e8m0, kK1Mx, D, stream, nullptr, part),
                    "svdq_quantize_act_lowrank_down_mx launch");
 }
 
@@ -507,6 +552,7 @@ int svdq_linear_mx(const void* X, int x_dtype, int64_t ldx, const float* inv_smo
   uint8_t* a_codes = base + L.codes;
   uint8_t* a_e8m0 = base + L.scales;
   float* D = R > 0 ? reinterpret_cast<float*>(base + L.d) : nullptr;
+  float* part = L.total > L.part ? reinterpret_cast<float*>(base + L.part) : nullptr;
   if (int s = validate_k1(X, x_dtype, M, K, ldx, inv_smooth, L1p, R, SVDQ_GROUP, a_codes, a_e8m0,
                           D, fn))
     return s;
@@ -515,7 +561,7 @@ int svdq_linear_mx(const void* X, int x_dtype, int64_t ldx, const float* inv_smo
     return s;
   if (int s = device_ready()) return s;
   if (int s = check_hip(launch_k1(X, x_dtype == SVDQ_F16, M, K, ldx, inv_smooth, L1p, R, a_codes,
-                                  a_e8m0, true, D, stream),
+                                  a_e8m0, kK1Mx, D, stream, nullptr, part),
                         "svdq_linear_mx K1 launch"))
     return s;
   return check_hip(launch_k2_mx(a_codes, a_e8m0, w_codes, w_e8m0,

@@ -25,11 +25,19 @@ int resident_slots();
 enum K1Fmt { kK1Int4 = 0, kK1Mx = 1, kK1Int4Tiled = 2 };
 
 // conv: null for a linear layer; else X is the NHWC image and M, K are the
-// patch matrix's.
+// patch matrix's. part: null, or k1_split_bytes(M, K, R, fmt, conv) bytes
+// (16-byte aligned) for the partial D tiles of a split pre-kernel; without
+// it a shape that would split runs unsplit (ranks above 0).
 hipError_t launch_k1(const void* X, bool x_f16, int64_t M, int64_t K, int64_t ldx,
                      const float* inv_smooth, const uint16_t* L1p, int R, uint8_t* a_codes,
                      void* a_meta, int fmt, float* D, hipStream_t stream,
-                     const ConvGeom* conv = nullptr);
+                     const ConvGeom* conv = nullptr, float* part = nullptr);
+
+// Slices of the groups per row tile that the pre-kernel uses for this shape
+// on the current device (1: not split), and the bytes its partial D tiles
+// need (0 when not split or R = 0).
+int k1_slices(int64_t M, int64_t K, int R, int fmt, bool conv);
+size_t k1_split_bytes(int64_t M, int64_t K, int R, int fmt, bool conv);
 
 hipError_t launch_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* w_codes,
                      const uint16_t* w_scales, const float* D, const uint16_t* L2t, int R,

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(64 * WV, WV >= 16 ? 1 : 2) void k1_quant_down_kerne
     const XT* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
     const float* __restrict__ inv_smooth, const uint16_t* __restrict__ L1p, int R,
     uint8_t* __restrict__ a_codes, void* __restrict__ a_meta, float* __restrict__ D,
-    ConvGeom cg) {
+    ConvGeom cg, int S, float* __restrict__ Dpart) {
 #pragma clang fp contract(off)
   constexpr bool MX = FMT == kK1Mx;
   constexpr bool TILED = FMT == kK1Int4Tiled;
@@ -286,12 +286,17 @@ __global__ __launch_bounds__(64 * WV, WV >= 16 ? 1 : 2) void k1_quant_down_kerne
   // so each XCD takes one contiguous run of row tiles (neighbouring output
   // pixels of a convolution read the same input rows, which then stay in
   // that XCD's L2)
-  const int tile = xcd_contiguous(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+  // With S slices, workgroup (tile, slice) takes the slice's run of groups
+  // and leaves its partial D in Dpart for k1_reduce_kernel.
+  const int unit = xcd_contiguous(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+  const int tile = unit / S, slice = unit - tile * S;
   const int64_t row0 = static_cast<int64_t>(tile) * (16 * RT);
   const int G = static_cast<int>(K / kGroup);
+  const int g_lo = static_cast<int>(static_cast<int64_t>(slice) * G / S);
+  const int g_hi = static_cast<int>(static_cast<int64_t>(slice + 1) * G / S);
   const int ncb = R / 16;                            // real column blocks (<= NCB)
-  // this wave's groups are wave, wave+WAVES, ...: n_mine of them
-  const int n_mine = (G > wave) ? (G - wave + WAVES - 1) / WAVES : 0;
+  // this wave's groups are g_lo + wave, g_lo + wave + WAVES, ...: n_mine of them
+  const int n_mine = (g_hi - g_lo > wave) ? (g_hi - g_lo - wave + WAVES - 1) / WAVES : 0;
   const int64_t nchunks = (K + 127) / 128;
 
   // Per row tile: this lane's row (clamped to the last row for loads: rows
@@ -340,8 +345,8 @@ __global__ __launch_bounds__(64 * WV, WV >= 16 ? 1 : 2) void k1_quant_down_kerne
   };
 
   auto load_group = [&](GroupIn<XT, NCB, RT>& in, int i) {
-    int g = wave + WAVES * i;
-    g = g < G ? g : G - 1;
+    int g = g_lo + wave + WAVES * i;
+    g = g < g_hi ? g : g_hi - 1;
     const int k0 = g * kGroup;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -390,7 +395,7 @@ __global__ __launch_bounds__(64 * WV, WV >= 16 ? 1 : 2) void k1_quant_down_kerne
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int i = i0 + b;
-      const int g = wave + WAVES * i;
+      const int g = g_lo + wave + WAVES * i;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         uint32_t packed[2] = {0u, 0u};
@@ -503,7 +508,12 @@ __global__ __launch_bounds__(64 * WV, WV >= 16 ? 1 : 2) void k1_quant_down_kerne
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) s += dpart[w][r_][c_];
-      if (row0 + r_ < M) {
+      if (S > 1) {
+        // the slice's partial: rows of all tiles (gridDim.x / S of them),
+        // slice-major, fp32
+        const int64_t rows_all = static_cast<int64_t>(gridDim.x / S) * (16 * RT);
+        Dpart[(slice * rows_all + row0 + r_) * R + c_] = s;
+      } else if (row0 + r_ < M) {
         if constexpr (TILED || MX) {
           // fp16(D) in the up-projection's operand order: per 16-row block
           // and 32-rank chunk one 1 KB block, lane 16q + r holding row r,
@@ -521,18 +531,56 @@ __global__ __launch_bounds__(64 * WV, WV >= 16 ? 1 : 2) void k1_quant_down_kerne
   }
 }
 
+// Sums the S partial D tiles of the split pre-kernel in slice order and writes
+// fp16(D) in the up-projection's operand order (the tiled layouts' D_t): one
+// lane per (16-row block, 32-rank chunk, lane 16q + r), i.e. row r, ranks
+// 8q .. 8q+7 of the chunk, one 16-byte store.
+__global__ __launch_bounds__(256) void k1_reduce_kernel(const float* __restrict__ part, int S,
+                                                        int64_t rows_all, int64_t M, int R,
+                                                        uint16_t* __restrict__ Dt) {
+  const int RC = (R + 31) / 32;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t u = t >> 6;                       // (row block, rank chunk)
+  const int lane = static_cast<int>(t & 63);
+  const int64_t b = u / RC;
+  const int c = static_cast<int>(u - b * RC);
+  const int64_t m = 16 * b + (lane & 15);
+  const int k = 32 * c + 8 * (lane >> 4);
+  if (m >= M || k >= R) return;                   // R % 16 == 0: whole 8-runs are in or out
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int sl = 0; sl < S; ++sl) {
+    const float4* p = reinterpret_cast<const float4*>(part + (sl * rows_all + m) * R + k);
+    const float4 lo = p[0], hi = p[1];
+    acc[0] += lo.x; acc[1] += lo.y; acc[2] += lo.z; acc[3] += lo.w;
+    acc[4] += hi.x; acc[5] += hi.y; acc[6] += hi.z; acc[7] += hi.w;
+  }
+  uint4 o;
+  o.x = f2h(acc[0]) | (static_cast<uint32_t>(f2h(acc[1])) << 16);
+  o.y = f2h(acc[2]) | (static_cast<uint32_t>(f2h(acc[3])) << 16);
+  o.z = f2h(acc[4]) | (static_cast<uint32_t>(f2h(acc[5])) << 16);
+  o.w = f2h(acc[6]) | (static_cast<uint32_t>(f2h(acc[7])) << 16);
+  *reinterpret_cast<uint4*>(Dt + ((b * RC + c) * 64 + lane) * 8) = o;
+}
+
+// S slices of the groups per row tile (S = 1: no split), and where the slices'
+// partial D tiles go.
+struct K1Split {
+  int S;
+  float* part;
+};
+
 template <typename XT, int NCB, int RT, int NB, int WV = k1_waves<NCB>()>
 hipError_t launch_k1_rt(const void* X, int64_t M, int64_t K, int64_t ldx,
                         const float* inv_smooth, const uint16_t* L1p, int R,
                         uint8_t* a_codes, void* a_meta, int fmt, float* D, hipStream_t stream,
-                        const ConvGeom* conv) {
-  const dim3 block(64 * WV),
-      grid(static_cast<unsigned>((M + 16 * RT - 1) / (16 * RT)));
+                        const ConvGeom* conv, K1Split sp = K1Split{1, nullptr}) {
+  const int64_t tiles = (M + 16 * RT - 1) / (16 * RT);
+  const dim3 block(64 * WV), grid(static_cast<unsigned>(tiles * sp.S));
   const XT* x = static_cast<const XT*>(X);
   const ConvGeom cg = conv ? *conv : ConvGeom{};
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, x, M, K, ldx, inv_smooth, L1p, R, a_codes,
-                       a_meta, D, cg);
+                       a_meta, D, cg, sp.S, sp.part);
   };
   if (conv) {
     if (fmt == kK1Mx) go(k1_quant_down_kernel<XT, NCB, NB, kK1Mx, true, RT, WV>);
@@ -543,39 +591,64 @@ hipError_t launch_k1_rt(const void* X, int64_t M, int64_t K, int64_t ldx,
     else if (fmt == kK1Int4Tiled) go(k1_quant_down_kernel<XT, NCB, NB, kK1Int4Tiled, false, RT, WV>);
     else go(k1_quant_down_kernel<XT, NCB, NB, kK1Int4, false, RT, WV>);
   }
+  if (sp.S > 1 && R > 0) {
+    // every slice's partial is in place: sum them into D_t
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    const int64_t units = ((M + 15) / 16) * ((R + 31) / 32);
+    hipLaunchKernelGGL(k1_reduce_kernel, dim3(static_cast<unsigned>((units * 64 + 255) / 256)),
+                       dim3(256), 0, stream, sp.part, sp.S, tiles * 16 * RT, M, R,
+                       reinterpret_cast<uint16_t*>(D));
+  }
   return hipGetLastError();
 }
 
-// Two row tiles per workgroup once there are more row tiles than compute units
-// (resident_slots() / 2), up to rank 64 (beyond it the second tile's
-// registers cost occupancy). A row tile takes about the same time whatever
-// else runs, so with 16-row workgroups some compute units would run two of
-// them back to back; a 32-row workgroup costs less than that, and its waves
-// share one set of smoothing factors and L1 operands (measured on the
-// 12288-channel down-projection at 4608 rows: 41.0 us against 46.1 us; at
-// 4096 rows, one 16-row tile per compute unit, it would be 37% slower).
+// Two row tiles per workgroup once there are more 16-row tiles than compute
+// units (resident_slots() / 2), a row holds at least 16 groups of 64
+// channels and the rank is at most 64. A row tile takes about the same time
+// whatever else runs, so with 16-row workgroups some compute units would run
+// two of them back to back; a 32-row workgroup costs less than that, and its
+// waves share one set of smoothing factors and L1 operands. Each wave then
+// keeps two groups in flight, three on long rows (at least 12 groups per
+// wave) when every 32-row tile is resident at once. Measured inside the
+// layer's step on MI355X (median of the pre-kernel's launches), against one
+// 16-row tile per workgroup and one group in flight: DiT QKV 4608 x 3072 at
+// rank 32 15.6-15.9 against 17.2-18.0 us, its MXFP4 version 15.3-15.5
+// against 16.6-16.8 us; the 12288-channel down-projection at 4608 rows, three
+// groups in flight against one: 41.0 against 46.1 us. Rows of fewer than 16
+// groups keep 16-row tiles (32768 x 320: 11.8 against 12.7-13.2 us). At rank
+// 96 (9216 x 3072) two tiles with two groups in flight were faster with X
+// streamed from HBM alone but 1.3 us slower inside the step (42.6 against
+// 41.3 us), so ranks above 64 keep 16-row tiles. The convolution keeps its
+// own rule (two tiles on patch matrices of more tiles than compute units
+// unless the rows are short and every tile is resident: the 128 x 128 image
+// took 48.0 against 56.1 us).
 template <typename XT, int NCB>
 hipError_t launch_k1_t(const void* X, int64_t M, int64_t K, int64_t ldx,
                        const float* inv_smooth, const uint16_t* L1p, int R,
                        uint8_t* a_codes, void* a_meta, int fmt, float* D, hipStream_t stream,
-                       const ConvGeom* conv) {
+                       const ConvGeom* conv, float* part) {
+  const int64_t tiles = (M + 15) / 16, slots = static_cast<int64_t>(resident_slots());
+  const int64_t G = K / 64;
   if constexpr (NCB <= 4) {
-    const int64_t tiles = (M + 15) / 16, slots = static_cast<int64_t>(resident_slots());
-    // short rows (fewer than 12 groups of 64 channels per wave) with every
-    // 16-row tile resident at once: the 32-row tile's shared operands do not
-    // pay for its longer reduction (measured on the DiT QKV pre-kernel, 4608
-    // x 3072: 14.0 us against 15.6 us)
-    const bool short_rows = K / 64 < 12 * k1_waves<NCB>() && tiles <= slots;
-    if (2 * tiles > slots && !short_rows) {
-      // at most one 32-row workgroup per compute unit: each wave keeps three
-      // groups in flight (the registers of a second resident workgroup are
-      // not needed); measured 4% faster on the DiT QKV pre-kernel and 11% on
-      // the 12288-channel down-projection than one group in flight (16 waves
-      // with two groups each were slower than either)
-      if ((M + 31) / 32 <= slots / 2)
+    const bool all_resident = (M + 31) / 32 <= slots / 2;
+    if (conv != nullptr) {
+      const bool short_rows = G < 12 * k1_waves<NCB>() && tiles <= slots;
+      if (2 * tiles > slots && !short_rows) {
+        if (all_resident)
+          return launch_k1_rt<XT, NCB, 2, 3>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta,
+                                             fmt, D, stream, conv);
+        return launch_k1_rt<XT, NCB, 2, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt,
+                                           D, stream, conv);
+      }
+    } else if (2 * tiles > slots && G >= 16) {
+      const int S = k1_slices(M, K, R, fmt, false);
+      if (S > 1 && (R == 0 || part != nullptr))
+        return launch_k1_rt<XT, NCB, 2, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt,
+                                           D, stream, conv, K1Split{S, part});
+      if (G >= 12 * k1_waves<NCB>() && all_resident)
         return launch_k1_rt<XT, NCB, 2, 3>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt,
                                            D, stream, conv);
-      return launch_k1_rt<XT, NCB, 2, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D,
+      return launch_k1_rt<XT, NCB, 2, 2>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D,
                                          stream, conv);
     }
   }
@@ -587,18 +660,18 @@ template <typename XT>
 hipError_t launch_k1_dtype(const void* X, int64_t M, int64_t K, int64_t ldx,
                                   const float* inv_smooth, const uint16_t* L1p, int R,
                                   uint8_t* a_codes, void* a_meta, int fmt, float* D,
-                                  hipStream_t stream, const ConvGeom* conv) {
+                                  hipStream_t stream, const ConvGeom* conv, float* part) {
   switch (R / 16) {
-    case 0: return launch_k1_t<XT, 0>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
-    case 1: return launch_k1_t<XT, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
-    case 2: return launch_k1_t<XT, 2>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
-    case 3: return launch_k1_t<XT, 3>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
-    case 4: return launch_k1_t<XT, 4>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
-    case 5: return launch_k1_t<XT, 5>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
-    case 6: return launch_k1_t<XT, 6>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
+    case 0: return launch_k1_t<XT, 0>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv, part);
+    case 1: return launch_k1_t<XT, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv, part);
+    case 2: return launch_k1_t<XT, 2>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv, part);
+    case 3: return launch_k1_t<XT, 3>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv, part);
+    case 4: return launch_k1_t<XT, 4>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv, part);
+    case 5: return launch_k1_t<XT, 5>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv, part);
+    case 6: return launch_k1_t<XT, 6>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv, part);
     case 7:
-    case 8: return launch_k1_t<XT, 8>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
-    default: return launch_k1_t<XT, 16>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
+    case 8: return launch_k1_t<XT, 8>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv, part);
+    default: return launch_k1_t<XT, 16>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv, part);
   }
 }
 
@@ -606,10 +679,38 @@ hipError_t launch_k1_dtype(const void* X, int64_t M, int64_t K, int64_t ldx,
 
 hipError_t launch_k1(const void* X, bool x_f16, int64_t M, int64_t K, int64_t ldx,
                      const float* inv_smooth, const uint16_t* L1p, int R, uint8_t* a_codes,
-                     void* a_meta, int fmt, float* D, hipStream_t stream, const ConvGeom* conv) {
+                     void* a_meta, int fmt, float* D, hipStream_t stream, const ConvGeom* conv,
+                     float* part) {
   if (x_f16)
-    return launch_k1_dtype<_Float16>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
-  return launch_k1_dtype<float>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream, conv);
+    return launch_k1_dtype<_Float16>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D,
+                                     stream, conv, part);
+  return launch_k1_dtype<float>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D, stream,
+                                conv, part);
+}
+
+// Long rows (at least 12 groups per wave of a 32-row tile) with more 16-row
+// tiles than compute units: each 32-row tile's groups are split over S
+// workgroups, S = ceil(4 x compute units / 32-row tiles), at most G / 16, so
+// that about four units of work per compute unit even out the tiles left
+// over. Measured on MI355X on the 12288-channel down-projection at 4608 rows
+// (144 tiles, S = 8), the pre-kernel alone with X streamed from HBM: 41.5 us
+// plus 4 us for the reduction pass against 57.7 us unsplit. The canonical
+// layout (fp32 D), the convolution and ranks above 64 are not split.
+int k1_slices(int64_t M, int64_t K, int R, int fmt, bool conv) {
+  if (conv || fmt == kK1Int4 || R > 64 || M < 1 || K < 64) return 1;
+  const int64_t tiles = (M + 15) / 16, slots = resident_slots(), G = K / 64;
+  if (2 * tiles <= slots || G < 12 * 8) return 1;
+  const int64_t t32 = (M + 31) / 32, cus = slots / 2;
+  int64_t S = (4 * cus + t32 - 1) / t32;
+  if (S > G / 16) S = G / 16;
+  return S < 2 ? 1 : static_cast<int>(S);
+}
+
+size_t k1_split_bytes(int64_t M, int64_t K, int R, int fmt, bool conv) {
+  const int S = k1_slices(M, K, R, fmt, conv);
+  if (S == 1 || R == 0) return 0;
+  return static_cast<size_t>(S) * static_cast<size_t>((M + 31) / 32 * 32) *
+         static_cast<size_t>(R) * 4;
 }
 
 }  // namespace svdq

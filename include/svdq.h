@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 10
+#define SVDQ_ABI_VERSION 11
 
 /* status codes */
 enum {
@@ -345,15 +345,32 @@ size_t svdq_int4_w_scales_tiled_bytes(int64_t N, int64_t K);
 int svdq_pack_w4a4_tiles(const uint8_t* w_codes, const uint16_t* w_scales, int64_t N, int64_t K,
                          uint8_t* w_codes_t, float* w_scales_t);
 
+/* Bytes of the optional workspace of the tiled and MXFP4 pre-kernels
+ * (svdq_quantize_act_lowrank_down_tiled, _mx) for this shape on the current
+ * device: on long rows (at least 96 groups of 64, more 16-row tiles than
+ * compute units, R <= 64) the pre-kernel splits each 32-row tile's groups
+ * over several workgroups and needs room for their fp32 partial D tiles,
+ * which a second pass sums in a fixed order into D_t (SVDQuant abstract on
+ * ai-digest.ru: the fused low-rank branch must not cost the layer its
+ * speed; the split evens out row tiles that do not divide over the compute
+ * units). 0 when the shape is not split, or R == 0 (no D), or the sizes are
+ * invalid. */
+size_t svdq_quantize_act_workspace_bytes(int64_t M, int64_t K, int32_t R);
+
 /* Device: K1 (svdq_quantize_act_lowrank_down: the same smoothing, quantizer
  * and D) writing the codes, scales and D as a_ops_t, a_scales_t and D_t
  * (svdq_int4_act_tiled_bytes(M, K), svdq_int4_act_scales_tiled_bytes(M, K) and
  * svdq_int4_d_tiled_bytes(M, R) bytes, 16-byte aligned; D_t may be NULL when
- * R == 0). */
+ * R == 0). workspace: NULL, or at least svdq_quantize_act_workspace_bytes(M,
+ * K, R) bytes, 256-byte aligned (else SVDQ_ERR_WORKSPACE / SVDQ_ERR_ALIGN);
+ * with it a shape that splits runs split (its D_t sums the same terms in
+ * another order, within the same bound), without it unsplit. The codes and
+ * scales are the same either way. */
 int svdq_quantize_act_lowrank_down_tiled(const void* X, int x_dtype, int64_t M, int64_t K,
                                          int64_t ldx, const float* inv_smooth,
                                          const uint16_t* L1p, int32_t R, uint8_t* a_ops_t,
-                                         float* a_scales_t, uint16_t* D_t, hipStream_t stream);
+                                         float* a_scales_t, uint16_t* D_t, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
 
 /* Device: K2 (svdq_w4a4_gemm_lowrank_up: the same exact int32 group partials,
  * fp32 rescale, low-rank up-projection, bias and activation) on the tiled
@@ -366,8 +383,10 @@ int svdq_w4a4_gemm_lowrank_up_tiled(const uint8_t* a_ops_t, const float* a_scale
                                     int64_t K, int64_t ldy, int32_t activation,
                                     hipStream_t stream);
 
-/* Bytes of workspace svdq_linear_tiled needs: a_ops_t, a_scales_t and D_t, each
- * 256-byte aligned inside the workspace. */
+/* Bytes of workspace svdq_linear_tiled needs on the current device: a_ops_t,
+ * a_scales_t, D_t and the split pre-kernel's partial D tiles (see
+ * svdq_quantize_act_workspace_bytes), each 256-byte aligned inside the
+ * workspace. */
 size_t svdq_linear_tiled_workspace_bytes(int64_t M, int64_t K, int32_t R);
 
 /* The whole layer on the tiled path: the tiled K1 then the tiled K2 on
@@ -427,11 +446,13 @@ int svdq_pack_mx_tiles(const uint8_t* codes, const uint8_t* e8m0, int64_t rows, 
 /* K1-MX: as svdq_quantize_act_lowrank_down with the MXFP4 quantizer; a_codes_t
  * and a_exps_t in the tiled layouts (svdq_mx_*_tiled_bytes(M, K) bytes); D as
  * D_t (fp16 D in operand order, the layout of the tiled INT4 path; NULL when
- * R == 0). */
+ * R == 0). workspace: as for svdq_quantize_act_lowrank_down_tiled (the same
+ * svdq_quantize_act_workspace_bytes). */
 int svdq_quantize_act_lowrank_down_mx(const void* X, int x_dtype, int64_t M, int64_t K,
                                       int64_t ldx, const float* inv_smooth, const uint16_t* L1p,
                                       int32_t R, uint8_t* a_codes_t, uint8_t* a_exps_t,
-                                      uint16_t* D_t, hipStream_t stream);
+                                      uint16_t* D_t, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 /* K2-MX: Y[m,n] = sum_k deq(a)[m,k] * deq(w)[n,k] (products and sums in the
  * matrix core's fp32 accumulation, deq = E2M1 value * 2^e of its block)
@@ -445,9 +466,9 @@ int svdq_mx_gemm_lowrank_up(const uint8_t* a_codes_t, const uint8_t* a_exps_t,
                             int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
                             int32_t activation, hipStream_t stream);
 
-/* Bytes of workspace svdq_linear_mx needs: the tiled activation codes and
- * exponents and D_t, each 256-byte aligned inside the workspace (0 for invalid
- * sizes). */
+/* Bytes of workspace svdq_linear_mx needs on the current device: the tiled
+ * activation codes and exponents, D_t and the split pre-kernel's partial D
+ * tiles, each 256-byte aligned inside the workspace (0 for invalid sizes). */
 size_t svdq_linear_mx_workspace_bytes(int64_t M, int64_t K, int32_t R);
 
 /* The whole MXFP4 layer: K1-MX then K2-MX on `stream`, intermediates in `ws`;

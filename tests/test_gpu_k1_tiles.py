@@ -1,8 +1,11 @@
 """K1 with two 16-row tiles per workgroup on ragged row counts.
 
-Once there are more 16-row tiles than compute units, K1 gives each workgroup
-32 rows; with M not a multiple of 32 the last workgroup's second tile, or part
-of its first, lies past M. On such row counts the INT4 codes and scales, and
+Once there are more 16-row tiles than compute units, a row holds at least 16
+groups of 64 channels and the rank is at most 64, K1 gives each workgroup 32
+rows (two groups in flight per wave, three on rows of at least 96 groups);
+with M not a multiple of 32 the last workgroup's second tile, or part of its
+first, lies past M. The cases cover both ring depths, and rank 96 (16-row
+workgroups of four waves) with fp32 X on a ragged M. On such row counts the INT4 codes and scales, and
 the MXFP4 tiled codes and exponents, must be bit-exact against the oracle's
 quantizer on every row, D must stay within the down-projection's bound, and
 the INT4 output rows past M must stay untouched (canary bytes).
@@ -19,7 +22,7 @@ from test_gpu_mx import MxDevice, _oracle_w, read_act
 
 pytestmark = pytest.mark.gpu
 
-CASES = [(4100, 320, 32, "f16"), (4113, 256, 48, "f32"), (4127, 384, 16, "f16")]
+CASES = [(4100, 1024, 32, "f16"), (4113, 1024, 96, "f32"), (4127, 6144, 16, "f16")]
 
 
 def _inputs(M, K, xdt, seed):
@@ -88,3 +91,52 @@ def test_mx_two_row_tiles_ragged(case):
     assert np.array_equal(got_e, a_e8)
     Dg = int4_tiles.untile_d(d.D.cpu().numpy(), M, R).astype(np.float64)
     _check_d(Dg, xh, p.L1, K, f16_out=True)
+
+
+# Long rows (at least 96 groups) with more 16-row tiles than compute units:
+# with the optional workspace the tiled and MXFP4 pre-kernels split each
+# 32-row tile's groups over several workgroups and sum the partial D tiles in
+# a second pass; without it they run unsplit. Both must give the oracle's
+# codes and scales bit for bit, and D within the down-projection's bound plus
+# its one fp16 rounding, on ragged row counts.
+SPLIT = [(4100, 6144, 16, "f16"), (4113, 6144, 32, "f32")]
+
+
+@pytest.mark.parametrize("split", [True, False], ids=["split", "unsplit"])
+@pytest.mark.parametrize("case", SPLIT, ids=lambda c: f"{c[0]}x{c[1]}_r{c[2]}_{c[3]}")
+def test_tiled_long_rows_split_and_unsplit(case, split):
+    import bit_post_quantized_smooth_amd as sq
+    from test_gpu_tiled import TiledLayer, _check_k1_tiled
+    torch = torch_mod()
+    M, K, R, xdt = case
+    X, W = _inputs(M, K, xdt, seed=M + K + R + 2)
+    lam = sq.smoothing_factors(sq.channel_absmax(X), W)
+    p = sq.prepare_weights(W, lam, R)
+    _, inv_o, _, _ = oracle_prep(X, W, p, R)
+    assert sq.quantize_act_workspace_bytes(M, K, R) > 0      # the shape splits on MI355X
+    d = TiledLayer(X, p, None, "f16", k1_workspace=split)
+    d.k1()
+    torch.cuda.synchronize()
+    _check_k1_tiled(X, inv_o, p, K, d)
+
+
+@pytest.mark.parametrize("split", [True, False], ids=["split", "unsplit"])
+@pytest.mark.parametrize("case", SPLIT, ids=lambda c: f"{c[0]}x{c[1]}_r{c[2]}_{c[3]}")
+def test_mx_long_rows_split_and_unsplit(case, split):
+    import bit_post_quantized_smooth_amd as sq
+    torch = torch_mod()
+    M, K, R, xdt = case
+    X, W = _inputs(M, K, xdt, seed=M + K + R + 3)
+    lam = sq.smoothing_factors(sq.channel_absmax(X), W)
+    p = sq.prepare_weights_mx(W, lam, R)
+    inv, _, _ = _oracle_w(X, W, p, R)
+    d = MxDevice(X, p, None, k1_workspace=split)
+    d.k1()
+    torch.cuda.synchronize()
+    a_codes, a_e8, xh = O.mx_quantize_activation(X, inv)
+    got_c, got_e = read_act(d)
+    assert np.array_equal(got_c, a_codes)
+    assert np.array_equal(got_e, a_e8)
+    Dg = int4_tiles.untile_d(d.D.cpu().numpy(), M, R).astype(np.float64)
+    _check_d(Dg, xh, p.L1, K, f16_out=True)
+

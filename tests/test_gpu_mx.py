@@ -63,7 +63,10 @@ def read_act(d):
 
 
 class MxDevice:
-    def __init__(self, X, p, bias, y_dtype="f16"):
+    """The MXFP4 layer's device buffers. k1_workspace: K1-MX gets the optional
+    pre-kernel workspace (long rows then run split, as in svdq_linear_mx)."""
+
+    def __init__(self, X, p, bias, y_dtype="f16", k1_workspace=True):
         torch = torch_mod()
         self.M, self.K = X.shape
         self.N, self.R = p.N, p.rank
@@ -85,11 +88,14 @@ class MxDevice:
                             dtype=torch.int16, device="cuda")
         self.Y = torch.empty((self.M, self.N),
                              dtype=torch.float16 if y_dtype == "f16" else torch.float32, device="cuda")
+        need = sq_mod().quantize_act_workspace_bytes(self.M, self.K, self.R)
+        self.k1ws = (torch.full((max(need, 256),), 0xA5, dtype=torch.uint8, device="cuda")
+                     if k1_workspace else None)
 
     def k1(self):
         import bit_post_quantized_smooth_amd as sq
         sq.quantize_act_lowrank_down_mx(self.X, self.inv, self.L1p, self.R, self.a_codes, self.a_e8,
-                                        self.D if self.R else None)
+                                        self.D if self.R else None, workspace=self.k1ws)
 
     def k2(self, activation=None):
         import bit_post_quantized_smooth_amd as sq

@@ -37,7 +37,7 @@ def sq_mod():
 class TiledLayer:
     """Device buffers of one layer on the tiled path (weights packed by the library)."""
 
-    def __init__(self, X, p, bias, y_dtype="f16"):
+    def __init__(self, X, p, bias, y_dtype="f16", k1_workspace=True):
         torch = torch_mod()
         sq = sq_mod()
         self.M, self.K = X.shape
@@ -59,9 +59,16 @@ class TiledLayer:
                             dtype=torch.float16 if y_dtype == "f16" else torch.float32,
                             device="cuda")
 
+        # the optional pre-kernel workspace (long rows run split, as in
+        # svdq_linear_tiled), filled with garbage
+        need = sq.quantize_act_workspace_bytes(self.M, self.K, self.R)
+        self.k1ws = (torch.full((max(need, 256),), 0xA5, dtype=torch.uint8, device="cuda")
+                     if k1_workspace else None)
+
     def k1(self):
         sq_mod().quantize_act_lowrank_down_tiled(self.X, self.inv, self.L1p, self.R, self.ops,
-                                                 self.scales, self.D if self.R else None)
+                                                 self.scales, self.D if self.R else None,
+                                                 workspace=self.k1ws)
 
     def k2(self, activation=None):
         sq_mod().w4a4_gemm_lowrank_up_tiled(self.ops, self.scales, self.wc, self.ws,

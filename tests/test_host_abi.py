@@ -91,7 +91,7 @@ def test_one_hip_runtime_is_mapped():
 
 
 def test_version_and_status_strings():
-    assert _lib.abi_version() == 10
+    assert _lib.abi_version() == 11
     for s in range(12):
         assert _lib.status_str(s) and _lib.status_str(s) != "unknown status"
     assert _lib.status_str(99) == "unknown status"
@@ -451,11 +451,23 @@ def test_device_entry_points_reject_bad_arguments():
     la[17] = 0x10080
     assert L.svdq_linear(*la) == _lib.ERR_ALIGN
     # MXFP4 K1 / K2 / layer
-    assert L.svdq_quantize_act_lowrank_down_mx(A16, 1, 16, 64, 64, A16, A16, 16, A16, None, A16, None) == _lib.ERR_NULL
-    assert L.svdq_quantize_act_lowrank_down_mx(A16, 1, 16, 96, 96, A16, A16, 16, A16, A16, A16, None) == _lib.ERR_GROUP
-    assert L.svdq_quantize_act_lowrank_down_mx(A16, 1, 16, 64, 64, A16, A16, 24, A16, A16, A16, None) == _lib.ERR_RANK
-    assert L.svdq_quantize_act_lowrank_down_mx(A16, 1, 16, 64, 64, A16, A16, 16, A16, MIS, A16, None) == _lib.ERR_ALIGN
-    assert L.svdq_quantize_act_lowrank_down_mx(A16, 3, 16, 64, 64, A16, A16, 16, A16, A16, A16, None) == _lib.ERR_DTYPE
+    assert L.svdq_quantize_act_lowrank_down_mx(A16, 1, 16, 64, 64, A16, A16, 16, A16, None, A16, None, 0, None) == _lib.ERR_NULL
+    assert L.svdq_quantize_act_lowrank_down_mx(A16, 1, 16, 96, 96, A16, A16, 16, A16, A16, A16, None, 0, None) == _lib.ERR_GROUP
+    assert L.svdq_quantize_act_lowrank_down_mx(A16, 1, 16, 64, 64, A16, A16, 24, A16, A16, A16, None, 0, None) == _lib.ERR_RANK
+    assert L.svdq_quantize_act_lowrank_down_mx(A16, 1, 16, 64, 64, A16, A16, 16, A16, MIS, A16, None, 0, None) == _lib.ERR_ALIGN
+    assert L.svdq_quantize_act_lowrank_down_mx(A16, 3, 16, 64, 64, A16, A16, 16, A16, A16, A16, None, 0, None) == _lib.ERR_DTYPE
+    # the pre-kernels' optional workspace (split long rows): too small, misaligned
+    big = (4608, 12288, 32)
+    need_k1 = L.svdq_quantize_act_workspace_bytes(*big)
+    assert need_k1 > 0
+    k1t = [A16, 1, big[0], big[1], big[1], A16, A16, big[2], A16, A16, A16, 0x10000, need_k1 - 1,
+           None]
+    assert L.svdq_quantize_act_lowrank_down_tiled(*k1t) == _lib.ERR_WORKSPACE
+    assert "workspace" in _lib.last_error()
+    assert L.svdq_quantize_act_lowrank_down_mx(*k1t) == _lib.ERR_WORKSPACE
+    k1t[11], k1t[12] = 0x10040, need_k1
+    assert L.svdq_quantize_act_lowrank_down_tiled(*k1t) == _lib.ERR_ALIGN
+    assert L.svdq_quantize_act_lowrank_down_mx(*k1t) == _lib.ERR_ALIGN
     mxa = [A16, A16, A16, A16, A16, A16, 16, None, A16, 1, 16, 16, 64, 16, 0, None]
     bad = list(mxa); bad[3] = None
     assert L.svdq_mx_gemm_lowrank_up(*bad) == _lib.ERR_NULL
@@ -545,6 +557,37 @@ def test_device_entry_points_reject_bad_arguments():
     assert L.svdq_gelu_tanh_f16(A16, A16, 0, None) == _lib.OK          # empty: nothing to do
 
 
+def test_pre_kernel_workspace_sizes():
+    """The split pre-kernel's partial tiles: S slices x rows rounded up to 32 x R
+    fp32 on long rows with more 16-row tiles than compute units (256 here:
+    without a device the library assumes MI355X's), nothing otherwise, and the
+    fused entry points' workspaces grow by exactly that (256-byte aligned)."""
+    L = _lib.lib
+    ws = L.svdq_quantize_act_workspace_bytes
+    # 4608 x 12288: 144 tiles of 32 rows, S = ceil(4 * 256 / 144) = 8
+    assert ws(4608, 12288, 32) == 8 * 4608 * 32 * 4
+    # 4100 x 6144: 129 tiles, ceil(1024 / 129) = 8, capped at G / 16 = 6; rows
+    # rounded up to 4128
+    assert ws(4100, 6144, 16) == 6 * 4128 * 16 * 4
+    # 8200 rows: 257 tiles, S = ceil(1024 / 257) = 4
+    assert ws(8200, 6144, 32) == 4 * 8224 * 32 * 4
+    for shape in [(4608, 3072, 32),     # short rows: 48 groups
+                  (4096, 12288, 32),    # 256 tiles of 16 rows: one per compute unit
+                  (4608, 12288, 0),     # no D
+                  (4608, 12288, 96),    # rank above 64
+                  (4608, 12280, 32), (0, 12288, 32), (4608, 12288, 24)]:
+        assert ws(*shape) == 0, shape
+    for M, K, R in [(4608, 12288, 32), (4608, 3072, 32), (4100, 6144, 16)]:
+        extra = (ws(M, K, R) + 255) // 256 * 256
+        base_t = (((M + 15) // 16) * (K // 64) * 1024 + ((M + 127) // 128) * (K // 64) * 512
+                  + (((M + 15) // 16) * ((R + 31) // 32) * 1024 + 255) // 256 * 256)
+        assert L.svdq_linear_tiled_workspace_bytes(M, K, R) == base_t + extra
+        C = (K + 127) // 128
+        base_m = (((M + 15) // 16) * C * 1024 + ((M + 63) // 64) * C * 256
+                  + (((M + 15) // 16) * ((R + 31) // 32) * 1024 + 255) // 256 * 256)
+        assert L.svdq_linear_mx_workspace_bytes(M, K, R) == base_m + extra
+
+
 def _has_gpu():
     try:
         import torch
@@ -561,7 +604,7 @@ def test_device_entry_points_report_no_device():
     args = [A16, A16, A16, A16, A16, A16, 16, None, A16, 1, 16, 16, 64, 16, 64, 0, None]
     assert L.svdq_w4a4_gemm_lowrank_up(*args) == _lib.ERR_NO_DEVICE
     assert L.svdq_gelu_tanh_f16(A16, A16, 8, None) == _lib.ERR_NO_DEVICE
-    assert L.svdq_quantize_act_lowrank_down_mx(A16, 1, 16, 64, 64, A16, A16, 16, A16, A16, A16, None) == _lib.ERR_NO_DEVICE
+    assert L.svdq_quantize_act_lowrank_down_mx(A16, 1, 16, 64, 64, A16, A16, 16, A16, A16, A16, None, 0, None) == _lib.ERR_NO_DEVICE
     assert L.svdq_mx_gemm_lowrank_up(A16, A16, A16, A16, A16, A16, 16, None, A16, 1, 16, 16, 64, 16, 0, None) == _lib.ERR_NO_DEVICE
     geo = [1, 8, 8, 64, 3, 3, 1, 1]
     assert L.svdq_quantize_act_lowrank_down_conv(A16, 1, *geo, A16, A16, 16, A16, A16, A16, None) == _lib.ERR_NO_DEVICE
