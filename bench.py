@@ -840,10 +840,12 @@ def conv_cpu_baseline(L, X, Wm, prep, bias, budget_s):
 
 def conv_main(args, torch, sq, wl, probe):
     """Step = one UNet convolution on one batch: K1 on the implicit patch matrix
-    of the NHWC image, then K2 (the same kernels as svdq_conv2d, or with
-    --format mxfp4 their MXFP4 versions, as svdq_conv2d_mx)."""
+    of the NHWC image, then K2 (the same kernels as svdq_conv2d_tiled on the
+    tiled INT4 path, svdq_conv2d with --path canonical, or with --format mxfp4
+    their MXFP4 versions, as svdq_conv2d_mx)."""
     L, X, Wc = wl.conv_inputs(args.conv)
     mx = args.format == "mxfp4"
+    tiled = args.path == "tiled" and not mx
     if args.format == "w4a16":
         raise SystemExit("--conv runs the INT4 or MXFP4 format")
     Wm = Wc.reshape(L.K, L.N)
@@ -855,6 +857,8 @@ def conv_main(args, torch, sq, wl, probe):
                                    else np.ascontiguousarray(a)).to("cuda")
     if mx:
         wct, wet = sq.pack_mx_tiles(prep.w_codes, prep.w_scales, K)
+    elif tiled:
+        wct, wet = sq.pack_w4a4_tiles(prep.w_codes, prep.w_scales, K)
     else:
         wct, wet = prep.w_codes, prep.w_scales
     ydt = torch.float16 if L.y_dtype == "f16" else torch.float32
@@ -863,18 +867,25 @@ def conv_main(args, torch, sq, wl, probe):
         s = dict(X=d(X), inv=d(prep.inv_smooth), L1p=d(prep.L1p), L2t=d(prep.L2t), wc=d(wct),
                  ws=d(wet), b=d(bias),
                  D=(torch.empty(max(sq.int4_d_tiled_bytes(M, R), 2) // 2, dtype=torch.int16,
-                                device="cuda") if mx else
+                                device="cuda") if mx or tiled else
                     torch.empty((M, R), dtype=torch.float32, device="cuda")),
                  Y=torch.empty((L.batch, L.OH, L.OW, N), dtype=ydt, device="cuda"))
-        if mx:
+        if tiled:
+            s.update(ac=torch.empty(sq.int4_act_tiled_bytes(M, K), dtype=torch.uint8,
+                                    device="cuda"),
+                     asc=torch.empty(sq.int4_act_scales_tiled_bytes(M, K) // 4,
+                                     dtype=torch.float32, device="cuda"))
+        elif mx:
             s.update(ac=torch.empty(sq.mx_codes_tiled_bytes(M, K), dtype=torch.uint8, device="cuda"),
                      asc=torch.empty(sq.mx_exps_tiled_bytes(M, K), dtype=torch.uint8, device="cuda"))
         else:
             s.update(ac=torch.empty((M, K // 2), dtype=torch.uint8, device="cuda"),
                      asc=torch.empty((M, K // 64), dtype=torch.int16, device="cuda"))
         sets.append(s)
-    k1f = sq.quantize_act_lowrank_down_conv_mx if mx else sq.quantize_act_lowrank_down_conv
-    k2f = sq.mx_gemm_lowrank_up if mx else sq.w4a4_gemm_lowrank_up
+    k1f = (sq.quantize_act_lowrank_down_conv_mx if mx else
+           sq.quantize_act_lowrank_down_conv_tiled if tiled else sq.quantize_act_lowrank_down_conv)
+    k2f = (sq.mx_gemm_lowrank_up if mx else sq.w4a4_gemm_lowrank_up_tiled if tiled else
+           sq.w4a4_gemm_lowrank_up)
 
     class _Runner:
         def launches(self, i):
@@ -913,9 +924,10 @@ def conv_main(args, torch, sq, wl, probe):
                                f"{L.KH}x{L.KW} stride {L.stride} pad {L.pad} -> {N} channels "
                                f"(patch matrix {M}x{K}), rank {R}, {fmt_txt}, Y {L.y_dtype}",
                    "M": M, "K": K, "N": N, "rank": R, "format": args.format,
+                   "path": "tiled" if tiled else ("mxfp4" if mx else "canonical"),
                    "buffer_sets": args.sets},
         F["pct"]: round(100.0 * value / F["peak"], 2),
-        "roofline": {"bound": "mfma", "kernel": F["kname"],
+        "roofline": {"bound": "mfma", "kernel": "k2t_w4a4_kernel" if tiled else F["kname"],
                      "achieved": round(ops / k2_avg / 1e12, 2), "peak": F["peak"],
                      "unit": F["unit"], "frac": round(ops / k2_avg / 1e12 / F["peak"], 4),
                      "traffic": None, "algorithmic_bytes": b2,

@@ -751,6 +751,38 @@ def conv2d(X, KH: int, KW: int, stride: int, pad: int, inv_smooth, L1p, L2t, R: 
           "svdq_conv2d")
 
 
+def quantize_act_lowrank_down_conv_tiled(X, KH: int, KW: int, stride: int, pad: int, inv_smooth,
+                                         L1p, R: int, a_ops_t, a_scales_t, D_t, stream=None):
+    """K1 on the patch matrix of the NHWC image X, writing the tiled INT4 layouts."""
+    B, H, W, Cc, OH, OW, M, K = _conv_shape(X, KH, KW, stride, pad)
+    _down(K, R, inv_smooth, L1p)
+    _act_side_tiled(M, K, R, a_ops_t, a_scales_t, D_t)
+    _on_gpu(X, inv_smooth, L1p if R else None, a_ops_t, a_scales_t, D_t if R else None)
+    check(lib.svdq_quantize_act_lowrank_down_conv_tiled(
+        _tp(X), _dt(X), B, H, W, Cc, KH, KW, stride, pad, _tp(inv_smooth),
+        _tp(L1p) if R else None, R, _tp(a_ops_t), _tp(a_scales_t), _tp(D_t) if R else None,
+        _stream(stream)), "svdq_quantize_act_lowrank_down_conv_tiled")
+
+
+def conv2d_tiled(X, KH: int, KW: int, stride: int, pad: int, inv_smooth, L1p, L2t, R: int,
+                 w_codes_t, w_scales_t, bias, Y, ws, stream=None, activation=None):
+    """The whole convolution on the tiled INT4 path (weights from pack_w4a4_tiles)."""
+    B, H, W, Cc, OH, OW, M, K = _conv_shape(X, KH, KW, stride, pad)
+    N = _conv_out(Y, B, OH, OW)
+    _down(K, R, inv_smooth, L1p)
+    _weights_tiled(N, K, R, w_codes_t, w_scales_t, L2t)
+    _bias(bias, N)
+    _buf("ws", ws, _BYTES + _HALF + _F32, min_bytes=linear_tiled_workspace_bytes(M, K, R))
+    _on_gpu(X, inv_smooth, L1p if R else None, L2t if R else None, w_codes_t, w_scales_t, bias, Y,
+            ws)
+    check(lib.svdq_conv2d_tiled(_tp(X), _dt(X), B, H, W, Cc, KH, KW, stride, pad, _tp(inv_smooth),
+                                _tp(L1p) if R else None, _tp(L2t) if R else None, R,
+                                _tp(w_codes_t), _tp(w_scales_t), _tp(bias), _tp(Y), _dt(Y), N,
+                                _tp(ws), ws.numel() * ws.element_size(), _act(activation),
+                                _stream(stream)),
+          "svdq_conv2d_tiled")
+
+
 def quantize_act_lowrank_down_conv_mx(X, KH: int, KW: int, stride: int, pad: int, inv_smooth,
                                       L1p, R: int, a_codes_t, a_exps_t, D, stream=None):
     """K1-MX on the patch matrix of the NHWC image X: tiled codes and exponents, D."""
@@ -908,16 +940,17 @@ class Conv2d:
     ``prep`` is the INT4 or MXFP4 prep of the K x N weight matrix whose row
     (kh*KW + kw)*C + c is filter tap (kh, kw, c) (a KH x KW x C x N filter
     reshaped). ``Conv2d(prep, KH, KW, stride, pad, bias)(X)`` maps an NHWC
-    image to the NHWC output (batch x OH x OW x N)."""
+    image to the NHWC output (batch x OH x OW x N); with ``tiled=True`` an INT4
+    prep runs the tiled path (svdq_conv2d_tiled)."""
 
     def __init__(self, prep: Prepared, KH: int, KW: int, stride: int = 1, pad: int = 0,
                  bias: Optional[np.ndarray] = None, device="cuda", out_dtype=None,
-                 activation=None):
+                 activation=None, tiled: bool = False):
         if prep.fmt not in ("int4", "mxfp4"):
             raise ValueError("convolutions run in the INT4 and MXFP4 formats")
         if prep.K % (KH * KW) != 0:
             raise ValueError(f"K={prep.K} is not KH*KW*C for a {KH}x{KW} kernel")
-        self.lin = Linear(prep, bias, device, out_dtype, activation)
+        self.lin = Linear(prep, bias, device, out_dtype, activation, tiled=tiled)
         self.KH, self.KW, self.stride, self.pad = KH, KW, stride, pad
         self.C = prep.K // (KH * KW)
 
@@ -933,7 +966,7 @@ class Conv2d:
             Y = torch.empty((B, OH, OW, lin.N), dtype=lin.out_dtype or X.dtype,
                             device=lin.device)
         ws = lin.workspace(max(B * OH * OW, 1))
-        run = conv2d_mx if lin.fmt == "mxfp4" else conv2d
+        run = conv2d_mx if lin.fmt == "mxfp4" else conv2d_tiled if lin.tiled else conv2d
         run(X, self.KH, self.KW, self.stride, self.pad, lin.inv_smooth, lin.L1p, lin.L2t, lin.R,
             lin.w_codes, lin.w_scales, lin.bias, Y, ws, stream, lin.activation)
         return Y

@@ -263,13 +263,16 @@ struct GroupIn {
 // matrix instruction's lane order (lane 16q + r: row r, codes 16q .. 16q+15
 // of the group, widened to int8 16*q in widen_codes' order) and the scale in
 // fp32, in the 128-row band layout of svdq.h.
-template <typename XT, int NCB, int NB, int FMT, bool CONV, int RT, int WV>
+// SPLIT: the instance that splits rows over S workgroups (S is 1 in the others,
+// whose code then carries none of the slice arithmetic).
+template <typename XT, int NCB, int NB, int FMT, bool CONV, int RT, int WV, bool SPLIT = false>
 __global__ __launch_bounds__(64 * WV, WV >= 16 ? 1 : 2) void k1_quant_down_kernel(
     const XT* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
     const float* __restrict__ inv_smooth, const uint16_t* __restrict__ L1p, int R,
     uint8_t* __restrict__ a_codes, void* __restrict__ a_meta, float* __restrict__ D,
-    ConvGeom cg, int S, float* __restrict__ Dpart) {
+    ConvGeom cg, int S_arg, float* __restrict__ Dpart) {
 #pragma clang fp contract(off)
+  const int S = SPLIT ? S_arg : 1;
   constexpr bool MX = FMT == kK1Mx;
   constexpr bool TILED = FMT == kK1Int4Tiled;
   constexpr int WAVES = WV;
@@ -508,7 +511,7 @@ __global__ __launch_bounds__(64 * WV, WV >= 16 ? 1 : 2) void k1_quant_down_kerne
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) s += dpart[w][r_][c_];
-      if (S > 1) {
+      if (SPLIT) {
         // the slice's partial: rows of all tiles (gridDim.x / S of them),
         // slice-major, fp32
         const int64_t rows_all = static_cast<int64_t>(gridDim.x / S) * (16 * RT);
@@ -575,13 +578,33 @@ hipError_t launch_k1_rt(const void* X, int64_t M, int64_t K, int64_t ldx,
                         uint8_t* a_codes, void* a_meta, int fmt, float* D, hipStream_t stream,
                         const ConvGeom* conv, K1Split sp = K1Split{1, nullptr}) {
   const int64_t tiles = (M + 16 * RT - 1) / (16 * RT);
-  const dim3 block(64 * WV), grid(static_cast<unsigned>(tiles * sp.S));
+  // only two-tile workgroups with one group in flight, on the tiled layouts of a
+  // linear layer, have a split instance (the launch rule asks for no other)
+  const bool split = RT == 2 && NB == 1 && NCB <= 4 && sp.S > 1 && conv == nullptr &&
+                     fmt != kK1Int4;
+  const dim3 block(64 * WV), grid(static_cast<unsigned>(tiles * (split ? sp.S : 1)));
   const XT* x = static_cast<const XT*>(X);
   const ConvGeom cg = conv ? *conv : ConvGeom{};
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, x, M, K, ldx, inv_smooth, L1p, R, a_codes,
                        a_meta, D, cg, sp.S, sp.part);
   };
+  if constexpr (RT == 2 && NB == 1 && NCB <= 4) {
+    if (split) {
+      if (fmt == kK1Mx) go(k1_quant_down_kernel<XT, NCB, NB, kK1Mx, false, RT, WV, true>);
+      else go(k1_quant_down_kernel<XT, NCB, NB, kK1Int4Tiled, false, RT, WV, true>);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+      if (R > 0) {
+        // every slice's partial is in place: sum them into D_t
+        const int64_t units = ((M + 15) / 16) * ((R + 31) / 32);
+        hipLaunchKernelGGL(k1_reduce_kernel,
+                           dim3(static_cast<unsigned>((units * 64 + 255) / 256)), dim3(256), 0,
+                           stream, sp.part, sp.S, tiles * 16 * RT, M, R,
+                           reinterpret_cast<uint16_t*>(D));
+      }
+      return hipGetLastError();
+    }
+  }
   if (conv) {
     if (fmt == kK1Mx) go(k1_quant_down_kernel<XT, NCB, NB, kK1Mx, true, RT, WV>);
     else if (fmt == kK1Int4Tiled) go(k1_quant_down_kernel<XT, NCB, NB, kK1Int4Tiled, true, RT, WV>);
@@ -590,14 +613,6 @@ hipError_t launch_k1_rt(const void* X, int64_t M, int64_t K, int64_t ldx,
     if (fmt == kK1Mx) go(k1_quant_down_kernel<XT, NCB, NB, kK1Mx, false, RT, WV>);
     else if (fmt == kK1Int4Tiled) go(k1_quant_down_kernel<XT, NCB, NB, kK1Int4Tiled, false, RT, WV>);
     else go(k1_quant_down_kernel<XT, NCB, NB, kK1Int4, false, RT, WV>);
-  }
-  if (sp.S > 1 && R > 0) {
-    // every slice's partial is in place: sum them into D_t
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    const int64_t units = ((M + 15) / 16) * ((R + 31) / 32);
-    hipLaunchKernelGGL(k1_reduce_kernel, dim3(static_cast<unsigned>((units * 64 + 255) / 256)),
-                       dim3(256), 0, stream, sp.part, sp.S, tiles * 16 * RT, M, R,
-                       reinterpret_cast<uint16_t*>(D));
   }
   return hipGetLastError();
 }

@@ -581,6 +581,27 @@ int svdq_conv2d(const void* X, int x_dtype, int64_t batch, int64_t H, int64_t W,
                 const uint16_t* w_scales, const float* bias, void* Y, int y_dtype, int64_t N,
                 void* ws, size_t ws_bytes, int32_t activation, hipStream_t stream);
 
+/* Device: K1 on the patch matrix writing the tiled INT4 layouts (a_ops_t,
+ * a_scales_t, D_t), as svdq_quantize_act_lowrank_down_tiled would give for the
+ * patch matrix in memory without a workspace (bit-exact). */
+int svdq_quantize_act_lowrank_down_conv_tiled(const void* X, int x_dtype, int64_t batch,
+                                              int64_t H, int64_t W, int64_t C, int32_t KH,
+                                              int32_t KW, int32_t stride, int32_t pad,
+                                              const float* inv_smooth, const uint16_t* L1p,
+                                              int32_t R, uint8_t* a_ops_t, float* a_scales_t,
+                                              uint16_t* D_t, hipStream_t stream);
+
+/* Device: the whole convolution on the tiled INT4 path: K1 on the patch matrix
+ * into `ws` in the tiled layouts, then K2T (svdq_w4a4_gemm_lowrank_up_tiled)
+ * into Y (ldy = N); the weights tiled by svdq_pack_w4a4_tiles. ws: 256-byte
+ * aligned, at least svdq_linear_tiled_workspace_bytes(M, K, R) bytes. */
+int svdq_conv2d_tiled(const void* X, int x_dtype, int64_t batch, int64_t H, int64_t W, int64_t C,
+                      int32_t KH, int32_t KW, int32_t stride, int32_t pad,
+                      const float* inv_smooth, const uint16_t* L1p, const uint16_t* L2t,
+                      int32_t R, const uint8_t* w_codes_t, const float* w_scales_t,
+                      const float* bias, void* Y, int y_dtype, int64_t N, void* ws,
+                      size_t ws_bytes, int32_t activation, hipStream_t stream);
+
 /* Device: K1-MX on the patch matrix: the tiled E2M1 codes and E8M0 exponents
  * and D_t, as svdq_quantize_act_lowrank_down_mx would give for the patch
  * matrix in memory (bit-exact). */

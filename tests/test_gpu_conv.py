@@ -6,9 +6,10 @@ patch matrix, and codes, scales, D and Y against the linear entry points run
 on the same patch matrix materialised in device memory (the two must agree to
 the bit: the same values reach the same arithmetic). Within 2e-3 * max|Y| and
 the strict element-wise bound: Y against the oracle, on every element for the
-small cases and on sampled output pixels at the UNet sizes. The MXFP4
-convolution (K1-MX on the patches, K2-MX) is held to the same bar against the
-oracle's MXFP4 functions."""
+small cases and on sampled output pixels at the UNet sizes. The tiled INT4
+convolution (K1 writing the operand tiles, then K2T) is held to the same bar
+against the tiled linear path and the oracle, and the MXFP4 convolution (K1-MX
+on the patches, K2-MX) against the oracle's MXFP4 functions."""
 import numpy as np
 import pytest
 
@@ -208,6 +209,86 @@ def test_conv_workspace_reuse_smaller_image():
     wc, ws = O.quantize_residual_from_factors(O.conv_weight_matrix(Wc), lam, p.L1, p.L2)
     Yo = O.linear(Xcol, inv, p.L1, p.L2, wc, ws, b, "f16")
     assert rel_err(Ys.cpu().numpy().reshape(small.M, 64), Yo) <= TOL_Y
+
+
+# ---------------------------------------------------------------------------
+# the tiled INT4 convolution: K1 on the implicit patch matrix writing K2T's
+# operand tiles, then K2T
+
+
+def _run_tiled(L: wl.ConvLayer, X, p, bias):
+    """Tiled K1-conv alone (outputs prefilled with canaries), and the whole
+    convolution through Conv2d(tiled=True)."""
+    import bit_post_quantized_smooth_amd as sq
+    torch = torch_mod()
+    M, K, R = L.M, L.K, p.rank
+    Xd = dev(X)
+    ops = torch.full((sq.int4_act_tiled_bytes(M, K),), 0x5A, dtype=torch.uint8, device="cuda")
+    sc = torch.full((sq.int4_act_scales_tiled_bytes(M, K) // 4,), float("nan"),
+                    dtype=torch.float32, device="cuda")
+    Dt = _dt_buffer(M, R)
+    sq.quantize_act_lowrank_down_conv_tiled(Xd, L.KH, L.KW, L.stride, L.pad, dev(p.inv_smooth),
+                                            dev(p.L1p) if R else None, R, ops, sc,
+                                            Dt if R else None)
+    conv = sq.Conv2d(p, L.KH, L.KW, L.stride, L.pad, bias, tiled=True,
+                     out_dtype=torch.float16 if L.y_dtype == "f16" else torch.float32)
+    Y = conv(Xd)
+    torch.cuda.synchronize()
+    assert Y.shape == (L.batch, L.OH, L.OW, p.N)
+    return ops, sc, Dt, Y
+
+
+def _check_tiled_against_linear(L, Xcol, p, bias, got):
+    """The tiled linear entry points on the materialised patch matrix (the
+    pre-kernel without a workspace: unsplit, as the convolution's) give the
+    same bits: operand tiles, scales, D_t and Y."""
+    from test_gpu_tiled import TiledLayer
+    torch = torch_mod()
+    ops, sc, Dt, Y = got
+    d = TiledLayer(Xcol, p, bias, L.y_dtype, k1_workspace=False)
+    d.k1()
+    d.k2()
+    torch.cuda.synchronize()
+    assert torch.equal(ops, d.ops)
+    assert torch.equal(sc.view(torch.int32), d.scales.view(torch.int32))
+    if p.rank:
+        assert torch.equal(Dt, d.D)
+    assert torch.equal(Y.reshape(L.M, p.N).view(torch.uint8), d.Y.view(torch.uint8))
+
+
+@pytest.mark.parametrize("L", EDGE, ids=lambda L: L.name.replace(" ", "_"))
+def test_conv_tiled_edge_every_element(L):
+    X, Wc, b = _edge_inputs(L, seed=L.H * 131 + L.W * 7 + L.C + L.KH + L.stride + 5)
+    p, Xcol, o = _setup(L, X, Wc, b)
+    got = _run_tiled(L, X, p, b)
+    _check_tiled_against_linear(L, Xcol, p, b, got)
+    Yg = got[3].cpu().numpy().reshape(L.M, L.N)
+    Yo = O.linear(Xcol, o.inv, p.L1, p.L2, o.wc, o.ws, b, L.y_dtype)
+    assert rel_err(Yg, Yo) <= TOL_Y
+    Ye, env, jump = oracle_rows_exact(Xcol, o.inv, p, o.wc, o.ws, b, np.arange(L.M))
+    assert_y_strict(Yg, Ye, env, jump, L.y_dtype, L.K // 64, p.rank)
+
+
+@pytest.mark.parametrize("idx", range(1, len(wl.CONV_LAYERS)),
+                         ids=lambda i: wl.CONV_LAYERS[i].name.replace(" ", "_"))
+def test_conv_tiled_unet_sizes(idx):
+    """UNet layers at full size on the tiled path: whole tensors against the tiled
+    linear path on the materialised patch matrix, sampled output pixels (with the
+    image borders) against the oracle."""
+    L, X, Wc = wl.conv_inputs(idx)
+    b = wl.bias(wl.CONV_CFG, idx, L.N)
+    p, Xcol, o = _setup(L, X, Wc, b)
+    got = _run_tiled(L, X, p, b)
+    _check_tiled_against_linear(L, Xcol, p, b, got)
+    rows = sample_rows(L.M, seed=idx + 7)
+    border = [0, L.OW - 1, (L.OH - 1) * L.OW, L.OH * L.OW - 1, L.OH * L.OW, L.M - 1]
+    rows = np.unique(np.concatenate([rows, border]))
+    Yg = got[3].cpu().numpy().reshape(L.M, L.N)
+    Yo = oracle_rows(Xcol, o.inv, p, o.wc, o.ws, b, rows, L.y_dtype)
+    assert rel_err(Yg[rows], Yo) <= TOL_Y
+    Ye, env, jump = oracle_rows_exact(Xcol, o.inv, p, o.wc, o.ws, b, rows)
+    assert_y_strict(Yg[rows], Ye, env, jump, L.y_dtype, L.K // 64, p.rank)
+    assert np.all(np.isfinite(Yg))
 
 
 # ---------------------------------------------------------------------------

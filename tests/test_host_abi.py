@@ -612,6 +612,13 @@ def test_device_entry_points_report_no_device():
     assert L.svdq_conv2d(A16, 1, *geo, A16, A16, A16, 16, A16, A16, None, A16, 1, 16, 0x10000,
                          need_c, 0, None) == _lib.ERR_NO_DEVICE
     assert L.svdq_quantize_act_lowrank_down_conv_mx(A16, 1, *geo, A16, A16, 16, A16, A16, A16, None) == _lib.ERR_NO_DEVICE
+    assert L.svdq_quantize_act_lowrank_down_conv_tiled(A16, 1, *geo, A16, A16, 16, A16, A16, A16,
+                                                       None) == _lib.ERR_NO_DEVICE
+    need_ct = L.svdq_linear_tiled_workspace_bytes(64, 576, 16)
+    assert L.svdq_conv2d_tiled(A16, 1, *geo, A16, A16, A16, 16, A16, A16, None, A16, 1, 16,
+                               0x10000, need_ct, 0, None) == _lib.ERR_NO_DEVICE
+    assert L.svdq_conv2d_tiled(A16, 1, *geo, A16, A16, A16, 16, A16, A16, None, A16, 1, 16,
+                               0x10000, need_ct - 1, 0, None) == _lib.ERR_WORKSPACE
     need_cm = L.svdq_linear_mx_workspace_bytes(64, 576, 16)
     assert L.svdq_conv2d_mx(A16, 1, *geo, A16, A16, A16, 16, A16, A16, None, A16, 1, 16, 0x10000,
                             need_cm, 0, None) == _lib.ERR_NO_DEVICE
