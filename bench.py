@@ -411,6 +411,10 @@ class Sets:
         # the sets: the launches of one stream never overlap
         need = sq.quantize_act_workspace_bytes(M, K, self.R) if (self.tiled or self.mx) else 0
         self.k1ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+        # the tiled GEMM's optional workspace (an under-filled long-K GEMM runs
+        # split along K)
+        need = sq.gemm_tiled_workspace_bytes(M, self.N, K) if self.tiled else 0
+        self.k2ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
 
     def k1(self, i, X=None):
         s = self.sets[i % len(self.sets)]
@@ -436,8 +440,12 @@ class Sets:
         f = (self.sq.mx_gemm_lowrank_up if self.mx
              else self.sq.w4a4_gemm_lowrank_up_tiled if self.tiled
              else self.sq.w4a4_gemm_lowrank_up)
-        f(s["ac"], s["asc"], s["wc"], s["ws"], s["D"] if self.R else None, s["L2t"], self.R, s["b"],
-          Y, self.K)
+        if self.tiled:
+            f(s["ac"], s["asc"], s["wc"], s["ws"], s["D"] if self.R else None, s["L2t"], self.R,
+              s["b"], Y, self.K, workspace=self.k2ws)
+        else:
+            f(s["ac"], s["asc"], s["wc"], s["ws"], s["D"] if self.R else None, s["L2t"], self.R,
+              s["b"], Y, self.K)
 
     def launches(self, i):
         return [("k1", lambda: self.k1(i)), ("k2", lambda: self.k2(i))]
@@ -886,6 +894,10 @@ def conv_main(args, torch, sq, wl, probe):
            sq.quantize_act_lowrank_down_conv_tiled if tiled else sq.quantize_act_lowrank_down_conv)
     k2f = (sq.mx_gemm_lowrank_up if mx else sq.w4a4_gemm_lowrank_up_tiled if tiled else
            sq.w4a4_gemm_lowrank_up)
+    # the tiled GEMM's split along K on under-filled shapes (as svdq_conv2d_tiled
+    # with a workspace that holds it)
+    need = sq.gemm_tiled_workspace_bytes(M, N, K) if tiled else 0
+    k2kw = dict(workspace=torch.empty(need, dtype=torch.uint8, device="cuda")) if need else {}
 
     class _Runner:
         def launches(self, i):
@@ -893,7 +905,7 @@ def conv_main(args, torch, sq, wl, probe):
             return [("k1", lambda: k1f(s["X"], L.KH, L.KW, L.stride, L.pad, s["inv"], s["L1p"], R,
                                        s["ac"], s["asc"], s["D"])),
                     ("k2", lambda: k2f(s["ac"], s["asc"], s["wc"], s["ws"], s["D"], s["L2t"], R,
-                                       s["b"], s["Y"].view(M, N), K))]
+                                       s["b"], s["Y"].view(M, N), K, **k2kw))]
 
     settled = settle(torch, _Runner(), args.settle_ms)
     t_step, _, per = time_steps(torch, _Runner(), args.steps, args.warmup, probe)

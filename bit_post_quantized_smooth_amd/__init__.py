@@ -9,7 +9,7 @@ from .api import (Conv2d, Linear, Prepared, channel_absmax, clock_mark, clock_pr
                   clock_rates, concat_lora, int4_act_tiled_bytes, int4_act_scales_tiled_bytes, int4_d_tiled_bytes,
                   int4_w_codes_tiled_bytes, int4_w_scales_tiled_bytes, linear_tiled,
                   linear_tiled_workspace_bytes, pack_w4a4_tiles, quantize_act_lowrank_down_tiled,
-                  quantize_act_workspace_bytes, w4a4_gemm_lowrank_up_tiled,
+                  quantize_act_workspace_bytes, w4a4_gemm_lowrank_up_tiled, gemm_tiled_workspace_bytes,
                   conv2d, conv2d_mx, conv2d_tiled, conv_out_size, conv_patch_absmax, debug_group_partials,
                   gelu_tanh_f16, linear, linear_canonical, linear_canonical_workspace_bytes,
                   linear_mx, linear_mx_workspace_bytes, pack_lowrank,
@@ -25,7 +25,7 @@ __all__ = ["Conv2d", "Linear", "Prepared", "channel_absmax", "clock_mark", "cloc
            "clock_rates", "concat_lora", "int4_act_tiled_bytes", "int4_act_scales_tiled_bytes", "int4_d_tiled_bytes",
            "int4_w_codes_tiled_bytes", "int4_w_scales_tiled_bytes", "linear_tiled",
            "linear_tiled_workspace_bytes", "pack_w4a4_tiles", "quantize_act_lowrank_down_tiled",
-           "quantize_act_workspace_bytes", "w4a4_gemm_lowrank_up_tiled", "conv2d", "conv2d_mx", "conv2d_tiled",
+           "quantize_act_workspace_bytes", "w4a4_gemm_lowrank_up_tiled", "gemm_tiled_workspace_bytes", "conv2d", "conv2d_mx", "conv2d_tiled",
            "conv_out_size", "conv_patch_absmax", "debug_group_partials",
            "gelu_tanh_f16", "linear", "linear_canonical", "linear_canonical_workspace_bytes",
            "linear_mx", "linear_mx_workspace_bytes", "pack_lowrank",

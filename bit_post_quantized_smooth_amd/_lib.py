@@ -78,8 +78,9 @@ _SIGS = {
     "svdq_quantize_act_workspace_bytes": (C.c_size_t, [_i64, _i64, _i32]),
     "svdq_quantize_act_lowrank_down_tiled": (_int, [_p, _int, _i64, _i64, _i64, _p, _p, _i32,
                                                     _p, _p, _p, _p, C.c_size_t, _p]),
+    "svdq_gemm_tiled_workspace_bytes": (C.c_size_t, [_i64, _i64, _i64]),
     "svdq_w4a4_gemm_lowrank_up_tiled": (_int, [_p, _p, _p, _p, _p, _p, _i32, _p, _p, _int, _i64,
-                                               _i64, _i64, _i64, _i32, _p]),
+                                               _i64, _i64, _i64, _i32, _p, C.c_size_t, _p]),
     "svdq_linear_tiled_workspace_bytes": (C.c_size_t, [_i64, _i64, _i32]),
     "svdq_linear_tiled": (_int, [_p, _int, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _int, _i64,
                                  _i64, _i64, _i64, _p, C.c_size_t, _i32, _p]),

@@ -477,8 +477,8 @@ def quantize_act_workspace_bytes(M: int, K: int, R: int) -> int:
     return int(lib.svdq_quantize_act_workspace_bytes(M, K, R))
 
 
-def _k1_ws(workspace):
-    """(pointer, bytes) of the optional pre-kernel workspace."""
+def _opt_ws(workspace):
+    """(pointer, bytes) of an optional workspace (the pre-kernels', the tiled GEMM's)."""
     if workspace is None:
         return None, 0
     if workspace.dtype != _torch().uint8 or not workspace.is_contiguous():
@@ -497,7 +497,7 @@ def quantize_act_lowrank_down_tiled(X, inv_smooth, L1p, R: int, a_ops_t, a_scale
     _down(K, R, inv_smooth, L1p)
     _act_side_tiled(M, K, R, a_ops_t, a_scales_t, D)
     _on_gpu(X, inv_smooth, L1p if R else None, a_ops_t, a_scales_t, D if R else None, workspace)
-    wp, wb = _k1_ws(workspace)
+    wp, wb = _opt_ws(workspace)
     check(lib.svdq_quantize_act_lowrank_down_tiled(_tp(X), _dt(X), M, K, X.stride(0),
                                                    _tp(inv_smooth), _tp(L1p) if R else None, R,
                                                    _tp(a_ops_t), _tp(a_scales_t),
@@ -506,9 +506,17 @@ def quantize_act_lowrank_down_tiled(X, inv_smooth, L1p, R: int, a_ops_t, a_scale
           "svdq_quantize_act_lowrank_down_tiled")
 
 
+def gemm_tiled_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Bytes of the tiled GEMM's optional workspace on the current device (its
+    split along K); 0 when the shape does not split."""
+    return int(lib.svdq_gemm_tiled_workspace_bytes(M, N, K))
+
+
 def w4a4_gemm_lowrank_up_tiled(a_ops_t, a_scales_t, w_codes_t, w_scales_t, D_t, L2t, R: int, bias,
-                               Y, K: int, stream=None, activation=None):
-    """K2 on the tiled layouts (D_t: the pre-kernel's fp16 D in operand order)."""
+                               Y, K: int, stream=None, activation=None, workspace=None):
+    """K2 on the tiled layouts (D_t: the pre-kernel's fp16 D in operand order).
+    workspace: None, or gemm_tiled_workspace_bytes(M, N, K) bytes (uint8) on the
+    same device, with which an under-filled long-K GEMM runs split along K."""
     D = D_t
     _mat("Y", Y, None, None)
     M, N = Y.shape
@@ -516,12 +524,13 @@ def w4a4_gemm_lowrank_up_tiled(a_ops_t, a_scales_t, w_codes_t, w_scales_t, D_t, 
     _weights_tiled(N, K, R, w_codes_t, w_scales_t, L2t)
     _bias(bias, N)
     _on_gpu(a_ops_t, a_scales_t, w_codes_t, w_scales_t, D if R else None, L2t if R else None, bias,
-            Y)
+            Y, workspace)
+    wp, wb = _opt_ws(workspace)
     check(lib.svdq_w4a4_gemm_lowrank_up_tiled(_tp(a_ops_t), _tp(a_scales_t), _tp(w_codes_t),
                                               _tp(w_scales_t), _tp(D) if R else None,
                                               _tp(L2t) if R else None, R, _tp(bias), _tp(Y),
                                               _dt(Y), M, N, K, Y.stride(0), _act(activation),
-                                              _stream(stream)),
+                                              wp, wb, _stream(stream)),
           "svdq_w4a4_gemm_lowrank_up_tiled")
 
 
@@ -573,7 +582,7 @@ def quantize_act_lowrank_down_mx(X, inv_smooth, L1p, R: int, a_codes_t, a_exps_t
     _down(K, R, inv_smooth, L1p)
     _act_side(M, K, R, a_codes_t, a_exps_t, D, mx=True)
     _on_gpu(X, inv_smooth, L1p if R else None, a_codes_t, a_exps_t, D if R else None, workspace)
-    wp, wb = _k1_ws(workspace)
+    wp, wb = _opt_ws(workspace)
     check(lib.svdq_quantize_act_lowrank_down_mx(_tp(X), _dt(X), M, K, X.stride(0), _tp(inv_smooth),
                                                 _tp(L1p) if R else None, R, _tp(a_codes_t),
                                                 _tp(a_exps_t), _tp(D) if R else None, wp, wb,
@@ -908,7 +917,9 @@ class Linear:
         elif self.fmt == "mxfp4":
             need = linear_mx_workspace_bytes(M, self.K, self.R)
         elif self.tiled:
-            need = linear_tiled_workspace_bytes(M, self.K, self.R)
+            # the layer's intermediates, then room for the GEMM's split along K
+            need = (linear_tiled_workspace_bytes(M, self.K, self.R)
+                    + gemm_tiled_workspace_bytes(M, self.N, self.K))
         else:
             need = linear_workspace_bytes(M, self.K, self.R)
         if self.ws is None or self.ws.numel() < need:

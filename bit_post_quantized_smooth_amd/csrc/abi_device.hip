@@ -412,12 +412,47 @@ int check_k2t_shape(int64_t M, int64_t N, int64_t K, const char* fn) {
 }
 }  // namespace
 
+size_t svdq_gemm_tiled_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) return 0;
+  return k2t_split_bytes(M, N, K);
+}
+
+namespace {
+// The optional workspace of the tiled GEMM: null (unsplit), or at least
+// svdq_gemm_tiled_workspace_bytes and 256-byte aligned. Returns the partial
+// buffer to hand to the launcher (null: run unsplit).
+int k2t_workspace(void* ws, size_t ws_bytes, int64_t M, int64_t N, int64_t K, const char* fn,
+                  float** part) {
+  *part = nullptr;
+  if (ws == nullptr) return SVDQ_OK;
+  const size_t need = k2t_split_bytes(M, N, K);
+  if (ws_bytes < need) {
+    set_error("%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    return SVDQ_ERR_WORKSPACE;
+  }
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) {
+    set_error("%s: workspace must be 256-byte aligned", fn);
+    return SVDQ_ERR_ALIGN;
+  }
+  *part = need > 0 ? static_cast<float*>(ws) : nullptr;
+  return SVDQ_OK;
+}
+
+// The fused tiled entry points: the tiled GEMM's partials follow the layout's
+// `total` bytes when the caller's workspace holds them (else unsplit).
+float* k2t_part_after(void* ws, size_t ws_bytes, size_t total, int64_t M, int64_t N, int64_t K) {
+  const size_t need = k2t_split_bytes(M, N, K);
+  if (need == 0 || ws_bytes < total + need) return nullptr;
+  return reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + total);
+}
+}  // namespace
+
 int svdq_w4a4_gemm_lowrank_up_tiled(const uint8_t* a_ops_t, const float* a_scales_t,
                                     const uint8_t* w_codes_t, const float* w_scales_t,
                                     const uint16_t* D_t, const uint16_t* L2t, int32_t R,
                                     const float* bias, void* Y, int y_dtype, int64_t M, int64_t N,
-                                    int64_t K, int64_t ldy, int32_t activation,
-                                    hipStream_t stream) {
+                                    int64_t K, int64_t ldy, int32_t activation, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
   clear_error();
   const char* fn = "svdq_w4a4_gemm_lowrank_up_tiled";
   if (int s = validate_k2(a_ops_t, a_scales_t, w_codes_t, w_scales_t,
@@ -426,10 +461,12 @@ int svdq_w4a4_gemm_lowrank_up_tiled(const uint8_t* a_ops_t, const float* a_scale
     return s;
   if (int s = check_k2t_shape(M, N, K, fn)) return s;
   if (int s = check_activation(activation, fn)) return s;
+  float* part = nullptr;
+  if (int s = k2t_workspace(workspace, workspace_bytes, M, N, K, fn, &part)) return s;
   if (int s = device_ready()) return s;
   return check_hip(launch_k2t(a_ops_t, a_scales_t, w_codes_t, w_scales_t, D_t, L2t, R, bias, Y,
                               y_dtype == SVDQ_F16, M, N, K, ldy,
-                              activation == SVDQ_ACT_GELU_TANH, stream),
+                              activation == SVDQ_ACT_GELU_TANH, stream, part),
                    "svdq_w4a4_gemm_lowrank_up_tiled launch");
 }
 
@@ -480,7 +517,7 @@ int svdq_linear_tiled(const void* X, int x_dtype, int64_t ldx, const float* inv_
   return check_hip(launch_k2t(a_ops, a_scales, w_codes_t, w_scales_t,
                               reinterpret_cast<const uint16_t*>(D), L2t, R, bias, Y,
                               y_dtype == SVDQ_F16, M, N, K, ldy, activation == SVDQ_ACT_GELU_TANH,
-                              stream),
+                              stream, k2t_part_after(ws, ws_bytes, L.total, M, N, K)),
                    "svdq_linear_tiled K2 launch");
 }
 
@@ -702,7 +739,8 @@ int svdq_conv2d_tiled(const void* X, int x_dtype, int64_t batch, int64_t H, int6
   return check_hip(launch_k2t(a_ops, a_scales, w_codes_t, w_scales_t,
                               reinterpret_cast<const uint16_t*>(D), L2t, R, bias, Y,
                               y_dtype == SVDQ_F16, cs.M, N, cs.K, N,
-                              activation == SVDQ_ACT_GELU_TANH, stream),
+                              activation == SVDQ_ACT_GELU_TANH, stream,
+                              k2t_part_after(ws, ws_bytes, L.total, cs.M, N, cs.K)),
                    "svdq_conv2d_tiled K2 launch");
 }
 

@@ -47,10 +47,18 @@ hipError_t launch_k2(const uint8_t* a_codes, const uint16_t* a_scales, const uin
 // K2T on the tiled INT4 layouts (svdq.h): a_ops / a_scales from the
 // pre-kernel's tiled instance, the weight codes and scale pairs from
 // svdq_pack_w4a4_tiles.
+// part: null, or k2t_split_bytes(M, N, K) bytes (16-byte aligned) for the
+// fp32 partial tiles of the split-along-K kernel; without it every shape runs
+// unsplit.
 hipError_t launch_k2t(const uint8_t* a_ops, const float* a_scales, const uint8_t* w_codes_t,
                       const float* w_scales_t, const uint16_t* Dt, const uint16_t* L2t, int R,
                       const float* bias, void* Y, bool y_f16, int64_t M, int64_t N, int64_t K,
-                      int64_t ldy, bool gelu, hipStream_t stream);
+                      int64_t ldy, bool gelu, hipStream_t stream, float* part = nullptr);
+
+// Slices along K that K2T uses for this shape on the current device (1: not
+// split) and the bytes of its partial tiles (0 when not split).
+int k2t_ksplit(int64_t M, int64_t N, int64_t K);
+size_t k2t_split_bytes(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_k2_mx(const uint8_t* a_codes, const uint8_t* a_e8m0, const uint8_t* w_codes,
                         const uint8_t* w_e8m0, const uint16_t* Dt, const uint16_t* L2t, int R,

@@ -93,6 +93,7 @@ struct Shape {
   static_assert(COPIES * (KAHEAD - 1) < 16, "vmcnt field");
 };
 constexpr int kWaitAll = 0x0070;                    // vmcnt(0) lgkmcnt(0)
+constexpr int kPartTile = 128 * 128;                // floats of one partial tile
 
 template <int RB, int CB>
 struct TScales {
@@ -183,7 +184,10 @@ __device__ __forceinline__ void lowrank_up_tiled(v4f (&acc)[RB][CB],
 }
 
 // One tile of Y: rows m0 .. m0 + 16*RB - 1, columns n0 .. n0 + 64*CB - 1.
-template <int RB, int CB, bool Y_F16, bool GELU>
+// PART: groups g_lo .. g_hi - 1 only, the low-rank term only when `lowrank`,
+// and the fp32 sums go to `part` (16384 floats, lane order: block (i, j) of
+// wave w at ((w*RB + i)*CB + j) * 256) for k2t_reduce_kernel; no epilogue.
+template <int RB, int CB, bool Y_F16, bool GELU, bool PART = false>
 __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __restrict__ a_ops,
                                        const float* __restrict__ a_scales,
                                        const uint8_t* __restrict__ w_codes,
@@ -192,12 +196,14 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
                                        const uint16_t* __restrict__ L2t, int R,
                                        const float* __restrict__ bias, void* __restrict__ Y,
                                        int64_t M, int64_t N, int64_t K, int64_t ldy, int64_t m0,
-                                       int64_t n0) {
+                                       int64_t n0, int g_lo = 0, int g_hi = -1,
+                                       bool lowrank = true, float* __restrict__ part = nullptr) {
   using S = Shape<RB, CB>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int rl = lane & 15, q = lane >> 4;
   const int G = static_cast<int>(K / kGroup);
+  const int g_first = g_lo, g_end = g_hi < 0 ? G : g_hi;   // this tile's groups
   const int64_t Mb = (M + 15) / 16, Ns = (N + 31) / 32;
   const int64_t nw = n0 + S::WCOLS * wave;          // the wave's first column
   const int rb0 = static_cast<int>((m0 % 128) / 16);   // the tile's first row block in its band
@@ -221,7 +227,7 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
   const uint32_t lo4 = 4u * static_cast<uint32_t>(lane);
 
   auto copy = [&](TStage& s, int g) {
-    g = g < G ? g : G - 1;
+    g = g < g_end ? g : g_end - 1;
     const int64_t o = static_cast<int64_t>(g) * kBlk;
 #pragma unroll
     for (int c = 0; c < S::ACOPY; ++c)
@@ -244,7 +250,7 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
   };
 
 #pragma unroll
-  for (int c = 0; c < KAHEAD; ++c) copy(st[c], c);
+  for (int c = 0; c < KAHEAD; ++c) copy(st[c], g_first + c);
 
   // the low-rank branch starts the accumulators while the first groups copy
   v4f acc[RB][CB];
@@ -252,7 +258,7 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
   for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int j = 0; j < CB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  lowrank_up_tiled<RB, CB>(acc, Dt, L2t, R, M, N, m0, nw);
+  if (!PART || lowrank) lowrank_up_tiled<RB, CB>(acc, Dt, L2t, R, M, N, m0, nw);
 
   // Iteration g computes group g from stage g % KSTAGES. Its barrier follows
   // this wave's wait for its own copies of group g, so after it every copy of
@@ -263,7 +269,7 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
   // the kernel at three waves per SIMD.
   const v4i seed = v4i{kMagicSeed, kMagicSeed, kMagicSeed, kMagicSeed};
   int sg = 0, sp = KSTAGES - 1;                 // stages of groups g and g-1
-  for (int g = 0; g < G; ++g) {
+  for (int g = g_first; g < g_end; ++g) {
     const TStage& s = st[sg];
     __builtin_amdgcn_s_waitcnt(S::WAIT_AHEAD);
     __builtin_amdgcn_s_barrier();
@@ -326,6 +332,14 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
   // before the LDS is used for the output
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __builtin_amdgcn_s_barrier();
+  if constexpr (PART) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+        *reinterpret_cast<v4f*>(part + (((wave * RB + i) * CB + j) * 64 + lane) * 4) = acc[i][j];
+    return;
+  }
   if constexpr (Y_F16 && RB == 8 && CB == 2) {
     static_assert(sizeof(TStage) * KSTAGES >= 128 * 256, "a 128 x 128 fp16 tile in LDS");
     if (m0 + 128 <= M && n0 + 128 <= N &&
@@ -377,34 +391,93 @@ __device__ __forceinline__ void tile_t(TStage (&st)[KSTAGES], const uint8_t* __r
 // banded order; the rest take the remaining tiles in `split` pieces (2: 64 x
 // 128 halves, 4: 64 x 64 quarters). A piece wholly outside Y returns at once
 // (the same for every wave of the workgroup, before any barrier).
-template <bool Y_F16, bool GELU>
+// PART: split along K. Every tile is taken by `split` workgroups, slice s
+// computing groups s*G/split .. (s+1)*G/split - 1 (slice 0 with the low-rank
+// term) into its fp32 partial tile in `partial`; k2t_reduce_kernel finishes Y.
+template <bool Y_F16, bool GELU, bool PART = false>
 __global__ __launch_bounds__(NT, 3) void k2t_w4a4_kernel(
     const uint8_t* __restrict__ a_ops, const float* __restrict__ a_scales,
     const uint8_t* __restrict__ w_codes, const float* __restrict__ w_scales,
     const uint16_t* __restrict__ Dt, const uint16_t* __restrict__ L2t, int R,
     const float* __restrict__ bias, void* __restrict__ Y, int64_t M, int64_t N, int64_t K,
-    int64_t ldy, int tiles_m, int tiles_n, int n_full, int split) {
+    int64_t ldy, int tiles_m, int tiles_n, int n_full, int split, float* __restrict__ partial) {
   __shared__ TStage st[KSTAGES];
   const int b = static_cast<int>(blockIdx.x);
   int tm, tn;
-  if (b < n_full) {
-    banded_tile(xcd_contiguous(b, n_full), tiles_m, tiles_n, tm, tn);
-    tile_t<8, 2, Y_F16, GELU>(st, a_ops, a_scales, w_codes, w_scales, Dt, L2t, R, bias, Y, M, N, K,
-                              ldy, static_cast<int64_t>(tm) * 128, static_cast<int64_t>(tn) * 128);
+  if constexpr (PART) {
+    const int T = tiles_m * tiles_n;
+    const int unit = xcd_contiguous(b, T * split);
+    const int tile = unit / split, slice = unit - tile * split;
+    banded_tile(tile, tiles_m, tiles_n, tm, tn);
+    const int G = static_cast<int>(K / kGroup);
+    tile_t<8, 2, Y_F16, GELU, true>(st, a_ops, a_scales, w_codes, w_scales, Dt, L2t, R, bias, Y, M,
+                                    N, K, ldy, static_cast<int64_t>(tm) * 128,
+                                    static_cast<int64_t>(tn) * 128, slice * G / split,
+                                    (slice + 1) * G / split, slice == 0,
+                                    partial + (static_cast<int64_t>(slice) * T + tile) * kPartTile);
     return;
+  } else {
+    if (b < n_full) {
+      banded_tile(xcd_contiguous(b, n_full), tiles_m, tiles_n, tm, tn);
+      tile_t<8, 2, Y_F16, GELU>(st, a_ops, a_scales, w_codes, w_scales, Dt, L2t, R, bias, Y, M, N,
+                                K, ldy, static_cast<int64_t>(tm) * 128,
+                                static_cast<int64_t>(tn) * 128);
+      return;
+    }
+    const int u = b - n_full;
+    banded_tile(n_full + u / split, tiles_m, tiles_n, tm, tn);
+    const int part = u % split;
+    const int64_t m0 = static_cast<int64_t>(tm) * 128 + 64 * (split == 2 ? part : part >> 1);
+    const int64_t n0 = static_cast<int64_t>(tn) * 128 + (split == 4 ? 64 * (part & 1) : 0);
+    if (m0 >= M || n0 >= N) return;
+    if (split == 2)
+      tile_t<4, 2, Y_F16, GELU>(st, a_ops, a_scales, w_codes, w_scales, Dt, L2t, R, bias, Y, M, N,
+                                K, ldy, m0, n0);
+    else
+      tile_t<4, 1, Y_F16, GELU>(st, a_ops, a_scales, w_codes, w_scales, Dt, L2t, R, bias, Y, M, N,
+                                K, ldy, m0, n0);
   }
-  const int u = b - n_full;
-  banded_tile(n_full + u / split, tiles_m, tiles_n, tm, tn);
-  const int part = u % split;
-  const int64_t m0 = static_cast<int64_t>(tm) * 128 + 64 * (split == 2 ? part : part >> 1);
-  const int64_t n0 = static_cast<int64_t>(tn) * 128 + (split == 4 ? 64 * (part & 1) : 0);
-  if (m0 >= M || n0 >= N) return;
-  if (split == 2)
-    tile_t<4, 2, Y_F16, GELU>(st, a_ops, a_scales, w_codes, w_scales, Dt, L2t, R, bias, Y, M, N, K,
-                              ldy, m0, n0);
-  else
-    tile_t<4, 1, Y_F16, GELU>(st, a_ops, a_scales, w_codes, w_scales, Dt, L2t, R, bias, Y, M, N, K,
-                              ldy, m0, n0);
+}
+
+// Y from the partial tiles of the split kernel: the S slices summed in slice
+// order, then bias, the activation and one rounding, as the unsplit
+// epilogue does. One thread per 4 consecutive outputs (a lane's float4).
+template <bool Y_F16, bool GELU>
+__global__ __launch_bounds__(256) void k2t_reduce_kernel(const float* __restrict__ part, int S,
+                                                         int T, int tiles_m, int tiles_n,
+                                                         const float* __restrict__ bias,
+                                                         void* __restrict__ Y, int64_t M,
+                                                         int64_t N, int64_t ldy) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= static_cast<int64_t>(T) * (kPartTile / 4)) return;
+  const int tile = static_cast<int>(t / (kPartTile / 4));
+  const int r = static_cast<int>(t - static_cast<int64_t>(tile) * (kPartTile / 4));
+  const int lane = r & 63, blk = r >> 6;             // blk = (wave*8 + i)*2 + j
+  const int j = blk & 1, i = (blk >> 1) & 7, w = blk >> 4;
+  int tm, tn;
+  banded_tile(tile, tiles_m, tiles_n, tm, tn);
+  const int64_t m = static_cast<int64_t>(tm) * 128 + 16 * i + (lane & 15);
+  const int64_t n = static_cast<int64_t>(tn) * 128 + 32 * w + 16 * j + 4 * (lane >> 4);
+  if (m >= M || n >= N) return;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int sl = 0; sl < S; ++sl) {
+    const float4 p = *reinterpret_cast<const float4*>(
+        part + ((static_cast<int64_t>(sl) * T + tile) * (kPartTile / 4) + r) * 4);
+    v[0] += p.x;
+    v[1] += p.y;
+    v[2] += p.z;
+    v[3] += p.w;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (n + e >= N) break;
+    float y = v[e] + (bias != nullptr ? bias[n + e] : 0.f);
+    if constexpr (GELU) y = gelu_tanh_f32(y);
+    if constexpr (Y_F16)
+      static_cast<uint16_t*>(Y)[m * ldy + n + e] = f2h(y);
+    else
+      static_cast<float*>(Y)[m * ldy + n + e] = y;
+  }
 }
 
 // Workgroups of this kernel resident at once on the current device (compute
@@ -429,13 +502,60 @@ int k2t_slots() {
 
 }  // namespace
 
+// Split along K when the tiles fill at most a quarter of the resident
+// workgroup slots and the rows hold at least 32 groups (the UNet's 32x32
+// convolution: 160 tiles for 768 slots, each running 180 groups in series):
+// `split` = slots / tiles, at most G / 16 and 8, so that the slices about
+// fill the slots. The partial tiles cost a pass over S x 64 KB per tile;
+// measured on MI355X inside the step, the 32x32 convolution's GEMM took 60.6
+// against 75.5 us split in 4, the 64x64 one (320 tiles, 90 groups) 66.8
+// against 56.5 us split in 2, hence the quarter.
+int k2t_ksplit(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < kGroup) return 1;
+  const int64_t T = ((M + 127) / 128) * ((N + 127) / 128), slots = k2t_slots(), G = K / kGroup;
+  if (4 * T > slots || G < 32) return 1;
+  int64_t S = slots / T;
+  if (S > G / 16) S = G / 16;
+  if (S > 8) S = 8;
+  return S < 2 ? 1 : static_cast<int>(S);
+}
+
+size_t k2t_split_bytes(int64_t M, int64_t N, int64_t K) {
+  const int S = k2t_ksplit(M, N, K);
+  if (S == 1) return 0;
+  const int64_t T = ((M + 127) / 128) * ((N + 127) / 128);
+  return static_cast<size_t>(S) * static_cast<size_t>(T) * kPartTile * 4;
+}
+
 hipError_t launch_k2t(const uint8_t* a_ops, const float* a_scales, const uint8_t* w_codes_t,
                       const float* w_scales_t, const uint16_t* Dt, const uint16_t* L2t, int R,
                       const float* bias, void* Y, bool y_f16, int64_t M, int64_t N, int64_t K,
-                      int64_t ldy, bool gelu, hipStream_t stream) {
+                      int64_t ldy, bool gelu, hipStream_t stream, float* part) {
   const int tiles_m = static_cast<int>((M + 127) / 128);
   const int tiles_n = static_cast<int>((N + 127) / 128);
   const int T = tiles_m * tiles_n;
+  const int KS = part != nullptr ? k2t_ksplit(M, N, K) : 1;
+  if (KS > 1) {
+    const dim3 grid(static_cast<unsigned>(T * KS)), block(NT);
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, grid, block, 0, stream, a_ops, a_scales, w_codes_t, w_scales_t,
+                         Dt, L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n, 0, KS, part);
+    };
+    auto red = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(T * (kPartTile / 4 / 256))),
+                         dim3(256), 0, stream, part, KS, T, tiles_m, tiles_n, bias, Y, M, N, ldy);
+    };
+    if (y_f16)
+      gelu ? go(k2t_w4a4_kernel<true, true, true>) : go(k2t_w4a4_kernel<true, false, true>);
+    else
+      gelu ? go(k2t_w4a4_kernel<false, true, true>) : go(k2t_w4a4_kernel<false, false, true>);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    if (y_f16)
+      gelu ? red(k2t_reduce_kernel<true, true>) : red(k2t_reduce_kernel<true, false>);
+    else
+      gelu ? red(k2t_reduce_kernel<false, true>) : red(k2t_reduce_kernel<false, false>);
+    return hipGetLastError();
+  }
   // the tiles of a thin last round are cut into halves or quarters, so that
   // they fill more of the resident workgroup slots
   const int S = k2t_slots();
@@ -446,7 +566,7 @@ hipError_t launch_k2t(const uint8_t* a_ops, const float* a_scales, const uint8_t
   const dim3 grid(static_cast<unsigned>(n_full + split * n_split)), block(NT);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, a_ops, a_scales, w_codes_t, w_scales_t, Dt,
-                       L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n, n_full, split);
+                       L2t, R, bias, Y, M, N, K, ldy, tiles_m, tiles_n, n_full, split, nullptr);
   };
   if (y_f16)
     gelu ? go(k2t_w4a4_kernel<true, true>) : go(k2t_w4a4_kernel<true, false>);

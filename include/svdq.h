@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 11
+#define SVDQ_ABI_VERSION 12
 
 /* status codes */
 enum {
@@ -372,16 +372,29 @@ int svdq_quantize_act_lowrank_down_tiled(const void* X, int x_dtype, int64_t M, 
                                          float* a_scales_t, uint16_t* D_t, void* workspace,
                                          size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of the tiled GEMM's optional workspace for this shape on the current
+ * device: when its 128 x 128 tiles fill at most a quarter of the resident
+ * workgroup slots and K holds at least 32 groups (an under-filled long-K
+ * GEMM, e.g. the UNet's 32x32 convolution), every tile is split along K over
+ * several workgroups whose fp32 partial tiles a second pass sums in slice
+ * order before the bias, the activation and the rounding. 0 when the shape is
+ * not split or the sizes are invalid. */
+size_t svdq_gemm_tiled_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
 /* Device: K2 (svdq_w4a4_gemm_lowrank_up: the same exact int32 group partials,
  * fp32 rescale, low-rank up-projection, bias and activation) on the tiled
  * layouts. The order of the fp32 sums differs from K2's (the low-rank term
- * first), within the same rounding bound. */
+ * first), within the same rounding bound. workspace: NULL, or at least
+ * svdq_gemm_tiled_workspace_bytes(M, N, K) bytes, 256-byte aligned (else
+ * SVDQ_ERR_WORKSPACE / SVDQ_ERR_ALIGN); with it a shape that splits runs split
+ * along K (the same sums in another order, within the same bound), without it
+ * unsplit. */
 int svdq_w4a4_gemm_lowrank_up_tiled(const uint8_t* a_ops_t, const float* a_scales_t,
                                     const uint8_t* w_codes_t, const float* w_scales_t,
                                     const uint16_t* D_t, const uint16_t* L2t, int32_t R,
                                     const float* bias, void* Y, int y_dtype, int64_t M, int64_t N,
-                                    int64_t K, int64_t ldy, int32_t activation,
-                                    hipStream_t stream);
+                                    int64_t K, int64_t ldy, int32_t activation, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace svdq_linear_tiled needs on the current device: a_ops_t,
  * a_scales_t, D_t and the split pre-kernel's partial D tiles (see
@@ -391,7 +404,9 @@ size_t svdq_linear_tiled_workspace_bytes(int64_t M, int64_t K, int32_t R);
 
 /* The whole layer on the tiled path: the tiled K1 then the tiled K2 on
  * `stream`, intermediates in `ws` (256-byte aligned); the weights tiled by
- * svdq_pack_w4a4_tiles. */
+ * svdq_pack_w4a4_tiles. When `ws` holds svdq_gemm_tiled_workspace_bytes(M, N,
+ * K) more bytes after svdq_linear_tiled_workspace_bytes(M, K, R), an
+ * under-filled GEMM runs split along K there. */
 int svdq_linear_tiled(const void* X, int x_dtype, int64_t ldx, const float* inv_smooth,
                       const uint16_t* L1p, const uint16_t* L2t, int32_t R,
                       const uint8_t* w_codes_t, const float* w_scales_t, const float* bias,
@@ -594,7 +609,9 @@ int svdq_quantize_act_lowrank_down_conv_tiled(const void* X, int x_dtype, int64_
 /* Device: the whole convolution on the tiled INT4 path: K1 on the patch matrix
  * into `ws` in the tiled layouts, then K2T (svdq_w4a4_gemm_lowrank_up_tiled)
  * into Y (ldy = N); the weights tiled by svdq_pack_w4a4_tiles. ws: 256-byte
- * aligned, at least svdq_linear_tiled_workspace_bytes(M, K, R) bytes. */
+ * aligned, at least svdq_linear_tiled_workspace_bytes(M, K, R) bytes, and as
+ * for svdq_linear_tiled svdq_gemm_tiled_workspace_bytes(M, N, K) more for the
+ * split along K. */
 int svdq_conv2d_tiled(const void* X, int x_dtype, int64_t batch, int64_t H, int64_t W, int64_t C,
                       int32_t KH, int32_t KW, int32_t stride, int32_t pad,
                       const float* inv_smooth, const uint16_t* L1p, const uint16_t* L2t,

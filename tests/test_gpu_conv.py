@@ -240,12 +240,13 @@ def _run_tiled(L: wl.ConvLayer, X, p, bias):
 
 def _check_tiled_against_linear(L, Xcol, p, bias, got):
     """The tiled linear entry points on the materialised patch matrix (the
-    pre-kernel without a workspace: unsplit, as the convolution's) give the
-    same bits: operand tiles, scales, D_t and Y."""
+    pre-kernel without a workspace: unsplit, as the convolution's; the GEMM with
+    its workspace, split along K where Conv2d splits it) give the same bits:
+    operand tiles, scales, D_t and Y."""
     from test_gpu_tiled import TiledLayer
     torch = torch_mod()
     ops, sc, Dt, Y = got
-    d = TiledLayer(Xcol, p, bias, L.y_dtype, k1_workspace=False)
+    d = TiledLayer(Xcol, p, bias, L.y_dtype, k1_workspace=False, k2_workspace=True)
     d.k1()
     d.k2()
     torch.cuda.synchronize()

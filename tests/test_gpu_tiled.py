@@ -37,7 +37,7 @@ def sq_mod():
 class TiledLayer:
     """Device buffers of one layer on the tiled path (weights packed by the library)."""
 
-    def __init__(self, X, p, bias, y_dtype="f16", k1_workspace=True):
+    def __init__(self, X, p, bias, y_dtype="f16", k1_workspace=True, k2_workspace=False):
         torch = torch_mod()
         sq = sq_mod()
         self.M, self.K = X.shape
@@ -64,6 +64,11 @@ class TiledLayer:
         need = sq.quantize_act_workspace_bytes(self.M, self.K, self.R)
         self.k1ws = (torch.full((max(need, 256),), 0xA5, dtype=torch.uint8, device="cuda")
                      if k1_workspace else None)
+        # the GEMM's optional workspace (an under-filled long-K shape runs split
+        # along K), filled with garbage
+        need = sq.gemm_tiled_workspace_bytes(self.M, self.N, self.K)
+        self.k2ws = (torch.full((max(need, 256),), 0xA5, dtype=torch.uint8, device="cuda")
+                     if k2_workspace else None)
 
     def k1(self):
         sq_mod().quantize_act_lowrank_down_tiled(self.X, self.inv, self.L1p, self.R, self.ops,
@@ -73,7 +78,8 @@ class TiledLayer:
     def k2(self, activation=None):
         sq_mod().w4a4_gemm_lowrank_up_tiled(self.ops, self.scales, self.wc, self.ws,
                                             self.D if self.R else None, self.L2t, self.R,
-                                            self.bias, self.Y, self.K, activation=activation)
+                                            self.bias, self.Y, self.K, activation=activation,
+                                            workspace=self.k2ws)
 
 
 def _check_k1_tiled(X, inv_o, p, K, d):
@@ -265,3 +271,59 @@ def test_mlp_chain_tiled_fused_gelu():
     Yd = down(up(dev(X)))
     torch.cuda.synchronize()
     assert rel_err(Yd.cpu().numpy()[rows], Yo) <= 1e-2
+
+
+# Under-filled long-K GEMMs (at most half of the resident workgroup slots,
+# at least 32 groups) run split along K when the GEMM gets its workspace:
+# slice s of a tile sums groups s*G/S .. (s+1)*G/S - 1 (slice 0 with the
+# low-rank term) into an fp32 partial tile, and a second pass sums the slices
+# in order before the bias, the activation and the rounding. Y must meet the
+# oracle's element-wise bound, the fused entry point with room for the split
+# must give the same bits as the two calls, and the unsplit kernel the same
+# bound (its sums run in another order).
+SPLITK = [
+    # M, K, N, R, x, y, bias, activation: 16 x 5 tiles, S = 4; 8 x 5 tiles, S = 2
+    (2000, 4096, 600, 32, "f16", "f16", True, None),
+    (1024, 2560, 640, 16, "f32", "f32", False, "gelu_tanh"),
+]
+
+
+@pytest.mark.parametrize("case", SPLITK, ids=lambda c: "x".join(map(str, c[:4])) + f"_{c[5]}")
+def test_gemm_split_along_k(case):
+    sq = sq_mod()
+    torch = torch_mod()
+    M, K, N, R, xdt, ydt, use_bias, act = case
+    X, W, b = _edge_inputs(M, K, N, R, xdt, seed=M + K + N + R + 9)
+    lam = sq.smoothing_factors(sq.channel_absmax(X), W)
+    p = sq.prepare_weights(W, lam, R)
+    bias = b if use_bias else None
+    _, inv_o, wc, ws = oracle_prep(X, W, p)
+    assert sq.gemm_tiled_workspace_bytes(M, N, K) > 0        # the shape splits on MI355X
+    d = TiledLayer(X, p, bias, ydt, k2_workspace=True)
+    d.k1()
+    d.k2(activation=act)
+    torch.cuda.synchronize()
+    Yg = d.Y.cpu().numpy()
+    assert np.all(np.isfinite(Yg))
+    rows = sample_rows(M, seed=M + N)
+    if act is None:
+        Ye, env, jump = oracle_rows_exact(X, inv_o, p, wc, ws, bias, rows)
+        assert_y_strict(Yg[rows], Ye, env, jump, ydt, K // 64, R)
+    Yo = O.linear(X[rows], inv_o, p.L1, p.L2, wc, ws, bias, ydt, activation=act)
+    assert rel_err(Yg[rows], Yo) <= TOL_Y
+    # the fused entry point with room for the split: the same bits
+    need = sq.linear_tiled_workspace_bytes(M, K, R) + sq.gemm_tiled_workspace_bytes(M, N, K)
+    wsb = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    Y2 = torch.full_like(d.Y, float("nan"))
+    sq.linear_tiled(d.X, d.inv, d.L1p, d.L2t, R, d.wc, d.ws, d.bias, Y2, wsb, activation=act)
+    torch.cuda.synchronize()
+    assert torch.equal(d.Y.view(torch.uint8), Y2.view(torch.uint8))
+    # unsplit: the same bound
+    d2 = TiledLayer(X, p, bias, ydt, k2_workspace=False)
+    d2.k1()
+    d2.k2(activation=act)
+    torch.cuda.synchronize()
+    Yu = d2.Y.cpu().numpy()
+    if act is None:
+        assert_y_strict(Yu[rows], Ye, env, jump, ydt, K // 64, R)
+    assert rel_err(Yu, Yg) <= TOL_Y

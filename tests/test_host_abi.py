@@ -91,7 +91,7 @@ def test_one_hip_runtime_is_mapped():
 
 
 def test_version_and_status_strings():
-    assert _lib.abi_version() == 11
+    assert _lib.abi_version() == 12
     for s in range(12):
         assert _lib.status_str(s) and _lib.status_str(s) != "unknown status"
     assert _lib.status_str(99) == "unknown status"
@@ -586,6 +586,32 @@ def test_pre_kernel_workspace_sizes():
         base_m = (((M + 15) // 16) * C * 1024 + ((M + 63) // 64) * C * 256
                   + (((M + 15) // 16) * ((R + 31) // 32) * 1024 + 255) // 256 * 256)
         assert L.svdq_linear_mx_workspace_bytes(M, K, R) == base_m + extra
+
+
+def test_gemm_tiled_workspace_sizes():
+    """The tiled GEMM's split along K: S partial 128 x 128 fp32 tiles per tile
+    when the tiles fill at most a quarter of the resident slots and K holds at
+    least 32 groups, S = slots / tiles capped at G / 16 and 8. Without a device the
+    library takes 512 slots (2 per compute unit of MI355X); the GPU uses the
+    kernel's own occupancy. A workspace below the size is refused."""
+    L = _lib.lib
+    ws = L.svdq_gemm_tiled_workspace_bytes
+    # 16 x 8 tiles = a quarter of 512 slots, 180 groups: S = min(512 // 128, 11, 8) = 4
+    assert ws(2048, 1024, 11520) == 4 * 128 * 128 * 128 * 4
+    # 16 x 10 tiles: more than a quarter of 512 (on MI355X's 768 slots it splits)
+    assert ws(2048, 1280, 11520) == 0
+    # 8 x 5 tiles, K = 2560 (40 groups): S = min(12, 2, 8) = 2
+    assert ws(1024, 640, 2560) == 2 * 40 * 128 * 128 * 4
+    for shape in [(4608, 9216, 3072),    # 2592 tiles: no room to split
+                  (2048, 1280, 1280),    # 20 groups
+                  (2048, 1280, 1000), (0, 64, 4096), (64, 0, 4096)]:
+        assert ws(*shape) == 0, shape
+    need = ws(1024, 640, 2560)
+    args = [A16, A16, A16, A16, A16, A16, 16, None, A16, 1, 1024, 640, 2560, 640, 0, 0x10000,
+            need - 1, None]
+    assert L.svdq_w4a4_gemm_lowrank_up_tiled(*args) == _lib.ERR_WORKSPACE
+    args[15], args[16] = 0x10040, need
+    assert L.svdq_w4a4_gemm_lowrank_up_tiled(*args) == _lib.ERR_ALIGN
 
 
 def _has_gpu():
