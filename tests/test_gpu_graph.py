@@ -118,3 +118,33 @@ def test_canonical_entry_replays_in_a_graph(spec):
         Y.fill_(float("nan"))
 
     _replay_and_check(step, [Y], refill)
+
+
+@pytest.mark.parametrize("shape", [(4100, 6144, 256, 16), (2000, 4096, 600, 32)],
+                         ids=["k1_split_long_rows", "k2_split_along_k"])
+def test_split_paths_replay_in_a_graph(shape):
+    """The split pre-kernel (long rows) and the GEMM split along K (a quarter-
+    filled long-K grid) each launch a second, reducing kernel; captured with
+    their workspaces, they replay to the eager bits."""
+    import bit_post_quantized_smooth_amd as sq
+    from test_gpu_parity import _edge_inputs
+    M, K, N, R = shape
+    X, W, b = _edge_inputs(M, K, N, R, "f16", seed=M + K)
+    lam = sq.smoothing_factors(sq.channel_absmax(X), W)
+    p = sq.prepare_weights(W, lam, R)
+    d = TiledLayer(X, p, b, "f16", k1_workspace=True, k2_workspace=True)
+    assert (sq.quantize_act_workspace_bytes(M, K, R) > 0) or (sq.gemm_tiled_workspace_bytes(M, N, K) > 0)
+
+    def step():
+        d.k1()
+        d.k2()
+
+    def refill():
+        d.ops.fill_(0x5A)
+        d.scales.fill_(float("nan"))
+        d.D.fill_(-1)
+        d.Y.fill_(float("nan"))
+        d.k1ws.fill_(0xA5)
+        d.k2ws.fill_(0xA5)
+
+    _replay_and_check(step, [d.Y, d.scales, d.D], refill)
