@@ -580,7 +580,7 @@ hipError_t launch_k1_rt(const void* X, int64_t M, int64_t K, int64_t ldx,
   const int64_t tiles = (M + 16 * RT - 1) / (16 * RT);
   // only two-tile workgroups with one group in flight, on the tiled layouts of a
   // linear layer, have a split instance (the launch rule asks for no other)
-  const bool split = RT == 2 && NB == 1 && NCB <= 4 && sp.S > 1 && conv == nullptr &&
+  const bool split = RT == 2 && NB == 1 && NCB <= 6 && sp.S > 1 && conv == nullptr &&
                      fmt != kK1Int4;
   const dim3 block(64 * WV), grid(static_cast<unsigned>(tiles * (split ? sp.S : 1)));
   const XT* x = static_cast<const XT*>(X);
@@ -589,7 +589,7 @@ hipError_t launch_k1_rt(const void* X, int64_t M, int64_t K, int64_t ldx,
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, x, M, K, ldx, inv_smooth, L1p, R, a_codes,
                        a_meta, D, cg, sp.S, sp.part);
   };
-  if constexpr (RT == 2 && NB == 1 && NCB <= 4) {
+  if constexpr (RT == 2 && NB == 1 && NCB <= 6) {
     if (split) {
       if (fmt == kK1Mx) go(k1_quant_down_kernel<XT, NCB, NB, kK1Mx, false, RT, WV, true>);
       else go(k1_quant_down_kernel<XT, NCB, NB, kK1Int4Tiled, false, RT, WV, true>);
@@ -633,7 +633,8 @@ hipError_t launch_k1_rt(const void* X, int64_t M, int64_t K, int64_t ldx,
 // groups keep 16-row tiles (32768 x 320: 11.8 against 12.7-13.2 us). At rank
 // 96 (9216 x 3072) two tiles with two groups in flight were faster with X
 // streamed from HBM alone but 1.3 us slower inside the step (42.6 against
-// 41.3 us), so ranks above 64 keep 16-row tiles. The convolution keeps its
+// 41.3 us), so ranks above 64 keep 16-row tiles unless they are split (ranks
+// 80 and 96 with a workspace: k1_slices). The convolution keeps its
 // own rule (two tiles on patch matrices of more tiles than compute units
 // unless the rows are short and every tile is resident: the 128 x 128 image
 // took 48.0 against 56.1 us).
@@ -665,6 +666,14 @@ hipError_t launch_k1_t(const void* X, int64_t M, int64_t K, int64_t ldx,
                                            D, stream, conv);
       return launch_k1_rt<XT, NCB, 2, 2>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D,
                                          stream, conv);
+    }
+  } else if constexpr (NCB <= 6) {
+    // ranks 80 and 96: 32-row tiles split along K, or 16-row tiles
+    if (conv == nullptr && 2 * tiles > slots) {
+      const int S = k1_slices(M, K, R, fmt, false);
+      if (S > 1 && part != nullptr)
+        return launch_k1_rt<XT, NCB, 2, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt,
+                                           D, stream, conv, K1Split{S, part});
     }
   }
   return launch_k1_rt<XT, NCB, 1, 1>(X, M, K, ldx, inv_smooth, L1p, R, a_codes, a_meta, fmt, D,
@@ -709,12 +718,20 @@ hipError_t launch_k1(const void* X, bool x_f16, int64_t M, int64_t K, int64_t ld
 // that about four units of work per compute unit even out the tiles left
 // over. Measured on MI355X on the 12288-channel down-projection at 4608 rows
 // (144 tiles, S = 8), the pre-kernel alone with X streamed from HBM: 41.5 us
-// plus 4 us for the reduction pass against 57.7 us unsplit. The canonical
-// layout (fp32 D), the convolution and ranks above 64 are not split.
+// plus 4 us for the reduction pass against 57.7 us unsplit.
+// Ranks 80 and 96 are split whatever the row length: there the L1 operands
+// (K x R fp16, 590 KB at 3072 x 96) are read again from L2 by every row tile,
+// and 32-row tiles halve those reads; the split keeps the 32-row tiles from
+// leaving compute units idle. Measured on MI355X on the 3072-channel LoRA
+// layers at 9216 rows and rank 96 (288 tiles, S = 3), against 16-row tiles
+// unsplit: pre-kernel 38.0 against 41.5 us, the 19-layer chain 3.40 against
+// 3.58 ms in INT4 and 1.78 against 1.91 ms in MXFP4 (S = 2: 3.41 and 1.79 ms).
+// The canonical layout (fp32 D), the convolution and ranks above 96 are not
+// split.
 int k1_slices(int64_t M, int64_t K, int R, int fmt, bool conv) {
-  if (conv || fmt == kK1Int4 || R > 64 || M < 1 || K < 64) return 1;
+  if (conv || fmt == kK1Int4 || R > 96 || M < 1 || K < 64) return 1;
   const int64_t tiles = (M + 15) / 16, slots = resident_slots(), G = K / 64;
-  if (2 * tiles <= slots || G < 12 * 8) return 1;
+  if (2 * tiles <= slots || (R <= 64 && G < 12 * 8)) return 1;
   const int64_t t32 = (M + 31) / 32, cus = slots / 2;
   int64_t S = (4 * cus + t32 - 1) / t32;
   if (S > G / 16) S = G / 16;
