@@ -571,10 +571,17 @@ def test_pre_kernel_workspace_sizes():
     assert ws(4100, 6144, 16) == 6 * 4128 * 16 * 4
     # 8200 rows: 257 tiles, S = ceil(1024 / 257) = 4
     assert ws(8200, 6144, 32) == 4 * 8224 * 32 * 4
+    # ranks 80 and 96 split whatever the row length: 4608 x 12288 as above
+    # (S = 8); 9216 x 3072 (48 groups): 288 tiles, ceil(1024 / 288) = 4,
+    # capped at G / 16 = 3
+    assert ws(4608, 12288, 96) == 8 * 4608 * 96 * 4
+    assert ws(9216, 3072, 96) == 3 * 9216 * 96 * 4
+    assert ws(9216, 3072, 80) == 3 * 9216 * 80 * 4
     for shape in [(4608, 3072, 32),     # short rows: 48 groups
                   (4096, 12288, 32),    # 256 tiles of 16 rows: one per compute unit
                   (4608, 12288, 0),     # no D
-                  (4608, 12288, 96),    # rank above 64
+                  (4608, 12288, 112),   # rank above 96
+                  (4096, 3072, 96),     # rank 96, one 16-row tile per compute unit
                   (4608, 12280, 32), (0, 12288, 32), (4608, 12288, 24)]:
         assert ws(*shape) == 0, shape
     for M, K, R in [(4608, 12288, 32), (4608, 3072, 32), (4100, 6144, 16)]:
